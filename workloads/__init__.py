@@ -1,0 +1,383 @@
+"""Seeded synthetic SEACells workloads: points -> kNN kernel -> FW operands.
+
+This module produces inputs only. It holds none of the Frank-Wolfe
+arithmetic (no gradient, argmin or step); the f64 oracle and the HIP library
+both consume what it writes, and neither imports the other.
+
+The pages fix no dataset. Each workload is a seeded single-cell stand-in:
+
+* points: a C-component Gaussian mixture in d dimensions. Means are
+  N(0, 4 I) (sigma 2 per coordinate). The per-component std is 1, or
+  U(0.5, 2) for the larger configs. Component weights are equal, or Zipf
+  r^-s for the skewed config. Labels are i.i.d. from those weights.
+* kernel K: exact Euclidean kNN with the cell itself excluded and ties
+  broken by index. Adaptive Gaussian weights W_ij = exp(-d_ij^2 / (s_i s_j))
+  with s_i the distance to the kNN-th neighbour, then K = (W + W^T) / 2
+  with K_ii = 1. K^2 is never formed: products are K (K X) in f64.
+* B (n x k, column-stochastic): k distinct uniformly random init cells. For
+  s_B > 0, each column also takes s_B cells drawn uniformly, with
+  replacement, from its init cell's mixture component. Weights are
+  Dirichlet(1) on that support. This stands in for "B after s_B prior FW
+  steps" without running any FW step here.
+* A_prev (k x n, column-stochastic): column j is supported on the s_A
+  archetypes whose init cells lie nearest to x_j (ties by index), with
+  Dirichlet(1) weights.
+* operands, built in f64 with scipy.sparse, symmetrised where the maths says
+  symmetric, then cast once to f32 with sorted int32 indices and no stored
+  zeros:
+    t1 = B^T K^2 B (k x k), K2B = K^2 B (n x k), A_prev^T (n x k) for the A
+    update; K2B, AAt = A A^T (k x k), K2At = K^2 A^T (n x k) and B for the
+    B argmin.
+
+RNG: numpy PCG64 ``default_rng(1000 * index + seed)``. Draws happen in this
+order: means, scales, labels, noise, init cells, B supports, B weights,
+A weights.
+"""
+from __future__ import annotations
+
+import hashlib
+import json
+import os
+import time
+from dataclasses import asdict, dataclass, field
+
+import numpy as np
+import scipy.sparse as sp
+
+GENERATOR_VERSION = 1
+_REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@dataclass(frozen=True)
+class Config:
+    name: str
+    n: int            # cells
+    d: int            # point dimension
+    comps: int        # mixture components
+    knn: int          # neighbours per cell in the kernel graph
+    k: int            # archetypes
+    s_a: int          # non-zeros per A_prev column
+    s_b: int          # extra B support cells per column
+    scale: tuple | None = None   # per-component std range, None = 1
+    zipf: float | None = None    # component-weight exponent, None = equal
+    T: int = 50                  # A steps
+    index: int = 0               # RNG stream index
+
+
+CONFIGS = {
+    "c1": Config("c1", 2_000, 10, 5, 15, 25, 5, 0, index=1),
+    "c2": Config("c2", 20_000, 20, 10, 15, 250, 8, 3, index=2),
+    "c3": Config("c3", 100_000, 30, 20, 20, 1_300, 10, 10, scale=(0.5, 2.0), index=3),
+    "c4": Config("c4", 500_000, 30, 50, 20, 6_700, 12, 20, scale=(0.5, 2.0), index=4),
+    "c5": Config("c5", 1_000_000, 50, 100, 30, 10_000, 16, 30, scale=(0.5, 2.0), zipf=1.1,
+                 index=5),
+}
+
+DESCRIPTIONS = {
+    "c1": "n=2000 d=10 C=5 kNN=15 k=25 s_A=5 B one-hot T=50",
+    "c2": "n=20000 d=20 C=10 kNN=15 k=250 s_A=8 s_B=3 T=50",
+    "c3": "n=100000 d=30 C=20 std~U(0.5,2) kNN=20 k=1300 s_A=10 s_B=10 T=50",
+    "c4": "n=500000 d=30 C=50 std~U(0.5,2) kNN=20 k=6700 s_A=12 s_B=20 T=50",
+    "c5": "n=1000000 d=50 C=100 Zipf(1.1) std~U(0.5,2) kNN=30 k=10000 s_A=16 s_B=30 T=50",
+}
+
+
+@dataclass
+class Workload:
+    cfg: Config
+    seed: int
+    t1: sp.csr_matrix          # k x k, f32, symmetric
+    k2b: sp.csr_matrix         # n x k, f32
+    a_prev_t: sp.csr_matrix    # n x k, f32 (rows are columns of A_prev)
+    aat: sp.csr_matrix         # k x k, f32, symmetric
+    k2at: sp.csr_matrix        # n x k, f32
+    b: sp.csr_matrix           # n x k, f32
+    init_cells: np.ndarray     # [k]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def n(self):
+        return self.cfg.n
+
+    @property
+    def k(self):
+        return self.cfg.k
+
+    @property
+    def T(self):
+        return self.cfg.T
+
+    @property
+    def cap(self):
+        """Atom capacity: widest A_prev column plus one append per step."""
+        widest = int(np.diff(self.a_prev_t.indptr).max()) if self.n else 0
+        return widest + self.cfg.T
+
+
+# --------------------------------------------------------------------------
+# points and kernel
+# --------------------------------------------------------------------------
+
+def _points(cfg: Config, rng):
+    C, d, n = cfg.comps, cfg.d, cfg.n
+    means = rng.normal(0.0, 2.0, size=(C, d))
+    if cfg.scale is None:
+        scales = np.ones(C)
+    else:
+        scales = rng.uniform(cfg.scale[0], cfg.scale[1], size=C)
+    if cfg.zipf is None:
+        w = np.full(C, 1.0 / C)
+    else:
+        w = np.arange(1, C + 1, dtype=np.float64) ** (-cfg.zipf)
+        w /= w.sum()
+    labels = rng.choice(C, size=n, p=w)
+    noise = rng.normal(0.0, 1.0, size=(n, d))
+    X = means[labels] + scales[labels, None] * noise
+    return X, labels
+
+
+def _nearest(Q, P, kk, exclude_self=False, margin=8, block=2048):
+    """Exact kk nearest rows of P for every row of Q (Euclidean, f64).
+
+    Candidates come from an f32 pass on torch (GPU when present); the top
+    kk + margin candidates are re-ranked by exact f64 distance with ties
+    broken by index, so the result does not depend on the device.
+    """
+    import torch
+
+    dev = "cuda" if torch.cuda.is_available() else "cpu"
+    nq, npnt = Q.shape[0], P.shape[0]
+    m = min(kk + margin, npnt - (1 if exclude_self else 0))
+    Pt = torch.from_numpy(P.astype(np.float32)).to(dev)
+    psq = (Pt * Pt).sum(1)
+    Qt_all = torch.from_numpy(Q.astype(np.float32))
+    cand = np.empty((nq, m), np.int64)
+    for s in range(0, nq, block):
+        e = min(nq, s + block)
+        q = Qt_all[s:e].to(dev)
+        d2 = (q * q).sum(1)[:, None] + psq[None, :] - 2.0 * (q @ Pt.T)
+        if exclude_self:
+            r = torch.arange(e - s, device=dev)
+            d2[r, r + s] = float("inf")
+        _, idx = torch.topk(d2, m, dim=1, largest=False, sorted=False)
+        cand[s:e] = idx.cpu().numpy()
+    # exact re-rank
+    out_i = np.empty((nq, kk), np.int64)
+    out_d = np.empty((nq, kk), np.float64)
+    for s in range(0, nq, 16384):
+        e = min(nq, s + 16384)
+        c = cand[s:e]
+        diff = Q[s:e, None, :] - P[c]
+        dd = np.einsum("ijk,ijk->ij", diff, diff)
+        # sort by (distance, index): index first, then a stable sort on distance
+        o1 = np.argsort(c, axis=1, kind="stable")
+        c1 = np.take_along_axis(c, o1, 1)
+        d1 = np.take_along_axis(dd, o1, 1)
+        o2 = np.argsort(d1, axis=1, kind="stable")[:, :kk]
+        out_i[s:e] = np.take_along_axis(c1, o2, 1)
+        out_d[s:e] = np.take_along_axis(d1, o2, 1)
+    return out_i, out_d
+
+
+def _kernel(X, knn):
+    n = X.shape[0]
+    nb, d2 = _nearest(X, X, knn, exclude_self=True)
+    sig = np.sqrt(d2[:, -1])
+    sig = np.where(sig > 0, sig, 1.0)
+    rows = np.repeat(np.arange(n), knn)
+    cols = nb.ravel()
+    w = np.exp(-d2.ravel() / (sig[rows] * sig[cols]))
+    W = sp.csr_matrix((w, (rows, cols)), shape=(n, n))
+    K = ((W + W.T) * 0.5).tolil()
+    K.setdiag(1.0)
+    K = K.tocsr()
+    K.sort_indices()
+    return K
+
+
+# --------------------------------------------------------------------------
+# B, A_prev and operands
+# --------------------------------------------------------------------------
+
+def _b_matrix(cfg: Config, rng, labels, init):
+    n, k = cfg.n, cfg.k
+    members = [np.flatnonzero(labels == c) for c in range(cfg.comps)]
+    supports = []
+    for c in range(k):
+        cells = [int(init[c])]
+        if cfg.s_b > 0:
+            pool = members[labels[init[c]]]
+            cells.extend(int(x) for x in rng.choice(pool, size=cfg.s_b, replace=True))
+        supports.append(np.unique(np.asarray(cells, np.int64)))
+    rows, cols, vals = [], [], []
+    for c, sup in enumerate(supports):
+        wts = rng.dirichlet(np.ones(sup.shape[0])) if sup.shape[0] > 1 else np.ones(1)
+        rows.append(sup)
+        cols.append(np.full(sup.shape[0], c))
+        vals.append(wts)
+    return sp.csr_matrix((np.concatenate(vals), (np.concatenate(rows), np.concatenate(cols))),
+                         shape=(n, k))
+
+
+def _a_prev_t(cfg: Config, rng, X, init):
+    n, k = cfg.n, cfg.k
+    s_a = min(cfg.s_a, k)
+    nb, _ = _nearest(X, X[init], s_a, exclude_self=False)
+    wts = rng.dirichlet(np.ones(s_a), size=n)
+    rows = np.repeat(np.arange(n), s_a)
+    return sp.csr_matrix((wts.ravel(), (rows, nb.ravel())), shape=(n, k))
+
+
+def _f32(m, symmetric=False):
+    m = sp.csr_matrix(m, dtype=np.float64)
+    if symmetric:
+        m = sp.csr_matrix((m + m.T) * 0.5)
+    m.sum_duplicates()
+    m.sort_indices()
+    out = sp.csr_matrix((m.data.astype(np.float32), m.indices, m.indptr), shape=m.shape)
+    out.eliminate_zeros()
+    out.sort_indices()
+    if out.nnz >= 2 ** 31:
+        raise ValueError("operand has 2^31 or more non-zeros")
+    out.indices = out.indices.astype(np.int32)
+    out.indptr = out.indptr.astype(np.int32)
+    return out
+
+
+def _sha(*arrays):
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
+
+
+def generate(cfg: Config, seed: int = 0) -> Workload:
+    t0 = time.time()
+    rng = np.random.default_rng(1000 * cfg.index + seed)
+    X, labels = _points(cfg, rng)
+    t_pts = time.time()
+    K = _kernel(X, cfg.knn)
+    t_knn = time.time()
+    init = rng.choice(cfg.n, size=cfg.k, replace=False)
+    B = _b_matrix(cfg, rng, labels, init)
+    At = _a_prev_t(cfg, rng, X, init)
+    K2B = K @ (K @ B)
+    t1 = B.T @ K2B
+    K2At = K @ (K @ At)
+    AAt = At.T @ At
+    w = Workload(cfg, seed, t1=_f32(t1, symmetric=True), k2b=_f32(K2B), a_prev_t=_f32(At),
+                 aat=_f32(AAt, symmetric=True), k2at=_f32(K2At), b=_f32(B),
+                 init_cells=np.asarray(init, np.int64))
+    t_end = time.time()
+    w.meta = {
+        "generator_version": GENERATOR_VERSION,
+        "config": asdict(cfg),
+        "seed": seed,
+        "seconds": {"points": t_pts - t0, "kernel": t_knn - t_pts, "operands": t_end - t_knn},
+        "nnz": {nm: int(getattr(w, nm).nnz) for nm in ("t1", "k2b", "a_prev_t", "aat", "k2at", "b")},
+        "nnz_K": int(K.nnz),
+        "sha256": {nm: _sha(getattr(w, nm).indptr, getattr(w, nm).indices, getattr(w, nm).data)
+                   for nm in ("t1", "k2b", "a_prev_t", "aat", "k2at", "b")},
+    }
+    return w
+
+
+# --------------------------------------------------------------------------
+# cache
+# --------------------------------------------------------------------------
+
+def cache_dir():
+    return os.environ.get("SEACELLS_WORKLOAD_CACHE", os.path.join(_REPO, ".cache", "workloads"))
+
+
+_NAMES = ("t1", "k2b", "a_prev_t", "aat", "k2at", "b")
+
+
+def _save(w: Workload, path):
+    arrs = {"init_cells": w.init_cells}
+    for nm in _NAMES:
+        m = getattr(w, nm)
+        arrs[nm + "_ptr"], arrs[nm + "_idx"], arrs[nm + "_val"] = m.indptr, m.indices, m.data
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    tmp = path + ".tmp%d.npz" % os.getpid()
+    np.savez(tmp, **arrs)
+    os.replace(tmp, path)
+    with open(path + ".json", "w") as f:
+        json.dump(w.meta, f, indent=1)
+
+
+def _load(cfg: Config, seed: int, path) -> Workload:
+    z = np.load(path, allow_pickle=False)
+    n, k = cfg.n, cfg.k
+    shapes = {"t1": (k, k), "k2b": (n, k), "a_prev_t": (n, k), "aat": (k, k), "k2at": (n, k),
+              "b": (n, k)}
+    mats = {nm: sp.csr_matrix((z[nm + "_val"], z[nm + "_idx"], z[nm + "_ptr"]), shape=shapes[nm])
+            for nm in _NAMES}
+    with open(path + ".json") as f:
+        meta = json.load(f)
+    return Workload(cfg, seed, init_cells=z["init_cells"], meta=meta, **mats)
+
+
+def make(name_or_cfg, seed: int = 0, cache: bool = True) -> Workload:
+    """The workload for a named config ("c1".."c5") or a custom Config."""
+    cfg = CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
+    if not cache:
+        return generate(cfg, seed)
+    key = "%s_n%d_k%d_s%d_v%d.npz" % (cfg.name, cfg.n, cfg.k, seed, GENERATOR_VERSION)
+    path = os.path.join(cache_dir(), key)
+    if os.path.exists(path) and os.path.exists(path + ".json"):
+        with open(path + ".json") as f:
+            meta = json.load(f)
+        if meta.get("config") == json.loads(json.dumps(asdict(cfg))):
+            return _load(cfg, seed, path)
+    w = generate(cfg, seed)
+    _save(w, path)
+    return w
+
+
+# --------------------------------------------------------------------------
+# layout helpers (no arithmetic)
+# --------------------------------------------------------------------------
+
+def bt_padded(b: sp.csr_matrix, cap_b: int):
+    """B (n x k CSR) as padded B^T rows: idx [k, cap_b] u32, val [k, cap_b] f32, cnt [k]."""
+    bt = sp.csr_matrix(b.T)
+    bt.sort_indices()
+    k = bt.shape[0]
+    cnt = np.diff(bt.indptr).astype(np.uint32)
+    if k and int(cnt.max()) > cap_b:
+        raise ValueError("cap_b %d below the widest B column %d" % (cap_b, int(cnt.max())))
+    idx = np.zeros((k, cap_b), np.uint32)
+    val = np.zeros((k, cap_b), np.float32)
+    for c in range(k):
+        s, e = bt.indptr[c], bt.indptr[c + 1]
+        idx[c, : e - s] = bt.indices[s:e]
+        val[c, : e - s] = bt.data[s:e]
+    return idx, val, cnt
+
+
+# --------------------------------------------------------------------------
+# the source page's deterministic test fixtures
+# --------------------------------------------------------------------------
+
+def page_fixture(length: int, seed: int, zero_every: int) -> np.ndarray:
+    """The page's dense test fixture (test helper `fixture` of
+    bixverse-rs 0.6.4, seacells_kernels.rs): value ((37 i + 17 seed) mod 23
+    - 11) * 0.1 computed in f32, zero wherever (i + seed) is a multiple of
+    zero_every. Values are signed."""
+    i = np.arange(length, dtype=np.int64)
+    v = (np.float32(1.0) * ((i * 37 + seed * 17) % 23).astype(np.float32) - np.float32(11.0)) \
+        * np.float32(0.1)
+    v = v.astype(np.float32)
+    v[(i + seed) % zero_every == 0] = np.float32(0.0)
+    return v
+
+
+def dense_to_csr(a: np.ndarray) -> sp.csr_matrix:
+    """Row-major dense f32 to CSR keeping only non-zero entries (int32 indices)."""
+    m = sp.csr_matrix(np.asarray(a, np.float32))
+    m.eliminate_zeros()
+    m.sort_indices()
+    m.indices = m.indices.astype(np.int32)
+    m.indptr = m.indptr.astype(np.int32)
+    return m
