@@ -1,0 +1,192 @@
+/*
+ * seacells_fw.h - C ABI of the SEACells Frank-Wolfe hot path on MI355X
+ * (gfx950).
+ *
+ * The library runs the two data-parallel Frank-Wolfe updates of SEACells
+ * kernel archetypal analysis, min ||K - K B A||_F^2 over column-stochastic
+ * B (n x k) and A (k x n), on one GPU:
+ *
+ *   - the per-cell A column solve (seacells_fw_a_columns);
+ *   - the per-archetype B-gradient argmin over cells (seacells_fw_b_argmin)
+ *     and the B step that consumes it (seacells_fw_b_apply).
+ *
+ * The method is the one on the docs.rs source page "bixverse-rs 0.6.4 -
+ * src/gpu/sc_gpu/kernels/seacells_kernels.rs". Building K, K^2 B, t1,
+ * A A^T, K^2 A^T and the RSS stays with the caller on the host, as the
+ * page's module doc places it.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Sparse operands are CSR (seacells_csr). row_ptr, col_idx and val are
+ *   device pointers. Column indices are strictly ascending within a row and
+ *   below n_cols. nnz == row_ptr[n_rows] and nnz < 2^31. Values are finite.
+ *   These are preconditions: the library does not read device memory on the
+ *   host to check them.
+ * - Every n x k matrix is CSR over cells (rows = cells), as on the page's
+ *   module doc. k x k matrices (t1 = B^T K^2 B, A A^T) must be symmetric:
+ *   the page adds row `amin` of t1 where the maths adds column `amin`.
+ * - Ownership: the caller allocates and frees every buffer (inputs,
+ *   outputs, workspace, the status word). The library never allocates,
+ *   frees or synchronises. All work is enqueued on `stream` (a hipStream_t;
+ *   NULL = the default stream). Outputs are ready when the stream is.
+ * - Return value: SEACELLS_OK, or a negative SEACELLS_E_* code detected
+ *   synchronously on the host before any device work is enqueued
+ *   (SEACELLS_E_HIP: a launch failed; the HIP message is available from
+ *   seacells_last_error()).
+ * - *status (a device uint32) is overwritten by every call with the OR of
+ *   the SEACELLS_FLAG_* conditions the kernels detected; read it after the
+ *   stream synchronises. A non-zero status means the outputs are not valid.
+ * - Results are deterministic: no floating-point atomics, fixed reduction
+ *   orders; two calls on the same inputs give bitwise-equal outputs.
+ * - Calls that share a workspace or status word must not overlap.
+ * - There is no ceiling on k: state that does not fit the compute unit's
+ *   local memory moves to the workspace (A) or is split into column
+ *   slices (B).
+ */
+#ifndef SEACELLS_FW_H
+#define SEACELLS_FW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Host-detected errors (return values). */
+#define SEACELLS_OK 0
+#define SEACELLS_E_NULL (-1)      /* a required pointer is NULL */
+#define SEACELLS_E_SHAPE (-2)     /* n, k or T is 0, or operand shapes disagree */
+#define SEACELLS_E_WORKSPACE (-3) /* workspace smaller than the *_workspace() size */
+#define SEACELLS_E_TOO_LARGE (-4) /* n, k or nnz >= 2^31, n * cap >= 2^40, cap * 8 > 160 KB */
+#define SEACELLS_E_HIP (-5)       /* a HIP launch or query failed */
+
+/* Device-detected conditions (bits of *status). */
+#define SEACELLS_FLAG_CAP_OVERFLOW 0x1u     /* an A column needed more than `cap` atoms */
+#define SEACELLS_FLAG_PARTIALS_INVALID 0x2u /* a B partial was stale or out of range */
+#define SEACELLS_FLAG_B_CAP_OVERFLOW 0x4u   /* a padded B^T row was full */
+#define SEACELLS_FLAG_BAD_INDEX 0x8u        /* an index argument was out of range */
+#define SEACELLS_FLAG_NONFINITE 0x10u       /* a non-finite value reached an argmin */
+#define SEACELLS_FLAG_BAD_GAMMA 0x20u       /* a step size outside (0, 1] */
+
+typedef struct ihipStream_t *seacells_stream_t; /* == hipStream_t */
+
+/* A CSR matrix in device memory (the struct itself lives on the host). */
+typedef struct seacells_csr {
+    const uint32_t *row_ptr; /* [n_rows + 1], row_ptr[0] == 0, non-decreasing */
+    const uint32_t *col_idx; /* [nnz], strictly ascending within a row, < n_cols */
+    const float *val;        /* [nnz] */
+    uint32_t n_rows;
+    uint32_t n_cols;
+    uint32_t nnz;
+} seacells_csr;
+
+/*
+ * Workspace bytes seacells_fw_a_columns needs for these sizes (0 when the
+ * whole per-cell state fits in local memory). Depends only on its
+ * arguments.
+ */
+size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint32_t cap);
+
+/*
+ * A update: the per-cell column solve of `fw_columns_a_gpu` on the source
+ * page (its doc comment and the `a_columns_capacity` doc).
+ *
+ * For every cell j in [0, n), starting from a_j = row j of A_prev^T, run T
+ * Frank-Wolfe steps t = 0 .. T-1 of
+ *     g      = t1 . a_j - K2B[j, :]
+ *     idx_t  = argmin_c g[c]   (lowest c on a tie; -0 == +0)
+ *     a_j    = (1 - gamma_t) a_j + gamma_t e_idx_t
+ * with gamma_t = gamma[t], or 2 / (t + 2) when gamma is NULL.
+ *
+ * t1        k x k CSR, symmetric (B^T K^2 B).
+ * k2b       n x k CSR (K^2 B, rows = cells).
+ * a_prev_t  n x k CSR (A_prev^T: row j holds column j of A_prev).
+ * gamma     device [T] f32 step sizes in (0, 1], or NULL.
+ * cap       atom slots per cell: at least max_j nnz(a_prev_t row j) + T,
+ *           the page's `a_columns_capacity` rule. Overflow sets
+ *           SEACELLS_FLAG_CAP_OVERFLOW.
+ * atom_idx  device [n * cap] u32 out: the atoms of cell j at
+ *           [j * cap, j * cap + atom_cnt[j]): the seeds first in A_prev
+ *           order (a seed may end at weight 0: gamma_0 = 1 zeroes every
+ *           seed), then each newly picked index in order of first pick.
+ *           Indices are unique per cell. Slots past atom_cnt[j] are left
+ *           unchanged.
+ * atom_val  device [n * cap] f32 out: the matching weights of a_j.
+ * atom_cnt  device [n] u32 out.
+ * trace     device [n * T] u32 out, or NULL: trace[j * T + t] = idx_t.
+ * workspace device buffer of at least seacells_fw_a_columns_workspace()
+ *           bytes (may be NULL when that is 0), 256-byte aligned.
+ */
+int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
+                          const seacells_csr *a_prev_t, uint32_t n, uint32_t k,
+                          uint32_t T, uint32_t cap, const float *gamma,
+                          uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
+                          uint32_t *trace, void *workspace, size_t workspace_bytes,
+                          uint32_t *status, seacells_stream_t stream);
+
+/*
+ * Workspace bytes seacells_fw_b_argmin needs for these sizes (always > 0).
+ * Depends only on its arguments.
+ */
+size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k);
+
+/*
+ * B-gradient argmin: `fw_argmin_b` followed by `reduce_argmin_blocks` on
+ * the source page (their doc comments, and the tests
+ * `test_fw_argmin_b_handles_empty_rows` and
+ * `test_fw_argmin_b_tie_breaks_on_lowest_row`).
+ *
+ *     G[i, c]    = sum_m K2B[i, m] AAt[m, c] - K2At[i, c]   (never stored)
+ *     out_idx[c] = lowest i attaining min_i G[i, c]; out_val[c] = that min
+ *     gap        = sum_{i, c} B[i, c] G[i, c]  (the page's sum(B * G) half
+ *                  of the duality gap)
+ * Every row takes part, including rows whose K2B row is empty.
+ *
+ * k2b   n x k CSR (K^2 B).     aat   k x k CSR, symmetric (A A^T).
+ * k2at  n x k CSR (K^2 A^T).   b     n x k CSR (B), or NULL: gap = 0.
+ * out_val  device [k] f32 out.   out_idx  device [k] u32 out.
+ * gap      device [1] f32 out, or NULL.
+ * The reduce stage checks that every partial was written by this call and
+ * holds a row below n; otherwise it sets SEACELLS_FLAG_PARTIALS_INVALID.
+ */
+int seacells_fw_b_argmin(const seacells_csr *k2b, const seacells_csr *aat,
+                         const seacells_csr *k2at, const seacells_csr *b, uint32_t n,
+                         uint32_t k, float *out_val, uint32_t *out_idx, float *gap,
+                         void *workspace, size_t workspace_bytes, uint32_t *status,
+                         seacells_stream_t stream);
+
+/*
+ * B step: B_c <- (1 - gamma) B_c + gamma e_{arg_idx[c]} for every column c,
+ * the update the B argmin feeds (the page leaves it to its caller).
+ *
+ * B^T is held as padded rows, one per archetype: row c has bt_cnt[c]
+ * entries at bt_idx[c * cap_b + s] (cell indices, ascending) and
+ * bt_val[c * cap_b + s]. A cell not yet in the row is inserted at its
+ * sorted position. A full row is left unchanged and sets
+ * SEACELLS_FLAG_B_CAP_OVERFLOW; arg_idx[c] >= n sets
+ * SEACELLS_FLAG_BAD_INDEX (row unchanged).
+ *
+ * bt_idx, bt_val  device [k * cap_b], updated in place.
+ * bt_cnt          device [k], updated in place.
+ * arg_idx         device [k] (out_idx of seacells_fw_b_argmin).
+ * gamma           host scalar in (0, 1].
+ */
+int seacells_fw_b_apply(uint32_t *bt_idx, float *bt_val, uint32_t *bt_cnt, uint32_t n,
+                        uint32_t k, uint32_t cap_b, const uint32_t *arg_idx, float gamma,
+                        uint32_t *status, seacells_stream_t stream);
+
+/* Static text for a SEACELLS_E_* code. */
+const char *seacells_status_string(int code);
+
+/* Detail of the last SEACELLS_E_HIP on the calling thread ("" if none). */
+const char *seacells_last_error(void);
+
+/* ABI version, (major << 16) | minor. */
+int seacells_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEACELLS_FW_H */

@@ -1,0 +1,179 @@
+// Exported C ABI (include/seacells_fw.h): host-side validation, workspace
+// sizing and dispatch onto the caller's stream. Argument checks run before
+// any HIP call, so they also work on a machine without a GPU.
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/seacells_fw.h"
+#include "common.hpp"
+
+namespace seacells {
+
+static thread_local char g_last_error[256] = "";
+
+static int hip_fail(hipError_t e, const char *what) {
+  std::snprintf(g_last_error, sizeof g_last_error, "%s: %s", what, hipGetErrorString(e));
+  return SEACELLS_E_HIP;
+}
+
+hipError_t device_info(DeviceInfo *out) {
+  static DeviceInfo cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  if (!cache[dev].ok) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    cache[dev].cus = cus > 0 ? cus : 1;
+    cache[dev].ok = 1;
+  }
+  *out = cache[dev];
+  return hipSuccess;
+}
+
+// Per-call stamp for the B partials. Starts away from 0 so zero-filled or
+// leftover workspace never matches, and never takes the value 0.
+static uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0x5EAC0001u};
+  uint32_t e;
+  do {
+    e = counter.fetch_add(1u, std::memory_order_relaxed);
+  } while (e == 0u);
+  return e;
+}
+
+static int check_csr(const seacells_csr *m, uint32_t rows, uint32_t cols) {
+  if (m == nullptr || m->row_ptr == nullptr) return SEACELLS_E_NULL;
+  if (m->nnz > 0 && (m->col_idx == nullptr || m->val == nullptr)) return SEACELLS_E_NULL;
+  if (m->n_rows != rows || m->n_cols != cols) return SEACELLS_E_SHAPE;
+  if (m->nnz >= 0x80000000u) return SEACELLS_E_TOO_LARGE;
+  return SEACELLS_OK;
+}
+
+static Csr as_csr(const seacells_csr *m) {
+  Csr c;
+  c.ptr = m->row_ptr;
+  c.idx = m->col_idx;
+  c.val = m->val;
+  c.nnz = m->nnz;
+  return c;
+}
+
+}  // namespace seacells
+
+using namespace seacells;
+
+extern "C" {
+
+size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint32_t cap) {
+  if (n == 0 || k == 0 || cap == 0) return 0;
+  return plan_a(n, k, T, cap).ws_bytes;
+}
+
+int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
+                          const seacells_csr *a_prev_t, uint32_t n, uint32_t k, uint32_t T,
+                          uint32_t cap, const float *gamma, uint32_t *atom_idx, float *atom_val,
+                          uint32_t *atom_cnt, uint32_t *trace, void *workspace,
+                          size_t workspace_bytes, uint32_t *status, seacells_stream_t stream) {
+  if (t1 == nullptr || k2b == nullptr || a_prev_t == nullptr || atom_idx == nullptr ||
+      atom_val == nullptr || atom_cnt == nullptr || status == nullptr)
+    return SEACELLS_E_NULL;
+  if (n == 0 || k == 0 || T == 0 || cap == 0) return SEACELLS_E_SHAPE;
+  if (n >= 0x80000000u || k >= 0x80000000u) return SEACELLS_E_TOO_LARGE;
+  int rc;
+  if ((rc = check_csr(t1, k, k)) != SEACELLS_OK) return rc;
+  if ((rc = check_csr(k2b, n, k)) != SEACELLS_OK) return rc;
+  if ((rc = check_csr(a_prev_t, n, k)) != SEACELLS_OK) return rc;
+  if ((uint64_t)n * cap >= (1ull << 40) || (uint64_t)n * T >= (1ull << 40))
+    return SEACELLS_E_TOO_LARGE;
+  // per-wave LDS must at least hold the atom list
+  if ((uint64_t)cap * 8 > kLdsBytesPerCU) return SEACELLS_E_TOO_LARGE;
+  const APlan plan = plan_a(n, k, T, cap);
+  if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))
+    return SEACELLS_E_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_fw_a(plan, as_csr(t1), as_csr(k2b), as_csr(a_prev_t), n, k, T, cap, gamma, atom_idx,
+                  atom_val, atom_cnt, trace, workspace, status, s);
+  if (e != hipSuccess) return hip_fail(e, "fw_a_columns launch");
+  return SEACELLS_OK;
+}
+
+size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k) {
+  if (n == 0 || k == 0) return 0;
+  return plan_b(n, k).ws_bytes;
+}
+
+int seacells_fw_b_argmin(const seacells_csr *k2b, const seacells_csr *aat,
+                         const seacells_csr *k2at, const seacells_csr *b, uint32_t n, uint32_t k,
+                         float *out_val, uint32_t *out_idx, float *gap, void *workspace,
+                         size_t workspace_bytes, uint32_t *status, seacells_stream_t stream) {
+  if (k2b == nullptr || aat == nullptr || k2at == nullptr || out_val == nullptr ||
+      out_idx == nullptr || status == nullptr)
+    return SEACELLS_E_NULL;
+  if (n == 0 || k == 0) return SEACELLS_E_SHAPE;
+  if (n >= 0x80000000u || k >= 0x80000000u) return SEACELLS_E_TOO_LARGE;
+  int rc;
+  if ((rc = check_csr(k2b, n, k)) != SEACELLS_OK) return rc;
+  if ((rc = check_csr(aat, k, k)) != SEACELLS_OK) return rc;
+  if ((rc = check_csr(k2at, n, k)) != SEACELLS_OK) return rc;
+  if (b != nullptr && (rc = check_csr(b, n, k)) != SEACELLS_OK) return rc;
+  const BPlan plan = plan_b(n, k);
+  if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return SEACELLS_E_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SEACELLS_E_WORKSPACE;
+  Csr bc{};
+  if (b != nullptr) bc = as_csr(b);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_fw_b(plan, as_csr(k2b), as_csr(aat), as_csr(k2at), bc, n, k, out_val, out_idx, gap,
+                  workspace, status, next_epoch(), s);
+  if (e != hipSuccess) return hip_fail(e, "fw_b_argmin launch");
+  return SEACELLS_OK;
+}
+
+int seacells_fw_b_apply(uint32_t *bt_idx, float *bt_val, uint32_t *bt_cnt, uint32_t n,
+                        uint32_t k, uint32_t cap_b, const uint32_t *arg_idx, float gamma,
+                        uint32_t *status, seacells_stream_t stream) {
+  if (bt_idx == nullptr || bt_val == nullptr || bt_cnt == nullptr || arg_idx == nullptr ||
+      status == nullptr)
+    return SEACELLS_E_NULL;
+  if (n == 0 || k == 0 || cap_b == 0) return SEACELLS_E_SHAPE;
+  if (!(gamma > 0.0f && gamma <= 1.0f)) return SEACELLS_E_SHAPE;
+  if ((uint64_t)k * cap_b >= (1ull << 40)) return SEACELLS_E_TOO_LARGE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_fw_b_apply(bt_idx, bt_val, bt_cnt, n, k, cap_b, arg_idx, gamma, status, s);
+  if (e != hipSuccess) return hip_fail(e, "fw_b_apply launch");
+  return SEACELLS_OK;
+}
+
+const char *seacells_status_string(int code) {
+  switch (code) {
+    case SEACELLS_OK:
+      return "ok";
+    case SEACELLS_E_NULL:
+      return "a required pointer is NULL";
+    case SEACELLS_E_SHAPE:
+      return "a size is 0, an argument is out of range, or operand shapes disagree";
+    case SEACELLS_E_WORKSPACE:
+      return "workspace missing, misaligned or smaller than required";
+    case SEACELLS_E_TOO_LARGE:
+      return "an operand exceeds the 32-bit index range";
+    case SEACELLS_E_HIP:
+      return "a HIP launch or query failed";
+    default:
+      return "unknown status";
+  }
+}
+
+const char *seacells_last_error(void) { return g_last_error; }
+
+int seacells_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

@@ -1,0 +1,151 @@
+// Shared device helpers and internal host interface of the SEACells FW
+// library (gfx950, wave64). Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace seacells {
+
+constexpr uint32_t kWave = 64;
+constexpr uint32_t kLdsBytesPerCU = 160u * 1024u;  // gfx950 local data share
+
+// Device-side flags, same values as SEACELLS_FLAG_* in the public header.
+constexpr uint32_t kFlagCapOverflow = 0x1u;
+constexpr uint32_t kFlagPartialsInvalid = 0x2u;
+constexpr uint32_t kFlagBCapOverflow = 0x4u;
+constexpr uint32_t kFlagBadIndex = 0x8u;
+constexpr uint32_t kFlagNonfinite = 0x10u;
+constexpr uint32_t kFlagBadGamma = 0x20u;
+
+// A CSR as the kernels see it (device pointers).
+struct Csr {
+  const uint32_t *__restrict__ ptr;
+  const uint32_t *__restrict__ idx;
+  const float *__restrict__ val;
+  uint32_t nnz;  // entries stored; row ranges past it are treated as malformed
+};
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Monotone map of an f32 onto u32 (total order of the finite values and
+// +-inf). -0 is folded onto +0 first, so IEEE-equal values get equal keys
+// and a (key, index) minimum breaks a tie on the index alone.
+__device__ __forceinline__ uint32_t f32_order(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float f32_unorder(uint32_t o) {
+  const uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(u);
+}
+
+// Minimum of a u32 over the 64 lanes of the wave, returned in an SGPR.
+// Butterfly: quad_perm swaps (xor 1, xor 2), half-row and row mirrors
+// (within 8 and 16 lanes), then the gfx950 permlane16/32 swaps across rows.
+// DPP sources take 0xffffffff (the identity of min) where a lane has no
+// partner, so the min folds into one v_min_u32_dpp per step.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0xB1, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0x4E, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0x141, 0xF, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0x140, 0xF, 0xF, false));
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = min(x, min((uint32_t)r[0], (uint32_t)r[1]));
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    x = min(x, min((uint32_t)r[0], (uint32_t)r[1]));
+  }
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// (lowest value, then lowest index) over the wave. Lanes with nothing to
+// offer pass (+inf key, 0xffffffff).
+__device__ __forceinline__ uint32_t wave_argmin(float v, uint32_t i) {
+  const uint32_t key = f32_order(v);
+  const uint32_t best = wave_min_u32(key);
+  return wave_min_u32(key == best ? i : 0xffffffffu);
+}
+
+// Sum of an f32 over the wave in a fixed butterfly order (deterministic).
+__device__ __forceinline__ float wave_sum_f32(float x) {
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+// Ordering point between LDS accesses of different lanes of one wave. The
+// LDS executes one wavefront's operations in issue order, so only the
+// compiler has to be kept from moving accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float readlane_f32(float x, uint32_t lane) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(x), lane));
+}
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t x, uint32_t lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
+
+// ---------------------------------------------------------------------------
+// internal host interface (implemented in fw_a.hip / fw_b.hip)
+// ---------------------------------------------------------------------------
+
+struct DeviceInfo {
+  int cus = 0;
+  int ok = 0;
+};
+hipError_t device_info(DeviceInfo *out);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// --- A update -------------------------------------------------------------
+struct APlan {
+  uint32_t kpad;          // k rounded up to 4 (padding holds +inf)
+  uint32_t waves_per_block;
+  uint32_t lds_per_wave;  // bytes
+  bool h_in_lds;
+  uint32_t global_waves;  // waves that own a workspace slice (h in workspace)
+  size_t ws_bytes;
+};
+APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap);
+hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, uint32_t k,
+                       uint32_t T, uint32_t cap, const float *gamma, uint32_t *atom_idx,
+                       float *atom_val, uint32_t *atom_cnt, uint32_t *trace, void *ws,
+                       uint32_t *status, hipStream_t stream);
+
+// --- B argmin -------------------------------------------------------------
+struct BPlan {
+  uint32_t s4;            // float4 column chunks per lane in one slice
+  uint32_t slice_w;       // columns per slice = 256 * s4
+  uint32_t n_slices;
+  uint32_t n_row_blocks;  // row ranges; one work unit = (row range, slice)
+  uint32_t n_chunks;      // row-range groups of the first reduce stage
+  size_t off_keys, off_part2, off_gap, off_stamp, off_seg, ws_bytes;
+};
+BPlan plan_b(uint32_t n, uint32_t k);
+hipError_t launch_fw_b(const BPlan &plan, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
+                       uint32_t k, float *out_val, uint32_t *out_idx, float *gap, void *ws,
+                       uint32_t *status, uint32_t epoch, hipStream_t stream);
+hipError_t launch_fw_b_apply(uint32_t *bt_idx, float *bt_val, uint32_t *bt_cnt, uint32_t n,
+                             uint32_t k, uint32_t cap_b, const uint32_t *arg_idx, float gamma,
+                             uint32_t *status, hipStream_t stream);
+hipError_t launch_status_clear(uint32_t *status, hipStream_t stream);
+
+}  // namespace seacells

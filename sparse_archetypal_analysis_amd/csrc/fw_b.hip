@@ -1,0 +1,436 @@
+// B-gradient argmin and B step (`fw_argmin_b` and `reduce_argmin_blocks` on
+// the source page bixverse-rs 0.6.4, seacells_kernels.rs).
+//
+//   G[i, c] = sum_m K2B[i, m] AAt[m, c] - K2At[i, c]        (never stored)
+//   out[c]  = (min_i G[i, c], lowest i attaining it),  gap = sum B * G
+//
+// Work unit = (row range, column slice). A wave owns one unit at a time:
+// per row it scatters the AAt rows named by the row's K2B entries into a
+// dense slice accumulator in LDS (coalesced lane-strided reads of each AAt
+// row segment; the columns of one row are unique, so one scatter
+// instruction never collides), subtracts the K2At row, adds the row's
+// B . G term, then folds the slice into running (min, row) pairs held in
+// registers, 4 consecutive columns per float4 chunk, and clears the slice.
+// Rows run in ascending order under a strict `<`, so the lowest row wins a
+// tie inside a unit. The unit writes one (order-preserving f32 key << 32 |
+// row) per column, which makes "lower value, then lower row" a plain u64
+// minimum for the reduce stages, and a stamp with the call's epoch.
+//
+// Slices exist so k has no ceiling: a slice holds at most 2048 columns (8
+// KB of LDS and 64 registers per lane), and a segment table
+// seg[m, s] = first position of AAt row m with column >= s * slice_w
+// hands each slice its run of every AAt row without a search.
+//
+// The reduce is two kernels: stage 1 takes u64 minima over groups of row
+// ranges (coalesced over columns) and checks every stamp it consumes;
+// stage 2 finishes each column, checks that the winning row is below n,
+// and sums the gap partials in a fixed order.
+#include "common.hpp"
+
+namespace seacells {
+namespace {
+
+constexpr uint32_t kBThreads = 256;
+constexpr uint32_t kBUnitsTarget = 8192;
+constexpr uint32_t kBMaxS4 = 8;
+constexpr uint32_t kReduceCols = 64;  // columns per stage-1 block (one per lane)
+constexpr uint32_t kMaxChunks = 64;
+
+__device__ __forceinline__ uint64_t pack_key(float v, uint32_t row) {
+  return ((uint64_t)f32_order(v) << 32) | (uint64_t)row;
+}
+
+__device__ __forceinline__ bool row_ok(const Csr &m, uint32_t r, uint32_t &lo, uint32_t &hi) {
+  lo = m.ptr[r];
+  hi = m.ptr[r + 1];
+  if (hi > m.nnz || lo > hi) {
+    lo = hi = 0;
+    return false;
+  }
+  return true;
+}
+
+__global__ void __launch_bounds__(256)
+    seg_table_kernel(Csr aat, uint32_t k, uint32_t slice_w, uint32_t n_slices,
+                     uint32_t *__restrict__ seg) {
+  const uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t per_row = (uint64_t)n_slices + 1;
+  if (e >= (uint64_t)k * per_row) return;
+  const uint32_t m = (uint32_t)(e / per_row);
+  const uint32_t s = (uint32_t)(e - (uint64_t)m * per_row);
+  uint32_t lo, hi;
+  row_ok(aat, m, lo, hi);
+  if (s == n_slices) {
+    seg[e] = hi;
+    return;
+  }
+  const uint32_t target = s * slice_w;
+  while (lo < hi) {  // first position with column >= target
+    const uint32_t mid = lo + (hi - lo) / 2;
+    if (aat.idx[mid] < target)
+      lo = mid + 1;
+    else
+      hi = mid;
+  }
+  seg[e] = lo;
+}
+
+template <uint32_t S4>
+__global__ void __launch_bounds__(kBThreads)
+    fw_b_partials_kernel(Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n, uint32_t k,
+                         uint32_t n_slices, uint32_t n_row_blocks,
+                         const uint32_t *__restrict__ seg, uint64_t *__restrict__ part_key,
+                         float *__restrict__ part_gap, uint32_t *__restrict__ stamps,
+                         uint32_t epoch, uint32_t *__restrict__ status) {
+  constexpr uint32_t W = 256 * S4;
+  constexpr uint32_t NC = 4 * S4;  // columns per lane
+  extern __shared__ float lds_acc[];
+  const uint32_t lane = lane_id();
+  const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const uint32_t wpb = blockDim.x / kWave;
+  const uint32_t gwave = blockIdx.x * wpb + wib;
+  const uint32_t nwaves = gridDim.x * wpb;
+  float *acc = lds_acc + (size_t)wib * W;
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float inf = __builtin_inff();
+  uint32_t flags = 0;
+
+#pragma unroll
+  for (uint32_t s4 = 0; s4 < S4; ++s4)
+    *reinterpret_cast<float4 *>(acc + s4 * 256 + lane * 4) = zero4;
+  wave_lds_sync();
+
+  const uint32_t n_units = n_row_blocks * n_slices;
+  for (uint32_t unit = gwave; unit < n_units; unit += nwaves) {
+    const uint32_t rb = unit / n_slices;
+    const uint32_t sl = unit - rb * n_slices;
+    const uint32_t c0 = sl * W;
+    const uint32_t cw = (k - c0) < W ? (k - c0) : W;
+    const uint32_t r0 = (uint32_t)(((uint64_t)n * rb) / n_row_blocks);
+    const uint32_t r1 = (uint32_t)(((uint64_t)n * (rb + 1)) / n_row_blocks);
+
+    float bv[NC];
+    uint32_t bi[NC];
+#pragma unroll
+    for (uint32_t j = 0; j < NC; ++j) bv[j] = inf, bi[j] = 0xffffffffu;
+    float gsum = 0.0f;
+
+    for (uint32_t i = r0; i < r1; ++i) {
+      // -- acc[c] = sum_m K2B[i, m] AAt[m, c] over this slice
+      uint32_t e0, e1;
+      if (!row_ok(k2b, i, e0, e1)) flags |= kFlagBadIndex;
+      for (uint32_t eb = e0; eb < e1; eb += kWave) {
+        const uint32_t e = eb + lane;
+        uint32_t lo = 0, hi = 0;
+        float x = 0.0f;
+        if (e < e1) {
+          const uint32_t m = k2b.idx[e];
+          x = k2b.val[e];
+          if (m < k) {
+            if (seg != nullptr) {
+              const size_t sb = (size_t)m * (n_slices + 1) + sl;
+              lo = seg[sb];
+              hi = seg[sb + 1];
+            } else if (!row_ok(aat, m, lo, hi)) {
+              flags |= kFlagBadIndex;
+            }
+          } else {
+            flags |= kFlagBadIndex;
+          }
+        }
+        const uint32_t cnt = (e1 - eb) < kWave ? (e1 - eb) : kWave;
+        for (uint32_t u = 0; u < cnt; ++u) {
+          const uint32_t plo = readlane_u32(lo, u);
+          const uint32_t phi = readlane_u32(hi, u);
+          const float xs = readlane_f32(x, u);
+          for (uint32_t p = plo + lane; p < phi; p += kWave) {
+            const uint32_t c = aat.idx[p] - c0;
+            if (c < cw) acc[c] += xs * aat.val[p];
+          }
+          wave_lds_sync();
+        }
+      }
+      // -- acc[c] -= K2At[i, c]
+      uint32_t q0, q1;
+      if (!row_ok(k2at, i, q0, q1)) flags |= kFlagBadIndex;
+      for (uint32_t q = q0 + lane; q < q1; q += kWave) {
+        const uint32_t c = k2at.idx[q] - c0;
+        if (c < cw) acc[c] -= k2at.val[q];
+      }
+      wave_lds_sync();
+      // -- gap += sum_c B[i, c] G[i, c]
+      if (b.ptr != nullptr) {
+        uint32_t g0, g1;
+        if (!row_ok(b, i, g0, g1)) flags |= kFlagBadIndex;
+        for (uint32_t q = g0 + lane; q < g1; q += kWave) {
+          const uint32_t c = b.idx[q] - c0;
+          if (c < cw) gsum += b.val[q] * acc[c];
+        }
+      }
+      // -- running minimum per column (strict `<`: lowest row wins), clear
+#pragma unroll
+      for (uint32_t s4 = 0; s4 < S4; ++s4) {
+        const uint32_t cb = s4 * 256 + lane * 4;
+        float4 *slot = reinterpret_cast<float4 *>(acc + cb);
+        const float4 v = *slot;
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (uint32_t j = 0; j < 4; ++j) {
+          if (cb + j < cw && vv[j] < bv[4 * s4 + j]) {
+            bv[4 * s4 + j] = vv[j];
+            bi[4 * s4 + j] = i;
+          }
+        }
+        *slot = zero4;
+      }
+      wave_lds_sync();
+    }
+
+    // -- this unit's partials
+    uint64_t *out = part_key + (size_t)rb * k + c0;
+#pragma unroll
+    for (uint32_t s4 = 0; s4 < S4; ++s4) {
+      const uint32_t cb = s4 * 256 + lane * 4;
+#pragma unroll
+      for (uint32_t j = 0; j < 4; ++j)
+        if (cb + j < cw) out[cb + j] = pack_key(bv[4 * s4 + j], bi[4 * s4 + j]);
+    }
+    const float g = wave_sum_f32(gsum);
+    if (lane == 0) {
+      part_gap[unit] = g;
+      stamps[unit] = epoch;
+    }
+  }
+  flags = __builtin_amdgcn_readfirstlane(flags);
+  if (flags != 0 && lane == 0) atomicOr(status, flags);
+}
+
+// Stage 1: block (column group x, row-range chunk y); 4 waves x 64 lanes.
+// Lane l of every wave owns column x * 64 + l; wave w takes row ranges
+// rb = chunk_lo + w, + 4, ... . Keys are u64 minima, so the order in which
+// row ranges are combined does not matter.
+__global__ void __launch_bounds__(256)
+    fw_b_reduce1_kernel(const uint64_t *__restrict__ part_key, const uint32_t *__restrict__ stamps,
+                        uint32_t n_row_blocks, uint32_t n_slices, uint32_t slice_w,
+                        uint32_t n_chunks, uint32_t k, uint32_t epoch,
+                        uint64_t *__restrict__ part2, uint32_t *__restrict__ status) {
+  __shared__ uint64_t red[4][kReduceCols];
+  const uint32_t lane = lane_id();
+  const uint32_t w = threadIdx.x / kWave;
+  const uint32_t c = blockIdx.x * kReduceCols + lane;
+  const uint32_t ch = blockIdx.y;
+  const uint32_t lo = (uint32_t)(((uint64_t)n_row_blocks * ch) / n_chunks);
+  const uint32_t hi = (uint32_t)(((uint64_t)n_row_blocks * (ch + 1)) / n_chunks);
+  uint64_t best = ~0ull;
+  uint32_t flags = 0;
+  if (c < k) {
+    const uint32_t sl = c / slice_w;
+    for (uint32_t rb = lo + w; rb < hi; rb += 4) {
+      const uint64_t key = part_key[(size_t)rb * k + c];
+      best = key < best ? key : best;
+      if (stamps[(size_t)rb * n_slices + sl] != epoch) flags |= kFlagPartialsInvalid;
+    }
+  }
+  red[w][lane] = best;
+  __syncthreads();
+  if (w == 0 && c < k) {
+    uint64_t m = red[0][lane];
+    for (uint32_t x = 1; x < 4; ++x) m = red[x][lane] < m ? red[x][lane] : m;
+    part2[(size_t)ch * k + c] = m;
+  }
+  if (flags != 0) atomicOr(status, flags);
+}
+
+// Stage 2: one thread per column over the chunk minima; the last block
+// sums the gap partials (f64, fixed order).
+__global__ void __launch_bounds__(256)
+    fw_b_reduce2_kernel(const uint64_t *__restrict__ part2, uint32_t n_chunks,
+                        const float *__restrict__ part_gap, uint32_t n_units, uint32_t n,
+                        uint32_t k, float *__restrict__ out_val, uint32_t *__restrict__ out_idx,
+                        float *__restrict__ gap, uint32_t *__restrict__ status) {
+  const uint32_t col_blocks = (k + 255) / 256;
+  if (blockIdx.x < col_blocks) {
+    const uint32_t c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= k) return;
+    uint64_t best = ~0ull;
+    for (uint32_t ch = 0; ch < n_chunks; ++ch) {
+      const uint64_t key = part2[(size_t)ch * k + c];
+      best = key < best ? key : best;
+    }
+    const uint32_t row = (uint32_t)best;
+    const float v = f32_unorder((uint32_t)(best >> 32));
+    uint32_t flags = 0;
+    if (row >= n) flags |= kFlagPartialsInvalid;
+    if (!__builtin_isfinite(v)) flags |= kFlagNonfinite;
+    out_val[c] = v;
+    out_idx[c] = row;
+    if (flags != 0) atomicOr(status, flags);
+  } else {
+    __shared__ double red[256];
+    double s = 0.0;
+    for (uint32_t u = threadIdx.x; u < n_units; u += 256) s += (double)part_gap[u];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (uint32_t w = 128; w > 0; w >>= 1) {
+      if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0 && gap != nullptr) *gap = (float)red[0];
+  }
+}
+
+// B step on padded B^T rows, one thread per archetype.
+__global__ void __launch_bounds__(256)
+    fw_b_apply_kernel(uint32_t *__restrict__ bt_idx, float *__restrict__ bt_val,
+                      uint32_t *__restrict__ bt_cnt, uint32_t n, uint32_t k, uint32_t cap_b,
+                      const uint32_t *__restrict__ arg_idx, float gamma,
+                      uint32_t *__restrict__ status) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= k) return;
+  uint32_t *idx = bt_idx + (size_t)c * cap_b;
+  float *val = bt_val + (size_t)c * cap_b;
+  const uint32_t cnt = bt_cnt[c];
+  const uint32_t i = arg_idx[c];
+  if (cnt > cap_b || i >= n) {
+    atomicOr(status, kFlagBadIndex);
+    return;
+  }
+  uint32_t pos = 0;
+  while (pos < cnt && idx[pos] < i) ++pos;
+  const bool present = pos < cnt && idx[pos] == i;
+  if (!present && cnt == cap_b) {
+    atomicOr(status, kFlagBCapOverflow);
+    return;
+  }
+  const float keep = 1.0f - gamma;
+  for (uint32_t s = 0; s < cnt; ++s) val[s] *= keep;
+  if (present) {
+    val[pos] += gamma;
+  } else {
+    for (uint32_t s = cnt; s > pos; --s) {
+      idx[s] = idx[s - 1];
+      val[s] = val[s - 1];
+    }
+    idx[pos] = i;
+    val[pos] = gamma;
+    bt_cnt[c] = cnt + 1;
+  }
+}
+
+__global__ void status_clear_kernel(uint32_t *__restrict__ status) { *status = 0u; }
+
+template <uint32_t S4>
+hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
+                           uint32_t k, const uint32_t *seg, uint64_t *keys, float *gap_part,
+                           uint32_t *stamps, uint32_t epoch, uint32_t *status,
+                           hipStream_t stream) {
+  DeviceInfo dev;
+  hipError_t e = device_info(&dev);
+  if (e != hipSuccess) return e;
+  const uint32_t lds = (kBThreads / kWave) * 256 * S4 * sizeof(float);
+  static int bpc = -1;
+  if (bpc < 0) {
+    int v = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &v, reinterpret_cast<const void *>(&fw_b_partials_kernel<S4>), kBThreads, lds);
+    if (e != hipSuccess) return e;
+    bpc = v < 1 ? 1 : v;
+  }
+  const uint64_t units = (uint64_t)p.n_row_blocks * p.n_slices;
+  const uint64_t want = (units + 3) / 4;
+  const uint64_t resident = (uint64_t)dev.cus * (uint64_t)bpc;
+  const uint32_t blocks = (uint32_t)(want < resident ? want : resident);
+  hipLaunchKernelGGL(fw_b_partials_kernel<S4>, dim3(blocks), dim3(kBThreads), lds, stream, k2b,
+                     aat, k2at, b, n, k, p.n_slices, p.n_row_blocks, seg, keys, gap_part, stamps,
+                     epoch, status);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+BPlan plan_b(uint32_t n, uint32_t k) {
+  BPlan p{};
+  const uint32_t chunks = (k + 255u) / 256u;
+  p.s4 = chunks < kBMaxS4 ? (chunks < 1 ? 1 : chunks) : kBMaxS4;
+  p.slice_w = 256u * p.s4;
+  p.n_slices = (k + p.slice_w - 1) / p.slice_w;
+  uint32_t rb = kBUnitsTarget / p.n_slices;
+  if (rb < 1) rb = 1;
+  if (rb > n) rb = n;
+  p.n_row_blocks = rb;
+  p.n_chunks = rb < kMaxChunks ? rb : kMaxChunks;
+  const size_t units = (size_t)p.n_row_blocks * p.n_slices;
+  size_t off = 0;
+  p.off_keys = off;
+  off = align_up(off + (size_t)p.n_row_blocks * k * sizeof(uint64_t), 256);
+  p.off_part2 = off;
+  off = align_up(off + (size_t)p.n_chunks * k * sizeof(uint64_t), 256);
+  p.off_gap = off;
+  off = align_up(off + units * sizeof(float), 256);
+  p.off_stamp = off;
+  off = align_up(off + units * sizeof(uint32_t), 256);
+  p.off_seg = off;
+  if (p.n_slices > 1) off = align_up(off + (size_t)k * (p.n_slices + 1) * sizeof(uint32_t), 256);
+  p.ws_bytes = off;
+  return p;
+}
+
+hipError_t launch_status_clear(uint32_t *status, hipStream_t stream) {
+  hipLaunchKernelGGL(status_clear_kernel, dim3(1), dim3(1), 0, stream, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
+                       uint32_t k, float *out_val, uint32_t *out_idx, float *gap, void *ws,
+                       uint32_t *status, uint32_t epoch, hipStream_t stream) {
+  char *base = static_cast<char *>(ws);
+  uint64_t *keys = reinterpret_cast<uint64_t *>(base + p.off_keys);
+  uint64_t *part2 = reinterpret_cast<uint64_t *>(base + p.off_part2);
+  float *gap_part = reinterpret_cast<float *>(base + p.off_gap);
+  uint32_t *stamps = reinterpret_cast<uint32_t *>(base + p.off_stamp);
+  uint32_t *seg = p.n_slices > 1 ? reinterpret_cast<uint32_t *>(base + p.off_seg) : nullptr;
+  hipError_t e;
+  if (seg != nullptr) {
+    const uint64_t total = (uint64_t)k * (p.n_slices + 1);
+    hipLaunchKernelGGL(seg_table_kernel, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0,
+                       stream, aat, k, p.slice_w, p.n_slices, seg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  switch (p.s4) {
+#define SEACELLS_B_CASE(S)                                                                      \
+  case S:                                                                                       \
+    e = launch_partials<S>(p, k2b, aat, k2at, b, n, k, seg, keys, gap_part, stamps, epoch,      \
+                           status, stream);                                                     \
+    break;
+    SEACELLS_B_CASE(1)
+    SEACELLS_B_CASE(2)
+    SEACELLS_B_CASE(3)
+    SEACELLS_B_CASE(4)
+    SEACELLS_B_CASE(5)
+    SEACELLS_B_CASE(6)
+    SEACELLS_B_CASE(7)
+    SEACELLS_B_CASE(8)
+#undef SEACELLS_B_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const dim3 g1((k + kReduceCols - 1) / kReduceCols, p.n_chunks);
+  hipLaunchKernelGGL(fw_b_reduce1_kernel, g1, dim3(256), 0, stream, keys, stamps, p.n_row_blocks,
+                     p.n_slices, p.slice_w, p.n_chunks, k, epoch, part2, status);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const uint32_t units = p.n_row_blocks * p.n_slices;
+  hipLaunchKernelGGL(fw_b_reduce2_kernel, dim3((k + 255) / 256 + 1), dim3(256), 0, stream, part2,
+                     p.n_chunks, gap_part, units, n, k, out_val, out_idx, gap, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_fw_b_apply(uint32_t *bt_idx, float *bt_val, uint32_t *bt_cnt, uint32_t n,
+                             uint32_t k, uint32_t cap_b, const uint32_t *arg_idx, float gamma,
+                             uint32_t *status, hipStream_t stream) {
+  hipLaunchKernelGGL(fw_b_apply_kernel, dim3((k + 255) / 256), dim3(256), 0, stream, bt_idx,
+                     bt_val, bt_cnt, n, k, cap_b, arg_idx, gamma, status);
+  return hipGetLastError();
+}
+
+}  // namespace seacells

@@ -1,0 +1,236 @@
+"""Thin ctypes binding of ``libseacells_fw.so`` (include/seacells_fw.h).
+
+The functions carry the C names and only marshal arguments: device tensors
+become raw pointers, torch's current stream becomes the hipStream_t. Every
+step of the computation runs in the library's HIP kernels; there is no CPU
+fallback, and a missing library is an error.
+
+PyTorch provides device memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+from . import _build
+
+SEACELLS_OK = 0
+ERRORS = {-1: "E_NULL", -2: "E_SHAPE", -3: "E_WORKSPACE", -4: "E_TOO_LARGE", -5: "E_HIP"}
+FLAGS = {0x1: "CAP_OVERFLOW", 0x2: "PARTIALS_INVALID", 0x4: "B_CAP_OVERFLOW", 0x8: "BAD_INDEX",
+         0x10: "NONFINITE", 0x20: "BAD_GAMMA"}
+
+EXPORTS = ("seacells_fw_a_columns_workspace", "seacells_fw_a_columns",
+           "seacells_fw_b_argmin_workspace", "seacells_fw_b_argmin", "seacells_fw_b_apply",
+           "seacells_status_string", "seacells_last_error", "seacells_version")
+
+
+class seacells_csr(ctypes.Structure):
+    _fields_ = [("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+                ("val", ctypes.c_void_p), ("n_rows", ctypes.c_uint32),
+                ("n_cols", ctypes.c_uint32), ("nnz", ctypes.c_uint32)]
+
+
+_CSR_P = ctypes.POINTER(seacells_csr)
+_VP = ctypes.c_void_p
+_U32 = ctypes.c_uint32
+_lib = None
+
+
+class SeacellsError(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def load():
+    """The loaded library. Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _build.LIB
+    if not os.path.exists(path):
+        raise SeacellsError("libseacells_fw.so is not built; run __graft_entry__.build() "
+                            "(or python -m sparse_archetypal_analysis_amd._build)")
+    lib = ctypes.CDLL(path)
+    lib.seacells_fw_a_columns_workspace.restype = ctypes.c_size_t
+    lib.seacells_fw_a_columns_workspace.argtypes = [_U32, _U32, _U32, _U32]
+    lib.seacells_fw_a_columns.restype = ctypes.c_int
+    lib.seacells_fw_a_columns.argtypes = [_CSR_P, _CSR_P, _CSR_P, _U32, _U32, _U32, _U32, _VP, _VP,
+                                          _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP]
+    lib.seacells_fw_b_argmin_workspace.restype = ctypes.c_size_t
+    lib.seacells_fw_b_argmin_workspace.argtypes = [_U32, _U32]
+    lib.seacells_fw_b_argmin.restype = ctypes.c_int
+    lib.seacells_fw_b_argmin.argtypes = [_CSR_P, _CSR_P, _CSR_P, _CSR_P, _U32, _U32, _VP, _VP, _VP,
+                                         _VP, ctypes.c_size_t, _VP, _VP]
+    lib.seacells_fw_b_apply.restype = ctypes.c_int
+    lib.seacells_fw_b_apply.argtypes = [_VP, _VP, _VP, _U32, _U32, _U32, _VP, ctypes.c_float,
+                                        _VP, _VP]
+    lib.seacells_status_string.restype = ctypes.c_char_p
+    lib.seacells_status_string.argtypes = [ctypes.c_int]
+    lib.seacells_last_error.restype = ctypes.c_char_p
+    lib.seacells_last_error.argtypes = []
+    lib.seacells_version.restype = ctypes.c_int
+    lib.seacells_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check_rc(rc: int):
+    if rc != SEACELLS_OK:
+        lib = load()
+        msg = lib.seacells_status_string(rc).decode()
+        if rc == -5:
+            msg += ": " + lib.seacells_last_error().decode()
+        raise SeacellsError("%s (%d): %s" % (ERRORS.get(rc, "?"), rc, msg))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class DeviceCSR:
+    """A CSR operand held in device memory as int32 / float32 tensors.
+
+    The C side reads the int32 index tensors as u32; values must stay below
+    2^31 (checked when built from the host).
+    """
+
+    def __init__(self, row_ptr: torch.Tensor, col_idx: torch.Tensor, val: torch.Tensor, shape):
+        for t, dt in ((row_ptr, torch.int32), (col_idx, torch.int32), (val, torch.float32)):
+            if t.dtype != dt or not t.is_contiguous() or t.device.type != "cuda":
+                raise SeacellsError("CSR arrays must be contiguous cuda int32/int32/float32")
+        if row_ptr.numel() != shape[0] + 1 or col_idx.numel() != val.numel():
+            raise SeacellsError("CSR array lengths do not match the shape")
+        self.row_ptr, self.col_idx, self.val = row_ptr, col_idx, val
+        self.shape = (int(shape[0]), int(shape[1]))
+        self.nnz = int(val.numel())
+
+    @classmethod
+    def from_scipy(cls, m, device="cuda"):
+        ptr = np.asarray(m.indptr)
+        if ptr[-1] >= 2 ** 31:
+            raise SeacellsError("operand has 2^31 or more non-zeros")
+        return cls(torch.from_numpy(ptr.astype(np.int32)).to(device),
+                   torch.from_numpy(np.asarray(m.indices).astype(np.int32)).to(device),
+                   torch.from_numpy(np.asarray(m.data).astype(np.float32)).to(device),
+                   m.shape)
+
+    def struct(self) -> seacells_csr:
+        return seacells_csr(self.row_ptr.data_ptr(),
+                            self.col_idx.data_ptr() if self.nnz else None,
+                            self.val.data_ptr() if self.nnz else None,
+                            self.shape[0], self.shape[1], self.nnz)
+
+
+def new_status(device="cuda") -> torch.Tensor:
+    return torch.zeros(1, dtype=torch.int32, device=device)
+
+
+def status_flags(status: torch.Tensor) -> list:
+    """Names of the flags set in a status word (synchronises)."""
+    v = int(status.item()) & 0xffffffff
+    return [nm for bit, nm in FLAGS.items() if v & bit]
+
+
+def raise_on_status(status: torch.Tensor):
+    names = status_flags(status)
+    if names:
+        raise SeacellsError("device status: " + ", ".join(names))
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def seacells_fw_a_columns_workspace(n, k, T, cap) -> int:
+    return int(load().seacells_fw_a_columns_workspace(n, k, T, cap))
+
+
+def seacells_fw_a_columns(t1: DeviceCSR, k2b: DeviceCSR, a_prev_t: DeviceCSR, n: int, k: int,
+                          T: int, cap: int, gamma=None, atom_idx=None, atom_val=None,
+                          atom_cnt=None, trace=None, workspace=None, status=None, stream=None):
+    """A update. Returns (atom_idx [n, cap], atom_val [n, cap], atom_cnt [n], trace, status).
+
+    Outputs and workspace are allocated when not given; pass ``trace=True``
+    to get the per-step argmin trace [n, T].
+    """
+    lib = load()
+    dev = t1.row_ptr.device
+    if atom_idx is None:
+        atom_idx = torch.empty((n, cap), dtype=torch.int32, device=dev)
+    if atom_val is None:
+        atom_val = torch.empty((n, cap), dtype=torch.float32, device=dev)
+    if atom_cnt is None:
+        atom_cnt = torch.empty(n, dtype=torch.int32, device=dev)
+    if trace is True:
+        trace = torch.empty((n, T), dtype=torch.int32, device=dev)
+    elif trace is False:
+        trace = None
+    if status is None:
+        status = new_status(dev)
+    ws_bytes = seacells_fw_a_columns_workspace(n, k, T, cap)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    s1, s2, s3 = t1.struct(), k2b.struct(), a_prev_t.struct()
+    rc = lib.seacells_fw_a_columns(ctypes.byref(s1), ctypes.byref(s2), ctypes.byref(s3), n, k, T,
+                                   cap, _ptr(gamma), _ptr(atom_idx), _ptr(atom_val),
+                                   _ptr(atom_cnt), _ptr(trace), _ptr(workspace),
+                                   0 if workspace is None else workspace.numel(), _ptr(status),
+                                   _stream(stream))
+    _check_rc(rc)
+    return atom_idx, atom_val, atom_cnt, trace, status
+
+
+def seacells_fw_b_argmin_workspace(n, k) -> int:
+    return int(load().seacells_fw_b_argmin_workspace(n, k))
+
+
+def seacells_fw_b_argmin(k2b: DeviceCSR, aat: DeviceCSR, k2at: DeviceCSR, b, n: int, k: int,
+                         out_val=None, out_idx=None, gap=None, workspace=None, status=None,
+                         stream=None):
+    """B-gradient argmin. Returns (out_val [k], out_idx [k], gap [1], status)."""
+    lib = load()
+    dev = k2b.row_ptr.device
+    if out_val is None:
+        out_val = torch.empty(k, dtype=torch.float32, device=dev)
+    if out_idx is None:
+        out_idx = torch.empty(k, dtype=torch.int32, device=dev)
+    if gap is None:
+        gap = torch.empty(1, dtype=torch.float32, device=dev)
+    if status is None:
+        status = new_status(dev)
+    ws_bytes = seacells_fw_b_argmin_workspace(n, k)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    s1, s2, s3 = k2b.struct(), aat.struct(), k2at.struct()
+    sb = b.struct() if b is not None else None
+    rc = lib.seacells_fw_b_argmin(ctypes.byref(s1), ctypes.byref(s2), ctypes.byref(s3),
+                                  ctypes.byref(sb) if sb is not None else None, n, k,
+                                  _ptr(out_val), _ptr(out_idx), _ptr(gap), _ptr(workspace),
+                                  workspace.numel(), _ptr(status), _stream(stream))
+    _check_rc(rc)
+    return out_val, out_idx, gap, status
+
+
+def seacells_fw_b_apply(bt_idx, bt_val, bt_cnt, n: int, arg_idx, gamma: float, status=None,
+                        stream=None):
+    """B step in place on padded B^T rows ([k, cap_b] int32 / float32, [k] int32)."""
+    lib = load()
+    k, cap_b = bt_idx.shape
+    if status is None:
+        status = new_status(bt_idx.device)
+    rc = lib.seacells_fw_b_apply(_ptr(bt_idx), _ptr(bt_val), _ptr(bt_cnt), n, k, cap_b,
+                                 _ptr(arg_idx), float(gamma), _ptr(status), _stream(stream))
+    _check_rc(rc)
+    return bt_idx, bt_val, bt_cnt, status

@@ -1,0 +1,40 @@
+"""Run the HIP entry points on host-side workloads (GPU test helper)."""
+import numpy as np
+import torch
+
+import sparse_archetypal_analysis_amd as saa
+
+
+def dev(m):
+    return saa.DeviceCSR.from_scipy(m)
+
+
+def run_a(w, T=None, cap=None, gamma=None, trace=True, ops=None):
+    T = w.T if T is None else T
+    cap = w.cap if cap is None else cap
+    g = None if gamma is None else torch.tensor(np.asarray(gamma, np.float32), device="cuda")
+    t1, k2b, ap = ops if ops is not None else (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
+    ai, av, ac, tr, st = saa.seacells_fw_a_columns(t1, k2b, ap, w.n, w.k, T, cap, gamma=g,
+                                                   trace=trace)
+    torch.cuda.synchronize()
+    return (ai.cpu().numpy(), av.cpu().numpy(), ac.cpu().numpy(),
+            tr.cpu().numpy() if tr is not None else None, saa.status_flags(st))
+
+
+def run_b(w, with_b=True, ops=None):
+    k2b, aat, k2at, b = ops if ops is not None else (dev(w.k2b), dev(w.aat), dev(w.k2at),
+                                                     dev(w.b) if with_b else None)
+    v, i, g, st = saa.seacells_fw_b_argmin(k2b, aat, k2at, b, w.n, w.k)
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), i.cpu().numpy(), float(g.cpu().numpy()[0]), saa.status_flags(st)
+
+
+def run_b_dense(k2b, t1, t2, b):
+    """B argmin on dense page-style fixtures (converted to CSR)."""
+    import workloads as W
+    n, k = k2b.shape
+    cfg = W.Config("fixture", n, 0, 0, 0, k, 0, 0)
+    w = W.Workload(cfg, 0, t1=W.dense_to_csr(t1), k2b=W.dense_to_csr(k2b),
+                   a_prev_t=W.dense_to_csr(np.zeros((n, k))), aat=W.dense_to_csr(t1),
+                   k2at=W.dense_to_csr(t2), b=W.dense_to_csr(b), init_cells=np.zeros(0, np.int64))
+    return w, run_b(w)

@@ -1,0 +1,146 @@
+"""Acceptance rules for GPU results against the f64 oracle (test helper).
+
+Argmin indices: the GPU's pick p at a step (or for a column) is accepted when
+it equals the oracle's, or when the oracle's f64 gradient at p lies within
+TIE_REL of the minimum, relative to max(|g_min|, |g_second|, S). S is the
+size of the terms the gradient is a difference of: in f32 the error of g
+scales with S, not with |g|, so a tie window relative to |g| alone would
+reject rounding-level disagreements at g ~ 0. Outside such near ties the
+index must match exactly.
+
+A values: the oracle replays the GPU's own trajectory (every step forced to
+the GPU's pick, after the pick is checked as above). Each entry of the GPU's
+A column must then be within A_ABS of the replayed f64 column.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+import oracle
+
+TIE_REL = 1e-5   # near-tie window, relative
+A_ABS = 1e-5     # A entries after T steps, absolute
+B_ABS = 1e-5     # B entries after the B step, absolute
+VAL_REL, VAL_ABS = 1e-4, 1e-5   # B minimum values (the page's policy)
+GAP_REL = 1e-3                  # sum(B * G) (the page's policy)
+
+
+def dense_atoms(atom_idx, atom_val, atom_cnt, k):
+    """Scatter GPU atom lists [m, cap] into dense [m, k] (f64)."""
+    m, cap = atom_idx.shape
+    out = np.zeros((m, k), np.float64)
+    for r in range(m):
+        c = int(atom_cnt[r])
+        assert 0 <= c <= cap
+        ids = atom_idx[r, :c].astype(np.int64)
+        assert np.all((ids >= 0) & (ids < k)), "atom index out of range"
+        assert np.unique(ids).shape[0] == c, "duplicate atom in a cell"
+        out[r, ids] = atom_val[r, :c]
+    return out
+
+
+@dataclass
+class AReport:
+    steps: int
+    exact: int
+    near_tie: int
+    zero_tie_mismatch: int
+    max_abs_err: float
+    worst_window: float
+
+
+def check_atom_layout(atom_idx, atom_cnt, trace, a_prev_t, cells):
+    """Seeds first in A_prev order, then each new pick in order of first pick."""
+    for r, j in enumerate(cells):
+        s0, s1 = a_prev_t.indptr[j], a_prev_t.indptr[j + 1]
+        seeds = list(a_prev_t.indices[s0:s1])
+        want = list(seeds)
+        for p in trace[r]:
+            if int(p) not in want:
+                want.append(int(p))
+        got = list(atom_idx[r, :atom_cnt[r]].astype(np.int64))
+        assert got == want, (j, got[:10], want[:10])
+
+
+def check_a(w, gpu_trace, atom_idx, atom_val, atom_cnt, cells, gamma=None, T=None,
+            strict_zero_ties=True) -> AReport:
+    """Trace replay of the A update for ``cells``; returns counts and errors."""
+    T = w.T if T is None else T
+    cells = np.asarray(cells, np.int64)
+    trace = np.asarray(gpu_trace, np.int64)
+    assert trace.shape == (cells.shape[0], T)
+    assert np.all((trace >= 0) & (trace < w.k)), "trace index out of range"
+    rep = oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, T, cells=cells, force=trace,
+                              gamma=gamma)
+    exact = trace == rep.pick
+    window = TIE_REL * np.maximum(np.maximum(np.abs(rep.g_min), np.abs(rep.g_second)),
+                                  rep.g_scale)
+    excess = rep.g_taken - rep.g_min
+    ok = exact | (excess <= window)
+    bad = np.argwhere(~ok)
+    if bad.shape[0]:
+        r, t = bad[0]
+        raise AssertionError(
+            "cell %d step %d: gpu picked %d (g=%.9g), oracle %d (g=%.9g, second %.9g, scale %.3g); "
+            "%d bad steps" % (cells[r], t, trace[r, t], rep.g_taken[r, t], rep.pick[r, t],
+                              rep.g_min[r, t], rep.g_second[r, t], rep.g_scale[r, t], bad.shape[0]))
+    # Structural zeros: with non-negative t1, a column outside supp(t2_j) whose
+    # f64 gradient is exactly 0 was never touched by a picked t1 row, so the
+    # f32 state holds an exact 0 there as well and the lowest such column must
+    # win bit for bit. (A zero reached by cancellation against t2 is only a
+    # rounding-level tie and falls under the window above.)
+    zero_tie = (rep.g_min == 0.0) & (rep.g_taken == 0.0) & ~exact
+    if strict_zero_ties and np.any(zero_tie) and (w.t1.data.min(initial=0.0) >= 0.0):
+        rr, tt = np.nonzero(zero_tie)
+        t2 = w.k2b[cells[rr]]
+        t2_gpu = np.asarray(t2[np.arange(rr.shape[0]), trace[rr, tt]]).ravel()
+        t2_orc = np.asarray(t2[np.arange(rr.shape[0]), rep.pick[rr, tt]]).ravel()
+        structural = (t2_gpu == 0.0) & (t2_orc == 0.0)
+        assert not np.any(structural), "lowest-index rule broken at a structural zero tie"
+        zero_tie[rr[~structural], tt[~structural]] = False
+    got = dense_atoms(atom_idx, atom_val, atom_cnt, w.k)
+    err = float(np.max(np.abs(got - rep.a))) if got.size else 0.0
+    assert err <= A_ABS, "A entries differ from the replayed oracle by %.3g" % err
+    check_atom_layout(atom_idx, atom_cnt, trace, w.a_prev_t, cells)
+    return AReport(int(trace.size), int(exact.sum()), int((~exact).sum()), int(zero_tie.sum()),
+                   err, float(np.max(excess / np.maximum(window, 1e-300))) if excess.size else 0.0)
+
+
+@dataclass
+class BReport:
+    exact: int
+    near_tie: int
+    max_val_rel: float
+    gap_rel: float
+
+
+def check_b(w, out_val, out_idx, gap, n=None, k=None, b=True, res=None) -> BReport:
+    n = w.n if n is None else n
+    k = w.k if k is None else k
+    if res is None:
+        res = oracle.fw_b_argmin(w.k2b, w.aat, w.k2at, w.b if b else None, n, k)
+    out_idx = np.asarray(out_idx, np.int64)
+    out_val = np.asarray(out_val, np.float64)
+    assert np.all((out_idx >= 0) & (out_idx < n)), "argmin row out of range"
+    exact = out_idx == res.row
+    mism = np.flatnonzero(~exact)
+    if mism.shape[0]:
+        g, sc = oracle.fw_b_grad_at(w.k2b, w.aat, w.k2at, n, k, out_idx[mism], mism)
+        scale = np.maximum.reduce([np.abs(res.val[mism]), np.abs(res.second[mism]), sc,
+                                   res.row_scale[res.row[mism]]])
+        over = (g - res.val[mism]) > TIE_REL * scale
+        if np.any(over):
+            c = mism[np.argmax(over)]
+            raise AssertionError("column %d: gpu row %d, oracle row %d (min %.9g, second %.9g)"
+                                 % (c, out_idx[c], res.row[c], res.val[c], res.second[c]))
+    tol = VAL_ABS + VAL_REL * np.abs(res.val)
+    dv = np.abs(out_val - res.val)
+    assert np.all(dv <= tol), "min values differ: worst %.3g" % float(np.max(dv - tol))
+    grel = 0.0
+    if gap is not None and b:
+        grel = abs(float(gap) - res.gap) / max(abs(res.gap), 1e-4 / GAP_REL)
+        assert grel <= GAP_REL, "gap %.9g vs oracle %.9g" % (float(gap), res.gap)
+    return BReport(int(exact.sum()), int((~exact).sum()),
+                   float(np.max(dv / np.maximum(np.abs(res.val), 1e-30))), grel)

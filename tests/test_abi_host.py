@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_archetypal_analysis_amd as saa
+from sparse_archetypal_analysis_amd import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "seacells_fw.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(seacells_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = saa.load()
+    names = header_functions()
+    assert set(names) == set(native.EXPORTS)
+    for nm in names:
+        assert hasattr(lib, nm), nm
+
+
+def test_version_and_status_strings():
+    lib = saa.load()
+    assert lib.seacells_version() >> 16 == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.seacells_status_string(code) != b"unknown status"
+    assert lib.seacells_status_string(7) == b"unknown status"
+    assert lib.seacells_last_error() == b""
+
+
+def csr(rows, cols, nnz=0, ptr=0x1000):
+    return native.seacells_csr(ptr, 0x2000 if nnz else None, 0x3000 if nnz else None, rows, cols,
+                               nnz)
+
+
+def call_a(t1, k2b, ap, n, k, T, cap, ws=None, ws_bytes=0, outs=True, status=0x9000):
+    lib = saa.load()
+    o = 0x4000 if outs else None
+    return lib.seacells_fw_a_columns(ctypes.byref(t1) if t1 else None,
+                                     ctypes.byref(k2b) if k2b else None,
+                                     ctypes.byref(ap) if ap else None, n, k, T, cap, None, o, o,
+                                     o, None, ws, ws_bytes, status, None)
+
+
+def test_a_columns_rejects_bad_arguments_on_host():
+    n, k, T, cap = 10, 4, 5, 8
+    t1, k2b, ap = csr(k, k, 3), csr(n, k, 5), csr(n, k, 5)
+    assert call_a(None, k2b, ap, n, k, T, cap) == -1
+    assert call_a(t1, k2b, ap, n, k, T, cap, outs=False) == -1
+    assert call_a(t1, k2b, ap, n, k, T, cap, status=None) == -1
+    assert call_a(t1, k2b, ap, 0, k, T, cap) == -2
+    assert call_a(t1, k2b, ap, n, k, 0, cap) == -2
+    assert call_a(t1, k2b, ap, n, k, T, 0) == -2
+    assert call_a(csr(k + 1, k, 3), k2b, ap, n, k, T, cap) == -2
+    assert call_a(t1, csr(n, k + 1, 5), ap, n, k, T, cap) == -2
+    assert call_a(t1, k2b, csr(n - 1, k, 5), n, k, T, cap) == -2
+    assert call_a(t1, k2b, csr(n, k, 2 ** 31), n, k, T, cap) == -4
+    # non-empty operand without index/value arrays
+    bad = native.seacells_csr(0x1000, None, None, n, k, 5)
+    assert call_a(t1, bad, ap, n, k, T, cap) == -1
+
+
+def test_a_columns_workspace_only_when_state_leaves_lds():
+    assert saa.seacells_fw_a_columns_workspace(1000, 1300, 50, 60) == 0
+    assert saa.seacells_fw_a_columns_workspace(1000, 10000, 50, 66) == 0
+    big = saa.seacells_fw_a_columns_workspace(1000, 60000, 50, 66)
+    assert big >= 1000 * 60000 * 4 and big % 256 == 0
+    # a large-k call without that workspace is refused on the host
+    n, k, T, cap = 1000, 60000, 50, 66
+    assert call_a(csr(k, k, 3), csr(n, k, 5), csr(n, k, 5), n, k, T, cap) == -3
+
+
+def test_b_argmin_rejects_bad_arguments_on_host():
+    lib = saa.load()
+    n, k = 100, 30
+    k2b, aat, k2at, b = csr(n, k, 5), csr(k, k, 5), csr(n, k, 5), csr(n, k, 5)
+    ws = saa.seacells_fw_b_argmin_workspace(n, k)
+    assert ws > 0 and ws % 256 == 0
+
+    def call(k2b=k2b, aat=aat, k2at=k2at, b=b, n=n, k=k, ws_ptr=0x100000, ws_bytes=ws,
+             out=0x4000, status=0x9000):
+        r = lambda m: ctypes.byref(m) if m is not None else None
+        return lib.seacells_fw_b_argmin(r(k2b), r(aat), r(k2at), r(b), n, k, out, out, None,
+                                        ws_ptr, ws_bytes, status, None)
+    assert call(k2b=None) == -1
+    assert call(out=None) == -1
+    assert call(status=None) == -1
+    assert call(n=0) == -2
+    assert call(aat=csr(k, k + 1, 5)) == -2
+    assert call(b=csr(n + 1, k, 5)) == -2
+    assert call(ws_bytes=ws - 1) == -3
+    assert call(ws_ptr=None) == -3
+    assert call(ws_ptr=0x100010) == -3        # not 256-byte aligned
+    assert call(k2at=csr(n, k, 2 ** 31)) == -4
+
+
+def test_b_workspace_grows_with_slices():
+    one = saa.seacells_fw_b_argmin_workspace(100_000, 1300)
+    many = saa.seacells_fw_b_argmin_workspace(100_000, 10_000)
+    assert one > 0 and many > one
+
+
+def test_b_apply_rejects_bad_arguments_on_host():
+    lib = saa.load()
+    p = 0x4000
+    assert lib.seacells_fw_b_apply(None, p, p, 10, 4, 3, p, 0.5, p, None) == -1
+    assert lib.seacells_fw_b_apply(p, p, p, 10, 0, 3, p, 0.5, p, None) == -2
+    assert lib.seacells_fw_b_apply(p, p, p, 10, 4, 0, p, 0.5, p, None) == -2
+    assert lib.seacells_fw_b_apply(p, p, p, 10, 4, 3, p, 0.0, p, None) == -2
+    assert lib.seacells_fw_b_apply(p, p, p, 10, 4, 3, p, 1.5, p, None) == -2
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(saa.SeacellsError):
+        saa.DeviceCSR(torch.zeros(3, dtype=torch.int32), torch.zeros(0, dtype=torch.int32),
+                      torch.zeros(0), (2, 2))

@@ -1,0 +1,150 @@
+"""A update on the GPU against the f64 oracle (trace replay)."""
+import numpy as np
+import pytest
+
+import workloads as W
+from tests import parity
+from tests.gpu_run import dev, run_a
+
+pytestmark = pytest.mark.gpu
+
+
+def assert_same_result(r0, r1):
+    """Bitwise equality of trace, counts and the valid atom slots."""
+    ai0, av0, ac0, tr0, _ = r0
+    ai1, av1, ac1, tr1, _ = r1
+    np.testing.assert_array_equal(tr0, tr1)
+    np.testing.assert_array_equal(ac0, ac1)
+    mask = np.arange(ai0.shape[1])[None, :] < ac0[:, None]
+    np.testing.assert_array_equal(ai0[mask], ai1[mask])
+    np.testing.assert_array_equal(av0[mask].view(np.uint32), av1[mask].view(np.uint32))
+
+
+def identity_workload():
+    n, k = 4, 2
+    B = np.zeros((n, k), np.float32)
+    B[0, 0] = B[1, 1] = 1.0
+    cfg = W.Config("identity", n, 0, 0, 0, k, 2, 0, T=50)
+    return W.Workload(cfg, 0, t1=W.dense_to_csr(np.eye(2)), k2b=W.dense_to_csr(B),
+                      a_prev_t=W.dense_to_csr(np.full((n, k), 0.5)), aat=W.dense_to_csr(np.eye(2)),
+                      k2at=W.dense_to_csr(B), b=W.dense_to_csr(B), init_cells=np.zeros(0, np.int64))
+
+
+def test_identity_kernel_worked_example_exact_ties():
+    w = identity_workload()
+    ai, av, ac, tr, flags = run_a(w)
+    assert flags == []
+    T = 50
+    # exact ties in f32 as in f64: the lowest index must win, bit for bit
+    assert tr[0].tolist() == [0] * T
+    assert tr[1].tolist() == [1, 0] + [1] * (T - 2)
+    assert tr[2].tolist() == [t % 2 for t in range(T)]
+    assert tr[3].tolist() == [t % 2 for t in range(T)]
+    dense = parity.dense_atoms(ai, av, ac, 2)
+    want = np.array([[1, 0], [4 / 2550, 1 - 4 / 2550], [25 / 51, 26 / 51], [25 / 51, 26 / 51]])
+    np.testing.assert_allclose(dense, want, rtol=0, atol=parity.A_ABS)
+    assert ac.tolist() == [2, 2, 2, 2]            # the two seeds, no appends
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_config_all_cells(name):
+    w = W.make(name)
+    ai, av, ac, tr, flags = run_a(w)
+    assert flags == []
+    rep = parity.check_a(w, tr, ai, av, ac, np.arange(w.n))
+    print("\n%s: %s" % (name, rep))
+    assert rep.near_tie <= 1e-3 * rep.steps
+
+
+def test_c3_full_size_sampled_cells():
+    w = W.make("c3")
+    ai, av, ac, tr, flags = run_a(w)
+    assert flags == []
+    rng = np.random.default_rng(3)
+    cells = np.unique(np.concatenate([[0, w.n - 1], rng.choice(w.n, size=400, replace=False)]))
+    rep = parity.check_a(w, tr[cells], ai[cells], av[cells], ac[cells], cells)
+    print("\nc3 sampled: %s" % (rep,))
+    # properties that hold for every cell at any size
+    assert np.all(ac >= np.diff(w.a_prev_t.indptr)) and np.all(ac <= w.cap)
+    assert np.all((tr >= 0) & (tr < w.k))
+    dense_sum = np.zeros(w.n)
+    for s in range(ai.shape[1]):
+        dense_sum += np.where(s < ac, av[:, s], 0.0)
+    np.testing.assert_allclose(dense_sum, 1.0, atol=1e-5)
+
+
+def test_ragged_signed_operands_dense_path():
+    w = W.random_workload(1237, 333, t1_per_row=12, k2b_per_row=9, s_a=7, seed=5, signed=True)
+    ai, av, ac, tr, flags = run_a(w)
+    assert flags == []
+    parity.check_a(w, tr, ai, av, ac, np.arange(w.n))
+
+
+def test_large_k_state_in_workspace():
+    # k * 4 bytes exceeds the 160 KB LDS of a compute unit: h lives in workspace
+    import sparse_archetypal_analysis_amd as saa
+    w = W.random_workload(37, 45_000, t1_per_row=6, k2b_per_row=20, s_a=5, seed=7, T=30)
+    assert saa.seacells_fw_a_columns_workspace(w.n, w.k, 30, w.cap) > 0
+    ai, av, ac, tr, flags = run_a(w, T=30)
+    assert flags == []
+    parity.check_a(w, tr, ai, av, ac, np.arange(w.n), T=30)
+
+
+def test_empty_rows_and_columns():
+    # empty K2B rows (g = t1 . a), empty A_prev columns (g = -t2), and both
+    w = W.random_workload(300, 40, s_a=3, seed=9, empty_k2b_every=3, empty_ap_every=4)
+    ai, av, ac, tr, flags = run_a(w)
+    assert flags == []
+    parity.check_a(w, tr, ai, av, ac, np.arange(w.n))
+    both = [j for j in range(w.n) if j % 12 == 0]
+    # g is identically 0 at step 0 when both are empty: the lowest column wins
+    assert all(tr[j, 0] == 0 for j in both)
+
+
+def test_single_archetype_and_single_step():
+    w = W.random_workload(65, 1, s_a=1, seed=11)
+    ai, av, ac, tr, flags = run_a(w)
+    assert flags == [] and np.all(tr == 0)
+    np.testing.assert_array_equal(parity.dense_atoms(ai, av, ac, 1), np.ones((65, 1)))
+    w = W.make("c1")
+    ai, av, ac, tr, flags = run_a(w, T=1, cap=w.cap - w.T + 1)
+    assert flags == []
+    parity.check_a(w, tr, ai, av, ac, np.arange(w.n), T=1)
+
+
+def test_step_size_table_and_scale_folding():
+    w = W.make("c1")
+    T = 120
+    # gamma_0 = 1 then 0.55 per step: the running scale (0.45^t) drops below
+    # 2^-64 and is folded back into the state
+    gam = np.full(T, 0.55, np.float32)
+    gam[0] = 1.0
+    ai, av, ac, tr, flags = run_a(w, T=T, cap=w.cap - w.T + T, gamma=gam)
+    assert flags == []
+    parity.check_a(w, tr, ai, av, ac, np.arange(w.n), gamma=gam.astype(np.float64), T=T)
+    # the default schedule passed as an explicit f32 table matches NULL
+    tab = (2.0 / (np.arange(w.T) + 2.0)).astype(np.float32)
+    assert_same_result(run_a(w), run_a(w, gamma=tab))
+
+
+def test_cap_overflow_is_reported():
+    w = W.make("c1")
+    ai, av, ac, tr, flags = run_a(w)
+    need = int(ac.max())
+    _, _, ac2, _, flags2 = run_a(w, cap=need - 1)
+    assert "CAP_OVERFLOW" in flags2
+    assert int(ac2.max()) <= need - 1
+
+
+def test_bad_step_size_is_reported():
+    w = W.make("c1")
+    gam = np.full(w.T, 0.5, np.float32)
+    gam[3] = 1.5
+    *_, flags = run_a(w, gamma=gam)
+    assert "BAD_GAMMA" in flags
+
+
+def test_deterministic_bitwise():
+    w = W.make("c2")
+    ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
+    assert_same_result(run_a(w, ops=ops), run_a(w, ops=ops))

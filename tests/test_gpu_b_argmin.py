@@ -1,0 +1,148 @@
+"""B-gradient argmin and B step on the GPU against the f64 oracle."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_archetypal_analysis_amd as saa
+import workloads as W
+from tests import parity
+from tests.gpu_run import dev, run_b, run_b_dense
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_fixtures.json")
+
+
+def page_problem(n, k):
+    fx = json.load(open(GOLDEN))["fixture"]["operands"]
+    return (W.page_fixture(n * k, *fx["k2b"]).reshape(n, k),
+            W.page_fixture(k * k, *fx["t1"]).reshape(k, k),
+            W.page_fixture(n * k, *fx["t2"]).reshape(n, k),
+            W.page_fixture(n * k, *fx["b"]).reshape(n, k))
+
+
+@pytest.mark.parametrize("n,k", [(40, 7), (257, 33), (1000, 130), (3000, 300), (300, 1100)])
+def test_page_fixtures(n, k):
+    # signed values and a non-symmetric t1: the row-scatter form is still the
+    # page's G[i, c] = sum_m K2B[i, m] t1[m, c] - t2[i, c]
+    w, (v, i, g, flags) = run_b_dense(*page_problem(n, k))
+    assert flags == []
+    rep = parity.check_b(w, v, i, g)
+    assert rep.near_tie * 50 <= k
+
+
+def test_page_empty_rows_exact():
+    cfg = json.load(open(GOLDEN))["empty_rows"]
+    k2b, t1, t2, b = page_problem(cfg["n"], cfg["k"])
+    k2b[::cfg["blank_every"]] = 0.0
+    w, (v, i, g, flags) = run_b_dense(k2b, t1, t2, b)
+    assert flags == []
+    res = oracle.fw_b_argmin(w.k2b, w.aat, w.k2at, w.b, w.n, w.k)
+    np.testing.assert_array_equal(i, res.row)
+    parity.check_b(w, v, i, g, res=res)
+
+
+def test_page_tie_breaks_on_lowest_row():
+    cfg = json.load(open(GOLDEN))["tie_break"]
+    n, k = cfg["n"], cfg["k"]
+    k2b = np.tile(-1.0 - np.arange(k, dtype=np.float32), (n, 1))
+    w, (v, i, g, flags) = run_b_dense(k2b, np.eye(k, dtype=np.float32),
+                                      np.zeros((n, k), np.float32), np.zeros((n, k), np.float32))
+    assert flags == []
+    np.testing.assert_array_equal(i, np.zeros(k))
+    np.testing.assert_array_equal(v, -1.0 - np.arange(k))
+
+
+def test_identity_kernel_worked_example():
+    n, k = 4, 2
+    B = np.zeros((n, k), np.float32)
+    B[0, 0] = B[1, 1] = 1.0
+    aat = np.ones((k, k), np.float32)
+    k2at = np.full((n, k), 0.5, np.float32)
+    w, (v, i, g, flags) = run_b_dense(B, aat, k2at, B)
+    assert flags == []
+    np.testing.assert_array_equal(i, [2, 2])
+    np.testing.assert_array_equal(v, [-0.5, -0.5])
+    assert g == 1.0
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_configs_all_columns(name):
+    w = W.make(name)
+    v, i, g, flags = run_b(w)
+    assert flags == []
+    rep = parity.check_b(w, v, i, g)
+    print("\n%s: %s" % (name, rep))
+
+
+@pytest.mark.parametrize("n,k", [(3000, 2100), (500, 5000), (2, 9000)])
+def test_column_slices(n, k):
+    w = W.random_workload(n, k, aat_per_row=30, k2b_per_row=12, k2at_per_row=10, seed=n + k)
+    v, i, g, flags = run_b(w)
+    assert flags == []
+    parity.check_b(w, v, i, g)
+
+
+def test_single_row_single_column_and_no_b():
+    w = W.random_workload(1, 1, seed=2)
+    v, i, g, flags = run_b(w)
+    assert flags == [] and i.tolist() == [0]
+    parity.check_b(w, v, i, g)
+    w = W.make("c1")
+    v, i, g, flags = run_b(w, with_b=False)
+    assert flags == [] and g == 0.0
+    parity.check_b(w, v, i, None, b=False)
+
+
+def test_deterministic_bitwise():
+    w = W.make("c2")
+    ops = (dev(w.k2b), dev(w.aat), dev(w.k2at), dev(w.b))
+    r1, r2 = run_b(w, ops=ops), run_b(w, ops=ops)
+    for a, b in zip(r1[:3], r2[:3]):
+        np.testing.assert_array_equal(a, b)
+
+
+def _apply(bt_idx, bt_val, bt_cnt, n, arg, gam):
+    ti = torch.from_numpy(bt_idx.astype(np.int32)).cuda()
+    tv = torch.from_numpy(bt_val.astype(np.float32)).cuda()
+    tc = torch.from_numpy(bt_cnt.astype(np.int32)).cuda()
+    ta = torch.from_numpy(np.asarray(arg, np.int32)).cuda()
+    _, _, _, st = saa.seacells_fw_b_apply(ti, tv, tc, n, ta, gam)
+    torch.cuda.synchronize()
+    return ti.cpu().numpy(), tv.cpu().numpy(), tc.cpu().numpy(), saa.status_flags(st)
+
+
+def test_b_step_after_argmin():
+    w = W.make("c2")
+    v, i, g, flags = run_b(w)
+    cap_b = int(np.diff(w.b.tocsc().indptr).max()) + 2
+    bi, bv, bc = W.bt_padded(w.b, cap_b)
+    gam = 2.0 / 5.0
+    gi, gv, gc, fl = _apply(bi, bv, bc, w.n, i, gam)
+    assert fl == []
+    oi, ov, oc = oracle.fw_b_apply(bi, bv, bc, i, gam)
+    np.testing.assert_array_equal(gc, oc)
+    for c in range(w.k):
+        np.testing.assert_array_equal(gi[c, :gc[c]], oi[c, :oc[c]])
+    err = max(float(np.max(np.abs(gv[c, :gc[c]] - ov[c, :oc[c]]))) for c in range(w.k))
+    assert err <= parity.B_ABS
+
+
+def test_b_step_overflow_and_bad_index_flags():
+    k, cap_b, n = 5, 3, 50
+    bi = np.tile(np.array([1, 4, 9], np.uint32), (k, 1))
+    bv = np.full((k, cap_b), 1.0 / 3, np.float32)
+    bc = np.full(k, 3, np.uint32)
+    arg = np.array([4, 4, 4, 4, 4])          # present: fine
+    *_, fl = _apply(bi, bv, bc, n, arg, 0.5)
+    assert fl == []
+    arg = np.array([4, 7, 4, 4, 4])          # column 1 would need a 4th slot
+    gi, gv, gc, fl = _apply(bi, bv, bc, n, arg, 0.5)
+    assert fl == ["B_CAP_OVERFLOW"] and gc[1] == 3
+    np.testing.assert_array_equal(gv[1], bv[1])         # row left unchanged
+    arg = np.array([4, 4, 4, 4, 50])         # row index out of range
+    *_, fl = _apply(bi, bv, bc, n, arg, 0.5)
+    assert fl == ["BAD_INDEX"]

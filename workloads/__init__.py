@@ -381,3 +381,66 @@ def dense_to_csr(a: np.ndarray) -> sp.csr_matrix:
     m.indices = m.indices.astype(np.int32)
     m.indptr = m.indptr.astype(np.int32)
     return m
+
+
+# --------------------------------------------------------------------------
+# random sparse operands for shape and edge cases (no kernel construction)
+# --------------------------------------------------------------------------
+
+def _rand_csr(rng, rows, cols, per_row, signed=False, empty_every=0, lo=0.05, hi=1.0):
+    per_row = max(0, min(per_row, cols))
+    indptr = [0]
+    indices, data = [], []
+    for r in range(rows):
+        if empty_every and r % empty_every == 0:
+            indptr.append(len(indices))
+            continue
+        cnt = int(rng.integers(0, 2 * per_row + 1)) if per_row else 0
+        cnt = min(cnt, cols)
+        cs = np.sort(rng.choice(cols, size=cnt, replace=False))
+        vs = rng.uniform(lo, hi, size=cnt)
+        if signed:
+            vs *= rng.choice([-1.0, 1.0], size=cnt)
+        indices.extend(cs.tolist())
+        data.extend(vs.tolist())
+        indptr.append(len(indices))
+    return sp.csr_matrix((np.asarray(data, np.float64), np.asarray(indices, np.int64),
+                          np.asarray(indptr, np.int64)), shape=(rows, cols))
+
+
+def random_workload(n: int, k: int, t1_per_row: int = 8, k2b_per_row: int = 6, s_a: int = 4,
+                    T: int = 50, seed: int = 0, signed: bool = False, empty_k2b_every: int = 0,
+                    empty_ap_every: int = 0, aat_per_row: int = 8, k2at_per_row: int = 6,
+                    b_per_col: int = 3) -> Workload:
+    """Random sparse operands of the right shapes and symmetry, for cases the
+    kernel-based workloads do not reach (large k with tiny n, empty rows,
+    signed values, ragged sizes). Values are uniform in [0.05, 1) (times a
+    random sign when ``signed``); A_prev rows are Dirichlet(1) on random
+    supports; B columns are Dirichlet(1) on random cells."""
+    rng = np.random.default_rng(seed)
+    t1 = _rand_csr(rng, k, k, t1_per_row, signed)
+    k2b = _rand_csr(rng, n, k, k2b_per_row, signed, empty_every=empty_k2b_every)
+    aat = _rand_csr(rng, k, k, aat_per_row, signed)
+    k2at = _rand_csr(rng, n, k, k2at_per_row, signed)
+    rows, cols, vals = [], [], []
+    for j in range(n):
+        if empty_ap_every and j % empty_ap_every == 0:
+            continue
+        s = min(s_a, k)
+        sup = np.sort(rng.choice(k, size=s, replace=False))
+        rows.extend([j] * s)
+        cols.extend(sup.tolist())
+        vals.extend(rng.dirichlet(np.ones(s)).tolist())
+    ap = sp.csr_matrix((vals, (rows, cols)), shape=(n, k))
+    brow, bcol, bval = [], [], []
+    for c in range(k):
+        s = min(b_per_col, n)
+        sup = rng.choice(n, size=s, replace=False)
+        brow.extend(sup.tolist())
+        bcol.extend([c] * s)
+        bval.extend(rng.dirichlet(np.ones(s)).tolist())
+    b = sp.csr_matrix((bval, (brow, bcol)), shape=(n, k))
+    cfg = Config("random", n, 0, 0, 0, k, s_a, b_per_col, T=T, index=0)
+    return Workload(cfg, seed, t1=_f32(t1, symmetric=True), k2b=_f32(k2b), a_prev_t=_f32(ap),
+                    aat=_f32(aat, symmetric=True), k2at=_f32(k2at), b=_f32(b),
+                    init_cells=np.zeros(0, np.int64), meta={"random": True})
