@@ -124,6 +124,21 @@ def cpu_baseline(w, budget_s=12.0):
             "a_cells_per_s": rate_a, "b_cells_per_s": rate_b}
 
 
+def copy_calibration(mib):
+    """A plain elementwise copy of known size: it reads and writes exactly
+    mib MiB per launch, so FETCH_SIZE / WRITE_SIZE of this kernel give the
+    scale between those counters and bytes."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,7 +147,13 @@ def main():
     ap.add_argument("--config", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 launches), the reference "
+                         "kernel that scales the HBM byte counters")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the multi-GPU sharding of this path is "
               "described in DESIGN.md and not built; run with --gpus 1", file=sys.stderr)
