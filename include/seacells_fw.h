@@ -58,7 +58,7 @@ extern "C" {
 #define SEACELLS_E_NULL (-1)      /* a required pointer is NULL */
 #define SEACELLS_E_SHAPE (-2)     /* n, k or T is 0, or operand shapes disagree */
 #define SEACELLS_E_WORKSPACE (-3) /* workspace smaller than the *_workspace() size */
-#define SEACELLS_E_TOO_LARGE (-4) /* n, k or nnz >= 2^31, n * cap >= 2^40, cap * 8 > 160 KB */
+#define SEACELLS_E_TOO_LARGE (-4) /* n, k or nnz >= 2^31, n * cap >= 2^40, atom list > LDS */
 #define SEACELLS_E_HIP (-5)       /* a HIP launch or query failed */
 
 /* Device-detected conditions (bits of *status). */

@@ -89,9 +89,10 @@ int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
   if ((rc = check_csr(a_prev_t, n, k)) != SEACELLS_OK) return rc;
   if ((uint64_t)n * cap >= (1ull << 40) || (uint64_t)n * T >= (1ull << 40))
     return SEACELLS_E_TOO_LARGE;
-  // per-wave LDS must at least hold the atom list
-  if ((uint64_t)cap * 8 > kLdsBytesPerCU) return SEACELLS_E_TOO_LARGE;
+  if (cap >= 0x10000000u) return SEACELLS_E_TOO_LARGE;
   const APlan plan = plan_a(n, k, T, cap);
+  // per-wave LDS must at least hold the atom list
+  if (plan.waves_per_block == 0) return SEACELLS_E_TOO_LARGE;
   if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))
     return SEACELLS_E_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -117,11 +117,14 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // --- A update -------------------------------------------------------------
 struct APlan {
-  uint32_t kpad;          // k rounded up to 4 (padding holds +inf)
-  uint32_t waves_per_block;
-  uint32_t lds_per_wave;  // bytes
+  uint32_t kpad;               // scan length: k + 1 rounded up to 256 (padding holds +inf)
+  uint32_t waves_per_block;    // 0: the atom list alone does not fit in LDS
+  uint32_t lds_per_wave;       // bytes
+  uint32_t sched_words;        // LDS words of the per-block step schedule (0: computed per step)
   bool h_in_lds;
-  uint32_t global_waves;  // waves that own a workspace slice (h in workspace)
+  bool reg_atoms;              // atoms in registers (cap <= 128), else in LDS
+  uint32_t global_waves;       // waves that own a workspace slice (state in workspace)
+  uint32_t ws_words_per_wave;  // state words per wave in the workspace
   size_t ws_bytes;
 };
 APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap);

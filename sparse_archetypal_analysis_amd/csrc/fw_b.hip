@@ -201,8 +201,8 @@ __global__ void __launch_bounds__(kBThreads)
       stamps[unit] = epoch;
     }
   }
-  flags = __builtin_amdgcn_readfirstlane(flags);
-  if (flags != 0 && lane == 0) atomicOr(status, flags);
+  // some flags are raised by single lanes: every lane that saw one reports it
+  if (flags != 0) atomicOr(status, flags);
 }
 
 // Stage 1: block (column group x, row-range chunk y); 4 waves x 64 lanes.

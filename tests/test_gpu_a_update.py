@@ -148,3 +148,39 @@ def test_deterministic_bitwise():
     w = W.make("c2")
     ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
     assert_same_result(run_a(w, ops=ops), run_a(w, ops=ops))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "empty"])
+def test_support_argmin_equals_dense_scan(name, monkeypatch):
+    # On non-negative data the argmin is taken from the minimum over supp(t2)
+    # and the touched-column bitmap; it must give the very index a dense scan
+    # of the same f32 state gives, at every step of every cell.
+    if name == "empty":
+        w = W.random_workload(300, 40, s_a=3, seed=9, empty_k2b_every=3, empty_ap_every=4)
+    else:
+        w = W.make(name)
+    ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
+    monkeypatch.setenv("SEACELLS_A_DENSE_ARGMIN", "1")
+    dense = run_a(w, ops=ops)
+    monkeypatch.delenv("SEACELLS_A_DENSE_ARGMIN")
+    fast = run_a(w, ops=ops)
+    assert dense[4] == [] and fast[4] == []
+    assert_same_result(dense, fast)
+
+
+def test_large_capacity_keeps_atoms_in_lds():
+    # cap > 128: the atom list moves from registers to LDS
+    w = W.make("c1")
+    T = 200
+    ai, av, ac, tr, flags = run_a(w, T=T, cap=w.cap - w.T + T)
+    assert flags == []
+    cells = np.arange(0, w.n, 5)
+    parity.check_a(w, tr[cells], ai[cells], av[cells], ac[cells], cells, T=T)
+
+
+def test_large_k_and_large_capacity():
+    # state in workspace and atoms in LDS together
+    w = W.random_workload(37, 45_000, t1_per_row=6, k2b_per_row=20, s_a=5, seed=17, T=140)
+    ai, av, ac, tr, flags = run_a(w, T=140)
+    assert flags == []
+    parity.check_a(w, tr, ai, av, ac, np.arange(w.n), T=140)
