@@ -7,10 +7,11 @@
 // Work unit = (row range, column slice). A wave owns one unit at a time:
 // per row it scatters the AAt rows named by the row's K2B entries into a
 // dense slice accumulator in LDS (coalesced lane-strided reads of each AAt
-// row segment; the columns of one row are unique, so one scatter
-// instruction never collides), subtracts the K2At row, adds the row's
-// B . G term, then folds the slice into running (min, row) pairs held in
-// registers, 4 consecutive columns per float4 chunk, and clears the slice.
+// row segment, four runs in flight at a time; the columns of one row are
+// unique, so one scatter instruction never collides), subtracts the K2At
+// row, adds the row's B . G term, then folds the slice into running
+// (min, row) pairs held in registers, 4 consecutive columns per float4
+// chunk, and clears the slice.
 // Rows run in ascending order under a strict `<`, so the lowest row wins a
 // tie inside a unit. The unit writes one (order-preserving f32 key << 32 |
 // row) per column, which makes "lower value, then lower row" a plain u64
@@ -35,6 +36,14 @@ constexpr uint32_t kBUnitsTarget = 8192;
 constexpr uint32_t kBMaxS4 = 8;
 constexpr uint32_t kReduceCols = 64;  // columns per stage-1 block (one per lane)
 constexpr uint32_t kMaxChunks = 64;
+
+constexpr uint32_t kGatherRows = 4;  // AAt runs whose loads are in flight together
+constexpr uint32_t kNoCol = 0xffffffffu;
+
+// acc[c] += v (LDS read, add, write). One wave's LDS operations execute in
+// issue order and the columns of one row are unique, so the sum order per
+// column is the program order.
+__device__ __forceinline__ void lds_add(float *p, float v) { *p = *p + v; }
 
 __device__ __forceinline__ uint64_t pack_key(float v, uint32_t row) {
   return ((uint64_t)f32_order(v) << 32) | (uint64_t)row;
@@ -139,15 +148,35 @@ __global__ void __launch_bounds__(kBThreads)
           }
         }
         const uint32_t cnt = (e1 - eb) < kWave ? (e1 - eb) : kWave;
-        for (uint32_t u = 0; u < cnt; ++u) {
-          const uint32_t plo = readlane_u32(lo, u);
-          const uint32_t phi = readlane_u32(hi, u);
-          const float xs = readlane_f32(x, u);
-          for (uint32_t p = plo + lane; p < phi; p += kWave) {
-            const uint32_t c = aat.idx[p] - c0;
-            if (c < cw) acc[c] += xs * aat.val[p];
+        // kGatherRows AAt runs in flight at a time (their first two chunks);
+        // the adds still go row after row, so every column sums its terms in
+        // K2B order and the result does not depend on the timing
+        for (uint32_t u = 0; u < cnt; u += kGatherRows) {
+          uint32_t plo[kGatherRows], phi[kGatherRows];
+          float xs[kGatherRows], va[kGatherRows], vb[kGatherRows];
+          uint32_t ca[kGatherRows], cb[kGatherRows];
+#pragma unroll
+          for (uint32_t g = 0; g < kGatherRows; ++g) {
+            const uint32_t src = (u + g) < kWave ? (u + g) : (kWave - 1);
+            const bool on = (u + g) < cnt;
+            plo[g] = on ? readlane_u32(lo, src) : 0u;
+            phi[g] = on ? readlane_u32(hi, src) : 0u;
+            xs[g] = readlane_f32(x, src);
+            const uint32_t pa = plo[g] + lane, pb = pa + kWave;
+            ca[g] = kNoCol, va[g] = 0.0f, cb[g] = kNoCol, vb[g] = 0.0f;
+            if (pa < phi[g]) ca[g] = aat.idx[pa], va[g] = aat.val[pa];
+            if (pb < phi[g]) cb[g] = aat.idx[pb], vb[g] = aat.val[pb];
           }
-          wave_lds_sync();
+#pragma unroll
+          for (uint32_t g = 0; g < kGatherRows; ++g) {
+            const uint32_t c_a = ca[g] - c0, c_b = cb[g] - c0;
+            if (c_a < cw) lds_add(acc + c_a, xs[g] * va[g]);
+            if (c_b < cw) lds_add(acc + c_b, xs[g] * vb[g]);
+            for (uint32_t p = plo[g] + 2 * kWave + lane; p < phi[g]; p += kWave) {
+              const uint32_t c = aat.idx[p] - c0;
+              if (c < cw) lds_add(acc + c, xs[g] * aat.val[p]);
+            }
+          }
         }
       }
       // -- acc[c] -= K2At[i, c]
@@ -155,7 +184,7 @@ __global__ void __launch_bounds__(kBThreads)
       if (!row_ok(k2at, i, q0, q1)) flags |= kFlagBadIndex;
       for (uint32_t q = q0 + lane; q < q1; q += kWave) {
         const uint32_t c = k2at.idx[q] - c0;
-        if (c < cw) acc[c] -= k2at.val[q];
+        if (c < cw) lds_add(acc + c, -k2at.val[q]);
       }
       wave_lds_sync();
       // -- gap += sum_c B[i, c] G[i, c]
