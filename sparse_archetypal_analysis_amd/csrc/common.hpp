@@ -117,7 +117,8 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // --- A update -------------------------------------------------------------
 struct APlan {
-  uint32_t kpad;               // scan length: k + 1 rounded up to 256 (padding holds +inf)
+  uint32_t group;              // lanes per cell (16, 32 or 64)
+  uint32_t kpad;               // scan length: k + 1 rounded up to 4 * group (padding holds +inf)
   uint32_t waves_per_block;    // 0: the atom list alone does not fit in LDS
   uint32_t lds_per_wave;       // bytes
   uint32_t sched_words;        // LDS words of the per-block step schedule (0: computed per step)

@@ -184,3 +184,20 @@ def test_large_k_and_large_capacity():
     ai, av, ac, tr, flags = run_a(w, T=140)
     assert flags == []
     parity.check_a(w, tr, ai, av, ac, np.arange(w.n), T=140)
+
+
+def test_lane_group_widths_agree_bitwise(monkeypatch):
+    # 16, 32 or 64 lanes per cell only changes which lanes carry a cell; each
+    # column sees the same operations in the same order, so the results must
+    # be bit-identical (and match the oracle)
+    w = W.random_workload(777, 300, t1_per_row=14, k2b_per_row=10, s_a=6, seed=23)
+    ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
+    res = {}
+    for g in ("16", "32", "64"):
+        monkeypatch.setenv("SEACELLS_A_GROUP", g)
+        res[g] = run_a(w, ops=ops)
+        assert res[g][4] == []
+    monkeypatch.delenv("SEACELLS_A_GROUP")
+    assert_same_result(res["16"], res["32"])
+    assert_same_result(res["16"], res["64"])
+    parity.check_a(w, res["32"][3], res["32"][0], res["32"][1], res["32"][2], np.arange(w.n))
