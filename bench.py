@@ -164,7 +164,7 @@ def main():
     import workloads as W
 
     t_gen = time.time()
-    w = W.make(args.config)
+    w = W.make(args.config, log=lambda m: print(m, file=sys.stderr, flush=True))
     t_gen = time.time() - t_gen
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

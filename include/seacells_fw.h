@@ -82,9 +82,13 @@ typedef struct seacells_csr {
 } seacells_csr;
 
 /*
- * Workspace bytes seacells_fw_a_columns needs for these sizes (0 when the
- * whole per-cell state fits in local memory). Depends only on its
- * arguments.
+ * Workspace bytes seacells_fw_a_columns needs for these sizes. 0 when the
+ * dense per-cell state fits in local memory and k is small; for large k
+ * (from 2048) it holds two counters and a queue of n cell ids (the cells
+ * the compact per-cell state hands to the dense kernel); when not even the
+ * dense state fits in local memory it also holds per-wave state slices.
+ * Depends only on its arguments (and on the SEACELLS_A_* experiment
+ * variables of the environment, which must be the same at the call).
  */
 size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint32_t cap);
 

@@ -126,6 +126,15 @@ struct APlan {
   bool reg_atoms;              // atoms in registers (cap <= 128), else in LDS
   uint32_t global_waves;       // waves that own a workspace slice (state in workspace)
   uint32_t ws_words_per_wave;  // state words per wave in the workspace
+  // support state (large k): a first pass settles most cells, the dense
+  // kernel above takes the cells it queues
+  bool support;
+  uint32_t nwords;             // 32-column words of the bitmaps
+  uint32_t hc_cap;             // longest K2B row the support state holds
+  uint32_t sup_lds_per_wave;   // bytes
+  uint32_t sup_waves_per_block;
+  size_t ws_list_off;          // queued cells (the counter sits at offset 0)
+  size_t ws_dense_off;         // dense state slices
   size_t ws_bytes;
 };
 APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap);

@@ -195,7 +195,8 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
                         float *__restrict__ atom_val, uint32_t *__restrict__ atom_cnt,
                         uint32_t *__restrict__ trace, float *__restrict__ state_ws,
                         uint32_t sched_words, uint32_t lds_words_per_wave, uint32_t dense_only,
-                        uint32_t *__restrict__ status) {
+                        const uint32_t *__restrict__ cell_list,
+                        const uint32_t *__restrict__ cell_count, uint32_t *__restrict__ status) {
   extern __shared__ uint32_t lds[];
   const uint32_t lane = lane_id();
   const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -203,6 +204,12 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
   const uint32_t gwave = blockIdx.x * wpb + wib;
   const uint32_t nwaves = gridDim.x * wpb;
   uint32_t flags = 0;
+  // cells: 0 .. n-1, or the first *cell_count entries of cell_list
+  uint32_t ncells = n;
+  if (cell_list != nullptr) {
+    const uint32_t c = *cell_count;
+    ncells = c < n ? c : n;
+  }
 
   // -- the step schedule, once per block
   const StepSched *sched = reinterpret_cast<const StepSched *>(lds);
@@ -248,13 +255,14 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
         v = 0.0f;
       }
       if (!valid) c = dummy, v = 0.0f;
-      h[c] = h[c] + alpha * v;
+      h[c] = __builtin_fmaf(alpha, v, h[c]);
       lane_neg |= (v < 0.0f);
     }
     return __ballot(lane_neg) != 0;
   };
 
-  for (uint32_t cell = gwave; cell < n; cell += nwaves) {
+  for (uint32_t slot = gwave; slot < ncells; slot += nwaves) {
+    const uint32_t cell = cell_list != nullptr ? cell_list[slot] : slot;
     // -- t2 = this cell's K2B row: the first kT2Regs * 64 entries in registers
     uint32_t q0 = k2b_ptr[cell], q1 = k2b_ptr[cell + 1];
     if (q1 > k2b_nnz || q0 > q1) {
@@ -336,7 +344,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       for (uint32_t r = 0; r < kT2Regs; ++r) {
         if (r < nchk) {
           const uint32_t c = t2c[r];
-          const float hn = h[c] - alpha * t2v[r];
+          const float hn = __builtin_fmaf(-alpha, t2v[r], h[c]);
           h[c] = hn;
           if (hn < bv) bv = hn, bi = c, br = r;
         }
@@ -347,7 +355,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
         if (q < q1) {
           const uint32_t c = k2b_idx[q];
           if (c < k) {
-            const float hn = h[c] - alpha * k2b_val[q];
+            const float hn = __builtin_fmaf(-alpha, k2b_val[q], h[c]);
             h[c] = hn;
             if (hn < bv) bv = hn, bi = c, br = nr;
           }
@@ -388,15 +396,15 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       if constexpr (kRegAtoms) {
 #pragma unroll
         for (uint32_t j = 0; j < kWaveAtomSlots; ++j) {
-          float v = aval[j] * sc.keep;
-          if (aidx[j] == idx) v += sc.gam, hit = true;
-          aval[j] = v;
+          const bool at = aidx[j] == idx;
+          aval[j] = at ? __builtin_fmaf(aval[j], sc.keep, sc.gam) : aval[j] * sc.keep;
+          hit |= at;
         }
       } else {
         for (uint32_t s = lane; s < cnt; s += kWave) {
-          float v = s_aval[s] * sc.keep;
-          if (s_aidx[s] == idx) v += sc.gam, hit = true;
-          s_aval[s] = v;
+          const bool at = s_aidx[s] == idx;
+          s_aval[s] = at ? __builtin_fmaf(s_aval[s], sc.keep, sc.gam) : s_aval[s] * sc.keep;
+          hit |= at;
         }
       }
       if (__ballot(hit) == 0) {
@@ -542,7 +550,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
           v = 0.0f;
         }
       }
-      h[c] = h[c] + alpha * v;
+      h[c] = __builtin_fmaf(alpha, v, h[c]);
       lane_neg |= (v < 0.0f);
     }
     return (__ballot(lane_neg) & gmask) != 0;
@@ -637,7 +645,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       for (uint32_t r = 0; r < kT2Regs; ++r) {
         if (r < nchk) {
           const uint32_t c = t2c[r];
-          const float hn = h[c] - alpha * t2v[r];
+          const float hn = __builtin_fmaf(-alpha, t2v[r], h[c]);
           h[c] = hn;
           if (hn < bv) bv = hn, bi = c;
         }
@@ -649,7 +657,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
         if (valid) {
           const uint32_t c = k2b_idx[q];
           if (c < k) {
-            const float hn = h[c] - alpha * k2b_val[q];
+            const float hn = __builtin_fmaf(-alpha, k2b_val[q], h[c]);
             h[c] = hn;
             if (hn < bv) bv = hn, bi = c;
           }
@@ -687,16 +695,16 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
 #pragma unroll
         for (uint32_t j = 0; j < AS; ++j) {
           if (j * G < cap) {
-            float v = aval[j] * sc.keep;
-            if (aidx[j] == idx) v += sc.gam, hit = true;
-            aval[j] = v;
+            const bool at = aidx[j] == idx;
+            aval[j] = at ? __builtin_fmaf(aval[j], sc.keep, sc.gam) : aval[j] * sc.keep;
+            hit |= at;
           }
         }
       } else {
         for (uint32_t s = gl; s < cnt; s += G) {
-          float v = s_aval[s] * sc.keep;
-          if (s_aidx[s] == idx) v += sc.gam, hit = true;
-          s_aval[s] = v;
+          const bool at = s_aidx[s] == idx;
+          s_aval[s] = at ? __builtin_fmaf(s_aval[s], sc.keep, sc.gam) : s_aval[s] * sc.keep;
+          hit |= at;
         }
       }
       if ((__ballot(hit) & gmask) == 0) {
@@ -764,12 +772,418 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
   if (flags != 0) atomicOr(status, flags);
 }
 
+// ---------------------------------------------------------------------------
+// Support state for large k (one cell per wave64).
+//
+// With non-negative data, g outside supp(t2) is a sum of non-negative
+// products, so the argmin needs the state only on supp(t2) (the cell's K2B
+// row, at most hc_cap entries) plus, for columns outside it, whether any
+// non-zero product has landed there since the last restart. Per cell the
+// wave keeps in LDS:
+//   rec[w]  for each 32-column word w: the supp(t2) bits of the word and the
+//           position in the row of its first entry, so a column's position
+//           is rec.y + popcount of the bits below it;
+//   cov[w]  bits of the columns outside supp(t2) that hold a non-zero
+//           product (the padding columns >= k are marked as well);
+//   hc[p]   h at the p-th column of supp(t2).
+// That is ~12 bytes per 32 columns + 4 per t2 entry instead of 4 per column.
+// Every value of hc is produced by the same operations, in the same order,
+// as the dense state's value at that column, so the picks are the dense
+// kernel's picks:
+//   min over supp(t2) < 0   -> that minimum (the dense rule);
+//   otherwise the minimum is 0 if any column holds 0: the lowest column
+//   outside cov and supp(t2), or of supp(t2) with hc == 0.
+// A cell leaves this path (it is queued for the dense kernel, which redoes
+// it from the start) on anything the support state cannot represent: a
+// negative product, a K2B row longer than hc_cap or not strictly ascending,
+// a malformed row or index, a scale fold, a step with no zero and a
+// positive minimum, or an invalid step size.
+// base[byte_off / sizeof(T)] with a 32-bit byte offset from a wave-uniform
+// base: one offset register serves loads from several arrays (valid while
+// the array holds fewer than 2^30 four-byte entries).
+template <typename T>
+__device__ __forceinline__ T load_at(const T *__restrict__ base, uint32_t byte_off) {
+  return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
+constexpr uint32_t kSupT2Regs = 4;  // chunks of 64 t2 entries held in registers
+constexpr uint32_t kRowBatch = 2;   // chunks of a t1 row whose loads are in flight together
+
+__global__ void __launch_bounds__(kABlockMaxThreads)
+    fw_a_support_kernel(const uint32_t *__restrict__ t1_ptr, const uint32_t *__restrict__ t1_idx,
+                        const float *__restrict__ t1_val, uint32_t t1_nnz,
+                        const uint32_t *__restrict__ k2b_ptr, const uint32_t *__restrict__ k2b_idx,
+                        const float *__restrict__ k2b_val, uint32_t k2b_nnz,
+                        const uint32_t *__restrict__ ap_ptr, const uint32_t *__restrict__ ap_idx,
+                        const float *__restrict__ ap_val, uint32_t ap_nnz, uint32_t n,
+                        uint32_t k, uint32_t T, uint32_t cap, const float *__restrict__ gamma,
+                        uint32_t *__restrict__ atom_idx, float *__restrict__ atom_val,
+                        uint32_t *__restrict__ atom_cnt, uint32_t *__restrict__ trace,
+                        uint32_t nwords, uint32_t hc_cap, uint32_t sched_words,
+                        uint32_t lds_words_per_wave, uint32_t *__restrict__ defer_cnt,
+                        uint32_t *__restrict__ defer_list, uint32_t *__restrict__ status) {
+  extern __shared__ uint32_t lds[];
+  const uint32_t lane = lane_id();
+  const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+
+  // -- the step schedule, once per block (the dense kernel reports its flags)
+  const StepSched *sched = reinterpret_cast<const StepSched *>(lds);
+  if (threadIdx.x == 0) {
+    StepSched *w = reinterpret_cast<StepSched *>(lds);
+    float s = 1.0f;
+    uint32_t f = 0;
+    for (uint32_t t = 0; t < T; ++t) w[t] = sched_step(gamma, t, s, f);
+    lds[sched_words - 1] = f;
+  }
+  __syncthreads();
+  const bool sched_ok = lds[sched_words - 1] == 0u;
+  uint32_t flags = 0;
+
+  uint32_t *wl = lds + sched_words + (size_t)wib * lds_words_per_wave;
+  uint2 *rec = reinterpret_cast<uint2 *>(wl);     // nwords + 1 (the last one stays 0)
+  uint32_t *cov = wl + 2 * (nwords + 1);           // nwords + 1
+  float *hc = reinterpret_cast<float *>(cov + nwords + 1);  // hc_cap + one dummy per lane
+  const uint32_t pad_bits = (k & 31u) != 0u ? ~((1u << (k & 31u)) - 1u) : 0u;
+  const float inf = __builtin_inff();
+
+  // h += alpha * t1[p0:p1] (one row of t1) on supp(t2); marks the other
+  // columns that receive a non-zero product when `cover`. The loads of up
+  // to kRowBatch chunks are issued before any is used. Returns true when
+  // the row cannot be handled here (a bad index or a negative value).
+  // Each lane owns one dummy slot past the state (value 0, only ever given
+  // +0) and one all-zero bitmap word past the real ones, so lanes without an
+  // entry take the same path as the others and no branch splits the batch.
+  float *hdummy = hc + hc_cap + lane;
+  const uint32_t cdummy = nwords * 32u;  // column of the all-zero word
+
+  // h += alpha * t1[p0:p1] (one row of t1) on supp(t2); marks the other
+  // columns that receive a non-zero product when `cover`. All loads of a
+  // batch of kRowBatch chunks are in flight together, then all bitmap
+  // lookups, then all state reads, then the writes (the positions of one
+  // row are distinct). Returns true when the row cannot be handled here (a
+  // bad index or a negative value).
+  auto scatter_row = [&](uint32_t p0, uint32_t p1, float alpha, bool cover,
+                         uint32_t nq) -> bool {
+    const uint32_t nit = (p1 - p0 + kWave - 1) / kWave;
+    bool lane_bad = false;
+    for (uint32_t i0 = 0; i0 < nit; i0 += kRowBatch) {
+      uint32_t cc[kRowBatch];
+      float vv[kRowBatch];
+#pragma unroll
+      for (uint32_t b = 0; b < kRowBatch; ++b) {
+        const uint32_t p = p0 + (i0 + b) * kWave + lane;
+        const uint32_t pc = (i0 + b < nit && p < p1) ? p : p0;  // in range; dropped below
+        cc[b] = load_at(t1_idx, pc * 4u);
+        vv[b] = load_at(t1_val, pc * 4u);
+      }
+      uint2 rw[kRowBatch];
+#pragma unroll
+      for (uint32_t b = 0; b < kRowBatch; ++b) {
+        const uint32_t p = p0 + (i0 + b) * kWave + lane;
+        const bool valid = i0 + b < nit && p < p1;
+        lane_bad |= valid && (cc[b] >= k || vv[b] < 0.0f);
+        if (!valid || cc[b] >= k) cc[b] = cdummy, vv[b] = 0.0f;
+        rw[b] = rec[cc[b] >> 5];
+      }
+      float *hp[kRowBatch];
+      float hv[kRowBatch];
+      bool in_t2[kRowBatch];
+#pragma unroll
+      for (uint32_t b = 0; b < kRowBatch; ++b) {
+        const uint32_t bit = 1u << (cc[b] & 31u);
+        const uint32_t pos = rw[b].y + __popc(rw[b].x & (bit - 1u));
+        in_t2[b] = (rw[b].x & bit) != 0u && pos < nq;
+        hp[b] = in_t2[b] ? hc + pos : hdummy;
+        hv[b] = *hp[b];
+      }
+#pragma unroll
+      for (uint32_t b = 0; b < kRowBatch; ++b)
+        *hp[b] = __builtin_fmaf(alpha, in_t2[b] ? vv[b] : 0.0f, hv[b]);
+      if (cover) {
+#pragma unroll
+        for (uint32_t b = 0; b < kRowBatch; ++b)
+          if (!in_t2[b] && alpha * vv[b] != 0.0f) atomicOr(&cov[cc[b] >> 5], 1u << (cc[b] & 31u));
+      }
+    }
+    return __ballot(lane_bad) != 0;
+  };
+
+  uint32_t *work = defer_cnt + 1;  // next cell to take
+  for (;;) {
+    // cells are taken one at a time from a counter: no block waits for a
+    // slot while others idle, and expensive cells spread by themselves
+    uint32_t cell = 0;
+    if (lane == 0) cell = atomicAdd(work, 1u);
+    cell = __builtin_amdgcn_readfirstlane(cell);
+    if (cell >= n) break;
+    wave_lds_sync();
+    const uint32_t q0 = k2b_ptr[cell], q1 = k2b_ptr[cell + 1];
+    const uint32_t s0 = ap_ptr[cell], s1 = ap_ptr[cell + 1];
+    bool deferred = !sched_ok || q1 > k2b_nnz || q0 > q1 || q1 - q0 > hc_cap ||
+                    s1 > ap_nnz || s0 > s1 || s1 - s0 > cap;
+    const uint32_t nq = deferred ? 0u : q1 - q0;
+
+    uint32_t t2c[kSupT2Regs];
+    float t2v[kSupT2Regs];
+    const uint32_t nchq = (nq + kWave - 1) / kWave;
+    const uint32_t nchr = nchq < kSupT2Regs ? nchq : kSupT2Regs;
+    if (!deferred) {
+      // -- clear the words and the state
+      for (uint32_t w = lane; w <= nwords; w += kWave) {
+        rec[w] = make_uint2(0u, 0u);
+        cov[w] = (w == nwords - 1u) ? pad_bits : 0u;
+      }
+      for (uint32_t p = lane; p < nq; p += kWave) hc[p] = 0.0f;
+      *hdummy = 0.0f;
+      wave_lds_sync();
+      // -- supp(t2) bits and first positions; the first chunks also go to registers
+      bool bad = false;
+      auto add_entry = [&](uint32_t p, uint32_t &c, float &v) {
+        c = kNone;
+        v = 0.0f;
+        if (p < nq) {
+          c = k2b_idx[q0 + p];
+          v = k2b_val[q0 + p];
+          const uint32_t prev = p > 0u ? k2b_idx[q0 + p - 1u] : kNone;
+          if (c >= k || (p > 0u && prev >= c)) {
+            bad = true;
+          } else {
+            atomicOr(&rec[c >> 5].x, 1u << (c & 31u));
+            if (p == 0u || (prev >> 5) != (c >> 5)) rec[c >> 5].y = p;
+          }
+        }
+      };
+#pragma unroll
+      for (uint32_t r = 0; r < kSupT2Regs; ++r) {
+        t2c[r] = kNone;
+        t2v[r] = 0.0f;
+        if (r < nchr) add_entry(r * kWave + lane, t2c[r], t2v[r]);
+      }
+      for (uint32_t i = nchr; i < nchq; ++i) {
+        uint32_t c;
+        float v;
+        add_entry(i * kWave + lane, c, v);
+      }
+      deferred = __ballot(bad) != 0;
+    }
+    wave_lds_sync();
+
+    // -- atoms from A_prev's column, each with the range of its t1 row
+    uint32_t cnt = deferred ? 0u : s1 - s0;
+    uint32_t aidx[kWaveAtomSlots], arow0[kWaveAtomSlots], arow1[kWaveAtomSlots];
+    float aval[kWaveAtomSlots];
+    bool bad_seed = false;
+#pragma unroll
+    for (uint32_t j = 0; j < kWaveAtomSlots; ++j) {
+      const uint32_t s = j * kWave + lane;
+      aidx[j] = kNone;
+      aval[j] = 0.0f;
+      arow0[j] = arow1[j] = 0u;
+      if (s < cnt) {
+        const uint32_t m = ap_idx[s0 + s];
+        aidx[j] = m;
+        aval[j] = ap_val[s0 + s];
+        if (m >= k || aval[j] < 0.0f) {
+          bad_seed = true;
+        } else {
+          arow0[j] = t1_ptr[m];
+          arow1[j] = t1_ptr[m + 1];
+          if (arow1[j] > t1_nnz || arow0[j] > arow1[j]) bad_seed = true;
+        }
+      }
+    }
+    if (__ballot(bad_seed) != 0) deferred = true;
+    // -- h = t1 . a_prev, seed by seed in A_prev order
+    for (uint32_t s = 0; s < cnt && !deferred; ++s) {
+      const uint32_t j = s / kWave, l = s % kWave;
+      uint32_t p0 = 0, p1 = 0;
+      float am = 0.0f;
+#pragma unroll
+      for (uint32_t jj = 0; jj < kWaveAtomSlots; ++jj) {
+        if (jj == j) {
+          p0 = readlane_u32(arow0[jj], l);
+          p1 = readlane_u32(arow1[jj], l);
+          am = readlane_f32(aval[jj], l);
+        }
+      }
+      deferred = scatter_row(p0, p1, am, true, nq);
+      wave_lds_sync();
+    }
+
+    // -- h -= alpha * t2, and the minimum of h over supp(t2) (lowest column)
+    float mval = inf;
+    uint32_t midx = kNone;
+    auto t2_pass = [&](float alpha) {
+      float bv = inf;
+      uint32_t bi = kNone, br = 0;
+      float *tp[kSupT2Regs];
+      float tv[kSupT2Regs];
+#pragma unroll
+      for (uint32_t r = 0; r < kSupT2Regs; ++r) {
+        if (r < nchr) {
+          const uint32_t p = r * kWave + lane;
+          tp[r] = p < nq ? hc + p : hdummy;
+          tv[r] = *tp[r];
+        }
+      }
+#pragma unroll
+      for (uint32_t r = 0; r < kSupT2Regs; ++r) {
+        if (r < nchr) {
+          const float hn = __builtin_fmaf(-alpha, t2v[r], tv[r]);
+          *tp[r] = hn;
+          const float cand = t2c[r] != kNone ? hn : inf;
+          if (cand < bv) bv = cand, bi = t2c[r], br = r;
+        }
+      }
+      uint32_t nr = nchr;
+      for (uint32_t pb = kSupT2Regs * kWave; pb < nq; pb += kWave, ++nr) {
+        const uint32_t p = pb + lane;
+        if (p < nq) {
+          const float hn = __builtin_fmaf(-alpha, k2b_val[q0 + p], hc[p]);
+          hc[p] = hn;
+          if (hn < bv) bv = hn, bi = k2b_idx[q0 + p], br = nr;
+        }
+      }
+      const uint32_t key = f32_order(bv);
+      const uint32_t best = wave_min_u32(key);
+      mval = f32_unorder(best);
+      midx = kNone;
+      for (uint32_t r = 0; r < nr; ++r) {
+        const uint64_t m = __ballot(key == best && br == r && bi != kNone);
+        if (m != 0) {
+          midx = readlane_u32(bi, (uint32_t)__builtin_ctzll(m));
+          break;
+        }
+      }
+    };
+    if (!deferred) t2_pass(1.0f);
+    wave_lds_sync();
+
+    uint32_t acov = 0;  // bit j: the row of the atom in slot j is marked in cov
+    for (uint32_t t = 0; t < T && !deferred; ++t) {
+      const StepSched sc = sched[t];
+      if (sc.fold > 0.0f) {
+        deferred = true;
+        break;
+      }
+      // -- argmin
+      uint32_t idx = midx;
+      if (!(mval < 0.0f)) {
+        uint32_t cand = kNone;
+        for (uint32_t w0 = 0; w0 < nwords; w0 += kWave) {
+          const uint32_t w = w0 + lane;
+          if (w < nwords && cand == kNone) {
+            const uint32_t z = ~(rec[w].x | cov[w]);
+            if (z != 0u) cand = w * 32u + (uint32_t)__builtin_ctz(z);
+          }
+        }
+        cand = wave_min_u32(cand);
+        if (mval == 0.0f && midx < cand) cand = midx;
+        if (cand == kNone) {  // every column positive: only a dense scan decides
+          deferred = true;
+          break;
+        }
+        idx = cand;
+      }
+      if (trace != nullptr && lane == 0) trace[(size_t)cell * T + t] = idx;
+
+      // -- atoms: scale every weight, add gamma at idx or append idx
+      const bool restart = sc.keep == 0.0f;
+      if (restart) acov = 0;
+      bool hit = false, fresh = false;
+      uint32_t hp0 = 0, hp1 = 0;
+#pragma unroll
+      for (uint32_t j = 0; j < kWaveAtomSlots; ++j) {
+        const bool at = aidx[j] == idx;
+        aval[j] = at ? __builtin_fmaf(aval[j], sc.keep, sc.gam) : aval[j] * sc.keep;
+        if (at) {
+          hit = true;
+          fresh = ((acov >> j) & 1u) == 0u;
+          acov |= 1u << j;
+          hp0 = arow0[j];
+          hp1 = arow1[j];
+        }
+      }
+      bool cover = __ballot(fresh) != 0;
+      const uint64_t hits = __ballot(hit);
+      uint32_t p0, p1;
+      if (hits != 0) {
+        const uint32_t hl = (uint32_t)__builtin_ctzll(hits);
+        p0 = readlane_u32(hp0, hl);
+        p1 = readlane_u32(hp1, hl);
+      } else {
+        cover = true;
+        p0 = t1_ptr[idx];
+        p1 = t1_ptr[idx + 1];
+        if (p1 > t1_nnz || p0 > p1) {
+          deferred = true;
+          break;
+        }
+        if (cnt < cap) {
+          const uint32_t j = cnt / kWave, l = cnt % kWave;
+#pragma unroll
+          for (uint32_t jj = 0; jj < kWaveAtomSlots; ++jj)
+            if (jj == j && lane == l)
+              aidx[jj] = idx, aval[jj] = sc.gam, arow0[jj] = p0, arow1[jj] = p1,
+              acov |= 1u << jj;
+          ++cnt;
+        } else {
+          flags |= kFlagCapOverflow;
+        }
+      }
+
+      // -- state: restart when gamma == 1
+      if (restart) {
+        for (uint32_t p = lane; p < nq; p += kWave) hc[p] = 0.0f;
+        for (uint32_t w = lane; w < nwords; w += kWave)
+          cov[w] = (w == nwords - 1u) ? pad_bits : 0u;
+      }
+      wave_lds_sync();
+      // -- h += alpha * t1[idx, :]
+      if (scatter_row(p0, p1, sc.alpha, cover, nq)) {
+        deferred = true;
+        break;
+      }
+      wave_lds_sync();
+      // -- h -= alpha * t2
+      t2_pass(sc.alpha);
+      wave_lds_sync();
+    }
+
+    if (deferred) {
+      // the dense kernel redoes this cell from the start (and writes all of it)
+      if (lane == 0) {
+        const uint32_t slot = atomicAdd(defer_cnt, 1u);
+        defer_list[slot] = cell;
+      }
+      continue;
+    }
+    // -- write the atoms
+    const size_t base = (size_t)cell * cap;
+#pragma unroll
+    for (uint32_t j = 0; j < kWaveAtomSlots; ++j) {
+      const uint32_t s = j * kWave + lane;
+      if (s < cnt) {
+        atom_idx[base + s] = aidx[j];
+        atom_val[base + s] = aval[j];
+      }
+    }
+    if (lane == 0) atom_cnt[cell] = cnt;
+  }
+  if (flags != 0) atomicOr(status, flags);
+}
+
+__global__ void zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
+  if (threadIdx.x < count) p[threadIdx.x] = 0u;
+}
+
 template <uint32_t G, bool kHInLds, bool kRegAtoms>
 hipError_t launch_variant(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr k2b, Csr ap,
                           uint32_t n, uint32_t k, uint32_t T, uint32_t cap, const float *gamma,
                           uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
-                          uint32_t *trace, void *ws, uint32_t dense_only, uint32_t *status,
-                          hipStream_t stream) {
+                          uint32_t *trace, void *ws, uint32_t dense_only,
+                          const uint32_t *cell_list, const uint32_t *cell_count,
+                          uint32_t *status, hipStream_t stream) {
   static bool configured = false;
   auto kern = [] {
     if constexpr (G == kWave)
@@ -800,17 +1214,81 @@ hipError_t launch_variant(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr 
   } else {
     blocks = plan.global_waves / wpb;  // each wave owns workspace slices
   }
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads),
-                     lds_bytes, stream, t1.ptr, t1.idx, t1.val, t1.nnz, k2b.ptr, k2b.idx,
-                     k2b.val, k2b.nnz, ap.ptr, ap.idx, ap.val, ap.nnz, n, k, plan.kpad, T, cap,
-                     gamma, atom_idx, atom_val, atom_cnt, trace, static_cast<float *>(ws),
-                     plan.sched_words, plan.lds_per_wave / 4, dense_only, status);
+  float *state_ws = reinterpret_cast<float *>(static_cast<char *>(ws) + plan.ws_dense_off);
+  if constexpr (G == kWave) {
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr, t1.idx,
+                       t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
+                       ap.val, ap.nnz, n, k, plan.kpad, T, cap, gamma, atom_idx, atom_val,
+                       atom_cnt, trace, state_ws, plan.sched_words, plan.lds_per_wave / 4,
+                       dense_only, cell_list, cell_count, status);
+  } else {
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr, t1.idx,
+                       t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
+                       ap.val, ap.nnz, n, k, plan.kpad, T, cap, gamma, atom_idx, atom_val,
+                       atom_cnt, trace, state_ws, plan.sched_words, plan.lds_per_wave / 4,
+                       dense_only, status);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr k2b, Csr ap,
+                          uint32_t n, uint32_t k, uint32_t T, uint32_t cap, const float *gamma,
+                          uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
+                          uint32_t *trace, uint32_t *defer_cnt, uint32_t *defer_list,
+                          uint32_t *status, hipStream_t stream) {
+  static bool configured = false;
+  auto fn = reinterpret_cast<const void *>(&fw_a_support_kernel);
+  const uint32_t wpb = plan.sup_waves_per_block;
+  const uint32_t threads = wpb * kWave;
+  const uint32_t lds_bytes = plan.sched_words * 4 + wpb * plan.sup_lds_per_wave;
+  hipError_t e;
+  if (!configured) {
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytesPerCU);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  int bpc = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, threads, lds_bytes);
+  if (e != hipSuccess) return e;
+  if (bpc < 1) bpc = 1;
+  const uint64_t want = ((uint64_t)n + wpb - 1) / wpb;
+  const uint64_t cap_blocks = (uint64_t)dev.cus * (uint64_t)bpc;
+  const uint32_t blocks = (uint32_t)(want < cap_blocks ? want : cap_blocks);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, defer_cnt, 2u);
+  hipLaunchKernelGGL(fw_a_support_kernel, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr,
+                     t1.idx, t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
+                     ap.val, ap.nnz, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt, trace,
+                     plan.nwords, plan.hc_cap, plan.sched_words, plan.sup_lds_per_wave / 4,
+                     defer_cnt, defer_list, status);
   return hipGetLastError();
 }
 
 bool dense_only_requested() {
   const char *v = getenv("SEACELLS_A_DENSE_ARGMIN");
   return v != nullptr && v[0] == '1';
+}
+
+constexpr uint32_t kSupportMinK = 2048;     // support state from this k on
+constexpr uint32_t kSupWavesPerBlock = 4;
+constexpr uint32_t kSupDefaultWaves = 24;   // resident waves per CU the LDS is sized for
+constexpr uint32_t kSupMinHc = 256;         // smallest useful t2 capacity
+constexpr uint32_t kSupMaxHc = 8192;
+
+// SEACELLS_A_SUPPORT: "0" never uses the support state, "1" uses it for any
+// k (experiments and tests); unset: by k.
+int support_mode() {
+  const char *v = getenv("SEACELLS_A_SUPPORT");
+  if (v == nullptr || v[0] == 0) return -1;
+  return v[0] == '0' ? 0 : 1;
+}
+
+uint32_t support_waves_per_cu() {
+  const char *v = getenv("SEACELLS_A_SUPPORT_WAVES");
+  if (v != nullptr) {
+    const int w = atoi(v);
+    if (w >= 4 && w <= 32) return (uint32_t)w;
+  }
+  return kSupDefaultWaves;
 }
 
 // Lanes per cell: from the environment for experiments, else by k.
@@ -846,7 +1324,6 @@ APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap) {
     p.waves_per_block = w >= 4 ? 4 : (w >= 2 ? 2 : 1);
     p.global_waves = 0;
     p.ws_words_per_wave = 0;
-    p.ws_bytes = 0;
   } else {
     p.h_in_lds = false;
     p.lds_per_wave = (uint32_t)(atom_words * 4);
@@ -857,8 +1334,42 @@ APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap) {
     const uint32_t gw = (cells + cpw - 1) / cpw;
     p.global_waves = (gw + p.waves_per_block - 1) / p.waves_per_block * p.waves_per_block;
     p.ws_words_per_wave = cpw * p.kpad;
-    p.ws_bytes = align_up((size_t)p.global_waves * p.ws_words_per_wave * 4, 256);
   }
+  const size_t dense_ws = p.h_in_lds ? 0 : (size_t)p.global_waves * p.ws_words_per_wave * 4;
+
+  // support state for large k: picks equal to the dense kernel's (cells it
+  // cannot settle are queued for the dense kernel)
+  p.support = false;
+  const int mode = support_mode();
+  if (mode != 0 && p.group == kWave && p.reg_atoms && p.sched_words != 0 &&
+      !dense_only_requested() && (mode == 1 || k >= kSupportMinK)) {
+    p.nwords = (k + 31u) / 32u;
+    const uint32_t target = support_waves_per_cu();
+    const uint32_t blocks = (target + kSupWavesPerBlock - 1) / kSupWavesPerBlock;
+    const size_t per_block = kLdsBytesPerCU / blocks;
+    const size_t sched_b = (size_t)p.sched_words * 4;
+    const size_t per_wave = per_block > sched_b ? (per_block - sched_b) / kSupWavesPerBlock : 0;
+    const size_t fixed = ((size_t)p.nwords + 1) * 12 + (size_t)kWave * 4;
+    if (per_wave >= fixed + 4 * kSupMinHc) {
+      size_t hc = (per_wave - fixed) / 4;
+      hc = hc / 64 * 64;
+      if (hc > kSupMaxHc) hc = kSupMaxHc;
+      p.hc_cap = (uint32_t)hc;
+      p.sup_lds_per_wave =
+          (uint32_t)(align_up(((size_t)p.nwords + 1) * 3 + hc + kWave, 4) * 4);
+      p.sup_waves_per_block = kSupWavesPerBlock;
+      p.support = true;
+    }
+  }
+  // workspace: [deferred-cell counter | deferred-cell list | dense state slices]
+  if (p.support) {
+    p.ws_list_off = 256;
+    p.ws_dense_off = align_up(p.ws_list_off + (size_t)n * 4, 256);
+  } else {
+    p.ws_list_off = 0;
+    p.ws_dense_off = 0;
+  }
+  p.ws_bytes = dense_ws > 0 || p.support ? align_up(p.ws_dense_off + dense_ws, 256) : 0;
   return p;
 }
 
@@ -870,9 +1381,20 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
   const uint32_t dense_only = dense_only_requested() ? 1u : 0u;
+  const uint32_t *cell_list = nullptr, *cell_count = nullptr;
+  // the support kernel addresses t1 with 32-bit byte offsets
+  if (plan.support && t1.nnz < (1u << 30)) {
+    uint32_t *cnt = static_cast<uint32_t *>(ws);
+    uint32_t *list = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + plan.ws_list_off);
+    e = launch_support(plan, dev, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
+                       atom_cnt, trace, cnt, list, status, stream);
+    if (e != hipSuccess) return e;
+    cell_list = list;
+    cell_count = cnt;
+  }
 #define SEACELLS_A_ARGS \
   plan, dev, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt, trace, ws, \
-      dense_only, status, stream
+      dense_only, cell_list, cell_count, status, stream
 #define SEACELLS_A_GROUP(GW)                                                                \
   if (plan.group == GW) {                                                                   \
     if (plan.h_in_lds)                                                                      \

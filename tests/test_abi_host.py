@@ -67,9 +67,13 @@ def test_a_columns_rejects_bad_arguments_on_host():
     assert call_a(t1, bad, ap, n, k, T, cap) == -1
 
 
-def test_a_columns_workspace_only_when_state_leaves_lds():
+def test_a_columns_workspace_sizes():
+    # dense state in LDS: no workspace
     assert saa.seacells_fw_a_columns_workspace(1000, 1300, 50, 60) == 0
-    assert saa.seacells_fw_a_columns_workspace(1000, 10000, 50, 66) == 0
+    # support state (large k): a counter and the queue of cells left to the dense kernel
+    sup = saa.seacells_fw_a_columns_workspace(1000, 10000, 50, 66)
+    assert sup >= 256 + 1000 * 4 and sup % 256 == 0
+    # k too large for either state in LDS: dense state slices in the workspace
     big = saa.seacells_fw_a_columns_workspace(1000, 60000, 50, 66)
     assert big >= 1000 * 60000 * 4 and big % 256 == 0
     # a large-k call without that workspace is refused on the host

@@ -201,3 +201,60 @@ def test_lane_group_widths_agree_bitwise(monkeypatch):
     assert_same_result(res["16"], res["32"])
     assert_same_result(res["16"], res["64"])
     parity.check_a(w, res["32"][3], res["32"][0], res["32"][1], res["32"][2], np.arange(w.n))
+
+
+def _support_case(name):
+    if name in ("c1", "c2", "c3"):
+        return W.make(name), {}
+    if name == "empty":
+        return W.random_workload(300, 40, s_a=3, seed=9, empty_k2b_every=3, empty_ap_every=4), {}
+    if name == "signed":      # every cell leaves the support path at its first negative product
+        return W.random_workload(400, 333, t1_per_row=12, k2b_per_row=9, s_a=7, seed=5,
+                                 signed=True), {}
+    if name == "long_rows":   # K2B rows from 0 to 1600 entries: some exceed the support capacity
+        return W.random_workload(200, 3000, t1_per_row=40, k2b_per_row=800, s_a=6, seed=29), {}
+    if name == "fold":        # the running scale is folded back: those cells go to the dense kernel
+        w = W.make("c1")
+        gam = np.full(120, 0.55, np.float32)
+        gam[0] = 1.0
+        return w, {"T": 120, "cap": w.cap - w.T + 120, "gamma": gam}
+    if name == "restarts":    # gamma = 1 every 7 steps: support state and marks restart
+        w = W.make("c2")
+        gam = (2.0 / (np.arange(60) % 7 + 2.0)).astype(np.float32)
+        return w, {"T": 60, "cap": w.cap - w.T + 60, "gamma": gam}
+    if name == "bad_gamma":
+        w = W.make("c1")
+        gam = np.full(w.T, 0.5, np.float32)
+        gam[3] = 1.5
+        return w, {"gamma": gam}
+    if name == "cap_overflow":
+        return W.make("c1"), {"cap": 12}
+    raise KeyError(name)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "empty", "signed", "long_rows", "fold",
+                                  "restarts", "bad_gamma", "cap_overflow"])
+def test_support_state_equals_dense_kernel(name, monkeypatch):
+    # The support state (h kept on supp(t2) only, plus bitmaps) must give the
+    # dense kernel's results bit for bit; cells it cannot settle are redone by
+    # the dense kernel. Forced on here for every k, with one cell per wave.
+    w, kw = _support_case(name)
+    ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
+    monkeypatch.setenv("SEACELLS_A_GROUP", "64")
+    monkeypatch.setenv("SEACELLS_A_SUPPORT", "0")
+    dense = run_a(w, ops=ops, **kw)
+    monkeypatch.setenv("SEACELLS_A_SUPPORT", "1")
+    for waves in ("20", "32"):    # two support capacities
+        monkeypatch.setenv("SEACELLS_A_SUPPORT_WAVES", waves)
+        sup = run_a(w, ops=ops, **kw)
+        assert sup[4] == dense[4]
+        assert_same_result(dense, sup)
+    if name in ("c1", "c2", "empty", "long_rows"):
+        parity.check_a(w, sup[3], sup[0], sup[1], sup[2], np.arange(w.n))
+
+
+def test_support_state_is_the_default_for_large_k():
+    import sparse_archetypal_analysis_amd as saa
+    # the workspace then carries the queue of cells left to the dense kernel
+    assert saa.seacells_fw_a_columns_workspace(1000, 6700, 50, 62) >= 1000 * 4
+    assert saa.seacells_fw_a_columns_workspace(1000, 1300, 50, 60) == 0

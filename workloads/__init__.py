@@ -188,9 +188,10 @@ def _kernel(X, knn):
     cols = nb.ravel()
     w = np.exp(-d2.ravel() / (sig[rows] * sig[cols]))
     W = sp.csr_matrix((w, (rows, cols)), shape=(n, n))
-    K = ((W + W.T) * 0.5).tolil()
-    K.setdiag(1.0)
-    K = K.tocsr()
+    # the cell itself is excluded from its neighbours, so the diagonal of W
+    # is structurally empty and adding I sets K_ii = 1
+    K = ((W + W.T) * 0.5 + sp.identity(n, format="csr")).tocsr()
+    K.sum_duplicates()
     K.sort_indices()
     return K
 
@@ -251,24 +252,36 @@ def _sha(*arrays):
     return h.hexdigest()
 
 
-def generate(cfg: Config, seed: int = 0) -> Workload:
+def _progress(log, what, t0):
+    if log is not None:
+        log("[workload] %s done at %.1f s" % (what, time.time() - t0))
+
+
+def generate(cfg: Config, seed: int = 0, log=None) -> Workload:
+    """Build one workload. ``log`` (optional) receives one line per stage."""
     t0 = time.time()
     rng = np.random.default_rng(1000 * cfg.index + seed)
     X, labels = _points(cfg, rng)
     t_pts = time.time()
+    _progress(log, "points", t0)
     K = _kernel(X, cfg.knn)
     t_knn = time.time()
+    _progress(log, "kNN kernel (%d nnz)" % K.nnz, t0)
     init = rng.choice(cfg.n, size=cfg.k, replace=False)
     B = _b_matrix(cfg, rng, labels, init)
     At = _a_prev_t(cfg, rng, X, init)
+    _progress(log, "B and A_prev", t0)
     K2B = K @ (K @ B)
     t1 = B.T @ K2B
+    _progress(log, "K2B and t1", t0)
     K2At = K @ (K @ At)
     AAt = At.T @ At
+    _progress(log, "K2At and AAt", t0)
     w = Workload(cfg, seed, t1=_f32(t1, symmetric=True), k2b=_f32(K2B), a_prev_t=_f32(At),
                  aat=_f32(AAt, symmetric=True), k2at=_f32(K2At), b=_f32(B),
                  init_cells=np.asarray(init, np.int64))
     t_end = time.time()
+    _progress(log, "f32 operands", t0)
     w.meta = {
         "generator_version": GENERATOR_VERSION,
         "config": asdict(cfg),
@@ -318,11 +331,15 @@ def _load(cfg: Config, seed: int, path) -> Workload:
     return Workload(cfg, seed, init_cells=z["init_cells"], meta=meta, **mats)
 
 
-def make(name_or_cfg, seed: int = 0, cache: bool = True) -> Workload:
-    """The workload for a named config ("c1".."c5") or a custom Config."""
+def make(name_or_cfg, seed: int = 0, cache: bool = True, log=None) -> Workload:
+    """The workload for a named config ("c1".."c5") or a custom Config.
+
+    ``log`` (optional, e.g. a print to stderr) receives one line per stage
+    when the workload has to be generated.
+    """
     cfg = CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
     if not cache:
-        return generate(cfg, seed)
+        return generate(cfg, seed, log)
     key = "%s_n%d_k%d_s%d_v%d.npz" % (cfg.name, cfg.n, cfg.k, seed, GENERATOR_VERSION)
     path = os.path.join(cache_dir(), key)
     if os.path.exists(path) and os.path.exists(path + ".json"):
@@ -330,7 +347,7 @@ def make(name_or_cfg, seed: int = 0, cache: bool = True) -> Workload:
             meta = json.load(f)
         if meta.get("config") == json.loads(json.dumps(asdict(cfg))):
             return _load(cfg, seed, path)
-    w = generate(cfg, seed)
+    w = generate(cfg, seed, log)
     _save(w, path)
     return w
 
