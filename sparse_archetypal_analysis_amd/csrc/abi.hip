@@ -106,7 +106,7 @@ int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
 
 size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k) {
   if (n == 0 || k == 0) return 0;
-  return plan_b(n, k).ws_bytes;
+  return b_workspace_bound(n, k);
 }
 
 int seacells_fw_b_argmin(const seacells_csr *k2b, const seacells_csr *aat,
@@ -123,7 +123,7 @@ int seacells_fw_b_argmin(const seacells_csr *k2b, const seacells_csr *aat,
   if ((rc = check_csr(aat, k, k)) != SEACELLS_OK) return rc;
   if ((rc = check_csr(k2at, n, k)) != SEACELLS_OK) return rc;
   if (b != nullptr && (rc = check_csr(b, n, k)) != SEACELLS_OK) return rc;
-  const BPlan plan = plan_b(n, k);
+  const BPlan plan = plan_b(n, k, aat->nnz);
   if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return SEACELLS_E_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SEACELLS_E_WORKSPACE;
   Csr bc{};

@@ -130,10 +130,8 @@ struct APlan {
   // kernel above takes the cells it queues
   bool support;
   uint32_t nwords;             // 32-column words of the bitmaps
-  uint32_t hc_cap;             // longest K2B row the support state holds
-  uint32_t sup_lds_per_wave;   // bytes
-  uint32_t sup_waves_per_block;
-  size_t ws_list_off;          // queued cells (the counter sits at offset 0)
+  size_t ws_list_off;          // cells for the long-row pass (counters sit at offset 0)
+  size_t ws_list2_off;         // cells for the dense kernel
   size_t ws_dense_off;         // dense state slices
   size_t ws_bytes;
 };
@@ -145,14 +143,15 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
 
 // --- B argmin -------------------------------------------------------------
 struct BPlan {
-  uint32_t s4;            // float4 column chunks per lane in one slice
-  uint32_t slice_w;       // columns per slice = 256 * s4
+  uint32_t s4;            // float4 column chunks per lane of the accumulator
+  uint32_t slice_w;       // columns per slice (<= 256 * s4)
   uint32_t n_slices;
   uint32_t n_row_blocks;  // row ranges; one work unit = (row range, slice)
   uint32_t n_chunks;      // row-range groups of the first reduce stage
   size_t off_keys, off_part2, off_gap, off_stamp, off_seg, ws_bytes;
 };
-BPlan plan_b(uint32_t n, uint32_t k);
+BPlan plan_b(uint32_t n, uint32_t k, uint64_t aat_nnz);
+size_t b_workspace_bound(uint32_t n, uint32_t k);  // over every aat_nnz
 hipError_t launch_fw_b(const BPlan &plan, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
                        uint32_t k, float *out_val, uint32_t *out_idx, float *gap, void *ws,
                        uint32_t *status, uint32_t epoch, hipStream_t stream);

@@ -50,6 +50,13 @@ constexpr uint32_t kSchedMax = 256;   // steps whose schedule is tabulated in LD
 constexpr uint32_t kT2Regs = 4;       // chunks of G t2 entries held in registers
 constexpr uint32_t kRegAtomMax = 128; // atoms per cell held in registers
 constexpr uint32_t kNone = 0xffffffffu;
+constexpr uint32_t kSupportMinK = 2048;     // support state from this k on
+constexpr uint32_t kSupWavesPerBlock = 4;
+constexpr uint32_t kSupDefaultWaves = 24;   // resident waves per CU the LDS is sized for
+constexpr uint32_t kSupWideWaves = 16;      // the same with 512 t2 entries in registers
+constexpr uint32_t kSupLongWaves = 8;       // the same for the pass over long K2B rows
+constexpr uint32_t kSupMinHc = 256;         // smallest useful t2 capacity
+constexpr uint32_t kSupMaxHc = 8192;
 
 struct StepSched {
   float gam;    // gamma_t
@@ -798,6 +805,17 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
 // negative product, a K2B row longer than hc_cap or not strictly ascending,
 // a malformed row or index, a scale fold, a step with no zero and a
 // positive minimum, or an invalid step size.
+// Work lists of one support pass (device pointers into the workspace).
+struct SupQueues {
+  const uint32_t *in_list;  // cells to take, or nullptr for 0 .. n-1
+  const uint32_t *in_cnt;   // entries of in_list
+  uint32_t *work;           // next entry to take (starts at 0)
+  uint32_t *long_list;      // cells whose K2B row exceeds hc_cap, or nullptr: to dense_list
+  uint32_t *long_cnt;
+  uint32_t *dense_list;     // cells for the dense kernel
+  uint32_t *dense_cnt;
+};
+
 // base[byte_off / sizeof(T)] with a 32-bit byte offset from a wave-uniform
 // base: one offset register serves loads from several arrays (valid while
 // the array holds fewer than 2^30 four-byte entries).
@@ -806,9 +824,11 @@ __device__ __forceinline__ T load_at(const T *__restrict__ base, uint32_t byte_o
   return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 
-constexpr uint32_t kSupT2Regs = 4;  // chunks of 64 t2 entries held in registers
+constexpr uint32_t kTailPos = 0x80000000u;  // marks a t2 position (not a column) in the pass
 constexpr uint32_t kRowBatch = 2;   // chunks of a t1 row whose loads are in flight together
 
+// TR: chunks of 64 t2 entries held in registers (the rest are re-read).
+template <uint32_t TR>
 __global__ void __launch_bounds__(kABlockMaxThreads)
     fw_a_support_kernel(const uint32_t *__restrict__ t1_ptr, const uint32_t *__restrict__ t1_idx,
                         const float *__restrict__ t1_val, uint32_t t1_nnz,
@@ -820,8 +840,8 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
                         uint32_t *__restrict__ atom_idx, float *__restrict__ atom_val,
                         uint32_t *__restrict__ atom_cnt, uint32_t *__restrict__ trace,
                         uint32_t nwords, uint32_t hc_cap, uint32_t sched_words,
-                        uint32_t lds_words_per_wave, uint32_t *__restrict__ defer_cnt,
-                        uint32_t *__restrict__ defer_list, uint32_t *__restrict__ status) {
+                        uint32_t lds_words_per_wave, SupQueues q,
+                        uint32_t *__restrict__ status) {
   extern __shared__ uint32_t lds[];
   const uint32_t lane = lane_id();
   const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -908,25 +928,32 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
     return __ballot(lane_bad) != 0;
   };
 
-  uint32_t *work = defer_cnt + 1;  // next cell to take
+  uint32_t ncells = n;
+  if (q.in_list != nullptr) {
+    const uint32_t c = *q.in_cnt;
+    ncells = c < n ? c : n;
+  }
   for (;;) {
     // cells are taken one at a time from a counter: no block waits for a
     // slot while others idle, and expensive cells spread by themselves
-    uint32_t cell = 0;
-    if (lane == 0) cell = atomicAdd(work, 1u);
-    cell = __builtin_amdgcn_readfirstlane(cell);
-    if (cell >= n) break;
+    uint32_t slot = 0;
+    if (lane == 0) slot = atomicAdd(q.work, 1u);
+    slot = __builtin_amdgcn_readfirstlane(slot);
+    if (slot >= ncells) break;
+    const uint32_t cell = q.in_list != nullptr ? q.in_list[slot] : slot;
     wave_lds_sync();
     const uint32_t q0 = k2b_ptr[cell], q1 = k2b_ptr[cell + 1];
     const uint32_t s0 = ap_ptr[cell], s1 = ap_ptr[cell + 1];
-    bool deferred = !sched_ok || q1 > k2b_nnz || q0 > q1 || q1 - q0 > hc_cap ||
-                    s1 > ap_nnz || s0 > s1 || s1 - s0 > cap;
+    bool deferred = !sched_ok || q1 > k2b_nnz || q0 > q1 || s1 > ap_nnz || s0 > s1 ||
+                    s1 - s0 > cap;
+    const bool too_long = !deferred && q1 - q0 > hc_cap;
+    deferred = deferred || too_long;
     const uint32_t nq = deferred ? 0u : q1 - q0;
 
-    uint32_t t2c[kSupT2Regs];
-    float t2v[kSupT2Regs];
+    uint32_t t2c[TR];
+    float t2v[TR];
     const uint32_t nchq = (nq + kWave - 1) / kWave;
-    const uint32_t nchr = nchq < kSupT2Regs ? nchq : kSupT2Regs;
+    const uint32_t nchr = nchq < TR ? nchq : TR;
     if (!deferred) {
       // -- clear the words and the state
       for (uint32_t w = lane; w <= nwords; w += kWave) {
@@ -954,7 +981,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
         }
       };
 #pragma unroll
-      for (uint32_t r = 0; r < kSupT2Regs; ++r) {
+      for (uint32_t r = 0; r < TR; ++r) {
         t2c[r] = kNone;
         t2v[r] = 0.0f;
         if (r < nchr) add_entry(r * kWave + lane, t2c[r], t2v[r]);
@@ -1016,10 +1043,10 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
     auto t2_pass = [&](float alpha) {
       float bv = inf;
       uint32_t bi = kNone, br = 0;
-      float *tp[kSupT2Regs];
-      float tv[kSupT2Regs];
+      float *tp[TR];
+      float tv[TR];
 #pragma unroll
-      for (uint32_t r = 0; r < kSupT2Regs; ++r) {
+      for (uint32_t r = 0; r < TR; ++r) {
         if (r < nchr) {
           const uint32_t p = r * kWave + lane;
           tp[r] = p < nq ? hc + p : hdummy;
@@ -1027,7 +1054,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
         }
       }
 #pragma unroll
-      for (uint32_t r = 0; r < kSupT2Regs; ++r) {
+      for (uint32_t r = 0; r < TR; ++r) {
         if (r < nchr) {
           const float hn = __builtin_fmaf(-alpha, t2v[r], tv[r]);
           *tp[r] = hn;
@@ -1035,13 +1062,26 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
           if (cand < bv) bv = cand, bi = t2c[r], br = r;
         }
       }
+      // entries past the registers: values re-read from K2B (two chunks in
+      // flight), tracked by position; the column is read for the winner only
       uint32_t nr = nchr;
-      for (uint32_t pb = kSupT2Regs * kWave; pb < nq; pb += kWave, ++nr) {
-        const uint32_t p = pb + lane;
-        if (p < nq) {
-          const float hn = __builtin_fmaf(-alpha, k2b_val[q0 + p], hc[p]);
-          hc[p] = hn;
-          if (hn < bv) bv = hn, bi = k2b_idx[q0 + p], br = nr;
+      for (uint32_t pb = TR * kWave; pb < nq; pb += 2 * kWave, nr += 2) {
+        float tv2[2], hv2[2];
+        float *tp2[2];
+#pragma unroll
+        for (uint32_t b = 0; b < 2; ++b) {
+          const uint32_t p = pb + b * kWave + lane;
+          tv2[b] = p < nq ? k2b_val[q0 + p] : 0.0f;
+          tp2[b] = p < nq ? hc + p : hdummy;
+          hv2[b] = *tp2[b];
+        }
+#pragma unroll
+        for (uint32_t b = 0; b < 2; ++b) {
+          const uint32_t p = pb + b * kWave + lane;
+          const float hn = __builtin_fmaf(-alpha, tv2[b], hv2[b]);
+          *tp2[b] = hn;
+          const float cand = p < nq ? hn : inf;
+          if (cand < bv) bv = cand, bi = kTailPos | p, br = nr + b;
         }
       }
       const uint32_t key = f32_order(bv);
@@ -1055,6 +1095,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
           break;
         }
       }
+      if (midx != kNone && (midx & kTailPos) != 0u) midx = k2b_idx[q0 + (midx & ~kTailPos)];
     };
     if (!deferred) t2_pass(1.0f);
     wave_lds_sync();
@@ -1151,10 +1192,13 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
     }
 
     if (deferred) {
-      // the dense kernel redoes this cell from the start (and writes all of it)
+      // a pass with a larger capacity, or the dense kernel, redoes this cell
+      // from the start (and writes all of it)
       if (lane == 0) {
-        const uint32_t slot = atomicAdd(defer_cnt, 1u);
-        defer_list[slot] = cell;
+        if (too_long && q.long_list != nullptr)
+          q.long_list[atomicAdd(q.long_cnt, 1u)] = cell;
+        else
+          q.dense_list[atomicAdd(q.dense_cnt, 1u)] = cell;
       }
       continue;
     }
@@ -1175,6 +1219,51 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
 
 __global__ void zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
   if (threadIdx.x < count) p[threadIdx.x] = 0u;
+}
+
+// SEACELLS_A_SUPPORT: "0" never uses the support state, "1" uses it for any
+// k (experiments and tests); unset: by k.
+int support_mode() {
+  const char *v = getenv("SEACELLS_A_SUPPORT");
+  if (v == nullptr || v[0] == 0) return -1;
+  return v[0] == '0' ? 0 : 1;
+}
+
+uint32_t support_waves_per_cu() {
+  const char *v = getenv("SEACELLS_A_SUPPORT_WAVES");
+  if (v != nullptr) {
+    const int w = atoi(v);
+    if (w >= 4 && w <= 32) return (uint32_t)w;
+  }
+  return kSupDefaultWaves;
+}
+
+// LDS of one support wave when `waves` waves per CU are resident: the
+// bitmaps, one dummy per lane and the largest state (t2 entries, a multiple
+// of 64) that fits. False when not even kSupMinHc entries fit.
+bool support_tier_size(const APlan &p, uint32_t waves, uint32_t &hc_out, uint32_t &lpw_out) {
+  const size_t sched_b = (size_t)p.sched_words * 4;
+  const size_t fixed = ((size_t)p.nwords + 1) * 12 + (size_t)kWave * 4;
+  const uint32_t blocks = (waves + kSupWavesPerBlock - 1) / kSupWavesPerBlock;
+  const size_t per_block = kLdsBytesPerCU / blocks;
+  const size_t per_wave = per_block > sched_b ? (per_block - sched_b) / kSupWavesPerBlock : 0;
+  if (per_wave < fixed + 4 * kSupMinHc) return false;
+  size_t hc = (per_wave - fixed) / 4;
+  hc = hc / 64 * 64;
+  if (hc > kSupMaxHc) hc = kSupMaxHc;
+  hc_out = (uint32_t)hc;
+  lpw_out = (uint32_t)(align_up(((size_t)p.nwords + 1) * 3 + hc + kWave, 4) * 4);
+  return true;
+}
+
+// Resident waves per CU of the first support pass: the target, lowered
+// (in whole blocks) until its LDS fits.
+uint32_t first_pass_waves(const APlan &p, bool wide) {
+  uint32_t w = support_waves_per_cu();
+  if (wide && w > kSupWideWaves) w = kSupWideWaves;  // register-limited
+  uint32_t hc, lpw;
+  while (w > kSupWavesPerBlock && !support_tier_size(p, w, hc, lpw)) w -= kSupWavesPerBlock;
+  return w;
 }
 
 template <uint32_t G, bool kHInLds, bool kRegAtoms>
@@ -1231,22 +1320,29 @@ hipError_t launch_variant(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr 
   return hipGetLastError();
 }
 
-hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr k2b, Csr ap,
-                          uint32_t n, uint32_t k, uint32_t T, uint32_t cap, const float *gamma,
-                          uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
-                          uint32_t *trace, uint32_t *defer_cnt, uint32_t *defer_list,
+hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, uint32_t tier, Csr t1,
+                          Csr k2b, Csr ap, uint32_t n, uint32_t k, uint32_t T, uint32_t cap,
+                          const float *gamma, uint32_t *atom_idx, float *atom_val,
+                          uint32_t *atom_cnt, uint32_t *trace, const SupQueues &q,
                           uint32_t *status, hipStream_t stream) {
-  static bool configured = false;
-  auto fn = reinterpret_cast<const void *>(&fw_a_support_kernel);
-  const uint32_t wpb = plan.sup_waves_per_block;
-  const uint32_t threads = wpb * kWave;
-  const uint32_t lds_bytes = plan.sched_words * 4 + wpb * plan.sup_lds_per_wave;
+  // t2 entries in registers: 256 for short K2B rows, 512 when rows are long
+  // on average (the first pass) or by construction (the long-row pass)
+  const bool wide = tier > 0 || k2b.nnz > (uint64_t)n * 192u;
+  const uint32_t waves = tier > 0 ? kSupLongWaves : first_pass_waves(plan, wide);
+  uint32_t hc_cap = 0, lpw = 0;
+  if (!support_tier_size(plan, waves, hc_cap, lpw)) return hipErrorInvalidValue;
+  auto kern = wide ? &fw_a_support_kernel<8> : &fw_a_support_kernel<4>;
+  auto fn = reinterpret_cast<const void *>(kern);
+  static bool configured[2] = {false, false};
   hipError_t e;
-  if (!configured) {
+  if (!configured[wide]) {
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytesPerCU);
     if (e != hipSuccess) return e;
-    configured = true;
+    configured[wide] = true;
   }
+  const uint32_t wpb = kSupWavesPerBlock;
+  const uint32_t threads = wpb * kWave;
+  const uint32_t lds_bytes = plan.sched_words * 4 + wpb * lpw;
   int bpc = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&bpc, fn, threads, lds_bytes);
   if (e != hipSuccess) return e;
@@ -1254,12 +1350,10 @@ hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr 
   const uint64_t want = ((uint64_t)n + wpb - 1) / wpb;
   const uint64_t cap_blocks = (uint64_t)dev.cus * (uint64_t)bpc;
   const uint32_t blocks = (uint32_t)(want < cap_blocks ? want : cap_blocks);
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, defer_cnt, 2u);
-  hipLaunchKernelGGL(fw_a_support_kernel, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr,
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr,
                      t1.idx, t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
                      ap.val, ap.nnz, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt, trace,
-                     plan.nwords, plan.hc_cap, plan.sched_words, plan.sup_lds_per_wave / 4,
-                     defer_cnt, defer_list, status);
+                     plan.nwords, hc_cap, plan.sched_words, lpw / 4, q, status);
   return hipGetLastError();
 }
 
@@ -1268,28 +1362,6 @@ bool dense_only_requested() {
   return v != nullptr && v[0] == '1';
 }
 
-constexpr uint32_t kSupportMinK = 2048;     // support state from this k on
-constexpr uint32_t kSupWavesPerBlock = 4;
-constexpr uint32_t kSupDefaultWaves = 24;   // resident waves per CU the LDS is sized for
-constexpr uint32_t kSupMinHc = 256;         // smallest useful t2 capacity
-constexpr uint32_t kSupMaxHc = 8192;
-
-// SEACELLS_A_SUPPORT: "0" never uses the support state, "1" uses it for any
-// k (experiments and tests); unset: by k.
-int support_mode() {
-  const char *v = getenv("SEACELLS_A_SUPPORT");
-  if (v == nullptr || v[0] == 0) return -1;
-  return v[0] == '0' ? 0 : 1;
-}
-
-uint32_t support_waves_per_cu() {
-  const char *v = getenv("SEACELLS_A_SUPPORT_WAVES");
-  if (v != nullptr) {
-    const int w = atoi(v);
-    if (w >= 4 && w <= 32) return (uint32_t)w;
-  }
-  return kSupDefaultWaves;
-}
 
 // Lanes per cell: from the environment for experiments, else by k.
 uint32_t group_width(uint32_t k) {
@@ -1338,35 +1410,26 @@ APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap) {
   const size_t dense_ws = p.h_in_lds ? 0 : (size_t)p.global_waves * p.ws_words_per_wave * 4;
 
   // support state for large k: picks equal to the dense kernel's (cells it
-  // cannot settle are queued for the dense kernel)
+  // cannot settle are queued for the dense kernel). Pass 0 is sized for
+  // many resident waves; K2B rows longer than its capacity go to pass 1,
+  // which holds the longest rows with fewer waves.
   p.support = false;
   const int mode = support_mode();
   if (mode != 0 && p.group == kWave && p.reg_atoms && p.sched_words != 0 &&
       !dense_only_requested() && (mode == 1 || k >= kSupportMinK)) {
     p.nwords = (k + 31u) / 32u;
-    const uint32_t target = support_waves_per_cu();
-    const uint32_t blocks = (target + kSupWavesPerBlock - 1) / kSupWavesPerBlock;
-    const size_t per_block = kLdsBytesPerCU / blocks;
-    const size_t sched_b = (size_t)p.sched_words * 4;
-    const size_t per_wave = per_block > sched_b ? (per_block - sched_b) / kSupWavesPerBlock : 0;
-    const size_t fixed = ((size_t)p.nwords + 1) * 12 + (size_t)kWave * 4;
-    if (per_wave >= fixed + 4 * kSupMinHc) {
-      size_t hc = (per_wave - fixed) / 4;
-      hc = hc / 64 * 64;
-      if (hc > kSupMaxHc) hc = kSupMaxHc;
-      p.hc_cap = (uint32_t)hc;
-      p.sup_lds_per_wave =
-          (uint32_t)(align_up(((size_t)p.nwords + 1) * 3 + hc + kWave, 4) * 4);
-      p.sup_waves_per_block = kSupWavesPerBlock;
-      p.support = true;
-    }
+    // the narrow first pass needs the least LDS: if even it does not fit,
+    // there is no support state (the sizes of every pass are set at launch)
+    uint32_t hc, lpw;
+    if (support_tier_size(p, kSupWavesPerBlock, hc, lpw)) p.support = true;
   }
-  // workspace: [deferred-cell counter | deferred-cell list | dense state slices]
+  // workspace: [counters | long-row queue | dense queue | dense state slices]
   if (p.support) {
     p.ws_list_off = 256;
-    p.ws_dense_off = align_up(p.ws_list_off + (size_t)n * 4, 256);
+    p.ws_list2_off = align_up(p.ws_list_off + (size_t)n * 4, 256);
+    p.ws_dense_off = align_up(p.ws_list2_off + (size_t)n * 4, 256);
   } else {
-    p.ws_list_off = 0;
+    p.ws_list_off = p.ws_list2_off = 0;
     p.ws_dense_off = 0;
   }
   p.ws_bytes = dense_ws > 0 || p.support ? align_up(p.ws_dense_off + dense_ws, 256) : 0;
@@ -1384,13 +1447,30 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
   const uint32_t *cell_list = nullptr, *cell_count = nullptr;
   // the support kernel addresses t1 with 32-bit byte offsets
   if (plan.support && t1.nnz < (1u << 30)) {
-    uint32_t *cnt = static_cast<uint32_t *>(ws);
-    uint32_t *list = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + plan.ws_list_off);
-    e = launch_support(plan, dev, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
-                       atom_cnt, trace, cnt, list, status, stream);
+    char *w8 = static_cast<char *>(ws);
+    uint32_t *ctr = reinterpret_cast<uint32_t *>(w8);  // work0, work1, long, dense
+    uint32_t *long_list = reinterpret_cast<uint32_t *>(w8 + plan.ws_list_off);
+    uint32_t *dense_list = reinterpret_cast<uint32_t *>(w8 + plan.ws_list2_off);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, ctr, 4u);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // a second pass when it holds longer K2B rows than the first
+    const bool wide0 = k2b.nnz > (uint64_t)n * 192u;
+    uint32_t hc0 = 0, hc1 = 0, lpw_unused;
+    support_tier_size(plan, first_pass_waves(plan, wide0), hc0, lpw_unused);
+    const bool two = support_tier_size(plan, kSupLongWaves, hc1, lpw_unused) && hc1 > hc0;
+    SupQueues q0{nullptr, nullptr, ctr + 0, two ? long_list : nullptr, ctr + 2, dense_list,
+                 ctr + 3};
+    e = launch_support(plan, dev, 0, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
+                       atom_cnt, trace, q0, status, stream);
     if (e != hipSuccess) return e;
-    cell_list = list;
-    cell_count = cnt;
+    if (two) {
+      SupQueues q1{long_list, ctr + 2, ctr + 1, nullptr, nullptr, dense_list, ctr + 3};
+      e = launch_support(plan, dev, 1, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
+                         atom_cnt, trace, q1, status, stream);
+      if (e != hipSuccess) return e;
+    }
+    cell_list = dense_list;
+    cell_count = ctr + 3;
   }
 #define SEACELLS_A_ARGS \
   plan, dev, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt, trace, ws, \

@@ -38,6 +38,9 @@ constexpr uint32_t kReduceCols = 64;  // columns per stage-1 block (one per lane
 constexpr uint32_t kMaxChunks = 64;
 
 constexpr uint32_t kGatherRows = 4;  // AAt runs whose loads are in flight together
+constexpr uint32_t kXcds = 8;        // MI355X: 8 XCDs of 32 CUs, each with its own 4 MB L2
+constexpr size_t kSliceAatBytes = 5u << 19;  // AAt bytes per slice kept within one L2 (2.5 MB)
+constexpr uint32_t kMaxSlices = 128;
 constexpr uint32_t kNoCol = 0xffffffffu;
 
 // acc[c] += v (LDS read, add, write). One wave's LDS operations execute in
@@ -87,19 +90,35 @@ __global__ void __launch_bounds__(256)
 template <uint32_t S4>
 __global__ void __launch_bounds__(kBThreads)
     fw_b_partials_kernel(Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n, uint32_t k,
-                         uint32_t n_slices, uint32_t n_row_blocks,
+                         uint32_t slice_w, uint32_t n_slices, uint32_t n_row_blocks,
                          const uint32_t *__restrict__ seg, uint64_t *__restrict__ part_key,
                          float *__restrict__ part_gap, uint32_t *__restrict__ stamps,
                          uint32_t epoch, uint32_t *__restrict__ status) {
-  constexpr uint32_t W = 256 * S4;
-  constexpr uint32_t NC = 4 * S4;  // columns per lane
+  constexpr uint32_t W = 256 * S4;  // accumulator columns (>= slice_w)
+  constexpr uint32_t NC = 4 * S4;   // columns per lane
   extern __shared__ float lds_acc[];
   const uint32_t lane = lane_id();
   const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t wpb = blockDim.x / kWave;
-  const uint32_t gwave = blockIdx.x * wpb + wib;
-  const uint32_t nwaves = gridDim.x * wpb;
   float *acc = lds_acc + (size_t)wib * W;
+
+  // Blocks are dealt to the XCDs round-robin, so block b runs on XCD
+  // b % kXcds. Each XCD takes its own slices (all row blocks of them), or,
+  // with fewer slices than XCDs, its share of the row blocks of one slice,
+  // and walks them slice after slice: the AAt columns an XCD gathers stay
+  // in its L2. (On another placement only the speed changes.)
+  const uint32_t xcd = blockIdx.x % kXcds;
+  const uint32_t wx = (blockIdx.x / kXcds) * wpb + wib;
+  const uint32_t nwx = (gridDim.x / kXcds) * wpb;
+  uint32_t sl0, sl_step, rb0, rb_step;
+  if (n_slices >= kXcds) {
+    sl0 = xcd, sl_step = kXcds, rb0 = 0, rb_step = 1;
+  } else {
+    sl0 = xcd % n_slices, sl_step = kXcds, rb0 = xcd / n_slices, rb_step = kXcds / n_slices;
+  }
+  const uint32_t my_sl = sl0 < n_slices ? (n_slices - sl0 + sl_step - 1) / sl_step : 0u;
+  const uint32_t my_rb = rb0 < n_row_blocks ? (n_row_blocks - rb0 + rb_step - 1) / rb_step : 0u;
+  const uint32_t my_units = my_sl * my_rb;
   const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
   const float inf = __builtin_inff();
   uint32_t flags = 0;
@@ -109,12 +128,13 @@ __global__ void __launch_bounds__(kBThreads)
     *reinterpret_cast<float4 *>(acc + s4 * 256 + lane * 4) = zero4;
   wave_lds_sync();
 
-  const uint32_t n_units = n_row_blocks * n_slices;
-  for (uint32_t unit = gwave; unit < n_units; unit += nwaves) {
-    const uint32_t rb = unit / n_slices;
-    const uint32_t sl = unit - rb * n_slices;
-    const uint32_t c0 = sl * W;
-    const uint32_t cw = (k - c0) < W ? (k - c0) : W;
+  for (uint32_t u = wx; u < my_units; u += nwx) {
+    const uint32_t js = u / my_rb;
+    const uint32_t rb = rb0 + (u - js * my_rb) * rb_step;
+    const uint32_t sl = sl0 + js * sl_step;
+    const uint32_t unit = rb * n_slices + sl;
+    const uint32_t c0 = sl * slice_w;
+    const uint32_t cw = (k - c0) < slice_w ? (k - c0) : slice_w;
     const uint32_t r0 = (uint32_t)(((uint64_t)n * rb) / n_row_blocks);
     const uint32_t r1 = (uint32_t)(((uint64_t)n * (rb + 1)) / n_row_blocks);
 
@@ -368,21 +388,39 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
   const uint64_t units = (uint64_t)p.n_row_blocks * p.n_slices;
   const uint64_t want = (units + 3) / 4;
   const uint64_t resident = (uint64_t)dev.cus * (uint64_t)bpc;
-  const uint32_t blocks = (uint32_t)(want < resident ? want : resident);
-  hipLaunchKernelGGL(fw_b_partials_kernel<S4>, dim3(blocks), dim3(kBThreads), lds, stream, k2b,
-                     aat, k2at, b, n, k, p.n_slices, p.n_row_blocks, seg, keys, gap_part, stamps,
-                     epoch, status);
+  uint64_t blocks = want < resident ? want : resident;
+  blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // the same number of blocks on every XCD
+  hipLaunchKernelGGL(fw_b_partials_kernel<S4>, dim3((uint32_t)blocks), dim3(kBThreads), lds,
+                     stream, k2b, aat, k2at, b, n, k, p.slice_w, p.n_slices, p.n_row_blocks, seg,
+                     keys, gap_part, stamps, epoch, status);
   return hipGetLastError();
 }
 
 }  // namespace
 
-BPlan plan_b(uint32_t n, uint32_t k) {
+// Slices: one when k fits one accumulator; otherwise enough that each holds
+// at most ~2.5 MB of AAt (the L2 share of one XCD), as 2, 4 or a multiple
+// of 8 slices so that they spread evenly over the XCDs.
+static uint32_t slices_for(uint32_t k, uint64_t aat_nnz) {
+  const uint32_t wmax = 256u * kBMaxS4;
+  if (k <= wmax) return 1;
+  uint64_t s = (k + wmax - 1) / wmax;
+  const uint64_t by_l2 = (aat_nnz * 8 + kSliceAatBytes - 1) / kSliceAatBytes;
+  if (by_l2 > s) s = by_l2;
+  if (s <= 2) return 2;
+  if (s <= 4) return 4;
+  s = (s + kXcds - 1) / kXcds * kXcds;
+  if (s > kMaxSlices) s = kMaxSlices;
+  const uint64_t most = (k + 3) / 4;  // slices of at least 4 columns
+  return (uint32_t)(s < most ? s : most);
+}
+
+static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices) {
   BPlan p{};
-  const uint32_t chunks = (k + 255u) / 256u;
-  p.s4 = chunks < kBMaxS4 ? (chunks < 1 ? 1 : chunks) : kBMaxS4;
-  p.slice_w = 256u * p.s4;
+  p.n_slices = n_slices;
+  p.slice_w = (uint32_t)align_up((k + n_slices - 1) / n_slices, 4);
   p.n_slices = (k + p.slice_w - 1) / p.slice_w;
+  p.s4 = (p.slice_w + 255u) / 256u;
   uint32_t rb = kBUnitsTarget / p.n_slices;
   if (rb < 1) rb = 1;
   if (rb > n) rb = n;
@@ -402,6 +440,17 @@ BPlan plan_b(uint32_t n, uint32_t k) {
   if (p.n_slices > 1) off = align_up(off + (size_t)k * (p.n_slices + 1) * sizeof(uint32_t), 256);
   p.ws_bytes = off;
   return p;
+}
+
+BPlan plan_b(uint32_t n, uint32_t k, uint64_t aat_nnz) {
+  return plan_with_slices(n, k, slices_for(k, aat_nnz));
+}
+
+size_t b_workspace_bound(uint32_t n, uint32_t k) {
+  // AAt has at most k * k entries: the most slices any call can take
+  const size_t most = plan_b(n, k, (uint64_t)k * k).ws_bytes;
+  const size_t fewest = plan_b(n, k, 0).ws_bytes;
+  return most > fewest ? most : fewest;
 }
 
 hipError_t launch_status_clear(uint32_t *status, hipStream_t stream) {

@@ -80,9 +80,14 @@ def test_ragged_signed_operands_dense_path():
     parity.check_a(w, tr, ai, av, ac, np.arange(w.n))
 
 
-def test_large_k_state_in_workspace():
-    # k * 4 bytes exceeds the 160 KB LDS of a compute unit: h lives in workspace
+@pytest.mark.parametrize("support", ["0", "default"])
+def test_large_k_state_in_workspace(support, monkeypatch):
+    # k * 4 bytes exceeds the 160 KB LDS of a compute unit: the dense state
+    # lives in workspace (support "0"); by default the compact state takes
+    # the cells, with fewer waves per CU
     import sparse_archetypal_analysis_amd as saa
+    if support == "0":
+        monkeypatch.setenv("SEACELLS_A_SUPPORT", "0")
     w = W.random_workload(37, 45_000, t1_per_row=6, k2b_per_row=20, s_a=5, seed=7, T=30)
     assert saa.seacells_fw_a_columns_workspace(w.n, w.k, 30, w.cap) > 0
     ai, av, ac, tr, flags = run_a(w, T=30)
@@ -211,8 +216,11 @@ def _support_case(name):
     if name == "signed":      # every cell leaves the support path at its first negative product
         return W.random_workload(400, 333, t1_per_row=12, k2b_per_row=9, s_a=7, seed=5,
                                  signed=True), {}
-    if name == "long_rows":   # K2B rows from 0 to 1600 entries: some exceed the support capacity
+    if name == "long_rows":   # K2B rows from 0 to 1600 entries: some exceed the first pass
         return W.random_workload(200, 3000, t1_per_row=40, k2b_per_row=800, s_a=6, seed=29), {}
+    if name == "very_long_rows":  # up to 12000 entries: some exceed the long-row pass too
+        return W.random_workload(40, 12000, t1_per_row=60, k2b_per_row=3000, s_a=6, seed=31,
+                                 T=20), {"T": 20}
     if name == "fold":        # the running scale is folded back: those cells go to the dense kernel
         w = W.make("c1")
         gam = np.full(120, 0.55, np.float32)
@@ -232,8 +240,9 @@ def _support_case(name):
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "empty", "signed", "long_rows", "fold",
-                                  "restarts", "bad_gamma", "cap_overflow"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "empty", "signed", "long_rows",
+                                  "very_long_rows", "fold", "restarts", "bad_gamma",
+                                  "cap_overflow"])
 def test_support_state_equals_dense_kernel(name, monkeypatch):
     # The support state (h kept on supp(t2) only, plus bitmaps) must give the
     # dense kernel's results bit for bit; cells it cannot settle are redone by

@@ -229,6 +229,72 @@ def _a_prev_t(cfg: Config, rng, X, init):
     return sp.csr_matrix((wts.ravel(), (rows, nb.ravel())), shape=(n, k))
 
 
+_SPGEMM_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_spgemm.c")
+_SPGEMM_LIB = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspgemm.so")
+_spgemm_lib = None
+
+
+def build_spgemm(force: bool = True) -> str:
+    """Compile the generator's sparse-product helper (gcc, OpenMP)."""
+    import subprocess
+    if force or not os.path.exists(_SPGEMM_LIB) or \
+            os.path.getmtime(_SPGEMM_LIB) < os.path.getmtime(_SPGEMM_SRC):
+        tmp = _SPGEMM_LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-o", tmp,
+                        _SPGEMM_SRC], check=True)
+        os.replace(tmp, _SPGEMM_LIB)
+    return _SPGEMM_LIB
+
+
+def _spgemm_load():
+    global _spgemm_lib
+    if _spgemm_lib is None:
+        import ctypes
+        build_spgemm(force=False)
+        lib = ctypes.CDLL(_SPGEMM_LIB)
+        P = ctypes.c_void_p
+        I = ctypes.c_int64
+        lib.spgemm_count.argtypes = [I, I, P, P, P, P, P]
+        lib.spgemm_fill.argtypes = [I, I, P, P, P, P, P, P, P, P, P, P]
+        _spgemm_lib = lib
+    return _spgemm_lib
+
+
+def _matmul(A: sp.csr_matrix, B: sp.csr_matrix) -> sp.csr_matrix:
+    """A @ B in f64 with the values scipy's product gives (same summation
+    order), sorted columns and no stored zeros, over all host cores."""
+    lib = _spgemm_load()
+    A = sp.csr_matrix(A, dtype=np.float64)
+    B = sp.csr_matrix(B, dtype=np.float64)
+    ap = np.ascontiguousarray(A.indptr, np.int64)
+    ai = np.ascontiguousarray(A.indices, np.int32)
+    av = np.ascontiguousarray(A.data, np.float64)
+    bp = np.ascontiguousarray(B.indptr, np.int64)
+    bi = np.ascontiguousarray(B.indices, np.int32)
+    bv = np.ascontiguousarray(B.data, np.float64)
+    n, m = A.shape[0], B.shape[1]
+    cnt = np.empty(n, np.int64)
+    P = lambda a: a.ctypes.data
+    if lib.spgemm_count(n, m, P(ap), P(ai), P(bp), P(bi), P(cnt)) != 0:
+        raise MemoryError("sparse product: out of memory")
+    cp = np.zeros(n + 1, np.int64)
+    np.cumsum(cnt, out=cp[1:])
+    ci = np.empty(int(cp[-1]), np.int32)
+    cv = np.empty(int(cp[-1]), np.float64)
+    kept = np.empty(n, np.int64)
+    if lib.spgemm_fill(n, m, P(ap), P(ai), P(av), P(bp), P(bi), P(bv), P(cp), P(ci), P(cv),
+                       P(kept)) != 0:
+        raise MemoryError("sparse product: out of memory")
+    if not np.array_equal(kept, cnt):  # exact zeros were dropped: close the gaps
+        keep = np.arange(ci.shape[0]) - np.repeat(cp[:-1], cnt) < np.repeat(kept, cnt)
+        ci, cv = ci[keep], cv[keep]
+        cp = np.zeros(n + 1, np.int64)
+        np.cumsum(kept, out=cp[1:])
+    out = sp.csr_matrix((cv, ci, cp), shape=(n, m))
+    out.has_sorted_indices = True
+    return out
+
+
 def _f32(m, symmetric=False):
     m = sp.csr_matrix(m, dtype=np.float64)
     if symmetric:
@@ -271,10 +337,10 @@ def generate(cfg: Config, seed: int = 0, log=None) -> Workload:
     B = _b_matrix(cfg, rng, labels, init)
     At = _a_prev_t(cfg, rng, X, init)
     _progress(log, "B and A_prev", t0)
-    K2B = K @ (K @ B)
+    K2B = _matmul(K, _matmul(K, B))
     t1 = B.T @ K2B
     _progress(log, "K2B and t1", t0)
-    K2At = K @ (K @ At)
+    K2At = _matmul(K, _matmul(K, At))
     AAt = At.T @ At
     _progress(log, "K2At and AAt", t0)
     w = Workload(cfg, seed, t1=_f32(t1, symmetric=True), k2b=_f32(K2B), a_prev_t=_f32(At),
