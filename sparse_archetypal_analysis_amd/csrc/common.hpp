@@ -148,7 +148,7 @@ struct BPlan {
   uint32_t n_slices;
   uint32_t n_row_blocks;  // row ranges; one work unit = (row range, slice)
   uint32_t n_chunks;      // row-range groups of the first reduce stage
-  size_t off_keys, off_part2, off_gap, off_stamp, off_seg, ws_bytes;
+  size_t off_keys, off_part2, off_gap, off_stamp, off_work, off_seg, ws_bytes;
 };
 BPlan plan_b(uint32_t n, uint32_t k, uint64_t aat_nnz);
 size_t b_workspace_bound(uint32_t n, uint32_t k);  // over every aat_nnz

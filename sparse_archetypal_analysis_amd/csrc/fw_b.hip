@@ -41,6 +41,15 @@ constexpr uint32_t kGatherRows = 4;  // AAt runs whose loads are in flight toget
 constexpr uint32_t kXcds = 8;        // MI355X: 8 XCDs of 32 CUs, each with its own 4 MB L2
 constexpr size_t kSliceAatBytes = 5u << 19;  // AAt bytes per slice kept within one L2 (2.5 MB)
 constexpr uint32_t kMaxSlices = 128;
+constexpr uint32_t kSlicedRowBlocks = 4096;  // row ranges per slice when k is sliced
+constexpr uint32_t kAccPad = 32;             // floats between the two accumulators
+
+// base[byte_off / 4] with a 32-bit byte offset from a wave-uniform base (the
+// array must hold fewer than 2^30 entries)
+template <typename T>
+__device__ __forceinline__ T load_at(const T *__restrict__ base, uint32_t byte_off) {
+  return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
 constexpr uint32_t kNoCol = 0xffffffffu;
 
 // acc[c] += v (LDS read, add, write). One wave's LDS operations execute in
@@ -87,20 +96,32 @@ __global__ void __launch_bounds__(256)
   seg[e] = lo;
 }
 
-template <uint32_t S4>
+// kDual: the two half-waves gather different K2B entries into two
+// accumulators (for the short AAt runs of narrow slices); each column then
+// sums the even-numbered entries of the row in one accumulator and the odd
+// ones in the other, each in K2B order, and adds the two at the end.
+template <uint32_t S4, bool kDual>
 __global__ void __launch_bounds__(kBThreads)
     fw_b_partials_kernel(Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n, uint32_t k,
                          uint32_t slice_w, uint32_t n_slices, uint32_t n_row_blocks,
                          const uint32_t *__restrict__ seg, uint64_t *__restrict__ part_key,
                          float *__restrict__ part_gap, uint32_t *__restrict__ stamps,
-                         uint32_t epoch, uint32_t *__restrict__ status) {
+                         uint32_t *__restrict__ xcd_work, uint32_t epoch,
+                         uint32_t *__restrict__ status) {
   constexpr uint32_t W = 256 * S4;  // accumulator columns (>= slice_w)
   constexpr uint32_t NC = 4 * S4;   // columns per lane
+  constexpr uint32_t NACC = kDual ? 2 : 1;
   extern __shared__ float lds_acc[];
   const uint32_t lane = lane_id();
   const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t wpb = blockDim.x / kWave;
-  float *acc = lds_acc + (size_t)wib * W;
+  // the second accumulator sits kAccPad floats further on, so that equal
+  // columns of the two halves fall in different LDS banks
+  constexpr uint32_t ACC2 = W + kAccPad;
+  float *acc = lds_acc + (size_t)wib * (kDual ? W + ACC2 : W);
+  const uint32_t half = kDual ? (lane >> 5) : 0u;
+  const uint32_t hl = kDual ? (lane & 31u) : lane;  // lane within its half
+  float *acc_h = acc + half * ACC2;                   // this half's accumulator
 
   // Blocks are dealt to the XCDs round-robin, so block b runs on XCD
   // b % kXcds. Each XCD takes its own slices (all row blocks of them), or,
@@ -108,8 +129,6 @@ __global__ void __launch_bounds__(kBThreads)
   // and walks them slice after slice: the AAt columns an XCD gathers stay
   // in its L2. (On another placement only the speed changes.)
   const uint32_t xcd = blockIdx.x % kXcds;
-  const uint32_t wx = (blockIdx.x / kXcds) * wpb + wib;
-  const uint32_t nwx = (gridDim.x / kXcds) * wpb;
   uint32_t sl0, sl_step, rb0, rb_step;
   if (n_slices >= kXcds) {
     sl0 = xcd, sl_step = kXcds, rb0 = 0, rb_step = 1;
@@ -124,11 +143,19 @@ __global__ void __launch_bounds__(kBThreads)
   uint32_t flags = 0;
 
 #pragma unroll
-  for (uint32_t s4 = 0; s4 < S4; ++s4)
-    *reinterpret_cast<float4 *>(acc + s4 * 256 + lane * 4) = zero4;
+  for (uint32_t a = 0; a < NACC; ++a)
+#pragma unroll
+    for (uint32_t s4 = 0; s4 < S4; ++s4)
+      *reinterpret_cast<float4 *>(acc + a * ACC2 + s4 * 256 + lane * 4) = zero4;
   wave_lds_sync();
 
-  for (uint32_t u = wx; u < my_units; u += nwx) {
+  // units in slice-major order, taken one at a time from the XCD's counter:
+  // the XCD's waves sweep one slice before the next
+  for (;;) {
+    uint32_t u = 0;
+    if (lane == 0) u = atomicAdd(xcd_work + xcd, 1u);
+    u = __builtin_amdgcn_readfirstlane(u);
+    if (u >= my_units) break;
     const uint32_t js = u / my_rb;
     const uint32_t rb = rb0 + (u - js * my_rb) * rb_step;
     const uint32_t sl = sl0 + js * sl_step;
@@ -168,6 +195,42 @@ __global__ void __launch_bounds__(kBThreads)
           }
         }
         const uint32_t cnt = (e1 - eb) < kWave ? (e1 - eb) : kWave;
+        if constexpr (kDual) {
+          // entries u + 2g (lanes 0-31) and u + 2g + 1 (lanes 32-63): runs of
+          // kGatherRows pairs in flight, 32 lanes per run
+          for (uint32_t u = 0; u < cnt; u += 2 * kGatherRows) {
+            uint32_t plo[kGatherRows], phi[kGatherRows];
+            float xs[kGatherRows], va[kGatherRows], vb[kGatherRows];
+            uint32_t ca[kGatherRows], cb[kGatherRows];
+#pragma unroll
+            for (uint32_t g = 0; g < kGatherRows; ++g) {
+              const uint32_t s0 = u + 2 * g, s1 = s0 + 1;
+              const uint32_t r0 = s0 < kWave ? s0 : kWave - 1, r1 = s1 < kWave ? s1 : kWave - 1;
+              const uint32_t lo0 = readlane_u32(lo, r0), lo1 = readlane_u32(lo, r1);
+              const uint32_t hi0 = readlane_u32(hi, r0), hi1 = readlane_u32(hi, r1);
+              const float x0 = readlane_f32(x, r0), x1 = readlane_f32(x, r1);
+              const bool on = (half ? s1 : s0) < cnt;
+              plo[g] = on ? (half ? lo1 : lo0) : 0u;
+              phi[g] = on ? (half ? hi1 : hi0) : 0u;
+              xs[g] = half ? x1 : x0;
+              const uint32_t pa = plo[g] + hl, pb = pa + 32;
+              ca[g] = kNoCol, va[g] = 0.0f, cb[g] = kNoCol, vb[g] = 0.0f;
+              if (pa < phi[g]) ca[g] = load_at(aat.idx, pa * 4u), va[g] = load_at(aat.val, pa * 4u);
+              if (pb < phi[g]) cb[g] = load_at(aat.idx, pb * 4u), vb[g] = load_at(aat.val, pb * 4u);
+            }
+#pragma unroll
+            for (uint32_t g = 0; g < kGatherRows; ++g) {
+              const uint32_t c_a = ca[g] - c0, c_b = cb[g] - c0;
+              if (c_a < cw) lds_add(acc_h + c_a, xs[g] * va[g]);
+              if (c_b < cw) lds_add(acc_h + c_b, xs[g] * vb[g]);
+              for (uint32_t p = plo[g] + 64 + hl; p < phi[g]; p += 32) {
+                const uint32_t c = load_at(aat.idx, p * 4u) - c0;
+                if (c < cw) lds_add(acc_h + c, xs[g] * load_at(aat.val, p * 4u));
+              }
+            }
+          }
+          continue;
+        }
         // kGatherRows AAt runs in flight at a time (their first two chunks);
         // the adds still go row after row, so every column sums its terms in
         // K2B order and the result does not depend on the timing
@@ -213,7 +276,7 @@ __global__ void __launch_bounds__(kBThreads)
         if (!row_ok(b, i, g0, g1)) flags |= kFlagBadIndex;
         for (uint32_t q = g0 + lane; q < g1; q += kWave) {
           const uint32_t c = b.idx[q] - c0;
-          if (c < cw) gsum += b.val[q] * acc[c];
+          if (c < cw) gsum += b.val[q] * (kDual ? acc[c] + acc[ACC2 + c] : acc[c]);
         }
       }
       // -- running minimum per column (strict `<`: lowest row wins), clear
@@ -221,7 +284,13 @@ __global__ void __launch_bounds__(kBThreads)
       for (uint32_t s4 = 0; s4 < S4; ++s4) {
         const uint32_t cb = s4 * 256 + lane * 4;
         float4 *slot = reinterpret_cast<float4 *>(acc + cb);
-        const float4 v = *slot;
+        float4 v = *slot;
+        if constexpr (kDual) {
+          float4 *slot2 = reinterpret_cast<float4 *>(acc + ACC2 + cb);
+          const float4 v2 = *slot2;
+          v.x += v2.x, v.y += v2.y, v.z += v2.z, v.w += v2.w;
+          *slot2 = zero4;
+        }
         const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (uint32_t j = 0; j < 4; ++j) {
@@ -368,20 +437,25 @@ __global__ void __launch_bounds__(256)
 
 __global__ void status_clear_kernel(uint32_t *__restrict__ status) { *status = 0u; }
 
-template <uint32_t S4>
+__global__ void zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
+  if (threadIdx.x < count) p[threadIdx.x] = 0u;
+}
+
+template <uint32_t S4, bool kDual>
 hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
                            uint32_t k, const uint32_t *seg, uint64_t *keys, float *gap_part,
-                           uint32_t *stamps, uint32_t epoch, uint32_t *status,
-                           hipStream_t stream) {
+                           uint32_t *stamps, uint32_t *xcd_work, uint32_t epoch,
+                           uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
-  const uint32_t lds = (kBThreads / kWave) * 256 * S4 * sizeof(float);
+  const uint32_t lds =
+      (kBThreads / kWave) * (kDual ? 2 * 256 * S4 + kAccPad : 256 * S4) * sizeof(float);
   static int bpc = -1;
   if (bpc < 0) {
     int v = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &v, reinterpret_cast<const void *>(&fw_b_partials_kernel<S4>), kBThreads, lds);
+        &v, reinterpret_cast<const void *>(&fw_b_partials_kernel<S4, kDual>), kBThreads, lds);
     if (e != hipSuccess) return e;
     bpc = v < 1 ? 1 : v;
   }
@@ -390,9 +464,10 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
   const uint64_t resident = (uint64_t)dev.cus * (uint64_t)bpc;
   uint64_t blocks = want < resident ? want : resident;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // the same number of blocks on every XCD
-  hipLaunchKernelGGL(fw_b_partials_kernel<S4>, dim3((uint32_t)blocks), dim3(kBThreads), lds,
+  auto kern = &fw_b_partials_kernel<S4, kDual>;
+  hipLaunchKernelGGL(kern, dim3((uint32_t)blocks), dim3(kBThreads), lds,
                      stream, k2b, aat, k2at, b, n, k, p.slice_w, p.n_slices, p.n_row_blocks, seg,
-                     keys, gap_part, stamps, epoch, status);
+                     keys, gap_part, stamps, xcd_work, epoch, status);
   return hipGetLastError();
 }
 
@@ -421,8 +496,7 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices) {
   p.slice_w = (uint32_t)align_up((k + n_slices - 1) / n_slices, 4);
   p.n_slices = (k + p.slice_w - 1) / p.slice_w;
   p.s4 = (p.slice_w + 255u) / 256u;
-  uint32_t rb = kBUnitsTarget / p.n_slices;
-  if (rb < 1) rb = 1;
+  uint32_t rb = p.n_slices > 1 ? kSlicedRowBlocks : kBUnitsTarget;
   if (rb > n) rb = n;
   p.n_row_blocks = rb;
   p.n_chunks = rb < kMaxChunks ? rb : kMaxChunks;
@@ -436,6 +510,8 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices) {
   off = align_up(off + units * sizeof(float), 256);
   p.off_stamp = off;
   off = align_up(off + units * sizeof(uint32_t), 256);
+  p.off_work = off;
+  off = align_up(off + kXcds * sizeof(uint32_t), 256);
   p.off_seg = off;
   if (p.n_slices > 1) off = align_up(off + (size_t)k * (p.n_slices + 1) * sizeof(uint32_t), 256);
   p.ws_bytes = off;
@@ -467,6 +543,7 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
   float *gap_part = reinterpret_cast<float *>(base + p.off_gap);
   uint32_t *stamps = reinterpret_cast<uint32_t *>(base + p.off_stamp);
   uint32_t *seg = p.n_slices > 1 ? reinterpret_cast<uint32_t *>(base + p.off_seg) : nullptr;
+  uint32_t *xcd_work = reinterpret_cast<uint32_t *>(base + p.off_work);
   hipError_t e;
   if (seg != nullptr) {
     const uint64_t total = (uint64_t)k * (p.n_slices + 1);
@@ -474,11 +551,18 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
                        stream, aat, k, p.slice_w, p.n_slices, seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // narrow slices give short AAt runs: gather two per wave instruction
+  // (that path addresses AAt with 32-bit byte offsets)
+  const bool dual = p.n_slices > 1 && aat.nnz < (1u << 30);
+  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, xcd_work, kXcds);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   switch (p.s4) {
 #define SEACELLS_B_CASE(S)                                                                      \
   case S:                                                                                       \
-    e = launch_partials<S>(p, k2b, aat, k2at, b, n, k, seg, keys, gap_part, stamps, epoch,      \
-                           status, stream);                                                     \
+    e = dual ? launch_partials<S, true>(p, k2b, aat, k2at, b, n, k, seg, keys, gap_part, stamps, \
+                                        xcd_work, epoch, status, stream)                        \
+             : launch_partials<S, false>(p, k2b, aat, k2at, b, n, k, seg, keys, gap_part,       \
+                                         stamps, xcd_work, epoch, status, stream);              \
     break;
     SEACELLS_B_CASE(1)
     SEACELLS_B_CASE(2)
