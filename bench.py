@@ -9,7 +9,10 @@ dominant kernel (algorithmic bytes per launch / average launch time from HIP
 events on the library's stream), and the f64 CPU oracle timed on a bounded
 sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--config c3] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--config c5] [--gpus 1]
+
+The default workload is the largest single-GPU configuration (n = 1M cells,
+k = 10000 archetypes); --config c1 .. c4 selects the smaller ones.
 """
 from __future__ import annotations
 
@@ -144,7 +147,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="c3")
+    ap.add_argument("--config", default="c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",

@@ -19,7 +19,7 @@
 //
 // Slices exist so k has no ceiling: a slice holds at most 2048 columns (8
 // KB of LDS and 64 registers per lane), and a segment table
-// seg[m, s] = first position of AAt row m with column >= s * slice_w
+// seg[s, m] = first position of AAt row m with column >= s * slice_w
 // hands each slice its run of every AAt row without a search.
 //
 // The reduce is two kernels: stage 1 takes u64 minima over groups of row
@@ -42,7 +42,8 @@ constexpr uint32_t kXcds = 8;        // MI355X: 8 XCDs of 32 CUs, each with its 
 constexpr size_t kSliceAatBytes = 5u << 19;  // AAt bytes per slice kept within one L2 (2.5 MB)
 constexpr uint32_t kMaxSlices = 128;
 constexpr uint32_t kSlicedRowBlocks = 4096;  // row ranges per slice when k is sliced
-constexpr uint32_t kAccPad = 32;             // floats between the two accumulators
+constexpr uint32_t kAccPad = 32;             // dummy slots after each dual accumulator
+constexpr uint32_t kStageSlots = kWave + 8;  // staged triples (a run of pairs reads past 64)
 
 // base[byte_off / 4] with a 32-bit byte offset from a wave-uniform base (the
 // array must hold fewer than 2^30 entries)
@@ -74,11 +75,11 @@ __device__ __forceinline__ bool row_ok(const Csr &m, uint32_t r, uint32_t &lo, u
 __global__ void __launch_bounds__(256)
     seg_table_kernel(Csr aat, uint32_t k, uint32_t slice_w, uint32_t n_slices,
                      uint32_t *__restrict__ seg) {
+  // slice-major: seg[s * k + m], so the lookups of one slice share lines
   const uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const uint64_t per_row = (uint64_t)n_slices + 1;
-  if (e >= (uint64_t)k * per_row) return;
-  const uint32_t m = (uint32_t)(e / per_row);
-  const uint32_t s = (uint32_t)(e - (uint64_t)m * per_row);
+  if (e >= (uint64_t)k * ((uint64_t)n_slices + 1)) return;
+  const uint32_t s = (uint32_t)(e / k);
+  const uint32_t m = (uint32_t)(e - (uint64_t)s * k);
   uint32_t lo, hi;
   row_ok(aat, m, lo, hi);
   if (s == n_slices) {
@@ -115,10 +116,13 @@ __global__ void __launch_bounds__(kBThreads)
   const uint32_t lane = lane_id();
   const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const uint32_t wpb = blockDim.x / kWave;
-  // the second accumulator sits kAccPad floats further on, so that equal
-  // columns of the two halves fall in different LDS banks
+  // dual: each accumulator is followed by one dummy slot per lane of its
+  // half (so the second one also starts 32 floats off the bank pattern of
+  // the first), then the staged entry triples
   constexpr uint32_t ACC2 = W + kAccPad;
-  float *acc = lds_acc + (size_t)wib * (kDual ? W + ACC2 : W);
+  constexpr uint32_t WAVE_FLOATS = kDual ? 2 * ACC2 + kStageSlots * 4 : W;
+  float *acc = lds_acc + (size_t)wib * WAVE_FLOATS;
+  uint4 *stage = reinterpret_cast<uint4 *>(acc + 2 * ACC2);
   const uint32_t half = kDual ? (lane >> 5) : 0u;
   const uint32_t hl = kDual ? (lane & 31u) : lane;  // lane within its half
   float *acc_h = acc + half * ACC2;                   // this half's accumulator
@@ -147,14 +151,24 @@ __global__ void __launch_bounds__(kBThreads)
 #pragma unroll
     for (uint32_t s4 = 0; s4 < S4; ++s4)
       *reinterpret_cast<float4 *>(acc + a * ACC2 + s4 * 256 + lane * 4) = zero4;
+  if constexpr (kDual) {
+    if (lane < kAccPad) acc[W + lane] = 0.0f, acc[ACC2 + W + lane] = 0.0f;
+    if (lane < kStageSlots - kWave) stage[kWave + lane] = make_uint4(0u, 0u, 0u, 0u);
+  }
   wave_lds_sync();
 
-  // units in slice-major order, taken one at a time from the XCD's counter:
-  // the XCD's waves sweep one slice before the next
-  for (;;) {
-    uint32_t u = 0;
-    if (lane == 0) u = atomicAdd(xcd_work + xcd, 1u);
-    u = __builtin_amdgcn_readfirstlane(u);
+  // units in slice-major order. With several slices they are taken one at
+  // a time from the XCD's counter, so the XCD's waves sweep one slice before
+  // the next; a single slice keeps a fixed order (one unit per wave or so).
+  const bool dynamic = n_slices > 1;
+  const uint32_t wx = (blockIdx.x / kXcds) * wpb + wib;
+  const uint32_t nwx = (gridDim.x / kXcds) * wpb;
+  for (uint32_t pass = 0;; ++pass) {
+    uint32_t u = wx + pass * nwx;
+    if (dynamic) {
+      if (lane == 0) u = atomicAdd(xcd_work + xcd, 1u);
+      u = __builtin_amdgcn_readfirstlane(u);
+    }
     if (u >= my_units) break;
     const uint32_t js = u / my_rb;
     const uint32_t rb = rb0 + (u - js * my_rb) * rb_step;
@@ -184,9 +198,8 @@ __global__ void __launch_bounds__(kBThreads)
           x = k2b.val[e];
           if (m < k) {
             if (seg != nullptr) {
-              const size_t sb = (size_t)m * (n_slices + 1) + sl;
-              lo = seg[sb];
-              hi = seg[sb + 1];
+              lo = seg[(size_t)sl * k + m];
+              hi = seg[(size_t)(sl + 1) * k + m];
             } else if (!row_ok(aat, m, lo, hi)) {
               flags |= kFlagBadIndex;
             }
@@ -197,38 +210,43 @@ __global__ void __launch_bounds__(kBThreads)
         const uint32_t cnt = (e1 - eb) < kWave ? (e1 - eb) : kWave;
         if constexpr (kDual) {
           // entries u + 2g (lanes 0-31) and u + 2g + 1 (lanes 32-63): runs of
-          // kGatherRows pairs in flight, 32 lanes per run
+          // kGatherRows pairs in flight, 32 lanes per run. Each chunk's
+          // (run start, run end, K2B value) goes through LDS once, and a half
+          // reads its entry's triple with one broadcast load.
+          stage[lane] = make_uint4(lo, lane < cnt ? hi : lo, __float_as_uint(x), 0u);
+          wave_lds_sync();
           for (uint32_t u = 0; u < cnt; u += 2 * kGatherRows) {
             uint32_t plo[kGatherRows], phi[kGatherRows];
             float xs[kGatherRows], va[kGatherRows], vb[kGatherRows];
             uint32_t ca[kGatherRows], cb[kGatherRows];
 #pragma unroll
             for (uint32_t g = 0; g < kGatherRows; ++g) {
-              const uint32_t s0 = u + 2 * g, s1 = s0 + 1;
-              const uint32_t r0 = s0 < kWave ? s0 : kWave - 1, r1 = s1 < kWave ? s1 : kWave - 1;
-              const uint32_t lo0 = readlane_u32(lo, r0), lo1 = readlane_u32(lo, r1);
-              const uint32_t hi0 = readlane_u32(hi, r0), hi1 = readlane_u32(hi, r1);
-              const float x0 = readlane_f32(x, r0), x1 = readlane_f32(x, r1);
-              const bool on = (half ? s1 : s0) < cnt;
-              plo[g] = on ? (half ? lo1 : lo0) : 0u;
-              phi[g] = on ? (half ? hi1 : hi0) : 0u;
-              xs[g] = half ? x1 : x0;
+              const uint4 t = stage[u + 2 * g + half];  // slots >= cnt hold empty runs
+              plo[g] = t.x;
+              phi[g] = t.y;
+              xs[g] = __uint_as_float(t.z);
               const uint32_t pa = plo[g] + hl, pb = pa + 32;
               ca[g] = kNoCol, va[g] = 0.0f, cb[g] = kNoCol, vb[g] = 0.0f;
               if (pa < phi[g]) ca[g] = load_at(aat.idx, pa * 4u), va[g] = load_at(aat.val, pa * 4u);
               if (pb < phi[g]) cb[g] = load_at(aat.idx, pb * 4u), vb[g] = load_at(aat.val, pb * 4u);
             }
+            // columns outside the slice (none for sorted rows; lanes without
+            // an entry) go to this lane's dummy slot past the accumulator
 #pragma unroll
             for (uint32_t g = 0; g < kGatherRows; ++g) {
               const uint32_t c_a = ca[g] - c0, c_b = cb[g] - c0;
-              if (c_a < cw) lds_add(acc_h + c_a, xs[g] * va[g]);
-              if (c_b < cw) lds_add(acc_h + c_b, xs[g] * vb[g]);
+              float *qa = acc_h + (c_a < cw ? c_a : W + hl);
+              float *qb = acc_h + (c_b < cw ? c_b : W + hl);
+              *qa = __builtin_fmaf(xs[g], va[g], *qa);
+              *qb = __builtin_fmaf(xs[g], vb[g], *qb);
               for (uint32_t p = plo[g] + 64 + hl; p < phi[g]; p += 32) {
                 const uint32_t c = load_at(aat.idx, p * 4u) - c0;
-                if (c < cw) lds_add(acc_h + c, xs[g] * load_at(aat.val, p * 4u));
+                float *q = acc_h + (c < cw ? c : W + hl);
+                *q = __builtin_fmaf(xs[g], load_at(aat.val, p * 4u), *q);
               }
             }
           }
+          wave_lds_sync();
           continue;
         }
         // kGatherRows AAt runs in flight at a time (their first two chunks);
@@ -449,8 +467,9 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
-  const uint32_t lds =
-      (kBThreads / kWave) * (kDual ? 2 * 256 * S4 + kAccPad : 256 * S4) * sizeof(float);
+  const uint32_t lds = (kBThreads / kWave) *
+                       (kDual ? 2 * (256 * S4 + kAccPad) + kStageSlots * 4 : 256 * S4) *
+                       sizeof(float);
   static int bpc = -1;
   if (bpc < 0) {
     int v = 0;
