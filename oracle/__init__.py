@@ -65,6 +65,12 @@ def _load():
         [ctypes.c_uint32] * 3 + [_U32P, _U32P, _F32P] * 3 + [_F64P, _U32P, ctypes.c_uint32,
                                                               _I64P, _F64P, _U32P, _F64P, _F64P,
                                                               _F64P, _F64P, ctypes.c_int])
+    lib.oracle_fw_a_columns_pruned.restype = ctypes.c_int
+    lib.oracle_fw_a_columns_pruned.argtypes = (
+        [ctypes.c_uint32] * 3 + [_U32P, _U32P, _F32P] * 3 + [_F64P, _U32P, ctypes.c_uint32,
+                                                              _I64P, ctypes.c_double, _F64P,
+                                                              _U32P, _F64P, _F64P, _F64P, _F64P,
+                                                              _U32P, _F64P, ctypes.c_int])
     lib.oracle_fw_b_argmin.restype = ctypes.c_int
     lib.oracle_fw_b_argmin.argtypes = (
         [ctypes.c_uint32] * 2 + [_U32P, _U32P, _F32P] * 4 + [_F64P, _U32P, _F64P, _F64P, _F64P,
@@ -123,15 +129,19 @@ class ATrace:
     g_second: np.ndarray   # [m, T]
     g_scale: np.ndarray    # [m, T]
     g_taken: np.ndarray    # [m, T] g at the index used for the update
+    drops: np.ndarray = None   # [m, T] weights dropped per step (pruned runs only)
+    margin: np.ndarray = None  # [m, T] min | |a| - threshold | before the drop (pruned runs)
 
 
 def fw_a_columns(t1, k2b, a_prev_t, n: int, k: int, T: int, cells=None, force=None,
-                 gamma=None, n_threads=None) -> ATrace:
+                 gamma=None, n_threads=None, prune=None) -> ATrace:
     """Oracle A update for ``cells`` (default: all n cells).
 
     ``force`` ([len(cells), T] int, -1 = free) replays another trajectory:
     the update takes the forced index while the oracle's own argmin and the
-    tie statistics are still reported for that state.
+    tie statistics are still reported for that state. ``prune`` (a
+    threshold >= 0) adds the page's drop-and-renormalise step after every
+    update and fills ``drops`` and ``margin``.
     """
     lib = _load()
     t1p = _csr(t1, k, k)
@@ -150,15 +160,21 @@ def fw_a_columns(t1, k2b, a_prev_t, n: int, k: int, T: int, cells=None, force=No
     a = np.empty((m, k), np.float64)
     pick = np.empty((m, T), np.uint32)
     gmin, g2, gs, gt = (np.empty((m, T), np.float64) for _ in range(4))
-    rc = lib.oracle_fw_a_columns(
-        n, k, T, _p(t1p[0], _U32P), _p(t1p[1], _U32P), _p(t1p[2], _F32P),
-        _p(k2p[0], _U32P), _p(k2p[1], _U32P), _p(k2p[2], _F32P),
-        _p(app[0], _U32P), _p(app[1], _U32P), _p(app[2], _F32P),
-        _p(gamma, _F64P), _p(cells, _U32P), m, _p(force, _I64P), _p(a, _F64P),
-        _p(pick, _U32P), _p(gmin, _F64P), _p(g2, _F64P), _p(gs, _F64P), _p(gt, _F64P),
-        _threads(n_threads))
+    ops = (n, k, T, _p(t1p[0], _U32P), _p(t1p[1], _U32P), _p(t1p[2], _F32P),
+           _p(k2p[0], _U32P), _p(k2p[1], _U32P), _p(k2p[2], _F32P),
+           _p(app[0], _U32P), _p(app[1], _U32P), _p(app[2], _F32P),
+           _p(gamma, _F64P), _p(cells, _U32P), m, _p(force, _I64P))
+    outs = (_p(pick, _U32P), _p(gmin, _F64P), _p(g2, _F64P), _p(gs, _F64P), _p(gt, _F64P))
+    if prune is None:
+        rc = lib.oracle_fw_a_columns(*ops, _p(a, _F64P), *outs, _threads(n_threads))
+        _check(rc)
+        return ATrace(cells, a, pick, gmin, g2, gs, gt)
+    drops = np.empty((m, T), np.uint32)
+    margin = np.empty((m, T), np.float64)
+    rc = lib.oracle_fw_a_columns_pruned(*ops, float(prune), _p(a, _F64P), *outs,
+                                        _p(drops, _U32P), _p(margin, _F64P), _threads(n_threads))
     _check(rc)
-    return ATrace(cells, a, pick, gmin, g2, gs, gt)
+    return ATrace(cells, a, pick, gmin, g2, gs, gt, drops, margin)
 
 
 @dataclass

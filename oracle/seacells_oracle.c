@@ -57,6 +57,10 @@ static int oracle_threads(int requested) {
 #endif
 }
 
+/* Weight sum at or below which the renormalisation is skipped (the page's
+ * `A_RENORM_FLOOR`, mirroring the CPU side's floor). */
+#define ORACLE_RENORM_FLOOR 1e-15
+
 /* Check a CSR: monotone row pointers, column indices below n_cols. */
 static int check_csr(uint32_t rows, uint32_t cols, const uint32_t *ptr,
                      const uint32_t *idx) {
@@ -92,16 +96,17 @@ static int check_csr(uint32_t rows, uint32_t cols, const uint32_t *ptr,
  * (trace replay); the oracle's own argmin is still reported in pick.
  * a_out: [n_cells * k] dense f64 result.
  */
-int oracle_fw_a_columns(uint32_t n, uint32_t k, uint32_t T,
-                        const uint32_t *t1_ptr, const uint32_t *t1_idx,
-                        const float *t1_val, const uint32_t *k2b_ptr,
-                        const uint32_t *k2b_idx, const float *k2b_val,
-                        const uint32_t *ap_ptr, const uint32_t *ap_idx,
-                        const float *ap_val, const double *gamma,
-                        const uint32_t *cells, uint32_t n_cells,
-                        const int64_t *force, double *a_out, uint32_t *pick,
-                        double *g_min, double *g_second, double *g_scale,
-                        double *g_taken, int n_threads) {
+static int fw_a_columns_impl(uint32_t n, uint32_t k, uint32_t T,
+                             const uint32_t *t1_ptr, const uint32_t *t1_idx,
+                             const float *t1_val, const uint32_t *k2b_ptr,
+                             const uint32_t *k2b_idx, const float *k2b_val,
+                             const uint32_t *ap_ptr, const uint32_t *ap_idx,
+                             const float *ap_val, const double *gamma,
+                             const uint32_t *cells, uint32_t n_cells,
+                             const int64_t *force, int prune, double threshold,
+                             double *a_out, uint32_t *pick, double *g_min,
+                             double *g_second, double *g_scale, double *g_taken,
+                             uint32_t *drops, double *margin, int n_threads) {
     if (k == 0 || !t1_val || !k2b_val || !ap_val || !cells || !a_out)
         return ORACLE_E_ARG;
     int rc;
@@ -171,12 +176,88 @@ int oracle_fw_a_columns(uint32_t n, uint32_t k, uint32_t T,
                 const double gam = gamma ? gamma[t] : 2.0 / ((double)t + 2.0);
                 for (uint32_t c = 0; c < k; ++c) a[c] *= (1.0 - gam);
                 a[take] += gam;
+
+                if (prune) {
+                    /* drop every non-zero weight with |a| <= threshold, then
+                       scale the rest back to unit sum unless the sum is at or
+                       below the floor */
+                    uint32_t nd = 0;
+                    double near = INFINITY;
+                    for (uint32_t c = 0; c < k; ++c) {
+                        if (a[c] == 0.0) continue;
+                        const double d = fabs(fabs(a[c]) - threshold);
+                        if (d < near) near = d;
+                        if (!(a[c] > threshold || a[c] < -threshold)) {
+                            a[c] = 0.0;
+                            ++nd;
+                        }
+                    }
+                    double total = 0.0;
+                    for (uint32_t c = 0; c < k; ++c) total += a[c];
+                    if (total > ORACLE_RENORM_FLOOR) {
+                        const double r = 1.0 / total;
+                        for (uint32_t c = 0; c < k; ++c) a[c] *= r;
+                    }
+                    if (drops) drops[e] = nd;
+                    if (margin) margin[e] = near;
+                }
             }
         }
         free(t2);
         free(w);
     }
     return fail ? ORACLE_E_ALLOC : 0;
+}
+
+int oracle_fw_a_columns(uint32_t n, uint32_t k, uint32_t T,
+                        const uint32_t *t1_ptr, const uint32_t *t1_idx,
+                        const float *t1_val, const uint32_t *k2b_ptr,
+                        const uint32_t *k2b_idx, const float *k2b_val,
+                        const uint32_t *ap_ptr, const uint32_t *ap_idx,
+                        const float *ap_val, const double *gamma,
+                        const uint32_t *cells, uint32_t n_cells,
+                        const int64_t *force, double *a_out, uint32_t *pick,
+                        double *g_min, double *g_second, double *g_scale,
+                        double *g_taken, int n_threads) {
+    return fw_a_columns_impl(n, k, T, t1_ptr, t1_idx, t1_val, k2b_ptr, k2b_idx,
+                             k2b_val, ap_ptr, ap_idx, ap_val, gamma, cells,
+                             n_cells, force, 0, 0.0, a_out, pick, g_min,
+                             g_second, g_scale, g_taken, NULL, NULL, n_threads);
+}
+
+/*
+ * A update with pruning and renormalisation (`fw_columns_a_gpu` with
+ * `pruning`, its comments on dropping and renormalising, and
+ * `A_RENORM_FLOOR`).
+ *
+ * Each step is the step above, followed by:
+ *     every weight with a[c] != 0 and -threshold <= a[c] <= threshold is set
+ *     to 0 (dropped; its slot is kept, so a later pick of c starts from 0);
+ *     total = sum_c a[c]; if total > 1e-15, a = a / total (as a * (1/total)).
+ * The gradient of the next step is recomputed from the new a, which is what
+ * the page's incremental correction of w (subtract each dropped atom's t1 row,
+ * scale by the renormalisation factor) maintains.
+ * Extra trace outputs ([n_cells * T], nullable):
+ *   drops  - number of weights dropped at step t
+ *   margin - min over the non-zero weights before the drop of
+ *            | |a[c]| - threshold | (+inf when there are none): how close the
+ *            step's drop decisions were
+ */
+int oracle_fw_a_columns_pruned(
+    uint32_t n, uint32_t k, uint32_t T, const uint32_t *t1_ptr,
+    const uint32_t *t1_idx, const float *t1_val, const uint32_t *k2b_ptr,
+    const uint32_t *k2b_idx, const float *k2b_val, const uint32_t *ap_ptr,
+    const uint32_t *ap_idx, const float *ap_val, const double *gamma,
+    const uint32_t *cells, uint32_t n_cells, const int64_t *force,
+    double threshold, double *a_out, uint32_t *pick, double *g_min,
+    double *g_second, double *g_scale, double *g_taken, uint32_t *drops,
+    double *margin, int n_threads) {
+    if (!(threshold >= 0.0)) return ORACLE_E_ARG;
+    return fw_a_columns_impl(n, k, T, t1_ptr, t1_idx, t1_val, k2b_ptr, k2b_idx,
+                             k2b_val, ap_ptr, ap_idx, ap_val, gamma, cells,
+                             n_cells, force, 1, threshold, a_out, pick, g_min,
+                             g_second, g_scale, g_taken, drops, margin,
+                             n_threads);
 }
 
 /*

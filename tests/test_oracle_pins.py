@@ -493,3 +493,119 @@ def test_b_apply_matches_convex_step():
     with pytest.raises(RuntimeError):
         oracle.fw_b_apply(full_idx, full_val, np.full(k, cap_b, np.uint32),
                           np.full(k, n - 1, np.uint32), gam)
+
+
+# --------------------------------------------------------------------------
+# P9: the pruning + renormalisation variant of the A update (the page's
+# `fw_columns_a_gpu` with `pruning`, and `A_RENORM_FLOOR`)
+# --------------------------------------------------------------------------
+
+def _dense(m):
+    return np.asarray(m.todense(), np.float64)
+
+
+def _prune_ref(a, thr):
+    """Drop-and-renormalise written out on one dense column (numpy)."""
+    a = a.copy()
+    drop = (a != 0.0) & (np.abs(a) <= thr)
+    a[drop] = 0.0
+    tot = a.sum()
+    if tot > 1e-15:
+        a = a * (1.0 / tot)
+    return a, int(drop.sum())
+
+
+def test_p9_threshold_zero_only_renormalises(c1):
+    # nothing can drop at threshold 0 (the weights are >= 0 and 0 is exempt),
+    # and a column that sums to 1 is renormalised by a factor 1 +- rounding
+    w = c1
+    r0 = oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, w.T)
+    r1 = oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, w.T, prune=0.0)
+    assert r1.drops.sum() == 0
+    np.testing.assert_array_equal(r0.pick, r1.pick)
+    np.testing.assert_allclose(r1.a, r0.a, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", ["c1", "empty"])
+def test_p9_threshold_above_one_drops_everything(case, c1):
+    # every weight is <= 1, so every step ends with a = 0 (the sum is 0 and the
+    # renormalisation is skipped); the gradient from step 1 on is -t2_j, whose
+    # lowest argmin is the lowest column holding the row's maximum (column 0
+    # for an empty K2B row)
+    if case == "c1":
+        w = c1
+    else:
+        w = W.random_workload(90, 9, s_a=3, seed=41, empty_k2b_every=4)
+    r = oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, w.T, prune=2.0)
+    r0 = oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, 1)
+    np.testing.assert_array_equal(r.pick[:, 0], r0.pick[:, 0])
+    t2 = _dense(w.k2b)
+    want = np.argmin(-t2, axis=1)   # numpy's argmin returns the first minimum
+    for t in range(1, w.T):
+        np.testing.assert_array_equal(r.pick[:, t], want)
+    assert np.all(r.a == 0.0)
+    assert np.all(r.drops >= 1)
+
+
+def _first_drop_cases():
+    rng = np.random.default_rng(9)
+    out = []
+    for seed in range(8):
+        w = W.random_workload(16, 6, t1_per_row=4, k2b_per_row=3, s_a=3, seed=100 + seed, T=24)
+        out.append((w, 0.0371 + 0.01 * rng.random()))
+    return out
+
+
+def test_p9_drops_and_renormalisation_follow_the_unpruned_state():
+    # Up to the first step whose updated weights include one at or below the
+    # threshold, the pruned run is the plain run (renormalised by 1 +- eps);
+    # at that step exactly those weights drop and the rest is divided by its
+    # sum; the next pick is the argmin of the dense gradient of that column.
+    checked = 0
+    for w, thr in _first_drop_cases():
+        t1, t2 = _dense(w.t1), _dense(w.k2b)
+        for j in range(w.n):
+            cells = np.array([j])
+            prev = _dense(w.a_prev_t)[j]
+            # unpruned weights after every step, from runs of length 1..T
+            states = [oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, t + 1,
+                                          cells=cells).a[0] for t in range(w.T)]
+            rp = oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, w.T, cells=cells,
+                                     prune=thr)
+            td = next((t for t, a in enumerate(states)
+                       if np.any((a != 0) & (np.abs(a) <= thr))), None)
+            if td is None or td + 1 >= w.T:
+                continue
+            a = states[td]
+            nz = a[a != 0]
+            if np.min(np.abs(np.abs(nz) - thr)) < 1e-9:
+                continue  # a decision on the threshold itself: not a fair case
+            ru = oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, w.T, cells=cells)
+            np.testing.assert_array_equal(rp.pick[0, :td + 1], ru.pick[0, :td + 1])
+            assert np.all(rp.drops[0, :td] == 0)
+            want_a, nd = _prune_ref(a, thr)
+            assert rp.drops[0, td] == nd >= 1
+            got = oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, td + 1, cells=cells,
+                                      prune=thr).a[0]
+            np.testing.assert_allclose(got, want_a, rtol=0, atol=1e-12)
+            g = t1 @ want_a - t2[j]
+            srt = np.sort(g)
+            if srt.shape[0] > 1 and srt[1] - srt[0] < 1e-9:
+                continue  # tie: the order of rounding decides
+            assert rp.pick[0, td + 1] == int(np.argmin(g))
+            checked += 1
+    assert checked >= 12
+
+
+def test_p9_invariants_after_every_prefix(c1):
+    # after any number of steps: weights >= 0, none in (0, threshold], and the
+    # column sums to 1 unless everything was dropped
+    w = c1
+    thr = 0.0213
+    cells = np.arange(0, w.n, 37)
+    for T in (1, 2, 7, 19, 50):
+        r = oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, T, cells=cells, prune=thr)
+        assert np.all(r.a >= 0.0)
+        assert not np.any((r.a > 0.0) & (r.a <= thr))
+        s = r.a.sum(axis=1)
+        assert np.all((np.abs(s - 1.0) < 1e-12) | (s == 0.0))
