@@ -6,7 +6,8 @@
  * kernel archetypal analysis, min ||K - K B A||_F^2 over column-stochastic
  * B (n x k) and A (k x n), on one GPU:
  *
- *   - the per-cell A column solve (seacells_fw_a_columns);
+ *   - the per-cell A column solve (seacells_fw_a_columns), and its pruning
+ *     variant (seacells_fw_a_columns_pruned);
  *   - the per-archetype B-gradient argmin over cells (seacells_fw_b_argmin)
  *     and the B step that consumes it (seacells_fw_b_apply).
  *
@@ -128,6 +129,30 @@ int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
                           uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
                           uint32_t *trace, void *workspace, size_t workspace_bytes,
                           uint32_t *status, seacells_stream_t stream);
+
+/*
+ * A update with pruning and renormalisation: `fw_columns_a_gpu` with
+ * `pruning` on the source page (its comments on dropping below the threshold
+ * and renormalising the survivors, and `A_RENORM_FLOOR`).
+ *
+ * Every step is the step of seacells_fw_a_columns, then:
+ *     every atom weight with a != 0 and -threshold <= a <= threshold becomes
+ *     0 (its slot stays, so a later pick of that index lands back in it);
+ *     total = sum of the weights; if total > 1e-15 every weight is multiplied
+ *     by 1 / total (and the gradient state with it).
+ * threshold   f32, finite and >= 0 (else SEACELLS_E_SHAPE); compared in f32.
+ * Other arguments, outputs, errors and the workspace
+ * (seacells_fw_a_columns_workspace covers both entry points) are those of
+ * seacells_fw_a_columns; atom_val holds 0 for a dropped slot. A cell that
+ * drops an atom is finished by the dense-state kernel, so pruning that bites
+ * costs more than the plain update.
+ */
+int seacells_fw_a_columns_pruned(const seacells_csr *t1, const seacells_csr *k2b,
+                                 const seacells_csr *a_prev_t, uint32_t n, uint32_t k,
+                                 uint32_t T, uint32_t cap, const float *gamma, float threshold,
+                                 uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
+                                 uint32_t *trace, void *workspace, size_t workspace_bytes,
+                                 uint32_t *status, seacells_stream_t stream);
 
 /*
  * Workspace bytes seacells_fw_b_argmin needs for these sizes (always > 0).

@@ -70,18 +70,23 @@ extern "C" {
 
 size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint32_t cap) {
   if (n == 0 || k == 0 || cap == 0) return 0;
-  return plan_a(n, k, T, cap).ws_bytes;
+  // one size covers the plain and the pruning entry point
+  const size_t plain = plan_a(n, k, T, cap, false).ws_bytes;
+  const size_t pruned = plan_a(n, k, T, cap, true).ws_bytes;
+  return plain > pruned ? plain : pruned;
 }
 
-int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
-                          const seacells_csr *a_prev_t, uint32_t n, uint32_t k, uint32_t T,
-                          uint32_t cap, const float *gamma, uint32_t *atom_idx, float *atom_val,
-                          uint32_t *atom_cnt, uint32_t *trace, void *workspace,
-                          size_t workspace_bytes, uint32_t *status, seacells_stream_t stream) {
+static int a_columns(const seacells_csr *t1, const seacells_csr *k2b,
+                     const seacells_csr *a_prev_t, uint32_t n, uint32_t k, uint32_t T,
+                     uint32_t cap, const float *gamma, bool prune, float threshold,
+                     uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt, uint32_t *trace,
+                     void *workspace, size_t workspace_bytes, uint32_t *status,
+                     seacells_stream_t stream) {
   if (t1 == nullptr || k2b == nullptr || a_prev_t == nullptr || atom_idx == nullptr ||
       atom_val == nullptr || atom_cnt == nullptr || status == nullptr)
     return SEACELLS_E_NULL;
   if (n == 0 || k == 0 || T == 0 || cap == 0) return SEACELLS_E_SHAPE;
+  if (prune && !(threshold >= 0.0f && threshold <= 3.4e38f)) return SEACELLS_E_SHAPE;
   if (n >= 0x80000000u || k >= 0x80000000u) return SEACELLS_E_TOO_LARGE;
   int rc;
   if ((rc = check_csr(t1, k, k)) != SEACELLS_OK) return rc;
@@ -90,7 +95,7 @@ int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
   if ((uint64_t)n * cap >= (1ull << 40) || (uint64_t)n * T >= (1ull << 40))
     return SEACELLS_E_TOO_LARGE;
   if (cap >= 0x10000000u) return SEACELLS_E_TOO_LARGE;
-  const APlan plan = plan_a(n, k, T, cap);
+  const APlan plan = plan_a(n, k, T, cap, prune);
   // per-wave LDS must at least hold the atom list
   if (plan.waves_per_block == 0) return SEACELLS_E_TOO_LARGE;
   if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))
@@ -98,10 +103,29 @@ int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = launch_status_clear(status, s);
   if (e != hipSuccess) return hip_fail(e, "status clear");
-  e = launch_fw_a(plan, as_csr(t1), as_csr(k2b), as_csr(a_prev_t), n, k, T, cap, gamma, atom_idx,
-                  atom_val, atom_cnt, trace, workspace, status, s);
+  e = launch_fw_a(plan, as_csr(t1), as_csr(k2b), as_csr(a_prev_t), n, k, T, cap, gamma,
+                  threshold, atom_idx, atom_val, atom_cnt, trace, workspace, status, s);
   if (e != hipSuccess) return hip_fail(e, "fw_a_columns launch");
   return SEACELLS_OK;
+}
+
+int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
+                          const seacells_csr *a_prev_t, uint32_t n, uint32_t k, uint32_t T,
+                          uint32_t cap, const float *gamma, uint32_t *atom_idx, float *atom_val,
+                          uint32_t *atom_cnt, uint32_t *trace, void *workspace,
+                          size_t workspace_bytes, uint32_t *status, seacells_stream_t stream) {
+  return a_columns(t1, k2b, a_prev_t, n, k, T, cap, gamma, false, 0.0f, atom_idx, atom_val,
+                   atom_cnt, trace, workspace, workspace_bytes, status, stream);
+}
+
+int seacells_fw_a_columns_pruned(const seacells_csr *t1, const seacells_csr *k2b,
+                                 const seacells_csr *a_prev_t, uint32_t n, uint32_t k,
+                                 uint32_t T, uint32_t cap, const float *gamma, float threshold,
+                                 uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
+                                 uint32_t *trace, void *workspace, size_t workspace_bytes,
+                                 uint32_t *status, seacells_stream_t stream) {
+  return a_columns(t1, k2b, a_prev_t, n, k, T, cap, gamma, true, threshold, atom_idx, atom_val,
+                   atom_cnt, trace, workspace, workspace_bytes, status, stream);
 }
 
 size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k) {

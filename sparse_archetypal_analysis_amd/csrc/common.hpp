@@ -117,6 +117,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // --- A update -------------------------------------------------------------
 struct APlan {
+  bool prune;                  // the pruning + renormalisation variant
   uint32_t group;              // lanes per cell (16, 32 or 64)
   uint32_t kpad;               // scan length: k + 1 rounded up to 4 * group (padding holds +inf)
   uint32_t waves_per_block;    // 0: the atom list alone does not fit in LDS
@@ -135,11 +136,11 @@ struct APlan {
   size_t ws_dense_off;         // dense state slices
   size_t ws_bytes;
 };
-APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap);
+APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap, bool prune);
 hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, uint32_t k,
-                       uint32_t T, uint32_t cap, const float *gamma, uint32_t *atom_idx,
-                       float *atom_val, uint32_t *atom_cnt, uint32_t *trace, void *ws,
-                       uint32_t *status, hipStream_t stream);
+                       uint32_t T, uint32_t cap, const float *gamma, float prune_thr,
+                       uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt, uint32_t *trace,
+                       void *ws, uint32_t *status, hipStream_t stream);
 
 // --- B argmin -------------------------------------------------------------
 struct BPlan {

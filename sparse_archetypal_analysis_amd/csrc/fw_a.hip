@@ -57,6 +57,7 @@ constexpr uint32_t kSupWideWaves = 16;      // the same with 512 t2 entries in r
 constexpr uint32_t kSupLongWaves = 8;       // the same for the pass over long K2B rows
 constexpr uint32_t kSupMinHc = 256;         // smallest useful t2 capacity
 constexpr uint32_t kSupMaxHc = 8192;
+constexpr float kRenormFloor = 1e-15f;      // the page's A_RENORM_FLOOR
 
 struct StepSched {
   float gam;    // gamma_t
@@ -189,7 +190,9 @@ __device__ __forceinline__ uint32_t dense_argmin(const float *h, uint32_t nch, u
 // uniform trip counts, a ballot walk for the index of the t2 minimum).
 constexpr uint32_t kWaveAtomSlots = 2;  // atom slots per lane in registers
 
-template <bool kHInLds, bool kRegAtoms>
+// kPrune: after every step, drop the atoms at or below the threshold and
+// renormalise (the page's pruning variant); the scale s is then per cell.
+template <bool kHInLds, bool kRegAtoms, bool kPrune>
 __global__ void __launch_bounds__(kABlockMaxThreads)
     fw_a_wave_kernel(const uint32_t *__restrict__ t1_ptr, const uint32_t *__restrict__ t1_idx,
                         const float *__restrict__ t1_val, uint32_t t1_nnz,
@@ -203,7 +206,8 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
                         uint32_t *__restrict__ trace, float *__restrict__ state_ws,
                         uint32_t sched_words, uint32_t lds_words_per_wave, uint32_t dense_only,
                         const uint32_t *__restrict__ cell_list,
-                        const uint32_t *__restrict__ cell_count, uint32_t *__restrict__ status) {
+                        const uint32_t *__restrict__ cell_count, float prune_thr,
+                        uint32_t *__restrict__ status) {
   extern __shared__ uint32_t lds[];
   const uint32_t lane = lane_id();
   const uint32_t wib = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -387,6 +391,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
     wave_lds_sync();
 
     float s_run = 1.0f;
+    float s_cell = 1.0f;  // this cell's scale (pruning only)
     for (uint32_t t = 0; t < T; ++t) {
       const StepSched sc = sched_words != 0 ? sched[t] : sched_step(gamma, t, s_run, flags);
 
@@ -432,24 +437,93 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       }
 
       // -- state: restart when gamma == 1, fold the scale back in when due
+      // (with pruning the scale is this cell's own: s_k = s * (1 - gamma))
+      float alpha = sc.alpha, fold = sc.fold, s_k = 1.0f;
+      if constexpr (kPrune) {
+        s_k = sc.keep == 0.0f ? 1.0f : s_cell * sc.keep;
+        fold = 0.0f;
+        if (sc.keep != 0.0f && s_k < 0x1p-64f) fold = s_k, s_k = 1.0f;
+        alpha = sc.gam / s_k;
+      }
       if (sc.keep == 0.0f) {
         clear_state<kWave>(h, k, nch, lane);
         mono = dense_only == 0;
-      } else if (sc.fold > 0.0f) {
+      } else if (fold > 0.0f) {
         for (uint32_t i = 0; i < nch; ++i) {
           float4 *q = reinterpret_cast<float4 *>(h + i * 256 + lane * 4);
           float4 v = *q;
-          v.x *= sc.fold, v.y *= sc.fold, v.z *= sc.fold, v.w *= sc.fold;
+          v.x *= fold, v.y *= fold, v.z *= fold, v.w *= fold;
           *q = v;
         }
         mono = false;
       }
       wave_lds_sync();
       // -- h += alpha * t1[idx, :]
-      if (scatter_row(idx, sc.alpha)) mono = false;
+      if (scatter_row(idx, alpha)) mono = false;
       wave_lds_sync();
-      // -- h -= alpha * t2
-      t2_pass(sc.alpha);
+      float beta = alpha;
+      if constexpr (kPrune) {
+        // -- drop: every non-zero weight with |a| <= threshold goes to 0 (its
+        // slot stays), and its t1 row leaves w, slot by slot
+        for (uint32_t c0 = 0; c0 < cnt; c0 += kWave) {
+          float dv = 0.0f;
+          uint32_t dm = 0;
+          bool drop = false;
+          if constexpr (kRegAtoms) {
+#pragma unroll
+            for (uint32_t j = 0; j < kWaveAtomSlots; ++j) {
+              if (j * kWave == c0) {
+                const float v = aval[j];
+                drop = c0 + lane < cnt && v != 0.0f && !(v > prune_thr || v < -prune_thr);
+                if (drop) dv = v, dm = aidx[j], aval[j] = 0.0f;
+              }
+            }
+          } else {
+            const uint32_t sl = c0 + lane;
+            if (sl < cnt) {
+              const float v = s_aval[sl];
+              drop = v != 0.0f && !(v > prune_thr || v < -prune_thr);
+              if (drop) dv = v, dm = s_aidx[sl], s_aval[sl] = 0.0f;
+            }
+          }
+          for (uint64_t msk = __ballot(drop); msk != 0; msk &= msk - 1) {
+            const uint32_t l = (uint32_t)__builtin_ctzll(msk);
+            const uint32_t m = readlane_u32(dm, l);
+            const float d = readlane_f32(dv, l);
+            if (m < k) {
+              scatter_row(m, -d / s_k);
+              mono = false;  // products leave w: only a dense scan decides
+            }
+            wave_lds_sync();
+          }
+        }
+        // -- renormalise: a and w by 1 / sum(a) unless the sum is at or below
+        // the floor; in g = s h form the factor goes into s, and the t2 term,
+        // which it must not scale, gets a correction in the pass below
+        float part = 0.0f;
+        if constexpr (kRegAtoms) {
+#pragma unroll
+          for (uint32_t j = 0; j < kWaveAtomSlots; ++j) part += aval[j];
+        } else {
+          for (uint32_t sl = lane; sl < cnt; sl += kWave) part += s_aval[sl];
+        }
+        const float total = wave_sum_f32(part);  // the same in every lane
+        float r = 1.0f;
+        if (total > kRenormFloor) {
+          r = 1.0f / total;
+          beta = alpha - (1.0f - total) / s_k;
+          if constexpr (kRegAtoms) {
+#pragma unroll
+            for (uint32_t j = 0; j < kWaveAtomSlots; ++j) aval[j] *= r;
+          } else {
+            for (uint32_t sl = lane; sl < cnt; sl += kWave) s_aval[sl] *= r;
+          }
+        }
+        s_cell = s_k * r;
+        wave_lds_sync();
+      }
+      // -- h -= beta * t2
+      t2_pass(beta);
       wave_lds_sync();
     }
 
@@ -828,7 +902,9 @@ constexpr uint32_t kTailPos = 0x80000000u;  // marks a t2 position (not a column
 constexpr uint32_t kRowBatch = 2;   // chunks of a t1 row whose loads are in flight together
 
 // TR: chunks of 64 t2 entries held in registers (the rest are re-read).
-template <uint32_t TR>
+// kPrune: the pruning variant; a step that drops an atom sends the cell to
+// the dense kernel, the renormalisation is done here as the dense kernel does.
+template <uint32_t TR, bool kPrune>
 __global__ void __launch_bounds__(kABlockMaxThreads)
     fw_a_support_kernel(const uint32_t *__restrict__ t1_ptr, const uint32_t *__restrict__ t1_idx,
                         const float *__restrict__ t1_val, uint32_t t1_nnz,
@@ -840,7 +916,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
                         uint32_t *__restrict__ atom_idx, float *__restrict__ atom_val,
                         uint32_t *__restrict__ atom_cnt, uint32_t *__restrict__ trace,
                         uint32_t nwords, uint32_t hc_cap, uint32_t sched_words,
-                        uint32_t lds_words_per_wave, SupQueues q,
+                        uint32_t lds_words_per_wave, SupQueues q, float prune_thr,
                         uint32_t *__restrict__ status) {
   extern __shared__ uint32_t lds[];
   const uint32_t lane = lane_id();
@@ -1101,9 +1177,18 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
     wave_lds_sync();
 
     uint32_t acov = 0;  // bit j: the row of the atom in slot j is marked in cov
+    float s_cell = 1.0f;  // this cell's scale (pruning only)
     for (uint32_t t = 0; t < T && !deferred; ++t) {
       const StepSched sc = sched[t];
-      if (sc.fold > 0.0f) {
+      float alpha = sc.alpha, s_k = 1.0f;
+      if constexpr (kPrune) {
+        s_k = sc.keep == 0.0f ? 1.0f : s_cell * sc.keep;
+        if (sc.keep != 0.0f && s_k < 0x1p-64f) {
+          deferred = true;
+          break;
+        }
+        alpha = sc.gam / s_k;
+      } else if (sc.fold > 0.0f) {
         deferred = true;
         break;
       }
@@ -1181,13 +1266,39 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       }
       wave_lds_sync();
       // -- h += alpha * t1[idx, :]
-      if (scatter_row(p0, p1, sc.alpha, cover, nq)) {
+      if (scatter_row(p0, p1, alpha, cover, nq)) {
         deferred = true;
         break;
       }
       wave_lds_sync();
-      // -- h -= alpha * t2
-      t2_pass(sc.alpha);
+      float beta = alpha;
+      if constexpr (kPrune) {
+        // a drop subtracts products from w: the dense kernel takes the cell
+        bool drop = false;
+#pragma unroll
+        for (uint32_t j = 0; j < kWaveAtomSlots; ++j)
+          drop |= j * kWave + lane < cnt && aval[j] != 0.0f &&
+                  !(aval[j] > prune_thr || aval[j] < -prune_thr);
+        if (__ballot(drop) != 0) {
+          deferred = true;
+          break;
+        }
+        // renormalise exactly as the dense kernel does
+        float part = 0.0f;
+#pragma unroll
+        for (uint32_t j = 0; j < kWaveAtomSlots; ++j) part += aval[j];
+        const float total = wave_sum_f32(part);
+        float r = 1.0f;
+        if (total > kRenormFloor) {
+          r = 1.0f / total;
+          beta = alpha - (1.0f - total) / s_k;
+#pragma unroll
+          for (uint32_t j = 0; j < kWaveAtomSlots; ++j) aval[j] *= r;
+        }
+        s_cell = s_k * r;
+      }
+      // -- h -= beta * t2
+      t2_pass(beta);
       wave_lds_sync();
     }
 
@@ -1272,23 +1383,23 @@ hipError_t launch_variant(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr 
                           uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
                           uint32_t *trace, void *ws, uint32_t dense_only,
                           const uint32_t *cell_list, const uint32_t *cell_count,
-                          uint32_t *status, hipStream_t stream) {
-  static bool configured = false;
-  auto kern = [] {
-    if constexpr (G == kWave)
-      return &fw_a_wave_kernel<kHInLds, kRegAtoms>;
-    else
-      return &fw_a_group_kernel<G, kHInLds, kRegAtoms>;
-  }();
-  auto fn = reinterpret_cast<const void *>(kern);
+                          float prune_thr, uint32_t *status, hipStream_t stream) {
+  static bool configured[2] = {false, false};
+  const bool prune = plan.prune;  // (the plan takes one cell per wave when pruning)
+  const void *fn;
+  if constexpr (G == kWave)
+    fn = prune ? reinterpret_cast<const void *>(&fw_a_wave_kernel<kHInLds, kRegAtoms, true>)
+               : reinterpret_cast<const void *>(&fw_a_wave_kernel<kHInLds, kRegAtoms, false>);
+  else
+    fn = reinterpret_cast<const void *>(&fw_a_group_kernel<G, kHInLds, kRegAtoms>);
   const uint32_t wpb = plan.waves_per_block;
   const uint32_t threads = wpb * kWave;
   const uint32_t lds_bytes = plan.sched_words * 4 + wpb * plan.lds_per_wave;
   hipError_t e;
-  if (!configured) {
+  if (!configured[prune]) {
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytesPerCU);
     if (e != hipSuccess) return e;
-    configured = true;
+    configured[prune] = true;
   }
   uint32_t blocks;
   const uint32_t cpw = kWave / G;
@@ -1305,12 +1416,15 @@ hipError_t launch_variant(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr 
   }
   float *state_ws = reinterpret_cast<float *>(static_cast<char *>(ws) + plan.ws_dense_off);
   if constexpr (G == kWave) {
+    auto kern = prune ? &fw_a_wave_kernel<kHInLds, kRegAtoms, true>
+                      : &fw_a_wave_kernel<kHInLds, kRegAtoms, false>;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr, t1.idx,
                        t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
                        ap.val, ap.nnz, n, k, plan.kpad, T, cap, gamma, atom_idx, atom_val,
                        atom_cnt, trace, state_ws, plan.sched_words, plan.lds_per_wave / 4,
-                       dense_only, cell_list, cell_count, status);
+                       dense_only, cell_list, cell_count, prune_thr, status);
   } else {
+    auto kern = &fw_a_group_kernel<G, kHInLds, kRegAtoms>;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr, t1.idx,
                        t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
                        ap.val, ap.nnz, n, k, plan.kpad, T, cap, gamma, atom_idx, atom_val,
@@ -1324,21 +1438,24 @@ hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, uint32_t tie
                           Csr k2b, Csr ap, uint32_t n, uint32_t k, uint32_t T, uint32_t cap,
                           const float *gamma, uint32_t *atom_idx, float *atom_val,
                           uint32_t *atom_cnt, uint32_t *trace, const SupQueues &q,
-                          uint32_t *status, hipStream_t stream) {
+                          float prune_thr, uint32_t *status, hipStream_t stream) {
   // t2 entries in registers: 256 for short K2B rows, 512 when rows are long
   // on average (the first pass) or by construction (the long-row pass)
   const bool wide = tier > 0 || k2b.nnz > (uint64_t)n * 192u;
   const uint32_t waves = tier > 0 ? kSupLongWaves : first_pass_waves(plan, wide);
   uint32_t hc_cap = 0, lpw = 0;
   if (!support_tier_size(plan, waves, hc_cap, lpw)) return hipErrorInvalidValue;
-  auto kern = wide ? &fw_a_support_kernel<8> : &fw_a_support_kernel<4>;
+  const bool prune = plan.prune;
+  auto kern = wide ? (prune ? &fw_a_support_kernel<8, true> : &fw_a_support_kernel<8, false>)
+                   : (prune ? &fw_a_support_kernel<4, true> : &fw_a_support_kernel<4, false>);
   auto fn = reinterpret_cast<const void *>(kern);
-  static bool configured[2] = {false, false};
+  static bool configured[4] = {false, false, false, false};
+  const int which = (wide ? 2 : 0) + (prune ? 1 : 0);
   hipError_t e;
-  if (!configured[wide]) {
+  if (!configured[which]) {
     e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytesPerCU);
     if (e != hipSuccess) return e;
-    configured[wide] = true;
+    configured[which] = true;
   }
   const uint32_t wpb = kSupWavesPerBlock;
   const uint32_t threads = wpb * kWave;
@@ -1353,7 +1470,7 @@ hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, uint32_t tie
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr,
                      t1.idx, t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
                      ap.val, ap.nnz, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt, trace,
-                     plan.nwords, hc_cap, plan.sched_words, lpw / 4, q, status);
+                     plan.nwords, hc_cap, plan.sched_words, lpw / 4, q, prune_thr, status);
   return hipGetLastError();
 }
 
@@ -1379,9 +1496,10 @@ uint32_t group_width(uint32_t k) {
 
 }  // namespace
 
-APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap) {
+APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap, bool prune) {
   APlan p{};
-  p.group = group_width(k);
+  p.prune = prune;
+  p.group = prune ? kWave : group_width(k);  // pruning runs one cell per wave
   const uint32_t cpw = kWave / p.group;
   p.kpad = (uint32_t)align_up((size_t)k + 1, 4 * p.group);  // >= 1 padding column
   p.reg_atoms = cap <= kRegAtomMax;
@@ -1437,9 +1555,9 @@ APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap) {
 }
 
 hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, uint32_t k,
-                       uint32_t T, uint32_t cap, const float *gamma, uint32_t *atom_idx,
-                       float *atom_val, uint32_t *atom_cnt, uint32_t *trace, void *ws,
-                       uint32_t *status, hipStream_t stream) {
+                       uint32_t T, uint32_t cap, const float *gamma, float prune_thr,
+                       uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt, uint32_t *trace,
+                       void *ws, uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
@@ -1461,12 +1579,12 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
     SupQueues q0{nullptr, nullptr, ctr + 0, two ? long_list : nullptr, ctr + 2, dense_list,
                  ctr + 3};
     e = launch_support(plan, dev, 0, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
-                       atom_cnt, trace, q0, status, stream);
+                       atom_cnt, trace, q0, prune_thr, status, stream);
     if (e != hipSuccess) return e;
     if (two) {
       SupQueues q1{long_list, ctr + 2, ctr + 1, nullptr, nullptr, dense_list, ctr + 3};
       e = launch_support(plan, dev, 1, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
-                         atom_cnt, trace, q1, status, stream);
+                         atom_cnt, trace, q1, prune_thr, status, stream);
       if (e != hipSuccess) return e;
     }
     cell_list = dense_list;
@@ -1474,7 +1592,7 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
   }
 #define SEACELLS_A_ARGS \
   plan, dev, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt, trace, ws, \
-      dense_only, cell_list, cell_count, status, stream
+      dense_only, cell_list, cell_count, prune_thr, status, stream
 #define SEACELLS_A_GROUP(GW)                                                                \
   if (plan.group == GW) {                                                                   \
     if (plan.h_in_lds)                                                                      \

@@ -23,6 +23,7 @@ FLAGS = {0x1: "CAP_OVERFLOW", 0x2: "PARTIALS_INVALID", 0x4: "B_CAP_OVERFLOW", 0x
          0x10: "NONFINITE", 0x20: "BAD_GAMMA"}
 
 EXPORTS = ("seacells_fw_a_columns_workspace", "seacells_fw_a_columns",
+           "seacells_fw_a_columns_pruned",
            "seacells_fw_b_argmin_workspace", "seacells_fw_b_argmin", "seacells_fw_b_apply",
            "seacells_status_string", "seacells_last_error", "seacells_version")
 
@@ -62,6 +63,10 @@ def load():
     lib.seacells_fw_a_columns.restype = ctypes.c_int
     lib.seacells_fw_a_columns.argtypes = [_CSR_P, _CSR_P, _CSR_P, _U32, _U32, _U32, _U32, _VP, _VP,
                                           _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP]
+    lib.seacells_fw_a_columns_pruned.restype = ctypes.c_int
+    lib.seacells_fw_a_columns_pruned.argtypes = [_CSR_P, _CSR_P, _CSR_P, _U32, _U32, _U32, _U32,
+                                                 _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP,
+                                                 ctypes.c_size_t, _VP, _VP]
     lib.seacells_fw_b_argmin_workspace.restype = ctypes.c_size_t
     lib.seacells_fw_b_argmin_workspace.argtypes = [_U32, _U32]
     lib.seacells_fw_b_argmin.restype = ctypes.c_int
@@ -165,6 +170,21 @@ def seacells_fw_a_columns(t1: DeviceCSR, k2b: DeviceCSR, a_prev_t: DeviceCSR, n:
     Outputs and workspace are allocated when not given; pass ``trace=True``
     to get the per-step argmin trace [n, T].
     """
+    return _a_columns(None, t1, k2b, a_prev_t, n, k, T, cap, gamma, atom_idx, atom_val,
+                      atom_cnt, trace, workspace, status, stream)
+
+
+def seacells_fw_a_columns_pruned(t1: DeviceCSR, k2b: DeviceCSR, a_prev_t: DeviceCSR, n: int,
+                                 k: int, T: int, cap: int, threshold: float, gamma=None,
+                                 atom_idx=None, atom_val=None, atom_cnt=None, trace=None,
+                                 workspace=None, status=None, stream=None):
+    """A update with the pruning + renormalisation step; as seacells_fw_a_columns."""
+    return _a_columns(float(threshold), t1, k2b, a_prev_t, n, k, T, cap, gamma, atom_idx,
+                      atom_val, atom_cnt, trace, workspace, status, stream)
+
+
+def _a_columns(threshold, t1, k2b, a_prev_t, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt,
+               trace, workspace, status, stream):
     lib = load()
     dev = t1.row_ptr.device
     if atom_idx is None:
@@ -183,11 +203,15 @@ def seacells_fw_a_columns(t1: DeviceCSR, k2b: DeviceCSR, a_prev_t: DeviceCSR, n:
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     s1, s2, s3 = t1.struct(), k2b.struct(), a_prev_t.struct()
-    rc = lib.seacells_fw_a_columns(ctypes.byref(s1), ctypes.byref(s2), ctypes.byref(s3), n, k, T,
-                                   cap, _ptr(gamma), _ptr(atom_idx), _ptr(atom_val),
-                                   _ptr(atom_cnt), _ptr(trace), _ptr(workspace),
-                                   0 if workspace is None else workspace.numel(), _ptr(status),
-                                   _stream(stream))
+    tail = (_ptr(atom_idx), _ptr(atom_val), _ptr(atom_cnt), _ptr(trace), _ptr(workspace),
+            0 if workspace is None else workspace.numel(), _ptr(status), _stream(stream))
+    if threshold is None:
+        rc = lib.seacells_fw_a_columns(ctypes.byref(s1), ctypes.byref(s2), ctypes.byref(s3), n,
+                                       k, T, cap, _ptr(gamma), *tail)
+    else:
+        rc = lib.seacells_fw_a_columns_pruned(ctypes.byref(s1), ctypes.byref(s2),
+                                              ctypes.byref(s3), n, k, T, cap, _ptr(gamma),
+                                              threshold, *tail)
     _check_rc(rc)
     return atom_idx, atom_val, atom_cnt, trace, status
 

@@ -9,13 +9,17 @@ def dev(m):
     return saa.DeviceCSR.from_scipy(m)
 
 
-def run_a(w, T=None, cap=None, gamma=None, trace=True, ops=None):
+def run_a(w, T=None, cap=None, gamma=None, trace=True, ops=None, prune=None):
     T = w.T if T is None else T
     cap = w.cap if cap is None else cap
     g = None if gamma is None else torch.tensor(np.asarray(gamma, np.float32), device="cuda")
     t1, k2b, ap = ops if ops is not None else (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
-    ai, av, ac, tr, st = saa.seacells_fw_a_columns(t1, k2b, ap, w.n, w.k, T, cap, gamma=g,
-                                                   trace=trace)
+    if prune is None:
+        ai, av, ac, tr, st = saa.seacells_fw_a_columns(t1, k2b, ap, w.n, w.k, T, cap, gamma=g,
+                                                       trace=trace)
+    else:
+        ai, av, ac, tr, st = saa.seacells_fw_a_columns_pruned(t1, k2b, ap, w.n, w.k, T, cap,
+                                                              prune, gamma=g, trace=trace)
     torch.cuda.synchronize()
     return (ai.cpu().numpy(), av.cpu().numpy(), ac.cpu().numpy(),
             tr.cpu().numpy() if tr is not None else None, saa.status_flags(st))

@@ -25,6 +25,11 @@ A_ABS = 1e-5     # A entries after T steps, absolute
 B_ABS = 1e-5     # B entries after the B step, absolute
 VAL_REL, VAL_ABS = 1e-4, 1e-5   # B minimum values (the page's policy)
 GAP_REL = 1e-3                  # sum(B * G) (the page's policy)
+# Pruning: a cell whose replayed weights came within this distance of the
+# threshold at some step is left out (f32 and f64 weights may fall on either
+# side of it: f32 weights of ~0.02 carry ~1e-7 of rounding after 50 steps);
+# outside that band both take the same drop decisions.
+PRUNE_MARGIN = 1e-6
 
 
 def dense_atoms(atom_idx, atom_val, atom_cnt, k):
@@ -49,6 +54,7 @@ class AReport:
     zero_tie_mismatch: int
     max_abs_err: float
     worst_window: float
+    skipped: int = 0          # cells left out for a drop decision within PRUNE_MARGIN
 
 
 def check_atom_layout(atom_idx, atom_cnt, trace, a_prev_t, cells):
@@ -65,15 +71,30 @@ def check_atom_layout(atom_idx, atom_cnt, trace, a_prev_t, cells):
 
 
 def check_a(w, gpu_trace, atom_idx, atom_val, atom_cnt, cells, gamma=None, T=None,
-            strict_zero_ties=True) -> AReport:
-    """Trace replay of the A update for ``cells``; returns counts and errors."""
+            strict_zero_ties=True, prune=None) -> AReport:
+    """Trace replay of the A update for ``cells``; returns counts and errors.
+
+    ``prune`` (a threshold) replays the pruning variant. Its drop steps take
+    products back out of the state, so a column can return to an exact 0 in
+    f64 but not in f32: the structural zero-tie rule is not applied then."""
     T = w.T if T is None else T
     cells = np.asarray(cells, np.int64)
     trace = np.asarray(gpu_trace, np.int64)
+    atom_idx, atom_val, atom_cnt = np.asarray(atom_idx), np.asarray(atom_val), np.asarray(atom_cnt)
     assert trace.shape == (cells.shape[0], T)
     assert np.all((trace >= 0) & (trace < w.k)), "trace index out of range"
     rep = oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, T, cells=cells, force=trace,
-                              gamma=gamma)
+                              gamma=gamma, prune=prune)
+    skipped = 0
+    if prune is not None:
+        strict_zero_ties = False
+        keep = ~np.any(rep.margin < PRUNE_MARGIN, axis=1)
+        skipped = int((~keep).sum())
+        if skipped:
+            cells, trace = cells[keep], trace[keep]
+            atom_idx, atom_val, atom_cnt = atom_idx[keep], atom_val[keep], atom_cnt[keep]
+            for f in ("a", "pick", "g_min", "g_second", "g_scale", "g_taken"):
+                setattr(rep, f, getattr(rep, f)[keep])
     exact = trace == rep.pick
     window = TIE_REL * np.maximum(np.maximum(np.abs(rep.g_min), np.abs(rep.g_second)),
                                   rep.g_scale)
@@ -105,7 +126,8 @@ def check_a(w, gpu_trace, atom_idx, atom_val, atom_cnt, cells, gamma=None, T=Non
     assert err <= A_ABS, "A entries differ from the replayed oracle by %.3g" % err
     check_atom_layout(atom_idx, atom_cnt, trace, w.a_prev_t, cells)
     return AReport(int(trace.size), int(exact.sum()), int((~exact).sum()), int(zero_tie.sum()),
-                   err, float(np.max(excess / np.maximum(window, 1e-300))) if excess.size else 0.0)
+                   err, float(np.max(excess / np.maximum(window, 1e-300))) if excess.size else 0.0,
+                   skipped)
 
 
 @dataclass

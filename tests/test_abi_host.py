@@ -126,3 +126,19 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(saa.SeacellsError):
         saa.DeviceCSR(torch.zeros(3, dtype=torch.int32), torch.zeros(0, dtype=torch.int32),
                       torch.zeros(0), (2, 2))
+
+
+def test_a_columns_pruned_rejects_bad_threshold_on_host():
+    lib = saa.load()
+    n, k, T, cap = 10, 4, 5, 8
+    t1, k2b, ap = csr(k, k, 3), csr(n, k, 5), csr(n, k, 5)
+    o = 0x4000
+
+    def call(thr, t1=t1):
+        return lib.seacells_fw_a_columns_pruned(ctypes.byref(t1), ctypes.byref(k2b),
+                                                ctypes.byref(ap), n, k, T, cap, None, thr, o, o,
+                                                o, None, None, 0, 0x9000, None)
+    assert call(-0.1) == -2
+    assert call(float("nan")) == -2
+    assert call(float("inf")) == -2
+    assert call(0.5, t1=csr(k + 1, k, 3)) == -2
