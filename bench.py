@@ -9,10 +9,13 @@ dominant kernel (algorithmic bytes per launch / average launch time from HIP
 events on the library's stream), and the f64 CPU oracle timed on a bounded
 sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--config c5] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--config c5] [--gpus 1] [--prune THR]
 
 The default workload is the largest single-GPU configuration (n = 1M cells,
-k = 10000 archetypes); --config c1 .. c4 selects the smaller ones.
+k = 10000 archetypes); --config c1 .. c4 selects the smaller ones. --prune
+runs the A update's pruning variant (weights at or below THR dropped after
+every step, then the column renormalised); its byte model leaves out the t1
+rows that drops take back out, so its GB/s is a lower bound.
 """
 from __future__ import annotations
 
@@ -150,6 +153,8 @@ def main():
     ap.add_argument("--config", default="c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--prune", type=float, default=None, metavar="THR",
+                    help="time the A update's pruning variant with threshold THR")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 launches), the reference "
                          "kernel that scales the HBM byte counters")
@@ -193,11 +198,18 @@ def main():
     st_a, st_b, st_p = saa.new_status(dev), saa.new_status(dev), saa.new_status(dev)
     stream = torch.cuda.current_stream()
 
+    prune = args.prune
+    if prune is None:
+        a_update = saa.seacells_fw_a_columns
+    else:
+        def a_update(*a, **kw):
+            return saa.seacells_fw_a_columns_pruned(*a, threshold=prune, **kw)
+
     # one traced run (outside the timing) for the byte model: the trace is
     # deterministic, so the timed runs take the same picks
     trace = torch.empty((n, T), dtype=torch.int32, device=dev)
-    saa.seacells_fw_a_columns(t1, k2b, ap_, n, k, T, cap, atom_idx=atom_idx, atom_val=atom_val,
-                              atom_cnt=atom_cnt, trace=trace, workspace=ws_a, status=st_a)
+    a_update(t1, k2b, ap_, n, k, T, cap, atom_idx=atom_idx, atom_val=atom_val,
+             atom_cnt=atom_cnt, trace=trace, workspace=ws_a, status=st_a)
     torch.cuda.synchronize()
     saa.raise_on_status(st_a)
     bytes_a = algorithmic_bytes_a(w, trace.cpu().numpy(), atom_cnt.cpu().numpy())
@@ -209,9 +221,8 @@ def main():
     def step(t, marks=None):
         if marks:
             marks[0].record(stream)
-        saa.seacells_fw_a_columns(t1, k2b, ap_, n, k, T, cap, atom_idx=atom_idx,
-                                  atom_val=atom_val, atom_cnt=atom_cnt, workspace=ws_a,
-                                  status=st_a, stream=stream)
+        a_update(t1, k2b, ap_, n, k, T, cap, atom_idx=atom_idx, atom_val=atom_val,
+                 atom_cnt=atom_cnt, workspace=ws_a, status=st_a, stream=stream)
         if marks:
             marks[1].record(stream)
         saa.seacells_fw_b_argmin(k2b, aat, k2at, bm, n, k, out_val=out_val, out_idx=out_idx,
@@ -246,7 +257,7 @@ def main():
         ach, per_launch, sha = a_gbps, bytes_a, source_sha("fw_a.hip")
     else:
         ach, per_launch, sha = b_gbps, bytes_b, source_sha("fw_b.hip")
-    traffic = traffic_from_profile(dominant, args.config, sha)
+    traffic = None if prune is not None else traffic_from_profile(dominant, args.config, sha)
 
     rec = {
         "metric": METRIC,
@@ -262,7 +273,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "%s: %s" % (args.config, W.DESCRIPTIONS.get(args.config, "")),
-                   "n": n, "k": k, "T": T, "cap": cap, "nnz": w.meta.get("nnz")},
+                   "n": n, "k": k, "T": T, "cap": cap, "nnz": w.meta.get("nnz"),
+                   "prune_threshold": prune},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS,
                      "bytes_per_launch": per_launch, "traffic": traffic},
