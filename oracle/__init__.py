@@ -64,13 +64,13 @@ def _load():
     lib.oracle_fw_a_columns.argtypes = (
         [ctypes.c_uint32] * 3 + [_U32P, _U32P, _F32P] * 3 + [_F64P, _U32P, ctypes.c_uint32,
                                                               _I64P, _F64P, _U32P, _F64P, _F64P,
-                                                              _F64P, _F64P, ctypes.c_int])
+                                                              _F64P, _F64P, _F64P, ctypes.c_int])
     lib.oracle_fw_a_columns_pruned.restype = ctypes.c_int
     lib.oracle_fw_a_columns_pruned.argtypes = (
         [ctypes.c_uint32] * 3 + [_U32P, _U32P, _F32P] * 3 + [_F64P, _U32P, ctypes.c_uint32,
                                                               _I64P, ctypes.c_double, _F64P,
                                                               _U32P, _F64P, _F64P, _F64P, _F64P,
-                                                              _U32P, _F64P, ctypes.c_int])
+                                                              _F64P, _U32P, _F64P, ctypes.c_int])
     lib.oracle_fw_b_argmin.restype = ctypes.c_int
     lib.oracle_fw_b_argmin.argtypes = (
         [ctypes.c_uint32] * 2 + [_U32P, _U32P, _F32P] * 4 + [_F64P, _U32P, _F64P, _F64P, _F64P,
@@ -129,8 +129,16 @@ class ATrace:
     g_second: np.ndarray   # [m, T]
     g_scale: np.ndarray    # [m, T]
     g_taken: np.ndarray    # [m, T] g at the index used for the update
+    g_dot: np.ndarray = None   # [m, T] <g, a> at each step's iterate (before the update)
     drops: np.ndarray = None   # [m, T] weights dropped per step (pruned runs only)
     margin: np.ndarray = None  # [m, T] min | |a| - threshold | before the drop (pruned runs)
+
+    @property
+    def fw_gap(self) -> np.ndarray:
+        """[m, T] Frank-Wolfe duality gap of each step's iterate a_t:
+        <g_t, a_t> - min_c g_t[c] = max over simplex vertices e_v of
+        <g_t, a_t - e_v> (g without the factor 2, as on the page)."""
+        return self.g_dot - self.g_min
 
 
 def fw_a_columns(t1, k2b, a_prev_t, n: int, k: int, T: int, cells=None, force=None,
@@ -159,22 +167,23 @@ def fw_a_columns(t1, k2b, a_prev_t, n: int, k: int, T: int, cells=None, force=No
             raise ValueError("gamma must be [T]")
     a = np.empty((m, k), np.float64)
     pick = np.empty((m, T), np.uint32)
-    gmin, g2, gs, gt = (np.empty((m, T), np.float64) for _ in range(4))
+    gmin, g2, gs, gt, gd = (np.empty((m, T), np.float64) for _ in range(5))
     ops = (n, k, T, _p(t1p[0], _U32P), _p(t1p[1], _U32P), _p(t1p[2], _F32P),
            _p(k2p[0], _U32P), _p(k2p[1], _U32P), _p(k2p[2], _F32P),
            _p(app[0], _U32P), _p(app[1], _U32P), _p(app[2], _F32P),
            _p(gamma, _F64P), _p(cells, _U32P), m, _p(force, _I64P))
-    outs = (_p(pick, _U32P), _p(gmin, _F64P), _p(g2, _F64P), _p(gs, _F64P), _p(gt, _F64P))
+    outs = (_p(pick, _U32P), _p(gmin, _F64P), _p(g2, _F64P), _p(gs, _F64P), _p(gt, _F64P),
+            _p(gd, _F64P))
     if prune is None:
         rc = lib.oracle_fw_a_columns(*ops, _p(a, _F64P), *outs, _threads(n_threads))
         _check(rc)
-        return ATrace(cells, a, pick, gmin, g2, gs, gt)
+        return ATrace(cells, a, pick, gmin, g2, gs, gt, gd)
     drops = np.empty((m, T), np.uint32)
     margin = np.empty((m, T), np.float64)
     rc = lib.oracle_fw_a_columns_pruned(*ops, float(prune), _p(a, _F64P), *outs,
                                         _p(drops, _U32P), _p(margin, _F64P), _threads(n_threads))
     _check(rc)
-    return ATrace(cells, a, pick, gmin, g2, gs, gt, drops, margin)
+    return ATrace(cells, a, pick, gmin, g2, gs, gt, gd, drops, margin)
 
 
 @dataclass
@@ -184,6 +193,13 @@ class BResult:
     second: np.ndarray     # [k] runner-up value
     gap: float             # sum(B * G)
     row_scale: np.ndarray  # [n]
+
+    @property
+    def fw_gap(self) -> float:
+        """Full Frank-Wolfe duality gap of the B subproblem: sum(B * G) minus
+        sum_c min_i G[i, c] = max over vertex matrices S (one-hot columns)
+        of <G, B - S> (G without the factor 2, as on the page)."""
+        return self.gap - float(np.sum(self.val))
 
 
 def fw_b_argmin(k2b, aat, k2at, b, n: int, k: int, n_threads=None) -> BResult:

@@ -92,6 +92,9 @@ static int check_csr(uint32_t rows, uint32_t cols, const uint32_t *ptr,
  *   g_scale  - max(max_c |(t1 a)[c]|, max_c |t2[c]|), the size of the terms
  *              g is a difference of
  *   g_taken  - g at the index actually used for the update
+ *   g_dot    - <g, a> = sum_c a[c] g[c] at this step's iterate (before the
+ *              update); g_dot - g_min is the Frank-Wolfe duality gap there,
+ *              max over simplex vertices e_v of <g, a - e_v>
  * force (nullable, [n_cells * T]): an entry >= 0 replaces idx in the update
  * (trace replay); the oracle's own argmin is still reported in pick.
  * a_out: [n_cells * k] dense f64 result.
@@ -106,7 +109,8 @@ static int fw_a_columns_impl(uint32_t n, uint32_t k, uint32_t T,
                              const int64_t *force, int prune, double threshold,
                              double *a_out, uint32_t *pick, double *g_min,
                              double *g_second, double *g_scale, double *g_taken,
-                             uint32_t *drops, double *margin, int n_threads) {
+                             double *g_dot, uint32_t *drops, double *margin,
+                             int n_threads) {
     if (k == 0 || !t1_val || !k2b_val || !ap_val || !cells || !a_out)
         return ORACLE_E_ARG;
     int rc;
@@ -172,6 +176,13 @@ static int fw_a_columns_impl(uint32_t n, uint32_t k, uint32_t T,
                 if (g_second) g_second[e] = second;
                 if (g_scale) g_scale[e] = scale;
                 if (g_taken) g_taken[e] = w[take] - t2[take];
+                if (g_dot) {
+                    /* <g, a> at this step's iterate: with g_min, the
+                       Frank-Wolfe duality gap <g, a> - min_c g[c] */
+                    double d = 0.0;
+                    for (uint32_t c = 0; c < k; ++c) d += a[c] * (w[c] - t2[c]);
+                    g_dot[e] = d;
+                }
 
                 const double gam = gamma ? gamma[t] : 2.0 / ((double)t + 2.0);
                 for (uint32_t c = 0; c < k; ++c) a[c] *= (1.0 - gam);
@@ -218,11 +229,12 @@ int oracle_fw_a_columns(uint32_t n, uint32_t k, uint32_t T,
                         const uint32_t *cells, uint32_t n_cells,
                         const int64_t *force, double *a_out, uint32_t *pick,
                         double *g_min, double *g_second, double *g_scale,
-                        double *g_taken, int n_threads) {
+                        double *g_taken, double *g_dot, int n_threads) {
     return fw_a_columns_impl(n, k, T, t1_ptr, t1_idx, t1_val, k2b_ptr, k2b_idx,
                              k2b_val, ap_ptr, ap_idx, ap_val, gamma, cells,
                              n_cells, force, 0, 0.0, a_out, pick, g_min,
-                             g_second, g_scale, g_taken, NULL, NULL, n_threads);
+                             g_second, g_scale, g_taken, g_dot, NULL, NULL,
+                             n_threads);
 }
 
 /*
@@ -250,13 +262,13 @@ int oracle_fw_a_columns_pruned(
     const uint32_t *ap_idx, const float *ap_val, const double *gamma,
     const uint32_t *cells, uint32_t n_cells, const int64_t *force,
     double threshold, double *a_out, uint32_t *pick, double *g_min,
-    double *g_second, double *g_scale, double *g_taken, uint32_t *drops,
-    double *margin, int n_threads) {
+    double *g_second, double *g_scale, double *g_taken, double *g_dot,
+    uint32_t *drops, double *margin, int n_threads) {
     if (!(threshold >= 0.0)) return ORACLE_E_ARG;
     return fw_a_columns_impl(n, k, T, t1_ptr, t1_idx, t1_val, k2b_ptr, k2b_idx,
                              k2b_val, ap_ptr, ap_idx, ap_val, gamma, cells,
                              n_cells, force, 1, threshold, a_out, pick, g_min,
-                             g_second, g_scale, g_taken, drops, margin,
+                             g_second, g_scale, g_taken, g_dot, drops, margin,
                              n_threads);
 }
 

@@ -609,3 +609,185 @@ def test_p9_invariants_after_every_prefix(c1):
         assert not np.any((r.a > 0.0) & (r.a <= thr))
         s = r.a.sum(axis=1)
         assert np.all((np.abs(s - 1.0) < 1e-12) | (s == 0.0))
+
+
+# --------------------------------------------------------------------------
+# P10: the full Frank-Wolfe duality gap of both updates (g and G without the
+# factor 2, as on the page): <g, a> - min_c g[c] for an A column, and
+# sum(B * G) - sum_c min_i G[i, c] for B
+# --------------------------------------------------------------------------
+
+def test_p10_identity_kernel_gaps_closed_form():
+    K, B, A, ops = identity_example()
+    T = 50
+    tr = oracle.fw_a_columns(ops["t1"], ops["k2b"], ops["a_prev_t"], 4, 2, T)
+    gap = tr.fw_gap
+    # g = a - B[j, :]. Cell 0: a_prev = (1/2, 1/2) gives g = (-1/2, 1/2) and
+    # gap 1/2; after step 0, a = e_0 is optimal and every gap is 0.
+    np.testing.assert_allclose(gap[0], [0.5] + [0.0] * (T - 1), rtol=0, atol=1e-15)
+    # Cell 1: 1/2, then 0 at e_1, then 8/9 at (2/3, 1/3); from step 2 on
+    # a_0 = x = 4/(t(t+1)) and g = (x, -x), so the gap is 2 x^2.
+    want1 = [0.5, 0.0] + [2.0 * (4.0 / (t * (t + 1))) ** 2 for t in range(2, T)]
+    np.testing.assert_allclose(gap[1], want1, rtol=1e-13, atol=1e-15)
+    assert abs(gap[1, 2] - 8 / 9) < 1e-15
+    # Cells 2, 3: g = a. Step 0 is the optimum (1/2, 1/2): gap 0. After an
+    # odd number m of steps a = ((m+1)/(2m), (m-1)/(2m)), gap (m+1)/(2m^2);
+    # after an even m >= 2, a = (m/(2(m+1)), (m+2)/(2(m+1))), gap
+    # (m+2)/(2(m+1)^2).
+    want = [0.0] + [(m + 1) / (2 * m * m) if m % 2 else (m + 2) / (2 * (m + 1) ** 2)
+                    for m in range(1, T)]
+    for j in (2, 3):
+        np.testing.assert_allclose(gap[j], want, rtol=1e-13, atol=1e-15)
+    assert abs(gap[2, T - 1] - 25 / 2401) < 1e-15
+    # B: G rows (1/2, 1/2) x 2 and (-1/2, -1/2) x 2, B = [e_0, e_1]:
+    # sum(B * G) = 1 and each column's minimum is -1/2, so the full gap is 2
+    res = oracle.fw_b_argmin(ops["k2b"], ops["aat"], ops["k2at"], ops["b"], 4, 2)
+    assert res.fw_gap == 2.0
+
+
+def test_p10_a_gap_is_the_steepest_vertex_descent_of_the_objective():
+    # gap = max over vertices e_v of -d/de f(A with column j moved towards e_v),
+    # halved (the page drops the factor 2), from central differences of
+    # ||K - K B A||^2 itself (exact up to rounding: f is quadratic in A)
+    rng = np.random.default_rng(101)
+    n, k, T = 7, 4, 5
+    K, B, A0 = dyadic_problem(n, k, rng)
+    ops = operands(K, B, A0)
+    Bf = ops["b"].toarray().astype(np.float64)
+    tr = oracle.fw_a_columns(ops["t1"], ops["k2b"], ops["a_prev_t"], n, k, T)
+    h = 1e-3
+    checked = 0
+    for j in range(n):
+        for t in range(T):
+            a = ops["a_prev_t"].toarray()[j].astype(np.float64) if t == 0 else \
+                oracle.fw_a_columns(ops["t1"], ops["k2b"], ops["a_prev_t"], n, k, t,
+                                    cells=[j]).a[0]
+            Acur = ops["a_prev_t"].toarray().T.astype(np.float64)
+            Acur[:, j] = a
+            best = -np.inf
+            for v in range(k):
+                d = -a.copy()
+                d[v] += 1.0
+                Ap, Am = Acur.copy(), Acur.copy()
+                Ap[:, j] += h * d
+                Am[:, j] -= h * d
+                slope = (dense.objective(K, Bf, Ap) - dense.objective(K, Bf, Am)) / (2 * h)
+                best = max(best, -0.5 * slope)
+            assert abs(tr.fw_gap[j, t] - best) <= 1e-8 * max(1.0, abs(best)), (j, t)
+            checked += 1
+    assert checked == n * T
+
+
+def _simplex_qp_min(Q, c):
+    """min 0.5 a^T Q a - c^T a over the simplex, Q positive semidefinite, by
+    enumerating supports: on each support the KKT system is linear; every
+    feasible solution is a candidate and the minimiser is one of them."""
+    import itertools
+    k = Q.shape[0]
+    best = np.inf
+    for r in range(1, k + 1):
+        for S in itertools.combinations(range(k), r):
+            S = list(S)
+            M = np.zeros((r + 1, r + 1))
+            M[:r, :r] = Q[np.ix_(S, S)]
+            M[:r, r] = 1.0
+            M[r, :r] = 1.0
+            rhs = np.concatenate([c[S], [1.0]])
+            sol = np.linalg.lstsq(M, rhs, rcond=None)[0]
+            aS = sol[:r]
+            if np.any(aS < -1e-12) or abs(aS.sum() - 1.0) > 1e-9:
+                continue
+            a = np.zeros(k)
+            a[S] = np.maximum(aS, 0.0)
+            a /= a.sum()
+            best = min(best, 0.5 * a @ Q @ a - c @ a)
+    return best
+
+
+def test_p10_a_gap_bounds_the_suboptimality():
+    # weak duality: q(a_t) - min_simplex q <= gap_t with q(a) = a^T t1 a / 2 -
+    # t2_j^T a, whose gradient is the page's g; t1 = B^T K^2 B is PSD
+    rng = np.random.default_rng(102)
+    n, k, T = 9, 5, 12
+    K, B, A0 = random_problem(n, k, rng)
+    ops = operands(K, B, A0)
+    t1 = ops["t1"].toarray().astype(np.float64)
+    t2 = ops["k2b"].toarray().astype(np.float64)
+    tr = oracle.fw_a_columns(ops["t1"], ops["k2b"], ops["a_prev_t"], n, k, T)
+    for j in range(n):
+        qstar = _simplex_qp_min(t1, t2[j])
+        for t in range(T):
+            a = ops["a_prev_t"].toarray()[j].astype(np.float64) if t == 0 else \
+                oracle.fw_a_columns(ops["t1"], ops["k2b"], ops["a_prev_t"], n, k, t,
+                                    cells=[j]).a[0]
+            sub = 0.5 * a @ t1 @ a - t2[j] @ a - qstar
+            assert sub >= -1e-12
+            assert tr.fw_gap[j, t] >= sub - 1e-12, (j, t, tr.fw_gap[j, t], sub)
+
+
+def test_p10_a_gap_vertex_optimum_is_zero():
+    # t1 = I, t2 = 5 e_0: from e_0 the gradient is -4 e_0 (gap 0); from e_1 it
+    # is e_1 - 5 e_0 (gap 1 - (-5) = 6)
+    k = 3
+    t1 = sp.identity(k, format="csr", dtype=np.float32)
+    k2b = sp.csr_matrix(np.array([[5.0, 0, 0], [5.0, 0, 0]], np.float32))
+    ap = sp.csr_matrix(np.array([[1.0, 0, 0], [0, 1.0, 0]], np.float32))
+    tr = oracle.fw_a_columns(t1, k2b, ap, 2, k, 3)
+    np.testing.assert_array_equal(tr.fw_gap[0], [0.0, 0.0, 0.0])
+    assert tr.fw_gap[1, 0] == 6.0
+
+
+def test_p10_b_full_gap_by_vertex_enumeration():
+    # max over every vertex matrix S (one-hot columns) of <G, B - S>, with G
+    # from the closed form 2 (K^2 B A A^T - K^2 A^T) / 2 of the dense module
+    import itertools
+    rng = np.random.default_rng(103)
+    for n, k in ((4, 2), (5, 3), (6, 2)):
+        K, B, A = random_problem(n, k, rng)
+        ops = operands(K, B, A)
+        Bf = ops["b"].toarray().astype(np.float64)
+        # the operands are f32: G from the f32-rounded products, as the oracle sees them
+        G = (ops["k2b"].toarray().astype(np.float64) @ ops["aat"].toarray().astype(np.float64)
+             - ops["k2at"].toarray().astype(np.float64))
+        best = -np.inf
+        for rows in itertools.product(range(n), repeat=k):
+            S = np.zeros((n, k))
+            S[list(rows), list(range(k))] = 1.0
+            best = max(best, float(np.sum(G * (Bf - S))))
+        res = oracle.fw_b_argmin(ops["k2b"], ops["aat"], ops["k2at"], ops["b"], n, k)
+        assert abs(res.fw_gap - best) <= 1e-12 * max(1.0, abs(best)), (n, k, res.fw_gap, best)
+        assert res.fw_gap >= 0.0
+        # and G itself agrees with half the closed-form gradient of the objective
+        # on the exact (f64) problem up to the f32 rounding of the operands
+        np.testing.assert_allclose(G, dense.grad_b(K, B, A) / 2, rtol=0, atol=1e-5)
+
+
+def test_p10_a_gap_on_a_forced_trajectory_uses_the_true_minimum():
+    # trace replay: the update follows forced (non-optimal) picks, and the
+    # gap at each iterate is still measured against its best vertex
+    rng = np.random.default_rng(104)
+    n, k, T = 5, 4, 6
+    K, B, A0 = dyadic_problem(n, k, rng)
+    ops = operands(K, B, A0)
+    Bf = ops["b"].toarray().astype(np.float64)
+    force = np.array([[(t + j) % k for t in range(T)] for j in range(n)], np.int64)
+    tr = oracle.fw_a_columns(ops["t1"], ops["k2b"], ops["a_prev_t"], n, k, T, force=force)
+    assert np.any(tr.pick != force)
+    h = 1e-3
+    for j in range(n):
+        for t in range(T):
+            a = ops["a_prev_t"].toarray()[j].astype(np.float64) if t == 0 else \
+                oracle.fw_a_columns(ops["t1"], ops["k2b"], ops["a_prev_t"], n, k, t, cells=[j],
+                                    force=force[j:j + 1, :t]).a[0]
+            Acur = ops["a_prev_t"].toarray().T.astype(np.float64)
+            Acur[:, j] = a
+            best = -np.inf
+            for v in range(k):
+                d = -a.copy()
+                d[v] += 1.0
+                Ap, Am = Acur.copy(), Acur.copy()
+                Ap[:, j] += h * d
+                Am[:, j] -= h * d
+                slope = (dense.objective(K, Bf, Ap) - dense.objective(K, Bf, Am)) / (2 * h)
+                best = max(best, -0.5 * slope)
+            assert abs(tr.fw_gap[j, t] - best) <= 1e-8 * max(1.0, abs(best)), (j, t)
