@@ -120,6 +120,14 @@ size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint3
  * atom_val  device [n * cap] f32 out: the matching weights of a_j.
  * atom_cnt  device [n] u32 out.
  * trace     device [n * T] u32 out, or NULL: trace[j * T + t] = idx_t.
+ * fw_gap    device [n] f32 out, or NULL: the Frank-Wolfe duality gap of
+ *           the returned column a_j (after the T steps), <g, a_j> -
+ *           min_c g[c] with g = t1 . a_j - K2B[j, :] (without the factor 2,
+ *           as on the page), i.e. the largest decrease rate of the objective
+ *           towards a simplex vertex, an upper bound on a_j's distance to
+ *           the optimum of its subproblem. The page's kernel computes only
+ *           the B side's sum(B * G) half. Computed in f32 from the state,
+ *           after the last step (no cost when NULL).
  * workspace device buffer of at least seacells_fw_a_columns_workspace()
  *           bytes (may be NULL when that is 0), 256-byte aligned.
  */
@@ -127,8 +135,9 @@ int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
                           const seacells_csr *a_prev_t, uint32_t n, uint32_t k,
                           uint32_t T, uint32_t cap, const float *gamma,
                           uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
-                          uint32_t *trace, void *workspace, size_t workspace_bytes,
-                          uint32_t *status, seacells_stream_t stream);
+                          uint32_t *trace, float *fw_gap, void *workspace,
+                          size_t workspace_bytes, uint32_t *status,
+                          seacells_stream_t stream);
 
 /*
  * A update with pruning and renormalisation: `fw_columns_a_gpu` with
@@ -143,7 +152,8 @@ int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
  * threshold   f32, finite and >= 0 (else SEACELLS_E_SHAPE); compared in f32.
  * Other arguments, outputs, errors and the workspace
  * (seacells_fw_a_columns_workspace covers both entry points) are those of
- * seacells_fw_a_columns; atom_val holds 0 for a dropped slot. A cell that
+ * seacells_fw_a_columns (fw_gap: of the pruned, renormalised column that is
+ * returned); atom_val holds 0 for a dropped slot. A cell that
  * drops an atom is finished by the dense-state kernel, so pruning that bites
  * costs more than the plain update.
  */
@@ -151,8 +161,9 @@ int seacells_fw_a_columns_pruned(const seacells_csr *t1, const seacells_csr *k2b
                                  const seacells_csr *a_prev_t, uint32_t n, uint32_t k,
                                  uint32_t T, uint32_t cap, const float *gamma, float threshold,
                                  uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
-                                 uint32_t *trace, void *workspace, size_t workspace_bytes,
-                                 uint32_t *status, seacells_stream_t stream);
+                                 uint32_t *trace, float *fw_gap, void *workspace,
+                                 size_t workspace_bytes, uint32_t *status,
+                                 seacells_stream_t stream);
 
 /*
  * Workspace bytes seacells_fw_b_argmin needs for these sizes (always > 0).
@@ -170,19 +181,23 @@ size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k);
  *     out_idx[c] = lowest i attaining min_i G[i, c]; out_val[c] = that min
  *     gap        = sum_{i, c} B[i, c] G[i, c]  (the page's sum(B * G) half
  *                  of the duality gap)
+ *     fw_gap     = gap - sum_c out_val[c], the full Frank-Wolfe duality gap
+ *                  of B (max over vertex matrices S of <G, B - S>)
  * Every row takes part, including rows whose K2B row is empty.
  *
  * k2b   n x k CSR (K^2 B).     aat   k x k CSR, symmetric (A A^T).
  * k2at  n x k CSR (K^2 A^T).   b     n x k CSR (B), or NULL: gap = 0.
  * out_val  device [k] f32 out.   out_idx  device [k] u32 out.
  * gap      device [1] f32 out, or NULL.
+ * fw_gap   device [1] f32 out, or NULL; needs b (else SEACELLS_E_NULL).
+ *          Both sums are taken in f64 in a fixed order, then rounded.
  * The reduce stage checks that every partial was written by this call and
  * holds a row below n; otherwise it sets SEACELLS_FLAG_PARTIALS_INVALID.
  */
 int seacells_fw_b_argmin(const seacells_csr *k2b, const seacells_csr *aat,
                          const seacells_csr *k2at, const seacells_csr *b, uint32_t n,
                          uint32_t k, float *out_val, uint32_t *out_idx, float *gap,
-                         void *workspace, size_t workspace_bytes, uint32_t *status,
+                         float *fw_gap, void *workspace, size_t workspace_bytes, uint32_t *status,
                          seacells_stream_t stream);
 
 /*

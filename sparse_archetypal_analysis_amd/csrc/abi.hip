@@ -80,7 +80,7 @@ static int a_columns(const seacells_csr *t1, const seacells_csr *k2b,
                      const seacells_csr *a_prev_t, uint32_t n, uint32_t k, uint32_t T,
                      uint32_t cap, const float *gamma, bool prune, float threshold,
                      uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt, uint32_t *trace,
-                     void *workspace, size_t workspace_bytes, uint32_t *status,
+                     float *fw_gap, void *workspace, size_t workspace_bytes, uint32_t *status,
                      seacells_stream_t stream) {
   if (t1 == nullptr || k2b == nullptr || a_prev_t == nullptr || atom_idx == nullptr ||
       atom_val == nullptr || atom_cnt == nullptr || status == nullptr)
@@ -104,7 +104,7 @@ static int a_columns(const seacells_csr *t1, const seacells_csr *k2b,
   hipError_t e = launch_status_clear(status, s);
   if (e != hipSuccess) return hip_fail(e, "status clear");
   e = launch_fw_a(plan, as_csr(t1), as_csr(k2b), as_csr(a_prev_t), n, k, T, cap, gamma,
-                  threshold, atom_idx, atom_val, atom_cnt, trace, workspace, status, s);
+                  threshold, atom_idx, atom_val, atom_cnt, trace, fw_gap, workspace, status, s);
   if (e != hipSuccess) return hip_fail(e, "fw_a_columns launch");
   return SEACELLS_OK;
 }
@@ -112,20 +112,21 @@ static int a_columns(const seacells_csr *t1, const seacells_csr *k2b,
 int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
                           const seacells_csr *a_prev_t, uint32_t n, uint32_t k, uint32_t T,
                           uint32_t cap, const float *gamma, uint32_t *atom_idx, float *atom_val,
-                          uint32_t *atom_cnt, uint32_t *trace, void *workspace,
+                          uint32_t *atom_cnt, uint32_t *trace, float *fw_gap, void *workspace,
                           size_t workspace_bytes, uint32_t *status, seacells_stream_t stream) {
   return a_columns(t1, k2b, a_prev_t, n, k, T, cap, gamma, false, 0.0f, atom_idx, atom_val,
-                   atom_cnt, trace, workspace, workspace_bytes, status, stream);
+                   atom_cnt, trace, fw_gap, workspace, workspace_bytes, status, stream);
 }
 
 int seacells_fw_a_columns_pruned(const seacells_csr *t1, const seacells_csr *k2b,
                                  const seacells_csr *a_prev_t, uint32_t n, uint32_t k,
                                  uint32_t T, uint32_t cap, const float *gamma, float threshold,
                                  uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
-                                 uint32_t *trace, void *workspace, size_t workspace_bytes,
-                                 uint32_t *status, seacells_stream_t stream) {
+                                 uint32_t *trace, float *fw_gap, void *workspace,
+                                 size_t workspace_bytes, uint32_t *status,
+                                 seacells_stream_t stream) {
   return a_columns(t1, k2b, a_prev_t, n, k, T, cap, gamma, true, threshold, atom_idx, atom_val,
-                   atom_cnt, trace, workspace, workspace_bytes, status, stream);
+                   atom_cnt, trace, fw_gap, workspace, workspace_bytes, status, stream);
 }
 
 size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k) {
@@ -135,11 +136,13 @@ size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k) {
 
 int seacells_fw_b_argmin(const seacells_csr *k2b, const seacells_csr *aat,
                          const seacells_csr *k2at, const seacells_csr *b, uint32_t n, uint32_t k,
-                         float *out_val, uint32_t *out_idx, float *gap, void *workspace,
-                         size_t workspace_bytes, uint32_t *status, seacells_stream_t stream) {
+                         float *out_val, uint32_t *out_idx, float *gap, float *fw_gap,
+                         void *workspace, size_t workspace_bytes, uint32_t *status,
+                         seacells_stream_t stream) {
   if (k2b == nullptr || aat == nullptr || k2at == nullptr || out_val == nullptr ||
       out_idx == nullptr || status == nullptr)
     return SEACELLS_E_NULL;
+  if (fw_gap != nullptr && b == nullptr) return SEACELLS_E_NULL;  // the gap needs B
   if (n == 0 || k == 0) return SEACELLS_E_SHAPE;
   if (n >= 0x80000000u || k >= 0x80000000u) return SEACELLS_E_TOO_LARGE;
   int rc;
@@ -156,7 +159,7 @@ int seacells_fw_b_argmin(const seacells_csr *k2b, const seacells_csr *aat,
   hipError_t e = launch_status_clear(status, s);
   if (e != hipSuccess) return hip_fail(e, "status clear");
   e = launch_fw_b(plan, as_csr(k2b), as_csr(aat), as_csr(k2at), bc, n, k, out_val, out_idx, gap,
-                  workspace, status, next_epoch(), s);
+                  fw_gap, workspace, status, next_epoch(), s);
   if (e != hipSuccess) return hip_fail(e, "fw_b_argmin launch");
   return SEACELLS_OK;
 }

@@ -140,7 +140,7 @@ APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap, bool prune);
 hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, uint32_t k,
                        uint32_t T, uint32_t cap, const float *gamma, float prune_thr,
                        uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt, uint32_t *trace,
-                       void *ws, uint32_t *status, hipStream_t stream);
+                       float *fw_gap, void *ws, uint32_t *status, hipStream_t stream);
 
 // --- B argmin -------------------------------------------------------------
 struct BPlan {
@@ -154,8 +154,9 @@ struct BPlan {
 BPlan plan_b(uint32_t n, uint32_t k, uint64_t aat_nnz);
 size_t b_workspace_bound(uint32_t n, uint32_t k);  // over every aat_nnz
 hipError_t launch_fw_b(const BPlan &plan, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
-                       uint32_t k, float *out_val, uint32_t *out_idx, float *gap, void *ws,
-                       uint32_t *status, uint32_t epoch, hipStream_t stream);
+                       uint32_t k, float *out_val, uint32_t *out_idx, float *gap,
+                       float *fw_gap, void *ws, uint32_t *status, uint32_t epoch,
+                       hipStream_t stream);
 hipError_t launch_fw_b_apply(uint32_t *bt_idx, float *bt_val, uint32_t *bt_cnt, uint32_t n,
                              uint32_t k, uint32_t cap_b, const uint32_t *arg_idx, float gamma,
                              uint32_t *status, hipStream_t stream);

@@ -87,6 +87,26 @@ __device__ __forceinline__ StepSched sched_step(const float *gamma, uint32_t t, 
   return r;
 }
 
+// The step schedule of a block, written by one thread: T entries, then in
+// the last two of the sched_words words the scale s after the last step
+// (g = s h for the returned column) and the OR of the flags.
+__device__ void build_schedule(uint32_t *lds, uint32_t sched_words, const float *gamma,
+                               uint32_t T) {
+  StepSched *w = reinterpret_cast<StepSched *>(lds);
+  float s = 1.0f;
+  uint32_t f = 0;
+  for (uint32_t t = 0; t < T; ++t) w[t] = sched_step(gamma, t, s, f);
+  lds[sched_words - 2] = __float_as_uint(s);
+  lds[sched_words - 1] = f;
+}
+
+// Sum over each group of G consecutive lanes (every lane of a group gets it).
+template <uint32_t G>
+__device__ __forceinline__ float group_sum_f32(float x) {
+  for (int off = G / 2; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
 // Minimum of a u32 over each group of G consecutive lanes; every lane of a
 // group receives its group's minimum. Same butterfly as wave_min_u32,
 // stopped at the group width.
@@ -203,7 +223,8 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
                         uint32_t k, uint32_t kscan, uint32_t T, uint32_t cap,
                         const float *__restrict__ gamma, uint32_t *__restrict__ atom_idx,
                         float *__restrict__ atom_val, uint32_t *__restrict__ atom_cnt,
-                        uint32_t *__restrict__ trace, float *__restrict__ state_ws,
+                        uint32_t *__restrict__ trace, float *__restrict__ fw_gap,
+                        float *__restrict__ state_ws,
                         uint32_t sched_words, uint32_t lds_words_per_wave, uint32_t dense_only,
                         const uint32_t *__restrict__ cell_list,
                         const uint32_t *__restrict__ cell_count, float prune_thr,
@@ -225,13 +246,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
   // -- the step schedule, once per block
   const StepSched *sched = reinterpret_cast<const StepSched *>(lds);
   if (sched_words != 0) {
-    if (threadIdx.x == 0) {
-      StepSched *w = reinterpret_cast<StepSched *>(lds);
-      float s = 1.0f;
-      uint32_t f = 0;
-      for (uint32_t t = 0; t < T; ++t) w[t] = sched_step(gamma, t, s, f);
-      lds[sched_words - 1] = f;
-    }
+    if (threadIdx.x == 0) build_schedule(lds, sched_words, gamma, T);
     __syncthreads();
     flags |= lds[sched_words - 1];
   }
@@ -527,6 +542,35 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       wave_lds_sync();
     }
 
+    // -- the Frank-Wolfe duality gap of the returned column:
+    // <g, a> - min_c g[c] with g = s h (atoms of weight 0 add nothing)
+    float gap_out = 0.0f;
+    if (fw_gap != nullptr) {
+      float s_t;
+      if constexpr (kPrune)
+        s_t = s_cell;
+      else
+        s_t = sched_words != 0 ? __uint_as_float(lds[sched_words - 2]) : s_run;
+      const uint32_t gi = (mono && mval < 0.0f) ? midx : dense_argmin<kWave>(h, nch, lane);
+      float part = 0.0f;
+      if constexpr (kRegAtoms) {
+#pragma unroll
+        for (uint32_t j = 0; j < kWaveAtomSlots; ++j) {
+          const uint32_t m = aidx[j];
+          if (j * kWave + lane < cnt && m < k && aval[j] != 0.0f)
+            part = __builtin_fmaf(aval[j], h[m], part);
+        }
+      } else {
+        for (uint32_t sl = lane; sl < cnt; sl += kWave) {
+          const uint32_t m = s_aidx[sl];
+          const float am = s_aval[sl];
+          if (m < k && am != 0.0f) part = __builtin_fmaf(am, h[m], part);
+        }
+      }
+      const float gmin = gi < k ? h[gi] : __builtin_nanf("");
+      gap_out = s_t * (wave_sum_f32(part) - gmin);
+    }
+
     // -- write the atoms
     const size_t base = (size_t)cell * cap;
     if constexpr (kRegAtoms) {
@@ -544,7 +588,10 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
         atom_val[base + s] = s_aval[s];
       }
     }
-    if (lane == 0) atom_cnt[cell] = cnt;
+    if (lane == 0) {
+      atom_cnt[cell] = cnt;
+      if (fw_gap != nullptr) fw_gap[cell] = gap_out;
+    }
     wave_lds_sync();
   }
   // some flags are raised by single lanes: every lane that saw one reports it
@@ -563,7 +610,8 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
                         uint32_t k, uint32_t kscan, uint32_t T, uint32_t cap,
                         const float *__restrict__ gamma, uint32_t *__restrict__ atom_idx,
                         float *__restrict__ atom_val, uint32_t *__restrict__ atom_cnt,
-                        uint32_t *__restrict__ trace, float *__restrict__ state_ws,
+                        uint32_t *__restrict__ trace, float *__restrict__ fw_gap,
+                        float *__restrict__ state_ws,
                         uint32_t sched_words, uint32_t lds_words_per_wave, uint32_t dense_only,
                         uint32_t *__restrict__ status) {
   constexpr uint32_t CPW = kWave / G;           // cells per wave
@@ -581,13 +629,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
   // -- the step schedule, once per block
   const StepSched *sched = reinterpret_cast<const StepSched *>(lds);
   if (sched_words != 0) {
-    if (threadIdx.x == 0) {
-      StepSched *w = reinterpret_cast<StepSched *>(lds);
-      float s = 1.0f;
-      uint32_t f = 0;
-      for (uint32_t t = 0; t < T; ++t) w[t] = sched_step(gamma, t, s, f);
-      lds[sched_words - 1] = f;
-    }
+    if (threadIdx.x == 0) build_schedule(lds, sched_words, gamma, T);
     __syncthreads();
     flags |= lds[sched_words - 1];
   }
@@ -827,6 +869,35 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       wave_lds_sync();
     }
 
+    // -- the Frank-Wolfe duality gap of the returned column (per group)
+    float gap_out = 0.0f;
+    if (fw_gap != nullptr) {
+      const float s_t = sched_words != 0 ? __uint_as_float(lds[sched_words - 2]) : s_run;
+      const bool sparse_ok = mono && mval < 0.0f;
+      uint32_t gi = midx;
+      if (__ballot(!sparse_ok) != 0) {
+        const uint32_t d = dense_argmin<G>(h, nch, gl);
+        if (!sparse_ok) gi = d;
+      }
+      float part = 0.0f;
+      if constexpr (kRegAtoms) {
+#pragma unroll
+        for (uint32_t j = 0; j < AS; ++j) {
+          const uint32_t m = aidx[j];
+          if (j * G + gl < cnt && m < k && aval[j] != 0.0f)
+            part = __builtin_fmaf(aval[j], h[m], part);
+        }
+      } else {
+        for (uint32_t sl = gl; sl < cnt; sl += G) {
+          const uint32_t m = s_aidx[sl];
+          const float am = s_aval[sl];
+          if (m < k && am != 0.0f) part = __builtin_fmaf(am, h[m], part);
+        }
+      }
+      const float gmin = gi < k ? h[gi] : __builtin_nanf("");
+      gap_out = s_t * (group_sum_f32<G>(part) - gmin);
+    }
+
     // -- write the atoms
     if (active) {
       const size_t obase = (size_t)cell * cap;
@@ -845,7 +916,10 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
           atom_val[obase + s] = s_aval[s];
         }
       }
-      if (gl == 0) atom_cnt[cell] = cnt;
+      if (gl == 0) {
+        atom_cnt[cell] = cnt;
+        if (fw_gap != nullptr) fw_gap[cell] = gap_out;
+      }
     }
     wave_lds_sync();
   }
@@ -915,7 +989,8 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
                         uint32_t k, uint32_t T, uint32_t cap, const float *__restrict__ gamma,
                         uint32_t *__restrict__ atom_idx, float *__restrict__ atom_val,
                         uint32_t *__restrict__ atom_cnt, uint32_t *__restrict__ trace,
-                        uint32_t nwords, uint32_t hc_cap, uint32_t sched_words,
+                        float *__restrict__ fw_gap, uint32_t nwords, uint32_t hc_cap,
+                        uint32_t sched_words,
                         uint32_t lds_words_per_wave, SupQueues q, float prune_thr,
                         uint32_t *__restrict__ status) {
   extern __shared__ uint32_t lds[];
@@ -924,13 +999,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
 
   // -- the step schedule, once per block (the dense kernel reports its flags)
   const StepSched *sched = reinterpret_cast<const StepSched *>(lds);
-  if (threadIdx.x == 0) {
-    StepSched *w = reinterpret_cast<StepSched *>(lds);
-    float s = 1.0f;
-    uint32_t f = 0;
-    for (uint32_t t = 0; t < T; ++t) w[t] = sched_step(gamma, t, s, f);
-    lds[sched_words - 1] = f;
-  }
+  if (threadIdx.x == 0) build_schedule(lds, sched_words, gamma, T);
   __syncthreads();
   const bool sched_ok = lds[sched_words - 1] == 0u;
   uint32_t flags = 0;
@@ -1302,6 +1371,45 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       wave_lds_sync();
     }
 
+    // -- the Frank-Wolfe duality gap of the returned column, as the dense
+    // kernel computes it: min g is the minimum over supp(t2) when that is
+    // negative, else 0 where some column holds 0; h of an atom is the state
+    // on supp(t2), or 0 for a column no product reached. Anything else (no
+    // zero column, an atom of non-zero weight on a marked column) sends the
+    // cell to the dense kernel.
+    float gap_out = 0.0f;
+    if (fw_gap != nullptr && !deferred) {
+      const float s_t = kPrune ? s_cell : __uint_as_float(lds[sched_words - 2]);
+      bool unknown = false;
+      if (!(mval <= 0.0f)) {
+        bool zero = false;
+        for (uint32_t w0 = 0; w0 < nwords; w0 += kWave) {
+          const uint32_t w = w0 + lane;
+          if (w < nwords && ~(rec[w].x | cov[w]) != 0u) zero = true;
+        }
+        unknown = __ballot(zero) == 0;
+      }
+      float part = 0.0f;
+#pragma unroll
+      for (uint32_t j = 0; j < kWaveAtomSlots; ++j) {
+        const uint32_t m = aidx[j];
+        if (j * kWave + lane < cnt && m < k && aval[j] != 0.0f) {
+          const uint2 rw = rec[m >> 5];
+          const uint32_t bit = 1u << (m & 31u);
+          float hv = 0.0f;
+          if ((rw.x & bit) != 0u)
+            hv = hc[rw.y + __popc(rw.x & (bit - 1u))];
+          else if ((cov[m >> 5] & bit) != 0u)
+            unknown = true;
+          part = __builtin_fmaf(aval[j], hv, part);
+        }
+      }
+      if (__ballot(unknown) != 0)
+        deferred = true;
+      else
+        gap_out = s_t * (wave_sum_f32(part) - (mval < 0.0f ? mval : 0.0f));
+    }
+
     if (deferred) {
       // a pass with a larger capacity, or the dense kernel, redoes this cell
       // from the start (and writes all of it)
@@ -1323,7 +1431,10 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
         atom_val[base + s] = aval[j];
       }
     }
-    if (lane == 0) atom_cnt[cell] = cnt;
+    if (lane == 0) {
+      atom_cnt[cell] = cnt;
+      if (fw_gap != nullptr) fw_gap[cell] = gap_out;
+    }
   }
   if (flags != 0) atomicOr(status, flags);
 }
@@ -1381,7 +1492,7 @@ template <uint32_t G, bool kHInLds, bool kRegAtoms>
 hipError_t launch_variant(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr k2b, Csr ap,
                           uint32_t n, uint32_t k, uint32_t T, uint32_t cap, const float *gamma,
                           uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
-                          uint32_t *trace, void *ws, uint32_t dense_only,
+                          uint32_t *trace, float *fw_gap, void *ws, uint32_t dense_only,
                           const uint32_t *cell_list, const uint32_t *cell_count,
                           float prune_thr, uint32_t *status, hipStream_t stream) {
   static bool configured[2] = {false, false};
@@ -1421,15 +1532,16 @@ hipError_t launch_variant(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr 
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr, t1.idx,
                        t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
                        ap.val, ap.nnz, n, k, plan.kpad, T, cap, gamma, atom_idx, atom_val,
-                       atom_cnt, trace, state_ws, plan.sched_words, plan.lds_per_wave / 4,
-                       dense_only, cell_list, cell_count, prune_thr, status);
+                       atom_cnt, trace, fw_gap, state_ws, plan.sched_words,
+                       plan.lds_per_wave / 4, dense_only, cell_list, cell_count, prune_thr,
+                       status);
   } else {
     auto kern = &fw_a_group_kernel<G, kHInLds, kRegAtoms>;
     hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr, t1.idx,
                        t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
                        ap.val, ap.nnz, n, k, plan.kpad, T, cap, gamma, atom_idx, atom_val,
-                       atom_cnt, trace, state_ws, plan.sched_words, plan.lds_per_wave / 4,
-                       dense_only, status);
+                       atom_cnt, trace, fw_gap, state_ws, plan.sched_words,
+                       plan.lds_per_wave / 4, dense_only, status);
   }
   return hipGetLastError();
 }
@@ -1437,7 +1549,8 @@ hipError_t launch_variant(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr 
 hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, uint32_t tier, Csr t1,
                           Csr k2b, Csr ap, uint32_t n, uint32_t k, uint32_t T, uint32_t cap,
                           const float *gamma, uint32_t *atom_idx, float *atom_val,
-                          uint32_t *atom_cnt, uint32_t *trace, const SupQueues &q,
+                          uint32_t *atom_cnt, uint32_t *trace, float *fw_gap,
+                          const SupQueues &q,
                           float prune_thr, uint32_t *status, hipStream_t stream) {
   // t2 entries in registers: 256 for short K2B rows, 512 when rows are long
   // on average (the first pass) or by construction (the long-row pass)
@@ -1470,7 +1583,8 @@ hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, uint32_t tie
   hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr,
                      t1.idx, t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
                      ap.val, ap.nnz, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt, trace,
-                     plan.nwords, hc_cap, plan.sched_words, lpw / 4, q, prune_thr, status);
+                     fw_gap, plan.nwords, hc_cap, plan.sched_words, lpw / 4, q, prune_thr,
+                     status);
   return hipGetLastError();
 }
 
@@ -1557,7 +1671,7 @@ APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap, bool prune) {
 hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, uint32_t k,
                        uint32_t T, uint32_t cap, const float *gamma, float prune_thr,
                        uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt, uint32_t *trace,
-                       void *ws, uint32_t *status, hipStream_t stream) {
+                       float *fw_gap, void *ws, uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
@@ -1579,20 +1693,20 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
     SupQueues q0{nullptr, nullptr, ctr + 0, two ? long_list : nullptr, ctr + 2, dense_list,
                  ctr + 3};
     e = launch_support(plan, dev, 0, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
-                       atom_cnt, trace, q0, prune_thr, status, stream);
+                       atom_cnt, trace, fw_gap, q0, prune_thr, status, stream);
     if (e != hipSuccess) return e;
     if (two) {
       SupQueues q1{long_list, ctr + 2, ctr + 1, nullptr, nullptr, dense_list, ctr + 3};
       e = launch_support(plan, dev, 1, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
-                         atom_cnt, trace, q1, prune_thr, status, stream);
+                         atom_cnt, trace, fw_gap, q1, prune_thr, status, stream);
       if (e != hipSuccess) return e;
     }
     cell_list = dense_list;
     cell_count = ctr + 3;
   }
 #define SEACELLS_A_ARGS \
-  plan, dev, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt, trace, ws, \
-      dense_only, cell_list, cell_count, prune_thr, status, stream
+  plan, dev, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt, trace, fw_gap, \
+      ws, dense_only, cell_list, cell_count, prune_thr, status, stream
 #define SEACELLS_A_GROUP(GW)                                                                \
   if (plan.group == GW) {                                                                   \
     if (plan.h_in_lds)                                                                      \

@@ -415,6 +415,30 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Full Frank-Wolfe duality gap of the B subproblem: sum(B * G) - sum_c
+// min_i G[i, c]. One block: the gap partials are summed exactly as the
+// final reduce sums them (same order, f64), the column minima likewise.
+__global__ void __launch_bounds__(256)
+    fw_b_fw_gap_kernel(const float *__restrict__ part_gap, uint32_t n_units,
+                       const float *__restrict__ out_val, uint32_t k,
+                       float *__restrict__ fw_gap) {
+  __shared__ double red[2][256];
+  double s = 0.0, v = 0.0;
+  for (uint32_t u = threadIdx.x; u < n_units; u += 256) s += (double)part_gap[u];
+  for (uint32_t c = threadIdx.x; c < k; c += 256) v += (double)out_val[c];
+  red[0][threadIdx.x] = s;
+  red[1][threadIdx.x] = v;
+  __syncthreads();
+  for (uint32_t w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + w];
+      red[1][threadIdx.x] += red[1][threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *fw_gap = (float)(red[0][0] - red[1][0]);
+}
+
 // B step on padded B^T rows, one thread per archetype.
 __global__ void __launch_bounds__(256)
     fw_b_apply_kernel(uint32_t *__restrict__ bt_idx, float *__restrict__ bt_val,
@@ -554,8 +578,9 @@ hipError_t launch_status_clear(uint32_t *status, hipStream_t stream) {
 }
 
 hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
-                       uint32_t k, float *out_val, uint32_t *out_idx, float *gap, void *ws,
-                       uint32_t *status, uint32_t epoch, hipStream_t stream) {
+                       uint32_t k, float *out_val, uint32_t *out_idx, float *gap,
+                       float *fw_gap, void *ws, uint32_t *status, uint32_t epoch,
+                       hipStream_t stream) {
   char *base = static_cast<char *>(ws);
   uint64_t *keys = reinterpret_cast<uint64_t *>(base + p.off_keys);
   uint64_t *part2 = reinterpret_cast<uint64_t *>(base + p.off_part2);
@@ -603,7 +628,13 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
   const uint32_t units = p.n_row_blocks * p.n_slices;
   hipLaunchKernelGGL(fw_b_reduce2_kernel, dim3((k + 255) / 256 + 1), dim3(256), 0, stream, part2,
                      p.n_chunks, gap_part, units, n, k, out_val, out_idx, gap, status);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (fw_gap != nullptr) {
+    hipLaunchKernelGGL(fw_b_fw_gap_kernel, dim3(1), dim3(256), 0, stream, gap_part, units,
+                       out_val, k, fw_gap);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 hipError_t launch_fw_b_apply(uint32_t *bt_idx, float *bt_val, uint32_t *bt_cnt, uint32_t n,

@@ -62,16 +62,16 @@ def load():
     lib.seacells_fw_a_columns_workspace.argtypes = [_U32, _U32, _U32, _U32]
     lib.seacells_fw_a_columns.restype = ctypes.c_int
     lib.seacells_fw_a_columns.argtypes = [_CSR_P, _CSR_P, _CSR_P, _U32, _U32, _U32, _U32, _VP, _VP,
-                                          _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP]
+                                          _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP]
     lib.seacells_fw_a_columns_pruned.restype = ctypes.c_int
     lib.seacells_fw_a_columns_pruned.argtypes = [_CSR_P, _CSR_P, _CSR_P, _U32, _U32, _U32, _U32,
                                                  _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP,
-                                                 ctypes.c_size_t, _VP, _VP]
+                                                 _VP, ctypes.c_size_t, _VP, _VP]
     lib.seacells_fw_b_argmin_workspace.restype = ctypes.c_size_t
     lib.seacells_fw_b_argmin_workspace.argtypes = [_U32, _U32]
     lib.seacells_fw_b_argmin.restype = ctypes.c_int
     lib.seacells_fw_b_argmin.argtypes = [_CSR_P, _CSR_P, _CSR_P, _CSR_P, _U32, _U32, _VP, _VP, _VP,
-                                         _VP, ctypes.c_size_t, _VP, _VP]
+                                         _VP, _VP, ctypes.c_size_t, _VP, _VP]
     lib.seacells_fw_b_apply.restype = ctypes.c_int
     lib.seacells_fw_b_apply.argtypes = [_VP, _VP, _VP, _U32, _U32, _U32, _VP, ctypes.c_float,
                                         _VP, _VP]
@@ -164,27 +164,30 @@ def seacells_fw_a_columns_workspace(n, k, T, cap) -> int:
 
 def seacells_fw_a_columns(t1: DeviceCSR, k2b: DeviceCSR, a_prev_t: DeviceCSR, n: int, k: int,
                           T: int, cap: int, gamma=None, atom_idx=None, atom_val=None,
-                          atom_cnt=None, trace=None, workspace=None, status=None, stream=None):
+                          atom_cnt=None, trace=None, workspace=None, status=None, stream=None,
+                          fw_gap=None):
     """A update. Returns (atom_idx [n, cap], atom_val [n, cap], atom_cnt [n], trace, status).
 
     Outputs and workspace are allocated when not given; pass ``trace=True``
-    to get the per-step argmin trace [n, T].
+    to get the per-step argmin trace [n, T]. ``fw_gap`` (a float32 [n]
+    device tensor, filled in place) receives the Frank-Wolfe gap of each
+    returned column.
     """
     return _a_columns(None, t1, k2b, a_prev_t, n, k, T, cap, gamma, atom_idx, atom_val,
-                      atom_cnt, trace, workspace, status, stream)
+                      atom_cnt, trace, fw_gap, workspace, status, stream)
 
 
 def seacells_fw_a_columns_pruned(t1: DeviceCSR, k2b: DeviceCSR, a_prev_t: DeviceCSR, n: int,
                                  k: int, T: int, cap: int, threshold: float, gamma=None,
                                  atom_idx=None, atom_val=None, atom_cnt=None, trace=None,
-                                 workspace=None, status=None, stream=None):
+                                 workspace=None, status=None, stream=None, fw_gap=None):
     """A update with the pruning + renormalisation step; as seacells_fw_a_columns."""
     return _a_columns(float(threshold), t1, k2b, a_prev_t, n, k, T, cap, gamma, atom_idx,
-                      atom_val, atom_cnt, trace, workspace, status, stream)
+                      atom_val, atom_cnt, trace, fw_gap, workspace, status, stream)
 
 
 def _a_columns(threshold, t1, k2b, a_prev_t, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt,
-               trace, workspace, status, stream):
+               trace, fw_gap, workspace, status, stream):
     lib = load()
     dev = t1.row_ptr.device
     if atom_idx is None:
@@ -203,8 +206,11 @@ def _a_columns(threshold, t1, k2b, a_prev_t, n, k, T, cap, gamma, atom_idx, atom
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     s1, s2, s3 = t1.struct(), k2b.struct(), a_prev_t.struct()
-    tail = (_ptr(atom_idx), _ptr(atom_val), _ptr(atom_cnt), _ptr(trace), _ptr(workspace),
-            0 if workspace is None else workspace.numel(), _ptr(status), _stream(stream))
+    if fw_gap is not None and (fw_gap.dtype != torch.float32 or fw_gap.numel() < n):
+        raise SeacellsError("fw_gap must be a float32 tensor of at least n entries")
+    tail = (_ptr(atom_idx), _ptr(atom_val), _ptr(atom_cnt), _ptr(trace), _ptr(fw_gap),
+            _ptr(workspace), 0 if workspace is None else workspace.numel(), _ptr(status),
+            _stream(stream))
     if threshold is None:
         rc = lib.seacells_fw_a_columns(ctypes.byref(s1), ctypes.byref(s2), ctypes.byref(s3), n,
                                        k, T, cap, _ptr(gamma), *tail)
@@ -222,8 +228,12 @@ def seacells_fw_b_argmin_workspace(n, k) -> int:
 
 def seacells_fw_b_argmin(k2b: DeviceCSR, aat: DeviceCSR, k2at: DeviceCSR, b, n: int, k: int,
                          out_val=None, out_idx=None, gap=None, workspace=None, status=None,
-                         stream=None):
-    """B-gradient argmin. Returns (out_val [k], out_idx [k], gap [1], status)."""
+                         stream=None, fw_gap=None):
+    """B-gradient argmin. Returns (out_val [k], out_idx [k], gap [1], status).
+
+    ``fw_gap`` (a float32 [1] device tensor, filled in place) receives the
+    full Frank-Wolfe gap sum(B * G) - sum_c min_i G[i, c]; it needs ``b``.
+    """
     lib = load()
     dev = k2b.row_ptr.device
     if out_val is None:
@@ -241,8 +251,9 @@ def seacells_fw_b_argmin(k2b: DeviceCSR, aat: DeviceCSR, k2at: DeviceCSR, b, n: 
     sb = b.struct() if b is not None else None
     rc = lib.seacells_fw_b_argmin(ctypes.byref(s1), ctypes.byref(s2), ctypes.byref(s3),
                                   ctypes.byref(sb) if sb is not None else None, n, k,
-                                  _ptr(out_val), _ptr(out_idx), _ptr(gap), _ptr(workspace),
-                                  workspace.numel(), _ptr(status), _stream(stream))
+                                  _ptr(out_val), _ptr(out_idx), _ptr(gap), _ptr(fw_gap),
+                                  _ptr(workspace), workspace.numel(), _ptr(status),
+                                  _stream(stream))
     _check_rc(rc)
     return out_val, out_idx, gap, status
 

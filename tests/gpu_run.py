@@ -9,27 +9,42 @@ def dev(m):
     return saa.DeviceCSR.from_scipy(m)
 
 
-def run_a(w, T=None, cap=None, gamma=None, trace=True, ops=None, prune=None):
+def run_a(w, T=None, cap=None, gamma=None, trace=True, ops=None, prune=None, gap_out=None):
+    """A update on the GPU; the five outputs as numpy. ``gap_out`` (a list)
+    receives the per-cell Frank-Wolfe gap when given."""
     T = w.T if T is None else T
     cap = w.cap if cap is None else cap
     g = None if gamma is None else torch.tensor(np.asarray(gamma, np.float32), device="cuda")
     t1, k2b, ap = ops if ops is not None else (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
+    fg = None
+    if gap_out is not None:
+        fg = torch.full((w.n,), float("nan"), dtype=torch.float32, device="cuda")
     if prune is None:
         ai, av, ac, tr, st = saa.seacells_fw_a_columns(t1, k2b, ap, w.n, w.k, T, cap, gamma=g,
-                                                       trace=trace)
+                                                       trace=trace, fw_gap=fg)
     else:
         ai, av, ac, tr, st = saa.seacells_fw_a_columns_pruned(t1, k2b, ap, w.n, w.k, T, cap,
-                                                              prune, gamma=g, trace=trace)
+                                                              prune, gamma=g, trace=trace,
+                                                              fw_gap=fg)
     torch.cuda.synchronize()
+    if gap_out is not None:
+        gap_out.append(fg.cpu().numpy())
     return (ai.cpu().numpy(), av.cpu().numpy(), ac.cpu().numpy(),
             tr.cpu().numpy() if tr is not None else None, saa.status_flags(st))
 
 
-def run_b(w, with_b=True, ops=None):
+def run_b(w, with_b=True, ops=None, gap_out=None):
+    """B argmin on the GPU: (min values, rows, gap, flags). ``gap_out`` (a
+    list) receives the full Frank-Wolfe gap when given."""
     k2b, aat, k2at, b = ops if ops is not None else (dev(w.k2b), dev(w.aat), dev(w.k2at),
                                                      dev(w.b) if with_b else None)
-    v, i, g, st = saa.seacells_fw_b_argmin(k2b, aat, k2at, b, w.n, w.k)
+    fg = None
+    if gap_out is not None:
+        fg = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    v, i, g, st = saa.seacells_fw_b_argmin(k2b, aat, k2at, b, w.n, w.k, fw_gap=fg)
     torch.cuda.synchronize()
+    if gap_out is not None:
+        gap_out.append(float(fg.cpu().numpy()[0]))
     return v.cpu().numpy(), i.cpu().numpy(), float(g.cpu().numpy()[0]), saa.status_flags(st)
 
 

@@ -30,6 +30,11 @@ GAP_REL = 1e-3                  # sum(B * G) (the page's policy)
 # side of it: f32 weights of ~0.02 carry ~1e-7 of rounding after 50 steps);
 # outside that band both take the same drop decisions.
 PRUNE_MARGIN = 1e-6
+# Frank-Wolfe gap of the returned column, <g, a> - min g: each g entry
+# carries f32 rounding of ~T ulps of the term scale S (T = 50: ~3e-6 S; S is
+# the largest over the run, since drops take earlier terms back out), and
+# the minimum may sit at a near tie: within 2e-5 S.
+GAP_A_REL = 2e-5
 
 
 def dense_atoms(atom_idx, atom_val, atom_cnt, k):
@@ -55,6 +60,7 @@ class AReport:
     max_abs_err: float
     worst_window: float
     skipped: int = 0          # cells left out for a drop decision within PRUNE_MARGIN
+    gap_err: float = 0.0      # worst |fw_gap - oracle| / scale when the gap was checked
 
 
 def check_atom_layout(atom_idx, atom_cnt, trace, a_prev_t, cells):
@@ -71,7 +77,7 @@ def check_atom_layout(atom_idx, atom_cnt, trace, a_prev_t, cells):
 
 
 def check_a(w, gpu_trace, atom_idx, atom_val, atom_cnt, cells, gamma=None, T=None,
-            strict_zero_ties=True, prune=None) -> AReport:
+            strict_zero_ties=True, prune=None, fw_gap=None) -> AReport:
     """Trace replay of the A update for ``cells``; returns counts and errors.
 
     ``prune`` (a threshold) replays the pruning variant. Its drop steps take
@@ -93,7 +99,9 @@ def check_a(w, gpu_trace, atom_idx, atom_val, atom_cnt, cells, gamma=None, T=Non
         if skipped:
             cells, trace = cells[keep], trace[keep]
             atom_idx, atom_val, atom_cnt = atom_idx[keep], atom_val[keep], atom_cnt[keep]
-            for f in ("a", "pick", "g_min", "g_second", "g_scale", "g_taken"):
+            if fw_gap is not None:
+                fw_gap = np.asarray(fw_gap)[keep]
+            for f in ("a", "pick", "g_min", "g_second", "g_scale", "g_taken", "g_dot"):
                 setattr(rep, f, getattr(rep, f)[keep])
     exact = trace == rep.pick
     window = TIE_REL * np.maximum(np.maximum(np.abs(rep.g_min), np.abs(rep.g_second)),
@@ -125,9 +133,27 @@ def check_a(w, gpu_trace, atom_idx, atom_val, atom_cnt, cells, gamma=None, T=Non
     err = float(np.max(np.abs(got - rep.a))) if got.size else 0.0
     assert err <= A_ABS, "A entries differ from the replayed oracle by %.3g" % err
     check_atom_layout(atom_idx, atom_cnt, trace, w.a_prev_t, cells)
+    gap_err = 0.0
+    if fw_gap is not None and cells.shape[0]:
+        # the gap of the returned column a_T: the oracle replays the T steps
+        # and reports the gap at the start of one more (free) step; the f32
+        # state's rounding is relative to the largest terms it has held
+        # (pruning takes whole rows back out of it)
+        force1 = np.concatenate([trace, np.full((cells.shape[0], 1), -1, np.int64)], axis=1)
+        gam1 = None if gamma is None else np.concatenate([np.asarray(gamma, np.float64), [0.5]])
+        rep1 = oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, T + 1, cells=cells,
+                                   force=force1, gamma=gam1, prune=prune)
+        want = rep1.fw_gap[:, T]
+        scale = np.maximum(rep1.g_scale.max(axis=1), np.abs(want))
+        got = np.asarray(fw_gap, np.float64)
+        rel = np.abs(got - want) / np.maximum(scale, 1e-30)
+        worst = int(np.argmax(rel))
+        assert rel[worst] <= GAP_A_REL, ("cell %d: fw_gap %.9g, oracle %.9g (scale %.3g)"
+                                         % (cells[worst], got[worst], want[worst], scale[worst]))
+        gap_err = float(rel[worst])
     return AReport(int(trace.size), int(exact.sum()), int((~exact).sum()), int(zero_tie.sum()),
                    err, float(np.max(excess / np.maximum(window, 1e-300))) if excess.size else 0.0,
-                   skipped)
+                   skipped, gap_err)
 
 
 @dataclass
@@ -138,7 +164,7 @@ class BReport:
     gap_rel: float
 
 
-def check_b(w, out_val, out_idx, gap, n=None, k=None, b=True, res=None) -> BReport:
+def check_b(w, out_val, out_idx, gap, n=None, k=None, b=True, res=None, fw_gap=None) -> BReport:
     n = w.n if n is None else n
     k = w.k if k is None else k
     if res is None:
@@ -164,5 +190,11 @@ def check_b(w, out_val, out_idx, gap, n=None, k=None, b=True, res=None) -> BRepo
     if gap is not None and b:
         grel = abs(float(gap) - res.gap) / max(abs(res.gap), 1e-4 / GAP_REL)
         assert grel <= GAP_REL, "gap %.9g vs oracle %.9g" % (float(gap), res.gap)
+    if fw_gap is not None:
+        # the full gap sum(B * G) - sum_c min G, at the page's relative gap
+        # policy, relative to the size of the two sums it is a difference of
+        size = abs(res.gap) + float(np.sum(np.abs(res.val)))
+        assert abs(float(fw_gap) - res.fw_gap) <= GAP_REL * max(size, 1e-4 / GAP_REL), \
+            "fw_gap %.9g vs oracle %.9g" % (float(fw_gap), res.fw_gap)
     return BReport(int(exact.sum()), int((~exact).sum()),
                    float(np.max(dv / np.maximum(np.abs(res.val), 1e-30))), grel)

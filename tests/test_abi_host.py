@@ -46,7 +46,7 @@ def call_a(t1, k2b, ap, n, k, T, cap, ws=None, ws_bytes=0, outs=True, status=0x9
     return lib.seacells_fw_a_columns(ctypes.byref(t1) if t1 else None,
                                      ctypes.byref(k2b) if k2b else None,
                                      ctypes.byref(ap) if ap else None, n, k, T, cap, None, o, o,
-                                     o, None, ws, ws_bytes, status, None)
+                                     o, None, None, ws, ws_bytes, status, None)
 
 
 def test_a_columns_rejects_bad_arguments_on_host():
@@ -89,11 +89,12 @@ def test_b_argmin_rejects_bad_arguments_on_host():
     assert ws > 0 and ws % 256 == 0
 
     def call(k2b=k2b, aat=aat, k2at=k2at, b=b, n=n, k=k, ws_ptr=0x100000, ws_bytes=ws,
-             out=0x4000, status=0x9000):
+             out=0x4000, status=0x9000, fw_gap=None):
         r = lambda m: ctypes.byref(m) if m is not None else None
         return lib.seacells_fw_b_argmin(r(k2b), r(aat), r(k2at), r(b), n, k, out, out, None,
-                                        ws_ptr, ws_bytes, status, None)
+                                        fw_gap, ws_ptr, ws_bytes, status, None)
     assert call(k2b=None) == -1
+    assert call(b=None, fw_gap=0x5000) == -1   # the full gap needs B
     assert call(out=None) == -1
     assert call(status=None) == -1
     assert call(n=0) == -2
@@ -137,7 +138,7 @@ def test_a_columns_pruned_rejects_bad_threshold_on_host():
     def call(thr, t1=t1):
         return lib.seacells_fw_a_columns_pruned(ctypes.byref(t1), ctypes.byref(k2b),
                                                 ctypes.byref(ap), n, k, T, cap, None, thr, o, o,
-                                                o, None, None, 0, 0x9000, None)
+                                                o, None, None, None, 0, 0x9000, None)
     assert call(-0.1) == -2
     assert call(float("nan")) == -2
     assert call(float("inf")) == -2

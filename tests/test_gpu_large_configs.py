@@ -2,9 +2,10 @@
 k = 10000) at full size on the GPU, against the f64 oracle.
 
 A update: trace replay on a random sample of cells (the oracle redoes each
-sampled cell exactly), properties that hold for every cell, and the compact
-per-cell state against the dense kernel bit for bit on every cell.
-B argmin: every column against the full oracle.
+sampled cell exactly, with its Frank-Wolfe gap), properties that hold for
+every cell, and the compact per-cell state against the dense kernel bit for
+bit on every cell. B argmin: every column and the full gap against the full
+oracle.
 
 Each workload is generated once per module (about 12 s and 60 s on the GPU
 machine; kNN on the GPU, products on the host cores).
@@ -34,11 +35,14 @@ def big(request):
 
 def test_a_update_sampled_cells_and_invariants(big):
     name, w, ops = big
-    ai, av, ac, tr, flags = run_a(w, ops=ops)
+    gaps = []
+    ai, av, ac, tr, flags = run_a(w, ops=ops, gap_out=gaps)
     assert flags == []
     rng = np.random.default_rng(4 if name == "c4" else 5)
     cells = np.unique(np.concatenate([[0, w.n - 1], rng.choice(w.n, size=160, replace=False)]))
-    rep = parity.check_a(w, tr[cells], ai[cells], av[cells], ac[cells], cells)
+    rep = parity.check_a(w, tr[cells], ai[cells], av[cells], ac[cells], cells,
+                         fw_gap=gaps[0][cells])
+    assert not np.any(np.isnan(gaps[0]))
     print("\n%s sampled: %s" % (name, rep))
     parity.check_atom_layout(ai[cells], ac[cells], tr[cells], w.a_prev_t, cells)
     # every cell: counts within [seeds, cap], picks in range, weights on the simplex
@@ -67,7 +71,8 @@ def test_compact_state_equals_dense_kernel(big, monkeypatch):
 
 def test_b_argmin_all_columns(big):
     name, w, _ = big
-    v, i, g, flags = run_b(w)
+    gl = []
+    v, i, g, flags = run_b(w, gap_out=gl)
     assert flags == []
-    rep = parity.check_b(w, v, i, g)
+    rep = parity.check_b(w, v, i, g, fw_gap=gl[0])
     print("\n%s: %s" % (name, rep))
