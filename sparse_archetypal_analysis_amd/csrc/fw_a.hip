@@ -59,6 +59,14 @@ constexpr uint32_t kSupMinHc = 256;         // smallest useful t2 capacity
 constexpr uint32_t kSupMaxHc = 8192;
 constexpr float kRenormFloor = 1e-15f;      // the page's A_RENORM_FLOOR
 
+// base[byte_off / sizeof(T)] with a 32-bit byte offset from a wave-uniform
+// base: one offset register serves loads from several arrays (valid while
+// the array holds fewer than 2^30 four-byte entries).
+template <typename T>
+__device__ __forceinline__ T load_at(const T *__restrict__ base, uint32_t byte_off) {
+  return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
 struct StepSched {
   float gam;    // gamma_t
   float keep;   // 1 - gamma_t; 0 means restart
@@ -267,24 +275,35 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       flags |= kFlagBadIndex;
       p0 = p1 = 0;
     }
-    const uint32_t nit = (p1 - p0 + kWave - 1) / kWave;
-    bool lane_neg = false;
-    for (uint32_t i = 0; i < nit; ++i) {
-      const uint32_t p = p0 + i * kWave + lane;
-      const bool valid = p < p1;
-      const uint32_t pc = valid ? p : p1 - 1;
-      uint32_t c = t1_idx[pc];
-      float v = t1_val[pc];
-      if (c >= k) {
-        if (valid) flags |= kFlagBadIndex;
-        c = dummy;
-        v = 0.0f;
-      }
-      if (!valid) c = dummy, v = 0.0f;
-      h[c] = __builtin_fmaf(alpha, v, h[c]);
-      lane_neg |= (v < 0.0f);
+    uint32_t sgn = 0;  // OR of the values' bits: the sign bit marks a negative one (or -0)
+    uint32_t cmax = 0;  // largest column read: one range check per row
+    // the row from a wave-uniform base, addressed with 32-bit byte offsets
+    uint32_t len = p1 - p0;
+    if (len > (1u << 30)) {  // longer than any row of a k x k matrix can be
+      flags |= kFlagBadIndex;
+      len = 0;
     }
-    return __ballot(lane_neg) != 0;
+    const uint32_t *ri = t1_idx + p0;
+    const float *rv = t1_val + p0;
+    for (uint32_t o = lane; o - lane < len; o += kWave) {
+      const bool valid = o < len;
+      const uint32_t oc = min(o, len - 1u);  // in the row; dropped below
+      uint32_t c = load_at(ri, oc * 4u);
+      float v = load_at(rv, oc * 4u);
+      // both loads stay unconditional and in flight together (no branch
+      // around the value load for the lanes past the row end)
+      asm volatile("" : "+v"(c), "+v"(v));
+      cmax = max(cmax, c);
+      // an out-of-range column or a lane past the row end adds 0 to the
+      // +inf padding column
+      const bool ok = valid && c < k;
+      const uint32_t cs = ok ? c : dummy;
+      const float vs = ok ? v : 0.0f;
+      h[cs] = __builtin_fmaf(alpha, vs, h[cs]);
+      sgn |= __float_as_uint(vs);
+    }
+    if (cmax >= k) flags |= kFlagBadIndex;
+    return __ballot((int32_t)sgn < 0) != 0;
   };
 
   for (uint32_t slot = gwave; slot < ncells; slot += nwaves) {
@@ -387,12 +406,15 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
           }
         }
       }
-      // minimum value key over the wave, then the lowest column holding it:
-      // entries are ascending in (chunk, lane) order, so the first chunk with
-      // a matching lane and, in it, the lowest matching lane win
-      const uint32_t key = f32_order(bv);
+      // minimum over the wave, then the lowest column holding it: entries
+      // are ascending in (chunk, lane) order, so the first chunk with a
+      // matching lane and, in it, the lowest matching lane win. Only a
+      // negative minimum is used (the dense scan decides otherwise), so the
+      // key is ~bits: ordered like the values among negative numbers, and
+      // above every negative number for the others (-0 and +inf included).
+      const uint32_t key = ~__float_as_uint(bv);
       const uint32_t best = wave_min_u32(key);
-      mval = f32_unorder(best);
+      mval = __uint_as_float(~best);  // the minimum when negative; else only >= -0
       midx = kNone;
       for (uint32_t r = 0; r < nr; ++r) {
         const uint64_t m = __ballot(key == best && br == r && bi != kNone);
@@ -423,9 +445,11 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       if constexpr (kRegAtoms) {
 #pragma unroll
         for (uint32_t j = 0; j < kWaveAtomSlots; ++j) {
-          const bool at = aidx[j] == idx;
-          aval[j] = at ? __builtin_fmaf(aval[j], sc.keep, sc.gam) : aval[j] * sc.keep;
-          hit |= at;
+          if (j * kWave < cap) {  // (a wave-uniform test: one slot per lane when cap <= 64)
+            const bool at = aidx[j] == idx;
+            aval[j] = at ? __builtin_fmaf(aval[j], sc.keep, sc.gam) : aval[j] * sc.keep;
+            hit |= at;
+          }
         }
       } else {
         for (uint32_t s = lane; s < cnt; s += kWave) {
@@ -964,13 +988,6 @@ struct SupQueues {
   uint32_t *dense_cnt;
 };
 
-// base[byte_off / sizeof(T)] with a 32-bit byte offset from a wave-uniform
-// base: one offset register serves loads from several arrays (valid while
-// the array holds fewer than 2^30 four-byte entries).
-template <typename T>
-__device__ __forceinline__ T load_at(const T *__restrict__ base, uint32_t byte_off) {
-  return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
-}
 
 constexpr uint32_t kTailPos = 0x80000000u;  // marks a t2 position (not a column) in the pass
 constexpr uint32_t kRowBatch = 2;   // chunks of a t1 row whose loads are in flight together
