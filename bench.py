@@ -189,7 +189,7 @@ def main():
     atom_idx = torch.empty((n, cap), dtype=torch.int32, device=dev)
     atom_val = torch.empty((n, cap), dtype=torch.float32, device=dev)
     atom_cnt = torch.empty(n, dtype=torch.int32, device=dev)
-    ws_a_bytes = saa.seacells_fw_a_columns_workspace(n, k, T, cap)
+    ws_a_bytes = saa.seacells_fw_a_columns_workspace(n, k, T, cap, w.t1.nnz)
     ws_a = torch.empty(max(ws_a_bytes, 1), dtype=torch.uint8, device=dev)
     out_val = torch.empty(k, dtype=torch.float32, device=dev)
     out_idx = torch.empty(k, dtype=torch.int32, device=dev)

@@ -83,15 +83,18 @@ typedef struct seacells_csr {
 } seacells_csr;
 
 /*
- * Workspace bytes seacells_fw_a_columns needs for these sizes. 0 when the
- * dense per-cell state fits in local memory and k is small; for large k
- * (from 2048) it holds two counters and a queue of n cell ids (the cells
- * the compact per-cell state hands to the dense kernel); when not even the
- * dense state fits in local memory it also holds per-wave state slices.
- * Depends only on its arguments (and on the SEACELLS_A_* experiment
+ * Workspace bytes seacells_fw_a_columns needs for these sizes (t1_nnz: the
+ * non-zeros of t1). It holds a copy of t1 with every row padded to whole
+ * chunks of 64 entries (at most 8 * (t1_nnz + 64 k) bytes) when a wave
+ * takes one cell (k above 1024, or the pruning variant); for large k (from
+ * 2048) two counters and queues of n cell ids (the cells the compact
+ * per-cell state hands on); and per-wave state slices when not even one
+ * cell's dense state fits in local memory. 0 when none is needed (small
+ * k). Depends only on its arguments (and on the SEACELLS_A_* experiment
  * variables of the environment, which must be the same at the call).
  */
-size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint32_t cap);
+size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint32_t cap,
+                                       uint32_t t1_nnz);
 
 /*
  * A update: the per-cell column solve of `fw_columns_a_gpu` on the source
@@ -130,6 +133,7 @@ size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint3
  *           after the last step (no cost when NULL).
  * workspace device buffer of at least seacells_fw_a_columns_workspace()
  *           bytes (may be NULL when that is 0), 256-byte aligned.
+ * k must be below 2^30 (else SEACELLS_E_TOO_LARGE).
  */
 int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
                           const seacells_csr *a_prev_t, uint32_t n, uint32_t k,

@@ -68,11 +68,12 @@ using namespace seacells;
 
 extern "C" {
 
-size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint32_t cap) {
+size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint32_t cap,
+                                       uint32_t t1_nnz) {
   if (n == 0 || k == 0 || cap == 0) return 0;
   // one size covers the plain and the pruning entry point
-  const size_t plain = plan_a(n, k, T, cap, false).ws_bytes;
-  const size_t pruned = plan_a(n, k, T, cap, true).ws_bytes;
+  const size_t plain = plan_a(n, k, T, cap, false, t1_nnz).ws_bytes;
+  const size_t pruned = plan_a(n, k, T, cap, true, t1_nnz).ws_bytes;
   return plain > pruned ? plain : pruned;
 }
 
@@ -87,7 +88,7 @@ static int a_columns(const seacells_csr *t1, const seacells_csr *k2b,
     return SEACELLS_E_NULL;
   if (n == 0 || k == 0 || T == 0 || cap == 0) return SEACELLS_E_SHAPE;
   if (prune && !(threshold >= 0.0f && threshold <= 3.4e38f)) return SEACELLS_E_SHAPE;
-  if (n >= 0x80000000u || k >= 0x80000000u) return SEACELLS_E_TOO_LARGE;
+  if (n >= 0x80000000u || k >= 0x40000000u) return SEACELLS_E_TOO_LARGE;
   int rc;
   if ((rc = check_csr(t1, k, k)) != SEACELLS_OK) return rc;
   if ((rc = check_csr(k2b, n, k)) != SEACELLS_OK) return rc;
@@ -95,7 +96,7 @@ static int a_columns(const seacells_csr *t1, const seacells_csr *k2b,
   if ((uint64_t)n * cap >= (1ull << 40) || (uint64_t)n * T >= (1ull << 40))
     return SEACELLS_E_TOO_LARGE;
   if (cap >= 0x10000000u) return SEACELLS_E_TOO_LARGE;
-  const APlan plan = plan_a(n, k, T, cap, prune);
+  const APlan plan = plan_a(n, k, T, cap, prune, t1->nnz);
   // per-wave LDS must at least hold the atom list
   if (plan.waves_per_block == 0) return SEACELLS_E_TOO_LARGE;
   if (plan.ws_bytes > 0 && (workspace == nullptr || workspace_bytes < plan.ws_bytes))

@@ -134,9 +134,15 @@ struct APlan {
   size_t ws_list_off;          // cells for the long-row pass (counters sit at offset 0)
   size_t ws_list2_off;         // cells for the dense kernel
   size_t ws_dense_off;         // dense state slices
+  // one cell per wave: t1 copied with every row padded to whole chunks of 64
+  // (column byte offset, value) pairs, so a step reads rows without checks
+  bool padded;
+  uint32_t pad_chunks;         // bound on the chunks of all rows
+  size_t ws_pt_ptr_off;        // [k + 1] u32: 2 * first chunk of row r, | 1 if r has a value < 0
+  size_t ws_pt_ent_off;        // [pad_chunks * 64] uint2
   size_t ws_bytes;
 };
-APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap, bool prune);
+APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap, bool prune, uint32_t t1_nnz);
 hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, uint32_t k,
                        uint32_t T, uint32_t cap, const float *gamma, float prune_thr,
                        uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt, uint32_t *trace,

@@ -222,8 +222,7 @@ constexpr uint32_t kWaveAtomSlots = 2;  // atom slots per lane in registers
 // renormalise (the page's pruning variant); the scale s is then per cell.
 template <bool kHInLds, bool kRegAtoms, bool kPrune>
 __global__ void __launch_bounds__(kABlockMaxThreads)
-    fw_a_wave_kernel(const uint32_t *__restrict__ t1_ptr, const uint32_t *__restrict__ t1_idx,
-                        const float *__restrict__ t1_val, uint32_t t1_nnz,
+    fw_a_wave_kernel(const uint32_t *__restrict__ pt_ptr, const uint2 *__restrict__ pt_ent,
                         const uint32_t *__restrict__ k2b_ptr, const uint32_t *__restrict__ k2b_idx,
                         const float *__restrict__ k2b_val, uint32_t k2b_nnz,
                         const uint32_t *__restrict__ ap_ptr, const uint32_t *__restrict__ ap_idx,
@@ -267,43 +266,20 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
   const uint32_t dummy = k;  // first padding column: holds +inf
   const float inf = __builtin_inff();
 
-  // h += alpha * (row r of t1); columns of one row are unique, so no two
-  // lanes touch the same column. Returns whether some product was negative.
+  // h += alpha * (row r of t1), from the padded copy: whole chunks of 64
+  // (column byte offset, value) pairs, padding entries pointing at the +inf
+  // column with value 0. Columns of one row are unique, so no two lanes
+  // touch the same column. Returns whether the row holds a negative value.
+  char *hb = reinterpret_cast<char *>(h);
   auto scatter_row = [&](uint32_t r, float alpha) -> bool {
-    uint32_t p0 = t1_ptr[r], p1 = t1_ptr[r + 1];
-    if (p1 > t1_nnz || p0 > p1) {
-      flags |= kFlagBadIndex;
-      p0 = p1 = 0;
+    const uint32_t e0 = pt_ptr[r], e1 = pt_ptr[r + 1];
+    const uint32_t c0 = e0 >> 1, c1 = e1 >> 1;
+    for (uint32_t ch = c0; ch < c1; ++ch) {
+      const uint2 e = load_at(pt_ent + (size_t)ch * kWave, lane * 8u);
+      float *hp = reinterpret_cast<float *>(hb + e.x);
+      *hp = __builtin_fmaf(alpha, __uint_as_float(e.y), *hp);
     }
-    uint32_t sgn = 0;  // OR of the values' bits: the sign bit marks a negative one (or -0)
-    uint32_t cmax = 0;  // largest column read: one range check per row
-    // the row from a wave-uniform base, addressed with 32-bit byte offsets
-    uint32_t len = p1 - p0;
-    if (len > (1u << 30)) {  // longer than any row of a k x k matrix can be
-      flags |= kFlagBadIndex;
-      len = 0;
-    }
-    const uint32_t *ri = t1_idx + p0;
-    const float *rv = t1_val + p0;
-    for (uint32_t o = lane; o - lane < len; o += kWave) {
-      const bool valid = o < len;
-      const uint32_t oc = min(o, len - 1u);  // in the row; dropped below
-      uint32_t c = load_at(ri, oc * 4u);
-      float v = load_at(rv, oc * 4u);
-      // both loads stay unconditional and in flight together (no branch
-      // around the value load for the lanes past the row end)
-      asm volatile("" : "+v"(c), "+v"(v));
-      cmax = max(cmax, c);
-      // an out-of-range column or a lane past the row end adds 0 to the
-      // +inf padding column
-      const bool ok = valid && c < k;
-      const uint32_t cs = ok ? c : dummy;
-      const float vs = ok ? v : 0.0f;
-      h[cs] = __builtin_fmaf(alpha, vs, h[cs]);
-      sgn |= __float_as_uint(vs);
-    }
-    if (cmax >= k) flags |= kFlagBadIndex;
-    return __ballot((int32_t)sgn < 0) != 0;
+    return (e0 & 1u) != 0u;
   };
 
   for (uint32_t slot = gwave; slot < ncells; slot += nwaves) {
@@ -952,6 +928,103 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
 }
 
 // ---------------------------------------------------------------------------
+// Padded copy of t1 for the one-cell-per-wave kernel.
+//
+// pt_ptr[r] = 2 * (first chunk of row r) | (row r holds a value < 0), with
+// pt_ptr[k] = 2 * (all chunks); a row of len entries takes ceil(len / 64)
+// chunks of 64 entries (column * 4, value bits). Entries past the row end
+// point at column k (the state's +inf padding) with value 0. A malformed
+// row (end past nnz or before its start) or column (>= k) raises
+// BAD_INDEX; such a row is left empty and such an entry becomes padding.
+// If the chunks would exceed the bound the workspace was sized for (only
+// possible with malformed row pointers), every row is left empty.
+
+// One block: chunk counts per row and their exclusive prefix sum.
+__global__ void __launch_bounds__(1024)
+    pad_rows_kernel(const uint32_t *__restrict__ t1_ptr, uint32_t t1_nnz, uint32_t k,
+                    uint32_t pad_chunks, uint32_t *__restrict__ pt_ptr,
+                    uint32_t *__restrict__ status) {
+  __shared__ uint64_t part[1024];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t per = (k + 1023u) / 1024u;
+  const uint32_t r0 = tid * per < k ? tid * per : k;
+  const uint32_t r1 = r0 + per < k ? r0 + per : k;
+  auto chunks = [&](uint32_t r) -> uint32_t {
+    const uint32_t p0 = t1_ptr[r], p1 = t1_ptr[r + 1];
+    if (p1 > t1_nnz || p0 > p1) return 0xffffffffu;
+    return (p1 - p0 + kWave - 1) / kWave;
+  };
+  uint64_t sum = 0;
+  uint32_t bad = 0;
+  for (uint32_t r = r0; r < r1; ++r) {
+    const uint32_t c = chunks(r);
+    if (c == 0xffffffffu) bad = 1; else sum += c;
+  }
+  part[tid] = sum;
+  __syncthreads();
+  // inclusive scan of the 1024 partial sums (in 64 bits: malformed row
+  // pointers can make them large; the total is checked below)
+  for (uint32_t off = 1; off < 1024; off <<= 1) {
+    const uint64_t v = tid >= off ? part[tid - off] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const uint64_t total = part[1023];
+  __shared__ uint32_t any_bad;
+  if (tid == 0) any_bad = 0;
+  __syncthreads();
+  if (bad) atomicOr(&any_bad, 1u);
+  __syncthreads();
+  const bool overflow = total > pad_chunks;
+  uint64_t at = part[tid] - sum;
+  for (uint32_t r = r0; r < r1; ++r) {
+    uint32_t c = chunks(r);
+    if (c == 0xffffffffu) c = 0;
+    pt_ptr[r] = overflow ? 0u : (uint32_t)at << 1;
+    at += c;
+  }
+  if (tid == 1023) pt_ptr[k] = overflow ? 0u : (uint32_t)total << 1;
+  if (tid == 0 && (any_bad || overflow)) atomicOr(status, kFlagBadIndex);
+}
+
+// One wave per row: the row's entries into its chunks, padding after them;
+// a negative value sets the row's low bit.
+__global__ void __launch_bounds__(256)
+    pad_fill_kernel(const uint32_t *__restrict__ t1_ptr, const uint32_t *__restrict__ t1_idx,
+                    const float *__restrict__ t1_val, uint32_t t1_nnz, uint32_t k,
+                    uint32_t *__restrict__ pt_ptr, uint2 *__restrict__ pt_ent,
+                    uint32_t *__restrict__ status) {
+  const uint32_t lane = lane_id();
+  const uint32_t nw = gridDim.x * (blockDim.x / kWave);
+  uint32_t flags = 0;
+  for (uint32_t r = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; r < k; r += nw) {
+    const uint32_t c0 = pt_ptr[r] >> 1, c1 = pt_ptr[r + 1] >> 1;
+    uint32_t p0 = t1_ptr[r], p1 = t1_ptr[r + 1];
+    if (p1 > t1_nnz || p0 > p1) p0 = p1 = 0;
+    // never more entries than the chunks hold (pointers left empty above)
+    const uint32_t len = min(p1 - p0, (c1 - c0) * kWave);
+    bool neg = false;
+    for (uint32_t i = lane; i < (c1 - c0) * kWave; i += kWave) {
+      uint2 e = make_uint2(k * 4u, 0u);
+      if (i < len) {
+        const uint32_t c = t1_idx[p0 + i];
+        const float v = t1_val[p0 + i];
+        if (c < k) {
+          e = make_uint2(c * 4u, __float_as_uint(v));
+          neg |= v < 0.0f;
+        } else {
+          flags |= kFlagBadIndex;
+        }
+      }
+      pt_ent[(size_t)c0 * kWave + i] = e;
+    }
+    if (__ballot(neg) != 0 && lane == 0) atomicOr(&pt_ptr[r], 1u);
+  }
+  if (flags != 0) atomicOr(status, flags);
+}
+
+// ---------------------------------------------------------------------------
 // Support state for large k (one cell per wave64).
 //
 // With non-negative data, g outside supp(t2) is a sum of non-negative
@@ -1542,12 +1615,15 @@ hipError_t launch_variant(const APlan &plan, const DeviceInfo &dev, Csr t1, Csr 
   } else {
     blocks = plan.global_waves / wpb;  // each wave owns workspace slices
   }
-  float *state_ws = reinterpret_cast<float *>(static_cast<char *>(ws) + plan.ws_dense_off);
+  char *w8 = static_cast<char *>(ws);
+  float *state_ws = reinterpret_cast<float *>(w8 + plan.ws_dense_off);
   if constexpr (G == kWave) {
     auto kern = prune ? &fw_a_wave_kernel<kHInLds, kRegAtoms, true>
                       : &fw_a_wave_kernel<kHInLds, kRegAtoms, false>;
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr, t1.idx,
-                       t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
+    const uint32_t *pt_ptr = reinterpret_cast<const uint32_t *>(w8 + plan.ws_pt_ptr_off);
+    const uint2 *pt_ent = reinterpret_cast<const uint2 *>(w8 + plan.ws_pt_ent_off);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, pt_ptr, pt_ent,
+                       k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
                        ap.val, ap.nnz, n, k, plan.kpad, T, cap, gamma, atom_idx, atom_val,
                        atom_cnt, trace, fw_gap, state_ws, plan.sched_words,
                        plan.lds_per_wave / 4, dense_only, cell_list, cell_count, prune_thr,
@@ -1627,7 +1703,7 @@ uint32_t group_width(uint32_t k) {
 
 }  // namespace
 
-APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap, bool prune) {
+APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap, bool prune, uint32_t t1_nnz) {
   APlan p{};
   p.prune = prune;
   p.group = prune ? kWave : group_width(k);  // pruning runs one cell per wave
@@ -1672,16 +1748,26 @@ APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap, bool prune) {
     uint32_t hc, lpw;
     if (support_tier_size(p, kSupWavesPerBlock, hc, lpw)) p.support = true;
   }
-  // workspace: [counters | long-row queue | dense queue | dense state slices]
+  // workspace: [counters | long-row queue | dense queue | padded t1 | dense state slices]
+  size_t off = 0;
   if (p.support) {
     p.ws_list_off = 256;
     p.ws_list2_off = align_up(p.ws_list_off + (size_t)n * 4, 256);
-    p.ws_dense_off = align_up(p.ws_list2_off + (size_t)n * 4, 256);
+    off = p.ws_list2_off + (size_t)n * 4;
   } else {
     p.ws_list_off = p.ws_list2_off = 0;
-    p.ws_dense_off = 0;
   }
-  p.ws_bytes = dense_ws > 0 || p.support ? align_up(p.ws_dense_off + dense_ws, 256) : 0;
+  // the one-cell-per-wave kernel reads t1 from a padded copy: a row of len
+  // entries takes ceil(len / 64) chunks, at most nnz / 64 + k in all
+  p.padded = p.group == kWave;
+  if (p.padded) {
+    p.pad_chunks = (uint32_t)(((uint64_t)t1_nnz + kWave - 1) / kWave + k);
+    p.ws_pt_ptr_off = align_up(off, 256);
+    p.ws_pt_ent_off = align_up(p.ws_pt_ptr_off + ((size_t)k + 1) * 4, 256);
+    off = p.ws_pt_ent_off + (size_t)p.pad_chunks * kWave * sizeof(uint2);
+  }
+  p.ws_dense_off = align_up(off, 256);
+  p.ws_bytes = dense_ws > 0 || off > 0 ? align_up(p.ws_dense_off + dense_ws, 256) : 0;
   return p;
 }
 
@@ -1694,6 +1780,20 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
   if (e != hipSuccess) return e;
   const uint32_t dense_only = dense_only_requested() ? 1u : 0u;
   const uint32_t *cell_list = nullptr, *cell_count = nullptr;
+  if (plan.padded) {
+    char *w8 = static_cast<char *>(ws);
+    uint32_t *pt_ptr = reinterpret_cast<uint32_t *>(w8 + plan.ws_pt_ptr_off);
+    uint2 *pt_ent = reinterpret_cast<uint2 *>(w8 + plan.ws_pt_ent_off);
+    hipLaunchKernelGGL(pad_rows_kernel, dim3(1), dim3(1024), 0, stream, t1.ptr, t1.nnz, k,
+                       plan.pad_chunks, pt_ptr, status);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const uint32_t rows_per_block = 256 / kWave;
+    const uint32_t fill_blocks = (k + rows_per_block - 1) / rows_per_block;
+    hipLaunchKernelGGL(pad_fill_kernel, dim3(fill_blocks < 65535u ? fill_blocks : 65535u),
+                       dim3(256), 0, stream, t1.ptr, t1.idx, t1.val, t1.nnz, k, pt_ptr, pt_ent,
+                       status);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   // the support kernel addresses t1 with 32-bit byte offsets
   if (plan.support && t1.nnz < (1u << 30)) {
     char *w8 = static_cast<char *>(ws);

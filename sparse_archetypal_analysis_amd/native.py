@@ -59,7 +59,7 @@ def load():
                             "(or python -m sparse_archetypal_analysis_amd._build)")
     lib = ctypes.CDLL(path)
     lib.seacells_fw_a_columns_workspace.restype = ctypes.c_size_t
-    lib.seacells_fw_a_columns_workspace.argtypes = [_U32, _U32, _U32, _U32]
+    lib.seacells_fw_a_columns_workspace.argtypes = [_U32, _U32, _U32, _U32, _U32]
     lib.seacells_fw_a_columns.restype = ctypes.c_int
     lib.seacells_fw_a_columns.argtypes = [_CSR_P, _CSR_P, _CSR_P, _U32, _U32, _U32, _U32, _VP, _VP,
                                           _VP, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP]
@@ -158,8 +158,8 @@ def raise_on_status(status: torch.Tensor):
 # entry points
 # --------------------------------------------------------------------------
 
-def seacells_fw_a_columns_workspace(n, k, T, cap) -> int:
-    return int(load().seacells_fw_a_columns_workspace(n, k, T, cap))
+def seacells_fw_a_columns_workspace(n, k, T, cap, t1_nnz) -> int:
+    return int(load().seacells_fw_a_columns_workspace(n, k, T, cap, t1_nnz))
 
 
 def seacells_fw_a_columns(t1: DeviceCSR, k2b: DeviceCSR, a_prev_t: DeviceCSR, n: int, k: int,
@@ -202,7 +202,7 @@ def _a_columns(threshold, t1, k2b, a_prev_t, n, k, T, cap, gamma, atom_idx, atom
         trace = None
     if status is None:
         status = new_status(dev)
-    ws_bytes = seacells_fw_a_columns_workspace(n, k, T, cap)
+    ws_bytes = seacells_fw_a_columns_workspace(n, k, T, cap, t1.nnz)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     s1, s2, s3 = t1.struct(), k2b.struct(), a_prev_t.struct()

@@ -68,17 +68,24 @@ def test_a_columns_rejects_bad_arguments_on_host():
 
 
 def test_a_columns_workspace_sizes():
-    # dense state in LDS: no workspace
-    assert saa.seacells_fw_a_columns_workspace(1000, 1300, 50, 60) == 0
-    # support state (large k): a counter and the queue of cells left to the dense kernel
-    sup = saa.seacells_fw_a_columns_workspace(1000, 10000, 50, 66)
-    assert sup >= 256 + 1000 * 4 and sup % 256 == 0
+    # one cell per wave (always for the pruning variant, which the size also
+    # covers): the padded copy of t1, at most 8 (nnz + 64 k) bytes
+    for k, nnz in ((1000, 80_000), (1300, 108_000)):
+        pad = saa.seacells_fw_a_columns_workspace(1000, k, 50, 60, nnz)
+        assert 8 * (nnz + k) <= pad <= 8 * (nnz + 64 * k) + 4 * (k + 1) + 1024
+    # support state (large k): counters, the queues of cells, and the copy
+    sup = saa.seacells_fw_a_columns_workspace(1000, 10000, 50, 66, 10)
+    assert sup >= 256 + 2 * 1000 * 4 + 8 * 10000 and sup % 256 == 0
     # k too large for either state in LDS: dense state slices in the workspace
-    big = saa.seacells_fw_a_columns_workspace(1000, 60000, 50, 66)
+    big = saa.seacells_fw_a_columns_workspace(1000, 60000, 50, 66, 10)
     assert big >= 1000 * 60000 * 4 and big % 256 == 0
-    # a large-k call without that workspace is refused on the host
+    # a call without the workspace is refused on the host
     n, k, T, cap = 1000, 60000, 50, 66
     assert call_a(csr(k, k, 3), csr(n, k, 5), csr(n, k, 5), n, k, T, cap) == -3
+    assert call_a(csr(1300, 1300, 3), csr(n, 1300, 5), csr(n, 1300, 5), n, 1300, T, cap) == -3
+    # k from 2^30 on is refused
+    k = 2 ** 30
+    assert call_a(csr(k, k, 3), csr(n, k, 5), csr(n, k, 5), n, k, T, cap) == -4
 
 
 def test_b_argmin_rejects_bad_arguments_on_host():

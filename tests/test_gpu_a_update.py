@@ -89,7 +89,7 @@ def test_large_k_state_in_workspace(support, monkeypatch):
     if support == "0":
         monkeypatch.setenv("SEACELLS_A_SUPPORT", "0")
     w = W.random_workload(37, 45_000, t1_per_row=6, k2b_per_row=20, s_a=5, seed=7, T=30)
-    assert saa.seacells_fw_a_columns_workspace(w.n, w.k, 30, w.cap) > 0
+    assert saa.seacells_fw_a_columns_workspace(w.n, w.k, 30, w.cap, w.t1.nnz) > 0
     ai, av, ac, tr, flags = run_a(w, T=30)
     assert flags == []
     parity.check_a(w, tr, ai, av, ac, np.arange(w.n), T=30)
@@ -265,5 +265,5 @@ def test_support_state_equals_dense_kernel(name, monkeypatch):
 def test_support_state_is_the_default_for_large_k():
     import sparse_archetypal_analysis_amd as saa
     # the workspace then carries the queue of cells left to the dense kernel
-    assert saa.seacells_fw_a_columns_workspace(1000, 6700, 50, 62) >= 1000 * 4
-    assert saa.seacells_fw_a_columns_workspace(1000, 1300, 50, 60) == 0
+    big = saa.seacells_fw_a_columns_workspace(1000, 6700, 50, 62, 10)
+    assert big >= 2 * 1000 * 4 + saa.seacells_fw_a_columns_workspace(1000, 1000, 50, 60, 10)
