@@ -269,12 +269,24 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
   // h += alpha * (row r of t1), from the padded copy: whole chunks of 64
   // (column byte offset, value) pairs, padding entries pointing at the +inf
   // column with value 0. Columns of one row are unique, so no two lanes
-  // touch the same column. Returns whether the row holds a negative value.
+  // touch the same column; two chunks are in flight together (their reads
+  // before their writes: distinct columns, or the +inf column, which stays
+  // +inf). Returns whether the row holds a negative value.
   char *hb = reinterpret_cast<char *>(h);
   auto scatter_row = [&](uint32_t r, float alpha) -> bool {
     const uint32_t e0 = pt_ptr[r], e1 = pt_ptr[r + 1];
     const uint32_t c0 = e0 >> 1, c1 = e1 >> 1;
-    for (uint32_t ch = c0; ch < c1; ++ch) {
+    uint32_t ch = c0;
+    for (; ch + 1 < c1; ch += 2) {
+      const uint2 ea = load_at(pt_ent + (size_t)ch * kWave, lane * 8u);
+      const uint2 eb = load_at(pt_ent + (size_t)(ch + 1) * kWave, lane * 8u);
+      float *pa = reinterpret_cast<float *>(hb + ea.x);
+      float *pb = reinterpret_cast<float *>(hb + eb.x);
+      const float ha = *pa, hv = *pb;
+      *pa = __builtin_fmaf(alpha, __uint_as_float(ea.y), ha);
+      *pb = __builtin_fmaf(alpha, __uint_as_float(eb.y), hv);
+    }
+    if (ch < c1) {
       const uint2 e = load_at(pt_ent + (size_t)ch * kWave, lane * 8u);
       float *hp = reinterpret_cast<float *>(hb + e.x);
       *hp = __builtin_fmaf(alpha, __uint_as_float(e.y), *hp);
