@@ -194,7 +194,8 @@ def main():
     out_val = torch.empty(k, dtype=torch.float32, device=dev)
     out_idx = torch.empty(k, dtype=torch.int32, device=dev)
     gap = torch.empty(1, dtype=torch.float32, device=dev)
-    ws_b = torch.empty(saa.seacells_fw_b_argmin_workspace(n, k), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(saa.seacells_fw_b_argmin_workspace(n, k, w.aat.nnz), dtype=torch.uint8,
+                       device=dev)
     st_a, st_b, st_p = saa.new_status(dev), saa.new_status(dev), saa.new_status(dev)
     stream = torch.cuda.current_stream()
 

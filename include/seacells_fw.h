@@ -170,10 +170,13 @@ int seacells_fw_a_columns_pruned(const seacells_csr *t1, const seacells_csr *k2b
                                  seacells_stream_t stream);
 
 /*
- * Workspace bytes seacells_fw_b_argmin needs for these sizes (always > 0).
- * Depends only on its arguments.
+ * Workspace bytes seacells_fw_b_argmin needs for these sizes (always > 0;
+ * aat_nnz: the non-zeros of A A^T). It holds the per-row-range partials
+ * (8 bytes per column each), and, when k fits one column slice (k <= 2048),
+ * a copy of A A^T with every row padded to whole chunks of 64 entries (at
+ * most 8 * (aat_nnz + 64 k) bytes). Depends only on its arguments.
  */
-size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k);
+size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k, uint32_t aat_nnz);
 
 /*
  * B-gradient argmin: `fw_argmin_b` followed by `reduce_argmin_blocks` on

@@ -130,9 +130,9 @@ int seacells_fw_a_columns_pruned(const seacells_csr *t1, const seacells_csr *k2b
                    atom_cnt, trace, fw_gap, workspace, workspace_bytes, status, stream);
 }
 
-size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k) {
+size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k, uint32_t aat_nnz) {
   if (n == 0 || k == 0) return 0;
-  return b_workspace_bound(n, k);
+  return plan_b(n, k, aat_nnz).ws_bytes;
 }
 
 int seacells_fw_b_argmin(const seacells_csr *k2b, const seacells_csr *aat,

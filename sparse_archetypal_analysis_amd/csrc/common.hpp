@@ -155,10 +155,18 @@ struct BPlan {
   uint32_t n_slices;
   uint32_t n_row_blocks;  // row ranges; one work unit = (row range, slice)
   uint32_t n_chunks;      // row-range groups of the first reduce stage
-  size_t off_keys, off_part2, off_gap, off_stamp, off_work, off_seg, ws_bytes;
+  // narrow slices: the two half-waves gather different K2B entries (runs
+  // of AAt from the segment table); otherwise one wave per entry reads AAt
+  // copied per slice, the run of row m inside slice s padded to whole
+  // chunks of pa_ch (accumulator byte offset, value) pairs (chunk 0 is all
+  // padding): pa_seg[s * k + m] = first chunk of that run (slice-major).
+  bool dual;
+  uint32_t pa_ch;         // entries per chunk (64), 0 without the copy
+  uint64_t pa_chunks;     // bound on the chunks of all runs, chunk 0 included
+  size_t off_keys, off_part2, off_gap, off_stamp, off_work, off_seg, off_pa_seg, off_pa_ent;
+  size_t ws_bytes;
 };
 BPlan plan_b(uint32_t n, uint32_t k, uint64_t aat_nnz);
-size_t b_workspace_bound(uint32_t n, uint32_t k);  // over every aat_nnz
 hipError_t launch_fw_b(const BPlan &plan, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
                        uint32_t k, float *out_val, uint32_t *out_idx, float *gap,
                        float *fw_gap, void *ws, uint32_t *status, uint32_t epoch,

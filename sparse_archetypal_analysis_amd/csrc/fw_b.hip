@@ -6,9 +6,12 @@
 //
 // Work unit = (row range, column slice). A wave owns one unit at a time:
 // per row it scatters the AAt rows named by the row's K2B entries into a
-// dense slice accumulator in LDS (coalesced lane-strided reads of each AAt
-// row segment, four runs in flight at a time; the columns of one row are
-// unique, so one scatter instruction never collides), subtracts the K2At
+// dense slice accumulator in LDS (four runs in flight at a time; the
+// columns of one row are unique, so one scatter instruction never
+// collides). With one slice the runs come from a copy of AAt padded to
+// whole 64-entry chunks of (accumulator offset, value), so the gather does
+// no bounds or column arithmetic; narrow slices gather two short runs per
+// instruction (one per half-wave) straight from AAt. It then subtracts the K2At
 // row, adds the row's B . G term, then folds the slice into running
 // (min, row) pairs held in registers, 4 consecutive columns per float4
 // chunk, and clears the slice.
@@ -97,6 +100,114 @@ __global__ void __launch_bounds__(256)
   seg[e] = lo;
 }
 
+// ---------------------------------------------------------------------------
+// Padded copy of AAt per slice. The run of AAt row m inside slice s (all of
+// the row with one slice) takes ceil(len / ch) chunks of ch entries
+// (byte offset of the column in the slice accumulator, value); positions
+// past the run point at the dummy slot of the lane that reads them (W +
+// position % ch) with value 0, so a gather needs no bounds test and no
+// column arithmetic. Chunk 0 is padding only: empty runs read it.
+// pa_seg[s * k + m] = first chunk of the run; pa_seg[n_slices * k] = end.
+
+__device__ __forceinline__ uint32_t run_of(const Csr &aat, const uint32_t *seg, uint32_t k,
+                                           uint32_t s, uint32_t m, uint32_t &lo, bool &bad) {
+  uint32_t hi;
+  bad = false;
+  if (seg != nullptr) {
+    lo = seg[(size_t)s * k + m];
+    hi = seg[(size_t)(s + 1) * k + m];
+    if (hi < lo) hi = lo;
+  } else {
+    bad = !row_ok(aat, m, lo, hi);
+  }
+  return hi - lo;
+}
+
+// One block: chunk counts of every run and their exclusive prefix sum
+// (64-bit, checked against the bound the workspace was sized for; past it
+// every run is left empty and BAD_INDEX is raised).
+__global__ void __launch_bounds__(1024)
+    pa_seg_kernel(Csr aat, const uint32_t *__restrict__ seg, uint32_t k, uint32_t n_slices,
+                  uint32_t ch, uint64_t pa_chunks, uint32_t *__restrict__ pa_seg,
+                  uint32_t *__restrict__ status) {
+  __shared__ uint64_t part[1024];
+  const uint32_t tid = threadIdx.x;
+  const uint64_t total_runs = (uint64_t)k * n_slices;
+  const uint64_t per = (total_runs + 1023) / 1024;
+  const uint64_t e0 = (uint64_t)tid * per < total_runs ? (uint64_t)tid * per : total_runs;
+  const uint64_t e1 = e0 + per < total_runs ? e0 + per : total_runs;
+  uint64_t sum = 0;
+  uint32_t bad_any = 0;
+  for (uint64_t e = e0; e < e1; ++e) {
+    const uint32_t s = (uint32_t)(e / k), m = (uint32_t)(e - (uint64_t)s * k);
+    uint32_t lo;
+    bool bad;
+    const uint32_t len = run_of(aat, seg, k, s, m, lo, bad);
+    bad_any |= bad;
+    sum += (len + ch - 1) / ch;
+  }
+  part[tid] = sum;
+  __syncthreads();
+  for (uint32_t off = 1; off < 1024; off <<= 1) {
+    const uint64_t v = tid >= off ? part[tid - off] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const uint64_t total = part[1023] + 1;  // + the padding chunk 0
+  const bool overflow = total > pa_chunks;
+  uint64_t at = 1 + part[tid] - sum;
+  for (uint64_t e = e0; e < e1; ++e) {
+    const uint32_t s = (uint32_t)(e / k), m = (uint32_t)(e - (uint64_t)s * k);
+    uint32_t lo;
+    bool bad;
+    const uint32_t len = run_of(aat, seg, k, s, m, lo, bad);
+    pa_seg[e] = overflow ? 1u : (uint32_t)at;
+    at += (len + ch - 1) / ch;
+  }
+  if (tid == 1023) pa_seg[total_runs] = overflow ? 1u : (uint32_t)total;
+  if (bad_any) atomicOr(status, kFlagBadIndex);
+  if (tid == 0 && overflow) atomicOr(status, kFlagBadIndex);
+}
+
+// One wave per run: its entries, then padding; chunk 0 as padding.
+__global__ void __launch_bounds__(256)
+    pa_fill_kernel(Csr aat, const uint32_t *__restrict__ seg, uint32_t k, uint32_t n_slices,
+                   uint32_t slice_w, uint32_t ch, uint32_t w_acc,
+                   const uint32_t *__restrict__ pa_seg, uint2 *__restrict__ pa_ent,
+                   uint32_t *__restrict__ status) {
+  const uint32_t lane = lane_id();
+  const uint64_t nw = (uint64_t)gridDim.x * (blockDim.x / kWave);
+  const uint64_t total_runs = (uint64_t)k * n_slices;
+  const uint64_t first = (uint64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (first == 0)
+    for (uint32_t i = lane; i < ch; i += kWave) pa_ent[i] = make_uint2((w_acc + i) * 4u, 0u);
+  uint32_t flags = 0;
+  for (uint64_t e = first; e < total_runs; e += nw) {
+    const uint32_t s = (uint32_t)(e / k), m = (uint32_t)(e - (uint64_t)s * k);
+    const uint32_t c0 = s * slice_w;
+    const uint32_t cw = (k - c0) < slice_w ? (k - c0) : slice_w;
+    const uint32_t q0 = pa_seg[e], q1 = pa_seg[e + 1];
+    uint32_t lo;
+    bool bad;
+    uint32_t len = run_of(aat, seg, k, s, m, lo, bad);
+    const uint64_t room = (uint64_t)(q1 - q0) * ch;  // 0 when the runs were left empty
+    if (len > room) len = (uint32_t)room;
+    for (uint32_t i = lane; i < room; i += kWave) {
+      uint2 v = make_uint2((w_acc + i % ch) * 4u, 0u);
+      if (i < len) {
+        const uint32_t c = aat.idx[lo + i] - c0;
+        if (c < cw)
+          v = make_uint2(c * 4u, __float_as_uint(aat.val[lo + i]));
+        else
+          flags |= kFlagBadIndex;
+      }
+      pa_ent[(size_t)q0 * ch + i] = v;
+    }
+  }
+  if (flags != 0) atomicOr(status, flags);
+}
+
 // kDual: the two half-waves gather different K2B entries into two
 // accumulators (for the short AAt runs of narrow slices); each column then
 // sums the even-numbered entries of the row in one accumulator and the odd
@@ -105,7 +216,8 @@ template <uint32_t S4, bool kDual>
 __global__ void __launch_bounds__(kBThreads)
     fw_b_partials_kernel(Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n, uint32_t k,
                          uint32_t slice_w, uint32_t n_slices, uint32_t n_row_blocks,
-                         const uint32_t *__restrict__ seg, uint64_t *__restrict__ part_key,
+                         const uint32_t *__restrict__ seg, const uint32_t *__restrict__ pa_seg,
+                         const uint2 *__restrict__ pa_ent, uint64_t *__restrict__ part_key,
                          float *__restrict__ part_gap, uint32_t *__restrict__ stamps,
                          uint32_t *__restrict__ xcd_work, uint32_t epoch,
                          uint32_t *__restrict__ status) {
@@ -120,7 +232,7 @@ __global__ void __launch_bounds__(kBThreads)
   // half (so the second one also starts 32 floats off the bank pattern of
   // the first), then the staged entry triples
   constexpr uint32_t ACC2 = W + kAccPad;
-  constexpr uint32_t WAVE_FLOATS = kDual ? 2 * ACC2 + kStageSlots * 4 : W;
+  constexpr uint32_t WAVE_FLOATS = kDual ? 2 * ACC2 + kStageSlots * 4 : W + kWave;
   float *acc = lds_acc + (size_t)wib * WAVE_FLOATS;
   uint4 *stage = reinterpret_cast<uint4 *>(acc + 2 * ACC2);
   const uint32_t half = kDual ? (lane >> 5) : 0u;
@@ -154,6 +266,8 @@ __global__ void __launch_bounds__(kBThreads)
   if constexpr (kDual) {
     if (lane < kAccPad) acc[W + lane] = 0.0f, acc[ACC2 + W + lane] = 0.0f;
     if (lane < kStageSlots - kWave) stage[kWave + lane] = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    acc[W + lane] = 0.0f;  // the dummy slots padding entries add 0 to
   }
   wave_lds_sync();
 
@@ -189,24 +303,29 @@ __global__ void __launch_bounds__(kBThreads)
       // -- acc[c] = sum_m K2B[i, m] AAt[m, c] over this slice
       uint32_t e0, e1;
       if (!row_ok(k2b, i, e0, e1)) flags |= kFlagBadIndex;
+      const uint32_t *pseg = kDual ? nullptr : pa_seg + (size_t)sl * k;
       for (uint32_t eb = e0; eb < e1; eb += kWave) {
         const uint32_t e = eb + lane;
-        uint32_t lo = 0, hi = 0;
+        // this entry's run of AAt: [lo, hi) in AAt (two half-wave
+        // accumulators), or first chunk q0 and chunks nq of the padded copy
+        uint32_t lo = 0, hi = 0, q0 = 0, nq = 0;
         float x = 0.0f;
         if (e < e1) {
           const uint32_t m = k2b.idx[e];
           x = k2b.val[e];
           if (m < k) {
-            if (seg != nullptr) {
+            if constexpr (kDual) {
               lo = seg[(size_t)sl * k + m];
               hi = seg[(size_t)(sl + 1) * k + m];
-            } else if (!row_ok(aat, m, lo, hi)) {
-              flags |= kFlagBadIndex;
+            } else {
+              q0 = pseg[m];
+              nq = pseg[m + 1] - q0;
             }
           } else {
             flags |= kFlagBadIndex;
           }
         }
+        if (nq == 0) q0 = 0;  // empty: the padding chunk (adds 0 to dummy slots)
         const uint32_t cnt = (e1 - eb) < kWave ? (e1 - eb) : kWave;
         if constexpr (kDual) {
           // entries u + 2g (lanes 0-31) and u + 2g + 1 (lanes 32-63): runs of
@@ -249,33 +368,30 @@ __global__ void __launch_bounds__(kBThreads)
           wave_lds_sync();
           continue;
         }
-        // kGatherRows AAt runs in flight at a time (their first two chunks);
-        // the adds still go row after row, so every column sums its terms in
-        // K2B order and the result does not depend on the timing
+        // kGatherRows runs in flight at a time (their first chunks); the adds
+        // still go entry after entry, so every column sums its terms in K2B
+        // order and the result does not depend on the timing
         for (uint32_t u = 0; u < cnt; u += kGatherRows) {
-          uint32_t plo[kGatherRows], phi[kGatherRows];
-          float xs[kGatherRows], va[kGatherRows], vb[kGatherRows];
-          uint32_t ca[kGatherRows], cb[kGatherRows];
+          uint32_t gq[kGatherRows], gn[kGatherRows];
+          float xs[kGatherRows];
+          uint2 ea[kGatherRows];
 #pragma unroll
           for (uint32_t g = 0; g < kGatherRows; ++g) {
             const uint32_t src = (u + g) < kWave ? (u + g) : (kWave - 1);
             const bool on = (u + g) < cnt;
-            plo[g] = on ? readlane_u32(lo, src) : 0u;
-            phi[g] = on ? readlane_u32(hi, src) : 0u;
+            gq[g] = on ? readlane_u32(q0, src) : 0u;
+            gn[g] = on ? readlane_u32(nq, src) : 0u;
             xs[g] = readlane_f32(x, src);
-            const uint32_t pa = plo[g] + lane, pb = pa + kWave;
-            ca[g] = kNoCol, va[g] = 0.0f, cb[g] = kNoCol, vb[g] = 0.0f;
-            if (pa < phi[g]) ca[g] = aat.idx[pa], va[g] = aat.val[pa];
-            if (pb < phi[g]) cb[g] = aat.idx[pb], vb[g] = aat.val[pb];
+            ea[g] = load_at(pa_ent + (size_t)gq[g] * kWave, lane * 8u);
           }
 #pragma unroll
           for (uint32_t g = 0; g < kGatherRows; ++g) {
-            const uint32_t c_a = ca[g] - c0, c_b = cb[g] - c0;
-            if (c_a < cw) lds_add(acc + c_a, xs[g] * va[g]);
-            if (c_b < cw) lds_add(acc + c_b, xs[g] * vb[g]);
-            for (uint32_t p = plo[g] + 2 * kWave + lane; p < phi[g]; p += kWave) {
-              const uint32_t c = aat.idx[p] - c0;
-              if (c < cw) lds_add(acc + c, xs[g] * aat.val[p]);
+            float *q = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + ea[g].x);
+            *q = __builtin_fmaf(xs[g], __uint_as_float(ea[g].y), *q);
+            for (uint32_t j = 1; j < gn[g]; ++j) {
+              const uint2 eg = load_at(pa_ent + (size_t)(gq[g] + j) * kWave, lane * 8u);
+              float *qj = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + eg.x);
+              *qj = __builtin_fmaf(xs[g], __uint_as_float(eg.y), *qj);
             }
           }
         }
@@ -485,14 +601,15 @@ __global__ void zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
 
 template <uint32_t S4, bool kDual>
 hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
-                           uint32_t k, const uint32_t *seg, uint64_t *keys, float *gap_part,
-                           uint32_t *stamps, uint32_t *xcd_work, uint32_t epoch,
+                           uint32_t k, const uint32_t *seg, const uint32_t *pa_seg,
+                           const uint2 *pa_ent, uint64_t *keys,
+                           float *gap_part, uint32_t *stamps, uint32_t *xcd_work, uint32_t epoch,
                            uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
   const uint32_t lds = (kBThreads / kWave) *
-                       (kDual ? 2 * (256 * S4 + kAccPad) + kStageSlots * 4 : 256 * S4) *
+                       (kDual ? 2 * (256 * S4 + kAccPad) + kStageSlots * 4 : 256 * S4 + kWave) *
                        sizeof(float);
   static int bpc = -1;
   if (bpc < 0) {
@@ -510,7 +627,7 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
   auto kern = &fw_b_partials_kernel<S4, kDual>;
   hipLaunchKernelGGL(kern, dim3((uint32_t)blocks), dim3(kBThreads), lds,
                      stream, k2b, aat, k2at, b, n, k, p.slice_w, p.n_slices, p.n_row_blocks, seg,
-                     keys, gap_part, stamps, xcd_work, epoch, status);
+                     pa_seg, pa_ent, keys, gap_part, stamps, xcd_work, epoch, status);
   return hipGetLastError();
 }
 
@@ -533,7 +650,7 @@ static uint32_t slices_for(uint32_t k, uint64_t aat_nnz) {
   return (uint32_t)(s < most ? s : most);
 }
 
-static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices) {
+static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices, uint64_t aat_nnz) {
   BPlan p{};
   p.n_slices = n_slices;
   p.slice_w = (uint32_t)align_up((k + n_slices - 1) / n_slices, 4);
@@ -557,19 +674,23 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices) {
   off = align_up(off + kXcds * sizeof(uint32_t), 256);
   p.off_seg = off;
   if (p.n_slices > 1) off = align_up(off + (size_t)k * (p.n_slices + 1) * sizeof(uint32_t), 256);
+  // narrow slices gather two short AAt runs per wave instruction, reading
+  // AAt with 32-bit byte offsets; otherwise the padded AAt copy: a run of
+  // len entries takes ceil(len / 64) chunks, at most nnz / 64 + 1 per (row,
+  // slice) in all, plus chunk 0
+  p.dual = p.n_slices > 1 && aat_nnz < (1ull << 30);
+  p.pa_ch = p.dual ? 0u : kWave;
+  p.pa_chunks = p.dual ? 0u : (aat_nnz + kWave - 1) / kWave + (uint64_t)k * p.n_slices + 1;
+  p.off_pa_seg = off;
+  if (!p.dual) off = align_up(off + ((size_t)k * p.n_slices + 1) * sizeof(uint32_t), 256);
+  p.off_pa_ent = off;
+  off = align_up(off + (size_t)p.pa_chunks * p.pa_ch * sizeof(uint2), 256);
   p.ws_bytes = off;
   return p;
 }
 
 BPlan plan_b(uint32_t n, uint32_t k, uint64_t aat_nnz) {
-  return plan_with_slices(n, k, slices_for(k, aat_nnz));
-}
-
-size_t b_workspace_bound(uint32_t n, uint32_t k) {
-  // AAt has at most k * k entries: the most slices any call can take
-  const size_t most = plan_b(n, k, (uint64_t)k * k).ws_bytes;
-  const size_t fewest = plan_b(n, k, 0).ws_bytes;
-  return most > fewest ? most : fewest;
+  return plan_with_slices(n, k, slices_for(k, aat_nnz), aat_nnz);
 }
 
 hipError_t launch_status_clear(uint32_t *status, hipStream_t stream) {
@@ -587,6 +708,8 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
   float *gap_part = reinterpret_cast<float *>(base + p.off_gap);
   uint32_t *stamps = reinterpret_cast<uint32_t *>(base + p.off_stamp);
   uint32_t *seg = p.n_slices > 1 ? reinterpret_cast<uint32_t *>(base + p.off_seg) : nullptr;
+  uint32_t *pa_seg = reinterpret_cast<uint32_t *>(base + p.off_pa_seg);
+  uint2 *pa_ent = reinterpret_cast<uint2 *>(base + p.off_pa_ent);
   uint32_t *xcd_work = reinterpret_cast<uint32_t *>(base + p.off_work);
   hipError_t e;
   if (seg != nullptr) {
@@ -595,18 +718,29 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
                        stream, aat, k, p.slice_w, p.n_slices, seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // narrow slices give short AAt runs: gather two per wave instruction
-  // (that path addresses AAt with 32-bit byte offsets)
-  const bool dual = p.n_slices > 1 && aat.nnz < (1u << 30);
+  // the padded AAt copy (unless narrow slices gather two runs per wave
+  // instruction from AAt itself), then the partials
+  const bool dual = p.dual;
+  if (!dual) {
+    hipLaunchKernelGGL(pa_seg_kernel, dim3(1), dim3(1024), 0, stream, aat, seg, k, p.n_slices,
+                       p.pa_ch, p.pa_chunks, pa_seg, status);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const uint64_t runs = (uint64_t)k * p.n_slices;
+    const uint64_t blocks = (runs + 3) / 4;  // 4 waves per block, one run each
+    hipLaunchKernelGGL(pa_fill_kernel, dim3((uint32_t)(blocks < 65535u ? blocks : 65535u)),
+                       dim3(256), 0, stream, aat, seg, k, p.n_slices, p.slice_w, p.pa_ch,
+                       256u * p.s4, pa_seg, pa_ent, status);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, xcd_work, kXcds);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   switch (p.s4) {
 #define SEACELLS_B_CASE(S)                                                                      \
   case S:                                                                                       \
-    e = dual ? launch_partials<S, true>(p, k2b, aat, k2at, b, n, k, seg, keys, gap_part, stamps, \
-                                        xcd_work, epoch, status, stream)                        \
-             : launch_partials<S, false>(p, k2b, aat, k2at, b, n, k, seg, keys, gap_part,       \
-                                         stamps, xcd_work, epoch, status, stream);              \
+    e = dual ? launch_partials<S, true>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent, keys,  \
+                                        gap_part, stamps, xcd_work, epoch, status, stream)      \
+             : launch_partials<S, false>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent, keys, \
+                                         gap_part, stamps, xcd_work, epoch, status, stream);    \
     break;
     SEACELLS_B_CASE(1)
     SEACELLS_B_CASE(2)

@@ -68,7 +68,7 @@ def load():
                                                  _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP,
                                                  _VP, ctypes.c_size_t, _VP, _VP]
     lib.seacells_fw_b_argmin_workspace.restype = ctypes.c_size_t
-    lib.seacells_fw_b_argmin_workspace.argtypes = [_U32, _U32]
+    lib.seacells_fw_b_argmin_workspace.argtypes = [_U32, _U32, _U32]
     lib.seacells_fw_b_argmin.restype = ctypes.c_int
     lib.seacells_fw_b_argmin.argtypes = [_CSR_P, _CSR_P, _CSR_P, _CSR_P, _U32, _U32, _VP, _VP, _VP,
                                          _VP, _VP, ctypes.c_size_t, _VP, _VP]
@@ -222,8 +222,8 @@ def _a_columns(threshold, t1, k2b, a_prev_t, n, k, T, cap, gamma, atom_idx, atom
     return atom_idx, atom_val, atom_cnt, trace, status
 
 
-def seacells_fw_b_argmin_workspace(n, k) -> int:
-    return int(load().seacells_fw_b_argmin_workspace(n, k))
+def seacells_fw_b_argmin_workspace(n, k, aat_nnz) -> int:
+    return int(load().seacells_fw_b_argmin_workspace(n, k, aat_nnz))
 
 
 def seacells_fw_b_argmin(k2b: DeviceCSR, aat: DeviceCSR, k2at: DeviceCSR, b, n: int, k: int,
@@ -244,7 +244,7 @@ def seacells_fw_b_argmin(k2b: DeviceCSR, aat: DeviceCSR, k2at: DeviceCSR, b, n: 
         gap = torch.empty(1, dtype=torch.float32, device=dev)
     if status is None:
         status = new_status(dev)
-    ws_bytes = seacells_fw_b_argmin_workspace(n, k)
+    ws_bytes = seacells_fw_b_argmin_workspace(n, k, aat.nnz)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     s1, s2, s3 = k2b.struct(), aat.struct(), k2at.struct()

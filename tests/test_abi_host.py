@@ -92,7 +92,7 @@ def test_b_argmin_rejects_bad_arguments_on_host():
     lib = saa.load()
     n, k = 100, 30
     k2b, aat, k2at, b = csr(n, k, 5), csr(k, k, 5), csr(n, k, 5), csr(n, k, 5)
-    ws = saa.seacells_fw_b_argmin_workspace(n, k)
+    ws = saa.seacells_fw_b_argmin_workspace(n, k, 5)
     assert ws > 0 and ws % 256 == 0
 
     def call(k2b=k2b, aat=aat, k2at=k2at, b=b, n=n, k=k, ws_ptr=0x100000, ws_bytes=ws,
@@ -114,9 +114,11 @@ def test_b_argmin_rejects_bad_arguments_on_host():
 
 
 def test_b_workspace_grows_with_slices():
-    one = saa.seacells_fw_b_argmin_workspace(100_000, 1300)
-    many = saa.seacells_fw_b_argmin_workspace(100_000, 10_000)
+    one = saa.seacells_fw_b_argmin_workspace(100_000, 1300, 143_000)
+    many = saa.seacells_fw_b_argmin_workspace(100_000, 10_000, 6_500_000)
     assert one > 0 and many > one
+    # one slice: the padded copy of A A^T, at least 8 bytes per entry
+    assert one - saa.seacells_fw_b_argmin_workspace(100_000, 1300, 0) >= 8 * 143_000
 
 
 def test_b_apply_rejects_bad_arguments_on_host():
