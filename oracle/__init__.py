@@ -3,18 +3,20 @@
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package. The HIP library
 never calls it, and the two share no code: this package is C compiled with
-gcc (``seacells_oracle.c``) plus dense numpy (``dense.py``), both written
+gcc (``seacells_oracle.c``) plus dense numpy (``dense.py``) and scipy sparse
+products (``sparse.py``, the operand construction and the RSS), all written
 from the method as the source page states it (bixverse-rs 0.6.4,
-``seacells_kernels.rs``: the ``fw_columns_a_gpu`` and ``fw_argmin_b`` docs and
-the ``cpu_fw_argmin_b`` test reference).
+``seacells_kernels.rs``: the module doc, the ``fw_columns_a_gpu`` and
+``fw_argmin_b`` docs and the ``cpu_fw_argmin_b`` test reference).
 
 Every function here takes the same f32 CSR operands the GPU receives (as
 numpy arrays or ``scipy.sparse.csr_matrix``) and computes in f64.
 
-Parity pins: every function is pinned in ``tests/test_oracle_pins.py``
-against brute-force objective differences, vertex enumeration, closed forms,
-a worked example with K = I, special cases that reduce to library routines,
-and the independent dense implementation in ``dense.py``.
+Parity pins: every function is pinned in ``tests/test_oracle_pins.py`` (and
+``tests/test_oracle_sparse_pins.py`` for ``sparse.py``) against brute-force
+objective differences, vertex enumeration, closed forms, a worked example
+with K = I, special cases that reduce to library routines, brute-force loops
+on tiny inputs, and the independent dense implementation in ``dense.py``.
 """
 from __future__ import annotations
 

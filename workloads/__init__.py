@@ -94,6 +94,7 @@ class Workload:
     b: sp.csr_matrix           # n x k, f32
     init_cells: np.ndarray     # [k]
     meta: dict = field(default_factory=dict)
+    K: sp.csr_matrix | None = None  # n x n, f32, symmetric (None: not kept, see kernel_matrix)
 
     @property
     def n(self):
@@ -345,7 +346,7 @@ def generate(cfg: Config, seed: int = 0, log=None) -> Workload:
     _progress(log, "K2At and AAt", t0)
     w = Workload(cfg, seed, t1=_f32(t1, symmetric=True), k2b=_f32(K2B), a_prev_t=_f32(At),
                  aat=_f32(AAt, symmetric=True), k2at=_f32(K2At), b=_f32(B),
-                 init_cells=np.asarray(init, np.int64))
+                 init_cells=np.asarray(init, np.int64), K=_f32(K))
     t_end = time.time()
     _progress(log, "f32 operands", t0)
     w.meta = {
@@ -374,7 +375,7 @@ _NAMES = ("t1", "k2b", "a_prev_t", "aat", "k2at", "b")
 
 def _save(w: Workload, path):
     arrs = {"init_cells": w.init_cells}
-    for nm in _NAMES:
+    for nm in _NAMES + (("K",) if w.K is not None else ()):
         m = getattr(w, nm)
         arrs[nm + "_ptr"], arrs[nm + "_idx"], arrs[nm + "_val"] = m.indptr, m.indices, m.data
     os.makedirs(os.path.dirname(path), exist_ok=True)
@@ -392,9 +393,21 @@ def _load(cfg: Config, seed: int, path) -> Workload:
               "b": (n, k)}
     mats = {nm: sp.csr_matrix((z[nm + "_val"], z[nm + "_idx"], z[nm + "_ptr"]), shape=shapes[nm])
             for nm in _NAMES}
+    if "K_ptr" in z.files:
+        mats["K"] = sp.csr_matrix((z["K_val"], z["K_idx"], z["K_ptr"]), shape=(n, n))
     with open(path + ".json") as f:
         meta = json.load(f)
     return Workload(cfg, seed, init_cells=z["init_cells"], meta=meta, **mats)
+
+
+def kernel_matrix(w: Workload) -> sp.csr_matrix:
+    """K of a workload (f32, symmetric), rebuilt from its points when the
+    workload was loaded from a cache written without it."""
+    if w.K is None:
+        rng = np.random.default_rng(1000 * w.cfg.index + w.seed)
+        X, _ = _points(w.cfg, rng)
+        w.K = _f32(_kernel(X, w.cfg.knn))
+    return w.K
 
 
 def make(name_or_cfg, seed: int = 0, cache: bool = True, log=None) -> Workload:
