@@ -1,0 +1,101 @@
+/*
+ * seacells_sparse.h - C ABI of the sparse operations that build the
+ * Frank-Wolfe operands of SEACells on MI355X (gfx950), in the same library
+ * as seacells_fw.h (libseacells_fw.so).
+ *
+ * On the docs.rs source page "bixverse-rs 0.6.4 -
+ * src/gpu/sc_gpu/kernels/seacells_kernels.rs" the operands come from host
+ * routines (the page's module doc: kernel construction and the RSS stay on
+ * the host; its `lower_bound` doc names `csr_matmul_csr`, which sorts each
+ * output row, and `transpose_sparse`, which writes rows in ascending major
+ * order). These entry points do the same work on the device:
+ *
+ *   K^2 X  = K (K X)           two products        (X = B or A^T)
+ *   t1     = B^T (K^2 B)       a transpose, a product
+ *   A A^T  = (A^T)^T A^T       a transpose, a product
+ *   RSS    = ||K - K B A||_F^2 = <K, K> - 2 <K^2 B, A^T> + <t1, A A^T>
+ *            (three inner products, no n x n or dense product formed)
+ *
+ * Conventions (as in seacells_fw.h): CSR operands are seacells_csr with
+ * device pointers, column indices strictly ascending within a row, nnz <
+ * 2^31, finite values. The caller allocates every buffer; the library never
+ * allocates or synchronises and enqueues all work on `stream`. Return values
+ * are SEACELLS_OK or a negative SEACELLS_E_* code found on the host before
+ * anything is enqueued; *status (device) receives the OR of SEACELLS_FLAG_*
+ * conditions the kernels met. Results are deterministic (fixed summation
+ * orders, no floating-point atomics).
+ */
+#ifndef SEACELLS_SPARSE_H
+#define SEACELLS_SPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "seacells_fw.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The product's (or transpose's) output would hold 2^31 or more entries. */
+#define SEACELLS_FLAG_OUTPUT_TOO_LARGE 0x40u
+
+/*
+ * Product C = A B, step 1 of 2 (`csr_matmul_csr` on the page): the row
+ * pointer of C. a is m x p, b is p x q (else SEACELLS_E_SHAPE).
+ * c_row_ptr  device [m + 1] u32 out: c_row_ptr[i] = first entry of row i;
+ *            c_row_ptr[m] = nnz(C), for the caller to size c_col_idx and
+ *            c_val (read it after the stream synchronises). Row i holds every
+ *            column some product a[i, j] b[j, c] reaches, so a sum that cancels
+ *            to 0 stays as an explicit 0 (the page's host product drops it).
+ * SEACELLS_FLAG_OUTPUT_TOO_LARGE when nnz(C) would reach 2^31 (c_row_ptr
+ * is then not valid); BAD_INDEX for malformed rows or columns (skipped).
+ */
+int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint32_t *c_row_ptr,
+                             uint32_t *status, seacells_stream_t stream);
+
+/*
+ * Product C = A B, step 2 of 2: columns (ascending in every row) and values.
+ * c_row_ptr must be the output of seacells_csr_matmul_rows for the same a
+ * and b; c_col_idx and c_val hold c_row_ptr[m] entries each (device, out).
+ * c[i, c] = sum over the entries j of a's row i, in order, and then over
+ * b's row j, of a[i, j] * b[j, c], accumulated in f32 with fused
+ * multiply-adds in that order.
+ */
+int seacells_csr_matmul_fill(const seacells_csr *a, const seacells_csr *b,
+                             const uint32_t *c_row_ptr, uint32_t *c_col_idx, float *c_val,
+                             uint32_t *status, seacells_stream_t stream);
+
+/* Workspace bytes seacells_csr_transpose needs for an m x q matrix (> 0). */
+size_t seacells_csr_transpose_workspace(uint32_t m, uint32_t q);
+
+/*
+ * Transpose (`transpose_sparse` on the page): a is m x q; at (q x m) gets
+ * at_row_ptr [q + 1], at_col_idx and at_val [nnz(a)] (device, out), every
+ * row listing a's rows in ascending order. workspace: at least
+ * seacells_csr_transpose_workspace(m, q) bytes, 256-byte aligned.
+ */
+int seacells_csr_transpose(const seacells_csr *a, uint32_t *at_row_ptr, uint32_t *at_col_idx,
+                           float *at_val, void *workspace, size_t workspace_bytes,
+                           uint32_t *status, seacells_stream_t stream);
+
+/* Workspace bytes seacells_csr_dot needs (> 0). */
+size_t seacells_csr_dot_workspace(void);
+
+/*
+ * Inner product of two matrices of the same shape, accumulated:
+ *     *acc += alpha * sum_{i, c} x[i, c] y[i, c]
+ * acc  device [1] f64 (in/out). Products and sums in f64; rows are summed
+ * in a fixed order. With K, K^2 B, A^T, t1 and A A^T, three calls into one
+ * zeroed acc give the RSS (alpha = 1, -2, 1). workspace: at least
+ * seacells_csr_dot_workspace() bytes, 256-byte aligned.
+ */
+int seacells_csr_dot(const seacells_csr *x, const seacells_csr *y, double alpha, double *acc,
+                     void *workspace, size_t workspace_bytes, uint32_t *status,
+                     seacells_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SEACELLS_SPARSE_H */

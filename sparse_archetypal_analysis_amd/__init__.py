@@ -1,10 +1,14 @@
 """SEACells Frank-Wolfe hot path on MI355X (gfx950): HIP kernels behind a C ABI.
 
-``native`` binds ``libseacells_fw.so`` (include/seacells_fw.h); ``csrc/``
+``native`` binds ``libseacells_fw.so`` (include/seacells_fw.h for the A and B
+updates, include/seacells_sparse.h for the operand construction); ``csrc/``
 holds the HIP sources; ``_build`` compiles them in-tree.
 """
 from .native import (DeviceCSR, SeacellsError, load, new_status, raise_on_status,  # noqa: F401
                      seacells_fw_a_columns, seacells_fw_a_columns_pruned,
                      seacells_fw_a_columns_workspace,
                      seacells_fw_b_apply, seacells_fw_b_argmin, seacells_fw_b_argmin_workspace,
+                     seacells_csr_matmul_rows, seacells_csr_matmul_fill, csr_matmul,
+                     seacells_csr_transpose_workspace, seacells_csr_transpose,
+                     seacells_csr_dot_workspace, seacells_csr_dot, rss, device_operands,
                      status_flags)

@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libseacells_fw.so")
-SOURCES = ["abi.hip", "fw_a.hip", "fw_b.hip"]
+SOURCES = ["abi.hip", "fw_a.hip", "fw_b.hip", "sparse_ops.hip"]
 HEADERS = ["common.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,7 +29,7 @@ def stale() -> bool:
         return True
     t = os.path.getmtime(LIB)
     deps = sources() + [os.path.join(CSRC, h) for h in HEADERS] + \
-        [os.path.join(ROOT, "include", "seacells_fw.h")]
+        [os.path.join(ROOT, "include", h) for h in ("seacells_fw.h", "seacells_sparse.h")]
     return any(os.path.getmtime(d) > t for d in deps)
 
 

@@ -1,4 +1,4 @@
-// Exported C ABI (include/seacells_fw.h): host-side validation, workspace
+// Exported C ABI (include/seacells_fw.h, include/seacells_sparse.h): host-side validation, workspace
 // sizing and dispatch onto the caller's stream. Argument checks run before
 // any HIP call, so they also work on a machine without a GPU.
 #include <atomic>
@@ -6,6 +6,7 @@
 #include <cstring>
 
 #include "../../include/seacells_fw.h"
+#include "../../include/seacells_sparse.h"
 #include "common.hpp"
 
 namespace seacells {
@@ -179,6 +180,93 @@ int seacells_fw_b_apply(uint32_t *bt_idx, float *bt_val, uint32_t *bt_cnt, uint3
   if (e != hipSuccess) return hip_fail(e, "status clear");
   e = launch_fw_b_apply(bt_idx, bt_val, bt_cnt, n, k, cap_b, arg_idx, gamma, status, s);
   if (e != hipSuccess) return hip_fail(e, "fw_b_apply launch");
+  return SEACELLS_OK;
+}
+
+// --- sparse operations (seacells_sparse.h) ---------------------------------
+
+static int check_any_csr(const seacells_csr *m) {
+  if (m == nullptr || m->row_ptr == nullptr) return SEACELLS_E_NULL;
+  if (m->nnz > 0 && (m->col_idx == nullptr || m->val == nullptr)) return SEACELLS_E_NULL;
+  if (m->nnz >= 0x80000000u || m->n_rows >= 0x80000000u || m->n_cols >= 0x80000000u)
+    return SEACELLS_E_TOO_LARGE;
+  return SEACELLS_OK;
+}
+
+int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint32_t *c_row_ptr,
+                             uint32_t *status, seacells_stream_t stream) {
+  int rc;
+  if ((rc = check_any_csr(a)) != SEACELLS_OK || (rc = check_any_csr(b)) != SEACELLS_OK) return rc;
+  if (c_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
+  if (a->n_cols != b->n_rows) return SEACELLS_E_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_spgemm_count(as_csr(a), as_csr(b), a->n_rows, a->n_cols, b->n_cols, c_row_ptr,
+                          status, s);
+  if (e != hipSuccess) return hip_fail(e, "csr_matmul_rows launch");
+  return SEACELLS_OK;
+}
+
+int seacells_csr_matmul_fill(const seacells_csr *a, const seacells_csr *b,
+                             const uint32_t *c_row_ptr, uint32_t *c_col_idx, float *c_val,
+                             uint32_t *status, seacells_stream_t stream) {
+  int rc;
+  if ((rc = check_any_csr(a)) != SEACELLS_OK || (rc = check_any_csr(b)) != SEACELLS_OK) return rc;
+  if (c_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
+  if (a->n_cols != b->n_rows) return SEACELLS_E_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  // (empty outputs may pass NULL arrays: nothing is written then)
+  e = launch_spgemm_fill(as_csr(a), as_csr(b), a->n_rows, a->n_cols, b->n_cols, c_row_ptr,
+                         c_col_idx, c_val, status, s);
+  if (e != hipSuccess) return hip_fail(e, "csr_matmul_fill launch");
+  return SEACELLS_OK;
+}
+
+size_t seacells_csr_transpose_workspace(uint32_t m, uint32_t q) {
+  const size_t b = transpose_workspace(m, q);
+  return b > 0 ? b : 256;
+}
+
+int seacells_csr_transpose(const seacells_csr *a, uint32_t *at_row_ptr, uint32_t *at_col_idx,
+                           float *at_val, void *workspace, size_t workspace_bytes,
+                           uint32_t *status, seacells_stream_t stream) {
+  int rc;
+  if ((rc = check_any_csr(a)) != SEACELLS_OK) return rc;
+  if (at_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
+  if (a->nnz > 0 && (at_col_idx == nullptr || at_val == nullptr)) return SEACELLS_E_NULL;
+  if (workspace == nullptr ||
+      workspace_bytes < seacells_csr_transpose_workspace(a->n_rows, a->n_cols) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SEACELLS_E_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_transpose(as_csr(a), a->n_rows, a->n_cols, at_row_ptr, at_col_idx, at_val,
+                       workspace, status, s);
+  if (e != hipSuccess) return hip_fail(e, "csr_transpose launch");
+  return SEACELLS_OK;
+}
+
+size_t seacells_csr_dot_workspace(void) { return align_up(dot_workspace(), 256); }
+
+int seacells_csr_dot(const seacells_csr *x, const seacells_csr *y, double alpha, double *acc,
+                     void *workspace, size_t workspace_bytes, uint32_t *status,
+                     seacells_stream_t stream) {
+  int rc;
+  if ((rc = check_any_csr(x)) != SEACELLS_OK || (rc = check_any_csr(y)) != SEACELLS_OK) return rc;
+  if (acc == nullptr || status == nullptr) return SEACELLS_E_NULL;
+  if (x->n_rows != y->n_rows || x->n_cols != y->n_cols) return SEACELLS_E_SHAPE;
+  if (workspace == nullptr || workspace_bytes < seacells_csr_dot_workspace() ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SEACELLS_E_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_dot(as_csr(x), as_csr(y), x->n_rows, alpha, acc, workspace, status, s);
+  if (e != hipSuccess) return hip_fail(e, "csr_dot launch");
   return SEACELLS_OK;
 }
 

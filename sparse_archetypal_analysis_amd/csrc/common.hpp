@@ -18,6 +18,7 @@ constexpr uint32_t kFlagBCapOverflow = 0x4u;
 constexpr uint32_t kFlagBadIndex = 0x8u;
 constexpr uint32_t kFlagNonfinite = 0x10u;
 constexpr uint32_t kFlagBadGamma = 0x20u;
+constexpr uint32_t kFlagOutputTooLarge = 0x40u;
 
 // A CSR as the kernels see it (device pointers).
 struct Csr {
@@ -175,5 +176,19 @@ hipError_t launch_fw_b_apply(uint32_t *bt_idx, float *bt_val, uint32_t *bt_cnt, 
                              uint32_t k, uint32_t cap_b, const uint32_t *arg_idx, float gamma,
                              uint32_t *status, hipStream_t stream);
 hipError_t launch_status_clear(uint32_t *status, hipStream_t stream);
+
+// --- sparse operations that build the operands -----------------------------
+uint32_t tr_blocks(uint32_t m, uint32_t q);
+size_t transpose_workspace(uint32_t m, uint32_t q);
+size_t dot_workspace();
+hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
+                               uint32_t *c_ptr, uint32_t *status, hipStream_t stream);
+hipError_t launch_spgemm_fill(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
+                              const uint32_t *c_ptr, uint32_t *c_idx, float *c_val,
+                              uint32_t *status, hipStream_t stream);
+hipError_t launch_transpose(Csr a, uint32_t m, uint32_t q, uint32_t *at_ptr, uint32_t *at_idx,
+                            float *at_val, void *ws, uint32_t *status, hipStream_t stream);
+hipError_t launch_dot(Csr x, Csr y, uint32_t m, double alpha, double *acc, void *ws,
+                      uint32_t *status, hipStream_t stream);
 
 }  // namespace seacells

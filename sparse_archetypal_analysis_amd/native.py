@@ -1,4 +1,5 @@
-"""Thin ctypes binding of ``libseacells_fw.so`` (include/seacells_fw.h).
+"""Thin ctypes binding of ``libseacells_fw.so`` (include/seacells_fw.h,
+include/seacells_sparse.h).
 
 The functions carry the C names and only marshal arguments: device tensors
 become raw pointers, torch's current stream becomes the hipStream_t. Every
@@ -20,11 +21,14 @@ from . import _build
 SEACELLS_OK = 0
 ERRORS = {-1: "E_NULL", -2: "E_SHAPE", -3: "E_WORKSPACE", -4: "E_TOO_LARGE", -5: "E_HIP"}
 FLAGS = {0x1: "CAP_OVERFLOW", 0x2: "PARTIALS_INVALID", 0x4: "B_CAP_OVERFLOW", 0x8: "BAD_INDEX",
-         0x10: "NONFINITE", 0x20: "BAD_GAMMA"}
+         0x10: "NONFINITE", 0x20: "BAD_GAMMA", 0x40: "OUTPUT_TOO_LARGE"}
 
 EXPORTS = ("seacells_fw_a_columns_workspace", "seacells_fw_a_columns",
            "seacells_fw_a_columns_pruned",
            "seacells_fw_b_argmin_workspace", "seacells_fw_b_argmin", "seacells_fw_b_apply",
+           "seacells_csr_matmul_rows", "seacells_csr_matmul_fill",
+           "seacells_csr_transpose_workspace", "seacells_csr_transpose",
+           "seacells_csr_dot_workspace", "seacells_csr_dot",
            "seacells_status_string", "seacells_last_error", "seacells_version")
 
 
@@ -75,6 +79,19 @@ def load():
     lib.seacells_fw_b_apply.restype = ctypes.c_int
     lib.seacells_fw_b_apply.argtypes = [_VP, _VP, _VP, _U32, _U32, _U32, _VP, ctypes.c_float,
                                         _VP, _VP]
+    lib.seacells_csr_matmul_rows.restype = ctypes.c_int
+    lib.seacells_csr_matmul_rows.argtypes = [_CSR_P, _CSR_P, _VP, _VP, _VP]
+    lib.seacells_csr_matmul_fill.restype = ctypes.c_int
+    lib.seacells_csr_matmul_fill.argtypes = [_CSR_P, _CSR_P, _VP, _VP, _VP, _VP, _VP]
+    lib.seacells_csr_transpose_workspace.restype = ctypes.c_size_t
+    lib.seacells_csr_transpose_workspace.argtypes = [_U32, _U32]
+    lib.seacells_csr_transpose.restype = ctypes.c_int
+    lib.seacells_csr_transpose.argtypes = [_CSR_P, _VP, _VP, _VP, _VP, ctypes.c_size_t, _VP, _VP]
+    lib.seacells_csr_dot_workspace.restype = ctypes.c_size_t
+    lib.seacells_csr_dot_workspace.argtypes = []
+    lib.seacells_csr_dot.restype = ctypes.c_int
+    lib.seacells_csr_dot.argtypes = [_CSR_P, _CSR_P, ctypes.c_double, _VP, _VP, ctypes.c_size_t,
+                                     _VP, _VP]
     lib.seacells_status_string.restype = ctypes.c_char_p
     lib.seacells_status_string.argtypes = [ctypes.c_int]
     lib.seacells_last_error.restype = ctypes.c_char_p
@@ -269,3 +286,143 @@ def seacells_fw_b_apply(bt_idx, bt_val, bt_cnt, n: int, arg_idx, gamma: float, s
                                  _ptr(arg_idx), float(gamma), _ptr(status), _stream(stream))
     _check_rc(rc)
     return bt_idx, bt_val, bt_cnt, status
+
+
+# --------------------------------------------------------------------------
+# sparse operations (include/seacells_sparse.h)
+# --------------------------------------------------------------------------
+
+def seacells_csr_matmul_rows(a: DeviceCSR, b: DeviceCSR, c_row_ptr=None, status=None,
+                             stream=None):
+    """Row pointer of a @ b ([m + 1] int32, last entry = nnz). Returns (c_row_ptr, status)."""
+    lib = load()
+    dev = a.row_ptr.device
+    if c_row_ptr is None:
+        c_row_ptr = torch.empty(a.shape[0] + 1, dtype=torch.int32, device=dev)
+    if status is None:
+        status = new_status(dev)
+    sa, sb = a.struct(), b.struct()
+    rc = lib.seacells_csr_matmul_rows(ctypes.byref(sa), ctypes.byref(sb), _ptr(c_row_ptr),
+                                      _ptr(status), _stream(stream))
+    _check_rc(rc)
+    return c_row_ptr, status
+
+
+def seacells_csr_matmul_fill(a: DeviceCSR, b: DeviceCSR, c_row_ptr, c_col_idx, c_val,
+                             status=None, stream=None):
+    """Columns and values of a @ b into buffers sized by c_row_ptr[-1]."""
+    lib = load()
+    if status is None:
+        status = new_status(a.row_ptr.device)
+    sa, sb = a.struct(), b.struct()
+    rc = lib.seacells_csr_matmul_fill(ctypes.byref(sa), ctypes.byref(sb), _ptr(c_row_ptr),
+                                      _ptr(c_col_idx) if c_col_idx.numel() else None,
+                                      _ptr(c_val) if c_val.numel() else None, _ptr(status),
+                                      _stream(stream))
+    _check_rc(rc)
+    return c_col_idx, c_val, status
+
+
+def csr_matmul(a: DeviceCSR, b: DeviceCSR, status=None, stream=None) -> DeviceCSR:
+    """a @ b as a DeviceCSR: both passes, with one synchronisation between
+    them to size the outputs. Raises on a device status flag."""
+    dev = a.row_ptr.device
+    if status is None:
+        status = new_status(dev)
+    c_ptr, _ = seacells_csr_matmul_rows(a, b, status=status, stream=stream)
+    raise_on_status(status)  # synchronises; c_ptr[-1] is valid after it
+    nnz = int(c_ptr[-1].item()) & 0xffffffff
+    c_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+    c_val = torch.empty(nnz, dtype=torch.float32, device=dev)
+    seacells_csr_matmul_fill(a, b, c_ptr, c_idx, c_val, status=status, stream=stream)
+    return DeviceCSR(c_ptr, c_idx, c_val, (a.shape[0], b.shape[1]))
+
+
+def seacells_csr_transpose_workspace(m: int, q: int) -> int:
+    return int(load().seacells_csr_transpose_workspace(m, q))
+
+
+def seacells_csr_transpose(a: DeviceCSR, at_row_ptr=None, at_col_idx=None, at_val=None,
+                           workspace=None, status=None, stream=None):
+    """Transpose of a. Returns (DeviceCSR of a^T, status)."""
+    lib = load()
+    dev = a.row_ptr.device
+    m, q = a.shape
+    if at_row_ptr is None:
+        at_row_ptr = torch.empty(q + 1, dtype=torch.int32, device=dev)
+    if at_col_idx is None:
+        at_col_idx = torch.empty(a.nnz, dtype=torch.int32, device=dev)
+    if at_val is None:
+        at_val = torch.empty(a.nnz, dtype=torch.float32, device=dev)
+    if status is None:
+        status = new_status(dev)
+    if workspace is None:
+        workspace = torch.empty(seacells_csr_transpose_workspace(m, q), dtype=torch.uint8,
+                                device=dev)
+    sa = a.struct()
+    rc = lib.seacells_csr_transpose(ctypes.byref(sa), _ptr(at_row_ptr),
+                                    _ptr(at_col_idx) if at_col_idx.numel() else None,
+                                    _ptr(at_val) if at_val.numel() else None, _ptr(workspace),
+                                    workspace.numel(), _ptr(status), _stream(stream))
+    _check_rc(rc)
+    return DeviceCSR(at_row_ptr, at_col_idx, at_val, (q, m)), status
+
+
+def seacells_csr_dot_workspace() -> int:
+    return int(load().seacells_csr_dot_workspace())
+
+
+def seacells_csr_dot(x: DeviceCSR, y: DeviceCSR, alpha: float, acc, workspace=None, status=None,
+                     stream=None):
+    """acc[0] += alpha * sum(x * y) (acc: float64 [1] device tensor)."""
+    lib = load()
+    dev = x.row_ptr.device
+    if acc.dtype != torch.float64 or acc.numel() < 1:
+        raise SeacellsError("acc must be a float64 tensor")
+    if status is None:
+        status = new_status(dev)
+    if workspace is None:
+        workspace = torch.empty(seacells_csr_dot_workspace(), dtype=torch.uint8, device=dev)
+    sx, sy = x.struct(), y.struct()
+    rc = lib.seacells_csr_dot(ctypes.byref(sx), ctypes.byref(sy), float(alpha), _ptr(acc),
+                              _ptr(workspace), workspace.numel(), _ptr(status), _stream(stream))
+    _check_rc(rc)
+    return acc, status
+
+
+def rss(K: DeviceCSR, k2b: DeviceCSR, a_t: DeviceCSR, t1: DeviceCSR, aat: DeviceCSR,
+        acc=None, status=None, stream=None):
+    """||K - K B A||_F^2 = <K, K> - 2 <K^2 B, A^T> + <B^T K^2 B, A A^T>, as a
+    float64 [1] device tensor (three inner products on the device)."""
+    dev = K.row_ptr.device
+    if acc is None:
+        acc = torch.zeros(1, dtype=torch.float64, device=dev)
+    if status is None:
+        status = new_status(dev)
+    ws = torch.empty(seacells_csr_dot_workspace(), dtype=torch.uint8, device=dev)
+    seacells_csr_dot(K, K, 1.0, acc, ws, status, stream)
+    seacells_csr_dot(k2b, a_t, -2.0, acc, ws, status, stream)
+    seacells_csr_dot(t1, aat, 1.0, acc, ws, status, stream)
+    return acc, status
+
+
+def device_operands(K: DeviceCSR, B: DeviceCSR, At: DeviceCSR, status=None, stream=None) -> dict:
+    """Every Frank-Wolfe operand from K (n x n), B (n x k) and A^T (n x k),
+    built by the library's kernels:
+      kb = K B, k2b = K kb, bt = B^T, t1 = bt k2b, a = (A^T)^T, aat = a A^T,
+      kat = K A^T, k2at = K kat.
+    One synchronisation per product sizes its output. Raises on a device
+    status flag."""
+    if status is None:
+        status = new_status(K.row_ptr.device)
+    out = {}
+    out["kb"] = csr_matmul(K, B, status, stream)
+    out["k2b"] = csr_matmul(K, out["kb"], status, stream)
+    out["bt"], _ = seacells_csr_transpose(B, status=status, stream=stream)
+    out["t1"] = csr_matmul(out["bt"], out["k2b"], status, stream)
+    out["a"], _ = seacells_csr_transpose(At, status=status, stream=stream)
+    out["aat"] = csr_matmul(out["a"], At, status, stream)
+    out["kat"] = csr_matmul(K, At, status, stream)
+    out["k2at"] = csr_matmul(K, out["kat"], status, stream)
+    raise_on_status(status)
+    return out

@@ -13,9 +13,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_functions():
-    src = open(os.path.join(ROOT, "include", "seacells_fw.h")).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(seacells_\w+)\s*\(", src)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if fn.endswith(".h"):
+            src = open(os.path.join(inc, fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(seacells_\w+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -152,3 +157,39 @@ def test_a_columns_pruned_rejects_bad_threshold_on_host():
     assert call(float("nan")) == -2
     assert call(float("inf")) == -2
     assert call(0.5, t1=csr(k + 1, k, 3)) == -2
+
+
+# --- sparse operations (include/seacells_sparse.h) ---------------------------
+
+def test_sparse_ops_reject_bad_arguments_on_host():
+    lib = saa.load()
+    P = ctypes.byref
+    a, b = csr(5, 7, 3), csr(7, 4, 2)
+    st, out = 0x9000, 0x4000
+    # product: nulls, inner-dimension mismatch, too many entries
+    assert lib.seacells_csr_matmul_rows(None, P(b), out, st, None) == -1
+    assert lib.seacells_csr_matmul_rows(P(a), P(b), None, st, None) == -1
+    assert lib.seacells_csr_matmul_rows(P(a), P(b), out, None, None) == -1
+    assert lib.seacells_csr_matmul_rows(P(a), P(csr(6, 4, 2)), out, st, None) == -2
+    assert lib.seacells_csr_matmul_fill(P(a), P(csr(6, 4, 2)), out, out, out, st, None) == -2
+    assert lib.seacells_csr_matmul_fill(P(a), P(b), None, out, out, st, None) == -1
+    assert lib.seacells_csr_matmul_rows(P(csr(5, 7, 2 ** 31)), P(b), out, st, None) == -4
+    assert lib.seacells_csr_matmul_rows(P(csr(5, 7, 3, ptr=None)), P(b), out, st, None) == -1
+    # transpose: nulls and workspace
+    need = lib.seacells_csr_transpose_workspace(5, 7)
+    assert need >= 7 * 4 and need % 256 == 0
+    assert lib.seacells_csr_transpose(P(a), None, out, out, 0x10000, need, st, None) == -1
+    assert lib.seacells_csr_transpose(P(a), out, None, out, 0x10000, need, st, None) == -1
+    assert lib.seacells_csr_transpose(P(a), out, out, out, 0x10000, need - 1, st, None) == -3
+    assert lib.seacells_csr_transpose(P(a), out, out, out, 0x10004, need, st, None) == -3
+    assert lib.seacells_csr_transpose(P(a), out, out, out, None, need, st, None) == -3
+    # inner product: shapes, nulls, workspace
+    dneed = lib.seacells_csr_dot_workspace()
+    assert dneed > 0 and dneed % 256 == 0
+    x = csr(5, 7, 3)
+    assert lib.seacells_csr_dot(P(x), P(csr(5, 6, 3)), ctypes.c_double(1.0), out, 0x10000, dneed,
+                                st, None) == -2
+    assert lib.seacells_csr_dot(P(x), P(x), ctypes.c_double(1.0), None, 0x10000, dneed, st,
+                                None) == -1
+    assert lib.seacells_csr_dot(P(x), P(x), ctypes.c_double(1.0), out, 0x10000, dneed - 8, st,
+                                None) == -3
