@@ -40,9 +40,15 @@ extern "C" {
 /* The product's (or transpose's) output would hold 2^31 or more entries. */
 #define SEACELLS_FLAG_OUTPUT_TOO_LARGE 0x40u
 
+/* Workspace bytes seacells_csr_matmul_rows needs for a product with m rows
+ * (> 0; about 8 bytes per 4096 rows). */
+size_t seacells_csr_matmul_workspace(uint32_t m);
+
 /*
  * Product C = A B, step 1 of 2 (`csr_matmul_csr` on the page): the row
  * pointer of C. a is m x p, b is p x q (else SEACELLS_E_SHAPE).
+ * workspace: at least seacells_csr_matmul_workspace(m) bytes, 256-byte
+ * aligned (else SEACELLS_E_WORKSPACE).
  * c_row_ptr  device [m + 1] u32 out: c_row_ptr[i] = first entry of row i;
  *            c_row_ptr[m] = nnz(C), for the caller to size c_col_idx and
  *            c_val (read it after the stream synchronises). Row i holds every
@@ -52,7 +58,8 @@ extern "C" {
  * is then not valid); BAD_INDEX for malformed rows or columns (skipped).
  */
 int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint32_t *c_row_ptr,
-                             uint32_t *status, seacells_stream_t stream);
+                             void *workspace, size_t workspace_bytes, uint32_t *status,
+                             seacells_stream_t stream);
 
 /*
  * Product C = A B, step 2 of 2: columns (ascending in every row) and values.

@@ -193,17 +193,23 @@ static int check_any_csr(const seacells_csr *m) {
   return SEACELLS_OK;
 }
 
+size_t seacells_csr_matmul_workspace(uint32_t m) { return matmul_workspace(m); }
+
 int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint32_t *c_row_ptr,
-                             uint32_t *status, seacells_stream_t stream) {
+                             void *workspace, size_t workspace_bytes, uint32_t *status,
+                             seacells_stream_t stream) {
   int rc;
   if ((rc = check_any_csr(a)) != SEACELLS_OK || (rc = check_any_csr(b)) != SEACELLS_OK) return rc;
   if (c_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
   if (a->n_cols != b->n_rows) return SEACELLS_E_SHAPE;
+  if (workspace == nullptr || workspace_bytes < matmul_workspace(a->n_rows) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SEACELLS_E_WORKSPACE;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = launch_status_clear(status, s);
   if (e != hipSuccess) return hip_fail(e, "status clear");
   e = launch_spgemm_count(as_csr(a), as_csr(b), a->n_rows, a->n_cols, b->n_cols, c_row_ptr,
-                          status, s);
+                          workspace, status, s);
   if (e != hipSuccess) return hip_fail(e, "csr_matmul_rows launch");
   return SEACELLS_OK;
 }

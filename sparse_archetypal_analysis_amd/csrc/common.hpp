@@ -180,9 +180,10 @@ hipError_t launch_status_clear(uint32_t *status, hipStream_t stream);
 // --- sparse operations that build the operands -----------------------------
 uint32_t tr_blocks(uint32_t m, uint32_t q);
 size_t transpose_workspace(uint32_t m, uint32_t q);
+size_t matmul_workspace(uint32_t m);
 size_t dot_workspace();
 hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
-                               uint32_t *c_ptr, uint32_t *status, hipStream_t stream);
+                               uint32_t *c_ptr, void *ws, uint32_t *status, hipStream_t stream);
 hipError_t launch_spgemm_fill(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
                               const uint32_t *c_ptr, uint32_t *c_idx, float *c_val,
                               uint32_t *status, hipStream_t stream);

@@ -8,12 +8,17 @@
 //   a bitmap of the row's output columns is built in LDS (a window of
 //   16384 columns at a time), a popcount prefix over it gives every column
 //   its rank, and the products are added into an LDS slot per rank (a window
-//   of 2048 ranks at a time), then written out in column order. The entries
-//   of A's row are taken one after the other and each B row is spread over
-//   the lanes (the columns of one row are unique, so a lane-parallel add
-//   never collides): every output sums its products in A-entry order, then
-//   B-entry order, in f32 with fma. The output keeps every column that some
-//   product reaches (a sum that cancels to 0 stays as an explicit 0).
+//   of 1024 ranks at a time), then written out in column order (an LDS map
+//   from slot to column lets consecutive lanes store consecutive entries). The
+//   products of the row are flattened over the lanes: 64 entries of A at a
+//   time, one per lane, load their B row bounds together; a scan of the B row
+//   lengths numbers the products (A entry, then B entry) and each window of
+//   64 consecutive products goes one per lane. Adds into the slots run entry
+//   by entry within a window (the columns of one B row are unique, so lanes
+//   of one entry never collide), so every output sums its products in
+//   A-entry order, then B-entry order, in f32 with fma. The output keeps
+//   every column that some product reaches (a sum that cancels to 0 stays as
+//   an explicit 0).
 // Transpose: rows are cut into R blocks; one wave per block counts its
 //   entries per column, the counts become per-(block, column) write
 //   positions, and each wave writes its rows in order, so a transposed row
@@ -28,7 +33,8 @@ namespace {
 
 constexpr uint32_t kSpWaves = 4;        // waves per block
 constexpr uint32_t kSpWinWords = 512;   // bitmap words per column window (16384 columns)
-constexpr uint32_t kSpSlots = 2048;     // value slots per rank window
+constexpr uint32_t kSpSlots = 1024;     // value slots per rank window
+constexpr uint32_t kSpGroup = 4;        // product windows loaded together
 constexpr uint32_t kTrMaxBlocks = 1024;
 constexpr size_t kTrTableBytes = 64u << 20;  // per-(block, column) table of the transpose
 constexpr uint32_t kDotBlocks = 1024;
@@ -58,6 +64,12 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
   return x;
 }
 
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t x) {
+  for (int off = 32; off >= 1; off >>= 1)
+    x += (uint64_t)__shfl_xor((unsigned long long)x, off, kWave);
+  return x;
+}
+
 // Exclusive prefix sum over the wave (lane order).
 __device__ __forceinline__ uint32_t wave_excl_scan_u32(uint32_t x, uint32_t lane) {
   uint32_t incl = x;
@@ -68,6 +80,130 @@ __device__ __forceinline__ uint32_t wave_excl_scan_u32(uint32_t x, uint32_t lane
   return incl - x;
 }
 
+// Walk the products of A's row [a0, a1) in order, 64 at a time. For each
+// window f(valid, c, bv, a_own, own, owners) is called by the whole wave:
+// the lane holds product number base + lane if valid, with B column c and
+// value bv (0 unless kVal), the value a_own of its A entry, and own, that
+// entry's lane within the current chunk of 64 A entries; owners (uniform) is
+// the mask of chunk lanes with products in the window. Returns flags.
+template <bool kVal, class F>
+__device__ __forceinline__ uint32_t for_products(const Csr &a, const Csr &b, uint32_t p,
+                                                 uint32_t a0, uint32_t a1, uint32_t lane,
+                                                 F &&f) {
+  uint32_t flags = 0;
+  for (uint32_t ch = a0; ch < a1; ch += kWave) {
+    const uint32_t e = ch + lane;
+    uint32_t len = 0, b0 = 0;
+    float av = 0.0f;
+    if (e < a1) {
+      const uint32_t j = a.idx[e];
+      if (kVal) av = a.val[e];
+      uint32_t lo, hi;
+      if (j < p && sp_row(b, j, lo, hi)) {
+        b0 = lo;
+        len = hi - lo;
+      } else {
+        flags |= kFlagBadIndex;
+      }
+    }
+    // rows of a well-formed B are disjoint, so the 64 lengths sum below
+    // 2^31; overlapping rows (a malformed row pointer) could wrap the scan
+    if (wave_sum_u64(len) >= 0x80000000ull) {
+      flags |= kFlagBadIndex;
+      len = 0;
+    }
+    // off: number of the entry's first product; nondecreasing over the lanes
+    const uint32_t off = wave_excl_scan_u32(len, lane);
+    const uint32_t total = readlane_u32(off + len, kWave - 1);
+    if (total == 0) continue;
+    const uint64_t nonempty = __ballot(len > 0);
+    // State of the window starting at product `base` (< total): the lane's
+    // owner, its B entry t (for a lane past the end, the window's first
+    // product, so every lane loads from inside B), the owner's value and the
+    // owners of the window.
+    auto window = [&](uint32_t base, uint32_t &own, uint32_t &t, float &a_own, uint64_t &owners) {
+      const uint32_t pi = base + lane;
+      // the first owner is the last entry starting at or before base (it is
+      // never empty); the others start inside the window
+      const uint32_t l_lo = (uint32_t)__popcll(__ballot(off <= base)) - 1u;
+      const uint64_t upto = __ballot(off < base + kWave);  // lanes 0 .. l_hi
+      owners = nonempty & upto & ~((1ull << l_lo) - 1ull);
+      const uint32_t o_lo = readlane_u32(off, l_lo), b_lo = readlane_u32(b0, l_lo);
+      own = l_lo;
+      t = b_lo + (pi - o_lo);
+      a_own = kVal ? readlane_f32(av, l_lo) : 0.0f;
+      for (uint64_t mm = owners & (owners - 1ull); mm != 0; mm &= mm - 1ull) {
+        const uint32_t l = (uint32_t)__builtin_ctzll(mm);
+        const uint32_t ol = readlane_u32(off, l);
+        const uint32_t bl = readlane_u32(b0, l);
+        const float al = kVal ? readlane_f32(av, l) : 0.0f;
+        if (ol <= pi) {
+          own = l;
+          t = bl + (pi - ol);
+          a_own = al;
+        }
+      }
+      if (pi >= total) t = b_lo + (base - o_lo);
+    };
+    if (total <= kWave) {  // one window: no pipeline
+      uint32_t own, t;
+      float a_own;
+      uint64_t owners;
+      window(0, own, t, a_own, owners);
+      const uint32_t c = b.idx[t];
+      const float bv = kVal ? b.val[t] : 0.0f;
+      f(lane < total, c, bv, a_own, own, owners);
+      continue;
+    }
+    // Software pipeline over groups of kSpGroup windows: the loads of the
+    // next group are in flight while the current group is processed. A
+    // window past the end repeats the previous window's loads and is not
+    // processed, so the number of loads in flight never depends on the data.
+    const uint32_t last = (total - 1u) & ~(kWave - 1u);  // first product of the last window
+    uint32_t own[kSpGroup], c[kSpGroup];
+    uint64_t om[kSpGroup];
+    float ao[kSpGroup], bv[kSpGroup];
+    auto issue = [&](uint32_t g0) {  // g0 <= last
+      uint32_t t = 0;
+#pragma unroll
+      for (uint32_t u = 0; u < kSpGroup; ++u) {
+        const uint32_t wb = g0 + u * kWave;
+        if (u == 0 || wb <= last) {
+          window(wb, own[u], t, ao[u], om[u]);
+        } else {
+          own[u] = own[u - 1];
+          ao[u] = ao[u - 1];
+          om[u] = om[u - 1];
+        }
+        c[u] = b.idx[t];
+        bv[u] = kVal ? b.val[t] : 0.0f;
+      }
+    };
+    issue(0);
+    for (uint32_t g0 = 0; g0 < total; g0 += kSpGroup * kWave) {
+      uint32_t own_c[kSpGroup], c_c[kSpGroup];
+      uint64_t om_c[kSpGroup];
+      float ao_c[kSpGroup], bv_c[kSpGroup];
+#pragma unroll
+      for (uint32_t u = 0; u < kSpGroup; ++u) {
+        own_c[u] = own[u];
+        om_c[u] = om[u];
+        c_c[u] = c[u];
+        ao_c[u] = ao[u];
+        bv_c[u] = bv[u];
+      }
+      const uint32_t g1 = g0 + kSpGroup * kWave;
+      issue(g1 <= last ? g1 : last);
+#pragma unroll
+      for (uint32_t u = 0; u < kSpGroup; ++u) {
+        const uint32_t wb = g0 + u * kWave;
+        if (wb < total) f(wb + lane < total, c_c[u], bv_c[u], ao_c[u], own_c[u], om_c[u]);
+      }
+    }
+  }
+  return flags;
+}
+
 // Mark in bits[] (window starting at column w0, nw words) every column some
 // product of A's row [a0, a1) reaches. Returns the flags seen.
 __device__ __forceinline__ uint32_t mark_columns(const Csr &a, const Csr &b, uint32_t p,
@@ -75,23 +211,16 @@ __device__ __forceinline__ uint32_t mark_columns(const Csr &a, const Csr &b, uin
                                                  uint32_t w0, uint32_t nw, uint32_t *bits,
                                                  uint32_t lane) {
   uint32_t flags = 0;
-  for (uint32_t e = a0; e < a1; ++e) {
-    const uint32_t j = a.idx[e];
-    uint32_t b0, b1;
-    if (j >= p || !sp_row(b, j, b0, b1)) {
-      flags |= kFlagBadIndex;
-      continue;
-    }
-    for (uint32_t t = b0 + lane; t < b1; t += kWave) {
-      const uint32_t c = b.idx[t];
-      if (c >= q) {
-        flags |= kFlagBadIndex;
-        continue;
-      }
-      const uint32_t rel = c - w0;
-      if (rel < nw * 32u) atomicOr(&bits[rel >> 5], 1u << (rel & 31u));
-    }
-  }
+  flags |= for_products<false>(a, b, p, a0, a1, lane,
+                               [&](bool valid, uint32_t c, float, float, uint32_t, uint64_t) {
+                                 if (!valid) return;
+                                 if (c >= q) {
+                                   flags |= kFlagBadIndex;
+                                   return;
+                                 }
+                                 const uint32_t rel = c - w0;
+                                 if (rel < nw * 32u) atomicOr(&bits[rel >> 5], 1u << (rel & 31u));
+                               });
   return flags;
 }
 
@@ -124,36 +253,113 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
   if (flags != 0) atomicOr(status, flags);
 }
 
-// One block: ptr[0] = 0, ptr[1 .. count] becomes the inclusive prefix sum of
-// itself (64-bit, so a total of 2^31 or more is caught: then the flag is set
-// and every pointer is 0, so a later pass over them writes nothing).
-__global__ void __launch_bounds__(1024)
-    scan_counts_kernel(uint32_t *__restrict__ ptr, uint32_t count, uint32_t too_large_flag,
-                       uint32_t *__restrict__ status) {
-  __shared__ uint64_t part[1024];
-  const uint32_t tid = threadIdx.x;
-  const uint32_t per = (count + 1023u) / 1024u;
-  const uint32_t i0 = min(tid * per, count), i1 = min(i0 + per, count);
-  uint64_t sum = 0;
-  for (uint32_t i = i0; i < i1; ++i) sum += ptr[1 + i];
-  part[tid] = sum;
+// Row pointers from counts, in place: ptr[0] = 0 and ptr[1 .. count]
+// becomes the inclusive prefix sum of itself. Three passes over tiles of
+// kScanTile values (256 threads x 16 consecutive values): tile sums, one
+// block scanning the tile sums in 64 bits (part[G] = 1 when the total reaches
+// 2^31: the flag is set and every pointer becomes 0, so a later pass over
+// them writes nothing), then each tile scanned from its offset.
+constexpr uint32_t kScanThreads = 256, kScanItems = 16, kScanTile = kScanThreads * kScanItems;
+
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t x, uint32_t lane) {
+  for (uint32_t off = 1; off < kWave; off <<= 1) {
+    const uint64_t v = (uint64_t)__shfl_up((unsigned long long)x, off, kWave);
+    if (lane >= off) x += v;
+  }
+  return x;
+}
+
+// Exclusive scan over the 256 threads of a block; *total gets the sum.
+__device__ __forceinline__ uint64_t block_excl_scan_u64(uint64_t x, uint64_t *sh, uint64_t *total) {
+  const uint32_t lane = lane_id(), wid = threadIdx.x / kWave;
+  const uint64_t incl = wave_incl_scan_u64(x, lane);
+  if (lane == kWave - 1) sh[wid] = incl;
   __syncthreads();
-  for (uint32_t off = 1; off < 1024; off <<= 1) {
-    const uint64_t v = tid >= off ? part[tid - off] : 0u;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+  uint64_t before = 0, all = 0;
+  for (uint32_t w = 0; w < kScanThreads / kWave; ++w) {
+    if (w < wid) before += sh[w];
+    all += sh[w];
   }
-  const bool too_large = part[1023] >= 0x80000000ull;
-  uint64_t at = part[tid] - sum;
-  for (uint32_t i = i0; i < i1; ++i) {
-    at += ptr[1 + i];
-    ptr[1 + i] = too_large ? 0u : (uint32_t)at;
+  __syncthreads();
+  *total = all;
+  return before + incl - x;
+}
+
+__global__ void __launch_bounds__(kScanThreads)
+    scan_tile_sums_kernel(const uint32_t *__restrict__ x, uint32_t count,
+                          uint64_t *__restrict__ part) {
+  __shared__ uint64_t sh[kScanThreads / kWave];
+  const size_t i0 = (size_t)blockIdx.x * kScanTile + (size_t)threadIdx.x * kScanItems;
+  uint64_t sum = 0;
+  for (uint32_t k = 0; k < kScanItems; ++k)
+    if (i0 + k < count) sum += x[i0 + k];
+  uint64_t total;
+  block_excl_scan_u64(sum, sh, &total);
+  if (threadIdx.x == 0) part[blockIdx.x] = total;
+}
+
+__global__ void __launch_bounds__(kScanThreads)
+    scan_partials_kernel(uint64_t *__restrict__ part, uint32_t tiles, uint32_t *__restrict__ ptr,
+                         uint32_t too_large_flag, uint32_t *__restrict__ status) {
+  __shared__ uint64_t sh[kScanThreads / kWave];
+  uint64_t carry = 0;
+  for (uint32_t t0 = 0; t0 < tiles; t0 += kScanThreads) {
+    const uint32_t i = t0 + threadIdx.x;
+    const uint64_t v = i < tiles ? part[i] : 0u;
+    uint64_t total;
+    const uint64_t ex = block_excl_scan_u64(v, sh, &total);
+    if (i < tiles) part[i] = carry + ex;
+    carry += total;
   }
-  if (tid == 0) {
+  if (threadIdx.x == 0) {
+    const bool too_large = carry >= 0x80000000ull;
+    part[tiles] = too_large ? 1u : 0u;
     ptr[0] = 0u;
     if (too_large) atomicOr(status, too_large_flag);
   }
+}
+
+__global__ void __launch_bounds__(kScanThreads)
+    scan_apply_kernel(uint32_t *__restrict__ x, uint32_t count, const uint64_t *__restrict__ part,
+                      uint32_t tiles) {
+  __shared__ uint64_t sh[kScanThreads / kWave];
+  const size_t i0 = (size_t)blockIdx.x * kScanTile + (size_t)threadIdx.x * kScanItems;
+  uint32_t v[kScanItems];
+  uint64_t sum = 0;
+  for (uint32_t k = 0; k < kScanItems; ++k) {
+    v[k] = i0 + k < count ? x[i0 + k] : 0u;
+    sum += v[k];
+  }
+  uint64_t total;
+  uint64_t at = part[blockIdx.x] + block_excl_scan_u64(sum, sh, &total);
+  const bool too_large = part[tiles] != 0u;
+  for (uint32_t k = 0; k < kScanItems; ++k) {
+    at += v[k];
+    if (i0 + k < count) x[i0 + k] = too_large ? 0u : (uint32_t)at;
+  }
+}
+
+uint32_t scan_tiles(uint32_t count) { return (uint32_t)(((uint64_t)count + kScanTile - 1) / kScanTile); }
+
+// ptr[0 .. count]: see above. part: scan_tiles(count) + 1 u64 of workspace.
+hipError_t launch_scan(uint32_t *ptr, uint32_t count, uint64_t *part, uint32_t *status,
+                       hipStream_t stream) {
+  const uint32_t tiles = scan_tiles(count);
+  hipError_t e;
+  if (tiles > 0) {
+    hipLaunchKernelGGL(scan_tile_sums_kernel, dim3(tiles), dim3(kScanThreads), 0, stream, ptr + 1,
+                       count, part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(scan_partials_kernel, dim3(1), dim3(kScanThreads), 0, stream, part, tiles, ptr,
+                     kFlagOutputTooLarge, status);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tiles > 0) {
+    hipLaunchKernelGGL(scan_apply_kernel, dim3(tiles), dim3(kScanThreads), 0, stream, ptr + 1, count,
+                       part, tiles);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Columns and values of A B into the rows the count pass sized.
@@ -162,13 +368,15 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
                        const uint32_t *__restrict__ c_ptr, uint32_t *__restrict__ c_idx,
                        float *__restrict__ c_val, uint32_t *__restrict__ status) {
   __shared__ uint32_t bits_all[kSpWaves][kSpWinWords];
-  __shared__ uint32_t rank_all[kSpWaves][kSpWinWords];
+  __shared__ uint16_t rank_all[kSpWaves][kSpWinWords];
   __shared__ float acc_all[kSpWaves][kSpSlots];
+  __shared__ uint16_t colof_all[kSpWaves][kSpSlots];
   const uint32_t lane = lane_id();
   const uint32_t wib = threadIdx.x / kWave;
   uint32_t *bits = bits_all[wib];
-  uint32_t *rank = rank_all[wib];
+  uint16_t *rank = rank_all[wib];
   float *acc = acc_all[wib];
+  uint16_t *colof = colof_all[wib];
   uint32_t flags = 0;
   for (uint32_t r = blockIdx.x * kSpWaves + wib; r < m; r += gridDim.x * kSpWaves) {
     const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
@@ -191,42 +399,51 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
       uint32_t run = wave_excl_scan_u32(part, lane);
       const uint32_t nwin = wave_sum_u32(part);
       for (uint32_t w = v0w; w < v1w; ++w) {
-        rank[w] = run;
+        rank[w] = (uint16_t)run;  // < 16384: ranks within one column window
         run += __popc(bits[w]);
       }
       wave_lds_sync();
       for (uint32_t s0 = 0; s0 < nwin; s0 += kSpSlots) {
         const uint32_t ns = min(kSpSlots, nwin - s0);
         for (uint32_t s = lane; s < ns; s += kWave) acc[s] = 0.0f;
-        wave_lds_sync();
-        for (uint32_t e = a0; e < a1; ++e) {
-          const uint32_t j = a.idx[e];
-          const float av = a.val[e];
-          uint32_t b0, b1;
-          if (j >= p || !sp_row(b, j, b0, b1)) continue;  // flagged by the marking pass
-          for (uint32_t t = b0 + lane; t < b1; t += kWave) {
-            const uint32_t c = b.idx[t];
-            const uint32_t rel = c - w0;
-            if (c >= q || rel >= nw * 32u) continue;
-            const uint32_t w = rel >> 5, bit = 1u << (rel & 31u);
-            const uint32_t pos = rank[w] + __popc(bits[w] & (bit - 1u)) - s0;
-            if (pos < ns) acc[pos] = __builtin_fmaf(av, b.val[t], acc[pos]);
-          }
-          wave_lds_sync();
-        }
-        // out in column order: the lane owning word w writes its set bits
-        for (uint32_t w = lane; w < nw; w += kWave) {
-          uint32_t x = bits[w];
-          uint32_t pos = rank[w];
-          while (x != 0u) {
-            const uint32_t bpos = (uint32_t)__builtin_ctz(x);
-            x &= x - 1u;
-            const uint32_t slot = pos - s0;
-            if (slot < ns && done + pos < cnt) {
-              c_idx[(size_t)base + done + pos] = w0 + w * 32u + bpos;
-              c_val[(size_t)base + done + pos] = acc[slot];
+        // slot -> column within the window, from each lane's run of words
+        {
+          uint32_t pos = run - part;  // the lane's first rank (run ended at first + part)
+          for (uint32_t w = v0w; w < v1w && pos < s0 + ns; ++w) {
+            uint32_t x = bits[w];
+            while (x != 0u) {
+              const uint32_t bpos = (uint32_t)__builtin_ctz(x);
+              x &= x - 1u;
+              if (pos >= s0 && pos < s0 + ns) colof[pos - s0] = (uint16_t)(w * 32u + bpos);
+              ++pos;
             }
-            ++pos;
+          }
+        }
+        wave_lds_sync();
+        // (bad indices were flagged by the marking pass)
+        for_products<true>(a, b, p, a0, a1, lane,
+                           [&](bool valid, uint32_t c, float bv, float a_own, uint32_t own,
+                               uint64_t owners) {
+                             const uint32_t rel = c - w0;
+                             uint32_t pos = 0xffffffffu;
+                             if (valid && c < q && rel < nw * 32u) {
+                               const uint32_t w = rel >> 5, bit = 1u << (rel & 31u);
+                               pos = rank[w] + __popc(bits[w] & (bit - 1u)) - s0;
+                             }
+                             const bool mine = pos < ns;
+                             // entry by entry: the adds into one slot keep A-entry order
+                             for (uint64_t mm = owners; mm != 0; mm &= mm - 1ull) {
+                               const uint32_t l = (uint32_t)__builtin_ctzll(mm);
+                               if (mine && own == l) acc[pos] = __builtin_fmaf(a_own, bv, acc[pos]);
+                               wave_lds_sync();
+                             }
+                           });
+        // out in column order, consecutive lanes on consecutive entries
+        for (uint32_t s = lane; s < ns; s += kWave) {
+          const uint32_t o = done + s0 + s;
+          if (o < cnt) {
+            c_idx[(size_t)base + o] = w0 + colof[s];
+            c_val[(size_t)base + o] = acc[s];
           }
         }
         wave_lds_sync();
@@ -376,12 +593,28 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-uint32_t sp_blocks(uint32_t m, const DeviceInfo &dev) {
-  // enough blocks to fill the device a few times over, never more than rows need
+// Blocks for a row-per-wave kernel: as many as stay resident together (the
+// rows are dealt out in a grid stride), never more than the rows need.
+uint32_t sp_blocks(uint32_t m, const DeviceInfo &dev, int resident_per_cu) {
   const uint64_t want = ((uint64_t)m + kSpWaves - 1) / kSpWaves;
-  const uint64_t cap = (uint64_t)dev.cus * 8u;
+  const uint64_t cap = (uint64_t)dev.cus * (uint64_t)(resident_per_cu > 0 ? resident_per_cu : 1);
   return (uint32_t)(want < cap ? (want > 0 ? want : 1) : cap);
 }
+
+template <class K>
+int resident_blocks(K kernel, int &cache) {
+  if (cache == 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kernel, kSpWaves * kWave, 0) !=
+            hipSuccess ||
+        nb <= 0)
+      nb = 4;
+    cache = nb;
+  }
+  return cache;
+}
+
+int g_count_resident = 0, g_fill_resident = 0;
 
 }  // namespace
 
@@ -393,25 +626,32 @@ uint32_t tr_blocks(uint32_t m, uint32_t q) {
   return (uint32_t)(nb > 0 ? nb : 1);
 }
 
-size_t transpose_workspace(uint32_t m, uint32_t q) {
+static size_t tr_table_bytes(uint32_t m, uint32_t q) {
   return align_up((size_t)tr_blocks(m, q) * q * sizeof(uint32_t), 256);
 }
+
+static size_t scan_bytes(uint32_t count) {
+  return align_up(((size_t)scan_tiles(count) + 1) * sizeof(uint64_t), 256);
+}
+
+size_t transpose_workspace(uint32_t m, uint32_t q) { return tr_table_bytes(m, q) + scan_bytes(q); }
+
+size_t matmul_workspace(uint32_t m) { return scan_bytes(m); }
 
 size_t dot_workspace() { return kDotBlocks * sizeof(double); }
 
 hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
-                               uint32_t *c_ptr, uint32_t *status, hipStream_t stream) {
+                               uint32_t *c_ptr, void *ws, uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
   if (m > 0) {
-    hipLaunchKernelGGL(spgemm_count_kernel, dim3(sp_blocks(m, dev)), dim3(kSpWaves * kWave), 0,
+    const uint32_t nb = sp_blocks(m, dev, resident_blocks(spgemm_count_kernel, g_count_resident));
+    hipLaunchKernelGGL(spgemm_count_kernel, dim3(nb), dim3(kSpWaves * kWave), 0,
                        stream, a, b, m, p, q, c_ptr + 1, status);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(1024), 0, stream, c_ptr, m,
-                     kFlagOutputTooLarge, status);
-  return hipGetLastError();
+  return launch_scan(c_ptr, m, static_cast<uint64_t *>(ws), status, stream);
 }
 
 hipError_t launch_spgemm_fill(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
@@ -421,7 +661,8 @@ hipError_t launch_spgemm_fill(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
   if (m == 0) return hipSuccess;
-  hipLaunchKernelGGL(spgemm_fill_kernel, dim3(sp_blocks(m, dev)), dim3(kSpWaves * kWave), 0,
+  const uint32_t nb = sp_blocks(m, dev, resident_blocks(spgemm_fill_kernel, g_fill_resident));
+  hipLaunchKernelGGL(spgemm_fill_kernel, dim3(nb), dim3(kSpWaves * kWave), 0,
                      stream, a, b, m, p, q, c_ptr, c_idx, c_val, status);
   return hipGetLastError();
 }
@@ -439,9 +680,8 @@ hipError_t launch_transpose(Csr a, uint32_t m, uint32_t q, uint32_t *at_ptr, uin
     hipLaunchKernelGGL(tr_colsum_kernel, dim3(cb), dim3(256), 0, stream, q, nb, table, at_ptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(scan_counts_kernel, dim3(1), dim3(1024), 0, stream, at_ptr, q,
-                     kFlagOutputTooLarge, status);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  uint64_t *part = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + tr_table_bytes(m, q));
+  if ((e = launch_scan(at_ptr, q, part, status, stream)) != hipSuccess) return e;
   if (q > 0) {
     hipLaunchKernelGGL(tr_base_kernel, dim3(cb), dim3(256), 0, stream, q, nb, table, at_ptr);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -26,7 +26,7 @@ FLAGS = {0x1: "CAP_OVERFLOW", 0x2: "PARTIALS_INVALID", 0x4: "B_CAP_OVERFLOW", 0x
 EXPORTS = ("seacells_fw_a_columns_workspace", "seacells_fw_a_columns",
            "seacells_fw_a_columns_pruned",
            "seacells_fw_b_argmin_workspace", "seacells_fw_b_argmin", "seacells_fw_b_apply",
-           "seacells_csr_matmul_rows", "seacells_csr_matmul_fill",
+           "seacells_csr_matmul_workspace", "seacells_csr_matmul_rows", "seacells_csr_matmul_fill",
            "seacells_csr_transpose_workspace", "seacells_csr_transpose",
            "seacells_csr_dot_workspace", "seacells_csr_dot",
            "seacells_status_string", "seacells_last_error", "seacells_version")
@@ -79,8 +79,10 @@ def load():
     lib.seacells_fw_b_apply.restype = ctypes.c_int
     lib.seacells_fw_b_apply.argtypes = [_VP, _VP, _VP, _U32, _U32, _U32, _VP, ctypes.c_float,
                                         _VP, _VP]
+    lib.seacells_csr_matmul_workspace.restype = ctypes.c_size_t
+    lib.seacells_csr_matmul_workspace.argtypes = [_U32]
     lib.seacells_csr_matmul_rows.restype = ctypes.c_int
-    lib.seacells_csr_matmul_rows.argtypes = [_CSR_P, _CSR_P, _VP, _VP, _VP]
+    lib.seacells_csr_matmul_rows.argtypes = [_CSR_P, _CSR_P, _VP, _VP, ctypes.c_size_t, _VP, _VP]
     lib.seacells_csr_matmul_fill.restype = ctypes.c_int
     lib.seacells_csr_matmul_fill.argtypes = [_CSR_P, _CSR_P, _VP, _VP, _VP, _VP, _VP]
     lib.seacells_csr_transpose_workspace.restype = ctypes.c_size_t
@@ -292,8 +294,12 @@ def seacells_fw_b_apply(bt_idx, bt_val, bt_cnt, n: int, arg_idx, gamma: float, s
 # sparse operations (include/seacells_sparse.h)
 # --------------------------------------------------------------------------
 
-def seacells_csr_matmul_rows(a: DeviceCSR, b: DeviceCSR, c_row_ptr=None, status=None,
-                             stream=None):
+def seacells_csr_matmul_workspace(m: int) -> int:
+    return int(load().seacells_csr_matmul_workspace(m))
+
+
+def seacells_csr_matmul_rows(a: DeviceCSR, b: DeviceCSR, c_row_ptr=None, workspace=None,
+                             status=None, stream=None):
     """Row pointer of a @ b ([m + 1] int32, last entry = nnz). Returns (c_row_ptr, status)."""
     lib = load()
     dev = a.row_ptr.device
@@ -301,9 +307,13 @@ def seacells_csr_matmul_rows(a: DeviceCSR, b: DeviceCSR, c_row_ptr=None, status=
         c_row_ptr = torch.empty(a.shape[0] + 1, dtype=torch.int32, device=dev)
     if status is None:
         status = new_status(dev)
+    if workspace is None:
+        workspace = torch.empty(seacells_csr_matmul_workspace(a.shape[0]), dtype=torch.uint8,
+                                device=dev)
     sa, sb = a.struct(), b.struct()
     rc = lib.seacells_csr_matmul_rows(ctypes.byref(sa), ctypes.byref(sb), _ptr(c_row_ptr),
-                                      _ptr(status), _stream(stream))
+                                      _ptr(workspace), workspace.numel(), _ptr(status),
+                                      _stream(stream))
     _check_rc(rc)
     return c_row_ptr, status
 

@@ -167,14 +167,22 @@ def test_sparse_ops_reject_bad_arguments_on_host():
     a, b = csr(5, 7, 3), csr(7, 4, 2)
     st, out = 0x9000, 0x4000
     # product: nulls, inner-dimension mismatch, too many entries
-    assert lib.seacells_csr_matmul_rows(None, P(b), out, st, None) == -1
-    assert lib.seacells_csr_matmul_rows(P(a), P(b), None, st, None) == -1
-    assert lib.seacells_csr_matmul_rows(P(a), P(b), out, None, None) == -1
-    assert lib.seacells_csr_matmul_rows(P(a), P(csr(6, 4, 2)), out, st, None) == -2
+    mneed = lib.seacells_csr_matmul_workspace(5)
+    assert mneed > 0 and mneed % 256 == 0
+    ws = 0x10000
+    assert lib.seacells_csr_matmul_rows(None, P(b), out, ws, mneed, st, None) == -1
+    assert lib.seacells_csr_matmul_rows(P(a), P(b), None, ws, mneed, st, None) == -1
+    assert lib.seacells_csr_matmul_rows(P(a), P(b), out, ws, mneed, None, None) == -1
+    assert lib.seacells_csr_matmul_rows(P(a), P(csr(6, 4, 2)), out, ws, mneed, st, None) == -2
+    assert lib.seacells_csr_matmul_rows(P(a), P(b), out, None, mneed, st, None) == -3
+    assert lib.seacells_csr_matmul_rows(P(a), P(b), out, ws, mneed - 1, st, None) == -3
+    assert lib.seacells_csr_matmul_rows(P(a), P(b), out, ws + 4, mneed, st, None) == -3
     assert lib.seacells_csr_matmul_fill(P(a), P(csr(6, 4, 2)), out, out, out, st, None) == -2
     assert lib.seacells_csr_matmul_fill(P(a), P(b), None, out, out, st, None) == -1
-    assert lib.seacells_csr_matmul_rows(P(csr(5, 7, 2 ** 31)), P(b), out, st, None) == -4
-    assert lib.seacells_csr_matmul_rows(P(csr(5, 7, 3, ptr=None)), P(b), out, st, None) == -1
+    assert lib.seacells_csr_matmul_rows(P(csr(5, 7, 2 ** 31)), P(b), out, ws, mneed, st,
+                                        None) == -4
+    assert lib.seacells_csr_matmul_rows(P(csr(5, 7, 3, ptr=None)), P(b), out, ws, mneed, st,
+                                        None) == -1
     # transpose: nulls and workspace
     need = lib.seacells_csr_transpose_workspace(5, 7)
     assert need >= 7 * 4 and need % 256 == 0

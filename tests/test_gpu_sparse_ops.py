@@ -97,6 +97,21 @@ PRODUCT_CASES = {
 }
 
 
+def test_product_with_more_than_256_scan_tiles():
+    # 1.2M rows: the row-pointer scan runs over 293 tiles of 4096 counts
+    rng = np.random.default_rng(11)
+    m, p, q = 1_200_000, 5000, 300
+    nnz_a = 3 * m
+    rows = np.repeat(np.arange(m), 3)
+    cols = rng.integers(0, p, size=nnz_a)
+    a = sp.csr_matrix((rng.uniform(0.1, 1, nnz_a).astype(np.float32), (rows, cols)), shape=(m, p))
+    a.sum_duplicates()
+    a.sort_indices()
+    b = rand_csr(rng, p, q, 2, empty_every=3)
+    got = product_on_gpu(a, b)
+    check_product(got, S.matmul(a, b), what="1.2M rows")
+
+
 @pytest.mark.parametrize("case", sorted(PRODUCT_CASES))
 def test_product_matches_oracle(case):
     m, p, q, ra, rb, ex = PRODUCT_CASES[case]
