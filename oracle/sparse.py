@@ -120,18 +120,33 @@ def transpose(a) -> sp.csr_matrix:
     return out
 
 
+def _dots(x, y):
+    """(sum x * y, sum |x * y|) over the positions stored in both, in f64:
+    every position of the matrix with fewer entries is looked up among the
+    sorted positions of the other."""
+    if x.shape != y.shape:
+        raise ValueError("shapes differ")
+    X, Y = sp.csr_matrix(x), sp.csr_matrix(y)
+    if X.nnz < Y.nnz:
+        X, Y = Y, X
+    X.sort_indices()
+    Y.sort_indices()
+    kx, ky = _keys(X), _keys(Y)
+    at = np.searchsorted(kx, ky)
+    hit = at < kx.size
+    hit[hit] = kx[at[hit]] == ky[hit]
+    prod = X.data[at[hit]].astype(np.float64) * Y.data[hit].astype(np.float64)
+    return float(np.sum(prod)), float(np.sum(np.abs(prod)))
+
+
 def dot(x, y) -> float:
     """<X, Y> = sum over positions stored in both of x * y, in f64."""
-    X, Y = _f64(x), _f64(y)
-    if X.shape != Y.shape:
-        raise ValueError("shapes differ")
-    _, ix, iy = np.intersect1d(_keys(X), _keys(Y), assume_unique=True, return_indices=True)
-    return float(np.sum(X.data[ix] * Y.data[iy]))
+    return _dots(x, y)[0]
 
 
 def dot_abs(x, y) -> float:
     """sum |x * y| over the common positions (the scale of ``dot``'s rounding)."""
-    return dot(abs(_f64(x)), abs(_f64(y)))
+    return _dots(x, y)[1]
 
 
 @dataclass
@@ -178,3 +193,11 @@ def rss_scale(K, B, At) -> float:
     t1 = Bf.T @ k2b
     aat = Atf.T @ Atf
     return dot(Kf, Kf) + 2.0 * dot(k2b, Atf) + dot(t1, aat)
+
+
+def rss_of_operands(K, k2b, At, t1, aat):
+    """The same expansion evaluated on given operands K, K^2 B, A^T,
+    B^T K^2 B and A A^T (f64 sums): (value, scale), the scale as in
+    ``rss_scale``."""
+    (kk, kk_a), (ba, ba_a), (ta, ta_a) = _dots(K, K), _dots(k2b, At), _dots(t1, aat)
+    return kk - 2.0 * ba + ta, kk_a + 2.0 * ba_a + ta_a

@@ -9,6 +9,29 @@ def dev(m):
     return saa.DeviceCSR.from_scipy(m)
 
 
+def host(d, rows=None):
+    """A DeviceCSR back as a scipy CSR (f32 values, int64 indices); with
+    ``rows``, only those rows (copied slice by slice)."""
+    import scipy.sparse as sp
+    ptr = d.row_ptr.cpu().numpy().astype(np.int64)
+    if rows is None:
+        idx = d.col_idx.cpu().numpy().astype(np.int64)
+        val = d.val.cpu().numpy()
+        out = sp.csr_matrix((val, idx, ptr), shape=d.shape)
+    else:
+        rows = np.asarray(rows, np.int64)
+        lo, hi = ptr[rows], ptr[rows + 1]
+        idx = [d.col_idx[a:b].cpu().numpy().astype(np.int64) for a, b in zip(lo, hi)]
+        val = [d.val[a:b].cpu().numpy() for a, b in zip(lo, hi)]
+        p = np.zeros(rows.size + 1, np.int64)
+        np.cumsum(hi - lo, out=p[1:])
+        out = sp.csr_matrix((np.concatenate(val) if val else np.zeros(0, np.float32),
+                             np.concatenate(idx) if idx else np.zeros(0, np.int64), p),
+                            shape=(rows.size, d.shape[1]))
+    out.has_sorted_indices = True
+    return out
+
+
 def run_a(w, T=None, cap=None, gamma=None, trace=True, ops=None, prune=None, gap_out=None):
     """A update on the GPU; the five outputs as numpy. ``gap_out`` (a list)
     receives the per-cell Frank-Wolfe gap when given."""

@@ -198,3 +198,27 @@ def check_b(w, out_val, out_idx, gap, n=None, k=None, b=True, res=None, fw_gap=N
             "fw_gap %.9g vs oracle %.9g" % (float(fw_gap), res.fw_gap)
     return BReport(int(exact.sum()), int((~exact).sum()),
                    float(np.max(dv / np.maximum(np.abs(res.val), 1e-30))), grel)
+
+
+# --------------------------------------------------------------------------
+# sparse products (device operand construction)
+# --------------------------------------------------------------------------
+
+U32 = 2.0 ** -24  # unit roundoff of f32
+
+
+def check_product(got, want, extra_terms=0, what=""):
+    """A device product against oracle.sparse.matmul's: the stored pattern
+    bit-exact, and every value within the bound of an f32 sum of t fused
+    multiply-adds, 1.01 t 2^-24 sum|a b| (t = the entry's number of products
+    plus ``extra_terms`` for the rounding a chained factor carries). Returns
+    the largest error relative to sum|a b|."""
+    assert got.shape == want.shape, what
+    assert np.array_equal(got.indptr, want.indptr), what
+    assert np.array_equal(got.indices, want.indices), what
+    tol = 1.01 * (want.terms + extra_terms) * U32 * want.abs_value
+    err = np.abs(got.data.astype(np.float64) - want.value)
+    bad = np.flatnonzero(err > tol)
+    assert bad.size == 0, "%s: %d entries out of bound, first %s: got %r want %r tol %r" % (
+        what, bad.size, bad[:3], got.data[bad[:3]], want.value[bad[:3]], tol[bad[:3]])
+    return float((err / np.maximum(want.abs_value, 1e-300)).max()) if err.size else 0.0

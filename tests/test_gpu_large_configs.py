@@ -14,10 +14,14 @@ import sys
 
 import numpy as np
 import pytest
+import scipy.sparse as sp
+import torch
 
+import sparse_archetypal_analysis_amd as saa
 import workloads as W
+from oracle import sparse as S
 from tests import parity
-from tests.gpu_run import dev, run_a, run_b
+from tests.gpu_run import dev, host, run_a, run_b
 
 pytestmark = pytest.mark.gpu
 
@@ -76,3 +80,78 @@ def test_b_argmin_all_columns(big):
     assert flags == []
     rep = parity.check_b(w, v, i, g, fw_gap=gl[0])
     print("\n%s: %s" % (name, rep))
+
+
+def _place_rows(prod, rows, n):
+    """An n-row CSR holding the oracle rows ``prod`` at positions ``rows``
+    (ascending) and nothing elsewhere."""
+    counts = np.zeros(n, np.int64)
+    counts[rows] = np.diff(prod.indptr)
+    ptr = np.zeros(n + 1, np.int64)
+    np.cumsum(counts, out=ptr[1:])
+    return sp.csr_matrix((prod.value, prod.indices, ptr), shape=(n, prod.shape[1]))
+
+
+def _chain_rows(K, X, rows):
+    """Rows ``rows`` (ascending) of K (K X) by the oracle: the rows of K X
+    that K's rows reach, then the product with them. Returns the product and
+    the most terms in a first-level sum."""
+    nb = np.unique(K[rows].indices)
+    first = S.matmul_rows(K, X, nb)
+    second = S.matmul_rows(K, _place_rows(first, nb, K.shape[0]), rows)
+    return second, int(first.terms.max()) if first.terms.size else 0
+
+
+def test_device_operands_full_size(big):
+    name, w, _ = big
+    K = W.kernel_matrix(w)
+    st = saa.new_status()
+    dK, dAt = dev(K), dev(w.a_prev_t)
+    ops = saa.device_operands(dK, dev(w.b), dAt, status=st)
+    acc, _ = saa.rss(dK, ops["k2b"], dAt, ops["t1"], ops["aat"], status=st)
+    torch.cuda.synchronize()
+    assert saa.status_flags(st) == []
+    _log("%s: device operands built" % name)
+    # every entry against the generator's operands (f64 products of the f64
+    # kernel, rounded to f32; t1 and A A^T symmetrised)
+    for nm in ("k2b", "t1", "aat", "k2at"):
+        ref, d = getattr(w, nm), ops[nm]
+        assert d.nnz == ref.nnz, nm
+        assert torch.equal(d.row_ptr.cpu(), torch.from_numpy(ref.indptr.astype(np.int32))), nm
+        assert torch.equal(d.col_idx, torch.from_numpy(ref.indices.astype(np.int32)).cuda()), nm
+        rv = torch.from_numpy(ref.data).cuda().double()
+        rel = ((d.val.double() - rv).abs() / rv.abs()).max().item()
+        del rv
+        assert rel <= 2e-5, (nm, rel)
+    _log("%s: generator operands matched" % name)
+    # sampled rows against the oracle
+    rng = np.random.default_rng(40 if name == "c4" else 50)
+    rows = np.unique(np.concatenate([[0, w.n - 1], rng.choice(w.n, size=100, replace=False)]))
+    parity.check_product(host(ops["kb"], rows), S.matmul_rows(K, w.b, rows), what="K B")
+    parity.check_product(host(ops["kat"], rows), S.matmul_rows(K, w.a_prev_t, rows),
+                         what="K A^T")
+    want, l1 = _chain_rows(K, w.b, rows)
+    parity.check_product(host(ops["k2b"], rows), want, extra_terms=l1 + 1, what="K^2 B")
+    want, l1 = _chain_rows(K, w.a_prev_t, rows)
+    parity.check_product(host(ops["k2at"], rows), want, extra_terms=l1 + 1, what="K^2 A^T")
+    arch = np.unique(np.concatenate([[0, w.k - 1], rng.choice(w.k, size=30, replace=False)]))
+    bt = S.transpose(w.b)
+    cells = np.unique(bt[arch].indices)
+    k2b_cells, l1 = _chain_rows(K, w.b, cells)
+    t1_rows = S.matmul(bt[arch], _place_rows(k2b_cells, cells, w.n))
+    l2 = int(k2b_cells.terms.max()) if k2b_cells.terms.size else 0
+    parity.check_product(host(ops["t1"], arch), t1_rows, extra_terms=l1 + l2 + 2, what="t1")
+    a = S.transpose(w.a_prev_t)
+    parity.check_product(host(ops["aat"], arch), S.matmul_rows(a, w.a_prev_t, arch),
+                         what="A A^T")
+    # transposes bit for bit
+    for nm, ref in (("bt", bt), ("a", a)):
+        got = host(ops[nm])
+        assert np.array_equal(got.indptr, ref.indptr) and np.array_equal(got.indices, ref.indices)
+        assert np.array_equal(got.data.view(np.uint32), ref.data.astype(np.float32).view(np.uint32))
+    _log("%s: sampled rows matched" % name)
+    # RSS: the expansion on the generator's operands
+    val, scale = S.rss_of_operands(K, w.k2b, w.a_prev_t, w.t1, w.aat)
+    assert abs(float(acc.item()) - val) <= 1e-5 * scale, (float(acc.item()), val, scale)
+    print("\n%s: rss %.6e (oracle on generator operands %.6e, scale %.3e)" % (
+        name, float(acc.item()), val, scale))

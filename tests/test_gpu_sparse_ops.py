@@ -24,34 +24,10 @@ import torch
 import sparse_archetypal_analysis_amd as saa
 from oracle import sparse as S
 import workloads as W
-from tests.gpu_run import dev
+from tests.gpu_run import dev, host
+from tests.parity import check_product
 
 pytestmark = pytest.mark.gpu
-
-U = 2.0 ** -24
-
-
-def host(d: saa.DeviceCSR) -> sp.csr_matrix:
-    ptr = d.row_ptr.cpu().numpy().astype(np.int64)
-    idx = d.col_idx.cpu().numpy().astype(np.int64)
-    val = d.val.cpu().numpy()
-    out = sp.csr_matrix((val, idx, ptr), shape=d.shape)
-    out.has_sorted_indices = True
-    return out
-
-
-def check_product(got: sp.csr_matrix, want: S.Product, extra_terms=0, abs_value=None, what=""):
-    """Pattern bit-exact, values within the summation bound."""
-    assert got.shape == want.shape, what
-    assert np.array_equal(got.indptr, want.indptr), what
-    assert np.array_equal(got.indices, want.indices), what
-    scale = want.abs_value if abs_value is None else abs_value
-    tol = 1.01 * (want.terms + extra_terms) * U * scale
-    err = np.abs(got.data.astype(np.float64) - want.value)
-    bad = np.flatnonzero(err > tol)
-    assert bad.size == 0, "%s: %d entries out of bound, first %s: got %r want %r tol %r" % (
-        what, bad.size, bad[:3], got.data[bad[:3]], want.value[bad[:3]], tol[bad[:3]])
-    return float((err / np.maximum(scale, 1e-300)).max()) if err.size else 0.0
 
 
 def rand_csr(rng, m, q, per_row, signed=True, zeros=0.05, empty_every=0, dense_rows=()):

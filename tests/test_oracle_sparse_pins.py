@@ -180,6 +180,18 @@ def test_rss_equals_brute_force_objective(seed):
     assert S.rss(K, B, At) > 0
 
 
+def test_rss_of_operands_equals_brute_force():
+    rng = np.random.default_rng(31)
+    K, B, At = random_problem(rng, 25, 4)
+    Kd, Bd, Ad = K.toarray(), B.toarray(), At.toarray().T
+    k2b = sp.csr_matrix(Kd @ Kd @ Bd)
+    t1 = sp.csr_matrix(Bd.T @ Kd @ Kd @ Bd)
+    aat = sp.csr_matrix(Ad @ Ad.T)
+    val, scale = S.rss_of_operands(K, k2b, At, t1, aat)
+    assert abs(val - dense.objective(Kd, Bd, Ad)) <= 1e-12 * scale
+    assert abs(scale - S.rss_scale(K, B, At)) <= 1e-12 * scale
+
+
 def test_rss_closed_forms():
     n = 6
     K = sp.identity(n, format="csr")
