@@ -10,6 +10,10 @@ events on the library's stream), and the f64 CPU oracle timed on a bounded
 sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config c5] [--gpus 1] [--prune THR]
+                    [--no-operands] [--no-cpu-baseline]
+
+After the timed steps it also times the device construction of the
+operands from K, B and A^T ("operands": whole build and per step).
 
 The default workload is the largest single-GPU configuration (n = 1M cells,
 k = 10000 archetypes); --config c1 .. c4 selects the smaller ones. --prune
@@ -130,6 +134,71 @@ def cpu_baseline(w, budget_s=12.0):
             "a_cells_per_s": rate_a, "b_cells_per_s": rate_b}
 
 
+def time_operands(saa, W, w, stream, reps=3):
+    """The operand construction on the device (K^2 B, t1, A A^T, K^2 A^T and
+    the RSS from K, B and A^T): wall time of the whole build (one host
+    synchronisation per product sizes its output) and the device time of each
+    step from HIP events, outputs preallocated. For every product, the number
+    of multiply-adds and the gathered bytes they imply (each product reads its
+    B entry's column three times and its value once: 16 B)."""
+    import torch
+    D = saa.DeviceCSR.from_scipy
+    K = W.kernel_matrix(w)
+    dK, dB, dAt = D(K), D(w.b), D(w.a_prev_t)
+    st = saa.new_status()
+    ops = saa.device_operands(dK, dB, dAt, status=st)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        saa.device_operands(dK, dB, dAt, status=st)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1000.0 / reps
+
+    def dev_ms(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def n_products(a, b):
+        cols = a.col_idx.cpu().numpy()
+        lens = np.diff(b.row_ptr.cpu().numpy().astype(np.int64))
+        return int(np.dot(np.bincount(cols, minlength=a.shape[1]).astype(np.int64), lens))
+
+    res = {}
+    plan = (("kb = K B", "kb", dK, dB), ("k2b = K kb", "k2b", dK, ops["kb"]),
+            ("t1 = B^T k2b", "t1", ops["bt"], ops["k2b"]), ("aat = A A^T", "aat", ops["a"], dAt),
+            ("kat = K A^T", "kat", dK, dAt), ("k2at = K kat", "k2at", dK, ops["kat"]))
+    ws = torch.empty(saa.seacells_csr_matmul_workspace(max(K.shape[0], w.k)), dtype=torch.uint8,
+                     device="cuda")
+    for label, nm, a, b in plan:
+        c = ops[nm]
+
+        def prod(a=a, b=b, c=c):
+            saa.seacells_csr_matmul_rows(a, b, c.row_ptr, workspace=ws, status=st, stream=stream)
+            saa.seacells_csr_matmul_fill(a, b, c.row_ptr, c.col_idx, c.val, status=st,
+                                         stream=stream)
+        ms = dev_ms(prod)
+        npr = n_products(a, b)
+        res[label] = {"ms": ms, "nnz": c.nnz, "products": npr,
+                      "gather_gbps": 16.0 * npr / (ms * 1e-3) / 1e9}
+    for label, src, nm in (("bt = B^T", dB, "bt"), ("a = (A^T)^T", dAt, "a")):
+        t = ops[nm]
+        res[label] = {"ms": dev_ms(lambda src=src, t=t: saa.seacells_csr_transpose(
+            src, t.row_ptr, t.col_idx, t.val, status=st, stream=stream)), "nnz": t.nnz}
+    acc = torch.zeros(1, dtype=torch.float64, device="cuda")
+    res["rss"] = {"ms": dev_ms(lambda: saa.rss(dK, ops["k2b"], dAt, ops["t1"], ops["aat"],
+                                               acc=acc, status=st, stream=stream))}
+    saa.raise_on_status(st)
+    return {"ms_total": wall_ms, "device_ms_sum": float(sum(v["ms"] for v in res.values())),
+            "nnz_K": int(K.nnz), "steps": res,
+            "note": "ms_total includes one host synchronisation per product (output sizing)"}
+
+
 def copy_calibration(mib):
     """A plain elementwise copy of known size: it reads and writes exactly
     mib MiB per launch, so FETCH_SIZE / WRITE_SIZE of this kernel give the
@@ -152,6 +221,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-operands", action="store_true",
+                    help="skip timing the device operand construction")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--prune", type=float, default=None, metavar="THR",
                     help="time the A update's pruning variant with threshold THR")
@@ -286,6 +357,8 @@ def main():
         "generation_s": t_gen,
         "device": torch.cuda.get_device_name(dev),
     }
+    if not args.no_operands:
+        rec["operands"] = time_operands(saa, W, w, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)

@@ -53,7 +53,9 @@ size_t seacells_csr_matmul_workspace(uint32_t m);
  *            c_row_ptr[m] = nnz(C), for the caller to size c_col_idx and
  *            c_val (read it after the stream synchronises). Row i holds every
  *            column some product a[i, j] b[j, c] reaches, so a sum that cancels
- *            to 0 stays as an explicit 0 (the page's host product drops it).
+ *            to 0 stays as an explicit 0 (the page does not say whether its
+ *            host product keeps such zeros; with non-negative K, B and A no sum
+ *            cancels, so the operands are the same either way).
  * SEACELLS_FLAG_OUTPUT_TOO_LARGE when nnz(C) would reach 2^31 (c_row_ptr
  * is then not valid); BAD_INDEX for malformed rows or columns (skipped).
  */
@@ -90,7 +92,8 @@ int seacells_csr_transpose(const seacells_csr *a, uint32_t *at_row_ptr, uint32_t
 size_t seacells_csr_dot_workspace(void);
 
 /*
- * Inner product of two matrices of the same shape, accumulated:
+ * Inner product of two matrices of the same shape, accumulated (the operand
+ * with fewer entries is walked, the other searched):
  *     *acc += alpha * sum_{i, c} x[i, c] y[i, c]
  * acc  device [1] f64 (in/out). Products and sums in f64; rows are summed
  * in a fixed order. With K, K^2 B, A^T, t1 and A A^T, three calls into one

@@ -24,8 +24,9 @@
 //   positions, and each wave writes its rows in order, so a transposed row
 //   lists the original rows in ascending order (no atomics on positions).
 // Inner product <X, Y> over two matrices of the same shape: one wave per row
-//   looks each X entry up in Y's row (binary search), products in f64; the
-//   rows' partial sums are added in a fixed order.
+//   looks each entry of the operand with fewer entries up in the other's row
+//   (binary search), products in f64; the rows' partial sums are added in a
+//   fixed order.
 #include "common.hpp"
 
 namespace seacells {
@@ -693,6 +694,12 @@ hipError_t launch_transpose(Csr a, uint32_t m, uint32_t q, uint32_t *at_ptr, uin
 
 hipError_t launch_dot(Csr x, Csr y, uint32_t m, double alpha, double *acc, void *ws,
                       uint32_t *status, hipStream_t stream) {
+  // <X, Y> = <Y, X>: walk the operand with fewer entries, search the other
+  if (x.nnz > y.nnz) {
+    const Csr t = x;
+    x = y;
+    y = t;
+  }
   double *part = static_cast<double *>(ws);
   hipLaunchKernelGGL(dot_rows_kernel, dim3(kDotBlocks), dim3(256), 0, stream, x, y, m, part,
                      status);

@@ -31,6 +31,13 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, nm), nm
 
 
+def test_package_exports_every_wrapped_entry_point():
+    wrapped = [nm for nm in native.EXPORTS if hasattr(native, nm)]
+    assert len(wrapped) >= len(native.EXPORTS) - 3  # status/error/version have no wrapper
+    for nm in wrapped:
+        assert hasattr(saa, nm), nm
+
+
 def test_version_and_status_strings():
     lib = saa.load()
     assert lib.seacells_version() >> 16 == 1
