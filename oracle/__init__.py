@@ -3,8 +3,9 @@
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this package. The HIP library
 never calls it, and the two share no code: this package is C compiled with
-gcc (``seacells_oracle.c``) plus dense numpy (``dense.py``) and scipy sparse
-products (``sparse.py``, the operand construction and the RSS), all written
+gcc (``seacells_oracle.c``) plus dense numpy (``dense.py``), scipy sparse
+products (``sparse.py``: the operand construction, sparse add, the RSS) and
+the B update as a loop of Frank-Wolfe steps (``b_loop.py``), all written
 from the method as the source page states it (bixverse-rs 0.6.4,
 ``seacells_kernels.rs``: the module doc, the ``fw_columns_a_gpu`` and
 ``fw_argmin_b`` docs and the ``cpu_fw_argmin_b`` test reference).

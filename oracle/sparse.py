@@ -201,3 +201,31 @@ def rss_of_operands(K, k2b, At, t1, aat):
     ``rss_scale``."""
     (kk, kk_a), (ba, ba_a), (ta, ta_a) = _dots(K, K), _dots(k2b, At), _dots(t1, aat)
     return kk - 2.0 * ba + ta, kk_a + 2.0 * ba_a + ta_a
+
+
+def add(alpha, x, beta, y) -> sp.csr_matrix:
+    """alpha X + beta Y in f64 (the page's ``sparse_add_csr``, named in its
+    ``lower_bound`` doc, merges two sorted rows): the pattern is the union of
+    the stored patterns (a position stored in either operand stays stored,
+    even where the sum is 0), the values are scipy's f64 sum placed on it."""
+    X, Y = _f64(x), _f64(y)
+    if X.shape != Y.shape:
+        raise ValueError("shapes differ")
+    pat = (_indicator(X) + _indicator(Y)).tocsr()
+    pat.sort_indices()
+    val = (float(alpha) * X + float(beta) * Y).tocsr()
+    val.sort_indices()
+    out = sp.csr_matrix((_on_pattern(pat, val), pat.indices.copy(), pat.indptr.copy()),
+                        shape=X.shape)
+    out.has_sorted_indices = True
+    return out
+
+
+def picks(idx, n: int, value: float = 1.0) -> sp.csr_matrix:
+    """The n x k matrix holding ``value`` at (idx[c], c) for every column c
+    (a Frank-Wolfe vertex of the column-stochastic B when value is 1)."""
+    idx = np.asarray(idx, np.int64)
+    k = idx.shape[0]
+    out = sp.csr_matrix((np.full(k, float(value)), (idx, np.arange(k))), shape=(n, k))
+    out.sort_indices()
+    return out

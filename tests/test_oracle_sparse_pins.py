@@ -224,3 +224,148 @@ def test_operands_match_the_generators_products():
         assert rel.max() <= 2e-6, (nm, rel.max())
     assert np.array_equal(ops.bt.toarray(), w.b.toarray().T)
     assert np.array_equal(ops.a.toarray(), w.a_prev_t.toarray().T)
+
+
+# --------------------------------------------------------------------------
+# sparse add and the vertex matrix
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_add_equals_brute_force(seed):
+    rng = np.random.default_rng(60 + seed)
+    x = rand_csr(rng, 11, 9, 0.3, empty_rows=(3,))
+    y = rand_csr(rng, 11, 9, 0.3, empty_rows=(3, 5))
+    alpha, beta = 0.75, -1.5
+    got = S.add(alpha, x, beta, y)
+    want = {}
+    for m, coef in ((x, alpha), (y, beta)):
+        for i in range(m.shape[0]):
+            for e in range(m.indptr[i], m.indptr[i + 1]):
+                key = (i, int(m.indices[e]))
+                want[key] = want.get(key, 0.0) + coef * float(m.data[e])
+    seen = {}
+    for i in range(11):
+        cols = got.indices[got.indptr[i]:got.indptr[i + 1]]
+        assert np.all(np.diff(cols) > 0)
+        for e in range(got.indptr[i], got.indptr[i + 1]):
+            seen[(i, int(got.indices[e]))] = float(got.data[e])
+    assert seen.keys() == want.keys()  # union of the stored patterns, zeros included
+    for key, v in want.items():
+        assert abs(seen[key] - v) <= 1e-15
+    np.testing.assert_allclose(got.toarray(), alpha * x.toarray().astype(np.float64)
+                               + beta * y.toarray().astype(np.float64),
+                               rtol=0, atol=1e-15)
+    # a cancelling sum stays stored
+    c = S.add(1.0, sp.csr_matrix(np.array([[2.0, 0.0]])), 1.0, sp.csr_matrix(np.array([[-2.0, 1.0]])))
+    assert c.nnz == 2 and list(c.data) == [0.0, 1.0]
+
+
+def test_picks_is_the_vertex_matrix():
+    idx = np.array([3, 0, 3, 2])
+    P = S.picks(idx, 5, 0.25)
+    d = np.zeros((5, 4))
+    d[idx, np.arange(4)] = 0.25
+    np.testing.assert_array_equal(P.toarray(), d)
+    assert P.nnz == 4 and list(P.indices[P.indptr[3]:P.indptr[4]]) == [0, 2]
+
+
+# --------------------------------------------------------------------------
+# the B loop
+# --------------------------------------------------------------------------
+
+from oracle import b_loop as BL  # noqa: E402
+
+
+def loop_problem(rng, n, k):
+    K, B, At = random_problem(rng, n, k)
+    Kd, Bd, Ad = K.toarray(), B.toarray(), At.toarray().T
+    aat = Ad @ Ad.T
+    k2at = Kd @ Kd @ Ad.T
+    return K, B, Ad, sp.csr_matrix(aat), sp.csr_matrix(k2at)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_b_loop_gradient_is_half_the_objective_gradient(seed):
+    rng = np.random.default_rng(70 + seed)
+    n, k = 7, 3
+    K, B, Ad, aat, k2at = loop_problem(rng, n, k)
+    grad = dense.grad_b(K.toarray(), B.toarray(), Ad)  # 2 (K^2 B AA^T - K^2 A^T)
+    for r in range(n):
+        res = BL.fw_b_loop(K, B, aat, k2at, 1, force=np.full((1, k), r))
+        np.testing.assert_allclose(res.g_used[0], grad[r] / 2.0, rtol=0, atol=1e-12)
+    res = BL.fw_b_loop(K, B, aat, k2at, 1)
+    np.testing.assert_array_equal(res.pick[0], np.argmin(grad, axis=0))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_b_loop_direction_derivative_of_the_objective(seed):
+    # f(B) = ||K - K B A||^2 is quadratic in B: the central difference along
+    # the Frank-Wolfe direction S - B is exact up to rounding and equals
+    # 2 <G, S - B> = 2 (sum_c min_i G[i, c] - sum B * G)
+    rng = np.random.default_rng(80 + seed)
+    n, k = 8, 3
+    K, B, Ad, aat, k2at = loop_problem(rng, n, k)
+    res = BL.fw_b_loop(K, B, aat, k2at, 1)
+    Kd, Bd = K.toarray(), B.toarray()
+    Sv = np.zeros((n, k))
+    Sv[res.pick[0], np.arange(k)] = 1.0
+    d = Sv - Bd
+    eps = 1e-3
+    fd = (dense.objective(Kd, Bd + eps * d, Ad) - dense.objective(Kd, Bd - eps * d, Ad)) / (2 * eps)
+    want = 2.0 * (res.gmin[0].sum() - res.gap[0])
+    assert abs(fd - want) <= 1e-8 * max(1.0, abs(want))
+    assert want <= 0.0  # a descent direction (the vertex minimises the linear model)
+
+
+def test_b_loop_step_weights_closed_form():
+    # with gamma_t = 2/(t+2), B_T = sum_t 2(t+1)/(T(T+1)) S(used_t), whatever B_0
+    rng = np.random.default_rng(90)
+    n, k, T = 9, 4, 7
+    K, B, Ad, aat, k2at = loop_problem(rng, n, k)
+    res = BL.fw_b_loop(K, B, aat, k2at, T)
+    want = np.zeros((n, k))
+    for t in range(T):
+        want[res.used[t], np.arange(k)] += 2.0 * (t + 1) / (T * (T + 1))
+    np.testing.assert_allclose(res.b, want, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(res.b.sum(axis=0), 1.0, rtol=0, atol=1e-14)
+    Kd = K.toarray()
+    np.testing.assert_allclose(res.k2b, Kd @ Kd @ res.b, rtol=0, atol=1e-12)
+    # replaying its own picks reproduces the run
+    rep = BL.fw_b_loop(K, B, aat, k2at, T, force=res.pick)
+    np.testing.assert_array_equal(rep.b, res.b)
+    np.testing.assert_array_equal(rep.g_used, res.gmin)
+
+
+def test_b_loop_identity_kernel_trajectory():
+    # K = I, A = 1/2 everywhere (n = 4, k = 2): A A^T = 1, K^2 A^T = 1/2, so
+    # G[i, c] = (row sum of B at i) - 1/2 and every step picks the row with
+    # the smallest row sum, the lowest on a tie: 2, 0, 1, 3; then
+    # B_4 = (2/20, 4/20, 6/20, 8/20) on rows (2, 0, 1, 3) in both columns
+    n, k = 4, 2
+    K = sp.identity(n, format="csr")
+    B = np.zeros((n, k))
+    B[0, 0] = B[1, 1] = 1.0
+    A = np.full((k, n), 0.5)
+    res = BL.fw_b_loop(K, B, sp.csr_matrix(A @ A.T), sp.csr_matrix(A.T), 4)
+    assert res.pick.tolist() == [[2, 2], [0, 0], [1, 1], [3, 3]]
+    np.testing.assert_array_equal(res.gmin, np.full((4, 2), -0.5))
+    np.testing.assert_allclose(res.b, np.array([[0.2, 0.2], [0.3, 0.3], [0.1, 0.1], [0.4, 0.4]]),
+                               rtol=0, atol=1e-15)
+    # gap at step 0: sum(B * G) = 1 * (1 - 1/2) + 1 * (1 - 1/2) = 1
+    assert res.gap[0] == 1.0
+
+
+def test_b_loop_orientation_with_a_non_symmetric_middle_matrix():
+    # the page's G[i, c] = sum_m K^2B[i, m] t1[m, c] - K^2A^T[i, c] holds for
+    # any t1 (its own fixtures are not symmetric): brute-force loops
+    rng = np.random.default_rng(95)
+    n, k = 6, 3
+    K, B, Ad, _, k2at = loop_problem(rng, n, k)
+    mid = rng.uniform(-1, 1, size=(k, k))
+    Kd, Bd, T2 = K.toarray(), B.toarray(), k2at.toarray()
+    K2B = Kd @ Kd @ Bd
+    for r in range(n):
+        res = BL.fw_b_loop(K, B, sp.csr_matrix(mid), k2at, 1, force=np.full((1, k), r))
+        for c in range(k):
+            g = sum(K2B[r, m] * mid[m, c] for m in range(k)) - T2[r, c]
+            assert abs(res.g_used[0, c] - g) <= 1e-12
