@@ -104,6 +104,54 @@ int seacells_csr_dot(const seacells_csr *x, const seacells_csr *y, double alpha,
                      void *workspace, size_t workspace_bytes, uint32_t *status,
                      seacells_stream_t stream);
 
+/* Workspace bytes seacells_csr_add_rows needs for m rows (> 0). */
+size_t seacells_csr_add_workspace(uint32_t m);
+
+/*
+ * Sum C = alpha X + beta Y, step 1 of 2 (`sparse_add_csr` on the page, which
+ * merges two sorted rows): the row pointer of C. x and y have the same shape
+ * m x q (else SEACELLS_E_SHAPE) and nnz(x) + nnz(y) < 2^31. C's pattern is
+ * the union of the two stored patterns: a column stored in either row is
+ * stored, even where the sum is 0.
+ * c_row_ptr  device [m + 1] u32 out; c_row_ptr[m] = nnz(C).
+ * workspace: at least seacells_csr_add_workspace(m) bytes, 256-byte aligned.
+ * BAD_INDEX for malformed rows, columns >= q or rows not strictly ascending.
+ */
+int seacells_csr_add_rows(const seacells_csr *x, const seacells_csr *y, uint32_t *c_row_ptr,
+                          void *workspace, size_t workspace_bytes, uint32_t *status,
+                          seacells_stream_t stream);
+
+/*
+ * Sum C = alpha X + beta Y, step 2 of 2: columns (ascending) and values into
+ * c_col_idx and c_val (device, c_row_ptr[m] entries each). c_row_ptr must be
+ * seacells_csr_add_rows's output for the same x and y (else BAD_INDEX and no
+ * write beyond its row sizes). Each value is alpha x and beta y rounded to
+ * f32 separately, then their sum rounded (alpha x or beta y alone where only
+ * one operand stores the column).
+ */
+int seacells_csr_add_fill(float alpha, const seacells_csr *x, float beta, const seacells_csr *y,
+                          const uint32_t *c_row_ptr, uint32_t *c_col_idx, float *c_val,
+                          uint32_t *status, seacells_stream_t stream);
+
+/* Workspace bytes seacells_fw_b_vertex needs for k columns and n rows (> 0). */
+size_t seacells_fw_b_vertex_workspace(uint32_t k, uint32_t n);
+
+/*
+ * The Frank-Wolfe vertex of the B step: the n x k CSR matrix S holding
+ * `value` at (arg_idx[c], c) for every column c, where arg_idx [k] (device)
+ * is the B argmin's row per column (seacells_fw_b_argmin's out_idx). With
+ * it a B step is B <- (1 - gamma) B + gamma S (seacells_csr_add_* with value
+ * 1), and K^2 B follows as (1 - gamma) K^2 B + gamma K (K S) (two products
+ * and a sum), so a loop of B steps stays on the device.
+ * s_row_ptr [n + 1], s_col_idx [k], s_val [k] (device, out): every row's
+ * columns ascending. n >= 1 (else SEACELLS_E_SHAPE). workspace: at least
+ * seacells_fw_b_vertex_workspace(k, n) bytes, 256-byte aligned. A pick >= n
+ * is dropped and flagged BAD_INDEX.
+ */
+int seacells_fw_b_vertex(const uint32_t *arg_idx, uint32_t k, uint32_t n, float value,
+                         uint32_t *s_row_ptr, uint32_t *s_col_idx, float *s_val, void *workspace,
+                         size_t workspace_bytes, uint32_t *status, seacells_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

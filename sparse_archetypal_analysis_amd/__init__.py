@@ -12,4 +12,6 @@ from .native import (DeviceCSR, SeacellsError, load, new_status, raise_on_status
                      seacells_csr_matmul_fill, csr_matmul,
                      seacells_csr_transpose_workspace, seacells_csr_transpose,
                      seacells_csr_dot_workspace, seacells_csr_dot, rss, device_operands,
+                     seacells_csr_add_workspace, seacells_csr_add_rows, seacells_csr_add_fill,
+                     csr_add, seacells_fw_b_vertex_workspace, seacells_fw_b_vertex, fw_b_loop,
                      status_flags)

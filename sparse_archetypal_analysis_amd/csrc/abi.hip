@@ -276,6 +276,66 @@ int seacells_csr_dot(const seacells_csr *x, const seacells_csr *y, double alpha,
   return SEACELLS_OK;
 }
 
+size_t seacells_csr_add_workspace(uint32_t m) { return add_workspace(m); }
+
+int seacells_csr_add_rows(const seacells_csr *x, const seacells_csr *y, uint32_t *c_row_ptr,
+                          void *workspace, size_t workspace_bytes, uint32_t *status,
+                          seacells_stream_t stream) {
+  int rc;
+  if ((rc = check_any_csr(x)) != SEACELLS_OK || (rc = check_any_csr(y)) != SEACELLS_OK) return rc;
+  if (c_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
+  if (x->n_rows != y->n_rows || x->n_cols != y->n_cols) return SEACELLS_E_SHAPE;
+  if ((uint64_t)x->nnz + y->nnz >= 0x80000000ull) return SEACELLS_E_TOO_LARGE;
+  if (workspace == nullptr || workspace_bytes < add_workspace(x->n_rows) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SEACELLS_E_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_add_count(as_csr(x), as_csr(y), x->n_rows, x->n_cols, c_row_ptr, workspace, status, s);
+  if (e != hipSuccess) return hip_fail(e, "csr_add_rows launch");
+  return SEACELLS_OK;
+}
+
+int seacells_csr_add_fill(float alpha, const seacells_csr *x, float beta, const seacells_csr *y,
+                          const uint32_t *c_row_ptr, uint32_t *c_col_idx, float *c_val,
+                          uint32_t *status, seacells_stream_t stream) {
+  int rc;
+  if ((rc = check_any_csr(x)) != SEACELLS_OK || (rc = check_any_csr(y)) != SEACELLS_OK) return rc;
+  if (c_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
+  if ((x->nnz > 0 || y->nnz > 0) && (c_col_idx == nullptr || c_val == nullptr))
+    return SEACELLS_E_NULL;
+  if (x->n_rows != y->n_rows || x->n_cols != y->n_cols) return SEACELLS_E_SHAPE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_add_fill(alpha, as_csr(x), beta, as_csr(y), x->n_rows, c_row_ptr, c_col_idx, c_val,
+                      status, s);
+  if (e != hipSuccess) return hip_fail(e, "csr_add_fill launch");
+  return SEACELLS_OK;
+}
+
+size_t seacells_fw_b_vertex_workspace(uint32_t k, uint32_t n) { return vertex_workspace(k, n); }
+
+int seacells_fw_b_vertex(const uint32_t *arg_idx, uint32_t k, uint32_t n, float value,
+                         uint32_t *s_row_ptr, uint32_t *s_col_idx, float *s_val, void *workspace,
+                         size_t workspace_bytes, uint32_t *status, seacells_stream_t stream) {
+  if (s_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
+  if (k > 0 && (arg_idx == nullptr || s_col_idx == nullptr || s_val == nullptr))
+    return SEACELLS_E_NULL;
+  if (n == 0) return SEACELLS_E_SHAPE;
+  if (k >= 0x80000000u || n >= 0x80000000u) return SEACELLS_E_TOO_LARGE;
+  if (workspace == nullptr || workspace_bytes < vertex_workspace(k, n) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SEACELLS_E_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_vertex(arg_idx, k, n, value, s_row_ptr, s_col_idx, s_val, workspace, status, s);
+  if (e != hipSuccess) return hip_fail(e, "fw_b_vertex launch");
+  return SEACELLS_OK;
+}
+
 const char *seacells_status_string(int code) {
   switch (code) {
     case SEACELLS_OK:

@@ -181,6 +181,15 @@ hipError_t launch_status_clear(uint32_t *status, hipStream_t stream);
 uint32_t tr_blocks(uint32_t m, uint32_t q);
 size_t transpose_workspace(uint32_t m, uint32_t q);
 size_t matmul_workspace(uint32_t m);
+size_t add_workspace(uint32_t m);
+size_t vertex_workspace(uint32_t k, uint32_t n);
+hipError_t launch_add_count(Csr x, Csr y, uint32_t m, uint32_t q, uint32_t *c_ptr, void *ws,
+                            uint32_t *status, hipStream_t stream);
+hipError_t launch_add_fill(float alpha, Csr x, float beta, Csr y, uint32_t m, const uint32_t *c_ptr,
+                           uint32_t *c_idx, float *c_val, uint32_t *status, hipStream_t stream);
+hipError_t launch_vertex(const uint32_t *pick, uint32_t k, uint32_t n, float value, uint32_t *s_ptr,
+                         uint32_t *s_idx, float *s_val, void *ws, uint32_t *status,
+                         hipStream_t stream);
 size_t dot_workspace();
 hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
                                uint32_t *c_ptr, void *ws, uint32_t *status, hipStream_t stream);

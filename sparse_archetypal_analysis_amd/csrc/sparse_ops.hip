@@ -23,6 +23,14 @@
 //   entries per column, the counts become per-(block, column) write
 //   positions, and each wave writes its rows in order, so a transposed row
 //   lists the original rows in ascending order (no atomics on positions).
+// Sum C = alpha X + beta Y over the union of the two patterns (the page's
+//   `sparse_add_csr` merges two sorted rows): one wave per row; each entry's
+//   place in the merged row is its rank in its own row plus the number of
+//   smaller columns in the other row (a binary search) less the common
+//   columns below it (a scan of the matches), so the lanes write
+//   independently. A column stored in both is written once, from X's side.
+// The Frank-Wolfe vertex of the B step (1 at (pick of column c, c)) is the
+//   transpose of the k x n matrix with one entry per row.
 // Inner product <X, Y> over two matrices of the same shape: one wave per row
 //   looks each entry of the operand with fewer entries up in the other's row
 //   (binary search), products in f64; the rows' partial sums are added in a
@@ -540,6 +548,130 @@ __global__ void __launch_bounds__(kWave)
   }
 }
 
+// First position in idx[lo, hi) whose column is at least c.
+__device__ __forceinline__ uint32_t lower_bound_u32(const uint32_t *__restrict__ idx, uint32_t lo,
+                                                    uint32_t hi, uint32_t c) {
+  while (lo < hi) {
+    const uint32_t mid = lo + (hi - lo) / 2u;
+    if (idx[mid] < c)
+      lo = mid + 1u;
+    else
+      hi = mid;
+  }
+  return lo;
+}
+
+// A row's columns are below q and strictly ascending (flags otherwise).
+__device__ __forceinline__ uint32_t check_row(const Csr &a, uint32_t lo, uint32_t hi, uint32_t q,
+                                              uint32_t lane) {
+  uint32_t flags = 0;
+  for (uint32_t t = lo + lane; t < hi; t += kWave) {
+    const uint32_t c = a.idx[t];
+    if (c >= q || (t + 1u < hi && a.idx[t + 1u] <= c)) flags |= kFlagBadIndex;
+  }
+  return flags;
+}
+
+// Entries per row of X + Y into cnt[r] (the caller's row pointer + 1).
+__global__ void __launch_bounds__(kSpWaves * kWave)
+    csr_add_count_kernel(Csr x, Csr y, uint32_t m, uint32_t q, uint32_t *__restrict__ cnt,
+                         uint32_t *__restrict__ status) {
+  const uint32_t lane = lane_id();
+  const uint32_t wib = threadIdx.x / kWave;
+  uint32_t flags = 0;
+  for (uint32_t r = blockIdx.x * kSpWaves + wib; r < m; r += gridDim.x * kSpWaves) {
+    uint32_t x0, x1, y0, y1;
+    if (!sp_row(x, r, x0, x1) || !sp_row(y, r, y0, y1)) flags |= kFlagBadIndex;
+    flags |= check_row(x, x0, x1, q, lane) | check_row(y, y0, y1, q, lane);
+    // common columns: the shorter row's entries searched in the longer row
+    const bool xs = x1 - x0 <= y1 - y0;
+    const Csr &sm = xs ? x : y;
+    const Csr &lg = xs ? y : x;
+    const uint32_t s0 = xs ? x0 : y0, s1 = xs ? x1 : y1, l0 = xs ? y0 : x0, l1 = xs ? y1 : x1;
+    uint32_t common = 0;
+    for (uint32_t t = s0 + lane; t < s1; t += kWave) {
+      const uint32_t c = sm.idx[t];
+      const uint32_t pos = lower_bound_u32(lg.idx, l0, l1, c);
+      if (pos < l1 && lg.idx[pos] == c) ++common;
+    }
+    common = wave_sum_u32(common);
+    if (lane == 0) cnt[r] = (x1 - x0) + (y1 - y0) - common;
+  }
+  if (flags != 0) atomicOr(status, flags);
+}
+
+// Columns and values of alpha X + beta Y into the rows the count pass sized:
+// alpha x and beta y are each rounded to f32, then their sum (no fused form).
+__global__ void __launch_bounds__(kSpWaves * kWave)
+    csr_add_fill_kernel(float alpha, Csr x, float beta, Csr y, uint32_t m,
+                        const uint32_t *__restrict__ c_ptr, uint32_t *__restrict__ c_idx,
+                        float *__restrict__ c_val, uint32_t *__restrict__ status) {
+  const uint32_t lane = lane_id();
+  const uint32_t wib = threadIdx.x / kWave;
+  uint32_t flags = 0;
+  for (uint32_t r = blockIdx.x * kSpWaves + wib; r < m; r += gridDim.x * kSpWaves) {
+    const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
+    const uint32_t cnt = end >= base ? end - base : 0u;
+    uint32_t x0, x1, y0, y1;
+    if (!sp_row(x, r, x0, x1) || !sp_row(y, r, y0, y1)) flags |= kFlagBadIndex;
+    // place of an entry in the merged row: its rank in its own row, plus the
+    // columns below it in the other row, less the common columns below it
+    // (both rows ascending: the matched entries before it in its own row)
+    uint32_t common = 0;
+    for (uint32_t b = x0; b < x1; b += kWave) {
+      const uint32_t t = b + lane;
+      uint32_t p = y0;
+      bool both = false;
+      if (t < x1) {
+        p = lower_bound_u32(y.idx, y0, y1, x.idx[t]);
+        both = p < y1 && y.idx[p] == x.idx[t];
+      }
+      const uint32_t before = common + wave_excl_scan_u32(both ? 1u : 0u, lane);
+      common += wave_sum_u32(both ? 1u : 0u);
+      if (t < x1) {
+        const float ax = __fmul_rn(alpha, x.val[t]);
+        const float v = both ? __fadd_rn(ax, __fmul_rn(beta, y.val[p])) : ax;
+        const uint32_t pos = (t - x0) + (p - y0) - before;
+        if (pos < cnt) {
+          c_idx[(size_t)base + pos] = x.idx[t];
+          c_val[(size_t)base + pos] = v;
+        }
+      }
+    }
+    uint32_t common_y = 0;
+    for (uint32_t b = y0; b < y1; b += kWave) {
+      const uint32_t t = b + lane;
+      uint32_t p = x0;
+      bool both = false;
+      if (t < y1) {
+        p = lower_bound_u32(x.idx, x0, x1, y.idx[t]);
+        both = p < x1 && x.idx[p] == y.idx[t];
+      }
+      const uint32_t before = common_y + wave_excl_scan_u32(both ? 1u : 0u, lane);
+      common_y += wave_sum_u32(both ? 1u : 0u);
+      if (t < y1 && !both) {  // a column stored in both was written from X's side
+        const uint32_t pos = (t - y0) + (p - x0) - before;
+        if (pos < cnt) {
+          c_idx[(size_t)base + pos] = y.idx[t];
+          c_val[(size_t)base + pos] = __fmul_rn(beta, y.val[t]);
+        }
+      }
+    }
+    if ((x1 - x0) + (y1 - y0) - common != cnt || common_y != common)
+      flags |= kFlagBadIndex;  // not the count pass's pointers, or rows not ascending
+  }
+  if (flags != 0) atomicOr(status, flags);
+}
+
+// The k x n matrix with one entry per row (row c: column pick[c], value v):
+// its row pointer is 0 .. k and every value is v.
+__global__ void __launch_bounds__(256)
+    vertex_rows_kernel(uint32_t k, float v, uint32_t *__restrict__ ptr, float *__restrict__ val) {
+  const uint32_t c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c <= k) ptr[c] = c;
+  if (c < k) val[c] = v;
+}
+
 // <X, Y> row by row: each X entry is looked up in Y's (ascending) row.
 __global__ void __launch_bounds__(256)
     dot_rows_kernel(Csr x, Csr y, uint32_t m, double *__restrict__ part,
@@ -641,6 +773,13 @@ size_t matmul_workspace(uint32_t m) { return scan_bytes(m); }
 
 size_t dot_workspace() { return kDotBlocks * sizeof(double); }
 
+size_t add_workspace(uint32_t m) { return scan_bytes(m); }
+
+size_t vertex_workspace(uint32_t k, uint32_t n) {
+  return align_up(((size_t)k + 1) * sizeof(uint32_t), 256) + align_up((size_t)k * sizeof(float), 256) +
+         transpose_workspace(k, n);
+}
+
 hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
                                uint32_t *c_ptr, void *ws, uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
@@ -690,6 +829,50 @@ hipError_t launch_transpose(Csr a, uint32_t m, uint32_t q, uint32_t *at_ptr, uin
   hipLaunchKernelGGL(tr_fill_kernel, dim3(nb), dim3(kWave), 0, stream, a, m, q, nb, table,
                      at_idx, at_val);
   return hipGetLastError();
+}
+
+int g_add_count_resident = 0, g_add_fill_resident = 0;
+
+hipError_t launch_add_count(Csr x, Csr y, uint32_t m, uint32_t q, uint32_t *c_ptr, void *ws,
+                            uint32_t *status, hipStream_t stream) {
+  DeviceInfo dev;
+  hipError_t e = device_info(&dev);
+  if (e != hipSuccess) return e;
+  if (m > 0) {
+    const uint32_t nb = sp_blocks(m, dev, resident_blocks(csr_add_count_kernel, g_add_count_resident));
+    hipLaunchKernelGGL(csr_add_count_kernel, dim3(nb), dim3(kSpWaves * kWave), 0, stream, x, y, m,
+                       q, c_ptr + 1, status);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return launch_scan(c_ptr, m, static_cast<uint64_t *>(ws), status, stream);
+}
+
+hipError_t launch_add_fill(float alpha, Csr x, float beta, Csr y, uint32_t m, const uint32_t *c_ptr,
+                           uint32_t *c_idx, float *c_val, uint32_t *status, hipStream_t stream) {
+  DeviceInfo dev;
+  hipError_t e = device_info(&dev);
+  if (e != hipSuccess) return e;
+  if (m == 0) return hipSuccess;
+  const uint32_t nb = sp_blocks(m, dev, resident_blocks(csr_add_fill_kernel, g_add_fill_resident));
+  hipLaunchKernelGGL(csr_add_fill_kernel, dim3(nb), dim3(kSpWaves * kWave), 0, stream, alpha, x,
+                     beta, y, m, c_ptr, c_idx, c_val, status);
+  return hipGetLastError();
+}
+
+hipError_t launch_vertex(const uint32_t *pick, uint32_t k, uint32_t n, float value, uint32_t *s_ptr,
+                         uint32_t *s_idx, float *s_val, void *ws, uint32_t *status,
+                         hipStream_t stream) {
+  char *w = static_cast<char *>(ws);
+  uint32_t *ptr = reinterpret_cast<uint32_t *>(w);
+  w += align_up(((size_t)k + 1) * sizeof(uint32_t), 256);
+  float *val = reinterpret_cast<float *>(w);
+  w += align_up((size_t)k * sizeof(float), 256);
+  hipLaunchKernelGGL(vertex_rows_kernel, dim3((k + 1u + 255u) / 256u), dim3(256), 0, stream, k,
+                     value, ptr, val);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const Csr rows{ptr, pick, val, k};
+  return launch_transpose(rows, k, n, s_ptr, s_idx, s_val, w, status, stream);
 }
 
 hipError_t launch_dot(Csr x, Csr y, uint32_t m, double alpha, double *acc, void *ws,

@@ -29,6 +29,8 @@ EXPORTS = ("seacells_fw_a_columns_workspace", "seacells_fw_a_columns",
            "seacells_csr_matmul_workspace", "seacells_csr_matmul_rows", "seacells_csr_matmul_fill",
            "seacells_csr_transpose_workspace", "seacells_csr_transpose",
            "seacells_csr_dot_workspace", "seacells_csr_dot",
+           "seacells_csr_add_workspace", "seacells_csr_add_rows", "seacells_csr_add_fill",
+           "seacells_fw_b_vertex_workspace", "seacells_fw_b_vertex",
            "seacells_status_string", "seacells_last_error", "seacells_version")
 
 
@@ -94,6 +96,18 @@ def load():
     lib.seacells_csr_dot.restype = ctypes.c_int
     lib.seacells_csr_dot.argtypes = [_CSR_P, _CSR_P, ctypes.c_double, _VP, _VP, ctypes.c_size_t,
                                      _VP, _VP]
+    lib.seacells_csr_add_workspace.restype = ctypes.c_size_t
+    lib.seacells_csr_add_workspace.argtypes = [_U32]
+    lib.seacells_csr_add_rows.restype = ctypes.c_int
+    lib.seacells_csr_add_rows.argtypes = [_CSR_P, _CSR_P, _VP, _VP, ctypes.c_size_t, _VP, _VP]
+    lib.seacells_csr_add_fill.restype = ctypes.c_int
+    lib.seacells_csr_add_fill.argtypes = [ctypes.c_float, _CSR_P, ctypes.c_float, _CSR_P, _VP, _VP,
+                                          _VP, _VP, _VP]
+    lib.seacells_fw_b_vertex_workspace.restype = ctypes.c_size_t
+    lib.seacells_fw_b_vertex_workspace.argtypes = [_U32, _U32]
+    lib.seacells_fw_b_vertex.restype = ctypes.c_int
+    lib.seacells_fw_b_vertex.argtypes = [_VP, _U32, _U32, ctypes.c_float, _VP, _VP, _VP, _VP,
+                                         ctypes.c_size_t, _VP, _VP]
     lib.seacells_status_string.restype = ctypes.c_char_p
     lib.seacells_status_string.argtypes = [ctypes.c_int]
     lib.seacells_last_error.restype = ctypes.c_char_p
@@ -436,3 +450,120 @@ def device_operands(K: DeviceCSR, B: DeviceCSR, At: DeviceCSR, status=None, stre
     out["k2at"] = csr_matmul(K, out["kat"], status, stream)
     raise_on_status(status)
     return out
+
+
+def seacells_csr_add_workspace(m: int) -> int:
+    return int(load().seacells_csr_add_workspace(m))
+
+
+def seacells_csr_add_rows(x: DeviceCSR, y: DeviceCSR, c_row_ptr=None, workspace=None, status=None,
+                          stream=None):
+    """Row pointer of x + y (union pattern). Returns (c_row_ptr, status)."""
+    lib = load()
+    dev = x.row_ptr.device
+    if c_row_ptr is None:
+        c_row_ptr = torch.empty(x.shape[0] + 1, dtype=torch.int32, device=dev)
+    if status is None:
+        status = new_status(dev)
+    if workspace is None:
+        workspace = torch.empty(seacells_csr_add_workspace(x.shape[0]), dtype=torch.uint8,
+                                device=dev)
+    sx, sy = x.struct(), y.struct()
+    rc = lib.seacells_csr_add_rows(ctypes.byref(sx), ctypes.byref(sy), _ptr(c_row_ptr),
+                                   _ptr(workspace), workspace.numel(), _ptr(status),
+                                   _stream(stream))
+    _check_rc(rc)
+    return c_row_ptr, status
+
+
+def seacells_csr_add_fill(alpha: float, x: DeviceCSR, beta: float, y: DeviceCSR, c_row_ptr,
+                          c_col_idx, c_val, status=None, stream=None):
+    """Columns and values of alpha x + beta y into buffers sized by c_row_ptr[-1]."""
+    lib = load()
+    if status is None:
+        status = new_status(x.row_ptr.device)
+    sx, sy = x.struct(), y.struct()
+    rc = lib.seacells_csr_add_fill(float(alpha), ctypes.byref(sx), float(beta), ctypes.byref(sy),
+                                   _ptr(c_row_ptr), _ptr(c_col_idx) if c_col_idx.numel() else None,
+                                   _ptr(c_val) if c_val.numel() else None, _ptr(status),
+                                   _stream(stream))
+    _check_rc(rc)
+    return c_col_idx, c_val, status
+
+
+def csr_add(alpha: float, x: DeviceCSR, beta: float, y: DeviceCSR, status=None,
+            stream=None) -> DeviceCSR:
+    """alpha x + beta y as a DeviceCSR (both passes, one synchronisation to
+    size the output). Raises on a device status flag."""
+    dev = x.row_ptr.device
+    if status is None:
+        status = new_status(dev)
+    c_ptr, _ = seacells_csr_add_rows(x, y, status=status, stream=stream)
+    raise_on_status(status)
+    nnz = int(c_ptr[-1].item()) & 0xffffffff
+    c_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+    c_val = torch.empty(nnz, dtype=torch.float32, device=dev)
+    seacells_csr_add_fill(alpha, x, beta, y, c_ptr, c_idx, c_val, status=status, stream=stream)
+    return DeviceCSR(c_ptr, c_idx, c_val, x.shape)
+
+
+def seacells_fw_b_vertex_workspace(k: int, n: int) -> int:
+    return int(load().seacells_fw_b_vertex_workspace(k, n))
+
+
+def seacells_fw_b_vertex(arg_idx, n: int, value: float = 1.0, workspace=None, status=None,
+                         stream=None) -> DeviceCSR:
+    """The n x k vertex matrix S (``value`` at (arg_idx[c], c)) as a DeviceCSR."""
+    lib = load()
+    dev = arg_idx.device
+    k = int(arg_idx.numel())
+    if arg_idx.dtype != torch.int32 or not arg_idx.is_contiguous():
+        raise SeacellsError("arg_idx must be a contiguous int32 tensor")
+    if status is None:
+        status = new_status(dev)
+    if workspace is None:
+        workspace = torch.empty(seacells_fw_b_vertex_workspace(k, n), dtype=torch.uint8,
+                                device=dev)
+    s_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    s_idx = torch.empty(k, dtype=torch.int32, device=dev)
+    s_val = torch.empty(k, dtype=torch.float32, device=dev)
+    rc = lib.seacells_fw_b_vertex(_ptr(arg_idx) if k else None, k, n, float(value), _ptr(s_ptr),
+                                  _ptr(s_idx) if k else None, _ptr(s_val) if k else None,
+                                  _ptr(workspace), workspace.numel(), _ptr(status),
+                                  _stream(stream))
+    _check_rc(rc)
+    return DeviceCSR(s_ptr, s_idx, s_val, (n, k))
+
+
+def fw_b_loop(K: DeviceCSR, k2b: DeviceCSR, aat: DeviceCSR, k2at: DeviceCSR, b: DeviceCSR,
+              steps: int, gammas=None, status=None, stream=None):
+    """``steps`` Frank-Wolfe steps of the B update on the device, A fixed.
+
+    Step t: the B argmin (seacells_fw_b_argmin) gives the row of every
+    column; S is their vertex matrix; B <- (1 - g) B + g S and
+    K^2 B <- (1 - g) K^2 B + g K (K S), with g = gammas[t] (default
+    2 / (t + 2)). Returns (b, k2b, picks [steps, k], mins [steps, k],
+    gaps [steps]) with the last three on the device. Every product and sum
+    runs in the library; the host only reads output sizes.
+    """
+    n, k = k2b.shape
+    dev = k2b.row_ptr.device
+    if status is None:
+        status = new_status(dev)
+    picks = torch.empty((steps, k), dtype=torch.int32, device=dev)
+    mins = torch.empty((steps, k), dtype=torch.float32, device=dev)
+    gaps = torch.empty(steps, dtype=torch.float32, device=dev)
+    ws_b = torch.empty(seacells_fw_b_argmin_workspace(n, k, aat.nnz), dtype=torch.uint8,
+                       device=dev)
+    ws_v = torch.empty(seacells_fw_b_vertex_workspace(k, n), dtype=torch.uint8, device=dev)
+    for t in range(steps):
+        g = 2.0 / (t + 2.0) if gammas is None else float(gammas[t])
+        seacells_fw_b_argmin(k2b, aat, k2at, b, n, k, out_val=mins[t], out_idx=picks[t],
+                             gap=gaps[t:t + 1], workspace=ws_b, status=status, stream=stream)
+        S = seacells_fw_b_vertex(picks[t], n, 1.0, workspace=ws_v, status=status, stream=stream)
+        b = csr_add(1.0 - g, b, g, S, status=status, stream=stream)
+        k2s = csr_matmul(K, csr_matmul(K, S, status=status, stream=stream), status=status,
+                         stream=stream)
+        k2b = csr_add(1.0 - g, k2b, g, k2s, status=status, stream=stream)
+    raise_on_status(status)
+    return b, k2b, picks, mins, gaps

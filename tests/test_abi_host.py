@@ -208,3 +208,34 @@ def test_sparse_ops_reject_bad_arguments_on_host():
                                 None) == -1
     assert lib.seacells_csr_dot(P(x), P(x), ctypes.c_double(1.0), out, 0x10000, dneed - 8, st,
                                 None) == -3
+
+
+def test_sparse_add_and_vertex_reject_bad_arguments_on_host():
+    lib = saa.load()
+    P = ctypes.byref
+    st, out, ws = 0x9000, 0x4000, 0x10000
+    x, y = csr(5, 7, 3), csr(5, 7, 4)
+    need = lib.seacells_csr_add_workspace(5)
+    assert need > 0 and need % 256 == 0
+    assert lib.seacells_csr_add_rows(None, P(y), out, ws, need, st, None) == -1
+    assert lib.seacells_csr_add_rows(P(x), P(y), None, ws, need, st, None) == -1
+    assert lib.seacells_csr_add_rows(P(x), P(csr(5, 6, 4)), out, ws, need, st, None) == -2
+    assert lib.seacells_csr_add_rows(P(x), P(csr(4, 7, 4)), out, ws, need, st, None) == -2
+    assert lib.seacells_csr_add_rows(P(x), P(y), out, ws, need - 1, st, None) == -3
+    assert lib.seacells_csr_add_rows(P(x), P(y), out, ws + 8, need, st, None) == -3
+    assert lib.seacells_csr_add_rows(P(csr(5, 7, 2 ** 30)), P(csr(5, 7, 2 ** 30)), out, ws, need,
+                                     st, None) == -4
+    f = ctypes.c_float
+    assert lib.seacells_csr_add_fill(f(1), P(x), f(1), P(y), None, out, out, st, None) == -1
+    assert lib.seacells_csr_add_fill(f(1), P(x), f(1), P(y), out, None, out, st, None) == -1
+    assert lib.seacells_csr_add_fill(f(1), P(x), f(1), P(csr(5, 8, 1)), out, out, out, st,
+                                     None) == -2
+    vneed = lib.seacells_fw_b_vertex_workspace(10, 100)
+    assert vneed > 0 and vneed % 256 == 0
+    assert lib.seacells_fw_b_vertex(None, 10, 100, f(1), out, out, out, ws, vneed, st, None) == -1
+    assert lib.seacells_fw_b_vertex(out, 10, 100, f(1), None, out, out, ws, vneed, st, None) == -1
+    assert lib.seacells_fw_b_vertex(out, 10, 0, f(1), out, out, out, ws, vneed, st, None) == -2
+    assert lib.seacells_fw_b_vertex(out, 10, 100, f(1), out, out, out, ws, vneed - 1, st,
+                                    None) == -3
+    assert lib.seacells_fw_b_vertex(out, 2 ** 31, 100, f(1), out, out, out, ws, vneed, st,
+                                    None) == -4
