@@ -13,7 +13,8 @@ sample of the same workload.
                     [--no-operands] [--no-cpu-baseline]
 
 After the timed steps it also times the device construction of the
-operands from K, B and A^T ("operands": whole build and per step).
+operands from K, B and A^T ("operands": whole build and per step) and a few
+steps of the on-device B loop ("b_loop").
 
 The default workload is the largest single-GPU configuration (n = 1M cells,
 k = 10000 archetypes); --config c1 .. c4 selects the smaller ones. --prune
@@ -199,6 +200,29 @@ def time_operands(saa, W, w, stream, reps=3):
             "note": "ms_total includes one host synchronisation per product (output sizing)"}
 
 
+def time_b_loop(saa, W, w, steps, argmin_ms, stream):
+    """The B update as a loop of Frank-Wolfe steps on the device (A fixed):
+    per step the B argmin, the vertex matrix of its picks, B <- (1-g) B + g S
+    and K^2 B <- (1-g) K^2 B + g K (K S). Wall time per step (the host reads
+    output sizes once per product and sum), and what the update costs beyond
+    the argmin."""
+    import torch
+    D = saa.DeviceCSR.from_scipy
+    K = W.kernel_matrix(w)
+    dK, k2b, aat, k2at, b = D(K), D(w.k2b), D(w.aat), D(w.k2at), D(w.b)
+    st = saa.new_status()
+    saa.fw_b_loop(dK, k2b, aat, k2at, b, 1, status=st, stream=stream)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    b2, k2b2, _, _, _ = saa.fw_b_loop(dK, k2b, aat, k2at, b, steps, status=st, stream=stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / steps
+    saa.raise_on_status(st)
+    return {"steps": steps, "ms_per_step": ms, "argmin_ms": argmin_ms,
+            "update_ms_per_step": ms - argmin_ms, "nnz_b": b2.nnz, "nnz_k2b": k2b2.nnz,
+            "nnz_k2b_start": int(w.k2b.nnz)}
+
+
 def copy_calibration(mib):
     """A plain elementwise copy of known size: it reads and writes exactly
     mib MiB per launch, so FETCH_SIZE / WRITE_SIZE of this kernel give the
@@ -223,6 +247,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-operands", action="store_true",
                     help="skip timing the device operand construction")
+    ap.add_argument("--b-loop-steps", type=int, default=3,
+                    help="B-loop steps timed after the main steps (0 skips)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--prune", type=float, default=None, metavar="THR",
                     help="time the A update's pruning variant with threshold THR")
@@ -359,6 +385,8 @@ def main():
     }
     if not args.no_operands:
         rec["operands"] = time_operands(saa, W, w, stream)
+    if args.b_loop_steps > 0:
+        rec["b_loop"] = time_b_loop(saa, W, w, args.b_loop_steps, b_ms, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)

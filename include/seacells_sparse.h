@@ -152,6 +152,36 @@ int seacells_fw_b_vertex(const uint32_t *arg_idx, uint32_t k, uint32_t n, float 
                          uint32_t *s_row_ptr, uint32_t *s_col_idx, float *s_val, void *workspace,
                          size_t workspace_bytes, uint32_t *status, seacells_stream_t stream);
 
+/* Workspace bytes seacells_fw_a_to_csr_rows needs for n cells (> 0). */
+size_t seacells_fw_a_to_csr_workspace(uint32_t n);
+
+/*
+ * The A update's returned columns (seacells_fw_a_columns's atom_idx /
+ * atom_val [n, cap], atom_cnt [n], device) as the CSR A^T (n x k) that the
+ * next B update's operands are built from (A A^T = (A^T)^T A^T and
+ * K^2 A^T = K (K A^T), as the page's layout convention passes every n x k
+ * matrix), step 1 of 2: the row pointer. Row j holds cell j's atoms among
+ * its first min(atom_cnt[j], cap) slots whose weight is not 0, in ascending
+ * column order. at_row_ptr [n + 1] (device, out; at_row_ptr[n] = nnz).
+ * workspace: at least seacells_fw_a_to_csr_workspace(n) bytes, 256-byte
+ * aligned. BAD_INDEX for a count above cap or a column >= k (dropped).
+ */
+int seacells_fw_a_to_csr_rows(const uint32_t *atom_idx, const float *atom_val,
+                              const uint32_t *atom_cnt, uint32_t n, uint32_t k, uint32_t cap,
+                              uint32_t *at_row_ptr, void *workspace, size_t workspace_bytes,
+                              uint32_t *status, seacells_stream_t stream);
+
+/*
+ * Step 2 of 2: columns and weights into at_col_idx / at_val (device,
+ * at_row_ptr[n] entries each). at_row_ptr must be step 1's output for the same
+ * atoms (else BAD_INDEX and no write beyond its row sizes); a column held twice
+ * by one cell is flagged BAD_INDEX.
+ */
+int seacells_fw_a_to_csr_fill(const uint32_t *atom_idx, const float *atom_val,
+                              const uint32_t *atom_cnt, uint32_t n, uint32_t k, uint32_t cap,
+                              const uint32_t *at_row_ptr, uint32_t *at_col_idx, float *at_val,
+                              uint32_t *status, seacells_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

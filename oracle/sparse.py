@@ -229,3 +229,25 @@ def picks(idx, n: int, value: float = 1.0) -> sp.csr_matrix:
     out = sp.csr_matrix((np.full(k, float(value)), (idx, np.arange(k))), shape=(n, k))
     out.sort_indices()
     return out
+
+
+def atoms_to_csr(atom_idx, atom_val, atom_cnt, k: int) -> sp.csr_matrix:
+    """The A update's returned columns as A^T (n x k CSR): row j holds cell
+    j's atoms (the first atom_cnt[j] slots of its lists) with a non-zero
+    weight, in ascending column order."""
+    atom_idx = np.asarray(atom_idx)
+    atom_val = np.asarray(atom_val, np.float64)
+    n = atom_idx.shape[0]
+    rows, cols, vals = [], [], []
+    for j in range(n):
+        c = int(atom_cnt[j])
+        keep = atom_val[j, :c] != 0.0
+        order = np.argsort(atom_idx[j, :c][keep], kind="stable")
+        rows.append(np.full(int(keep.sum()), j))
+        cols.append(atom_idx[j, :c][keep][order].astype(np.int64))
+        vals.append(atom_val[j, :c][keep][order])
+    out = sp.csr_matrix((np.concatenate(vals) if vals else np.zeros(0),
+                         (np.concatenate(rows) if rows else np.zeros(0, np.int64),
+                          np.concatenate(cols) if cols else np.zeros(0, np.int64))), shape=(n, k))
+    out.sort_indices()
+    return out

@@ -336,6 +336,51 @@ int seacells_fw_b_vertex(const uint32_t *arg_idx, uint32_t k, uint32_t n, float 
   return SEACELLS_OK;
 }
 
+size_t seacells_fw_a_to_csr_workspace(uint32_t n) { return add_workspace(n); }
+
+static int check_atoms(const uint32_t *atom_idx, const float *atom_val, const uint32_t *atom_cnt,
+                       uint32_t n, uint32_t k, uint32_t cap) {
+  if (n > 0 && (atom_idx == nullptr || atom_val == nullptr || atom_cnt == nullptr))
+    return SEACELLS_E_NULL;
+  if (k == 0 || cap == 0) return SEACELLS_E_SHAPE;
+  if (n >= 0x80000000u || k >= 0x80000000u) return SEACELLS_E_TOO_LARGE;
+  return SEACELLS_OK;
+}
+
+int seacells_fw_a_to_csr_rows(const uint32_t *atom_idx, const float *atom_val,
+                              const uint32_t *atom_cnt, uint32_t n, uint32_t k, uint32_t cap,
+                              uint32_t *at_row_ptr, void *workspace, size_t workspace_bytes,
+                              uint32_t *status, seacells_stream_t stream) {
+  int rc;
+  if ((rc = check_atoms(atom_idx, atom_val, atom_cnt, n, k, cap)) != SEACELLS_OK) return rc;
+  if (at_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
+  if (workspace == nullptr || workspace_bytes < add_workspace(n) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SEACELLS_E_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_atoms_count(atom_idx, atom_val, atom_cnt, n, k, cap, at_row_ptr, workspace, status, s);
+  if (e != hipSuccess) return hip_fail(e, "fw_a_to_csr_rows launch");
+  return SEACELLS_OK;
+}
+
+int seacells_fw_a_to_csr_fill(const uint32_t *atom_idx, const float *atom_val,
+                              const uint32_t *atom_cnt, uint32_t n, uint32_t k, uint32_t cap,
+                              const uint32_t *at_row_ptr, uint32_t *at_col_idx, float *at_val,
+                              uint32_t *status, seacells_stream_t stream) {
+  int rc;
+  if ((rc = check_atoms(atom_idx, atom_val, atom_cnt, n, k, cap)) != SEACELLS_OK) return rc;
+  if (at_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_atoms_fill(atom_idx, atom_val, atom_cnt, n, k, cap, at_row_ptr, at_col_idx, at_val,
+                        status, s);
+  if (e != hipSuccess) return hip_fail(e, "fw_a_to_csr_fill launch");
+  return SEACELLS_OK;
+}
+
 const char *seacells_status_string(int code) {
   switch (code) {
     case SEACELLS_OK:

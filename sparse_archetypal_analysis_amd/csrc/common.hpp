@@ -182,6 +182,13 @@ uint32_t tr_blocks(uint32_t m, uint32_t q);
 size_t transpose_workspace(uint32_t m, uint32_t q);
 size_t matmul_workspace(uint32_t m);
 size_t add_workspace(uint32_t m);
+hipError_t launch_atoms_count(const uint32_t *atom_idx, const float *atom_val,
+                              const uint32_t *atom_cnt, uint32_t n, uint32_t k, uint32_t cap,
+                              uint32_t *at_ptr, void *ws, uint32_t *status, hipStream_t stream);
+hipError_t launch_atoms_fill(const uint32_t *atom_idx, const float *atom_val,
+                             const uint32_t *atom_cnt, uint32_t n, uint32_t k, uint32_t cap,
+                             const uint32_t *at_ptr, uint32_t *at_idx, float *at_val,
+                             uint32_t *status, hipStream_t stream);
 size_t vertex_workspace(uint32_t k, uint32_t n);
 hipError_t launch_add_count(Csr x, Csr y, uint32_t m, uint32_t q, uint32_t *c_ptr, void *ws,
                             uint32_t *status, hipStream_t stream);

@@ -672,6 +672,75 @@ __global__ void __launch_bounds__(256)
   if (c < k) val[c] = v;
 }
 
+// The A update's returned columns as A^T (n x k CSR), pass 1: atoms with a
+// non-zero weight per cell into cnt[j] (the caller's row pointer + 1).
+__global__ void __launch_bounds__(256)
+    atoms_count_kernel(const uint32_t *__restrict__ atom_idx, const float *__restrict__ atom_val,
+                       const uint32_t *__restrict__ atom_cnt, uint32_t n, uint32_t k, uint32_t cap,
+                       uint32_t *__restrict__ cnt, uint32_t *__restrict__ status) {
+  const uint32_t j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  uint32_t flags = 0;
+  uint32_t c = atom_cnt[j];
+  if (c > cap) {
+    flags |= kFlagBadIndex;
+    c = cap;
+  }
+  const size_t row = (size_t)j * cap;
+  uint32_t m = 0;
+  for (uint32_t s = 0; s < c; ++s) {
+    if (atom_val[row + s] == 0.0f) continue;
+    if (atom_idx[row + s] >= k)
+      flags |= kFlagBadIndex;
+    else
+      ++m;
+  }
+  cnt[j] = m;
+  if (flags != 0) atomicOr(status, flags);
+}
+
+// Pass 2: one wave per cell; each kept atom goes to its rank among the
+// cell's kept atoms by column (the columns of one cell's atoms are unique).
+__global__ void __launch_bounds__(kSpWaves * kWave)
+    atoms_fill_kernel(const uint32_t *__restrict__ atom_idx, const float *__restrict__ atom_val,
+                      const uint32_t *__restrict__ atom_cnt, uint32_t n, uint32_t k, uint32_t cap,
+                      const uint32_t *__restrict__ c_ptr, uint32_t *__restrict__ at_idx,
+                      float *__restrict__ at_val, uint32_t *__restrict__ status) {
+  const uint32_t lane = lane_id();
+  const uint32_t wib = threadIdx.x / kWave;
+  uint32_t flags = 0;
+  for (uint32_t r = blockIdx.x * kSpWaves + wib; r < n; r += gridDim.x * kSpWaves) {
+    const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
+    const uint32_t cnt = end >= base ? end - base : 0u;
+    const uint32_t c = min(atom_cnt[r], cap);
+    const uint32_t *__restrict__ ri = atom_idx + (size_t)r * cap;
+    const float *__restrict__ rv = atom_val + (size_t)r * cap;
+    uint32_t kept = 0;
+    for (uint32_t s0 = 0; s0 < c; s0 += kWave) {
+      const uint32_t s = s0 + lane;
+      const uint32_t mi = s < c ? ri[s] : 0xffffffffu;
+      const float mv = s < c ? rv[s] : 0.0f;
+      const bool mine = s < c && mv != 0.0f && mi < k;
+      uint32_t rank = 0, same = 0;
+      for (uint32_t t = 0; t < c; ++t) {  // every lane reads the same atom
+        const uint32_t it = ri[t];
+        if (rv[t] != 0.0f && it < k) {
+          rank += it < mi ? 1u : 0u;
+          same += it == mi ? 1u : 0u;
+        }
+      }
+      if (mine && same != 1u) flags |= kFlagBadIndex;  // a column twice in one cell
+      if (mine && rank < cnt) {
+        at_idx[(size_t)base + rank] = mi;
+        at_val[(size_t)base + rank] = mv;
+      }
+      kept += wave_sum_u32(mine ? 1u : 0u);
+    }
+    if (kept != cnt) flags |= kFlagBadIndex;  // not the count pass's row pointer
+  }
+  if (flags != 0) atomicOr(status, flags);
+}
+
 // <X, Y> row by row: each X entry is looked up in Y's (ascending) row.
 __global__ void __launch_bounds__(256)
     dot_rows_kernel(Csr x, Csr y, uint32_t m, double *__restrict__ part,
@@ -831,7 +900,33 @@ hipError_t launch_transpose(Csr a, uint32_t m, uint32_t q, uint32_t *at_ptr, uin
   return hipGetLastError();
 }
 
-int g_add_count_resident = 0, g_add_fill_resident = 0;
+int g_add_count_resident = 0, g_add_fill_resident = 0, g_atoms_fill_resident = 0;
+
+hipError_t launch_atoms_count(const uint32_t *atom_idx, const float *atom_val,
+                              const uint32_t *atom_cnt, uint32_t n, uint32_t k, uint32_t cap,
+                              uint32_t *at_ptr, void *ws, uint32_t *status, hipStream_t stream) {
+  hipError_t e;
+  if (n > 0) {
+    hipLaunchKernelGGL(atoms_count_kernel, dim3((n + 255u) / 256u), dim3(256), 0, stream, atom_idx,
+                       atom_val, atom_cnt, n, k, cap, at_ptr + 1, status);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return launch_scan(at_ptr, n, static_cast<uint64_t *>(ws), status, stream);
+}
+
+hipError_t launch_atoms_fill(const uint32_t *atom_idx, const float *atom_val,
+                             const uint32_t *atom_cnt, uint32_t n, uint32_t k, uint32_t cap,
+                             const uint32_t *at_ptr, uint32_t *at_idx, float *at_val,
+                             uint32_t *status, hipStream_t stream) {
+  DeviceInfo dev;
+  hipError_t e = device_info(&dev);
+  if (e != hipSuccess) return e;
+  if (n == 0) return hipSuccess;
+  const uint32_t nb = sp_blocks(n, dev, resident_blocks(atoms_fill_kernel, g_atoms_fill_resident));
+  hipLaunchKernelGGL(atoms_fill_kernel, dim3(nb), dim3(kSpWaves * kWave), 0, stream, atom_idx,
+                     atom_val, atom_cnt, n, k, cap, at_ptr, at_idx, at_val, status);
+  return hipGetLastError();
+}
 
 hipError_t launch_add_count(Csr x, Csr y, uint32_t m, uint32_t q, uint32_t *c_ptr, void *ws,
                             uint32_t *status, hipStream_t stream) {

@@ -31,6 +31,8 @@ EXPORTS = ("seacells_fw_a_columns_workspace", "seacells_fw_a_columns",
            "seacells_csr_dot_workspace", "seacells_csr_dot",
            "seacells_csr_add_workspace", "seacells_csr_add_rows", "seacells_csr_add_fill",
            "seacells_fw_b_vertex_workspace", "seacells_fw_b_vertex",
+           "seacells_fw_a_to_csr_workspace", "seacells_fw_a_to_csr_rows",
+           "seacells_fw_a_to_csr_fill",
            "seacells_status_string", "seacells_last_error", "seacells_version")
 
 
@@ -108,6 +110,14 @@ def load():
     lib.seacells_fw_b_vertex.restype = ctypes.c_int
     lib.seacells_fw_b_vertex.argtypes = [_VP, _U32, _U32, ctypes.c_float, _VP, _VP, _VP, _VP,
                                          ctypes.c_size_t, _VP, _VP]
+    lib.seacells_fw_a_to_csr_workspace.restype = ctypes.c_size_t
+    lib.seacells_fw_a_to_csr_workspace.argtypes = [_U32]
+    lib.seacells_fw_a_to_csr_rows.restype = ctypes.c_int
+    lib.seacells_fw_a_to_csr_rows.argtypes = [_VP, _VP, _VP, _U32, _U32, _U32, _VP, _VP,
+                                              ctypes.c_size_t, _VP, _VP]
+    lib.seacells_fw_a_to_csr_fill.restype = ctypes.c_int
+    lib.seacells_fw_a_to_csr_fill.argtypes = [_VP, _VP, _VP, _U32, _U32, _U32, _VP, _VP, _VP,
+                                              _VP, _VP]
     lib.seacells_status_string.restype = ctypes.c_char_p
     lib.seacells_status_string.argtypes = [ctypes.c_int]
     lib.seacells_last_error.restype = ctypes.c_char_p
@@ -567,3 +577,100 @@ def fw_b_loop(K: DeviceCSR, k2b: DeviceCSR, aat: DeviceCSR, k2at: DeviceCSR, b: 
         k2b = csr_add(1.0 - g, k2b, g, k2s, status=status, stream=stream)
     raise_on_status(status)
     return b, k2b, picks, mins, gaps
+
+
+def seacells_fw_a_to_csr_workspace(n: int) -> int:
+    return int(load().seacells_fw_a_to_csr_workspace(n))
+
+
+def seacells_fw_a_to_csr_rows(atom_idx, atom_val, atom_cnt, k: int, at_row_ptr=None,
+                              workspace=None, status=None, stream=None):
+    """Row pointer of A^T from the A update's atoms. Returns (at_row_ptr, status)."""
+    lib = load()
+    n, cap = atom_idx.shape
+    dev = atom_idx.device
+    if at_row_ptr is None:
+        at_row_ptr = torch.empty(n + 1, dtype=torch.int32, device=dev)
+    if status is None:
+        status = new_status(dev)
+    if workspace is None:
+        workspace = torch.empty(seacells_fw_a_to_csr_workspace(n), dtype=torch.uint8, device=dev)
+    _check_rc(lib.seacells_fw_a_to_csr_rows(_ptr(atom_idx), _ptr(atom_val), _ptr(atom_cnt), n, k,
+                                            cap, _ptr(at_row_ptr), _ptr(workspace),
+                                            workspace.numel(), _ptr(status), _stream(stream)))
+    return at_row_ptr, status
+
+
+def seacells_fw_a_to_csr_fill(atom_idx, atom_val, atom_cnt, k: int, at_row_ptr, at_col_idx,
+                              at_val, status=None, stream=None):
+    """Columns and weights of A^T into buffers sized by at_row_ptr[-1]."""
+    lib = load()
+    n, cap = atom_idx.shape
+    if status is None:
+        status = new_status(atom_idx.device)
+    _check_rc(lib.seacells_fw_a_to_csr_fill(_ptr(atom_idx), _ptr(atom_val), _ptr(atom_cnt), n, k,
+                                            cap, _ptr(at_row_ptr),
+                                            _ptr(at_col_idx) if at_col_idx.numel() else None,
+                                            _ptr(at_val) if at_val.numel() else None,
+                                            _ptr(status), _stream(stream)))
+    return at_col_idx, at_val, status
+
+
+def fw_a_to_csr(atom_idx, atom_val, atom_cnt, k: int, status=None, stream=None) -> DeviceCSR:
+    """The A update's atoms ([n, cap] int32 / float32, [n] int32) as the CSR
+    A^T (n x k): non-zero weights, columns ascending. One synchronisation
+    sizes the output; raises on a device status flag."""
+    n = atom_idx.shape[0]
+    dev = atom_idx.device
+    if status is None:
+        status = new_status(dev)
+    ptr, _ = seacells_fw_a_to_csr_rows(atom_idx, atom_val, atom_cnt, k, status=status,
+                                       stream=stream)
+    raise_on_status(status)
+    nnz = int(ptr[-1].item()) & 0xffffffff
+    idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+    val = torch.empty(nnz, dtype=torch.float32, device=dev)
+    seacells_fw_a_to_csr_fill(atom_idx, atom_val, atom_cnt, k, ptr, idx, val, status=status,
+                              stream=stream)
+    return DeviceCSR(ptr, idx, val, (n, k))
+
+
+def outer_iteration(K: DeviceCSR, b: DeviceCSR, k2b: DeviceCSR, a_t: DeviceCSR, steps_a: int,
+                    steps_b: int, cap=None, trace=False, status=None, stream=None) -> dict:
+    """One SEACells outer iteration on the device, every step in the library.
+
+    A update with B fixed: P = B^T K^2 B (a transpose and a product) and
+    t1 = (P + P^T) / 2 (exactly symmetric), then seacells_fw_a_columns from
+    A_prev = a_t for steps_a steps (cap default: widest row of a_t +
+    steps_a); its atoms become the new A^T. B update with A fixed:
+    A A^T = (A^T)^T A^T and K^2 A^T = K (K A^T), then fw_b_loop for
+    steps_b steps. Last, the RSS ||K - K B A||^2 of the new pair (f64).
+    Returns a dict: b, k2b, a_t, t1, aat, k2at (DeviceCSR), rss ([1] f64),
+    a_trace ([n, steps_a] when trace), b_picks, b_mins, b_gaps.
+    """
+    n, k = b.shape
+    dev = b.row_ptr.device
+    if status is None:
+        status = new_status(dev)
+    kw = dict(status=status, stream=stream)
+    bt, _ = seacells_csr_transpose(b, **kw)
+    p = csr_matmul(bt, k2b, **kw)
+    pt, _ = seacells_csr_transpose(p, **kw)
+    t1 = csr_add(0.5, p, 0.5, pt, **kw)
+    if cap is None:
+        rows = np.diff(a_t.row_ptr.cpu().numpy().astype(np.int64))
+        cap = int(rows.max() if rows.size else 0) + steps_a
+    ai, av, ac, tr, _ = seacells_fw_a_columns(t1, k2b, a_t, n, k, steps_a, cap, trace=bool(trace),
+                                              **kw)
+    raise_on_status(status)
+    a_t2 = fw_a_to_csr(ai, av, ac, k, **kw)
+    a, _ = seacells_csr_transpose(a_t2, **kw)
+    aat = csr_matmul(a, a_t2, **kw)
+    k2at = csr_matmul(K, csr_matmul(K, a_t2, **kw), **kw)
+    b2, k2b2, picks, mins, gaps = fw_b_loop(K, k2b, aat, k2at, b, steps_b, **kw)
+    bt2, _ = seacells_csr_transpose(b2, **kw)
+    p2 = csr_matmul(bt2, k2b2, **kw)
+    acc, _ = rss(K, k2b2, a_t2, p2, aat, **kw)
+    raise_on_status(status)
+    return {"b": b2, "k2b": k2b2, "a_t": a_t2, "t1": t1, "aat": aat, "k2at": k2at, "rss": acc,
+            "a_trace": tr, "b_picks": picks, "b_mins": mins, "b_gaps": gaps}

@@ -222,3 +222,36 @@ def check_product(got, want, extra_terms=0, what=""):
     assert bad.size == 0, "%s: %d entries out of bound, first %s: got %r want %r tol %r" % (
         what, bad.size, bad[:3], got.data[bad[:3]], want.value[bad[:3]], tol[bad[:3]])
     return float((err / np.maximum(want.abs_value, 1e-300)).max()) if err.size else 0.0
+
+
+def check_b_loop(K, b0, aat, k2at, T, res_gpu, gammas=None):
+    """The device B loop (saa.fw_b_loop's result) against oracle.b_loop
+    replaying its picks: every pick the oracle's or within the tie rule, the
+    minimum values and gaps under the B argmin's policy, B after the loop
+    within 1e-5, K^2 B within 5e-5 relative. Returns (picks that differ,
+    worst relative error of K^2 B)."""
+    from oracle import b_loop as BL
+    b_gpu, k2b_gpu, picks, mins, gaps = res_gpu
+    picks = picks.cpu().numpy().astype(np.int64)
+    mins = mins.cpu().numpy().astype(np.float64)
+    gaps = gaps.cpu().numpy().astype(np.float64)
+    n = b0.shape[0]
+    assert np.all((picks >= 0) & (picks < n))
+    orc = BL.fw_b_loop(K, b0, aat, k2at, T, gammas=gammas, force=picks)
+    exact = picks == orc.pick
+    second = np.where(np.isfinite(orc.second), orc.second, 0.0)
+    over = (orc.g_used - orc.gmin) > TIE_REL * np.maximum.reduce(
+        [np.abs(orc.gmin), np.abs(second), orc.scale])
+    assert not np.any(over & ~exact), "pick outside the tie rule at %s" % (
+        np.argwhere(over & ~exact)[:3].tolist(),)
+    tol = VAL_ABS + VAL_REL * np.abs(orc.g_used)
+    assert np.all(np.abs(mins - orc.g_used) <= tol), float(np.max(np.abs(mins - orc.g_used) - tol))
+    for t in range(T):
+        assert abs(gaps[t] - orc.gap[t]) <= GAP_REL * max(abs(orc.gap[t]), 1e-4 / GAP_REL), t
+    from tests.gpu_run import host
+    bd = host(b_gpu).toarray().astype(np.float64)
+    assert np.max(np.abs(bd - orc.b)) <= 1e-5
+    kd = host(k2b_gpu).toarray().astype(np.float64)
+    err = np.abs(kd - orc.k2b)
+    assert np.all(err <= 5e-5 * np.abs(orc.k2b) + 1e-6 * np.max(np.abs(orc.k2b)))
+    return int((~exact).sum()), float(np.max(err / np.maximum(np.abs(orc.k2b), 1e-30)))

@@ -239,3 +239,19 @@ def test_sparse_add_and_vertex_reject_bad_arguments_on_host():
                                     None) == -3
     assert lib.seacells_fw_b_vertex(out, 2 ** 31, 100, f(1), out, out, out, ws, vneed, st,
                                     None) == -4
+
+
+def test_atoms_to_csr_rejects_bad_arguments_on_host():
+    lib = saa.load()
+    st, out, ws = 0x9000, 0x4000, 0x10000
+    need = lib.seacells_fw_a_to_csr_workspace(10)
+    assert need > 0 and need % 256 == 0
+    assert lib.seacells_fw_a_to_csr_rows(None, out, out, 10, 5, 4, out, ws, need, st, None) == -1
+    assert lib.seacells_fw_a_to_csr_rows(out, out, out, 10, 0, 4, out, ws, need, st, None) == -2
+    assert lib.seacells_fw_a_to_csr_rows(out, out, out, 10, 5, 0, out, ws, need, st, None) == -2
+    assert lib.seacells_fw_a_to_csr_rows(out, out, out, 10, 5, 4, None, ws, need, st, None) == -1
+    assert lib.seacells_fw_a_to_csr_rows(out, out, out, 10, 5, 4, out, ws, need - 1, st,
+                                         None) == -3
+    assert lib.seacells_fw_a_to_csr_fill(out, out, out, 10, 5, 4, None, out, out, st, None) == -1
+    assert lib.seacells_fw_a_to_csr_fill(out, out, out, 2 ** 31, 5, 4, out, out, out, st,
+                                         None) == -4

@@ -106,30 +106,6 @@ def test_vertex_matrix_bit_exact(n, k):
     assert np.all(got.data == 0.5)
 
 
-def check_loop(w, K, T, res_gpu):
-    b_gpu, k2b_gpu, picks, mins, gaps = res_gpu
-    picks = picks.cpu().numpy().astype(np.int64)
-    mins = mins.cpu().numpy().astype(np.float64)
-    gaps = gaps.cpu().numpy().astype(np.float64)
-    assert np.all((picks >= 0) & (picks < w.n))
-    orc = BL.fw_b_loop(K, w.b, w.aat, w.k2at, T, force=picks)
-    exact = picks == orc.pick
-    over = (orc.g_used - orc.gmin) > parity.TIE_REL * np.maximum.reduce(
-        [np.abs(orc.gmin), np.abs(np.where(np.isfinite(orc.second), orc.second, 0.0)), orc.scale])
-    assert not np.any(over & ~exact), "pick outside the tie rule at %s" % (
-        np.argwhere(over & ~exact)[:3].tolist(),)
-    tol = parity.VAL_ABS + parity.VAL_REL * np.abs(orc.g_used)
-    assert np.all(np.abs(mins - orc.g_used) <= tol), float(np.max(np.abs(mins - orc.g_used) - tol))
-    for t in range(T):
-        assert abs(gaps[t] - orc.gap[t]) <= parity.GAP_REL * max(abs(orc.gap[t]), 1e-4 / parity.GAP_REL)
-    bd = host(b_gpu).toarray().astype(np.float64)
-    assert np.max(np.abs(bd - orc.b)) <= 1e-5
-    kd = host(k2b_gpu).toarray().astype(np.float64)
-    err = np.abs(kd - orc.k2b)
-    assert np.all(err <= 5e-5 * np.abs(orc.k2b) + 1e-6 * np.max(np.abs(orc.k2b)))
-    return int((~exact).sum()), float(np.max(err / np.maximum(np.abs(orc.k2b), 1e-30)))
-
-
 @pytest.mark.parametrize("name,T", [("c1", 12), ("c2", 8), ("c3", 3)])
 def test_b_loop_against_oracle_replay(name, T):
     w = W.make(name)
@@ -138,7 +114,7 @@ def test_b_loop_against_oracle_replay(name, T):
     res = saa.fw_b_loop(dev(K), dev(w.k2b), dev(w.aat), dev(w.k2at), dev(w.b), T, status=st)
     torch.cuda.synchronize()
     assert saa.status_flags(st) == []
-    flips, krel = check_loop(w, K, T, res)
+    flips, krel = parity.check_b_loop(K, w.b, w.aat, w.k2at, T, res)
     print("\n%s: %d steps, %d picks differ within the tie rule, K^2B max rel err %.2e"
           % (name, T, flips, krel))
 

@@ -369,3 +369,25 @@ def test_b_loop_orientation_with_a_non_symmetric_middle_matrix():
         for c in range(k):
             g = sum(K2B[r, m] * mid[m, c] for m in range(k)) - T2[r, c]
             assert abs(res.g_used[0, c] - g) <= 1e-12
+
+
+def test_atoms_to_csr_equals_dense_scatter():
+    rng = np.random.default_rng(99)
+    n, k, cap = 12, 9, 6
+    idx = np.zeros((n, cap), np.int32)
+    val = np.zeros((n, cap), np.float32)
+    cnt = rng.integers(0, cap + 1, size=n)
+    dense_a = np.zeros((n, k))
+    for j in range(n):
+        cols = rng.choice(k, size=cnt[j], replace=False)  # unique atoms, any order
+        w = rng.uniform(0, 1, size=cnt[j]).astype(np.float32)
+        w[rng.random(cnt[j]) < 0.3] = 0.0                   # zero weights are dropped
+        idx[j, :cnt[j]], val[j, :cnt[j]] = cols, w
+        idx[j, cnt[j]:] = 7                                 # slots past the count are ignored
+        val[j, cnt[j]:] = 5.0
+        dense_a[j, cols] = w
+    got = S.atoms_to_csr(idx, val, cnt, k)
+    np.testing.assert_array_equal(got.toarray(), dense_a)
+    assert got.nnz == int(np.count_nonzero(dense_a))
+    for j in range(n):
+        assert np.all(np.diff(got.indices[got.indptr[j]:got.indptr[j + 1]]) > 0)
