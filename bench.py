@@ -13,8 +13,9 @@ sample of the same workload.
                     [--no-operands] [--no-cpu-baseline]
 
 After the timed steps it also times the device construction of the
-operands from K, B and A^T ("operands": whole build and per step) and a few
-steps of the on-device B loop ("b_loop").
+operands from K, B and A^T ("operands": whole build and per step), a few
+steps of the on-device B loop ("b_loop") and one whole outer iteration
+("iteration": A update, operands, B loop, RSS).
 
 The default workload is the largest single-GPU configuration (n = 1M cells,
 k = 10000 archetypes); --config c1 .. c4 selects the smaller ones. --prune
@@ -223,6 +224,27 @@ def time_b_loop(saa, W, w, steps, argmin_ms, stream):
             "nnz_k2b_start": int(w.k2b.nnz)}
 
 
+def time_iteration(saa, W, w, steps_b, stream):
+    """One SEACells outer iteration on the device (saa.outer_iteration): t1,
+    the A update (T steps), A^T, A A^T, K^2 A^T, steps_b B steps and the
+    RSS. Wall time (one host read of each output size), and the RSS."""
+    import torch
+    D = saa.DeviceCSR.from_scipy
+    K = W.kernel_matrix(w)
+    dK, b, k2b, at = D(K), D(w.b), D(w.k2b), D(w.a_prev_t)
+    st = saa.new_status()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = saa.outer_iteration(dK, b, k2b, at, w.T, steps_b, status=st, stream=stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0
+    saa.raise_on_status(st)
+    return {"steps_a": w.T, "steps_b": steps_b, "ms": ms, "rss": float(res["rss"].item()),
+            "nnz_a_t": res["a_t"].nnz, "nnz_k2at": res["k2at"].nnz, "nnz_aat": res["aat"].nnz,
+            "note": "first call of the process (includes the padded copies and one-off "
+                    "allocations)"}
+
+
 def copy_calibration(mib):
     """A plain elementwise copy of known size: it reads and writes exactly
     mib MiB per launch, so FETCH_SIZE / WRITE_SIZE of this kernel give the
@@ -249,6 +271,8 @@ def main():
                     help="skip timing the device operand construction")
     ap.add_argument("--b-loop-steps", type=int, default=3,
                     help="B-loop steps timed after the main steps (0 skips)")
+    ap.add_argument("--iteration-b-steps", type=int, default=2,
+                    help="B steps of the timed outer iteration (0 skips the iteration)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--prune", type=float, default=None, metavar="THR",
                     help="time the A update's pruning variant with threshold THR")
@@ -387,6 +411,8 @@ def main():
         rec["operands"] = time_operands(saa, W, w, stream)
     if args.b_loop_steps > 0:
         rec["b_loop"] = time_b_loop(saa, W, w, args.b_loop_steps, b_ms, stream)
+    if args.iteration_b_steps > 0:
+        rec["iteration"] = time_iteration(saa, W, w, args.iteration_b_steps, stream)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(rec), flush=True)
