@@ -69,7 +69,9 @@ int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint3
  * and b; c_col_idx and c_val hold c_row_ptr[m] entries each (device, out).
  * c[i, c] = sum over the entries j of a's row i, in order, and then over
  * b's row j, of a[i, j] * b[j, c], accumulated in f32 with fused
- * multiply-adds in that order.
+ * multiply-adds in that order. c_col_idx / c_val may be NULL only when the
+ * product is empty (a non-empty row with no output arrays is skipped and
+ * flagged BAD_INDEX).
  */
 int seacells_csr_matmul_fill(const seacells_csr *a, const seacells_csr *b,
                              const uint32_t *c_row_ptr, uint32_t *c_col_idx, float *c_val,

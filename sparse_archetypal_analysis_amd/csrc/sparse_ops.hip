@@ -390,6 +390,10 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
   for (uint32_t r = blockIdx.x * kSpWaves + wib; r < m; r += gridDim.x * kSpWaves) {
     const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
     const uint32_t cnt = end >= base ? end - base : 0u;
+    if (cnt > 0 && (c_idx == nullptr || c_val == nullptr)) {  // no output arrays given
+      flags |= kFlagBadIndex;
+      continue;
+    }
     uint32_t a0, a1;
     if (!sp_row(a, r, a0, a1)) flags |= kFlagBadIndex;
     uint32_t done = 0;
@@ -612,6 +616,10 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
   for (uint32_t r = blockIdx.x * kSpWaves + wib; r < m; r += gridDim.x * kSpWaves) {
     const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
     const uint32_t cnt = end >= base ? end - base : 0u;
+    if (cnt > 0 && (c_idx == nullptr || c_val == nullptr)) {  // no output arrays given
+      flags |= kFlagBadIndex;
+      continue;
+    }
     uint32_t x0, x1, y0, y1;
     if (!sp_row(x, r, x0, x1) || !sp_row(y, r, y0, y1)) flags |= kFlagBadIndex;
     // place of an entry in the merged row: its rank in its own row, plus the
@@ -712,6 +720,10 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
   for (uint32_t r = blockIdx.x * kSpWaves + wib; r < n; r += gridDim.x * kSpWaves) {
     const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
     const uint32_t cnt = end >= base ? end - base : 0u;
+    if (cnt > 0 && (at_idx == nullptr || at_val == nullptr)) {  // no output arrays given
+      flags |= kFlagBadIndex;
+      continue;
+    }
     const uint32_t c = min(atom_cnt[r], cap);
     const uint32_t *__restrict__ ri = atom_idx + (size_t)r * cap;
     const float *__restrict__ rv = atom_val + (size_t)r * cap;

@@ -501,18 +501,47 @@ def seacells_csr_add_fill(alpha: float, x: DeviceCSR, beta: float, y: DeviceCSR,
     return c_col_idx, c_val, status
 
 
+class OutBuffers:
+    """Reusable output arrays for repeated sums or products of growing size:
+    a row pointer and index / value arrays kept with headroom, handed out as
+    views of the length each call needs (the arrays are reallocated only
+    when a call needs more)."""
+
+    def __init__(self, headroom: float = 1.25):
+        self.headroom = headroom
+        self.ptr = self.idx = self.val = None
+
+    def row_ptr(self, rows: int, dev):
+        if self.ptr is None or self.ptr.numel() != rows + 1 or self.ptr.device != dev:
+            self.ptr = torch.empty(rows + 1, dtype=torch.int32, device=dev)
+        return self.ptr
+
+    def entries(self, nnz: int, dev):
+        if self.idx is None or self.idx.numel() < nnz or self.idx.device != dev:
+            cap = max(int(nnz * self.headroom), 1)
+            self.idx = self.val = None  # let the old arrays go before the new ones exist
+            self.idx = torch.empty(cap, dtype=torch.int32, device=dev)
+            self.val = torch.empty(cap, dtype=torch.float32, device=dev)
+        return self.idx[:nnz], self.val[:nnz]
+
+
 def csr_add(alpha: float, x: DeviceCSR, beta: float, y: DeviceCSR, status=None,
-            stream=None) -> DeviceCSR:
+            stream=None, out: OutBuffers = None) -> DeviceCSR:
     """alpha x + beta y as a DeviceCSR (both passes, one synchronisation to
-    size the output). Raises on a device status flag."""
+    size the output). Raises on a device status flag. ``out`` (OutBuffers)
+    reuses its arrays; x and y must not live in them."""
     dev = x.row_ptr.device
     if status is None:
         status = new_status(dev)
-    c_ptr, _ = seacells_csr_add_rows(x, y, status=status, stream=stream)
+    c_ptr = out.row_ptr(x.shape[0], dev) if out is not None else None
+    c_ptr, _ = seacells_csr_add_rows(x, y, c_row_ptr=c_ptr, status=status, stream=stream)
     raise_on_status(status)
     nnz = int(c_ptr[-1].item()) & 0xffffffff
-    c_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
-    c_val = torch.empty(nnz, dtype=torch.float32, device=dev)
+    if out is not None:
+        c_idx, c_val = out.entries(nnz, dev)
+    else:
+        c_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+        c_val = torch.empty(nnz, dtype=torch.float32, device=dev)
     seacells_csr_add_fill(alpha, x, beta, y, c_ptr, c_idx, c_val, status=status, stream=stream)
     return DeviceCSR(c_ptr, c_idx, c_val, x.shape)
 
@@ -566,15 +595,18 @@ def fw_b_loop(K: DeviceCSR, k2b: DeviceCSR, aat: DeviceCSR, k2at: DeviceCSR, b: 
     ws_b = torch.empty(seacells_fw_b_argmin_workspace(n, k, aat.nnz), dtype=torch.uint8,
                        device=dev)
     ws_v = torch.empty(seacells_fw_b_vertex_workspace(k, n), dtype=torch.uint8, device=dev)
+    # B and K^2 B alternate between two sets of arrays (a sum reads the old
+    # matrix while it writes the new one), kept across steps with headroom
+    b_out, k_out = (OutBuffers(), OutBuffers()), (OutBuffers(), OutBuffers())
     for t in range(steps):
         g = 2.0 / (t + 2.0) if gammas is None else float(gammas[t])
         seacells_fw_b_argmin(k2b, aat, k2at, b, n, k, out_val=mins[t], out_idx=picks[t],
                              gap=gaps[t:t + 1], workspace=ws_b, status=status, stream=stream)
         S = seacells_fw_b_vertex(picks[t], n, 1.0, workspace=ws_v, status=status, stream=stream)
-        b = csr_add(1.0 - g, b, g, S, status=status, stream=stream)
+        b = csr_add(1.0 - g, b, g, S, status=status, stream=stream, out=b_out[t % 2])
         k2s = csr_matmul(K, csr_matmul(K, S, status=status, stream=stream), status=status,
                          stream=stream)
-        k2b = csr_add(1.0 - g, k2b, g, k2s, status=status, stream=stream)
+        k2b = csr_add(1.0 - g, k2b, g, k2s, status=status, stream=stream, out=k_out[t % 2])
     raise_on_status(status)
     return b, k2b, picks, mins, gaps
 
