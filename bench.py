@@ -141,8 +141,10 @@ def time_operands(saa, W, w, stream, reps=3):
     the RSS from K, B and A^T): wall time of the whole build (one host
     synchronisation per product sizes its output) and the device time of each
     step from HIP events, outputs preallocated. For every product, the number
-    of multiply-adds and the gathered bytes they imply (each product reads its
-    B entry's column three times and its value once: 16 B)."""
+    of multiply-adds and the gathered bytes they imply: each reads its B
+    entry's column in the rows pass and its column and value in the fill
+    pass (12 B), plus the column once more (16 B) when the fill pass has to
+    mark the row's columns again (no kept bitmaps)."""
     import torch
     D = saa.DeviceCSR.from_scipy
     K = W.kernel_matrix(w)
@@ -175,19 +177,24 @@ def time_operands(saa, W, w, stream, reps=3):
     plan = (("kb = K B", "kb", dK, dB), ("k2b = K kb", "k2b", dK, ops["kb"]),
             ("t1 = B^T k2b", "t1", ops["bt"], ops["k2b"]), ("aat = A A^T", "aat", ops["a"], dAt),
             ("kat = K A^T", "kat", dK, dAt), ("k2at = K kat", "k2at", dK, ops["kat"]))
-    ws = torch.empty(saa.seacells_csr_matmul_workspace(max(K.shape[0], w.k)), dtype=torch.uint8,
-                     device="cuda")
     for label, nm, a, b in plan:
         c = ops[nm]
+        # the workspace csr_matmul would take (the rows pass keeps its bitmaps)
+        nbytes = saa.seacells_csr_matmul_pattern_workspace(a.shape[0], b.shape[1])
+        kept = 0 < nbytes <= saa.native.PATTERN_WORKSPACE_LIMIT
+        if not kept:
+            nbytes = saa.seacells_csr_matmul_workspace(a.shape[0])
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
 
-        def prod(a=a, b=b, c=c):
+        def prod(a=a, b=b, c=c, ws=ws):
             saa.seacells_csr_matmul_rows(a, b, c.row_ptr, workspace=ws, status=st, stream=stream)
-            saa.seacells_csr_matmul_fill(a, b, c.row_ptr, c.col_idx, c.val, status=st,
-                                         stream=stream)
+            saa.seacells_csr_matmul_fill(a, b, c.row_ptr, c.col_idx, c.val, workspace=ws,
+                                         status=st, stream=stream)
         ms = dev_ms(prod)
         npr = n_products(a, b)
-        res[label] = {"ms": ms, "nnz": c.nnz, "products": npr,
-                      "gather_gbps": 16.0 * npr / (ms * 1e-3) / 1e9}
+        per = 12.0 if kept else 16.0
+        res[label] = {"ms": ms, "nnz": c.nnz, "products": npr, "gather_bytes_per_product": per,
+                      "gather_gbps": per * npr / (ms * 1e-3) / 1e9}
     for label, src, nm in (("bt = B^T", dB, "bt"), ("a = (A^T)^T", dAt, "a")):
         t = ops[nm]
         res[label] = {"ms": dev_ms(lambda src=src, t=t: saa.seacells_csr_transpose(

@@ -44,11 +44,19 @@ extern "C" {
  * (> 0; about 8 bytes per 4096 rows). */
 size_t seacells_csr_matmul_workspace(uint32_t m);
 
+/* Workspace bytes with which the rows pass also keeps every row's output
+ * columns (a bitmap, m * ceil(q / 32) words) for the fill pass, which then
+ * reads them instead of recomputing them: an m x q product with q <= 16384;
+ * 0 when q is larger (the fill pass always recomputes then). */
+size_t seacells_csr_matmul_pattern_workspace(uint32_t m, uint32_t q);
+
 /*
  * Product C = A B, step 1 of 2 (`csr_matmul_csr` on the page): the row
  * pointer of C. a is m x p, b is p x q (else SEACELLS_E_SHAPE).
  * workspace: at least seacells_csr_matmul_workspace(m) bytes, 256-byte
- * aligned (else SEACELLS_E_WORKSPACE).
+ * aligned (else SEACELLS_E_WORKSPACE); with at least
+ * seacells_csr_matmul_pattern_workspace(m, q) bytes it also keeps the rows'
+ * column bitmaps for step 2.
  * c_row_ptr  device [m + 1] u32 out: c_row_ptr[i] = first entry of row i;
  *            c_row_ptr[m] = nnz(C), for the caller to size c_col_idx and
  *            c_val (read it after the stream synchronises). Row i holds every
@@ -67,6 +75,10 @@ int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint3
  * Product C = A B, step 2 of 2: columns (ascending in every row) and values.
  * c_row_ptr must be the output of seacells_csr_matmul_rows for the same a
  * and b; c_col_idx and c_val hold c_row_ptr[m] entries each (device, out).
+ * workspace (may be NULL): the one step 1 used, unchanged since; when it is
+ * at least seacells_csr_matmul_pattern_workspace(m, q) bytes, the row
+ * bitmaps step 1 kept there are used (the caller guarantees they belong to
+ * this a and b), otherwise the columns are recomputed.
  * c[i, c] = sum over the entries j of a's row i, in order, and then over
  * b's row j, of a[i, j] * b[j, c], accumulated in f32 with fused
  * multiply-adds in that order. c_col_idx / c_val may be NULL only when the
@@ -75,7 +87,8 @@ int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint3
  */
 int seacells_csr_matmul_fill(const seacells_csr *a, const seacells_csr *b,
                              const uint32_t *c_row_ptr, uint32_t *c_col_idx, float *c_val,
-                             uint32_t *status, seacells_stream_t stream);
+                             void *workspace, size_t workspace_bytes, uint32_t *status,
+                             seacells_stream_t stream);
 
 /* Workspace bytes seacells_csr_transpose needs for an m x q matrix (> 0). */
 size_t seacells_csr_transpose_workspace(uint32_t m, uint32_t q);

@@ -8,7 +8,8 @@ from .native import (DeviceCSR, SeacellsError, load, new_status, raise_on_status
                      seacells_fw_a_columns, seacells_fw_a_columns_pruned,
                      seacells_fw_a_columns_workspace,
                      seacells_fw_b_apply, seacells_fw_b_argmin, seacells_fw_b_argmin_workspace,
-                     seacells_csr_matmul_workspace, seacells_csr_matmul_rows,
+                     seacells_csr_matmul_workspace, seacells_csr_matmul_pattern_workspace,
+                     seacells_csr_matmul_rows,
                      seacells_csr_matmul_fill, csr_matmul,
                      seacells_csr_transpose_workspace, seacells_csr_transpose,
                      seacells_csr_dot_workspace, seacells_csr_dot, rss, device_operands,

@@ -195,6 +195,18 @@ static int check_any_csr(const seacells_csr *m) {
 
 size_t seacells_csr_matmul_workspace(uint32_t m) { return matmul_workspace(m); }
 
+size_t seacells_csr_matmul_pattern_workspace(uint32_t m, uint32_t q) {
+  const size_t p = matmul_pattern_bytes(m, q);
+  return p == 0 ? 0 : matmul_workspace(m) + p;
+}
+
+// The rows pass's bitmaps, when the workspace holds them.
+static uint32_t *matmul_pattern(void *ws, size_t bytes, uint32_t m, uint32_t q) {
+  const size_t p = matmul_pattern_bytes(m, q);
+  if (ws == nullptr || p == 0 || bytes < matmul_workspace(m) + p) return nullptr;
+  return reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + matmul_workspace(m));
+}
+
 int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint32_t *c_row_ptr,
                              void *workspace, size_t workspace_bytes, uint32_t *status,
                              seacells_stream_t stream) {
@@ -209,14 +221,17 @@ int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint3
   hipError_t e = launch_status_clear(status, s);
   if (e != hipSuccess) return hip_fail(e, "status clear");
   e = launch_spgemm_count(as_csr(a), as_csr(b), a->n_rows, a->n_cols, b->n_cols, c_row_ptr,
-                          workspace, status, s);
+                          workspace,
+                          matmul_pattern(workspace, workspace_bytes, a->n_rows, b->n_cols), status,
+                          s);
   if (e != hipSuccess) return hip_fail(e, "csr_matmul_rows launch");
   return SEACELLS_OK;
 }
 
 int seacells_csr_matmul_fill(const seacells_csr *a, const seacells_csr *b,
                              const uint32_t *c_row_ptr, uint32_t *c_col_idx, float *c_val,
-                             uint32_t *status, seacells_stream_t stream) {
+                             void *workspace, size_t workspace_bytes, uint32_t *status,
+                             seacells_stream_t stream) {
   int rc;
   if ((rc = check_any_csr(a)) != SEACELLS_OK || (rc = check_any_csr(b)) != SEACELLS_OK) return rc;
   if (c_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
@@ -226,7 +241,9 @@ int seacells_csr_matmul_fill(const seacells_csr *a, const seacells_csr *b,
   if (e != hipSuccess) return hip_fail(e, "status clear");
   // (empty outputs may pass NULL arrays: nothing is written then)
   e = launch_spgemm_fill(as_csr(a), as_csr(b), a->n_rows, a->n_cols, b->n_cols, c_row_ptr,
-                         c_col_idx, c_val, status, s);
+                         c_col_idx, c_val,
+                         matmul_pattern(workspace, workspace_bytes, a->n_rows, b->n_cols), status,
+                         s);
   if (e != hipSuccess) return hip_fail(e, "csr_matmul_fill launch");
   return SEACELLS_OK;
 }

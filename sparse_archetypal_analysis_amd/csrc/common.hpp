@@ -181,6 +181,7 @@ hipError_t launch_status_clear(uint32_t *status, hipStream_t stream);
 uint32_t tr_blocks(uint32_t m, uint32_t q);
 size_t transpose_workspace(uint32_t m, uint32_t q);
 size_t matmul_workspace(uint32_t m);
+size_t matmul_pattern_bytes(uint32_t m, uint32_t q);
 size_t add_workspace(uint32_t m);
 hipError_t launch_atoms_count(const uint32_t *atom_idx, const float *atom_val,
                               const uint32_t *atom_cnt, uint32_t n, uint32_t k, uint32_t cap,
@@ -199,10 +200,11 @@ hipError_t launch_vertex(const uint32_t *pick, uint32_t k, uint32_t n, float val
                          hipStream_t stream);
 size_t dot_workspace();
 hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
-                               uint32_t *c_ptr, void *ws, uint32_t *status, hipStream_t stream);
+                               uint32_t *c_ptr, void *ws, uint32_t *pattern, uint32_t *status,
+                               hipStream_t stream);
 hipError_t launch_spgemm_fill(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
                               const uint32_t *c_ptr, uint32_t *c_idx, float *c_val,
-                              uint32_t *status, hipStream_t stream);
+                              const uint32_t *pattern, uint32_t *status, hipStream_t stream);
 hipError_t launch_transpose(Csr a, uint32_t m, uint32_t q, uint32_t *at_ptr, uint32_t *at_idx,
                             float *at_val, void *ws, uint32_t *status, hipStream_t stream);
 hipError_t launch_dot(Csr x, Csr y, uint32_t m, double alpha, double *acc, void *ws,

@@ -236,7 +236,8 @@ __device__ __forceinline__ uint32_t mark_columns(const Csr &a, const Csr &b, uin
 // Output columns per row of A B into cnt[r] (the caller's row pointer + 1).
 __global__ void __launch_bounds__(kSpWaves * kWave)
     spgemm_count_kernel(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
-                        uint32_t *__restrict__ cnt, uint32_t *__restrict__ status) {
+                        uint32_t *__restrict__ cnt, uint32_t *__restrict__ pattern,
+                        uint32_t *__restrict__ status) {
   __shared__ uint32_t bits_all[kSpWaves][kSpWinWords];
   const uint32_t lane = lane_id();
   const uint32_t wib = threadIdx.x / kWave;
@@ -253,7 +254,11 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
       flags |= mark_columns(a, b, p, q, a0, a1, (uint32_t)w0, nw, bits, lane);
       wave_lds_sync();
       uint32_t part = 0;
-      for (uint32_t w = lane; w < nw; w += kWave) part += __popc(bits[w]);
+      for (uint32_t w = lane; w < nw; w += kWave) {
+        const uint32_t x = bits[w];
+        part += __popc(x);
+        if (pattern != nullptr) pattern[(size_t)r * nw + w] = x;  // (one window only)
+      }
       total += wave_sum_u32(part);
       wave_lds_sync();
     }
@@ -375,7 +380,8 @@ hipError_t launch_scan(uint32_t *ptr, uint32_t count, uint64_t *part, uint32_t *
 __global__ void __launch_bounds__(kSpWaves * kWave)
     spgemm_fill_kernel(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
                        const uint32_t *__restrict__ c_ptr, uint32_t *__restrict__ c_idx,
-                       float *__restrict__ c_val, uint32_t *__restrict__ status) {
+                       float *__restrict__ c_val, const uint32_t *__restrict__ pattern,
+                       uint32_t *__restrict__ status) {
   __shared__ uint32_t bits_all[kSpWaves][kSpWinWords];
   __shared__ uint16_t rank_all[kSpWaves][kSpWinWords];
   __shared__ float acc_all[kSpWaves][kSpSlots];
@@ -400,9 +406,13 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
     for (uint64_t w0l = 0; w0l < q; w0l += (uint64_t)kSpWinWords * 32u) {
       const uint32_t w0 = (uint32_t)w0l;
       const uint32_t nw = (uint32_t)u64min(kSpWinWords, (q - w0l + 31u) / 32u);
-      for (uint32_t w = lane; w < nw; w += kWave) bits[w] = 0u;
-      wave_lds_sync();
-      flags |= mark_columns(a, b, p, q, a0, a1, w0, nw, bits, lane);
+      if (pattern != nullptr) {  // the count pass's bitmap of this row (one window)
+        for (uint32_t w = lane; w < nw; w += kWave) bits[w] = pattern[(size_t)r * nw + w];
+      } else {
+        for (uint32_t w = lane; w < nw; w += kWave) bits[w] = 0u;
+        wave_lds_sync();
+        flags |= mark_columns(a, b, p, q, a0, a1, w0, nw, bits, lane);
+      }
       wave_lds_sync();
       // ranks: each lane takes a contiguous run of words
       const uint32_t per = (nw + kWave - 1) / kWave;
@@ -852,6 +862,11 @@ size_t transpose_workspace(uint32_t m, uint32_t q) { return tr_table_bytes(m, q)
 
 size_t matmul_workspace(uint32_t m) { return scan_bytes(m); }
 
+size_t matmul_pattern_bytes(uint32_t m, uint32_t q) {
+  if (q == 0 || q > kSpWinWords * 32u) return 0;  // several column windows: not kept
+  return align_up((size_t)m * ((q + 31u) / 32u) * sizeof(uint32_t), 256);
+}
+
 size_t dot_workspace() { return kDotBlocks * sizeof(double); }
 
 size_t add_workspace(uint32_t m) { return scan_bytes(m); }
@@ -862,14 +877,15 @@ size_t vertex_workspace(uint32_t k, uint32_t n) {
 }
 
 hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
-                               uint32_t *c_ptr, void *ws, uint32_t *status, hipStream_t stream) {
+                               uint32_t *c_ptr, void *ws, uint32_t *pattern, uint32_t *status,
+                               hipStream_t stream) {
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
   if (m > 0) {
     const uint32_t nb = sp_blocks(m, dev, resident_blocks(spgemm_count_kernel, g_count_resident));
     hipLaunchKernelGGL(spgemm_count_kernel, dim3(nb), dim3(kSpWaves * kWave), 0,
-                       stream, a, b, m, p, q, c_ptr + 1, status);
+                       stream, a, b, m, p, q, c_ptr + 1, pattern, status);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return launch_scan(c_ptr, m, static_cast<uint64_t *>(ws), status, stream);
@@ -877,14 +893,14 @@ hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
 
 hipError_t launch_spgemm_fill(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
                               const uint32_t *c_ptr, uint32_t *c_idx, float *c_val,
-                              uint32_t *status, hipStream_t stream) {
+                              const uint32_t *pattern, uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
   if (m == 0) return hipSuccess;
   const uint32_t nb = sp_blocks(m, dev, resident_blocks(spgemm_fill_kernel, g_fill_resident));
   hipLaunchKernelGGL(spgemm_fill_kernel, dim3(nb), dim3(kSpWaves * kWave), 0,
-                     stream, a, b, m, p, q, c_ptr, c_idx, c_val, status);
+                     stream, a, b, m, p, q, c_ptr, c_idx, c_val, pattern, status);
   return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@ FLAGS = {0x1: "CAP_OVERFLOW", 0x2: "PARTIALS_INVALID", 0x4: "B_CAP_OVERFLOW", 0x
 EXPORTS = ("seacells_fw_a_columns_workspace", "seacells_fw_a_columns",
            "seacells_fw_a_columns_pruned",
            "seacells_fw_b_argmin_workspace", "seacells_fw_b_argmin", "seacells_fw_b_apply",
-           "seacells_csr_matmul_workspace", "seacells_csr_matmul_rows", "seacells_csr_matmul_fill",
+           "seacells_csr_matmul_workspace", "seacells_csr_matmul_pattern_workspace",
+           "seacells_csr_matmul_rows", "seacells_csr_matmul_fill",
            "seacells_csr_transpose_workspace", "seacells_csr_transpose",
            "seacells_csr_dot_workspace", "seacells_csr_dot",
            "seacells_csr_add_workspace", "seacells_csr_add_rows", "seacells_csr_add_fill",
@@ -88,7 +89,10 @@ def load():
     lib.seacells_csr_matmul_rows.restype = ctypes.c_int
     lib.seacells_csr_matmul_rows.argtypes = [_CSR_P, _CSR_P, _VP, _VP, ctypes.c_size_t, _VP, _VP]
     lib.seacells_csr_matmul_fill.restype = ctypes.c_int
-    lib.seacells_csr_matmul_fill.argtypes = [_CSR_P, _CSR_P, _VP, _VP, _VP, _VP, _VP]
+    lib.seacells_csr_matmul_fill.argtypes = [_CSR_P, _CSR_P, _VP, _VP, _VP, _VP, ctypes.c_size_t,
+                                             _VP, _VP]
+    lib.seacells_csr_matmul_pattern_workspace.restype = ctypes.c_size_t
+    lib.seacells_csr_matmul_pattern_workspace.argtypes = [_U32, _U32]
     lib.seacells_csr_transpose_workspace.restype = ctypes.c_size_t
     lib.seacells_csr_transpose_workspace.argtypes = [_U32, _U32]
     lib.seacells_csr_transpose.restype = ctypes.c_int
@@ -342,33 +346,51 @@ def seacells_csr_matmul_rows(a: DeviceCSR, b: DeviceCSR, c_row_ptr=None, workspa
     return c_row_ptr, status
 
 
+def seacells_csr_matmul_pattern_workspace(m: int, q: int) -> int:
+    return int(load().seacells_csr_matmul_pattern_workspace(m, q))
+
+
 def seacells_csr_matmul_fill(a: DeviceCSR, b: DeviceCSR, c_row_ptr, c_col_idx, c_val,
-                             status=None, stream=None):
-    """Columns and values of a @ b into buffers sized by c_row_ptr[-1]."""
+                             workspace=None, status=None, stream=None):
+    """Columns and values of a @ b into buffers sized by c_row_ptr[-1]
+    (``workspace``: the rows pass's, to reuse the row bitmaps it kept)."""
     lib = load()
     if status is None:
         status = new_status(a.row_ptr.device)
     sa, sb = a.struct(), b.struct()
     rc = lib.seacells_csr_matmul_fill(ctypes.byref(sa), ctypes.byref(sb), _ptr(c_row_ptr),
                                       _ptr(c_col_idx) if c_col_idx.numel() else None,
-                                      _ptr(c_val) if c_val.numel() else None, _ptr(status),
-                                      _stream(stream))
+                                      _ptr(c_val) if c_val.numel() else None,
+                                      _ptr(workspace),
+                                      0 if workspace is None else workspace.numel(),
+                                      _ptr(status), _stream(stream))
     _check_rc(rc)
     return c_col_idx, c_val, status
 
 
+PATTERN_WORKSPACE_LIMIT = 4 << 30  # bytes of row bitmaps csr_matmul keeps between its passes
+
+
 def csr_matmul(a: DeviceCSR, b: DeviceCSR, status=None, stream=None) -> DeviceCSR:
     """a @ b as a DeviceCSR: both passes, with one synchronisation between
-    them to size the outputs. Raises on a device status flag."""
+    them to size the outputs; the rows pass keeps its row bitmaps for the
+    fill pass when they take at most PATTERN_WORKSPACE_LIMIT bytes. Raises on
+    a device status flag."""
     dev = a.row_ptr.device
     if status is None:
         status = new_status(dev)
-    c_ptr, _ = seacells_csr_matmul_rows(a, b, status=status, stream=stream)
+    m, q = a.shape[0], b.shape[1]
+    ws_bytes = seacells_csr_matmul_pattern_workspace(m, q)
+    if ws_bytes == 0 or ws_bytes > PATTERN_WORKSPACE_LIMIT:
+        ws_bytes = seacells_csr_matmul_workspace(m)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    c_ptr, _ = seacells_csr_matmul_rows(a, b, workspace=ws, status=status, stream=stream)
     raise_on_status(status)  # synchronises; c_ptr[-1] is valid after it
     nnz = int(c_ptr[-1].item()) & 0xffffffff
     c_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
     c_val = torch.empty(nnz, dtype=torch.float32, device=dev)
-    seacells_csr_matmul_fill(a, b, c_ptr, c_idx, c_val, status=status, stream=stream)
+    seacells_csr_matmul_fill(a, b, c_ptr, c_idx, c_val, workspace=ws, status=status,
+                             stream=stream)
     return DeviceCSR(c_ptr, c_idx, c_val, (a.shape[0], b.shape[1]))
 
 

@@ -184,8 +184,13 @@ def test_sparse_ops_reject_bad_arguments_on_host():
     assert lib.seacells_csr_matmul_rows(P(a), P(b), out, None, mneed, st, None) == -3
     assert lib.seacells_csr_matmul_rows(P(a), P(b), out, ws, mneed - 1, st, None) == -3
     assert lib.seacells_csr_matmul_rows(P(a), P(b), out, ws + 4, mneed, st, None) == -3
-    assert lib.seacells_csr_matmul_fill(P(a), P(csr(6, 4, 2)), out, out, out, st, None) == -2
-    assert lib.seacells_csr_matmul_fill(P(a), P(b), None, out, out, st, None) == -1
+    assert lib.seacells_csr_matmul_fill(P(a), P(csr(6, 4, 2)), out, out, out, None, 0, st,
+                                        None) == -2
+    assert lib.seacells_csr_matmul_fill(P(a), P(b), None, out, out, None, 0, st, None) == -1
+    # the kept row bitmaps: m * ceil(q / 32) words after the scan partials, none past 16384 columns
+    assert lib.seacells_csr_matmul_pattern_workspace(5, 100) >= mneed + 5 * 4 * 4
+    assert lib.seacells_csr_matmul_pattern_workspace(5, 16384) > 0
+    assert lib.seacells_csr_matmul_pattern_workspace(5, 16385) == 0
     assert lib.seacells_csr_matmul_rows(P(csr(5, 7, 2 ** 31)), P(b), out, ws, mneed, st,
                                         None) == -4
     assert lib.seacells_csr_matmul_rows(P(csr(5, 7, 3, ptr=None)), P(b), out, ws, mneed, st,

@@ -103,6 +103,34 @@ def test_product_matches_oracle(case):
     print("\n%s: nnz %d, max error / sum|ab| = %.2e" % (case, got.nnz, rel))
 
 
+def test_product_with_kept_bitmaps_equals_recomputed_columns():
+    # the fill pass reading the rows pass's bitmaps, or marking the columns
+    # again, writes the same product bit for bit
+    rng = np.random.default_rng(12)
+    a = rand_csr(rng, 3000, 400, 9, empty_every=7)
+    b = rand_csr(rng, 400, 9000, 30, empty_every=5)
+    da, db = dev(a), dev(b)
+    m, q = a.shape[0], b.shape[1]
+    outs = []
+    for nbytes in (saa.seacells_csr_matmul_workspace(m),
+                   saa.seacells_csr_matmul_pattern_workspace(m, q)):
+        st = saa.new_status()
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        ptr, _ = saa.seacells_csr_matmul_rows(da, db, workspace=ws, status=st)
+        torch.cuda.synchronize()
+        nnz = int(ptr[-1].item())
+        idx = torch.empty(nnz, dtype=torch.int32, device="cuda")
+        val = torch.empty(nnz, dtype=torch.float32, device="cuda")
+        saa.seacells_csr_matmul_fill(da, db, ptr, idx, val, workspace=ws, status=st)
+        torch.cuda.synchronize()
+        assert saa.status_flags(st) == []
+        outs.append((ptr.cpu().numpy(), idx.cpu().numpy(), val.cpu().numpy().view(np.uint32)))
+    assert saa.seacells_csr_matmul_pattern_workspace(m, q) > saa.seacells_csr_matmul_workspace(m)
+    for x, y in zip(outs[0], outs[1]):
+        assert np.array_equal(x, y)
+    check_product(host(saa.csr_matmul(da, db)), S.matmul(a, b), what="kept bitmaps")
+
+
 def test_product_keeps_cancellation_as_explicit_zero():
     a = sp.csr_matrix((np.array([1.0, -1.0, 2.0], np.float32), np.array([0, 1, 1]),
                        np.array([0, 2, 3])), shape=(2, 2))
