@@ -291,8 +291,8 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the multi-GPU sharding of this path is "
-              "described in DESIGN.md and not built; run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the path's multi-GPU sharding is a design, "
+              "not built; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
