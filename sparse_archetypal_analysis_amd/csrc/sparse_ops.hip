@@ -237,7 +237,7 @@ __device__ __forceinline__ uint32_t mark_columns(const Csr &a, const Csr &b, uin
 __global__ void __launch_bounds__(kSpWaves * kWave)
     spgemm_count_kernel(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
                         uint32_t *__restrict__ cnt, uint32_t *__restrict__ pattern,
-                        uint32_t *__restrict__ status) {
+                        uint32_t *__restrict__ long_rows, uint32_t *__restrict__ status) {
   __shared__ uint32_t bits_all[kSpWaves][kSpWinWords];
   const uint32_t lane = lane_id();
   const uint32_t wib = threadIdx.x / kWave;
@@ -262,9 +262,17 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
       total += wave_sum_u32(part);
       wave_lds_sync();
     }
-    if (lane == 0) cnt[r] = total > 0xffffffffull ? 0xffffffffu : (uint32_t)total;
+    if (lane == 0) {
+      cnt[r] = total > 0xffffffffull ? 0xffffffffu : (uint32_t)total;
+      // rows of more than one value window: listed for the fill pass (any order)
+      if (long_rows != nullptr && total > kSpSlots) long_rows[1u + atomicAdd(long_rows, 1u)] = r;
+    }
   }
   if (flags != 0) atomicOr(status, flags);
+}
+
+__global__ void __launch_bounds__(64) zero_word_kernel(uint32_t *__restrict__ p) {
+  if (threadIdx.x == 0) p[0] = 0u;
 }
 
 // Row pointers from counts, in place: ptr[0] = 0 and ptr[1 .. count]
@@ -381,7 +389,7 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
     spgemm_fill_kernel(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
                        const uint32_t *__restrict__ c_ptr, uint32_t *__restrict__ c_idx,
                        float *__restrict__ c_val, const uint32_t *__restrict__ pattern,
-                       uint32_t *__restrict__ status) {
+                       const uint32_t *__restrict__ long_rows, uint32_t *__restrict__ status) {
   __shared__ uint32_t bits_all[kSpWaves][kSpWinWords];
   __shared__ uint16_t rank_all[kSpWaves][kSpWinWords];
   __shared__ float acc_all[kSpWaves][kSpSlots];
@@ -393,87 +401,148 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
   float *acc = acc_all[wib];
   uint16_t *colof = colof_all[wib];
   uint32_t flags = 0;
-  for (uint32_t r = blockIdx.x * kSpWaves + wib; r < m; r += gridDim.x * kSpWaves) {
-    const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
-    const uint32_t cnt = end >= base ? end - base : 0u;
-    if (cnt > 0 && (c_idx == nullptr || c_val == nullptr)) {  // no output arrays given
-      flags |= kFlagBadIndex;
-      continue;
+
+  // ranks of the bitmap words in bits[0, nw): each lane takes a contiguous run
+  // of words; returns the columns in the window, sets the lane's run and first
+  // rank
+  auto ranks = [&](uint32_t nw, uint32_t &v0w, uint32_t &v1w, uint32_t &first) -> uint32_t {
+    const uint32_t per = (nw + kWave - 1) / kWave;
+    v0w = min(lane * per, nw), v1w = min(v0w + per, nw);
+    uint32_t part = 0;
+    for (uint32_t w = v0w; w < v1w; ++w) part += __popc(bits[w]);
+    uint32_t run = wave_excl_scan_u32(part, lane);
+    const uint32_t nwin = wave_sum_u32(part);
+    first = run;
+    for (uint32_t w = v0w; w < v1w; ++w) {
+      rank[w] = (uint16_t)run;  // < 16384: ranks within one column window
+      run += __popc(bits[w]);
     }
-    uint32_t a0, a1;
-    if (!sp_row(a, r, a0, a1)) flags |= kFlagBadIndex;
-    uint32_t done = 0;
-    for (uint64_t w0l = 0; w0l < q; w0l += (uint64_t)kSpWinWords * 32u) {
-      const uint32_t w0 = (uint32_t)w0l;
-      const uint32_t nw = (uint32_t)u64min(kSpWinWords, (q - w0l + 31u) / 32u);
-      if (pattern != nullptr) {  // the count pass's bitmap of this row (one window)
-        for (uint32_t w = lane; w < nw; w += kWave) bits[w] = pattern[(size_t)r * nw + w];
+    wave_lds_sync();
+    return nwin;
+  };
+  // ranks s0 .. s0 + ns of row r's column window w0 (the window's first
+  // output at base + done): accumulate them and write them out
+  auto value_window = [&](uint32_t base, uint32_t cnt, uint32_t a0, uint32_t a1, uint32_t w0,
+                          uint32_t nw, uint32_t done, uint32_t s0, uint32_t ns, uint32_t v0w,
+                          uint32_t v1w, uint32_t first) {
+    for (uint32_t s = lane; s < ns; s += kWave) acc[s] = 0.0f;
+    // slot -> column within the window, from each lane's run of words
+    {
+      uint32_t pos = first;
+      for (uint32_t w = v0w; w < v1w && pos < s0 + ns; ++w) {
+        uint32_t x = bits[w];
+        while (x != 0u) {
+          const uint32_t bpos = (uint32_t)__builtin_ctz(x);
+          x &= x - 1u;
+          if (pos >= s0 && pos < s0 + ns) colof[pos - s0] = (uint16_t)(w * 32u + bpos);
+          ++pos;
+        }
+      }
+    }
+    wave_lds_sync();
+    // (bad indices were flagged by the marking pass)
+    for_products<true>(a, b, p, a0, a1, lane,
+                       [&](bool valid, uint32_t c, float bv, float a_own, uint32_t own,
+                           uint64_t owners) {
+                         const uint32_t rel = c - w0;
+                         uint32_t pos = 0xffffffffu;
+                         if (valid && c < q && rel < nw * 32u) {
+                           const uint32_t w = rel >> 5, bit = 1u << (rel & 31u);
+                           pos = rank[w] + __popc(bits[w] & (bit - 1u)) - s0;
+                         }
+                         const bool mine = pos < ns;
+                         // entry by entry: the adds into one slot keep A-entry order
+                         for (uint64_t mm = owners; mm != 0; mm &= mm - 1ull) {
+                           const uint32_t l = (uint32_t)__builtin_ctzll(mm);
+                           if (mine && own == l) acc[pos] = __builtin_fmaf(a_own, bv, acc[pos]);
+                           wave_lds_sync();
+                         }
+                       });
+    // out in column order, consecutive lanes on consecutive entries
+    for (uint32_t s = lane; s < ns; s += kWave) {
+      const uint32_t o = done + s0 + s;
+      if (o < cnt) {
+        c_idx[(size_t)base + o] = w0 + colof[s];
+        c_val[(size_t)base + o] = acc[s];
+      }
+    }
+    wave_lds_sync();
+  };
+
+  const uint32_t gw = blockIdx.x * kSpWaves + wib, nwaves = gridDim.x * kSpWaves;
+  if (pattern != nullptr) {
+    // one column window with the rows pass's bitmaps: the units are (row,
+    // value window), window 0 of every row, then the further windows of the
+    // long rows the rows pass listed, so a long row's windows run on
+    // different waves (each output still sums its products in order)
+    const uint32_t nw = (q + 31u) / 32u;
+    const uint32_t nvw = (q + kSpSlots - 1u) / kSpSlots;  // value windows a row can need
+    const uint32_t nlong = long_rows != nullptr ? min(long_rows[0], m) : 0u;
+    const uint64_t units = (uint64_t)m + (uint64_t)nlong * (nvw > 1u ? nvw - 1u : 0u);
+    for (uint64_t u = gw; u < units; u += nwaves) {
+      uint32_t r, vw;
+      if (u < m) {
+        r = (uint32_t)u, vw = 0;
       } else {
+        const uint64_t v = u - m;
+        r = long_rows[1u + (uint32_t)(v % nlong)];
+        vw = 1u + (uint32_t)(v / nlong);
+        if (r >= m) {  // (the list holds rows below m)
+          flags |= kFlagBadIndex;
+          continue;
+        }
+      }
+      const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
+      const uint32_t cnt = end >= base ? end - base : 0u;
+      const uint32_t s0 = vw * kSpSlots;
+      if (vw > 0 && s0 >= cnt) continue;
+      if (cnt > 0 && (c_idx == nullptr || c_val == nullptr)) {  // no output arrays given
+        flags |= kFlagBadIndex;
+        continue;
+      }
+      uint32_t a0, a1;
+      if (!sp_row(a, r, a0, a1)) flags |= kFlagBadIndex;
+      for (uint32_t w = lane; w < nw; w += kWave) bits[w] = pattern[(size_t)r * nw + w];
+      wave_lds_sync();
+      uint32_t v0w, v1w, first;
+      const uint32_t nwin = ranks(nw, v0w, v1w, first);
+      if (vw == 0 && nwin != cnt) flags |= kFlagBadIndex;  // not the rows pass's pointers
+      if (s0 < nwin)
+        value_window(base, cnt, a0, a1, 0u, nw, 0u, s0, min(kSpSlots, nwin - s0), v0w, v1w,
+                     first);
+      if (vw == 0 && nwin > kSpSlots && long_rows == nullptr) {  // (no list: finish the row here)
+        for (uint32_t s1 = kSpSlots; s1 < nwin; s1 += kSpSlots)
+          value_window(base, cnt, a0, a1, 0u, nw, 0u, s1, min(kSpSlots, nwin - s1), v0w, v1w,
+                       first);
+      }
+    }
+  } else {
+    for (uint32_t r = gw; r < m; r += nwaves) {
+      const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
+      const uint32_t cnt = end >= base ? end - base : 0u;
+      if (cnt > 0 && (c_idx == nullptr || c_val == nullptr)) {  // no output arrays given
+        flags |= kFlagBadIndex;
+        continue;
+      }
+      uint32_t a0, a1;
+      if (!sp_row(a, r, a0, a1)) flags |= kFlagBadIndex;
+      uint32_t done = 0;
+      for (uint64_t w0l = 0; w0l < q; w0l += (uint64_t)kSpWinWords * 32u) {
+        const uint32_t w0 = (uint32_t)w0l;
+        const uint32_t nw = (uint32_t)u64min(kSpWinWords, (q - w0l + 31u) / 32u);
         for (uint32_t w = lane; w < nw; w += kWave) bits[w] = 0u;
         wave_lds_sync();
         flags |= mark_columns(a, b, p, q, a0, a1, w0, nw, bits, lane);
-      }
-      wave_lds_sync();
-      // ranks: each lane takes a contiguous run of words
-      const uint32_t per = (nw + kWave - 1) / kWave;
-      const uint32_t v0w = min(lane * per, nw), v1w = min(v0w + per, nw);
-      uint32_t part = 0;
-      for (uint32_t w = v0w; w < v1w; ++w) part += __popc(bits[w]);
-      uint32_t run = wave_excl_scan_u32(part, lane);
-      const uint32_t nwin = wave_sum_u32(part);
-      for (uint32_t w = v0w; w < v1w; ++w) {
-        rank[w] = (uint16_t)run;  // < 16384: ranks within one column window
-        run += __popc(bits[w]);
-      }
-      wave_lds_sync();
-      for (uint32_t s0 = 0; s0 < nwin; s0 += kSpSlots) {
-        const uint32_t ns = min(kSpSlots, nwin - s0);
-        for (uint32_t s = lane; s < ns; s += kWave) acc[s] = 0.0f;
-        // slot -> column within the window, from each lane's run of words
-        {
-          uint32_t pos = run - part;  // the lane's first rank (run ended at first + part)
-          for (uint32_t w = v0w; w < v1w && pos < s0 + ns; ++w) {
-            uint32_t x = bits[w];
-            while (x != 0u) {
-              const uint32_t bpos = (uint32_t)__builtin_ctz(x);
-              x &= x - 1u;
-              if (pos >= s0 && pos < s0 + ns) colof[pos - s0] = (uint16_t)(w * 32u + bpos);
-              ++pos;
-            }
-          }
-        }
         wave_lds_sync();
-        // (bad indices were flagged by the marking pass)
-        for_products<true>(a, b, p, a0, a1, lane,
-                           [&](bool valid, uint32_t c, float bv, float a_own, uint32_t own,
-                               uint64_t owners) {
-                             const uint32_t rel = c - w0;
-                             uint32_t pos = 0xffffffffu;
-                             if (valid && c < q && rel < nw * 32u) {
-                               const uint32_t w = rel >> 5, bit = 1u << (rel & 31u);
-                               pos = rank[w] + __popc(bits[w] & (bit - 1u)) - s0;
-                             }
-                             const bool mine = pos < ns;
-                             // entry by entry: the adds into one slot keep A-entry order
-                             for (uint64_t mm = owners; mm != 0; mm &= mm - 1ull) {
-                               const uint32_t l = (uint32_t)__builtin_ctzll(mm);
-                               if (mine && own == l) acc[pos] = __builtin_fmaf(a_own, bv, acc[pos]);
-                               wave_lds_sync();
-                             }
-                           });
-        // out in column order, consecutive lanes on consecutive entries
-        for (uint32_t s = lane; s < ns; s += kWave) {
-          const uint32_t o = done + s0 + s;
-          if (o < cnt) {
-            c_idx[(size_t)base + o] = w0 + colof[s];
-            c_val[(size_t)base + o] = acc[s];
-          }
-        }
-        wave_lds_sync();
+        uint32_t v0w, v1w, first;
+        const uint32_t nwin = ranks(nw, v0w, v1w, first);
+        for (uint32_t s0 = 0; s0 < nwin; s0 += kSpSlots)
+          value_window(base, cnt, a0, a1, w0, nw, done, s0, min(kSpSlots, nwin - s0), v0w, v1w,
+                       first);
+        done += nwin;
       }
-      done += nwin;
+      if (done != cnt) flags |= kFlagBadIndex;  // row pointers not those of the count pass
     }
-    if (done != cnt) flags |= kFlagBadIndex;  // row pointers not those of the count pass
   }
   if (flags != 0) atomicOr(status, flags);
 }
@@ -862,9 +931,23 @@ size_t transpose_workspace(uint32_t m, uint32_t q) { return tr_table_bytes(m, q)
 
 size_t matmul_workspace(uint32_t m) { return scan_bytes(m); }
 
-size_t matmul_pattern_bytes(uint32_t m, uint32_t q) {
+// The rows pass's bitmaps (m x ceil(q / 32) words), then its list of rows
+// with more than one value window (a count, then the rows).
+static size_t matmul_bitmap_bytes(uint32_t m, uint32_t q) {
   if (q == 0 || q > kSpWinWords * 32u) return 0;  // several column windows: not kept
   return align_up((size_t)m * ((q + 31u) / 32u) * sizeof(uint32_t), 256);
+}
+
+size_t matmul_pattern_bytes(uint32_t m, uint32_t q) {
+  const size_t bm = matmul_bitmap_bytes(m, q);
+  return bm == 0 ? 0 : bm + align_up(((size_t)m + 1) * sizeof(uint32_t), 256);
+}
+
+static uint32_t *long_row_list(uint32_t *pattern, uint32_t m, uint32_t q) {
+  return pattern == nullptr
+             ? nullptr
+             : reinterpret_cast<uint32_t *>(reinterpret_cast<char *>(pattern) +
+                                            matmul_bitmap_bytes(m, q));
 }
 
 size_t dot_workspace() { return kDotBlocks * sizeof(double); }
@@ -882,10 +965,15 @@ hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
+  uint32_t *list = long_row_list(pattern, m, q);
+  if (list != nullptr) {
+    hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(64), 0, stream, list);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (m > 0) {
     const uint32_t nb = sp_blocks(m, dev, resident_blocks(spgemm_count_kernel, g_count_resident));
     hipLaunchKernelGGL(spgemm_count_kernel, dim3(nb), dim3(kSpWaves * kWave), 0,
-                       stream, a, b, m, p, q, c_ptr + 1, pattern, status);
+                       stream, a, b, m, p, q, c_ptr + 1, pattern, list, status);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return launch_scan(c_ptr, m, static_cast<uint64_t *>(ws), status, stream);
@@ -900,7 +988,8 @@ hipError_t launch_spgemm_fill(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
   if (m == 0) return hipSuccess;
   const uint32_t nb = sp_blocks(m, dev, resident_blocks(spgemm_fill_kernel, g_fill_resident));
   hipLaunchKernelGGL(spgemm_fill_kernel, dim3(nb), dim3(kSpWaves * kWave), 0,
-                     stream, a, b, m, p, q, c_ptr, c_idx, c_val, pattern, status);
+                     stream, a, b, m, p, q, c_ptr, c_idx, c_val, pattern,
+                     long_row_list(const_cast<uint32_t *>(pattern), m, q), status);
   return hipGetLastError();
 }
 

@@ -70,6 +70,9 @@ PRODUCT_CASES = {
     "wide_rows": (12, 64, 20000, 10, 120, {"dense_rows_a": (0, 5, 11)}),
     "one_column": (100, 30, 1, 5, 1, {}),
     "many_rows": (5000, 300, 700, 4, 6, {"empty_every_a": 11}),
+    # one column window (rows pass keeps its bitmaps) and rows of up to 7
+    # value windows: their further windows run as units of their own
+    "long_rows_kept": (300, 64, 12000, 6, 110, {"dense_rows_a": (0, 7, 150, 299)}),
 }
 
 
@@ -98,7 +101,7 @@ def test_product_matches_oracle(case):
     got = product_on_gpu(a, b)
     want = S.matmul(a, b)
     rel = check_product(got, want, what=case)
-    if case == "wide_rows":
+    if case in ("wide_rows", "long_rows_kept"):
         assert np.diff(got.indptr).max() > 2048  # several value windows per row
     print("\n%s: nnz %d, max error / sum|ab| = %.2e" % (case, got.nnz, rel))
 
@@ -107,7 +110,7 @@ def test_product_with_kept_bitmaps_equals_recomputed_columns():
     # the fill pass reading the rows pass's bitmaps, or marking the columns
     # again, writes the same product bit for bit
     rng = np.random.default_rng(12)
-    a = rand_csr(rng, 3000, 400, 9, empty_every=7)
+    a = rand_csr(rng, 3000, 400, 9, empty_every=7, dense_rows=(3, 1500, 2999))
     b = rand_csr(rng, 400, 9000, 30, empty_every=5)
     da, db = dev(a), dev(b)
     m, q = a.shape[0], b.shape[1]
