@@ -4,12 +4,17 @@
 // order of the original rows), and the sums the RSS identity needs
 // (||K - K B A||^2 = <K, K> - 2 <K^2 B, A^T> + <B^T K^2 B, A A^T>).
 //
-// Product C = A B, one wave per row of A:
-//   a bitmap of the row's output columns is built in LDS (a window of
-//   16384 columns at a time), a popcount prefix over it gives every column
-//   its rank, and the products are added into an LDS slot per rank (a window
-//   of 1024 ranks at a time), then written out in column order (an LDS map
-//   from slot to column lets consecutive lanes store consecutive entries). The
+// Product C = A B in two passes, one wave per row of A. The rows pass builds
+//   a bitmap of the row's output columns in LDS (a window of 16384 columns at
+//   a time) and counts them; a three-pass scan makes the counts the row
+//   pointer. With one column window it can keep every row's bitmap and a
+//   list of the rows longer than one value window for the fill pass. The
+//   fill pass takes the bitmap (kept, or built again), a popcount prefix over
+//   it gives every column its rank, and the products are added into an LDS
+//   slot per rank (a window of 1024 ranks at a time), then written out in
+//   column order (an LDS map from slot to column lets consecutive lanes store
+//   consecutive entries); with kept bitmaps the value windows of the listed
+//   rows run as units of their own on other waves. The
 //   products of the row are flattened over the lanes: 64 entries of A at a
 //   time, one per lane, load their B row bounds together; a scan of the B row
 //   lengths numbers the products (A entry, then B entry) and each window of
@@ -35,6 +40,8 @@
 //   looks each entry of the operand with fewer entries up in the other's row
 //   (binary search), products in f64; the rows' partial sums are added in a
 //   fixed order.
+// The A update's atoms as A^T: a thread per cell counts the atoms of non-zero
+//   weight, then a wave per cell places each at its rank by column.
 #include "common.hpp"
 
 namespace seacells {
