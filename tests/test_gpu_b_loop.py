@@ -131,3 +131,26 @@ def test_b_loop_with_a_step_size_table():
     assert np.max(np.abs(host(res[0]).toarray() - orc.b)) <= 1e-5
     kd = host(res[1]).toarray().astype(np.float64)
     assert np.all(np.abs(kd - orc.k2b) <= 5e-5 * np.abs(orc.k2b) + 1e-6 * np.max(np.abs(orc.k2b)))
+
+
+def test_b_loop_on_a_tiny_problem():
+    # n = 7 cells, k = 3 archetypes, every operand formed here in f64 from a
+    # random symmetric K, column-stochastic B and A, then cast to f32
+    rng = np.random.default_rng(77)
+    n, k, T = 7, 3, 6
+    Kd = rng.uniform(0, 1, size=(n, n)) * (rng.random((n, n)) < 0.5)
+    Kd = (Kd + Kd.T) / 2 + np.eye(n)
+    Bd = np.zeros((n, k))
+    for c in range(k):
+        sup = rng.choice(n, size=2, replace=False)
+        Bd[sup, c] = rng.dirichlet(np.ones(2))
+    Ad = rng.dirichlet(np.ones(k), size=n).T
+    f32 = lambda m: sp.csr_matrix(np.asarray(m, np.float32))
+    K, B = f32(Kd), f32(Bd)
+    Kf, Bf, Af = (np.asarray(M.toarray() if sp.issparse(M) else M, np.float64)
+                  for M in (K, B, f32(Ad)))
+    k2b, aat, k2at = f32(Kf @ Kf @ Bf), f32(Af @ Af.T), f32(Kf @ Kf @ Af.T)
+    res = saa.fw_b_loop(dev(K), dev(k2b), dev(aat), dev(k2at), dev(B), T)
+    torch.cuda.synchronize()
+    flips, krel = parity.check_b_loop(K, B, aat, k2at, T, res)
+    assert krel <= 5e-5

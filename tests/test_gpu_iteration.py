@@ -7,7 +7,8 @@ library. The oracle rebuilds every operand in f64 from K, B and A (never
 from a device output), replays the GPU's A picks (parity.check_a: each pick
 the oracle's or within the tie rule, the weights within 1e-5), forms A^T from
 its own replayed columns, then replays the GPU's B picks on its own A A^T and
-K^2 A^T (parity.check_b_loop), and evaluates ||K - K B A||^2 of its final pair
+K^2 A^T (parity.check_b_loop, with its operands' own f64 A: the minimum
+values also get 1e-5 of G's term scale), and evaluates ||K - K B A||^2 of its final pair
 through the expansion; the device RSS must agree within 1e-5 of the scale of
 the terms that cancel in it.
 """
@@ -71,7 +72,7 @@ def test_atoms_with_a_repeated_column_are_flagged():
     assert "BAD_INDEX" in saa.status_flags(st)
 
 
-@pytest.mark.parametrize("name,steps_b", [("c1", 6), ("c2", 4)])
+@pytest.mark.parametrize("name,steps_b", [("c1", 6), ("c2", 4), ("c3", 2)])
 def test_outer_iteration_against_oracle_replay(name, steps_b):
     w = W.make(name)
     K = W.kernel_matrix(w)
@@ -106,7 +107,7 @@ def test_outer_iteration_against_oracle_replay(name, steps_b):
     aat_o = S.matmul(S.transpose(at_o), at_o).csr()
     k2at_o = S.matmul(K, S.matmul(K, at_o).csr()).csr()
     res_b = (res["b"], res["k2b"], res["b_picks"], res["b_mins"], res["b_gaps"])
-    flips, krel = parity.check_b_loop(K, w.b, aat_o, k2at_o, steps_b, res_b)
+    flips, krel = parity.check_b_loop(K, w.b, aat_o, k2at_o, steps_b, res_b, own_operands=True)
     # RSS of the final pair, from the oracle's own final B and A
     from oracle import b_loop as BL
     orc = BL.fw_b_loop(K, w.b, aat_o, k2at_o, steps_b,
