@@ -78,7 +78,10 @@ int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint3
  * workspace (may be NULL): the one step 1 used, unchanged since; when it is
  * at least seacells_csr_matmul_pattern_workspace(m, q) bytes, the row
  * bitmaps step 1 kept there are used (the caller guarantees they belong to
- * this a and b), otherwise the columns are recomputed.
+ * this a and b), otherwise the columns are recomputed. c_capacity: the
+ * entries c_col_idx and c_val hold; when c_row_ptr[m] exceeds it nothing is
+ * written and SEACELLS_FLAG_OUTPUT_TOO_LARGE is raised (so a caller that
+ * sizes the outputs by a bound, without reading c_row_ptr[m], stays safe).
  * c[i, c] = sum over the entries j of a's row i, in order, and then over
  * b's row j, of a[i, j] * b[j, c], accumulated in f32 with fused
  * multiply-adds in that order. c_col_idx / c_val may be NULL only when the
@@ -87,8 +90,8 @@ int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint3
  */
 int seacells_csr_matmul_fill(const seacells_csr *a, const seacells_csr *b,
                              const uint32_t *c_row_ptr, uint32_t *c_col_idx, float *c_val,
-                             void *workspace, size_t workspace_bytes, uint32_t *status,
-                             seacells_stream_t stream);
+                             size_t c_capacity, void *workspace, size_t workspace_bytes,
+                             uint32_t *status, seacells_stream_t stream);
 
 /* Workspace bytes seacells_csr_transpose needs for an m x q matrix (> 0). */
 size_t seacells_csr_transpose_workspace(uint32_t m, uint32_t q);
@@ -142,11 +145,13 @@ int seacells_csr_add_rows(const seacells_csr *x, const seacells_csr *y, uint32_t
  * seacells_csr_add_rows's output for the same x and y (else BAD_INDEX and no
  * write beyond its row sizes). Each value is alpha x and beta y rounded to
  * f32 separately, then their sum rounded (alpha x or beta y alone where only
- * one operand stores the column).
+ * one operand stores the column). c_capacity: the entries c_col_idx and
+ * c_val hold; when c_row_ptr[m] exceeds it nothing is written and
+ * SEACELLS_FLAG_OUTPUT_TOO_LARGE is raised.
  */
 int seacells_csr_add_fill(float alpha, const seacells_csr *x, float beta, const seacells_csr *y,
                           const uint32_t *c_row_ptr, uint32_t *c_col_idx, float *c_val,
-                          uint32_t *status, seacells_stream_t stream);
+                          size_t c_capacity, uint32_t *status, seacells_stream_t stream);
 
 /* Workspace bytes seacells_fw_b_vertex needs for k columns and n rows (> 0). */
 size_t seacells_fw_b_vertex_workspace(uint32_t k, uint32_t n);

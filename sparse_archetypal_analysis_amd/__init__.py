@@ -16,5 +16,5 @@ from .native import (DeviceCSR, SeacellsError, load, new_status, raise_on_status
                      seacells_csr_add_workspace, seacells_csr_add_rows, seacells_csr_add_fill,
                      csr_add, seacells_fw_b_vertex_workspace, seacells_fw_b_vertex, fw_b_loop,
                      seacells_fw_a_to_csr_workspace, seacells_fw_a_to_csr_rows,
-                     seacells_fw_a_to_csr_fill, fw_a_to_csr, outer_iteration,
+                     seacells_fw_a_to_csr_fill, fw_a_to_csr, outer_iteration, csr_trim,
                      status_flags)

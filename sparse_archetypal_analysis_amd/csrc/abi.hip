@@ -230,8 +230,8 @@ int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint3
 
 int seacells_csr_matmul_fill(const seacells_csr *a, const seacells_csr *b,
                              const uint32_t *c_row_ptr, uint32_t *c_col_idx, float *c_val,
-                             void *workspace, size_t workspace_bytes, uint32_t *status,
-                             seacells_stream_t stream) {
+                             size_t c_capacity, void *workspace, size_t workspace_bytes,
+                             uint32_t *status, seacells_stream_t stream) {
   int rc;
   if ((rc = check_any_csr(a)) != SEACELLS_OK || (rc = check_any_csr(b)) != SEACELLS_OK) return rc;
   if (c_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
@@ -241,7 +241,7 @@ int seacells_csr_matmul_fill(const seacells_csr *a, const seacells_csr *b,
   if (e != hipSuccess) return hip_fail(e, "status clear");
   // (empty outputs may pass NULL arrays: nothing is written then)
   e = launch_spgemm_fill(as_csr(a), as_csr(b), a->n_rows, a->n_cols, b->n_cols, c_row_ptr,
-                         c_col_idx, c_val,
+                         c_col_idx, c_val, (uint64_t)c_capacity,
                          matmul_pattern(workspace, workspace_bytes, a->n_rows, b->n_cols), status,
                          s);
   if (e != hipSuccess) return hip_fail(e, "csr_matmul_fill launch");
@@ -316,7 +316,7 @@ int seacells_csr_add_rows(const seacells_csr *x, const seacells_csr *y, uint32_t
 
 int seacells_csr_add_fill(float alpha, const seacells_csr *x, float beta, const seacells_csr *y,
                           const uint32_t *c_row_ptr, uint32_t *c_col_idx, float *c_val,
-                          uint32_t *status, seacells_stream_t stream) {
+                          size_t c_capacity, uint32_t *status, seacells_stream_t stream) {
   int rc;
   if ((rc = check_any_csr(x)) != SEACELLS_OK || (rc = check_any_csr(y)) != SEACELLS_OK) return rc;
   if (c_row_ptr == nullptr || status == nullptr) return SEACELLS_E_NULL;
@@ -327,7 +327,7 @@ int seacells_csr_add_fill(float alpha, const seacells_csr *x, float beta, const 
   hipError_t e = launch_status_clear(status, s);
   if (e != hipSuccess) return hip_fail(e, "status clear");
   e = launch_add_fill(alpha, as_csr(x), beta, as_csr(y), x->n_rows, c_row_ptr, c_col_idx, c_val,
-                      status, s);
+                      (uint64_t)c_capacity, status, s);
   if (e != hipSuccess) return hip_fail(e, "csr_add_fill launch");
   return SEACELLS_OK;
 }

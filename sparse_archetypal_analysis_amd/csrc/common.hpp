@@ -194,7 +194,8 @@ size_t vertex_workspace(uint32_t k, uint32_t n);
 hipError_t launch_add_count(Csr x, Csr y, uint32_t m, uint32_t q, uint32_t *c_ptr, void *ws,
                             uint32_t *status, hipStream_t stream);
 hipError_t launch_add_fill(float alpha, Csr x, float beta, Csr y, uint32_t m, const uint32_t *c_ptr,
-                           uint32_t *c_idx, float *c_val, uint32_t *status, hipStream_t stream);
+                           uint32_t *c_idx, float *c_val, uint64_t c_cap, uint32_t *status,
+                           hipStream_t stream);
 hipError_t launch_vertex(const uint32_t *pick, uint32_t k, uint32_t n, float value, uint32_t *s_ptr,
                          uint32_t *s_idx, float *s_val, void *ws, uint32_t *status,
                          hipStream_t stream);
@@ -203,7 +204,7 @@ hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
                                uint32_t *c_ptr, void *ws, uint32_t *pattern, uint32_t *status,
                                hipStream_t stream);
 hipError_t launch_spgemm_fill(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
-                              const uint32_t *c_ptr, uint32_t *c_idx, float *c_val,
+                              const uint32_t *c_ptr, uint32_t *c_idx, float *c_val, uint64_t c_cap,
                               const uint32_t *pattern, uint32_t *status, hipStream_t stream);
 hipError_t launch_transpose(Csr a, uint32_t m, uint32_t q, uint32_t *at_ptr, uint32_t *at_idx,
                             float *at_val, void *ws, uint32_t *status, hipStream_t stream);

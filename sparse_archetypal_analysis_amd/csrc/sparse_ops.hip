@@ -395,8 +395,14 @@ hipError_t launch_scan(uint32_t *ptr, uint32_t count, uint64_t *part, uint32_t *
 __global__ void __launch_bounds__(kSpWaves * kWave)
     spgemm_fill_kernel(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
                        const uint32_t *__restrict__ c_ptr, uint32_t *__restrict__ c_idx,
-                       float *__restrict__ c_val, const uint32_t *__restrict__ pattern,
+                       float *__restrict__ c_val, uint64_t c_cap,
+                       const uint32_t *__restrict__ pattern,
                        const uint32_t *__restrict__ long_rows, uint32_t *__restrict__ status) {
+  // more entries than the output arrays hold: nothing is written
+  if (c_ptr[m] > c_cap) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, kFlagOutputTooLarge);
+    return;
+  }
   __shared__ uint32_t bits_all[kSpWaves][kSpWinWords];
   __shared__ uint16_t rank_all[kSpWaves][kSpWinWords];
   __shared__ float acc_all[kSpWaves][kSpSlots];
@@ -695,7 +701,12 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
 __global__ void __launch_bounds__(kSpWaves * kWave)
     csr_add_fill_kernel(float alpha, Csr x, float beta, Csr y, uint32_t m,
                         const uint32_t *__restrict__ c_ptr, uint32_t *__restrict__ c_idx,
-                        float *__restrict__ c_val, uint32_t *__restrict__ status) {
+                        float *__restrict__ c_val, uint64_t c_cap, uint32_t *__restrict__ status) {
+  // more entries than the output arrays hold: nothing is written
+  if (c_ptr[m] > c_cap) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(status, kFlagOutputTooLarge);
+    return;
+  }
   const uint32_t lane = lane_id();
   const uint32_t wib = threadIdx.x / kWave;
   uint32_t flags = 0;
@@ -987,7 +998,7 @@ hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
 }
 
 hipError_t launch_spgemm_fill(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
-                              const uint32_t *c_ptr, uint32_t *c_idx, float *c_val,
+                              const uint32_t *c_ptr, uint32_t *c_idx, float *c_val, uint64_t c_cap,
                               const uint32_t *pattern, uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
@@ -995,7 +1006,7 @@ hipError_t launch_spgemm_fill(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
   if (m == 0) return hipSuccess;
   const uint32_t nb = sp_blocks(m, dev, resident_blocks(spgemm_fill_kernel, g_fill_resident));
   hipLaunchKernelGGL(spgemm_fill_kernel, dim3(nb), dim3(kSpWaves * kWave), 0,
-                     stream, a, b, m, p, q, c_ptr, c_idx, c_val, pattern,
+                     stream, a, b, m, p, q, c_ptr, c_idx, c_val, c_cap, pattern,
                      long_row_list(const_cast<uint32_t *>(pattern), m, q), status);
   return hipGetLastError();
 }
@@ -1067,14 +1078,15 @@ hipError_t launch_add_count(Csr x, Csr y, uint32_t m, uint32_t q, uint32_t *c_pt
 }
 
 hipError_t launch_add_fill(float alpha, Csr x, float beta, Csr y, uint32_t m, const uint32_t *c_ptr,
-                           uint32_t *c_idx, float *c_val, uint32_t *status, hipStream_t stream) {
+                           uint32_t *c_idx, float *c_val, uint64_t c_cap, uint32_t *status,
+                           hipStream_t stream) {
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
   if (e != hipSuccess) return e;
   if (m == 0) return hipSuccess;
   const uint32_t nb = sp_blocks(m, dev, resident_blocks(csr_add_fill_kernel, g_add_fill_resident));
   hipLaunchKernelGGL(csr_add_fill_kernel, dim3(nb), dim3(kSpWaves * kWave), 0, stream, alpha, x,
-                     beta, y, m, c_ptr, c_idx, c_val, status);
+                     beta, y, m, c_ptr, c_idx, c_val, c_cap, status);
   return hipGetLastError();
 }
 

@@ -89,8 +89,8 @@ def load():
     lib.seacells_csr_matmul_rows.restype = ctypes.c_int
     lib.seacells_csr_matmul_rows.argtypes = [_CSR_P, _CSR_P, _VP, _VP, ctypes.c_size_t, _VP, _VP]
     lib.seacells_csr_matmul_fill.restype = ctypes.c_int
-    lib.seacells_csr_matmul_fill.argtypes = [_CSR_P, _CSR_P, _VP, _VP, _VP, _VP, ctypes.c_size_t,
-                                             _VP, _VP]
+    lib.seacells_csr_matmul_fill.argtypes = [_CSR_P, _CSR_P, _VP, _VP, _VP, ctypes.c_size_t, _VP,
+                                             ctypes.c_size_t, _VP, _VP]
     lib.seacells_csr_matmul_pattern_workspace.restype = ctypes.c_size_t
     lib.seacells_csr_matmul_pattern_workspace.argtypes = [_U32, _U32]
     lib.seacells_csr_transpose_workspace.restype = ctypes.c_size_t
@@ -108,7 +108,7 @@ def load():
     lib.seacells_csr_add_rows.argtypes = [_CSR_P, _CSR_P, _VP, _VP, ctypes.c_size_t, _VP, _VP]
     lib.seacells_csr_add_fill.restype = ctypes.c_int
     lib.seacells_csr_add_fill.argtypes = [ctypes.c_float, _CSR_P, ctypes.c_float, _CSR_P, _VP, _VP,
-                                          _VP, _VP, _VP]
+                                          _VP, ctypes.c_size_t, _VP, _VP]
     lib.seacells_fw_b_vertex_workspace.restype = ctypes.c_size_t
     lib.seacells_fw_b_vertex_workspace.argtypes = [_U32, _U32]
     lib.seacells_fw_b_vertex.restype = ctypes.c_int
@@ -361,7 +361,7 @@ def seacells_csr_matmul_fill(a: DeviceCSR, b: DeviceCSR, c_row_ptr, c_col_idx, c
     rc = lib.seacells_csr_matmul_fill(ctypes.byref(sa), ctypes.byref(sb), _ptr(c_row_ptr),
                                       _ptr(c_col_idx) if c_col_idx.numel() else None,
                                       _ptr(c_val) if c_val.numel() else None,
-                                      _ptr(workspace),
+                                      min(c_col_idx.numel(), c_val.numel()), _ptr(workspace),
                                       0 if workspace is None else workspace.numel(),
                                       _ptr(status), _stream(stream))
     _check_rc(rc)
@@ -371,11 +371,18 @@ def seacells_csr_matmul_fill(a: DeviceCSR, b: DeviceCSR, c_row_ptr, c_col_idx, c
 PATTERN_WORKSPACE_LIMIT = 4 << 30  # bytes of row bitmaps csr_matmul keeps between its passes
 
 
-def csr_matmul(a: DeviceCSR, b: DeviceCSR, status=None, stream=None) -> DeviceCSR:
-    """a @ b as a DeviceCSR: both passes, with one synchronisation between
-    them to size the outputs; the rows pass keeps its row bitmaps for the
-    fill pass when they take at most PATTERN_WORKSPACE_LIMIT bytes. Raises on
-    a device status flag."""
+def csr_matmul(a: DeviceCSR, b: DeviceCSR, status=None, stream=None, bound=None,
+               out: "OutBuffers" = None) -> DeviceCSR:
+    """a @ b as a DeviceCSR; the rows pass keeps its row bitmaps for the fill
+    pass when they take at most PATTERN_WORKSPACE_LIMIT bytes.
+
+    Without ``bound``: one synchronisation between the passes reads the
+    output size, and a device status flag raises. With ``bound`` (an upper
+    bound on the entries, e.g. the number of products): no synchronisation;
+    the outputs hold ``bound`` entries, the returned matrix's nnz is that
+    bound (its rows end at the true size), and a bound that is too small
+    raises OUTPUT_TOO_LARGE in ``status`` with nothing written. ``out``
+    (OutBuffers) reuses its arrays; a and b must not live in them."""
     dev = a.row_ptr.device
     if status is None:
         status = new_status(dev)
@@ -384,11 +391,19 @@ def csr_matmul(a: DeviceCSR, b: DeviceCSR, status=None, stream=None) -> DeviceCS
     if ws_bytes == 0 or ws_bytes > PATTERN_WORKSPACE_LIMIT:
         ws_bytes = seacells_csr_matmul_workspace(m)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    c_ptr, _ = seacells_csr_matmul_rows(a, b, workspace=ws, status=status, stream=stream)
-    raise_on_status(status)  # synchronises; c_ptr[-1] is valid after it
-    nnz = int(c_ptr[-1].item()) & 0xffffffff
-    c_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
-    c_val = torch.empty(nnz, dtype=torch.float32, device=dev)
+    c_ptr = out.row_ptr(m, dev) if out is not None else None
+    c_ptr, _ = seacells_csr_matmul_rows(a, b, c_row_ptr=c_ptr, workspace=ws, status=status,
+                                        stream=stream)
+    if bound is None:
+        raise_on_status(status)  # synchronises; c_ptr[-1] is valid after it
+        nnz = int(c_ptr[-1].item()) & 0xffffffff
+    else:
+        nnz = int(bound)
+    if out is not None:
+        c_idx, c_val = out.entries(nnz, dev)
+    else:
+        c_idx = torch.empty(nnz, dtype=torch.int32, device=dev)
+        c_val = torch.empty(nnz, dtype=torch.float32, device=dev)
     seacells_csr_matmul_fill(a, b, c_ptr, c_idx, c_val, workspace=ws, status=status,
                              stream=stream)
     return DeviceCSR(c_ptr, c_idx, c_val, (a.shape[0], b.shape[1]))
@@ -517,7 +532,8 @@ def seacells_csr_add_fill(alpha: float, x: DeviceCSR, beta: float, y: DeviceCSR,
     sx, sy = x.struct(), y.struct()
     rc = lib.seacells_csr_add_fill(float(alpha), ctypes.byref(sx), float(beta), ctypes.byref(sy),
                                    _ptr(c_row_ptr), _ptr(c_col_idx) if c_col_idx.numel() else None,
-                                   _ptr(c_val) if c_val.numel() else None, _ptr(status),
+                                   _ptr(c_val) if c_val.numel() else None,
+                                   min(c_col_idx.numel(), c_val.numel()), _ptr(status),
                                    _stream(stream))
     _check_rc(rc)
     return c_col_idx, c_val, status
@@ -548,17 +564,22 @@ class OutBuffers:
 
 
 def csr_add(alpha: float, x: DeviceCSR, beta: float, y: DeviceCSR, status=None,
-            stream=None, out: OutBuffers = None) -> DeviceCSR:
-    """alpha x + beta y as a DeviceCSR (both passes, one synchronisation to
-    size the output). Raises on a device status flag. ``out`` (OutBuffers)
-    reuses its arrays; x and y must not live in them."""
+            stream=None, out: OutBuffers = None, bound=None) -> DeviceCSR:
+    """alpha x + beta y as a DeviceCSR. Without ``bound``: one
+    synchronisation sizes the output and a device status flag raises; with
+    ``bound`` (at least nnz of the sum, e.g. nnz(x) + nnz(y)): no
+    synchronisation, as csr_matmul. ``out`` (OutBuffers) reuses its arrays;
+    x and y must not live in them."""
     dev = x.row_ptr.device
     if status is None:
         status = new_status(dev)
     c_ptr = out.row_ptr(x.shape[0], dev) if out is not None else None
     c_ptr, _ = seacells_csr_add_rows(x, y, c_row_ptr=c_ptr, status=status, stream=stream)
-    raise_on_status(status)
-    nnz = int(c_ptr[-1].item()) & 0xffffffff
+    if bound is None:
+        raise_on_status(status)
+        nnz = int(c_ptr[-1].item()) & 0xffffffff
+    else:
+        nnz = int(bound)
     if out is not None:
         c_idx, c_val = out.entries(nnz, dev)
     else:
@@ -618,19 +639,30 @@ def fw_b_loop(K: DeviceCSR, k2b: DeviceCSR, aat: DeviceCSR, k2at: DeviceCSR, b: 
                        device=dev)
     ws_v = torch.empty(seacells_fw_b_vertex_workspace(k, n), dtype=torch.uint8, device=dev)
     # B and K^2 B alternate between two sets of arrays (a sum reads the old
-    # matrix while it writes the new one), kept across steps with headroom
+    # matrix while it writes the new one), kept across steps with headroom.
+    # Sizes are read back per product and sum: bounds known on the host (K's
+    # largest row, K^2's largest row) are loose enough on kNN graphs with hub
+    # cells that the outputs they reserve cost more than the reads.
     b_out, k_out = (OutBuffers(), OutBuffers()), (OutBuffers(), OutBuffers())
+    kw = dict(status=status, stream=stream)
     for t in range(steps):
         g = 2.0 / (t + 2.0) if gammas is None else float(gammas[t])
         seacells_fw_b_argmin(k2b, aat, k2at, b, n, k, out_val=mins[t], out_idx=picks[t],
-                             gap=gaps[t:t + 1], workspace=ws_b, status=status, stream=stream)
-        S = seacells_fw_b_vertex(picks[t], n, 1.0, workspace=ws_v, status=status, stream=stream)
-        b = csr_add(1.0 - g, b, g, S, status=status, stream=stream, out=b_out[t % 2])
-        k2s = csr_matmul(K, csr_matmul(K, S, status=status, stream=stream), status=status,
-                         stream=stream)
-        k2b = csr_add(1.0 - g, k2b, g, k2s, status=status, stream=stream, out=k_out[t % 2])
+                             gap=gaps[t:t + 1], workspace=ws_b, **kw)
+        S = seacells_fw_b_vertex(picks[t], n, 1.0, workspace=ws_v, **kw)
+        b = csr_add(1.0 - g, b, g, S, out=b_out[t % 2], **kw)
+        k2s = csr_matmul(K, csr_matmul(K, S, **kw), **kw)
+        k2b = csr_add(1.0 - g, k2b, g, k2s, out=k_out[t % 2], **kw)
     raise_on_status(status)
     return b, k2b, picks, mins, gaps
+
+
+def csr_trim(m: DeviceCSR) -> DeviceCSR:
+    """The same matrix with nnz read from its row pointer (one
+    synchronisation): the exact size of an output of the bounded mode of
+    csr_matmul or csr_add."""
+    nnz = int(m.row_ptr[-1].item()) & 0xffffffff
+    return DeviceCSR(m.row_ptr, m.col_idx[:nnz], m.val[:nnz], m.shape)
 
 
 def seacells_fw_a_to_csr_workspace(n: int) -> int:

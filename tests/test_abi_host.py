@@ -184,9 +184,9 @@ def test_sparse_ops_reject_bad_arguments_on_host():
     assert lib.seacells_csr_matmul_rows(P(a), P(b), out, None, mneed, st, None) == -3
     assert lib.seacells_csr_matmul_rows(P(a), P(b), out, ws, mneed - 1, st, None) == -3
     assert lib.seacells_csr_matmul_rows(P(a), P(b), out, ws + 4, mneed, st, None) == -3
-    assert lib.seacells_csr_matmul_fill(P(a), P(csr(6, 4, 2)), out, out, out, None, 0, st,
+    assert lib.seacells_csr_matmul_fill(P(a), P(csr(6, 4, 2)), out, out, out, 8, None, 0, st,
                                         None) == -2
-    assert lib.seacells_csr_matmul_fill(P(a), P(b), None, out, out, None, 0, st, None) == -1
+    assert lib.seacells_csr_matmul_fill(P(a), P(b), None, out, out, 8, None, 0, st, None) == -1
     # the kept row bitmaps: m * ceil(q / 32) words after the scan partials, none past 16384 columns
     assert lib.seacells_csr_matmul_pattern_workspace(5, 100) >= mneed + 5 * 4 * 4
     assert lib.seacells_csr_matmul_pattern_workspace(5, 16384) > 0
@@ -231,9 +231,9 @@ def test_sparse_add_and_vertex_reject_bad_arguments_on_host():
     assert lib.seacells_csr_add_rows(P(csr(5, 7, 2 ** 30)), P(csr(5, 7, 2 ** 30)), out, ws, need,
                                      st, None) == -4
     f = ctypes.c_float
-    assert lib.seacells_csr_add_fill(f(1), P(x), f(1), P(y), None, out, out, st, None) == -1
-    assert lib.seacells_csr_add_fill(f(1), P(x), f(1), P(y), out, None, out, st, None) == -1
-    assert lib.seacells_csr_add_fill(f(1), P(x), f(1), P(csr(5, 8, 1)), out, out, out, st,
+    assert lib.seacells_csr_add_fill(f(1), P(x), f(1), P(y), None, out, out, 8, st, None) == -1
+    assert lib.seacells_csr_add_fill(f(1), P(x), f(1), P(y), out, None, out, 8, st, None) == -1
+    assert lib.seacells_csr_add_fill(f(1), P(x), f(1), P(csr(5, 8, 1)), out, out, out, 8, st,
                                      None) == -2
     vneed = lib.seacells_fw_b_vertex_workspace(10, 100)
     assert vneed > 0 and vneed % 256 == 0

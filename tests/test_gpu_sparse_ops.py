@@ -134,6 +134,32 @@ def test_product_with_kept_bitmaps_equals_recomputed_columns():
     check_product(host(saa.csr_matmul(da, db)), S.matmul(a, b), what="kept bitmaps")
 
 
+def test_product_fill_refuses_a_capacity_below_the_true_size():
+    rng = np.random.default_rng(13)
+    a = rand_csr(rng, 200, 50, 5)
+    b = rand_csr(rng, 50, 300, 6)
+    da, db = dev(a), dev(b)
+    ptr, _ = saa.seacells_csr_matmul_rows(da, db)
+    torch.cuda.synchronize()
+    nnz = int(ptr[-1].item())
+    idx = torch.full((nnz - 1,), -3, dtype=torch.int32, device="cuda")
+    val = torch.full((nnz - 1,), 7.0, dtype=torch.float32, device="cuda")
+    st = saa.new_status()
+    saa.seacells_csr_matmul_fill(da, db, ptr, idx, val, status=st)
+    torch.cuda.synchronize()
+    assert "OUTPUT_TOO_LARGE" in saa.status_flags(st)
+    assert bool((idx == -3).all()) and bool((val == 7.0).all())
+    # a bound above the true size is fine (the rows end at the true size)
+    st = saa.new_status()
+    c = saa.csr_matmul(da, db, status=st, bound=nnz + 50)
+    torch.cuda.synchronize()
+    assert saa.status_flags(st) == []
+    assert c.nnz == nnz + 50 and int(c.row_ptr[-1].item()) == nnz
+    exact = saa.csr_trim(c)
+    assert exact.nnz == nnz
+    check_product(host(exact), S.matmul(a, b), what="bounded output")
+
+
 def test_product_keeps_cancellation_as_explicit_zero():
     a = sp.csr_matrix((np.array([1.0, -1.0, 2.0], np.float32), np.array([0, 1, 1]),
                        np.array([0, 2, 3])), shape=(2, 2))
