@@ -368,29 +368,40 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
     }
 
     // -- h -= alpha * t2, and the minimum of h over supp(t2)
-    float mval;
-    uint32_t midx;
+    bool mneg = false;  // that minimum is negative (then midx holds its column)
+    uint32_t midx = kNone;
     auto t2_pass = [&](float alpha) {
       float bv = inf;
       uint32_t bi = kNone, br = 0;
-#pragma unroll
-      for (uint32_t r = 0; r < kT2Regs; ++r) {
-        if (r < nchk) {
-          const uint32_t c = t2c[r];
-          const float hn = __builtin_fmaf(-alpha, t2v[r], h[c]);
-          h[c] = hn;
-          if (hn < bv) bv = hn, bi = c, br = r;
-        }
-      }
+      auto reg_chunk = [&](uint32_t r) {
+        const uint32_t c = t2c[r];
+        const float hn = __builtin_fmaf(-alpha, t2v[r], h[c]);
+        h[c] = hn;
+        if (hn < bv) bv = hn, bi = c, br = r;
+      };
+      // the register chunks, nested so that a short row tests its length once
+      static_assert(kT2Regs == 4, "the nesting below holds four register chunks");
       uint32_t nr = nchk;
-      for (uint32_t qb = q_extra; qb < q1; qb += kWave, ++nr) {  // rows longer than 256
-        const uint32_t q = qb + lane;
-        if (q < q1) {
-          const uint32_t c = k2b_idx[q];
-          if (c < k) {
-            const float hn = __builtin_fmaf(-alpha, k2b_val[q], h[c]);
-            h[c] = hn;
-            if (hn < bv) bv = hn, bi = c, br = nr;
+      if (nchk > 0) {
+        reg_chunk(0);
+        if (nchk > 1) {
+          reg_chunk(1);
+          if (nchk > 2) {
+            reg_chunk(2);
+            if (nchk > 3) {
+              reg_chunk(3);
+              for (uint32_t qb = q_extra; qb < q1; qb += kWave, ++nr) {  // rows longer than 256
+                const uint32_t q = qb + lane;
+                if (q < q1) {
+                  const uint32_t c = k2b_idx[q];
+                  if (c < k) {
+                    const float hn = __builtin_fmaf(-alpha, k2b_val[q], h[c]);
+                    h[c] = hn;
+                    if (hn < bv) bv = hn, bi = c, br = nr;
+                  }
+                }
+              }
+            }
           }
         }
       }
@@ -400,17 +411,22 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       // negative minimum is used (the dense scan decides otherwise), so the
       // key is ~bits: ordered like the values among negative numbers, and
       // above every negative number for the others (-0 and +inf included).
+      // bv is never NaN (a NaN never compares below it), so the minimum is
+      // negative exactly when the smallest key lies below that of -0.
       const uint32_t key = ~__float_as_uint(bv);
       const uint32_t best = wave_min_u32(key);
-      mval = __uint_as_float(~best);  // the minimum when negative; else only >= -0
-      midx = kNone;
-      for (uint32_t r = 0; r < nr; ++r) {
-        const uint64_t m = __ballot(key == best && br == r && bi != kNone);
-        if (m != 0) {
-          midx = readlane_u32(bi, (uint32_t)__builtin_ctzll(m));
-          break;
+      mneg = best < 0x7fffffffu;
+      uint64_t m = __ballot(key == best);  // never empty: every lane takes part
+      if (nr > 1) {
+        for (uint32_t r = 0; r < nr; ++r) {
+          const uint64_t mr = m & __ballot(br == r);
+          if (mr != 0) {
+            m = mr;
+            break;
+          }
         }
       }
+      midx = readlane_u32(bi, (uint32_t)__builtin_ctzll(m | (1ull << 63)));
     };
     t2_pass(1.0f);
     wave_lds_sync();
@@ -421,7 +437,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       const StepSched sc = sched_words != 0 ? sched[t] : sched_step(gamma, t, s_run, flags);
 
       // -- argmin_c h[c], lowest column on a tie
-      uint32_t idx = (mono && mval < 0.0f) ? midx : dense_argmin<kWave>(h, nch, lane);
+      uint32_t idx = (mono && mneg) ? midx : dense_argmin<kWave>(h, nch, lane);
       if (idx >= k) {  // only when no entry compares below +inf (NaN state)
         flags |= kFlagNonfinite;
         idx = 0;
@@ -429,24 +445,26 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       if (trace != nullptr && lane == 0) trace[(size_t)cell * T + t] = idx;
 
       // -- atoms: scale every weight, add gamma at idx or append idx
-      bool hit = false;
+      uint64_t hits = 0;  // lanes whose slot holds idx
       if constexpr (kRegAtoms) {
 #pragma unroll
         for (uint32_t j = 0; j < kWaveAtomSlots; ++j) {
           if (j * kWave < cap) {  // (a wave-uniform test: one slot per lane when cap <= 64)
             const bool at = aidx[j] == idx;
             aval[j] = at ? __builtin_fmaf(aval[j], sc.keep, sc.gam) : aval[j] * sc.keep;
-            hit |= at;
+            hits |= __ballot(at);
           }
         }
       } else {
+        bool hit = false;
         for (uint32_t s = lane; s < cnt; s += kWave) {
           const bool at = s_aidx[s] == idx;
           s_aval[s] = at ? __builtin_fmaf(s_aval[s], sc.keep, sc.gam) : s_aval[s] * sc.keep;
           hit |= at;
         }
+        hits = __ballot(hit);
       }
-      if (__ballot(hit) == 0) {
+      if (hits == 0) {
         if (cnt < cap) {
           if constexpr (kRegAtoms) {
             const uint32_t j = cnt / kWave, l = cnt % kWave;
@@ -563,7 +581,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
         s_t = s_cell;
       else
         s_t = sched_words != 0 ? __uint_as_float(lds[sched_words - 2]) : s_run;
-      const uint32_t gi = (mono && mval < 0.0f) ? midx : dense_argmin<kWave>(h, nch, lane);
+      const uint32_t gi = (mono && mneg) ? midx : dense_argmin<kWave>(h, nch, lane);
       float part = 0.0f;
       if constexpr (kRegAtoms) {
 #pragma unroll
