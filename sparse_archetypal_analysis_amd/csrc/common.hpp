@@ -48,24 +48,21 @@ __device__ __forceinline__ float f32_unorder(uint32_t o) {
 }
 
 // Minimum of a u32 over the 64 lanes of the wave, returned in an SGPR.
-// Butterfly: quad_perm swaps (xor 1, xor 2), half-row and row mirrors
-// (within 8 and 16 lanes), then the gfx950 permlane16/32 swaps across rows.
-// DPP sources take 0xffffffff (the identity of min) where a lane has no
-// partner, so the min folds into one v_min_u32_dpp per step.
+// Called with every lane active. Within each row of 16 lanes: quad_perm
+// swaps (xor 1, xor 2), then the half-row and row mirrors; every lane of a
+// row then holds the row's minimum. Across rows: row_bcast:15 folds the last
+// lane of rows 0 and 2 into rows 1 and 3, row_bcast:31 folds lane 31 into
+// rows 2 and 3, so lane 63 ends with the minimum of all four rows. DPP
+// sources take 0xffffffff (the identity of min) where a lane has no partner
+// or its row is masked off, so each step is one v_min_u32_dpp.
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
   x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0xB1, 0xF, 0xF, false));
   x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0x4E, 0xF, 0xF, false));
   x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0x141, 0xF, 0xF, false));
   x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0x140, 0xF, 0xF, false));
-  {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    x = min(x, min((uint32_t)r[0], (uint32_t)r[1]));
-  }
-  {
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    x = min(x, min((uint32_t)r[0], (uint32_t)r[1]));
-  }
-  return __builtin_amdgcn_readfirstlane(x);
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0x142, 0xA, 0xF, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // (lowest value, then lowest index) over the wave. Lanes with nothing to

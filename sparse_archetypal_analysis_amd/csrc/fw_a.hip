@@ -116,10 +116,12 @@ __device__ __forceinline__ float group_sum_f32(float x) {
 }
 
 // Minimum of a u32 over each group of G consecutive lanes; every lane of a
-// group receives its group's minimum. Same butterfly as wave_min_u32,
-// stopped at the group width.
+// group receives its group's minimum (G = 64: wave_min_u32, uniform). The
+// in-row steps are wave_min_u32's, stopped at the group width; a 32-lane
+// group ends with a permlane16 swap, which gives both its rows the result.
 template <uint32_t G>
 __device__ __forceinline__ uint32_t group_min_u32(uint32_t x) {
+  if constexpr (G == 64) return wave_min_u32(x);
   x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0xB1, 0xF, 0xF, false));
   x = min(x, (uint32_t)__builtin_amdgcn_update_dpp((int)0xffffffff, (int)x, 0x4E, 0xF, 0xF, false));
   if constexpr (G >= 8)
@@ -129,11 +131,6 @@ __device__ __forceinline__ uint32_t group_min_u32(uint32_t x) {
   if constexpr (G >= 32) {
     const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
     x = min(x, min((uint32_t)r[0], (uint32_t)r[1]));
-  }
-  if constexpr (G >= 64) {
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    x = min(x, min((uint32_t)r[0], (uint32_t)r[1]));
-    return __builtin_amdgcn_readfirstlane(x);  // wave-uniform: keeps what follows scalar
   }
   return x;
 }
@@ -1352,14 +1349,20 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       const uint32_t key = f32_order(bv);
       const uint32_t best = wave_min_u32(key);
       mval = f32_unorder(best);
-      midx = kNone;
-      for (uint32_t r = 0; r < nr; ++r) {
-        const uint64_t m = __ballot(key == best && br == r && bi != kNone);
-        if (m != 0) {
-          midx = readlane_u32(bi, (uint32_t)__builtin_ctzll(m));
-          break;
+      // the lowest column holding the minimum: the lane when only one holds
+      // it, else the first chunk with a holder and its lowest lane (a lane
+      // keeps the first chunk where it reached its own minimum)
+      uint64_t m = __ballot(key == best);  // never empty: every lane takes part
+      if (nr > 1 && __builtin_popcountll(m) > 1) {
+        for (uint32_t r = 0; r < nr; ++r) {
+          const uint64_t mr = m & __ballot(br == r);
+          if (mr != 0) {
+            m = mr;
+            break;
+          }
         }
       }
+      midx = readlane_u32(bi, (uint32_t)__builtin_ctzll(m | (1ull << 63)));
       if (midx != kNone && (midx & kTailPos) != 0u) midx = k2b_idx[q0 + (midx & ~kTailPos)];
     };
     if (!deferred) t2_pass(1.0f);
