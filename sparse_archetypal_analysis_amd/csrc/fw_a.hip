@@ -50,6 +50,8 @@ constexpr uint32_t kSchedMax = 256;   // steps whose schedule is tabulated in LD
 constexpr uint32_t kT2Regs = 4;       // chunks of G t2 entries held in registers
 constexpr uint32_t kRegAtomMax = 128; // atoms per cell held in registers
 constexpr uint32_t kNone = 0xffffffffu;
+constexpr uint32_t kZeroKey = 0x80000000u;  // f32_order of -0 and +0
+constexpr uint32_t kInfKey = 0xff800000u;   // f32_order of +inf
 constexpr uint32_t kSupportMinK = 2048;     // support state from this k on
 constexpr uint32_t kSupWavesPerBlock = 4;
 constexpr uint32_t kSupDefaultWaves = 24;   // resident waves per CU the LDS is sized for
@@ -1300,6 +1302,9 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
     }
 
     // -- h -= alpha * t2, and the minimum of h over supp(t2) (lowest column)
+    // the minimum over supp(t2) as its order-preserving key (-0 and +0 share
+    // kZeroKey), and its value
+    uint32_t mkey = kInfKey;
     float mval = inf;
     uint32_t midx = kNone;
     auto t2_pass = [&](float alpha) {
@@ -1348,6 +1353,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       }
       const uint32_t key = f32_order(bv);
       const uint32_t best = wave_min_u32(key);
+      mkey = best;
       mval = f32_unorder(best);
       // the lowest column holding the minimum: the lane when only one holds
       // it, else the first chunk with a holder and its lowest lane (a lane
@@ -1386,7 +1392,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       }
       // -- argmin
       uint32_t idx = midx;
-      if (!(mval < 0.0f)) {
+      if (mkey >= kZeroKey) {  // not negative
         uint32_t cand = kNone;
         for (uint32_t w0 = 0; w0 < nwords; w0 += kWave) {
           const uint32_t w = w0 + lane;
@@ -1396,7 +1402,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
           }
         }
         cand = wave_min_u32(cand);
-        if (mval == 0.0f && midx < cand) cand = midx;
+        if (mkey == kZeroKey && midx < cand) cand = midx;
         if (cand == kNone) {  // every column positive: only a dense scan decides
           deferred = true;
           break;
@@ -1412,6 +1418,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       uint32_t hp0 = 0, hp1 = 0;
 #pragma unroll
       for (uint32_t j = 0; j < kWaveAtomSlots; ++j) {
+        if (j > 0 && j * kWave >= cap) break;  // (uniform: one slot per lane when cap <= 64)
         const bool at = aidx[j] == idx;
         aval[j] = at ? __builtin_fmaf(aval[j], sc.keep, sc.gam) : aval[j] * sc.keep;
         if (at) {
@@ -1504,7 +1511,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
     if (fw_gap != nullptr && !deferred) {
       const float s_t = kPrune ? s_cell : __uint_as_float(lds[sched_words - 2]);
       bool unknown = false;
-      if (!(mval <= 0.0f)) {
+      if (mkey > kZeroKey) {  // positive
         bool zero = false;
         for (uint32_t w0 = 0; w0 < nwords; w0 += kWave) {
           const uint32_t w = w0 + lane;
