@@ -368,13 +368,13 @@ __global__ void __launch_bounds__(kBThreads)
           wave_lds_sync();
           continue;
         }
-        // kGatherRows runs in flight at a time (their first chunks); the adds
-        // still go entry after entry, so every column sums its terms in K2B
-        // order and the result does not depend on the timing
+        // kGatherRows runs in flight at a time (their first three chunks); the
+        // adds still go entry after entry, so every column sums its terms in
+        // K2B order and the result does not depend on the timing
         for (uint32_t u = 0; u < cnt; u += kGatherRows) {
           uint32_t gq[kGatherRows], gn[kGatherRows];
           float xs[kGatherRows];
-          uint2 ea[kGatherRows];
+          uint2 ea[kGatherRows], eb[kGatherRows], ec[kGatherRows];
 #pragma unroll
           for (uint32_t g = 0; g < kGatherRows; ++g) {
             const uint32_t src = (u + g) < kWave ? (u + g) : (kWave - 1);
@@ -383,12 +383,23 @@ __global__ void __launch_bounds__(kBThreads)
             gn[g] = on ? readlane_u32(nq, src) : 0u;
             xs[g] = readlane_f32(x, src);
             ea[g] = load_at(pa_ent + (size_t)gq[g] * kWave, lane * 8u);
+            eb[g] = ec[g] = make_uint2(0u, 0u);
+            if (gn[g] > 1) eb[g] = load_at(pa_ent + (size_t)(gq[g] + 1) * kWave, lane * 8u);
+            if (gn[g] > 2) ec[g] = load_at(pa_ent + (size_t)(gq[g] + 2) * kWave, lane * 8u);
           }
 #pragma unroll
           for (uint32_t g = 0; g < kGatherRows; ++g) {
             float *q = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + ea[g].x);
             *q = __builtin_fmaf(xs[g], __uint_as_float(ea[g].y), *q);
-            for (uint32_t j = 1; j < gn[g]; ++j) {
+            if (gn[g] > 1) {
+              float *qb = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + eb[g].x);
+              *qb = __builtin_fmaf(xs[g], __uint_as_float(eb[g].y), *qb);
+            }
+            if (gn[g] > 2) {
+              float *qc = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + ec[g].x);
+              *qc = __builtin_fmaf(xs[g], __uint_as_float(ec[g].y), *qc);
+            }
+            for (uint32_t j = 3; j < gn[g]; ++j) {
               const uint2 eg = load_at(pa_ent + (size_t)(gq[g] + j) * kWave, lane * 8u);
               float *qj = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + eg.x);
               *qj = __builtin_fmaf(xs[g], __uint_as_float(eg.y), *qj);
