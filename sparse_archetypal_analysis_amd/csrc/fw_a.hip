@@ -1092,7 +1092,13 @@ struct SupQueues {
 
 
 constexpr uint32_t kTailPos = 0x80000000u;  // marks a t2 position (not a column) in the pass
-constexpr uint32_t kRowBatch = 2;   // chunks of a t1 row whose loads are in flight together
+constexpr uint32_t kRowBatch = 4;   // chunks of a t1 row whose loads are in flight together
+
+// a compile-time count passed to a generic lambda
+template <uint32_t N>
+struct Count {
+  static constexpr uint32_t value = N;
+};
 
 // TR: chunks of 64 t2 entries held in registers (the rest are re-read).
 // kPrune: the pruning variant; a step that drops an atom sends the cell to
@@ -1130,50 +1136,49 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
   const uint32_t pad_bits = (k & 31u) != 0u ? ~((1u << (k & 31u)) - 1u) : 0u;
   const float inf = __builtin_inff();
 
-  // h += alpha * t1[p0:p1] (one row of t1) on supp(t2); marks the other
-  // columns that receive a non-zero product when `cover`. The loads of up
-  // to kRowBatch chunks are issued before any is used. Returns true when
-  // the row cannot be handled here (a bad index or a negative value).
   // Each lane owns one dummy slot past the state (value 0, only ever given
   // +0) and one all-zero bitmap word past the real ones, so lanes without an
-  // entry take the same path as the others and no branch splits the batch.
+  // entry take the same path as the others and no branch splits a batch.
   float *hdummy = hc + hc_cap + lane;
   const uint32_t cdummy = nwords * 32u;  // column of the all-zero word
 
   // h += alpha * t1[p0:p1] (one row of t1) on supp(t2); marks the other
-  // columns that receive a non-zero product when `cover`. All loads of a
-  // batch of kRowBatch chunks are in flight together, then all bitmap
-  // lookups, then all state reads, then the writes (the positions of one
-  // row are distinct). Returns true when the row cannot be handled here (a
-  // bad index or a negative value).
+  // columns that receive a non-zero product when `cover`. The row goes in
+  // batches of kRowBatch chunks, then one batch of the 1 to 3 chunks left:
+  // all loads of a batch are in flight together, then all bitmap lookups,
+  // then all state reads, then the writes (the positions of one row are
+  // distinct). Returns true when the row cannot be handled here (a bad
+  // index or a negative value).
   auto scatter_row = [&](uint32_t p0, uint32_t p1, float alpha, bool cover,
                          uint32_t nq) -> bool {
     const uint32_t nit = (p1 - p0 + kWave - 1) / kWave;
     bool lane_bad = false;
-    for (uint32_t i0 = 0; i0 < nit; i0 += kRowBatch) {
-      uint32_t cc[kRowBatch];
-      float vv[kRowBatch];
+    // one batch of NB chunks from chunk i0 on (all of them within the row)
+    auto batch = [&](auto nb, uint32_t i0) {
+      constexpr uint32_t NB = decltype(nb)::value;
+      uint32_t cc[NB];
+      float vv[NB];
 #pragma unroll
-      for (uint32_t b = 0; b < kRowBatch; ++b) {
+      for (uint32_t b = 0; b < NB; ++b) {
         const uint32_t p = p0 + (i0 + b) * kWave + lane;
-        const uint32_t pc = (i0 + b < nit && p < p1) ? p : p0;  // in range; dropped below
+        const uint32_t pc = p < p1 ? p : p0;  // in range; dropped below
         cc[b] = load_at(t1_idx, pc * 4u);
         vv[b] = load_at(t1_val, pc * 4u);
       }
-      uint2 rw[kRowBatch];
+      uint2 rw[NB];
 #pragma unroll
-      for (uint32_t b = 0; b < kRowBatch; ++b) {
+      for (uint32_t b = 0; b < NB; ++b) {
         const uint32_t p = p0 + (i0 + b) * kWave + lane;
-        const bool valid = i0 + b < nit && p < p1;
+        const bool valid = p < p1;
         lane_bad |= valid && (cc[b] >= k || vv[b] < 0.0f);
         if (!valid || cc[b] >= k) cc[b] = cdummy, vv[b] = 0.0f;
         rw[b] = rec[cc[b] >> 5];
       }
-      float *hp[kRowBatch];
-      float hv[kRowBatch];
-      bool in_t2[kRowBatch];
+      float *hp[NB];
+      float hv[NB];
+      bool in_t2[NB];
 #pragma unroll
-      for (uint32_t b = 0; b < kRowBatch; ++b) {
+      for (uint32_t b = 0; b < NB; ++b) {
         const uint32_t bit = 1u << (cc[b] & 31u);
         const uint32_t pos = rw[b].y + __popc(rw[b].x & (bit - 1u));
         in_t2[b] = (rw[b].x & bit) != 0u && pos < nq;
@@ -1181,14 +1186,25 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
         hv[b] = *hp[b];
       }
 #pragma unroll
-      for (uint32_t b = 0; b < kRowBatch; ++b)
+      for (uint32_t b = 0; b < NB; ++b)
         *hp[b] = __builtin_fmaf(alpha, in_t2[b] ? vv[b] : 0.0f, hv[b]);
       if (cover) {
 #pragma unroll
-        for (uint32_t b = 0; b < kRowBatch; ++b)
+        for (uint32_t b = 0; b < NB; ++b)
           if (!in_t2[b] && alpha * vv[b] != 0.0f) atomicOr(&cov[cc[b] >> 5], 1u << (cc[b] & 31u));
       }
-    }
+    };
+    // full batches, then one batch of exactly the chunks left
+    uint32_t i0 = 0;
+    for (; i0 + kRowBatch <= nit; i0 += kRowBatch) batch(Count<kRowBatch>{}, i0);
+    const uint32_t rest = nit - i0;
+    static_assert(kRowBatch == 4, "the tail below covers 1 to 3 chunks");
+    if (rest == 3)
+      batch(Count<3>{}, i0);
+    else if (rest == 2)
+      batch(Count<2>{}, i0);
+    else if (rest == 1)
+      batch(Count<1>{}, i0);
     return __ballot(lane_bad) != 0;
   };
 
