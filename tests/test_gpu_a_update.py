@@ -216,6 +216,8 @@ def _support_case(name):
     if name == "signed":      # every cell leaves the support path at its first negative product
         return W.random_workload(400, 333, t1_per_row=12, k2b_per_row=9, s_a=7, seed=5,
                                  signed=True), {}
+    if name == "long_t1_rows":  # t1 rows of 0 to 10 chunks: full batches and every tail size
+        return W.random_workload(300, 2500, t1_per_row=300, k2b_per_row=40, s_a=6, seed=41), {}
     if name == "long_rows":   # K2B rows from 0 to 1600 entries: some exceed the first pass
         return W.random_workload(200, 3000, t1_per_row=40, k2b_per_row=800, s_a=6, seed=29), {}
     if name == "very_long_rows":  # up to 12000 entries: some exceed the long-row pass too
@@ -240,7 +242,7 @@ def _support_case(name):
     raise KeyError(name)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "empty", "signed", "long_rows",
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "empty", "signed", "long_t1_rows", "long_rows",
                                   "very_long_rows", "fold", "restarts", "bad_gamma",
                                   "cap_overflow"])
 def test_support_state_equals_dense_kernel(name, monkeypatch):
@@ -258,7 +260,7 @@ def test_support_state_equals_dense_kernel(name, monkeypatch):
         sup = run_a(w, ops=ops, **kw)
         assert sup[4] == dense[4]
         assert_same_result(dense, sup)
-    if name in ("c1", "c2", "empty", "long_rows"):
+    if name in ("c1", "c2", "empty", "long_t1_rows", "long_rows"):
         parity.check_a(w, sup[3], sup[0], sup[1], sup[2], np.arange(w.n))
 
 

@@ -86,6 +86,18 @@ def test_column_slices(n, k):
     parity.check_b(w, v, i, g)
 
 
+def test_one_slice_long_aat_runs():
+    # k <= 2048 (one slice, padded AAt copy): symmetric AAt rows of ~200 to
+    # ~680 entries, so a gathered run spans 4 to 11 chunks (the first three are
+    # loaded together with those of the neighbouring runs, the rest one by one)
+    w = W.random_workload(2000, 1500, aat_per_row=250, k2b_per_row=20, k2at_per_row=15, seed=77)
+    chunks = (np.diff(w.aat.indptr) + 63) // 64
+    assert chunks.min() >= 4 and chunks.max() >= 10
+    v, i, g, flags = run_b(w)
+    assert flags == []
+    parity.check_b(w, v, i, g)
+
+
 def test_single_row_single_column_and_no_b():
     w = W.random_workload(1, 1, seed=2)
     v, i, g, flags = run_b(w)
