@@ -1093,6 +1093,7 @@ struct SupQueues {
 
 constexpr uint32_t kTailPos = 0x80000000u;  // marks a t2 position (not a column) in the pass
 constexpr uint32_t kRowBatch = 4;   // chunks of a t1 row whose loads are in flight together
+constexpr uint32_t kT2Batch = 4;    // chunks of K2B past the registers re-read together
 
 // a compile-time count passed to a generic lambda
 template <uint32_t N>
@@ -1345,21 +1346,21 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
           if (cand < bv) bv = cand, bi = t2c[r], br = r;
         }
       }
-      // entries past the registers: values re-read from K2B (two chunks in
-      // flight), tracked by position; the column is read for the winner only
+      // entries past the registers: values re-read from K2B (kT2Batch chunks
+      // in flight), tracked by position; the column is read for the winner only
       uint32_t nr = nchr;
-      for (uint32_t pb = TR * kWave; pb < nq; pb += 2 * kWave, nr += 2) {
-        float tv2[2], hv2[2];
-        float *tp2[2];
+      for (uint32_t pb = TR * kWave; pb < nq; pb += kT2Batch * kWave, nr += kT2Batch) {
+        float tv2[kT2Batch], hv2[kT2Batch];
+        float *tp2[kT2Batch];
 #pragma unroll
-        for (uint32_t b = 0; b < 2; ++b) {
+        for (uint32_t b = 0; b < kT2Batch; ++b) {
           const uint32_t p = pb + b * kWave + lane;
           tv2[b] = p < nq ? k2b_val[q0 + p] : 0.0f;
           tp2[b] = p < nq ? hc + p : hdummy;
           hv2[b] = *tp2[b];
         }
 #pragma unroll
-        for (uint32_t b = 0; b < 2; ++b) {
+        for (uint32_t b = 0; b < kT2Batch; ++b) {
           const uint32_t p = pb + b * kWave + lane;
           const float hn = __builtin_fmaf(-alpha, tv2[b], hv2[b]);
           *tp2[b] = hn;
