@@ -212,7 +212,7 @@ __global__ void __launch_bounds__(256)
 // accumulators (for the short AAt runs of narrow slices); each column then
 // sums the even-numbered entries of the row in one accumulator and the odd
 // ones in the other, each in K2B order, and adds the two at the end.
-template <uint32_t S4, bool kDual>
+template <uint32_t S4, bool kDual, uint32_t kPairs>
 __global__ void __launch_bounds__(kBThreads)
     fw_b_partials_kernel(Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n, uint32_t k,
                          uint32_t slice_w, uint32_t n_slices, uint32_t n_row_blocks,
@@ -222,6 +222,9 @@ __global__ void __launch_bounds__(kBThreads)
                          uint32_t *__restrict__ xcd_work, uint32_t epoch,
                          uint32_t *__restrict__ status) {
   constexpr uint32_t W = 256 * S4;  // accumulator columns (>= slice_w)
+  // the staged triples a group of kPairs pairs reads stay inside the stage
+  static_assert((kWave - 1) / (2 * kPairs) * (2 * kPairs) + 2 * kPairs <= kStageSlots,
+                "stage slots");
   constexpr uint32_t NC = 4 * S4;   // columns per lane
   constexpr uint32_t NACC = kDual ? 2 : 1;
   extern __shared__ float lds_acc[];
@@ -329,17 +332,17 @@ __global__ void __launch_bounds__(kBThreads)
         const uint32_t cnt = (e1 - eb) < kWave ? (e1 - eb) : kWave;
         if constexpr (kDual) {
           // entries u + 2g (lanes 0-31) and u + 2g + 1 (lanes 32-63): runs of
-          // kGatherRows pairs in flight, 32 lanes per run. Each chunk's
+          // kPairs pairs in flight, 32 lanes per run. Each chunk's
           // (run start, run end, K2B value) goes through LDS once, and a half
           // reads its entry's triple with one broadcast load.
           stage[lane] = make_uint4(lo, lane < cnt ? hi : lo, __float_as_uint(x), 0u);
           wave_lds_sync();
-          for (uint32_t u = 0; u < cnt; u += 2 * kGatherRows) {
-            uint32_t plo[kGatherRows], phi[kGatherRows];
-            float xs[kGatherRows], va[kGatherRows], vb[kGatherRows];
-            uint32_t ca[kGatherRows], cb[kGatherRows];
+          for (uint32_t u = 0; u < cnt; u += 2 * kPairs) {
+            uint32_t plo[kPairs], phi[kPairs];
+            float xs[kPairs], va[kPairs], vb[kPairs];
+            uint32_t ca[kPairs], cb[kPairs];
 #pragma unroll
-            for (uint32_t g = 0; g < kGatherRows; ++g) {
+            for (uint32_t g = 0; g < kPairs; ++g) {
               const uint4 t = stage[u + 2 * g + half];  // slots >= cnt hold empty runs
               plo[g] = t.x;
               phi[g] = t.y;
@@ -352,7 +355,7 @@ __global__ void __launch_bounds__(kBThreads)
             // columns outside the slice (none for sorted rows; lanes without
             // an entry) go to this lane's dummy slot past the accumulator
 #pragma unroll
-            for (uint32_t g = 0; g < kGatherRows; ++g) {
+            for (uint32_t g = 0; g < kPairs; ++g) {
               const uint32_t c_a = ca[g] - c0, c_b = cb[g] - c0;
               float *qa = acc_h + (c_a < cw ? c_a : W + hl);
               float *qb = acc_h + (c_b < cw ? c_b : W + hl);
@@ -622,12 +625,25 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
   const uint32_t lds = (kBThreads / kWave) *
                        (kDual ? 2 * (256 * S4 + kAccPad) + kStageSlots * 4 : 256 * S4 + kWave) *
                        sizeof(float);
+  // narrow slices: kGatherRows pairs of runs in flight, or twice as many
+  // when that keeps as many blocks resident (the wider accumulators are
+  // register-bound already)
+  auto k_std = &fw_b_partials_kernel<S4, kDual, kGatherRows>;
+  auto k_deep = k_std;
+  if constexpr (kDual) k_deep = &fw_b_partials_kernel<S4, true, 2 * kGatherRows>;
   static int bpc = -1;
+  static bool deep = false;
   if (bpc < 0) {
-    int v = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &v, reinterpret_cast<const void *>(&fw_b_partials_kernel<S4, kDual>), kBThreads, lds);
+    int v = 0, v2 = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, reinterpret_cast<const void *>(k_std),
+                                                     kBThreads, lds);
     if (e != hipSuccess) return e;
+    if (kDual) {
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &v2, reinterpret_cast<const void *>(k_deep), kBThreads, lds);
+      if (e != hipSuccess) return e;
+    }
+    deep = kDual && v2 >= v;
     bpc = v < 1 ? 1 : v;
   }
   const uint64_t units = (uint64_t)p.n_row_blocks * p.n_slices;
@@ -635,8 +651,7 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
   const uint64_t resident = (uint64_t)dev.cus * (uint64_t)bpc;
   uint64_t blocks = want < resident ? want : resident;
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // the same number of blocks on every XCD
-  auto kern = &fw_b_partials_kernel<S4, kDual>;
-  hipLaunchKernelGGL(kern, dim3((uint32_t)blocks), dim3(kBThreads), lds,
+  hipLaunchKernelGGL(deep ? k_deep : k_std, dim3((uint32_t)blocks), dim3(kBThreads), lds,
                      stream, k2b, aat, k2at, b, n, k, p.slice_w, p.n_slices, p.n_row_blocks, seg,
                      pa_seg, pa_ent, keys, gap_part, stamps, xcd_work, epoch, status);
   return hipGetLastError();
