@@ -44,7 +44,7 @@ constexpr uint32_t kGatherRows = 4;  // AAt runs whose loads are in flight toget
 constexpr uint32_t kXcds = 8;        // MI355X: 8 XCDs of 32 CUs, each with its own 4 MB L2
 constexpr size_t kSliceAatBytes = 5u << 19;  // AAt bytes per slice kept within one L2 (2.5 MB)
 constexpr uint32_t kMaxSlices = 128;
-constexpr uint32_t kSlicedRowBlocks = 4096;  // row ranges per slice when k is sliced
+constexpr uint32_t kSlicedRowBlocks = 16384;  // row ranges per slice when k is sliced
 constexpr uint32_t kAccPad = 32;             // dummy slots after each dual accumulator
 constexpr uint32_t kStageSlots = kWave + 8;  // staged triples (a run of pairs reads past 64)
 
