@@ -14,11 +14,16 @@ The pages fix no dataset. Each workload is a seeded single-cell stand-in:
   broken by index. Adaptive Gaussian weights W_ij = exp(-d_ij^2 / (s_i s_j))
   with s_i the distance to the kNN-th neighbour, then K = (W + W^T) / 2
   with K_ii = 1. K^2 is never formed: products are K (K X) in f64.
-* B (n x k, column-stochastic): k distinct uniformly random init cells. For
-  s_B > 0, each column also takes s_B cells drawn uniformly, with
-  replacement, from its init cell's mixture component. Weights are
-  Dirichlet(1) on that support. This stands in for "B after s_B prior FW
-  steps" without running any FW step here.
+* B (n x k, column-stochastic): k distinct uniformly random init cells give
+  the one-hot start. For s_B > 0 the configs name "B after s_B prior FW
+  steps": that B is stored input data under ``workloads/prior_b/``, written
+  once by ``oracle/prior_b.py`` (s_B Frank-Wolfe B steps of the f64 oracle
+  from the one-hot start, with A = A_prev fixed). This module only loads
+  it, and checks that it was made from the same K and A_prev (SHA-256 of
+  both). The ``*_standin`` variants keep an earlier construction that runs
+  no FW step: each column also takes s_B cells drawn uniformly, with
+  replacement, from its init cell's mixture component, with Dirichlet(1)
+  weights.
 * A_prev (k x n, column-stochastic): column j is supported on the s_A
   archetypes whose init cells lie nearest to x_j (ties by index), with
   Dirichlet(1) weights.
@@ -30,8 +35,8 @@ The pages fix no dataset. Each workload is a seeded single-cell stand-in:
     B argmin.
 
 RNG: numpy PCG64 ``default_rng(1000 * index + seed)``. Draws happen in this
-order: means, scales, labels, noise, init cells, B supports, B weights,
-A weights.
+order: means, scales, labels, noise, init cells, (stand-in variants only:
+B supports, B weights), A weights.
 """
 from __future__ import annotations
 
@@ -44,7 +49,7 @@ from dataclasses import asdict, dataclass, field
 import numpy as np
 import scipy.sparse as sp
 
-GENERATOR_VERSION = 1
+GENERATOR_VERSION = 2
 _REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -57,11 +62,12 @@ class Config:
     knn: int          # neighbours per cell in the kernel graph
     k: int            # archetypes
     s_a: int          # non-zeros per A_prev column
-    s_b: int          # extra B support cells per column
+    s_b: int          # prior Frank-Wolfe B steps (stand-in: extra B cells per column)
     scale: tuple | None = None   # per-component std range, None = 1
     zipf: float | None = None    # component-weight exponent, None = equal
     T: int = 50                  # A steps
     index: int = 0               # RNG stream index
+    b_init: str = "fw"           # "fw": stored B after s_b FW steps; "standin": random cells
 
 
 CONFIGS = {
@@ -72,14 +78,23 @@ CONFIGS = {
     "c5": Config("c5", 1_000_000, 50, 100, 30, 10_000, 16, 30, scale=(0.5, 2.0), zipf=1.1,
                  index=5),
 }
+# the earlier B construction (no FW step), same points, kernel and init cells
+for _nm in ("c2", "c3", "c4", "c5"):
+    _c = CONFIGS[_nm]
+    CONFIGS[_nm + "_standin"] = Config(**{**asdict(_c), "name": _nm + "_standin",
+                                          "b_init": "standin"})
 
 DESCRIPTIONS = {
     "c1": "n=2000 d=10 C=5 kNN=15 k=25 s_A=5 B one-hot T=50",
-    "c2": "n=20000 d=20 C=10 kNN=15 k=250 s_A=8 s_B=3 T=50",
-    "c3": "n=100000 d=30 C=20 std~U(0.5,2) kNN=20 k=1300 s_A=10 s_B=10 T=50",
-    "c4": "n=500000 d=30 C=50 std~U(0.5,2) kNN=20 k=6700 s_A=12 s_B=20 T=50",
-    "c5": "n=1000000 d=50 C=100 Zipf(1.1) std~U(0.5,2) kNN=30 k=10000 s_A=16 s_B=30 T=50",
+    "c2": "n=20000 d=20 C=10 kNN=15 k=250 s_A=8 B after 3 FW steps T=50",
+    "c3": "n=100000 d=30 C=20 std~U(0.5,2) kNN=20 k=1300 s_A=10 B after 10 FW steps T=50",
+    "c4": "n=500000 d=30 C=50 std~U(0.5,2) kNN=20 k=6700 s_A=12 B after 20 FW steps T=50",
+    "c5": "n=1000000 d=50 C=100 Zipf(1.1) std~U(0.5,2) kNN=30 k=10000 s_A=16 "
+          "B after 30 FW steps T=50",
 }
+for _nm in ("c2", "c3", "c4", "c5"):
+    DESCRIPTIONS[_nm + "_standin"] = DESCRIPTIONS[_nm].split(" B after")[0] + \
+        " B stand-in (%d random same-component cells, Dirichlet(1)) T=50" % CONFIGS[_nm].s_b
 
 
 @dataclass
@@ -324,8 +339,36 @@ def _progress(log, what, t0):
         log("[workload] %s done at %.1f s" % (what, time.time() - t0))
 
 
-def generate(cfg: Config, seed: int = 0, log=None) -> Workload:
-    """Build one workload. ``log`` (optional) receives one line per stage."""
+PRIOR_B_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "prior_b")
+
+
+def prior_b_path(cfg: Config, seed: int = 0) -> str:
+    """Where the stored B after cfg.s_b prior FW steps lives."""
+    return os.path.join(PRIOR_B_DIR, "%s_s%d.npz" % (cfg.name, seed))
+
+
+@dataclass
+class Base:
+    """The inputs every operand is built from: K (n x n, f64, symmetric),
+    the k init cells, A_prev^T (n x k, f64) and, for the stand-in variants,
+    B (n x k, f64). No Frank-Wolfe arithmetic went into any of them."""
+    cfg: Config
+    seed: int
+    K: sp.csr_matrix
+    init: np.ndarray
+    At: sp.csr_matrix
+    B_standin: sp.csr_matrix | None
+    seconds: dict
+
+    def sha(self) -> dict:
+        """SHA-256 of K and A_prev^T as their f32 CSR operands."""
+        k32, a32 = _f32(self.K), _f32(self.At)
+        return {"K": _sha(k32.indptr, k32.indices, k32.data),
+                "a_prev_t": _sha(a32.indptr, a32.indices, a32.data)}
+
+
+def base(cfg: Config, seed: int = 0, log=None) -> Base:
+    """Points, kernel, init cells and A_prev (and the stand-in B)."""
     t0 = time.time()
     rng = np.random.default_rng(1000 * cfg.index + seed)
     X, labels = _points(cfg, rng)
@@ -335,27 +378,86 @@ def generate(cfg: Config, seed: int = 0, log=None) -> Workload:
     t_knn = time.time()
     _progress(log, "kNN kernel (%d nnz)" % K.nnz, t0)
     init = rng.choice(cfg.n, size=cfg.k, replace=False)
-    B = _b_matrix(cfg, rng, labels, init)
+    Bs = _b_matrix(cfg, rng, labels, init) if cfg.b_init == "standin" else None
     At = _a_prev_t(cfg, rng, X, init)
-    _progress(log, "B and A_prev", t0)
-    K2B = _matmul(K, _matmul(K, B))
+    _progress(log, "init cells and A_prev", t0)
+    return Base(cfg, seed, K, np.asarray(init, np.int64), At, Bs,
+                {"points": t_pts - t0, "kernel": t_knn - t_pts, "init_a": time.time() - t_knn})
+
+
+def one_hot_b(n: int, init) -> sp.csr_matrix:
+    """The one-hot start of B: column c is e_{init[c]} (n x k, f64)."""
+    k = len(init)
+    return sp.csr_matrix((np.ones(k), (np.asarray(init, np.int64), np.arange(k))), shape=(n, k))
+
+
+def k2_times(K: sp.csr_matrix, X: sp.csr_matrix) -> sp.csr_matrix:
+    """K (K X) in f64 (the kernel construction's product; K^2 is never formed)."""
+    return _matmul(K, _matmul(K, X))
+
+
+def load_prior_b(bs: Base) -> sp.csr_matrix:
+    """The stored B after cfg.s_b prior FW steps (n x k, f64), checked
+    against the K and A_prev it was computed from."""
+    cfg = bs.cfg
+    path = prior_b_path(cfg, bs.seed)
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            "%s is missing: the B after %d prior FW steps of config %s is written by "
+            "`python -m oracle.prior_b %s`" % (path, cfg.s_b, cfg.name, cfg.name))
+    z = np.load(path, allow_pickle=False)
+    want = bs.sha()
+    got = {"K": str(z["k_sha"]), "a_prev_t": str(z["a_prev_t_sha"])}
+    if got != want:
+        raise ValueError("%s was computed from another K or A_prev (SHA-256 %s, these inputs %s); "
+                         "rerun `python -m oracle.prior_b %s`" % (path, got, want, cfg.name))
+    if int(z["steps"]) != cfg.s_b:
+        raise ValueError("%s holds %d steps, config %s names %d"
+                         % (path, int(z["steps"]), cfg.name, cfg.s_b))
+    bt = sp.csr_matrix((z["bt_val"], z["bt_idx"], z["bt_ptr"]), shape=(cfg.k, cfg.n))
+    return sp.csr_matrix(bt.T)
+
+
+def operands(K: sp.csr_matrix, B: sp.csr_matrix, At: sp.csr_matrix, log=None, t0=None) -> dict:
+    """The f32 operands of both updates from K, B and A_prev^T (products in
+    f64, symmetrised where the maths is symmetric, one cast to f32)."""
+    t0 = time.time() if t0 is None else t0
+    K2B = k2_times(K, B)
     t1 = B.T @ K2B
     _progress(log, "K2B and t1", t0)
-    K2At = _matmul(K, _matmul(K, At))
+    K2At = k2_times(K, At)
     AAt = At.T @ At
     _progress(log, "K2At and AAt", t0)
-    w = Workload(cfg, seed, t1=_f32(t1, symmetric=True), k2b=_f32(K2B), a_prev_t=_f32(At),
-                 aat=_f32(AAt, symmetric=True), k2at=_f32(K2At), b=_f32(B),
-                 init_cells=np.asarray(init, np.int64), K=_f32(K))
+    return {"t1": _f32(t1, symmetric=True), "k2b": _f32(K2B), "a_prev_t": _f32(At),
+            "aat": _f32(AAt, symmetric=True), "k2at": _f32(K2At), "b": _f32(B)}
+
+
+def generate(cfg: Config, seed: int = 0, log=None) -> Workload:
+    """Build one workload. ``log`` (optional) receives one line per stage."""
+    t0 = time.time()
+    bs = base(cfg, seed, log)
+    if cfg.s_b == 0:
+        B, b_note = one_hot_b(cfg.n, bs.init), "one-hot at the init cells"
+    elif cfg.b_init == "standin":
+        B = bs.B_standin
+        b_note = "stand-in: init cell plus %d random same-component cells, Dirichlet(1)" % cfg.s_b
+    else:
+        B = load_prior_b(bs)
+        b_note = "after %d FW steps from the one-hot start (stored, %s)" % (
+            cfg.s_b, os.path.relpath(prior_b_path(cfg, seed), _REPO))
+    t_b = time.time()
+    ops = operands(bs.K, B, bs.At, log, t0)
+    w = Workload(cfg, seed, init_cells=bs.init, K=_f32(bs.K), **ops)
     t_end = time.time()
     _progress(log, "f32 operands", t0)
     w.meta = {
         "generator_version": GENERATOR_VERSION,
         "config": asdict(cfg),
         "seed": seed,
-        "seconds": {"points": t_pts - t0, "kernel": t_knn - t_pts, "operands": t_end - t_knn},
+        "b_init": b_note,
+        "seconds": dict(bs.seconds, operands=t_end - t_b),
         "nnz": {nm: int(getattr(w, nm).nnz) for nm in ("t1", "k2b", "a_prev_t", "aat", "k2at", "b")},
-        "nnz_K": int(K.nnz),
+        "nnz_K": int(w.K.nnz),
         "sha256": {nm: _sha(getattr(w, nm).indptr, getattr(w, nm).indices, getattr(w, nm).data)
                    for nm in ("t1", "k2b", "a_prev_t", "aat", "k2at", "b")},
     }
@@ -421,14 +523,26 @@ def make(name_or_cfg, seed: int = 0, cache: bool = True, log=None) -> Workload:
         return generate(cfg, seed, log)
     key = "%s_n%d_k%d_s%d_v%d.npz" % (cfg.name, cfg.n, cfg.k, seed, GENERATOR_VERSION)
     path = os.path.join(cache_dir(), key)
+    prior = _file_sha(prior_b_path(cfg, seed)) if cfg.s_b > 0 and cfg.b_init == "fw" else None
     if os.path.exists(path) and os.path.exists(path + ".json"):
         with open(path + ".json") as f:
             meta = json.load(f)
-        if meta.get("config") == json.loads(json.dumps(asdict(cfg))):
+        if meta.get("config") == json.loads(json.dumps(asdict(cfg))) and \
+                meta.get("prior_b_file_sha") == prior:
             return _load(cfg, seed, path)
     w = generate(cfg, seed, log)
+    w.meta["prior_b_file_sha"] = prior
     _save(w, path)
     return w
+
+
+def _file_sha(path):
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    with open(path, "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
 
 
 # --------------------------------------------------------------------------
