@@ -5,12 +5,24 @@ A step runs the A update (T = 50 Frank-Wolfe steps for every cell), the
 B-gradient argmin over all cells, and the B step, back to back on one
 stream, over a seeded synthetic kNN-kernel workload already resident in
 HBM. The JSON line reports cells/s for the whole step, the roofline of the
-dominant kernel (algorithmic bytes per launch / average launch time from HIP
-events on the library's stream), and the f64 CPU oracle timed on a bounded
-sample of the same workload.
+dominant call (algorithmic bytes per launch / average launch time from HIP
+events on the library's stream; beside it the bytes the rocprofv3 counters
+saw beyond L2 and the compulsory bytes, each as a fraction of HBM peak), and
+the f64 CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config c5] [--gpus 1] [--prune THR]
                     [--no-operands] [--no-cpu-baseline]
+    python bench.py --table [--table-configs c1,c2,c3,c4,c5]
+    python bench.py --summarize-profile OUT.md --config c5 --trace DIR --fetch DIR
+                    --write DIR --copy-fetch DIR --copy-write DIR [--counters DIR ...]
+
+--table times the A update and the B argmin alone on every workload (median
+of at least 20 calls, 5 at the two largest), with the oracle's times beside
+them (every cell and row at n <= 100k, 1 thread too at n <= 20k; a sample
+scaled up above). --summarize-profile turns rocprofv3 output folders (kernel
+trace, FETCH_SIZE and WRITE_SIZE runs of this script, the same counters on
+--copy-calibration) into a markdown summary and the per-call traffic record
+in profiles/traffic.json.
 
 After the timed steps it also times the device construction of the
 operands from K, B and A^T ("operands": whole build and per step), a few
@@ -65,6 +77,20 @@ def algorithmic_bytes_b(w):
             + 8 * gathers + 8 * w.k)
 
 
+def compulsory_bytes_a(w, atom_cnt):
+    """Every input of the A update read once (K2B, A_prev, t1 with their row
+    pointers) and the atoms and counts written."""
+    return (8 * (w.k2b.nnz + w.a_prev_t.nnz + w.t1.nnz) + 4 * (2 * (w.n + 1) + w.k + 1)
+            + 8 * int(atom_cnt.sum()) + 4 * w.n)
+
+
+def compulsory_bytes_b(w):
+    """Every input of the B argmin read once (K2B, K2At, B, AAt with their
+    row pointers) and the k (value, row) outputs written."""
+    return (8 * (w.k2b.nnz + w.k2at.nnz + w.b.nnz + w.aat.nnz) + 4 * (3 * (w.n + 1) + w.k + 1)
+            + 8 * w.k)
+
+
 def source_sha(*files):
     h = hashlib.sha256()
     for f in files:
@@ -73,18 +99,22 @@ def source_sha(*files):
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(kernel, workload, sha):
-    """HBM bytes per launch from the committed counter summary, or None when
-    the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+CALL_SOURCES = {"fw_a_columns": ("fw_a.hip", "common.hpp"),
+                "fw_b_argmin": ("fw_b.hip", "common.hpp")}
+
+
+def traffic_from_profile(call, workload, sha):
+    """Bytes beyond L2 per call from the committed counter record, or None
+    when the call's sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_JSON):
         return None
-    with open(path) as f:
+    with open(TRAFFIC_JSON) as f:
         rec = json.load(f)
-    e = rec.get(kernel, {}).get(workload)
+    e = rec.get(call, {}).get(workload)
     if not e or e.get("source_sha") != sha:
         return None
-    return e.get("hbm_bytes_per_launch")
+    return e.get("bytes_per_call")
 
 
 def cpu_baseline(w, budget_s=12.0):
@@ -286,6 +316,373 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
 
 
+# --------------------------------------------------------------------------
+# rocprofv3 summaries (CPU only)
+# --------------------------------------------------------------------------
+
+A_KERNELS = ("fw_a_", "pad_rows_kernel", "pad_fill_kernel")
+B_KERNELS = ("seg_table_kernel", "pa_seg_kernel", "pa_fill_kernel", "fw_b_partials_kernel",
+             "fw_b_reduce1_kernel", "fw_b_reduce2_kernel", "fw_b_fw_gap_kernel")
+
+
+def _kname(raw):
+    """A kernel's name without return type, namespaces and argument list."""
+    nm = raw.strip()
+    if nm.startswith("void "):
+        nm = nm[5:]
+    depth, cut = 0, len(nm)
+    for i, ch in enumerate(nm):  # the argument list: the first '(' outside <...>
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not nm[i:].startswith("(anonymous"):
+            cut = i
+            break
+    nm = nm[:cut]
+    for ns in ("seacells::(anonymous namespace)::", "seacells::"):
+        nm = nm.replace(ns, "")
+    return nm.strip()
+
+
+def _call_of(kernel):
+    if kernel.startswith(A_KERNELS):
+        return "fw_a_columns"
+    if kernel.startswith(B_KERNELS):
+        return "fw_b_argmin"
+    if kernel.startswith("fw_b_apply_kernel"):
+        return "fw_b_apply"
+    return None
+
+
+def _csv_rows(folder, suffix):
+    import csv
+    import glob
+    out = []
+    for path in sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True)):
+        with open(path, newline="") as f:
+            out.extend(csv.DictReader(f))
+    if not out:
+        raise FileNotFoundError("no *%s under %s" % (suffix, folder))
+    return out
+
+
+def _field(row, *names):
+    for nm in names:
+        if nm in row and row[nm] != "":
+            return row[nm]
+    raise KeyError(names)
+
+
+def _dispatches(folder):
+    """Kernel trace: [(kernel, start_ns, end_ns)] in start order."""
+    rows = _csv_rows(folder, "kernel_trace.csv")
+    out = [(_kname(_field(r, "Kernel_Name", "Name")), int(_field(r, "Start_Timestamp")),
+            int(_field(r, "End_Timestamp"))) for r in rows]
+    return sorted(out, key=lambda x: x[1])
+
+
+def _counter_totals(folder):
+    """Counter run: {counter: {kernel: [value per dispatch]}}."""
+    rows = _csv_rows(folder, "counter_collection.csv")
+    per = {}
+    for r in rows:
+        c = _field(r, "Counter_Name")
+        k = _kname(_field(r, "Kernel_Name", "Name"))
+        d = _field(r, "Dispatch_Id", "Correlation_Id")
+        per.setdefault(c, {}).setdefault(k, {}).setdefault(d, 0.0)
+        per[c][k][d] += float(_field(r, "Counter_Value"))
+    return {c: {k: list(v.values()) for k, v in ks.items()} for c, ks in per.items()}
+
+
+def _calls_in(kernels):
+    """Calls of the A update and the B argmin in a run, from one-per-call kernels."""
+    def count(prefixes):
+        for p in prefixes:
+            n = sum(len(v) for k, v in kernels.items() if k.startswith(p))
+            if n:
+                return n
+        return 0
+    return {"fw_a_columns": count(("pad_rows_kernel", "fw_a_group_kernel")),
+            "fw_b_argmin": count(("fw_b_reduce2_kernel",)),
+            "fw_b_apply": count(("fw_b_apply_kernel",))}
+
+
+def _copy_scale(folder, counter, nbytes):
+    """Bytes per counted KiB / 1024: the factor that turns the counter into
+    bytes for a copy of known size."""
+    tot = _counter_totals(folder)[counter]
+    cands = [v for k, v in tot.items() if "elementwise" in k or "Mul" in k]
+    vals = max(cands, key=lambda v: np.mean(v))
+    return nbytes / (float(np.median(vals)) * 1024.0)
+
+
+def summarize_profile(args):
+    """rocprofv3 folders -> markdown summary and the per-call traffic record."""
+    name = args.config
+    disp = _dispatches(args.trace)
+    by_k = {}
+    for k, t0, t1 in disp:
+        by_k.setdefault(k, []).append((t1 - t0) / 1000.0)
+    calls = _calls_in(by_k)
+    lines = ["# rocprofv3 summary: %s, workload %s" % (
+        ", ".join(sorted({c for c in map(_call_of, by_k) if c})), name), "",
+        "Commands (each a separate run on one MI355X, from the repository root; `<out>` is a "
+        "scratch folder):", ""]
+    for cmd in args.command.split(";;"):
+        if cmd.strip():
+            lines.append("    " + cmd.strip())
+    lines += ["", "## Kernel time (`--kernel-trace --stats`)", "",
+              "Calls in the traced run: %s." % ", ".join("%s %d" % kv for kv in calls.items()), "",
+              "| kernel | call | dispatches | per call | avg us | min us | max us |",
+              "|---|---|---|---|---|---|---|"]
+    per_call_us = {}
+    for k in sorted(by_k, key=lambda k: -sum(by_k[k])):
+        v = by_k[k]
+        c = _call_of(k)
+        m = len(v) / calls[c] if c and calls.get(c) else 0
+        lines.append("| %s | %s | %d | %s | %.1f | %.1f | %.1f |" % (
+            k, c or "-", len(v), ("%.0f" % m) if m else "-", np.mean(v), np.min(v), np.max(v)))
+        if c:
+            per_call_us[c] = per_call_us.get(c, 0.0) + sum(v) / max(calls[c], 1)
+    # kernels dispatched several times per call: one row per pass
+    passes = []
+    for k, v in by_k.items():
+        c = _call_of(k)
+        if c and calls.get(c) and len(v) % calls[c] == 0 and len(v) // calls[c] > 1:
+            m = len(v) // calls[c]
+            for j in range(m):
+                pv = v[j::m]
+                passes.append("| %s | pass %d of %d | %.1f | %.1f | %.1f |" % (
+                    k, j + 1, m, np.mean(pv), np.min(pv), np.max(pv)))
+    if passes:
+        lines += ["", "Kernels launched more than once per call, by pass (dispatch order within "
+                  "the call):", "", "| kernel | pass | avg us | min us | max us |",
+                  "|---|---|---|---|---|"] + passes
+    lines += ["", "Sum of a call's kernel times, per call: " + ", ".join(
+        "%s %.1f us" % kv for kv in sorted(per_call_us.items())) + "."]
+    rec = None
+    if args.fetch and args.write and args.copy_fetch and args.copy_write:
+        nbytes = 1024 * 1024 * 1024
+        fs = _copy_scale(args.copy_fetch, "FETCH_SIZE", nbytes)
+        ws = _copy_scale(args.copy_write, "WRITE_SIZE", nbytes)
+        fetch = _counter_totals(args.fetch)["FETCH_SIZE"]
+        write = _counter_totals(args.write)["WRITE_SIZE"]
+        cf, cw = _calls_in(fetch), _calls_in(write)
+        lines += ["", "## Bytes beyond L2 (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)", "",
+                  "The counters count the L2's requests to memory: HBM, and also reads the 256 MB "
+                  "MALL serves (an upper bound on HBM bytes). A plain 1 GiB device copy "
+                  "(`bench.py --copy-calibration 1024`) counts FETCH_SIZE and WRITE_SIZE such "
+                  "that bytes = FETCH_SIZE x %.4f + WRITE_SIZE x %.4f (KiB); every figure "
+                  "below is scaled by those factors." % (fs, ws), "",
+                  "| kernel | call | FETCH_SIZE KiB | WRITE_SIZE KiB | MB per dispatch |",
+                  "|---|---|---|---|---|"]
+        tot = {}
+        for k in sorted(set(fetch) | set(write)):
+            c = _call_of(k)
+            f = fetch.get(k, [0.0])
+            wv = write.get(k, [0.0])
+            mb = (np.mean(f) * fs + np.mean(wv) * ws) * 1024.0 / 1e6
+            lines.append("| %s | %s | %.1f | %.1f | %.1f |" % (k, c or "-", np.mean(f),
+                                                               np.mean(wv), mb))
+            if c and cf.get(c) and cw.get(c):
+                tot.setdefault(c, 0.0)
+                tot[c] += (sum(f) * fs / cf[c] + sum(wv) * ws / cw[c]) * 1024.0
+        lines += ["", "Bytes beyond L2 per call: " + ", ".join(
+            "%s %.4g GB" % (c, b / 1e9) for c, b in sorted(tot.items())) + "."]
+        rec = {}
+        for c, b in tot.items():
+            if c in CALL_SOURCES:
+                rec[c] = {"source_sha": source_sha(*CALL_SOURCES[c]), "bytes_per_call": b,
+                          "us_per_call_trace": per_call_us.get(c),
+                          "kernels": sorted(k for k in fetch if _call_of(k) == c),
+                          "fetch_scale": fs, "write_scale": ws}
+    for folder in args.counters:
+        tots = _counter_totals(folder)
+        names = sorted(tots)
+        lines += ["", "## Counters: %s (mean per dispatch)" % ", ".join(names), "",
+                  "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+        ks = sorted({k for c in names for k in tots[c] if _call_of(k)})
+        for k in ks:
+            lines.append("| %s | " % k + " | ".join(
+                "%.4g" % np.mean(tots[c][k]) if k in tots[c] else "-" for c in names) + " |")
+    with open(args.summarize_profile, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    if rec:
+        allrec = {}
+        if os.path.exists(TRAFFIC_JSON):
+            with open(TRAFFIC_JSON) as f:
+                allrec = json.load(f)
+        for c, e in rec.items():
+            allrec.setdefault(c, {})[name] = e
+        with open(TRAFFIC_JSON, "w") as f:
+            json.dump(allrec, f, indent=1, sort_keys=True)
+    print("wrote %s" % args.summarize_profile)
+
+
+def _median(xs):
+    return float(np.median(np.asarray(xs, np.float64)))
+
+
+class HotPath:
+    """Device operands, outputs and workspaces of one workload, allocated
+    once; call() runs one step of the hot path on `stream`."""
+
+    def __init__(self, saa, W, w, prune=None, cap_b_extra=64):
+        import torch
+        self.saa, self.w, self.prune = saa, w, prune
+        dev = torch.device("cuda:0")
+        D = saa.DeviceCSR.from_scipy
+        self.t1, self.k2b, self.ap, self.aat, self.k2at, self.bm = (
+            D(w.t1), D(w.k2b), D(w.a_prev_t), D(w.aat), D(w.k2at), D(w.b))
+        n, k, T, cap = w.n, w.k, w.T, w.cap
+        cap_b = int(np.diff(w.b.tocsc().indptr).max()) + cap_b_extra
+        bi, bv, bc = W.bt_padded(w.b, cap_b)
+        self.bt_idx = torch.from_numpy(bi.astype(np.int32)).to(dev)
+        self.bt_val = torch.from_numpy(bv).to(dev)
+        self.bt_cnt = torch.from_numpy(bc.astype(np.int32)).to(dev)
+        self.atom_idx = torch.empty((n, cap), dtype=torch.int32, device=dev)
+        self.atom_val = torch.empty((n, cap), dtype=torch.float32, device=dev)
+        self.atom_cnt = torch.empty(n, dtype=torch.int32, device=dev)
+        ws_a = saa.seacells_fw_a_columns_workspace(n, k, T, cap, w.t1.nnz)
+        self.ws_a = torch.empty(max(ws_a, 1), dtype=torch.uint8, device=dev)
+        self.out_val = torch.empty(k, dtype=torch.float32, device=dev)
+        self.out_idx = torch.empty(k, dtype=torch.int32, device=dev)
+        self.gap = torch.empty(1, dtype=torch.float32, device=dev)
+        self.ws_b = torch.empty(saa.seacells_fw_b_argmin_workspace(n, k, w.aat.nnz),
+                                dtype=torch.uint8, device=dev)
+        self.st_a, self.st_b, self.st_p = (saa.new_status(dev) for _ in range(3))
+
+    def a_update(self, stream, trace=None):
+        w = self.w
+        kw = dict(atom_idx=self.atom_idx, atom_val=self.atom_val, atom_cnt=self.atom_cnt,
+                  trace=trace, workspace=self.ws_a, status=self.st_a, stream=stream)
+        if self.prune is None:
+            self.saa.seacells_fw_a_columns(self.t1, self.k2b, self.ap, w.n, w.k, w.T, w.cap, **kw)
+        else:
+            self.saa.seacells_fw_a_columns_pruned(self.t1, self.k2b, self.ap, w.n, w.k, w.T,
+                                                  w.cap, self.prune, **kw)
+
+    def b_argmin(self, stream):
+        w = self.w
+        self.saa.seacells_fw_b_argmin(self.k2b, self.aat, self.k2at, self.bm, w.n, w.k,
+                                      out_val=self.out_val, out_idx=self.out_idx, gap=self.gap,
+                                      workspace=self.ws_b, status=self.st_b, stream=stream)
+
+    def b_apply(self, stream, t):
+        # the B loop's step index continues after the workload's s_B prior steps
+        self.saa.seacells_fw_b_apply(self.bt_idx, self.bt_val, self.bt_cnt, self.w.n,
+                                     self.out_idx, 2.0 / (self.w.cfg.s_b + 1 + t + 2),
+                                     status=self.st_p, stream=stream)
+
+    def raise_on_status(self):
+        for st in (self.st_a, self.st_b, self.st_p):
+            self.saa.raise_on_status(st)
+
+    def traced_bytes(self):
+        """One traced A update (outside any timing) for the byte models: the
+        trace is deterministic, so the timed calls take the same picks."""
+        import torch
+        w = self.w
+        trace = torch.empty((w.n, w.T), dtype=torch.int32, device="cuda")
+        self.a_update(torch.cuda.current_stream(), trace=trace)
+        torch.cuda.synchronize()
+        self.saa.raise_on_status(self.st_a)
+        tr, cnt = trace.cpu().numpy(), self.atom_cnt.cpu().numpy()
+        return {"fw_a_columns": algorithmic_bytes_a(w, tr, cnt),
+                "fw_b_argmin": algorithmic_bytes_b(w)}, \
+               {"fw_a_columns": compulsory_bytes_a(w, cnt), "fw_b_argmin": compulsory_bytes_b(w)}
+
+
+def call_roofline(call, ms, alg, comp, traffic):
+    """Rates and fractions of HBM peak for one call: algorithmic bytes (the
+    headline), bytes the counters saw beyond L2, and compulsory bytes."""
+    sec = ms * 1e-3
+    r = {"ms": ms, "achieved": alg / sec / 1e9, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+         "frac": alg / sec / 1e9 / PEAK_HBM_GBPS, "bytes_per_launch": alg,
+         "compulsory_bytes": comp, "frac_compulsory": comp / sec / 1e9 / PEAK_HBM_GBPS,
+         "traffic": traffic}
+    r["beyond_l2_gbps"] = None if traffic is None else traffic / sec / 1e9
+    r["frac_beyond_l2"] = None if traffic is None else traffic / sec / 1e9 / PEAK_HBM_GBPS
+    return r
+
+
+def cpu_table_row(name, w, threads):
+    """The oracle's t_A and t_B on the same workload: every cell and row up to
+    n = 100k, else a sample scaled to n (stated)."""
+    import oracle
+    import scipy.sparse as sp
+    out = {"threads": threads}
+    rng = np.random.default_rng(0)
+    if w.n <= 100_000:
+        t0 = time.time()
+        oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, w.T, n_threads=threads)
+        out["t_a_s"] = time.time() - t0
+        t0 = time.time()
+        oracle.fw_b_argmin(w.k2b, w.aat, w.k2at, w.b, w.n, w.k, n_threads=threads)
+        out["t_b_s"] = time.time() - t0
+        out["sample"] = "all cells and rows"
+    else:
+        m = 2000 if w.n <= 500_000 else 400
+        cells = rng.choice(w.n, size=m, replace=False)
+        t0 = time.time()
+        oracle.fw_a_columns(w.t1, w.k2b, w.a_prev_t, w.n, w.k, w.T, cells=cells,
+                            n_threads=threads)
+        out["t_a_s"] = (time.time() - t0) * w.n / m
+        r = min(w.n, 200_000)
+        rows = lambda x: sp.csr_matrix(x[:r])  # noqa: E731
+        t0 = time.time()
+        oracle.fw_b_argmin(rows(w.k2b), w.aat, rows(w.k2at), rows(w.b), r, w.k,
+                           n_threads=threads)
+        out["t_b_s"] = (time.time() - t0) * w.n / r
+        out["sample"] = "A on %d random cells, B on the first %d rows, scaled to n" % (m, r)
+    out["cells_per_s"] = w.n / (out["t_a_s"] + out["t_b_s"])
+    return out
+
+
+def run_table(args):
+    """The A update and the B argmin alone on each workload, with the
+    oracle's times beside them; one JSON line per workload."""
+    import torch
+    import sparse_archetypal_analysis_amd as saa
+    import workloads as W
+    threads = len(os.sched_getaffinity(0))
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    for name in args.table_configs.split(","):
+        w = W.make(name, log=lambda m: print(m, file=sys.stderr, flush=True))
+        hp = HotPath(saa, W, w)
+        alg, comp = hp.traced_bytes()
+        reps = 20 if w.n <= 100_000 else 5
+        res = {}
+        for call, fn in (("fw_a_columns", hp.a_update), ("fw_b_argmin", hp.b_argmin)):
+            for _ in range(3):
+                fn(stream)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(reps)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                fn(stream)
+                e1.record(stream)
+            torch.cuda.synchronize()
+            ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+            sha = source_sha(*CALL_SOURCES[call])
+            res[call] = call_roofline(call, _median(ms), alg[call], comp[call],
+                                      traffic_from_profile(call, name, sha))
+            res[call]["reps"] = reps
+        hp.raise_on_status()
+        rec = {"workload": "%s: %s" % (name, W.DESCRIPTIONS.get(name, "")), "n": w.n, "k": w.k,
+               "nnz": w.meta.get("nnz"), "calls": res,
+               "cells_per_s": w.n / ((res["fw_a_columns"]["ms"] + res["fw_b_argmin"]["ms"]) * 1e-3)}
+        if not args.no_cpu_baseline:
+            rec["oracle"] = cpu_table_row(name, w, threads)
+            if w.n <= 20_000:
+                rec["oracle_1_thread"] = cpu_table_row(name, w, 1)
+        print(json.dumps(rec), flush=True)
+        del hp
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -305,7 +702,19 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 launches), the reference "
                          "kernel that scales the HBM byte counters")
+    ap.add_argument("--table", action="store_true",
+                    help="time the A update and the B argmin on every workload, with the oracle")
+    ap.add_argument("--table-configs", default="c1,c2,c3,c4,c5")
+    ap.add_argument("--summarize-profile", metavar="OUT_MD", default=None,
+                    help="write a rocprofv3 summary (CPU only; see the module doc)")
+    for opt in ("--trace", "--fetch", "--write", "--copy-fetch", "--copy-write"):
+        ap.add_argument(opt, default=None)
+    ap.add_argument("--counters", nargs="*", default=[])
+    ap.add_argument("--command", default="", help="the profiled command, for the summary")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args)
+        return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
@@ -313,6 +722,9 @@ def main():
         print("bench.py measures one GPU only: the path's multi-GPU sharding is a design, "
               "not built; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.table:
+        run_table(args)
+        return
 
     import torch
     import sparse_archetypal_analysis_amd as saa
@@ -323,63 +735,25 @@ def main():
     t_gen = time.time() - t_gen
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    D = saa.DeviceCSR.from_scipy
-    t1, k2b, ap_, aat, k2at, bm = (D(w.t1), D(w.k2b), D(w.a_prev_t), D(w.aat), D(w.k2at), D(w.b))
     n, k, T, cap = w.n, w.k, w.T, w.cap
     steps, warm = args.steps, args.warmup
-    cap_b = int(np.diff(w.b.tocsc().indptr).max()) + steps + warm + 2
-    bi, bv, bc = W.bt_padded(w.b, cap_b)
-    bt_idx = torch.from_numpy(bi.astype(np.int32)).to(dev)
-    bt_val = torch.from_numpy(bv).to(dev)
-    bt_cnt = torch.from_numpy(bc.astype(np.int32)).to(dev)
-    # outputs and workspaces, allocated once
-    atom_idx = torch.empty((n, cap), dtype=torch.int32, device=dev)
-    atom_val = torch.empty((n, cap), dtype=torch.float32, device=dev)
-    atom_cnt = torch.empty(n, dtype=torch.int32, device=dev)
-    ws_a_bytes = saa.seacells_fw_a_columns_workspace(n, k, T, cap, w.t1.nnz)
-    ws_a = torch.empty(max(ws_a_bytes, 1), dtype=torch.uint8, device=dev)
-    out_val = torch.empty(k, dtype=torch.float32, device=dev)
-    out_idx = torch.empty(k, dtype=torch.int32, device=dev)
-    gap = torch.empty(1, dtype=torch.float32, device=dev)
-    ws_b = torch.empty(saa.seacells_fw_b_argmin_workspace(n, k, w.aat.nnz), dtype=torch.uint8,
-                       device=dev)
-    st_a, st_b, st_p = saa.new_status(dev), saa.new_status(dev), saa.new_status(dev)
-    stream = torch.cuda.current_stream()
-
     prune = args.prune
-    if prune is None:
-        a_update = saa.seacells_fw_a_columns
-    else:
-        def a_update(*a, **kw):
-            return saa.seacells_fw_a_columns_pruned(*a, threshold=prune, **kw)
-
-    # one traced run (outside the timing) for the byte model: the trace is
-    # deterministic, so the timed runs take the same picks
-    trace = torch.empty((n, T), dtype=torch.int32, device=dev)
-    a_update(t1, k2b, ap_, n, k, T, cap, atom_idx=atom_idx, atom_val=atom_val,
-             atom_cnt=atom_cnt, trace=trace, workspace=ws_a, status=st_a)
-    torch.cuda.synchronize()
-    saa.raise_on_status(st_a)
-    bytes_a = algorithmic_bytes_a(w, trace.cpu().numpy(), atom_cnt.cpu().numpy())
-    bytes_b = algorithmic_bytes_b(w)
-    del trace
+    hp = HotPath(saa, W, w, prune=prune, cap_b_extra=steps + warm + 2)
+    stream = torch.cuda.current_stream()
+    alg, comp = hp.traced_bytes()
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
 
     def step(t, marks=None):
         if marks:
             marks[0].record(stream)
-        a_update(t1, k2b, ap_, n, k, T, cap, atom_idx=atom_idx, atom_val=atom_val,
-                 atom_cnt=atom_cnt, workspace=ws_a, status=st_a, stream=stream)
+        hp.a_update(stream)
         if marks:
             marks[1].record(stream)
-        saa.seacells_fw_b_argmin(k2b, aat, k2at, bm, n, k, out_val=out_val, out_idx=out_idx,
-                                 gap=gap, workspace=ws_b, status=st_b, stream=stream)
+        hp.b_argmin(stream)
         if marks:
             marks[2].record(stream)
-        # B loop index continues after the s_B prior steps of the workload
-        saa.seacells_fw_b_apply(bt_idx, bt_val, bt_cnt, n, out_idx,
-                                2.0 / (w.cfg.s_b + 1 + t + 2), status=st_p, stream=stream)
+        hp.b_apply(stream, t)
         if marks:
             marks[3].record(stream)
 
@@ -391,22 +765,19 @@ def main():
         step(warm + t, ev[t])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for st in (st_a, st_b, st_p):
-        saa.raise_on_status(st)
+    hp.raise_on_status()
 
-    a_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    b_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    p_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    per = {c: [e[j].elapsed_time(e[j + 1]) for e in ev]
+           for j, c in enumerate(("fw_a_columns", "fw_b_argmin", "fw_b_apply"))}
     ms_step = wall * 1000.0 / steps
-    a_gbps = bytes_a / (a_ms * 1e-3) / 1e9
-    b_gbps = bytes_b / (b_ms * 1e-3) / 1e9
-    dominant = "fw_a_columns" if a_ms >= b_ms else "fw_b_argmin"
-    if dominant == "fw_a_columns":
-        ach, per_launch, sha = a_gbps, bytes_a, source_sha("fw_a.hip")
-    else:
-        ach, per_launch, sha = b_gbps, bytes_b, source_sha("fw_b.hip")
-    traffic = None if prune is not None else traffic_from_profile(dominant, args.config, sha)
-
+    calls = {}
+    for c in ("fw_a_columns", "fw_b_argmin"):
+        sha = source_sha(*CALL_SOURCES[c])
+        traffic = None if prune is not None else traffic_from_profile(c, args.config, sha)
+        calls[c] = call_roofline(c, float(np.mean(per[c])), alg[c], comp[c], traffic)
+        calls[c]["ms_median"] = _median(per[c])
+    dominant = max(calls, key=lambda c: calls[c]["ms"])
+    d = calls[dominant]
     rec = {
         "metric": METRIC,
         "value": n / (ms_step * 1e-3),
@@ -422,21 +793,30 @@ def main():
         "data": "synthetic",
         "config": {"workload": "%s: %s" % (args.config, W.DESCRIPTIONS.get(args.config, "")),
                    "n": n, "k": k, "T": T, "cap": cap, "nnz": w.meta.get("nnz"),
-                   "prune_threshold": prune},
-        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": ach, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": ach / PEAK_HBM_GBPS,
-                     "bytes_per_launch": per_launch, "traffic": traffic},
-        "kernels_ms": {"fw_a_columns": a_ms, "fw_b_argmin": b_ms, "fw_b_apply": p_ms},
-        "kernels_gbps": {"fw_a_columns": a_gbps, "fw_b_argmin": b_gbps},
-        "a_cells_per_s": n / (a_ms * 1e-3),
-        "b_cells_per_s": n / (b_ms * 1e-3),
+                   "b_init": w.meta.get("b_init"), "prune_threshold": prune},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": d["achieved"],
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": d["frac"],
+                     "traffic": d["traffic"], "bytes_per_launch": d["bytes_per_launch"],
+                     "frac_beyond_l2": d["frac_beyond_l2"],
+                     "compulsory_bytes": d["compulsory_bytes"],
+                     "frac_compulsory": d["frac_compulsory"],
+                     "note": "achieved = algorithmic bytes (every sparse entry the method "
+                             "touches, re-reads counted) / mean call time; frac_beyond_l2 = "
+                             "rocprofv3 FETCH_SIZE + WRITE_SIZE per call (HBM and MALL) / time "
+                             "/ peak; frac_compulsory = every input read once / time / peak"},
+        "calls": calls,
+        "kernels_ms": {c: float(np.mean(v)) for c, v in per.items()},
+        "kernels_ms_median": {c: _median(v) for c, v in per.items()},
+        "a_cells_per_s": n / (calls["fw_a_columns"]["ms"] * 1e-3),
+        "b_cells_per_s": n / (calls["fw_b_argmin"]["ms"] * 1e-3),
         "generation_s": t_gen,
         "device": torch.cuda.get_device_name(dev),
     }
     if not args.no_operands:
         rec["operands"] = time_operands(saa, W, w, stream)
     if args.b_loop_steps > 0:
-        rec["b_loop"] = time_b_loop(saa, W, w, args.b_loop_steps, b_ms, stream)
+        rec["b_loop"] = time_b_loop(saa, W, w, args.b_loop_steps, calls["fw_b_argmin"]["ms"],
+                                    stream)
     if args.iteration_b_steps > 0:
         rec["iteration"] = time_iteration(saa, W, w, args.iteration_b_steps, stream)
     if not args.no_cpu_baseline:

@@ -41,8 +41,10 @@
  *   orders; two calls on the same inputs give bitwise-equal outputs.
  * - Calls that share a workspace or status word must not overlap.
  * - There is no ceiling on k: state that does not fit the compute unit's
- *   local memory moves to the workspace (A) or is split into column
- *   slices (B).
+ *   local memory moves to the workspace (A) or is split into column slices
+ *   of at most 2048 columns (B, as many slices as k needs). What grows with
+ *   k is the workspace the *_workspace() queries report; a caller who cannot
+ *   provide it gets SEACELLS_E_WORKSPACE, never a silent no-op.
  */
 #ifndef SEACELLS_FW_H
 #define SEACELLS_FW_H
@@ -67,7 +69,7 @@ extern "C" {
 #define SEACELLS_FLAG_PARTIALS_INVALID 0x2u /* a B partial was stale or out of range */
 #define SEACELLS_FLAG_B_CAP_OVERFLOW 0x4u   /* a padded B^T row was full */
 #define SEACELLS_FLAG_BAD_INDEX 0x8u        /* an index argument was out of range */
-#define SEACELLS_FLAG_NONFINITE 0x10u       /* a non-finite value reached an argmin */
+#define SEACELLS_FLAG_NONFINITE 0x10u       /* an argmin found no finite minimum */
 #define SEACELLS_FLAG_BAD_GAMMA 0x20u       /* a step size outside (0, 1] */
 
 typedef struct ihipStream_t *seacells_stream_t; /* == hipStream_t */
@@ -90,8 +92,8 @@ typedef struct seacells_csr {
  * 2048) two counters and queues of n cell ids (the cells the compact
  * per-cell state hands on); and per-wave state slices when not even one
  * cell's dense state fits in local memory. 0 when none is needed (small
- * k). Depends only on its arguments (and on the SEACELLS_A_* experiment
- * variables of the environment, which must be the same at the call).
+ * k). Depends only on its arguments (and on the plan overrides of
+ * seacells_debug.h, which tests set; they must be the same at the call).
  */
 size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint32_t cap,
                                        uint32_t t1_nnz);
@@ -134,6 +136,9 @@ size_t seacells_fw_a_columns_workspace(uint32_t n, uint32_t k, uint32_t T, uint3
  * workspace device buffer of at least seacells_fw_a_columns_workspace()
  *           bytes (may be NULL when that is 0), 256-byte aligned.
  * k must be below 2^30 (else SEACELLS_E_TOO_LARGE).
+ * SEACELLS_FLAG_NONFINITE: a cell's gradient state held no value below +inf
+ * at some step (NaN or +inf everywhere: non-finite inputs); that step took
+ * index 0. Entries that are NaN among finite ones never win the argmin.
  */
 int seacells_fw_a_columns(const seacells_csr *t1, const seacells_csr *k2b,
                           const seacells_csr *a_prev_t, uint32_t n, uint32_t k,
@@ -172,8 +177,11 @@ int seacells_fw_a_columns_pruned(const seacells_csr *t1, const seacells_csr *k2b
 /*
  * Workspace bytes seacells_fw_b_argmin needs for these sizes (always > 0;
  * aat_nnz: the non-zeros of A A^T). It holds the per-row-range partials
- * (8 bytes per column each), and, when k fits one column slice (k <= 2048),
- * a copy of A A^T with every row padded to whole chunks of 64 entries (at
+ * (8 bytes per column each; 8192 row ranges for k <= 2048, else 16384, fewer
+ * when that would pass 2 GiB, at least one), one stamp and one gap partial
+ * per (row range, column slice), the column-slice table (4 (k + 1) bytes per
+ * slice when k > 2048), and, when k fits one column slice (k <= 2048), a
+ * copy of A A^T with every row padded to whole chunks of 64 entries (at
  * most 8 * (aat_nnz + 64 k) bytes). Depends only on its arguments.
  */
 size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k, uint32_t aat_nnz);
@@ -198,8 +206,11 @@ size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k, uint32_t aat_nnz);
  * gap      device [1] f32 out, or NULL.
  * fw_gap   device [1] f32 out, or NULL; needs b (else SEACELLS_E_NULL).
  *          Both sums are taken in f64 in a fixed order, then rounded.
- * The reduce stage checks that every partial was written by this call and
- * holds a row below n; otherwise it sets SEACELLS_FLAG_PARTIALS_INVALID.
+ * The reduce stage checks every partial it consumes: the stamp of its
+ * (row range, column slice) unit must be this call's, and its row must lie
+ * in the unit's row range (so below n); otherwise it sets
+ * SEACELLS_FLAG_PARTIALS_INVALID. SEACELLS_FLAG_NONFINITE: a column minimum
+ * is not finite, or some row range saw no value below +inf in a column.
  */
 int seacells_fw_b_argmin(const seacells_csr *k2b, const seacells_csr *aat,
                          const seacells_csr *k2at, const seacells_csr *b, uint32_t n,

@@ -32,20 +32,22 @@ class BLoop:
     gap: np.ndarray      # [T] sum(B_t * G_t)
     b: np.ndarray        # [n, k] B after the last step
     k2b: np.ndarray      # [n, k] K (K B) after the last step
+    k2b_used: np.ndarray = None  # [T, k, k] row used[t, c] of K^2 B_t (keep_rows only)
 
 
 def _dense(m) -> np.ndarray:
     return np.asarray(m.toarray() if sp.issparse(m) else m, np.float64)
 
 
-def fw_b_loop(K, B0, aat, k2at, T: int, gammas=None, force=None) -> BLoop:
+def fw_b_loop(K, B0, aat, k2at, T: int, gammas=None, force=None, keep_rows=False) -> BLoop:
     """T Frank-Wolfe steps of the B update from B0 (n x k).
 
     Step t: K^2 B_t = K (K B_t); G_t = K^2 B_t A A^T - K^2 A^T; the pick of
     column c is the lowest row minimising G_t[:, c]; B_{t+1} =
     (1 - gamma_t) B_t + gamma_t S_t. With ``force`` ([T, k]) the step uses
     force[t] instead of the pick (replaying another trajectory) and reports
-    G_t there.
+    G_t there. ``keep_rows`` also returns the rows of K^2 B_t that G_t was
+    read at (how a change of A A^T reaches those values).
     """
     Ks = sp.csr_matrix(K, dtype=np.float64)
     B = _dense(B0).copy()
@@ -56,6 +58,7 @@ def fw_b_loop(K, B0, aat, k2at, T: int, gammas=None, force=None) -> BLoop:
     out = {nm: np.zeros((T, k)) for nm in ("gmin", "second", "g_used", "scale")}
     pick = np.zeros((T, k), np.int64)
     used = np.zeros((T, k), np.int64)
+    rows = np.zeros((T, k, k)) if keep_rows else None
     gap = np.zeros(T)
     for t in range(T):
         K2B = Ks @ (Ks @ B)
@@ -70,10 +73,12 @@ def fw_b_loop(K, B0, aat, k2at, T: int, gammas=None, force=None) -> BLoop:
         u = p if force is None else np.asarray(force[t], np.int64)
         used[t] = u
         out["g_used"][t] = G[u, cols]
+        if keep_rows:
+            rows[t] = K2B[u]
         S = np.abs(K2B[u]) @ np.abs(AAt)  # [k, k]: rows u_c of |K^2 B| |AA^T|
         out["scale"][t] = S[cols, cols] + np.abs(K2At[u, cols])
         gap[t] = float(np.sum(B * G))
         g = 2.0 / (t + 2.0) if gammas is None else float(gammas[t])
         B *= 1.0 - g
         B[u, cols] += g
-    return BLoop(pick=pick, used=used, gap=gap, b=B, k2b=Ks @ (Ks @ B), **out)
+    return BLoop(pick=pick, used=used, gap=gap, b=B, k2b=Ks @ (Ks @ B), k2b_used=rows, **out)

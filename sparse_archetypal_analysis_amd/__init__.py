@@ -1,7 +1,8 @@
 """SEACells Frank-Wolfe hot path on MI355X (gfx950): HIP kernels behind a C ABI.
 
 ``native`` binds ``libseacells_fw.so`` (include/seacells_fw.h for the A and B
-updates, include/seacells_sparse.h for the operand construction); ``csrc/``
+updates, include/seacells_sparse.h for the operand construction,
+include/seacells_debug.h for the test hooks); ``csrc/``
 holds the HIP sources; ``_build`` compiles them in-tree.
 """
 from .native import (DeviceCSR, SeacellsError, load, new_status, raise_on_status,  # noqa: F401
@@ -17,4 +18,5 @@ from .native import (DeviceCSR, SeacellsError, load, new_status, raise_on_status
                      csr_add, seacells_fw_b_vertex_workspace, seacells_fw_b_vertex, fw_b_loop,
                      seacells_fw_a_to_csr_workspace, seacells_fw_a_to_csr_rows,
                      seacells_fw_a_to_csr_fill, fw_a_to_csr, outer_iteration, csr_trim,
-                     status_flags)
+                     seacells_debug_set_a_options, seacells_debug_b_layout,
+                     seacells_debug_b_last_epoch, seacells_debug_b_reduce, status_flags)

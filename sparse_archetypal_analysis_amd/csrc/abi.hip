@@ -1,10 +1,12 @@
-// Exported C ABI (include/seacells_fw.h, include/seacells_sparse.h): host-side validation, workspace
+// Exported C ABI (include/seacells_fw.h, include/seacells_sparse.h,
+// include/seacells_debug.h): host-side validation, workspace
 // sizing and dispatch onto the caller's stream. Argument checks run before
 // any HIP call, so they also work on a machine without a GPU.
 #include <atomic>
 #include <cstdio>
 #include <cstring>
 
+#include "../../include/seacells_debug.h"
 #include "../../include/seacells_fw.h"
 #include "../../include/seacells_sparse.h"
 #include "common.hpp"
@@ -37,12 +39,15 @@ hipError_t device_info(DeviceInfo *out) {
 
 // Per-call stamp for the B partials. Starts away from 0 so zero-filled or
 // leftover workspace never matches, and never takes the value 0.
+static thread_local uint32_t g_last_epoch = 0;
+
 static uint32_t next_epoch() {
   static std::atomic<uint32_t> counter{0x5EAC0001u};
   uint32_t e;
   do {
     e = counter.fetch_add(1u, std::memory_order_relaxed);
   } while (e == 0u);
+  g_last_epoch = e;
   return e;
 }
 
@@ -153,6 +158,7 @@ int seacells_fw_b_argmin(const seacells_csr *k2b, const seacells_csr *aat,
   if ((rc = check_csr(k2at, n, k)) != SEACELLS_OK) return rc;
   if (b != nullptr && (rc = check_csr(b, n, k)) != SEACELLS_OK) return rc;
   const BPlan plan = plan_b(n, k, aat->nnz);
+  if (plan.pa_chunks >= (1ull << 32)) return SEACELLS_E_TOO_LARGE;
   if (workspace == nullptr || workspace_bytes < plan.ws_bytes) return SEACELLS_E_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return SEACELLS_E_WORKSPACE;
   Csr bc{};
@@ -395,6 +401,60 @@ int seacells_fw_a_to_csr_fill(const uint32_t *atom_idx, const float *atom_val,
   e = launch_atoms_fill(atom_idx, atom_val, atom_cnt, n, k, cap, at_row_ptr, at_col_idx, at_val,
                         status, s);
   if (e != hipSuccess) return hip_fail(e, "fw_a_to_csr_fill launch");
+  return SEACELLS_OK;
+}
+
+// --- test and experiment hooks (seacells_debug.h) -------------------------
+
+int seacells_debug_set_a_options(const seacells_a_options *opt) {
+  AOptions o;
+  if (opt != nullptr) {
+    if (opt->support < -1 || opt->support > 1) return SEACELLS_E_SHAPE;
+    if (opt->support_waves != 0 && (opt->support_waves < 4 || opt->support_waves > 32))
+      return SEACELLS_E_SHAPE;
+    if (opt->dense_argmin < 0 || opt->dense_argmin > 1) return SEACELLS_E_SHAPE;
+    if (opt->group != 0 && opt->group != 16 && opt->group != 32 && opt->group != 64)
+      return SEACELLS_E_SHAPE;
+    o.support = opt->support;
+    o.support_waves = opt->support_waves;
+    o.dense_argmin = opt->dense_argmin == 1;
+    o.group = opt->group;
+  }
+  a_options() = o;
+  return SEACELLS_OK;
+}
+
+int seacells_debug_b_layout(uint32_t n, uint32_t k, uint32_t aat_nnz, seacells_b_layout *out) {
+  if (out == nullptr) return SEACELLS_E_NULL;
+  if (n == 0 || k == 0) return SEACELLS_E_SHAPE;
+  if (n >= 0x80000000u || k >= 0x80000000u) return SEACELLS_E_TOO_LARGE;
+  const BPlan p = plan_b(n, k, aat_nnz);
+  out->keys_offset = p.off_keys;
+  out->stamps_offset = p.off_stamp;
+  out->n_row_blocks = p.n_row_blocks;
+  out->n_slices = p.n_slices;
+  out->slice_w = p.slice_w;
+  out->reserved = 0;
+  return SEACELLS_OK;
+}
+
+uint32_t seacells_debug_b_last_epoch(void) { return g_last_epoch; }
+
+int seacells_debug_b_reduce(uint32_t n, uint32_t k, uint32_t aat_nnz, uint32_t epoch,
+                            float *out_val, uint32_t *out_idx, float *gap, void *workspace,
+                            size_t workspace_bytes, uint32_t *status, seacells_stream_t stream) {
+  if (out_val == nullptr || out_idx == nullptr || status == nullptr) return SEACELLS_E_NULL;
+  if (n == 0 || k == 0) return SEACELLS_E_SHAPE;
+  if (n >= 0x80000000u || k >= 0x80000000u) return SEACELLS_E_TOO_LARGE;
+  const BPlan plan = plan_b(n, k, aat_nnz);
+  if (workspace == nullptr || workspace_bytes < plan.ws_bytes ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SEACELLS_E_WORKSPACE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_status_clear(status, s);
+  if (e != hipSuccess) return hip_fail(e, "status clear");
+  e = launch_fw_b_reduce(plan, n, k, out_val, out_idx, gap, nullptr, workspace, status, epoch, s);
+  if (e != hipSuccess) return hip_fail(e, "fw_b reduce launch");
   return SEACELLS_OK;
 }
 

@@ -114,6 +114,17 @@ hipError_t device_info(DeviceInfo *out);
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // --- A update -------------------------------------------------------------
+// Plan overrides for tests and experiments (set through the debug ABI; the
+// defaults choose by k). Process-wide: the workspace query and the calls
+// read the same values.
+struct AOptions {
+  int support = -1;            // -1: by k; 0: never the support state; 1: for any k
+  uint32_t support_waves = 0;  // resident waves per CU the first support pass is sized for (0: default)
+  bool dense_argmin = false;   // a dense scan decides every step
+  uint32_t group = 0;          // lanes per cell of the dense kernels (0: by k; 16, 32, 64)
+};
+AOptions &a_options();
+
 struct APlan {
   bool prune;                  // the pruning + renormalisation variant
   uint32_t group;              // lanes per cell (16, 32 or 64)
@@ -169,6 +180,11 @@ hipError_t launch_fw_b(const BPlan &plan, Csr k2b, Csr aat, Csr k2at, Csr b, uin
                        uint32_t k, float *out_val, uint32_t *out_idx, float *gap,
                        float *fw_gap, void *ws, uint32_t *status, uint32_t epoch,
                        hipStream_t stream);
+// the two reduce stages alone, on the partials a launch_fw_b with the same
+// plan left in ws (stamped with `epoch`)
+hipError_t launch_fw_b_reduce(const BPlan &plan, uint32_t n, uint32_t k, float *out_val,
+                              uint32_t *out_idx, float *gap, float *fw_gap, void *ws,
+                              uint32_t *status, uint32_t epoch, hipStream_t stream);
 hipError_t launch_fw_b_apply(uint32_t *bt_idx, float *bt_val, uint32_t *bt_cnt, uint32_t n,
                              uint32_t k, uint32_t cap_b, const uint32_t *arg_idx, float gamma,
                              uint32_t *status, hipStream_t stream);

@@ -38,8 +38,6 @@
 //
 // Lanes with nothing to do in a sparse pass point at the first padding
 // column (value +inf, added weight 0).
-#include <stdlib.h>
-
 #include "common.hpp"
 
 namespace seacells {
@@ -204,7 +202,9 @@ __device__ __forceinline__ uint32_t dense_argmin(const float *h, uint32_t nch, u
   const uint32_t key = f32_order(bv);
   const uint32_t best = group_min_u32<G>(key);
   uint32_t cand = kNone;
-  if (key == best) {
+  // a lane with no value below +inf (padding, or a NaN state) offers none:
+  // a group with no such value returns kNone (>= k)
+  if (key == best && bv < __builtin_inff()) {
     const float4 v = *reinterpret_cast<const float4 *>(p + bch * 4 * G);
     const uint32_t j = (v.x == bv) ? 0u : (v.y == bv) ? 1u : (v.z == bv) ? 2u : 3u;
     cand = bch * 4 * G + gl * 4 + j;
@@ -1590,21 +1590,12 @@ __global__ void zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
   if (threadIdx.x < count) p[threadIdx.x] = 0u;
 }
 
-// SEACELLS_A_SUPPORT: "0" never uses the support state, "1" uses it for any
-// k (experiments and tests); unset: by k.
-int support_mode() {
-  const char *v = getenv("SEACELLS_A_SUPPORT");
-  if (v == nullptr || v[0] == 0) return -1;
-  return v[0] == '0' ? 0 : 1;
-}
+// Support state: -1 by k, 0 never, 1 for any k (tests and experiments).
+int support_mode() { return a_options().support; }
 
 uint32_t support_waves_per_cu() {
-  const char *v = getenv("SEACELLS_A_SUPPORT_WAVES");
-  if (v != nullptr) {
-    const int w = atoi(v);
-    if (w >= 4 && w <= 32) return (uint32_t)w;
-  }
-  return kSupDefaultWaves;
+  const uint32_t w = a_options().support_waves;
+  return (w >= 4 && w <= 32) ? w : kSupDefaultWaves;
 }
 
 // LDS of one support wave when `waves` waves per CU are resident: the
@@ -1738,19 +1729,12 @@ hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, uint32_t tie
   return hipGetLastError();
 }
 
-bool dense_only_requested() {
-  const char *v = getenv("SEACELLS_A_DENSE_ARGMIN");
-  return v != nullptr && v[0] == '1';
-}
+bool dense_only_requested() { return a_options().dense_argmin; }
 
-
-// Lanes per cell: from the environment for experiments, else by k.
+// Lanes per cell: an override for tests and experiments, else by k.
 uint32_t group_width(uint32_t k) {
-  const char *v = getenv("SEACELLS_A_GROUP");
-  if (v != nullptr) {
-    const int g = atoi(v);
-    if (g == 16 || g == 32 || g == 64) return (uint32_t)g;
-  }
+  const uint32_t g = a_options().group;
+  if (g == 16 || g == 32 || g == 64) return g;
   // small k: several cells per wave amortise the per-step fixed cost; large
   // k: one cell per wave keeps the dense fallback scan short
   if (k <= 512) return 16;
@@ -1759,6 +1743,11 @@ uint32_t group_width(uint32_t k) {
 }
 
 }  // namespace
+
+AOptions &a_options() {
+  static AOptions opt;
+  return opt;
+}
 
 APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap, bool prune, uint32_t t1_nnz) {
   APlan p{};

@@ -43,8 +43,8 @@ constexpr uint32_t kMaxChunks = 64;
 constexpr uint32_t kGatherRows = 4;  // AAt runs whose loads are in flight together
 constexpr uint32_t kXcds = 8;        // MI355X: 8 XCDs of 32 CUs, each with its own 4 MB L2
 constexpr size_t kSliceAatBytes = 5u << 19;  // AAt bytes per slice kept within one L2 (2.5 MB)
-constexpr uint32_t kMaxSlices = 128;
 constexpr uint32_t kSlicedRowBlocks = 16384;  // row ranges per slice when k is sliced
+constexpr uint64_t kKeysBudget = 1ull << 31;  // bytes of partial keys beyond which row ranges shrink
 constexpr uint32_t kAccPad = 32;             // dummy slots after each dual accumulator
 constexpr uint32_t kStageSlots = kWave + 8;  // staged triples (a run of pairs reads past 64)
 
@@ -55,6 +55,8 @@ __device__ __forceinline__ T load_at(const T *__restrict__ base, uint32_t byte_o
   return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
 }
 constexpr uint32_t kNoCol = 0xffffffffu;
+// the key a unit leaves in a column where no row gave a value below +inf
+constexpr uint64_t kNoValueKey = ((uint64_t)0xff800000u << 32) | 0xffffffffull;
 
 // acc[c] += v (LDS read, add, write). One wave's LDS operations execute in
 // issue order and the columns of one row are unique, so the sum order per
@@ -79,25 +81,27 @@ __global__ void __launch_bounds__(256)
     seg_table_kernel(Csr aat, uint32_t k, uint32_t slice_w, uint32_t n_slices,
                      uint32_t *__restrict__ seg) {
   // slice-major: seg[s * k + m], so the lookups of one slice share lines
-  const uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (uint64_t)k * ((uint64_t)n_slices + 1)) return;
-  const uint32_t s = (uint32_t)(e / k);
-  const uint32_t m = (uint32_t)(e - (uint64_t)s * k);
-  uint32_t lo, hi;
-  row_ok(aat, m, lo, hi);
-  if (s == n_slices) {
-    seg[e] = hi;
-    return;
+  const uint64_t total = (uint64_t)k * ((uint64_t)n_slices + 1);
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+    const uint32_t s = (uint32_t)(e / k);
+    const uint32_t m = (uint32_t)(e - (uint64_t)s * k);
+    uint32_t lo, hi;
+    row_ok(aat, m, lo, hi);
+    if (s == n_slices) {
+      seg[e] = hi;
+      continue;
+    }
+    const uint32_t target = s * slice_w;
+    while (lo < hi) {  // first position with column >= target
+      const uint32_t mid = lo + (hi - lo) / 2;
+      if (aat.idx[mid] < target)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    seg[e] = lo;
   }
-  const uint32_t target = s * slice_w;
-  while (lo < hi) {  // first position with column >= target
-    const uint32_t mid = lo + (hi - lo) / 2;
-    if (aat.idx[mid] < target)
-      lo = mid + 1;
-    else
-      hi = mid;
-  }
-  seg[e] = lo;
 }
 
 // ---------------------------------------------------------------------------
@@ -474,10 +478,14 @@ __global__ void __launch_bounds__(kBThreads)
 // Stage 1: block (column group x, row-range chunk y); 4 waves x 64 lanes.
 // Lane l of every wave owns column x * 64 + l; wave w takes row ranges
 // rb = chunk_lo + w, + 4, ... . Keys are u64 minima, so the order in which
-// row ranges are combined does not matter.
+// row ranges are combined does not matter. Every partial it consumes is
+// checked: the unit's stamp must be this call's epoch, and the key's row
+// must lie in the unit's row range [n rb / NB, n (rb + 1) / NB) (tested
+// without a division: n rb < (row + 1) NB <= n (rb + 1)). A unit whose
+// column never saw a value below +inf left (+inf, ~0): no finite value.
 __global__ void __launch_bounds__(256)
     fw_b_reduce1_kernel(const uint64_t *__restrict__ part_key, const uint32_t *__restrict__ stamps,
-                        uint32_t n_row_blocks, uint32_t n_slices, uint32_t slice_w,
+                        uint32_t n, uint32_t n_row_blocks, uint32_t n_slices, uint32_t slice_w,
                         uint32_t n_chunks, uint32_t k, uint32_t epoch,
                         uint64_t *__restrict__ part2, uint32_t *__restrict__ status) {
   __shared__ uint64_t red[4][kReduceCols];
@@ -495,6 +503,12 @@ __global__ void __launch_bounds__(256)
       const uint64_t key = part_key[(size_t)rb * k + c];
       best = key < best ? key : best;
       if (stamps[(size_t)rb * n_slices + sl] != epoch) flags |= kFlagPartialsInvalid;
+      const uint64_t row1 = (uint64_t)(uint32_t)key + 1u;
+      if (key == kNoValueKey)
+        flags |= kFlagNonfinite;
+      else if (!((uint64_t)n * rb < row1 * n_row_blocks &&
+                 row1 * n_row_blocks <= (uint64_t)n * (rb + 1u)))
+        flags |= kFlagPartialsInvalid;
     }
   }
   red[w][lane] = best;
@@ -526,7 +540,8 @@ __global__ void __launch_bounds__(256)
     const uint32_t row = (uint32_t)best;
     const float v = f32_unorder((uint32_t)(best >> 32));
     uint32_t flags = 0;
-    if (row >= n) flags |= kFlagPartialsInvalid;
+    // (+inf, ~0): no row gave this column a finite value (stage 1 flagged it)
+    if (row >= n && best != kNoValueKey) flags |= kFlagPartialsInvalid;
     if (!__builtin_isfinite(v)) flags |= kFlagNonfinite;
     out_val[c] = v;
     out_idx[c] = row;
@@ -660,19 +675,19 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
 }  // namespace
 
 // Slices: one when k fits one accumulator; otherwise enough that each holds
-// at most ~2.5 MB of AAt (the L2 share of one XCD), as 2, 4 or a multiple
-// of 8 slices so that they spread evenly over the XCDs.
+// at most ~2.5 MB of AAt (the L2 share of one XCD) and at most 2048
+// columns (so any k has a plan), as 2, 4 or a multiple of 8 slices so that
+// they spread evenly over the XCDs.
 static uint32_t slices_for(uint32_t k, uint64_t aat_nnz) {
   const uint32_t wmax = 256u * kBMaxS4;
   if (k <= wmax) return 1;
-  uint64_t s = (k + wmax - 1) / wmax;
+  uint64_t s = ((uint64_t)k + wmax - 1) / wmax;
   const uint64_t by_l2 = (aat_nnz * 8 + kSliceAatBytes - 1) / kSliceAatBytes;
   if (by_l2 > s) s = by_l2;
   if (s <= 2) return 2;
   if (s <= 4) return 4;
   s = (s + kXcds - 1) / kXcds * kXcds;
-  if (s > kMaxSlices) s = kMaxSlices;
-  const uint64_t most = (k + 3) / 4;  // slices of at least 4 columns
+  const uint64_t most = ((uint64_t)k + 3) / 4;  // slices of at least 4 columns
   return (uint32_t)(s < most ? s : most);
 }
 
@@ -682,10 +697,15 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices, uint64_
   p.slice_w = (uint32_t)align_up((k + n_slices - 1) / n_slices, 4);
   p.n_slices = (k + p.slice_w - 1) / p.slice_w;
   p.s4 = (p.slice_w + 255u) / 256u;
-  uint32_t rb = p.n_slices > 1 ? kSlicedRowBlocks : kBUnitsTarget;
+  uint64_t rb = p.n_slices > 1 ? kSlicedRowBlocks : kBUnitsTarget;
+  // the partial keys take n_row_blocks * k * 8 bytes: fewer row ranges for
+  // a very large k (one at least)
+  const uint64_t rb_budget = kKeysBudget / ((uint64_t)k * sizeof(uint64_t));
+  if (rb > rb_budget) rb = rb_budget;
   if (rb > n) rb = n;
-  p.n_row_blocks = rb;
-  p.n_chunks = rb < kMaxChunks ? rb : kMaxChunks;
+  if (rb < 1) rb = 1;
+  p.n_row_blocks = (uint32_t)rb;
+  p.n_chunks = p.n_row_blocks < kMaxChunks ? p.n_row_blocks : kMaxChunks;
   const size_t units = (size_t)p.n_row_blocks * p.n_slices;
   size_t off = 0;
   p.off_keys = off;
@@ -730,7 +750,6 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
                        hipStream_t stream) {
   char *base = static_cast<char *>(ws);
   uint64_t *keys = reinterpret_cast<uint64_t *>(base + p.off_keys);
-  uint64_t *part2 = reinterpret_cast<uint64_t *>(base + p.off_part2);
   float *gap_part = reinterpret_cast<float *>(base + p.off_gap);
   uint32_t *stamps = reinterpret_cast<uint32_t *>(base + p.off_stamp);
   uint32_t *seg = p.n_slices > 1 ? reinterpret_cast<uint32_t *>(base + p.off_seg) : nullptr;
@@ -740,8 +759,9 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
   hipError_t e;
   if (seg != nullptr) {
     const uint64_t total = (uint64_t)k * (p.n_slices + 1);
-    hipLaunchKernelGGL(seg_table_kernel, dim3((uint32_t)((total + 255) / 256)), dim3(256), 0,
-                       stream, aat, k, p.slice_w, p.n_slices, seg);
+    const uint64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(seg_table_kernel, dim3((uint32_t)(blocks < 65536u ? blocks : 65536u)),
+                       dim3(256), 0, stream, aat, k, p.slice_w, p.n_slices, seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // the padded AAt copy (unless narrow slices gather two runs per wave
@@ -781,9 +801,21 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
       return hipErrorInvalidValue;
   }
   if (e != hipSuccess) return e;
+  return launch_fw_b_reduce(p, n, k, out_val, out_idx, gap, fw_gap, ws, status, epoch, stream);
+}
+
+hipError_t launch_fw_b_reduce(const BPlan &p, uint32_t n, uint32_t k, float *out_val,
+                              uint32_t *out_idx, float *gap, float *fw_gap, void *ws,
+                              uint32_t *status, uint32_t epoch, hipStream_t stream) {
+  char *base = static_cast<char *>(ws);
+  const uint64_t *keys = reinterpret_cast<const uint64_t *>(base + p.off_keys);
+  uint64_t *part2 = reinterpret_cast<uint64_t *>(base + p.off_part2);
+  const float *gap_part = reinterpret_cast<const float *>(base + p.off_gap);
+  const uint32_t *stamps = reinterpret_cast<const uint32_t *>(base + p.off_stamp);
+  hipError_t e;
   const dim3 g1((k + kReduceCols - 1) / kReduceCols, p.n_chunks);
-  hipLaunchKernelGGL(fw_b_reduce1_kernel, g1, dim3(256), 0, stream, keys, stamps, p.n_row_blocks,
-                     p.n_slices, p.slice_w, p.n_chunks, k, epoch, part2, status);
+  hipLaunchKernelGGL(fw_b_reduce1_kernel, g1, dim3(256), 0, stream, keys, stamps, n,
+                     p.n_row_blocks, p.n_slices, p.slice_w, p.n_chunks, k, epoch, part2, status);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const uint32_t units = p.n_row_blocks * p.n_slices;
   hipLaunchKernelGGL(fw_b_reduce2_kernel, dim3((k + 255) / 256 + 1), dim3(256), 0, stream, part2,

@@ -1,5 +1,5 @@
 """Thin ctypes binding of ``libseacells_fw.so`` (include/seacells_fw.h,
-include/seacells_sparse.h).
+include/seacells_sparse.h, include/seacells_debug.h).
 
 The functions carry the C names and only marshal arguments: device tensors
 become raw pointers, torch's current stream becomes the hipStream_t. Every
@@ -34,6 +34,8 @@ EXPORTS = ("seacells_fw_a_columns_workspace", "seacells_fw_a_columns",
            "seacells_fw_b_vertex_workspace", "seacells_fw_b_vertex",
            "seacells_fw_a_to_csr_workspace", "seacells_fw_a_to_csr_rows",
            "seacells_fw_a_to_csr_fill",
+           "seacells_debug_set_a_options", "seacells_debug_b_layout",
+           "seacells_debug_b_last_epoch", "seacells_debug_b_reduce",
            "seacells_status_string", "seacells_last_error", "seacells_version")
 
 
@@ -41,6 +43,17 @@ class seacells_csr(ctypes.Structure):
     _fields_ = [("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
                 ("val", ctypes.c_void_p), ("n_rows", ctypes.c_uint32),
                 ("n_cols", ctypes.c_uint32), ("nnz", ctypes.c_uint32)]
+
+
+class seacells_a_options(ctypes.Structure):
+    _fields_ = [("support", ctypes.c_int32), ("support_waves", ctypes.c_uint32),
+                ("dense_argmin", ctypes.c_int32), ("group", ctypes.c_uint32)]
+
+
+class seacells_b_layout(ctypes.Structure):
+    _fields_ = [("keys_offset", ctypes.c_uint64), ("stamps_offset", ctypes.c_uint64),
+                ("n_row_blocks", ctypes.c_uint32), ("n_slices", ctypes.c_uint32),
+                ("slice_w", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
 
 
 _CSR_P = ctypes.POINTER(seacells_csr)
@@ -122,6 +135,15 @@ def load():
     lib.seacells_fw_a_to_csr_fill.restype = ctypes.c_int
     lib.seacells_fw_a_to_csr_fill.argtypes = [_VP, _VP, _VP, _U32, _U32, _U32, _VP, _VP, _VP,
                                               _VP, _VP]
+    lib.seacells_debug_set_a_options.restype = ctypes.c_int
+    lib.seacells_debug_set_a_options.argtypes = [ctypes.POINTER(seacells_a_options)]
+    lib.seacells_debug_b_layout.restype = ctypes.c_int
+    lib.seacells_debug_b_layout.argtypes = [_U32, _U32, _U32, ctypes.POINTER(seacells_b_layout)]
+    lib.seacells_debug_b_last_epoch.restype = ctypes.c_uint32
+    lib.seacells_debug_b_last_epoch.argtypes = []
+    lib.seacells_debug_b_reduce.restype = ctypes.c_int
+    lib.seacells_debug_b_reduce.argtypes = [_U32, _U32, _U32, _U32, _VP, _VP, _VP, _VP,
+                                            ctypes.c_size_t, _VP, _VP]
     lib.seacells_status_string.restype = ctypes.c_char_p
     lib.seacells_status_string.argtypes = [ctypes.c_int]
     lib.seacells_last_error.restype = ctypes.c_char_p
@@ -316,6 +338,49 @@ def seacells_fw_b_apply(bt_idx, bt_val, bt_cnt, n: int, arg_idx, gamma: float, s
                                  _ptr(arg_idx), float(gamma), _ptr(status), _stream(stream))
     _check_rc(rc)
     return bt_idx, bt_val, bt_cnt, status
+
+
+# --------------------------------------------------------------------------
+# test and experiment hooks (include/seacells_debug.h)
+# --------------------------------------------------------------------------
+
+def seacells_debug_set_a_options(support=-1, support_waves=0, dense_argmin=False, group=0):
+    """Plan overrides of the A update (process-wide); no arguments restore
+    the defaults."""
+    opt = seacells_a_options(int(support), int(support_waves), 1 if dense_argmin else 0,
+                             int(group))
+    _check_rc(load().seacells_debug_set_a_options(ctypes.byref(opt)))
+
+
+def seacells_debug_b_layout(n: int, k: int, aat_nnz: int) -> dict:
+    """Where seacells_fw_b_argmin keeps its partial keys and stamps."""
+    out = seacells_b_layout()
+    _check_rc(load().seacells_debug_b_layout(n, k, aat_nnz, ctypes.byref(out)))
+    return {nm: int(getattr(out, nm)) for nm, _ in seacells_b_layout._fields_ if nm != "reserved"}
+
+
+def seacells_debug_b_last_epoch() -> int:
+    return int(load().seacells_debug_b_last_epoch())
+
+
+def seacells_debug_b_reduce(n: int, k: int, aat_nnz: int, epoch: int, workspace, out_val=None,
+                            out_idx=None, gap=None, status=None, stream=None):
+    """The B argmin's reduce stages alone over the partials in ``workspace``.
+    Returns (out_val, out_idx, gap, status)."""
+    dev = workspace.device
+    if out_val is None:
+        out_val = torch.empty(k, dtype=torch.float32, device=dev)
+    if out_idx is None:
+        out_idx = torch.empty(k, dtype=torch.int32, device=dev)
+    if gap is None:
+        gap = torch.empty(1, dtype=torch.float32, device=dev)
+    if status is None:
+        status = new_status(dev)
+    rc = load().seacells_debug_b_reduce(n, k, aat_nnz, int(epoch) & 0xffffffff, _ptr(out_val),
+                                        _ptr(out_idx), _ptr(gap), _ptr(workspace),
+                                        workspace.numel(), _ptr(status), _stream(stream))
+    _check_rc(rc)
+    return out_val, out_idx, gap, status
 
 
 # --------------------------------------------------------------------------

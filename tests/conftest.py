@@ -26,3 +26,32 @@ def _announce_gpu_case(request):
     print("\n[gpu-case] %s" % request.node.nodeid, flush=True)
     sys.stdout.flush()
     yield
+
+
+class _AOptions:
+    """Plan overrides of the A update through the library's debug hook
+    (seacells_debug_set_a_options); merged across calls, reset after the test."""
+
+    def __init__(self):
+        self.cur = {}
+
+    def _apply(self):
+        import sparse_archetypal_analysis_amd as saa
+        saa.seacells_debug_set_a_options(**self.cur)
+
+    def set(self, **kw):
+        self.cur.update(kw)
+        self._apply()
+
+    def clear(self, *names):
+        for nm in names:
+            self.cur.pop(nm, None)
+        self._apply()
+
+
+@pytest.fixture
+def a_options():
+    opts = _AOptions()
+    yield opts
+    opts.cur = {}
+    opts._apply()

@@ -80,3 +80,51 @@ def run_b_dense(k2b, t1, t2, b):
                    a_prev_t=W.dense_to_csr(np.zeros((n, k))), aat=W.dense_to_csr(t1),
                    k2at=W.dense_to_csr(t2), b=W.dense_to_csr(b), init_cells=np.zeros(0, np.int64))
     return w, run_b(w)
+
+
+def run_a_as_timed(w, ops=None, calls=3):
+    """The A update exactly as the benchmark times it: outputs, workspace and
+    status allocated once, no trace, no gap, the call repeated on them.
+    Returns the last call's (atom_idx, atom_val, atom_cnt, flags)."""
+    n, k, T, cap = w.n, w.k, w.T, w.cap
+    t1, k2b, ap = ops if ops is not None else (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
+    ai = torch.empty((n, cap), dtype=torch.int32, device="cuda")
+    av = torch.empty((n, cap), dtype=torch.float32, device="cuda")
+    ac = torch.empty(n, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(saa.seacells_fw_a_columns_workspace(n, k, T, cap, t1.nnz), 1),
+                     dtype=torch.uint8, device="cuda")
+    st = saa.new_status()
+    for _ in range(calls):
+        saa.seacells_fw_a_columns(t1, k2b, ap, n, k, T, cap, atom_idx=ai, atom_val=av,
+                                  atom_cnt=ac, workspace=ws, status=st)
+    torch.cuda.synchronize()
+    return ai.cpu().numpy(), av.cpu().numpy(), ac.cpu().numpy(), saa.status_flags(st)
+
+
+def run_b_as_timed(w, ops=None, calls=3):
+    """The B argmin exactly as the benchmark times it: B given for the gap,
+    no full gap, outputs and workspace allocated once, the call repeated.
+    Returns (out_val, out_idx, gap, flags) of the last call."""
+    k2b, aat, k2at, b = ops if ops is not None else (dev(w.k2b), dev(w.aat), dev(w.k2at),
+                                                     dev(w.b))
+    v = torch.empty(w.k, dtype=torch.float32, device="cuda")
+    i = torch.empty(w.k, dtype=torch.int32, device="cuda")
+    g = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(saa.seacells_fw_b_argmin_workspace(w.n, w.k, aat.nnz), dtype=torch.uint8,
+                     device="cuda")
+    st = saa.new_status()
+    for _ in range(calls):
+        saa.seacells_fw_b_argmin(k2b, aat, k2at, b, w.n, w.k, out_val=v, out_idx=i, gap=g,
+                                 workspace=ws, status=st)
+    torch.cuda.synchronize()
+    return v.cpu().numpy(), i.cpu().numpy(), float(g.cpu().numpy()[0]), saa.status_flags(st)
+
+
+def assert_same_atoms(traced, timed):
+    """The timed call's atoms equal the traced call's bit for bit."""
+    ai0, av0, ac0 = traced[0], traced[1], traced[2]
+    ai1, av1, ac1 = timed[0], timed[1], timed[2]
+    np.testing.assert_array_equal(ac0, ac1)
+    mask = np.arange(ai0.shape[1])[None, :] < ac0[:, None]
+    np.testing.assert_array_equal(ai0[mask], ai1[mask])
+    np.testing.assert_array_equal(av0[mask].view(np.uint32), av1[mask].view(np.uint32))

@@ -17,6 +17,7 @@ from __future__ import annotations
 from dataclasses import dataclass
 
 import numpy as np
+import scipy.sparse as sp
 
 import oracle
 
@@ -201,6 +202,38 @@ def check_b(w, out_val, out_idx, gap, n=None, k=None, b=True, res=None, fw_gap=N
 
 
 # --------------------------------------------------------------------------
+# the B argmin's partials
+# --------------------------------------------------------------------------
+
+NO_VALUE_KEY = (0xff800000 << 32) | 0xffffffff   # (+inf, ~0): a unit that saw no finite value
+
+
+def check_b_partials(keys, stamps, epoch, n, slice_w):
+    """The check the B argmin's reduce makes on its partials, restated on the
+    host. keys [n_row_blocks, k] u64 (value key << 32 | row), stamps
+    [n_row_blocks, n_slices] u32. Every stamp must be this call's epoch, and
+    every key's row must lie in its row range [n rb / NB, n (rb + 1) / NB);
+    a key (+inf, ~0) means the unit saw no finite value. Returns the flags
+    the device raises for these partials ([] when they are valid)."""
+    keys = np.asarray(keys, np.uint64)
+    stamps = np.asarray(stamps, np.uint32)
+    nb, k = keys.shape
+    flags = set()
+    cols_slice = np.arange(k) // slice_w
+    if np.any(stamps[:, cols_slice] != np.uint32(epoch)):
+        flags.add("PARTIALS_INVALID")
+    rows = (keys & np.uint64(0xffffffff)).astype(np.int64)
+    rb = np.arange(nb, dtype=np.int64)[:, None]
+    lo, hi = (n * rb) // nb, (n * (rb + 1)) // nb
+    none = keys == np.uint64(NO_VALUE_KEY)
+    if np.any(none):
+        flags.add("NONFINITE")
+    if np.any(~none & ((rows < lo) | (rows >= hi))):
+        flags.add("PARTIALS_INVALID")
+    return sorted(flags)
+
+
+# --------------------------------------------------------------------------
 # sparse products (device operand construction)
 # --------------------------------------------------------------------------
 
@@ -224,18 +257,36 @@ def check_product(got, want, extra_terms=0, what=""):
     return float((err / np.maximum(want.abs_value, 1e-300)).max()) if err.size else 0.0
 
 
-def check_b_loop(K, b0, aat, k2at, T, res_gpu, gammas=None, own_operands=False):
+def a_change_bound(K, at, used, k2b_used, d_a):
+    """Bound on how far G_t[used[t, c], c] moves when every entry of A
+    (A^T = ``at``, n x k, non-negative) moves by at most d_a, with K, K2B >= 0:
+    d_a (sum_m K2B_t[u, m] (R[m] + R[c]) + (K K 1)[u]), R the row sums of A
+    (first order in d_a). ``k2b_used`` [T, k, k] holds the rows K2B_t[u, :]."""
+    n = K.shape[0]
+    R = np.asarray(at.sum(axis=0), np.float64).ravel()
+    Ks = sp.csr_matrix(K, dtype=np.float64)
+    k2one = np.asarray(Ks @ (Ks @ np.ones(n)), np.float64).ravel()
+    rows = np.abs(k2b_used)
+    return d_a * (np.einsum("tcm,m->tc", rows, R) + rows.sum(axis=2) * R[None, :] + k2one[used])
+
+
+def check_b_loop(K, b0, aat, k2at, T, res_gpu, gammas=None, a_err=None):
     """The device B loop (saa.fw_b_loop's result) against oracle.b_loop
     replaying its picks: every pick the oracle's or within the tie rule, the
     minimum values and gaps under the B argmin's policy, B after the loop
     within 1e-5, K^2 B within 5e-5 relative. Returns (picks that differ,
     worst relative error of K^2 B).
 
-    own_operands: the oracle's A A^T and K^2 A^T are its own (from its f64
-    replay of the A update) while the device's come from its f32 A; that
-    difference reaches G relative to the size of G's terms, not to |G|, so
-    the minimum values also get the tie rule's window, TIE_REL of the term
-    scale."""
+    a_err = (dA, at): the oracle's A A^T and K^2 A^T come from its own f64 A
+    (``at``, n x k, the A^T of its replay of the A update) while the
+    device's come from its f32 A, which differs from it by at most dA per
+    entry. With A >= 0 that moves G[i, c] = sum_m K2B[i, m] AAt[m, c] -
+    K2At[i, c] by at most dA (sum_m K2B[i, m] (R[m] + R[c]) + (K^2 1)[i])
+    (R: row sums of A, i.e. column sums of ``at``; K2B >= 0; the dA^2 terms
+    are below 1e-7 here), which is added to the tolerance of each minimum
+    value at its row. The device's products A A^T and K^2 A^T are also
+    rounded to f32, relative to the size of their terms, so the minimum
+    values then also get the tie rule's window, TIE_REL of G's term scale."""
     from oracle import b_loop as BL
     b_gpu, k2b_gpu, picks, mins, gaps = res_gpu
     picks = picks.cpu().numpy().astype(np.int64)
@@ -243,7 +294,7 @@ def check_b_loop(K, b0, aat, k2at, T, res_gpu, gammas=None, own_operands=False):
     gaps = gaps.cpu().numpy().astype(np.float64)
     n = b0.shape[0]
     assert np.all((picks >= 0) & (picks < n))
-    orc = BL.fw_b_loop(K, b0, aat, k2at, T, gammas=gammas, force=picks)
+    orc = BL.fw_b_loop(K, b0, aat, k2at, T, gammas=gammas, force=picks, keep_rows=a_err is not None)
     exact = picks == orc.pick
     second = np.where(np.isfinite(orc.second), orc.second, 0.0)
     over = (orc.g_used - orc.gmin) > TIE_REL * np.maximum.reduce(
@@ -251,9 +302,16 @@ def check_b_loop(K, b0, aat, k2at, T, res_gpu, gammas=None, own_operands=False):
     assert not np.any(over & ~exact), "pick outside the tie rule at %s" % (
         np.argwhere(over & ~exact)[:3].tolist(),)
     tol = VAL_ABS + VAL_REL * np.abs(orc.g_used)
-    if own_operands:
-        tol = tol + TIE_REL * orc.scale
-    assert np.all(np.abs(mins - orc.g_used) <= tol), float(np.max(np.abs(mins - orc.g_used) - tol))
+    if a_err is not None:
+        d_a, at = a_err
+        tol = tol + a_change_bound(K, at, orc.used, orc.k2b_used, d_a) + TIE_REL * orc.scale
+    bad = np.abs(mins - orc.g_used) > tol
+    if np.any(bad):
+        t, c = np.argwhere(bad)[0]
+        raise AssertionError("step %d column %d: device min %.9g, oracle %.9g, tol %.3g "
+                             "(scale %.3g); %d values out" % (t, c, mins[t, c], orc.g_used[t, c],
+                                                               tol[t, c], orc.scale[t, c],
+                                                               int(bad.sum())))
     for t in range(T):
         assert abs(gaps[t] - orc.gap[t]) <= GAP_REL * max(abs(orc.gap[t]), 1e-4 / GAP_REL), t
     from tests.gpu_run import host

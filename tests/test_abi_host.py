@@ -260,3 +260,39 @@ def test_atoms_to_csr_rejects_bad_arguments_on_host():
     assert lib.seacells_fw_a_to_csr_fill(out, out, out, 10, 5, 4, None, out, out, st, None) == -1
     assert lib.seacells_fw_a_to_csr_fill(out, out, out, 2 ** 31, 5, 4, out, out, out, st,
                                          None) == -4
+
+
+@pytest.mark.parametrize("k", [2048, 2049, 262_144, 262_145, 300_000, 1 << 24, (1 << 31) - 1])
+def test_b_argmin_has_a_plan_for_every_k(k):
+    # no ceiling on k: slices of at most 2048 columns cover every column, and
+    # the partial keys stay within 2 GiB by taking fewer row ranges (one at least)
+    n = 1_000_000
+    lay = saa.seacells_debug_b_layout(n, k, 8 * k)
+    assert 1 <= lay["slice_w"] <= 2048
+    assert lay["n_slices"] * lay["slice_w"] >= k > (lay["n_slices"] - 1) * lay["slice_w"]
+    assert lay["n_row_blocks"] >= 1
+    assert lay["n_row_blocks"] == 1 or lay["n_row_blocks"] * k * 8 <= 1 << 31
+    ws = saa.seacells_fw_b_argmin_workspace(n, k, 8 * k)
+    assert ws >= lay["keys_offset"] + lay["n_row_blocks"] * k * 8
+    assert ws >= lay["stamps_offset"] + lay["n_row_blocks"] * lay["n_slices"] * 4
+
+
+def test_debug_hooks_reject_bad_options():
+    lib = saa.load()
+    bad = native.seacells_a_options(2, 0, 0, 0)
+    assert lib.seacells_debug_set_a_options(ctypes.byref(bad)) == -2
+    bad = native.seacells_a_options(-1, 3, 0, 0)
+    assert lib.seacells_debug_set_a_options(ctypes.byref(bad)) == -2
+    bad = native.seacells_a_options(-1, 0, 0, 48)
+    assert lib.seacells_debug_set_a_options(ctypes.byref(bad)) == -2
+    assert lib.seacells_debug_set_a_options(None) == 0
+    # the overrides reach the workspace query (the support state's queues)
+    base = saa.seacells_fw_a_columns_workspace(1000, 6700, 50, 62, 10)
+    saa.seacells_debug_set_a_options(support=0)
+    try:
+        assert saa.seacells_fw_a_columns_workspace(1000, 6700, 50, 62, 10) < base
+    finally:
+        saa.seacells_debug_set_a_options()
+    assert saa.seacells_fw_a_columns_workspace(1000, 6700, 50, 62, 10) == base
+    assert lib.seacells_debug_b_layout(0, 5, 0, ctypes.byref(native.seacells_b_layout())) == -2
+    assert lib.seacells_debug_b_reduce(10, 5, 0, 1, None, None, None, None, 0, None, None) == -1

@@ -68,14 +68,14 @@ def test_large_configs_sampled_cells(name):
 
 
 @pytest.mark.parametrize("thr", [1e-6, 0.0213])
-def test_support_state_equals_dense_kernel(thr, monkeypatch):
+def test_support_state_equals_dense_kernel(thr, a_options):
     # 1e-6: nothing drops, the support state renormalises every step exactly
     # as the dense kernel does; 0.0213: cells drop atoms and are handed over
     w = W.random_workload(300, 3000, t1_per_row=40, k2b_per_row=60, s_a=6, seed=61)
     ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
-    monkeypatch.setenv("SEACELLS_A_SUPPORT", "0")
+    a_options.set(support=0)
     dense = run_a(w, ops=ops, prune=thr)
-    monkeypatch.setenv("SEACELLS_A_SUPPORT", "1")
+    a_options.set(support=1)
     sup = run_a(w, ops=ops, prune=thr)
     assert dense[4] == [] and sup[4] == []
     np.testing.assert_array_equal(dense[3], sup[3])

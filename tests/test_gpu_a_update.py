@@ -4,7 +4,7 @@ import pytest
 
 import workloads as W
 from tests import parity
-from tests.gpu_run import dev, run_a
+from tests.gpu_run import assert_same_atoms, dev, run_a, run_a_as_timed
 
 pytestmark = pytest.mark.gpu
 
@@ -56,14 +56,23 @@ def test_config_all_cells(name):
     assert rep.near_tie <= 1e-3 * rep.steps
 
 
-def test_c3_full_size_sampled_cells():
+def test_c3_full_size_all_cells():
+    # every one of the 100,000 cells replayed by the oracle (about 12 s of
+    # the f64 oracle on 16 host cores)
     w = W.make("c3")
-    ai, av, ac, tr, flags = run_a(w)
+    ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
+    gaps = []
+    ai, av, ac, tr, flags = run_a(w, ops=ops, gap_out=gaps)
     assert flags == []
-    rng = np.random.default_rng(3)
-    cells = np.unique(np.concatenate([[0, w.n - 1], rng.choice(w.n, size=400, replace=False)]))
-    rep = parity.check_a(w, tr[cells], ai[cells], av[cells], ac[cells], cells)
-    print("\nc3 sampled: %s" % (rep,))
+    cells = np.arange(w.n)
+    rep = parity.check_a(w, tr, ai, av, ac, cells)
+    print("\nc3 all cells: %s" % (rep,))
+    assert rep.near_tie <= 1e-3 * rep.steps
+    # the call the benchmark times (no trace, no gap, outputs and workspace
+    # reused over repeated calls) gives the same atoms bit for bit
+    timed = run_a_as_timed(w, ops=ops)
+    assert timed[3] == []
+    assert_same_atoms((ai, av, ac), timed)
     # properties that hold for every cell at any size
     assert np.all(ac >= np.diff(w.a_prev_t.indptr)) and np.all(ac <= w.cap)
     assert np.all((tr >= 0) & (tr < w.k))
@@ -81,13 +90,13 @@ def test_ragged_signed_operands_dense_path():
 
 
 @pytest.mark.parametrize("support", ["0", "default"])
-def test_large_k_state_in_workspace(support, monkeypatch):
+def test_large_k_state_in_workspace(support, a_options):
     # k * 4 bytes exceeds the 160 KB LDS of a compute unit: the dense state
     # lives in workspace (support "0"); by default the compact state takes
     # the cells, with fewer waves per CU
     import sparse_archetypal_analysis_amd as saa
     if support == "0":
-        monkeypatch.setenv("SEACELLS_A_SUPPORT", "0")
+        a_options.set(support=0)
     w = W.random_workload(37, 45_000, t1_per_row=6, k2b_per_row=20, s_a=5, seed=7, T=30)
     assert saa.seacells_fw_a_columns_workspace(w.n, w.k, 30, w.cap, w.t1.nnz) > 0
     ai, av, ac, tr, flags = run_a(w, T=30)
@@ -156,7 +165,7 @@ def test_deterministic_bitwise():
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "empty"])
-def test_support_argmin_equals_dense_scan(name, monkeypatch):
+def test_support_argmin_equals_dense_scan(name, a_options):
     # On non-negative data the argmin is taken from the minimum over supp(t2)
     # and the touched-column bitmap; it must give the very index a dense scan
     # of the same f32 state gives, at every step of every cell.
@@ -165,9 +174,9 @@ def test_support_argmin_equals_dense_scan(name, monkeypatch):
     else:
         w = W.make(name)
     ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
-    monkeypatch.setenv("SEACELLS_A_DENSE_ARGMIN", "1")
+    a_options.set(dense_argmin=True)
     dense = run_a(w, ops=ops)
-    monkeypatch.delenv("SEACELLS_A_DENSE_ARGMIN")
+    a_options.clear("dense_argmin")
     fast = run_a(w, ops=ops)
     assert dense[4] == [] and fast[4] == []
     assert_same_result(dense, fast)
@@ -191,7 +200,7 @@ def test_large_k_and_large_capacity():
     parity.check_a(w, tr, ai, av, ac, np.arange(w.n), T=140)
 
 
-def test_lane_group_widths_agree_bitwise(monkeypatch):
+def test_lane_group_widths_agree_bitwise(a_options):
     # 16, 32 or 64 lanes per cell only changes which lanes carry a cell; each
     # column sees the same operations in the same order, so the results must
     # be bit-identical (and match the oracle)
@@ -199,10 +208,10 @@ def test_lane_group_widths_agree_bitwise(monkeypatch):
     ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
     res = {}
     for g in ("16", "32", "64"):
-        monkeypatch.setenv("SEACELLS_A_GROUP", g)
+        a_options.set(group=int(g))
         res[g] = run_a(w, ops=ops)
         assert res[g][4] == []
-    monkeypatch.delenv("SEACELLS_A_GROUP")
+    a_options.clear("group")
     assert_same_result(res["16"], res["32"])
     assert_same_result(res["16"], res["64"])
     parity.check_a(w, res["32"][3], res["32"][0], res["32"][1], res["32"][2], np.arange(w.n))
@@ -245,18 +254,18 @@ def _support_case(name):
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "empty", "signed", "long_t1_rows", "long_rows",
                                   "very_long_rows", "fold", "restarts", "bad_gamma",
                                   "cap_overflow"])
-def test_support_state_equals_dense_kernel(name, monkeypatch):
+def test_support_state_equals_dense_kernel(name, a_options):
     # The support state (h kept on supp(t2) only, plus bitmaps) must give the
     # dense kernel's results bit for bit; cells it cannot settle are redone by
     # the dense kernel. Forced on here for every k, with one cell per wave.
     w, kw = _support_case(name)
     ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
-    monkeypatch.setenv("SEACELLS_A_GROUP", "64")
-    monkeypatch.setenv("SEACELLS_A_SUPPORT", "0")
+    a_options.set(group=64)
+    a_options.set(support=0)
     dense = run_a(w, ops=ops, **kw)
-    monkeypatch.setenv("SEACELLS_A_SUPPORT", "1")
+    a_options.set(support=1)
     for waves in ("20", "32"):    # two support capacities
-        monkeypatch.setenv("SEACELLS_A_SUPPORT_WAVES", waves)
+        a_options.set(support_waves=int(waves))
         sup = run_a(w, ops=ops, **kw)
         assert sup[4] == dense[4]
         assert_same_result(dense, sup)
@@ -269,3 +278,22 @@ def test_support_state_is_the_default_for_large_k():
     # the workspace then carries the queue of cells left to the dense kernel
     big = saa.seacells_fw_a_columns_workspace(1000, 6700, 50, 62, 10)
     assert big >= 2 * 1000 * 4 + saa.seacells_fw_a_columns_workspace(1000, 1000, 50, 60, 10)
+
+
+@pytest.mark.parametrize("group", [16, 64])
+def test_nan_state_raises_nonfinite(group, a_options):
+    # A cell whose K2B row holds NaN in every column has no gradient entry
+    # below +inf: the argmin finds no minimum, NONFINITE is raised, and the
+    # other cells (independent) are exactly those of the run without it.
+    import dataclasses
+    a_options.set(group=group)
+    w = W.random_workload(40, 24, t1_per_row=4, k2b_per_row=5, s_a=3, seed=71)
+    k2b = w.k2b.toarray()
+    k2b[7, :] = np.nan
+    bad = dataclasses.replace(w, k2b=W.dense_to_csr(k2b))
+    clean = run_a(w)
+    got = run_a(bad)
+    assert clean[4] == [] and got[4] == ["NONFINITE"]
+    keep = np.arange(w.n) != 7
+    assert_same_result(tuple(x[keep] for x in clean[:4]) + (None,),
+                       tuple(x[keep] for x in got[:4]) + (None,))

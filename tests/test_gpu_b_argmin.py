@@ -158,3 +158,53 @@ def test_b_step_overflow_and_bad_index_flags():
     arg = np.array([4, 4, 4, 4, 50])         # row index out of range
     *_, fl = _apply(bi, bv, bc, n, arg, 0.5)
     assert fl == ["BAD_INDEX"]
+
+
+def test_nonfinite_minimum_raises_flag():
+    import dataclasses
+    w = W.random_workload(300, 40, seed=73)
+    # K2At[i, c] = +inf makes G[i, c] = -inf: a non-finite column minimum
+    k2at = w.k2at.toarray()
+    k2at[17, 5] = np.inf
+    v, i, g, flags = run_b(dataclasses.replace(w, k2at=W.dense_to_csr(k2at)))
+    assert flags == ["NONFINITE"]
+    assert int(i[5]) == 17 and np.isneginf(v[5])
+    # a column that is NaN at every row: no row range sees a finite value
+    k2at = w.k2at.toarray()
+    k2at[:, 9] = np.nan
+    v, i, g, flags = run_b(dataclasses.replace(w, k2at=W.dense_to_csr(k2at)))
+    assert flags == ["NONFINITE"]
+    # the other columns are those of the clean run
+    v0, i0, _, f0 = run_b(w)
+    assert f0 == []
+    cols = np.arange(w.k) != 9
+    np.testing.assert_array_equal(i[cols], i0[cols])
+
+
+def test_large_k_many_slices():
+    # k = 300,000 needs 152 column slices of 1976 columns (the plan has no
+    # slice ceiling); a few hundred rows keep the oracle quick
+    import scipy.sparse as sp
+    rng = np.random.default_rng(79)
+    n, k = 200, 300_000
+
+    def rand(rows, cols, per_row):
+        nnz = rows * per_row
+        r = np.repeat(np.arange(rows), per_row)
+        c = rng.integers(0, cols, size=nnz)
+        m = sp.csr_matrix((rng.uniform(0.05, 1.0, size=nnz), (r, c)), shape=(rows, cols))
+        m.sum_duplicates()
+        return m
+
+    a = rand(k, k, 3)
+    cfg = W.Config("large_k", n, 0, 0, 0, k, 0, 0)
+    w = W.Workload(cfg, 0, t1=W._f32(a, symmetric=True), k2b=W._f32(rand(n, k, 40)),
+                   a_prev_t=W._f32(rand(n, k, 1)), aat=W._f32(a, symmetric=True),
+                   k2at=W._f32(rand(n, k, 30)), b=W._f32(rand(n, k, 2)),
+                   init_cells=np.zeros(0, np.int64))
+    lay = saa.seacells_debug_b_layout(n, k, w.aat.nnz)
+    assert lay["n_slices"] > 128 and lay["slice_w"] <= 2048
+    v, i, g, flags = run_b(w)
+    assert flags == []
+    rep = parity.check_b(w, v, i, g)
+    print("\nk=300000: %s" % (rep,))

@@ -80,8 +80,8 @@ def test_a_gap_without_a_step_table_and_with_folds():
                    fw_gap=gap)
 
 
-def test_a_gap_large_k_state_in_workspace(monkeypatch):
-    monkeypatch.setenv("SEACELLS_A_SUPPORT", "0")
+def test_a_gap_large_k_state_in_workspace(a_options):
+    a_options.set(support=0)
     w = W.random_workload(37, 45_000, t1_per_row=6, k2b_per_row=20, s_a=5, seed=7, T=30)
     (ai, av, ac, tr, _), gap = a_with_gap(w, T=30)
     parity.check_a(w, tr, ai, av, ac, np.arange(w.n), T=30, fw_gap=gap)
@@ -96,28 +96,28 @@ def test_a_gap_large_capacity_atoms_in_lds():
 
 @pytest.mark.parametrize("name", ["c2", "empty", "long_rows", "restarts", "fold"])
 @pytest.mark.parametrize("prune", [None, 1e-6])
-def test_a_gap_support_state_equals_dense_kernel(name, prune, monkeypatch):
+def test_a_gap_support_state_equals_dense_kernel(name, prune, a_options):
     # the compact state computes the gap from the same values in the same
     # order as the dense kernel: equal bit for bit (cells it cannot price go
     # to the dense kernel)
     w, kw = _support_case(name)
     ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
-    monkeypatch.setenv("SEACELLS_A_GROUP", "64")
-    monkeypatch.setenv("SEACELLS_A_SUPPORT", "0")
+    a_options.set(group=64)
+    a_options.set(support=0)
     dense, gd = a_with_gap(w, ops=ops, prune=prune, **kw)
-    monkeypatch.setenv("SEACELLS_A_SUPPORT", "1")
+    a_options.set(support=1)
     sup, gs = a_with_gap(w, ops=ops, prune=prune, **kw)
     np.testing.assert_array_equal(dense[3], sup[3])
     np.testing.assert_array_equal(gd.view(np.uint32), gs.view(np.uint32))
 
 
-def test_a_gap_lane_groups_agree(monkeypatch):
+def test_a_gap_lane_groups_agree(a_options):
     # 16 / 32 / 64 lanes per cell sum <g, a> in different orders: equal to
     # rounding, and each within the oracle's tolerance
     w = W.random_workload(777, 300, t1_per_row=14, k2b_per_row=10, s_a=6, seed=23)
     ops = (dev(w.t1), dev(w.k2b), dev(w.a_prev_t))
     for g in ("16", "32", "64"):
-        monkeypatch.setenv("SEACELLS_A_GROUP", g)
+        a_options.set(group=int(g))
         (ai, av, ac, tr, _), gap = a_with_gap(w, ops=ops)
         parity.check_a(w, tr, ai, av, ac, np.arange(w.n), fw_gap=gap)
 

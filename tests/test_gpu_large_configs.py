@@ -21,7 +21,7 @@ import sparse_archetypal_analysis_amd as saa
 import workloads as W
 from oracle import sparse as S
 from tests import parity
-from tests.gpu_run import dev, host, run_a, run_b
+from tests.gpu_run import assert_same_atoms, dev, host, run_a, run_a_as_timed, run_b, run_b_as_timed
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +43,10 @@ def test_a_update_sampled_cells_and_invariants(big):
     ai, av, ac, tr, flags = run_a(w, ops=ops, gap_out=gaps)
     assert flags == []
     rng = np.random.default_rng(4 if name == "c4" else 5)
-    cells = np.unique(np.concatenate([[0, w.n - 1], rng.choice(w.n, size=160, replace=False)]))
+    # the f64 oracle recomputes every gradient from scratch: ~270 cells/s at
+    # n = 500k, k = 6700 and ~40 cells/s at n = 1M, k = 10000 on 16 cores
+    size = 2000 if name == "c4" else 400
+    cells = np.unique(np.concatenate([[0, w.n - 1], rng.choice(w.n, size=size, replace=False)]))
     rep = parity.check_a(w, tr[cells], ai[cells], av[cells], ac[cells], cells,
                          fw_gap=gaps[0][cells])
     assert not np.any(np.isnan(gaps[0]))
@@ -56,14 +59,19 @@ def test_a_update_sampled_cells_and_invariants(big):
     sums = np.where(slot, av, 0.0).sum(axis=1)
     np.testing.assert_allclose(sums, 1.0, atol=1e-5)
     assert np.all(np.where(slot, av, 0.0) >= 0.0)
+    # the call the benchmark times (no trace, no gap, outputs and workspace
+    # reused over repeated calls) gives the same atoms bit for bit
+    timed = run_a_as_timed(w, ops=ops)
+    assert timed[3] == []
+    assert_same_atoms((ai, av, ac), timed)
 
 
-def test_compact_state_equals_dense_kernel(big, monkeypatch):
+def test_compact_state_equals_dense_kernel(big, a_options):
     # large k takes the compact per-cell state by default; the dense kernel
     # must give the same picks and weights bit for bit on every cell
     name, w, ops = big
     fast = run_a(w, ops=ops)
-    monkeypatch.setenv("SEACELLS_A_SUPPORT", "0")
+    a_options.set(support=0)
     dense = run_a(w, ops=ops)
     assert fast[4] == [] and dense[4] == []
     np.testing.assert_array_equal(fast[3], dense[3])
@@ -76,10 +84,22 @@ def test_compact_state_equals_dense_kernel(big, monkeypatch):
 def test_b_argmin_all_columns(big):
     name, w, _ = big
     gl = []
-    v, i, g, flags = run_b(w, gap_out=gl)
+    ops = (dev(w.k2b), dev(w.aat), dev(w.k2at), dev(w.b))
+    v, i, g, flags = run_b(w, ops=ops, gap_out=gl)
     assert flags == []
     rep = parity.check_b(w, v, i, g, fw_gap=gl[0])
     print("\n%s: %s" % (name, rep))
+    # the call the benchmark times (no full gap, reused workspace and
+    # outputs) and a call without B: the same minima and rows bit for bit
+    tv, ti, tg, tflags = run_b_as_timed(w, ops=ops)
+    assert tflags == []
+    np.testing.assert_array_equal(ti, i)
+    np.testing.assert_array_equal(tv.view(np.uint32), v.view(np.uint32))
+    assert np.float32(tg).view(np.uint32) == np.float32(g).view(np.uint32)
+    nv, ni, _, nflags = run_b(w, ops=ops[:3] + (None,))
+    assert nflags == []
+    np.testing.assert_array_equal(ni, i)
+    np.testing.assert_array_equal(nv.view(np.uint32), v.view(np.uint32))
 
 
 def _place_rows(prod, rows, n):

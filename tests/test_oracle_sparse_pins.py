@@ -391,3 +391,31 @@ def test_atoms_to_csr_equals_dense_scatter():
     assert got.nnz == int(np.count_nonzero(dense_a))
     for j in range(n):
         assert np.all(np.diff(got.indices[got.indptr[j]:got.indptr[j + 1]]) > 0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_b_loop_rows_and_the_a_change_bound(seed):
+    # keep_rows returns the rows of K (K B_t) that G_t was read at; a change
+    # of every A entry by at most d_a moves those G values by at most the
+    # bound the B-loop check adds (brute force on perturbed A)
+    from tests import parity
+    rng = np.random.default_rng(110 + seed)
+    n, k, T = 9, 4, 3
+    K, B, Ad, aat, k2at = loop_problem(rng, n, k)
+    res = BL.fw_b_loop(K, B, aat, k2at, T, keep_rows=True)
+    Kd = K.toarray()
+    Bt = B.toarray()
+    for t in range(T):
+        np.testing.assert_allclose(res.k2b_used[t], (Kd @ Kd @ Bt)[res.used[t]], rtol=0,
+                                   atol=1e-12)
+        Bt = Bt * (1.0 - 2.0 / (t + 2.0))
+        Bt[res.used[t], np.arange(k)] += 2.0 / (t + 2.0)
+    d_a = 1e-3
+    bound = parity.a_change_bound(K, sp.csr_matrix(Ad.T), res.used, res.k2b_used, d_a)
+    worst = 0.0
+    for _ in range(20):
+        A2 = np.clip(Ad + rng.uniform(-d_a, d_a, size=Ad.shape), 0.0, None)
+        rep = BL.fw_b_loop(K, B, sp.csr_matrix(A2 @ A2.T), sp.csr_matrix(Kd @ Kd @ A2.T), T,
+                           force=res.used)
+        worst = max(worst, float(np.max(np.abs(rep.g_used - res.g_used) / bound)))
+    assert worst <= 1.0 + 1e-6

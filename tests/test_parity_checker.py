@@ -108,3 +108,60 @@ def test_b_checker_flags_wrong_row_and_value():
         parity.check_b(w, v, res.row, res.gap, res=res)
     with pytest.raises(AssertionError):
         parity.check_b(w, res.val, res.row, res.gap * 1.01 + 1.0, res=res)
+
+
+# --- the B argmin's partials check, restated on the host -------------------
+
+def _order_key(v):
+    """Order-preserving u32 image of f32 values (-0 folded onto +0)."""
+    u = (np.asarray(v, np.float32) + np.float32(0.0)).view(np.uint32).astype(np.uint64)
+    neg = (u & np.uint64(0x80000000)) != 0
+    return np.where(neg, ~u & np.uint64(0xffffffff), u | np.uint64(0x80000000))
+
+
+@pytest.fixture(scope="module")
+def partials():
+    """Partials as the reduce receives them, built from the oracle on c1:
+    7 row ranges x 3 column slices, one key per (range, column)."""
+    w = W.make("c1")
+    nb, slice_w = 7, 10
+    n_slices = -(-w.k // slice_w)
+    keys = np.zeros((nb, w.k), np.uint64)
+    for rb in range(nb):
+        r0, r1 = w.n * rb // nb, w.n * (rb + 1) // nb
+        res = oracle.fw_b_argmin(w.k2b[r0:r1], w.aat, w.k2at[r0:r1], None, r1 - r0, w.k)
+        keys[rb] = (_order_key(res.val.astype(np.float32)) << np.uint64(32)) | \
+            (res.row.astype(np.uint64) + np.uint64(r0))
+    epoch = 0x5EAC1234
+    stamps = np.full((nb, n_slices), epoch, np.uint32)
+    return w, keys, stamps, epoch, slice_w
+
+
+def test_partials_rule_accepts_valid_partials_and_their_minimum_is_the_argmin(partials):
+    w, keys, stamps, epoch, slice_w = partials
+    assert parity.check_b_partials(keys, stamps, epoch, w.n, slice_w) == []
+    # the u64 minimum over row ranges is (lowest value, then lowest row)
+    best = keys.min(axis=0)
+    full = oracle.fw_b_argmin(w.k2b, w.aat, w.k2at, None, w.n, w.k)
+    np.testing.assert_array_equal((best & np.uint64(0xffffffff)).astype(np.int64), full.row)
+
+
+@pytest.mark.parametrize("fault", ["stale_stamp", "row_past_n", "row_of_another_range",
+                                   "wrong_epoch", "no_value"])
+def test_partials_rule_flags_each_planted_fault(partials, fault):
+    w, keys, stamps, epoch, slice_w = partials
+    keys, stamps = keys.copy(), stamps.copy()
+    want = ["PARTIALS_INVALID"]
+    if fault == "stale_stamp":
+        stamps[3, 1] = epoch - 1
+    elif fault == "row_past_n":
+        keys[2, 5] = (keys[2, 5] & ~np.uint64(0xffffffff)) | np.uint64(w.n + 5)
+    elif fault == "row_of_another_range":
+        r1 = w.n * 3 // 7  # first row of range 3, planted in range 2
+        keys[2, 5] = (keys[2, 5] & ~np.uint64(0xffffffff)) | np.uint64(r1)
+    elif fault == "wrong_epoch":
+        epoch += 1
+    else:
+        keys[4, 0] = np.uint64(parity.NO_VALUE_KEY)
+        want = ["NONFINITE"]
+    assert parity.check_b_partials(keys, stamps, epoch, w.n, slice_w) == want
