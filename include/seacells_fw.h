@@ -175,6 +175,33 @@ int seacells_fw_a_columns_pruned(const seacells_csr *t1, const seacells_csr *k2b
                                  seacells_stream_t stream);
 
 /*
+ * A update that allocates nothing, for callers that cannot call hipMalloc:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. It is seacells_fw_a_columns (same arguments, kernels, outputs
+ * and errors) with the workspace taken from a static device array of
+ * SEACELLS_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends. The caller still provides inputs, outputs and
+ * the status word.
+ *
+ * Returns SEACELLS_E_TOO_LARGE, before anything is enqueued, when
+ * seacells_fw_a_columns_workspace() for these sizes exceeds
+ * SEACELLS_NOALLOC_SCRATCH_BYTES (at n = 1M, k = 10000 it needs about 80
+ * MB). Every call on one GPU shares that GPU's array, and the library
+ * rewrites whatever it reads from it on each call: calls that overlap on one
+ * GPU (other streams, other threads) race and must not be issued. The first
+ * call on a device looks the array's device address up once (a HIP symbol
+ * query; SEACELLS_E_HIP if that fails).
+ */
+#define SEACELLS_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+int seacells_fw_a_columns_noalloc(const seacells_csr *t1, const seacells_csr *k2b,
+                                  const seacells_csr *a_prev_t, uint32_t n, uint32_t k,
+                                  uint32_t T, uint32_t cap, const float *gamma,
+                                  uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
+                                  uint32_t *trace, float *fw_gap, uint32_t *status,
+                                  seacells_stream_t stream);
+
+/*
  * Workspace bytes seacells_fw_b_argmin needs for these sizes (always > 0;
  * aat_nnz: the non-zeros of A A^T). It holds the per-row-range partials
  * (8 bytes per column each; 8192 row ranges for k <= 2048, else 16384, fewer

@@ -6,7 +6,7 @@ include/seacells_debug.h for the test hooks); ``csrc/``
 holds the HIP sources; ``_build`` compiles them in-tree.
 """
 from .native import (DeviceCSR, SeacellsError, load, new_status, raise_on_status,  # noqa: F401
-                     seacells_fw_a_columns, seacells_fw_a_columns_pruned,
+                     seacells_fw_a_columns, seacells_fw_a_columns_pruned, seacells_fw_a_columns_noalloc,
                      seacells_fw_a_columns_workspace,
                      seacells_fw_b_apply, seacells_fw_b_argmin, seacells_fw_b_argmin_workspace,
                      seacells_csr_matmul_workspace, seacells_csr_matmul_pattern_workspace,

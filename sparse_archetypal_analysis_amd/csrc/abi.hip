@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/seacells_debug.h"
 #include "../../include/seacells_fw.h"
@@ -134,6 +135,68 @@ int seacells_fw_a_columns_pruned(const seacells_csr *t1, const seacells_csr *k2b
                                  seacells_stream_t stream) {
   return a_columns(t1, k2b, a_prev_t, n, k, T, cap, gamma, true, threshold, atom_idx, atom_val,
                    atom_cnt, trace, fw_gap, workspace, workspace_bytes, status, stream);
+}
+
+// --- the A update without allocation ---------------------------------------
+
+}  // extern "C"
+
+namespace seacells {
+
+// The workspace of seacells_fw_a_columns_noalloc: one array per device (the
+// code object is loaded on each device the library runs on). In host code
+// `scratch` is a host-side stand-in, not a device address; the address comes
+// from hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[SEACELLS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static void *g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mutex;
+
+static hipError_t scratch_address(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace seacells
+
+extern "C" {
+
+int seacells_fw_a_columns_noalloc(const seacells_csr *t1, const seacells_csr *k2b,
+                                  const seacells_csr *a_prev_t, uint32_t n, uint32_t k,
+                                  uint32_t T, uint32_t cap, const float *gamma,
+                                  uint32_t *atom_idx, float *atom_val, uint32_t *atom_cnt,
+                                  uint32_t *trace, float *fw_gap, uint32_t *status,
+                                  seacells_stream_t stream) {
+  // the sizes are checked on the host before anything else (the argument
+  // checks of a_columns repeat them, and run before any device work)
+  if (t1 == nullptr || k2b == nullptr || a_prev_t == nullptr || atom_idx == nullptr ||
+      atom_val == nullptr || atom_cnt == nullptr || status == nullptr)
+    return SEACELLS_E_NULL;
+  if (n == 0 || k == 0 || T == 0 || cap == 0) return SEACELLS_E_SHAPE;
+  if (n >= 0x80000000u || k >= 0x40000000u || cap >= 0x10000000u) return SEACELLS_E_TOO_LARGE;
+  const size_t need = seacells_fw_a_columns_workspace(n, k, T, cap, t1->nnz);
+  if (need > SEACELLS_NOALLOC_SCRATCH_BYTES) return SEACELLS_E_TOO_LARGE;
+  void *ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return hip_fail(e, "scratch address");
+  }
+  return a_columns(t1, k2b, a_prev_t, n, k, T, cap, gamma, false, 0.0f, atom_idx, atom_val,
+                   atom_cnt, trace, fw_gap, ws, need > 0 ? (size_t)SEACELLS_NOALLOC_SCRATCH_BYTES : 0,
+                   status, stream);
 }
 
 size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k, uint32_t aat_nnz) {

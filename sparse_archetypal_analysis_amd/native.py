@@ -24,7 +24,7 @@ FLAGS = {0x1: "CAP_OVERFLOW", 0x2: "PARTIALS_INVALID", 0x4: "B_CAP_OVERFLOW", 0x
          0x10: "NONFINITE", 0x20: "BAD_GAMMA", 0x40: "OUTPUT_TOO_LARGE"}
 
 EXPORTS = ("seacells_fw_a_columns_workspace", "seacells_fw_a_columns",
-           "seacells_fw_a_columns_pruned",
+           "seacells_fw_a_columns_pruned", "seacells_fw_a_columns_noalloc",
            "seacells_fw_b_argmin_workspace", "seacells_fw_b_argmin", "seacells_fw_b_apply",
            "seacells_csr_matmul_workspace", "seacells_csr_matmul_pattern_workspace",
            "seacells_csr_matmul_rows", "seacells_csr_matmul_fill",
@@ -89,6 +89,9 @@ def load():
     lib.seacells_fw_a_columns_pruned.argtypes = [_CSR_P, _CSR_P, _CSR_P, _U32, _U32, _U32, _U32,
                                                  _VP, ctypes.c_float, _VP, _VP, _VP, _VP, _VP,
                                                  _VP, ctypes.c_size_t, _VP, _VP]
+    lib.seacells_fw_a_columns_noalloc.restype = ctypes.c_int
+    lib.seacells_fw_a_columns_noalloc.argtypes = [_CSR_P, _CSR_P, _CSR_P, _U32, _U32, _U32, _U32,
+                                                  _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]
     lib.seacells_fw_b_argmin_workspace.restype = ctypes.c_size_t
     lib.seacells_fw_b_argmin_workspace.argtypes = [_U32, _U32, _U32]
     lib.seacells_fw_b_argmin.restype = ctypes.c_int
@@ -287,6 +290,39 @@ def _a_columns(threshold, t1, k2b, a_prev_t, n, k, T, cap, gamma, atom_idx, atom
         rc = lib.seacells_fw_a_columns_pruned(ctypes.byref(s1), ctypes.byref(s2),
                                               ctypes.byref(s3), n, k, T, cap, _ptr(gamma),
                                               threshold, *tail)
+    _check_rc(rc)
+    return atom_idx, atom_val, atom_cnt, trace, status
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # SEACELLS_NOALLOC_SCRATCH_BYTES
+
+
+def seacells_fw_a_columns_noalloc(t1: DeviceCSR, k2b: DeviceCSR, a_prev_t: DeviceCSR, n: int,
+                                  k: int, T: int, cap: int, gamma=None, atom_idx=None,
+                                  atom_val=None, atom_cnt=None, trace=None, status=None,
+                                  stream=None, fw_gap=None):
+    """The A update with the library's static scratch as its workspace (the C
+    entry point allocates nothing; outputs given here are used as they are).
+    Returns (atom_idx, atom_val, atom_cnt, trace, status)."""
+    lib = load()
+    dev = t1.row_ptr.device
+    if atom_idx is None:
+        atom_idx = torch.empty((n, cap), dtype=torch.int32, device=dev)
+    if atom_val is None:
+        atom_val = torch.empty((n, cap), dtype=torch.float32, device=dev)
+    if atom_cnt is None:
+        atom_cnt = torch.empty(n, dtype=torch.int32, device=dev)
+    if trace is True:
+        trace = torch.empty((n, T), dtype=torch.int32, device=dev)
+    elif trace is False:
+        trace = None
+    if status is None:
+        status = new_status(dev)
+    s1, s2, s3 = t1.struct(), k2b.struct(), a_prev_t.struct()
+    rc = lib.seacells_fw_a_columns_noalloc(ctypes.byref(s1), ctypes.byref(s2), ctypes.byref(s3),
+                                           n, k, T, cap, _ptr(gamma), _ptr(atom_idx),
+                                           _ptr(atom_val), _ptr(atom_cnt), _ptr(trace),
+                                           _ptr(fw_gap), _ptr(status), _stream(stream))
     _check_rc(rc)
     return atom_idx, atom_val, atom_cnt, trace, status
 
