@@ -206,8 +206,9 @@ int seacells_fw_a_columns_noalloc(const seacells_csr *t1, const seacells_csr *k2
  * aat_nnz: the non-zeros of A A^T). It holds the per-row-range partials
  * (8 bytes per column each; 8192 row ranges for k <= 2048, else 16384, fewer
  * when that would pass 2 GiB, at least one), one stamp and one gap partial
- * per (row range, column slice), the column-slice table (4 (k + 1) bytes per
- * slice when k > 2048), and, when k fits one column slice (k <= 2048), a
+ * per (row range, column slice), when k > 2048 the column-slice tables of
+ * A A^T (4 (k + 1) bytes per slice) and of K2At's rows (4 (n + 1) bytes per
+ * slice), and, when k fits one column slice (k <= 2048), a
  * copy of A A^T with every row padded to whole chunks of 64 entries (at
  * most 8 * (aat_nnz + 64 k) bytes). Depends only on its arguments.
  */

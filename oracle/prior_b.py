@@ -62,9 +62,11 @@ def b_from_padded(idx, val, cnt, n: int) -> sp.csr_matrix:
 
 
 def prior_steps(K: sp.csr_matrix, init, At: sp.csr_matrix, steps: int, n_threads=None,
-                log=None):
+                log=None, checkpoint=None, key=None):
     """s FW steps of the B update from the one-hot start at ``init``.
 
+    ``checkpoint`` (a path): the state after every step is saved there, and a
+    run resumes from it when it holds the state of the same inputs (``key``).
     Returns (B n x k f64 CSR, picks [s, k], min values [s, k], gammas [s])."""
     n, k = K.shape[0], len(init)
     aat = _u32(W._f32(At.T @ At, symmetric=True))
@@ -78,30 +80,54 @@ def prior_steps(K: sp.csr_matrix, init, At: sp.csr_matrix, steps: int, n_threads
     picks = np.zeros((steps, k), np.uint32)
     mins = np.zeros((steps, k), np.float64)
     gammas = np.zeros(steps, np.float64)
+    done = 0
+    if checkpoint is not None and os.path.exists(checkpoint):
+        z = np.load(checkpoint, allow_pickle=False)
+        if str(z["key"]) == key and z["idx"].shape == idx.shape:
+            idx, val, cnt = z["idx"], z["val"], z["cnt"]
+            picks, mins, gammas = z["picks"], z["mins"], z["gammas"]
+            done = int(z["done"])
+            if log is not None:
+                log("[prior_b] resuming after step %d from %s" % (done, checkpoint))
     t0 = time.time()
-    for t in range(1, steps + 1):
+    for t in range(done + 1, steps + 1):
         B = b_from_padded(idx, val, cnt, n)
         k2b = W._f32(W.k2_times(K, B))
         r = oracle.fw_b_argmin(_u32(k2b), aat, k2at, None, n, k, n_threads=n_threads)
         g = 2.0 / (t + 2.0)
         idx, val, cnt = oracle.fw_b_apply(idx, val, cnt, r.row, g)
         picks[t - 1], mins[t - 1], gammas[t - 1] = r.row, r.val, g
+        if checkpoint is not None:
+            tmp = checkpoint + ".tmp.npz"
+            np.savez(tmp, idx=idx, val=val, cnt=cnt, picks=picks, mins=mins, gammas=gammas,
+                     done=np.int64(t), key=np.str_(key))
+            os.replace(tmp, checkpoint)
         if log is not None:
             log("[prior_b] step %d/%d: K2B %d nnz, B %d nnz, %.1f s"
                 % (t, steps, k2b.nnz, int(cnt.sum()), time.time() - t0))
     return b_from_padded(idx, val, cnt, n), picks, mins, gammas
 
 
-def write(name: str, seed: int = 0, n_threads=None, log=print) -> str:
+def write(name: str, seed: int = 0, n_threads=None, log=print, out_dir=None,
+          checkpoint_dir=None) -> str:
+    """Run the prior steps of config ``name`` and store B (under
+    ``workloads/prior_b/``, or ``out_dir``)."""
     cfg = W.CONFIGS[name]
     if cfg.s_b == 0 or cfg.b_init != "fw":
         raise ValueError("config %s has no prior FW steps" % name)
     bs = W.base(cfg, seed, log)
-    B, picks, mins, gammas = prior_steps(bs.K, bs.init, bs.At, cfg.s_b, n_threads, log)
+    sha = bs.sha()
+    ckpt = None
+    if checkpoint_dir is not None:
+        os.makedirs(checkpoint_dir, exist_ok=True)
+        ckpt = os.path.join(checkpoint_dir, "prior_b_%s_s%d.ckpt.npz" % (name, seed))
+    B, picks, mins, gammas = prior_steps(bs.K, bs.init, bs.At, cfg.s_b, n_threads, log,
+                                         checkpoint=ckpt, key=sha["K"] + sha["a_prev_t"])
     bt = sp.csr_matrix(B.T)
     bt.sort_indices()
-    sha = bs.sha()
     path = W.prior_b_path(cfg, seed)
+    if out_dir is not None:
+        path = os.path.join(out_dir, os.path.basename(path))
     os.makedirs(os.path.dirname(path), exist_ok=True)
     tmp = path + ".tmp%d.npz" % os.getpid()
     np.savez_compressed(tmp, bt_ptr=bt.indptr.astype(np.int64), bt_idx=bt.indices.astype(np.int32),
@@ -119,5 +145,13 @@ def write(name: str, seed: int = 0, n_threads=None, log=print) -> str:
 
 
 if __name__ == "__main__":
-    for nm in sys.argv[1:] or ["c2", "c3", "c4", "c5"]:
-        write(nm, log=lambda m: print(m, flush=True))
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("configs", nargs="*", default=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--out-dir", default=None, help="write there instead of workloads/prior_b")
+    ap.add_argument("--checkpoint-dir", default=None,
+                    help="save the state after every step there, and resume from it")
+    a = ap.parse_args()
+    for nm in a.configs:
+        write(nm, log=lambda m: print(m, flush=True), out_dir=a.out_dir,
+              checkpoint_dir=a.checkpoint_dir)

@@ -104,6 +104,41 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// Row-slice table of an n x k operand whose rows are read slice by slice
+// (K2At): rs[i * (n_slices + 1) + s] = first position of row i with column
+// >= s * slice_w, rs[i * (n_slices + 1) + n_slices] = the row's end, so the
+// unit of slice s reads only [rs[.. s], rs[.. s + 1]) of the row. Every
+// entry lies inside its row (a binary search of the row, whatever its
+// order); a malformed row gets an empty run everywhere and raises BAD_INDEX.
+__global__ void __launch_bounds__(256)
+    row_slice_kernel(Csr m, uint32_t n_rows, uint32_t slice_w, uint32_t n_slices,
+                     uint32_t *__restrict__ rs, uint32_t *__restrict__ status) {
+  const uint64_t per = (uint64_t)n_slices + 1;
+  const uint64_t total = (uint64_t)n_rows * per;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  uint32_t flags = 0;
+  for (uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+    const uint32_t i = (uint32_t)(e / per);
+    const uint32_t s = (uint32_t)(e - (uint64_t)i * per);
+    uint32_t lo, hi;
+    if (!row_ok(m, i, lo, hi)) flags |= kFlagBadIndex;
+    if (s == n_slices) {
+      rs[e] = hi;
+      continue;
+    }
+    const uint32_t target = s * slice_w;
+    while (lo < hi) {  // first position with column >= target
+      const uint32_t mid = lo + (hi - lo) / 2;
+      if (m.idx[mid] < target)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    rs[e] = lo;
+  }
+  if (flags != 0) atomicOr(status, flags);
+}
+
 // ---------------------------------------------------------------------------
 // Padded copy of AAt per slice. The run of AAt row m inside slice s (all of
 // the row with one slice) takes ceil(len / ch) chunks of ch entries
@@ -221,7 +256,8 @@ __global__ void __launch_bounds__(kBThreads)
     fw_b_partials_kernel(Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n, uint32_t k,
                          uint32_t slice_w, uint32_t n_slices, uint32_t n_row_blocks,
                          const uint32_t *__restrict__ seg, const uint32_t *__restrict__ pa_seg,
-                         const uint2 *__restrict__ pa_ent, uint64_t *__restrict__ part_key,
+                         const uint2 *__restrict__ pa_ent, const uint32_t *__restrict__ k2at_rs,
+                         uint64_t *__restrict__ part_key,
                          float *__restrict__ part_gap, uint32_t *__restrict__ stamps,
                          uint32_t *__restrict__ xcd_work, uint32_t epoch,
                          uint32_t *__restrict__ status) {
@@ -414,9 +450,17 @@ __global__ void __launch_bounds__(kBThreads)
           }
         }
       }
-      // -- acc[c] -= K2At[i, c]
+      // -- acc[c] -= K2At[i, c] (with several slices, only this slice's run
+      // of the row, from the row-slice table)
       uint32_t q0, q1;
-      if (!row_ok(k2at, i, q0, q1)) flags |= kFlagBadIndex;
+      if (k2at_rs != nullptr) {
+        const size_t r = (size_t)i * (n_slices + 1) + sl;
+        q0 = k2at_rs[r];
+        q1 = k2at_rs[r + 1];
+        if (q1 < q0) q1 = q0;
+      } else if (!row_ok(k2at, i, q0, q1)) {
+        flags |= kFlagBadIndex;
+      }
       for (uint32_t q = q0 + lane; q < q1; q += kWave) {
         const uint32_t c = k2at.idx[q] - c0;
         if (c < cw) lds_add(acc + c, -k2at.val[q]);
@@ -631,7 +675,7 @@ __global__ void zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
 template <uint32_t S4, bool kDual>
 hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
                            uint32_t k, const uint32_t *seg, const uint32_t *pa_seg,
-                           const uint2 *pa_ent, uint64_t *keys,
+                           const uint2 *pa_ent, const uint32_t *k2at_rs, uint64_t *keys,
                            float *gap_part, uint32_t *stamps, uint32_t *xcd_work, uint32_t epoch,
                            uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
@@ -668,7 +712,7 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // the same number of blocks on every XCD
   hipLaunchKernelGGL(deep ? k_deep : k_std, dim3((uint32_t)blocks), dim3(kBThreads), lds,
                      stream, k2b, aat, k2at, b, n, k, p.slice_w, p.n_slices, p.n_row_blocks, seg,
-                     pa_seg, pa_ent, keys, gap_part, stamps, xcd_work, epoch, status);
+                     pa_seg, pa_ent, k2at_rs, keys, gap_part, stamps, xcd_work, epoch, status);
   return hipGetLastError();
 }
 
@@ -720,6 +764,8 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices, uint64_
   off = align_up(off + kXcds * sizeof(uint32_t), 256);
   p.off_seg = off;
   if (p.n_slices > 1) off = align_up(off + (size_t)k * (p.n_slices + 1) * sizeof(uint32_t), 256);
+  p.off_rs = off;
+  if (p.n_slices > 1) off = align_up(off + (size_t)n * (p.n_slices + 1) * sizeof(uint32_t), 256);
   // narrow slices gather two short AAt runs per wave instruction, reading
   // AAt with 32-bit byte offsets; otherwise the padded AAt copy: a run of
   // len entries takes ceil(len / 64) chunks, at most nnz / 64 + 1 per (row,
@@ -756,7 +802,15 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
   uint32_t *pa_seg = reinterpret_cast<uint32_t *>(base + p.off_pa_seg);
   uint2 *pa_ent = reinterpret_cast<uint2 *>(base + p.off_pa_ent);
   uint32_t *xcd_work = reinterpret_cast<uint32_t *>(base + p.off_work);
+  uint32_t *k2at_rs = p.n_slices > 1 ? reinterpret_cast<uint32_t *>(base + p.off_rs) : nullptr;
   hipError_t e;
+  if (k2at_rs != nullptr) {
+    const uint64_t total = (uint64_t)n * (p.n_slices + 1);
+    const uint64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(row_slice_kernel, dim3((uint32_t)(blocks < 65536u ? blocks : 65536u)),
+                       dim3(256), 0, stream, k2at, n, p.slice_w, p.n_slices, k2at_rs, status);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (seg != nullptr) {
     const uint64_t total = (uint64_t)k * (p.n_slices + 1);
     const uint64_t blocks = (total + 255) / 256;
@@ -783,10 +837,12 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
   switch (p.s4) {
 #define SEACELLS_B_CASE(S)                                                                      \
   case S:                                                                                       \
-    e = dual ? launch_partials<S, true>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent, keys,  \
-                                        gap_part, stamps, xcd_work, epoch, status, stream)      \
-             : launch_partials<S, false>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent, keys, \
-                                         gap_part, stamps, xcd_work, epoch, status, stream);    \
+    e = dual ? launch_partials<S, true>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent,       \
+                                        k2at_rs, keys, gap_part, stamps, xcd_work, epoch,       \
+                                        status, stream)                                         \
+             : launch_partials<S, false>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent,      \
+                                         k2at_rs, keys, gap_part, stamps, xcd_work, epoch,      \
+                                         status, stream);                                       \
     break;
     SEACELLS_B_CASE(1)
     SEACELLS_B_CASE(2)
