@@ -321,7 +321,8 @@ def copy_calibration(mib):
 # --------------------------------------------------------------------------
 
 A_KERNELS = ("fw_a_", "pad_rows_kernel", "pad_fill_kernel")
-B_KERNELS = ("seg_table_kernel", "pa_seg_kernel", "pa_fill_kernel", "fw_b_partials_kernel",
+B_KERNELS = ("seg_table_kernel", "row_slice_kernel", "pa_seg_kernel", "pa_fill_kernel",
+             "fw_b_partials_kernel",
              "fw_b_reduce1_kernel", "fw_b_reduce2_kernel", "fw_b_fw_gap_kernel")
 
 

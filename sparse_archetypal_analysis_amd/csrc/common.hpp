@@ -142,6 +142,7 @@ struct APlan {
   uint32_t nwords;             // 32-column words of the bitmaps
   size_t ws_list_off;          // cells for the long-row pass (counters sit at offset 0)
   size_t ws_list2_off;         // cells for the dense kernel
+  size_t ws_keys_off, ws_hist_off, ws_order_off;  // the cells' locality order (support only)
   size_t ws_dense_off;         // dense state slices
   // one cell per wave: t1 copied with every row padded to whole chunks of 64
   // (column byte offset, value) pairs, so a step reads rows without checks

@@ -1081,15 +1081,94 @@ __global__ void __launch_bounds__(256)
 // positive minimum, or an invalid step size.
 // Work lists of one support pass (device pointers into the workspace).
 struct SupQueues {
-  const uint32_t *in_list;  // cells to take, or nullptr for 0 .. n-1
+  const uint32_t *in_list;  // cells to take, or nullptr for 0 .. n-1 (or `order`)
   const uint32_t *in_cnt;   // entries of in_list
   uint32_t *work;           // next entry to take (starts at 0)
+  // without in_list: the cells in a locality order, dealt to the XCDs in
+  // contiguous segments (xcd_work: one counter per segment), or nullptr
+  const uint32_t *order;
+  uint32_t *xcd_work;
   uint32_t *long_list;      // cells whose K2B row exceeds hc_cap, or nullptr: to dense_list
   uint32_t *long_cnt;
   uint32_t *dense_list;     // cells for the dense kernel
   uint32_t *dense_cnt;
 };
 
+
+constexpr uint32_t kAXcds = 8;  // MI355X: 8 XCDs, each with its own L2
+
+// Locality order of the cells for the support pass: cells sorted (counting
+// sort) by the column of the largest entry of their K2B row (the lowest
+// such column on a tie), i.e. the archetype with the most B mass within two
+// kernel hops: cells with the same key lie close together and pick
+// overlapping atoms. Only the order in which cells are processed changes:
+// every cell's outputs are the same whatever the order. One wave per cell.
+__global__ void __launch_bounds__(256)
+    cell_key_kernel(const uint32_t *__restrict__ k2b_ptr, const uint32_t *__restrict__ k2b_idx,
+                    const float *__restrict__ k2b_val, uint32_t k2b_nnz, uint32_t n, uint32_t k,
+                    uint32_t *__restrict__ keys, uint32_t *__restrict__ hist) {
+  const uint32_t lane = lane_id();
+  const uint32_t wpb = blockDim.x / kWave;
+  const uint32_t nw = gridDim.x * wpb;
+  for (uint32_t c = blockIdx.x * wpb + threadIdx.x / kWave; c < n; c += nw) {
+    const uint32_t lo = k2b_ptr[c], hi = k2b_ptr[c + 1];
+    uint32_t key = k;  // empty or malformed rows go last
+    if (lo < hi && hi <= k2b_nnz) {
+      uint32_t bk = 0xffffffffu, bc = 0xffffffffu;  // ~order(value), column
+      for (uint32_t p = lo + lane; p < hi; p += kWave) {
+        const uint32_t kv = ~f32_order(k2b_val[p]);  // larger value, smaller key
+        const uint32_t col = k2b_idx[p];
+        if (kv < bk || (kv == bk && col < bc)) bk = kv, bc = col;
+      }
+      const uint32_t best = wave_min_u32(bk);
+      const uint32_t col = wave_min_u32(bk == best ? bc : 0xffffffffu);
+      if (col < k) key = col;
+    }
+    if (lane == 0) {
+      keys[c] = key;
+      atomicAdd(hist + key, 1u);
+    }
+  }
+}
+
+// One block: exclusive prefix sum of the k + 1 bucket counts, in place.
+__global__ void __launch_bounds__(1024) key_scan_kernel(uint32_t *__restrict__ hist, uint32_t m) {
+  __shared__ uint32_t part[1024];
+  const uint32_t tid = threadIdx.x;
+  const uint32_t per = (m + 1023) / 1024;
+  const uint32_t e0 = tid * per < m ? tid * per : m;
+  const uint32_t e1 = e0 + per < m ? e0 + per : m;
+  uint32_t sum = 0;
+  for (uint32_t e = e0; e < e1; ++e) sum += hist[e];
+  part[tid] = sum;
+  __syncthreads();
+  for (uint32_t off = 1; off < 1024; off <<= 1) {
+    const uint32_t v = tid >= off ? part[tid - off] : 0u;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  uint32_t at = part[tid] - sum;
+  for (uint32_t e = e0; e < e1; ++e) {
+    const uint32_t c = hist[e];
+    hist[e] = at;
+    at += c;
+  }
+}
+
+// order[pos] = cell, pos taken from the cell's bucket (any order inside it)
+__global__ void __launch_bounds__(256)
+    cell_scatter_kernel(const uint32_t *__restrict__ keys, uint32_t n,
+                        uint32_t *__restrict__ offs, uint32_t *__restrict__ order) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t c = blockIdx.x * blockDim.x + threadIdx.x; c < n; c += stride)
+    order[atomicAdd(offs + keys[c], 1u)] = c;
+}
+
+__global__ void __launch_bounds__(256) fill_u32_kernel(uint32_t *__restrict__ p, uint32_t m) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < m; i += stride) p[i] = 0u;
+}
 
 constexpr uint32_t kTailPos = 0x80000000u;  // marks a t2 position (not a column) in the pass
 constexpr uint32_t kRowBatch = 4;   // chunks of a t1 row whose loads are in flight together
@@ -1214,14 +1293,44 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
     const uint32_t c = *q.in_cnt;
     ncells = c < n ? c : n;
   }
+  // With a locality order, the XCD this block runs on (blocks are dealt to
+  // the XCDs round-robin) takes its own segment of the order first, so the
+  // cells in flight on one XCD are neighbours and share the t1 rows of
+  // their atoms in that XCD's L2; then it helps with the other segments.
+  // (On another placement only the speed changes.)
+  const bool by_order = q.in_list == nullptr && q.order != nullptr;
+  uint32_t seg = blockIdx.x % kAXcds, segs_left = kAXcds;
   for (;;) {
     // cells are taken one at a time from a counter: no block waits for a
     // slot while others idle, and expensive cells spread by themselves
-    uint32_t slot = 0;
-    if (lane == 0) slot = atomicAdd(q.work, 1u);
-    slot = __builtin_amdgcn_readfirstlane(slot);
-    if (slot >= ncells) break;
-    const uint32_t cell = q.in_list != nullptr ? q.in_list[slot] : slot;
+    uint32_t cell;
+    if (by_order) {
+      cell = kNone;
+      while (segs_left > 0) {
+        const uint32_t lo = (uint32_t)(((uint64_t)n * seg) / kAXcds);
+        const uint32_t hi = (uint32_t)(((uint64_t)n * (seg + 1)) / kAXcds);
+        uint32_t s = 0;
+        if (lane == 0) s = atomicAdd(q.xcd_work + seg, 1u);
+        s = __builtin_amdgcn_readfirstlane(s);
+        if (s < hi - lo) {
+          cell = q.order[lo + s];
+          break;
+        }
+        seg = (seg + 1) % kAXcds;
+        --segs_left;
+      }
+      if (cell == kNone) break;
+    } else {
+      uint32_t slot = 0;
+      if (lane == 0) slot = atomicAdd(q.work, 1u);
+      slot = __builtin_amdgcn_readfirstlane(slot);
+      if (slot >= ncells) break;
+      cell = q.in_list != nullptr ? q.in_list[slot] : slot;
+    }
+    if (cell >= n) {  // a locality order that does not hold cell ids
+      flags |= kFlagBadIndex;
+      continue;
+    }
     wave_lds_sync();
     const uint32_t q0 = k2b_ptr[cell], q1 = k2b_ptr[cell + 1];
     const uint32_t s0 = ap_ptr[cell], s1 = ap_ptr[cell + 1];
@@ -1794,14 +1903,18 @@ APlan plan_a(uint32_t n, uint32_t k, uint32_t T, uint32_t cap, bool prune, uint3
     uint32_t hc, lpw;
     if (support_tier_size(p, kSupWavesPerBlock, hc, lpw)) p.support = true;
   }
-  // workspace: [counters | long-row queue | dense queue | padded t1 | dense state slices]
+  // workspace: [counters | long-row queue | dense queue | locality order:
+  // keys, bucket offsets, order | padded t1 | dense state slices]
   size_t off = 0;
   if (p.support) {
     p.ws_list_off = 256;
     p.ws_list2_off = align_up(p.ws_list_off + (size_t)n * 4, 256);
-    off = p.ws_list2_off + (size_t)n * 4;
+    p.ws_keys_off = align_up(p.ws_list2_off + (size_t)n * 4, 256);
+    p.ws_hist_off = align_up(p.ws_keys_off + (size_t)n * 4, 256);
+    p.ws_order_off = align_up(p.ws_hist_off + ((size_t)k + 1) * 4, 256);
+    off = p.ws_order_off + (size_t)n * 4;
   } else {
-    p.ws_list_off = p.ws_list2_off = 0;
+    p.ws_list_off = p.ws_list2_off = p.ws_keys_off = p.ws_hist_off = p.ws_order_off = 0;
   }
   // the one-cell-per-wave kernel reads t1 from a padded copy: a row of len
   // entries takes ceil(len / 64) chunks, at most nnz / 64 + k in all
@@ -1846,20 +1959,39 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
     uint32_t *ctr = reinterpret_cast<uint32_t *>(w8);  // work0, work1, long, dense
     uint32_t *long_list = reinterpret_cast<uint32_t *>(w8 + plan.ws_list_off);
     uint32_t *dense_list = reinterpret_cast<uint32_t *>(w8 + plan.ws_list2_off);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, ctr, 4u);
+    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, ctr, 16u);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // the locality order of the cells (counters 8 .. 15: one per XCD segment)
+    uint32_t *keys = reinterpret_cast<uint32_t *>(w8 + plan.ws_keys_off);
+    uint32_t *hist = reinterpret_cast<uint32_t *>(w8 + plan.ws_hist_off);
+    uint32_t *order = reinterpret_cast<uint32_t *>(w8 + plan.ws_order_off);
+    const uint32_t nb = (uint32_t)(((uint64_t)n + 255) / 256 < 4096 ? ((uint64_t)n + 255) / 256
+                                                                     : 4096);
+    const uint32_t hb = (uint32_t)(((uint64_t)k + 256) / 256 < 4096 ? ((uint64_t)k + 256) / 256
+                                                                     : 4096);
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(hb), dim3(256), 0, stream, hist, k + 1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const uint32_t kb = (uint32_t)(((uint64_t)n + 3) / 4 < 16384 ? ((uint64_t)n + 3) / 4 : 16384);
+    hipLaunchKernelGGL(cell_key_kernel, dim3(kb), dim3(256), 0, stream, k2b.ptr, k2b.idx, k2b.val,
+                       k2b.nnz, n, k, keys, hist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(key_scan_kernel, dim3(1), dim3(1024), 0, stream, hist, k + 1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(cell_scatter_kernel, dim3(nb), dim3(256), 0, stream, keys, n, hist, order);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // a second pass when it holds longer K2B rows than the first
     const bool wide0 = k2b.nnz > (uint64_t)n * 192u;
     uint32_t hc0 = 0, hc1 = 0, lpw_unused;
     support_tier_size(plan, first_pass_waves(plan, wide0), hc0, lpw_unused);
     const bool two = support_tier_size(plan, kSupLongWaves, hc1, lpw_unused) && hc1 > hc0;
-    SupQueues q0{nullptr, nullptr, ctr + 0, two ? long_list : nullptr, ctr + 2, dense_list,
-                 ctr + 3};
+    SupQueues q0{nullptr, nullptr, ctr + 0, order, ctr + 8, two ? long_list : nullptr, ctr + 2,
+                 dense_list, ctr + 3};
     e = launch_support(plan, dev, 0, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
                        atom_cnt, trace, fw_gap, q0, prune_thr, status, stream);
     if (e != hipSuccess) return e;
     if (two) {
-      SupQueues q1{long_list, ctr + 2, ctr + 1, nullptr, nullptr, dense_list, ctr + 3};
+      SupQueues q1{long_list, ctr + 2, ctr + 1, nullptr, nullptr, nullptr, nullptr, dense_list,
+                   ctr + 3};
       e = launch_support(plan, dev, 1, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
                          atom_cnt, trace, fw_gap, q1, prune_thr, status, stream);
       if (e != hipSuccess) return e;

@@ -392,18 +392,22 @@ __global__ void __launch_bounds__(kBThreads)
               if (pa < phi[g]) ca[g] = load_at(aat.idx, pa * 4u), va[g] = load_at(aat.val, pa * 4u);
               if (pb < phi[g]) cb[g] = load_at(aat.idx, pb * 4u), vb[g] = load_at(aat.val, pb * 4u);
             }
-            // columns outside the slice (none for sorted rows; lanes without
-            // an entry) go to this lane's dummy slot past the accumulator
+            // lanes without an entry go to this lane's dummy slot past the
+            // accumulator (their column is kNoCol; a column of a malformed
+            // row past the slice lands in the accumulator's padding or the
+            // dummy, both cleared or never read). The two entries of a lane
+            // belong to one run, so their columns differ: both old values are
+            // read before either is written (one LDS round trip per run; the
+            // dummy only ever takes + 0). Runs follow each other in K2B order.
 #pragma unroll
             for (uint32_t g = 0; g < kPairs; ++g) {
-              const uint32_t c_a = ca[g] - c0, c_b = cb[g] - c0;
-              float *qa = acc_h + (c_a < cw ? c_a : W + hl);
-              float *qb = acc_h + (c_b < cw ? c_b : W + hl);
-              *qa = __builtin_fmaf(xs[g], va[g], *qa);
-              *qb = __builtin_fmaf(xs[g], vb[g], *qb);
+              float *qa = acc_h + min(ca[g] - c0, W + hl);
+              float *qb = acc_h + min(cb[g] - c0, W + hl);
+              const float oa = *qa, ob = *qb;
+              *qa = __builtin_fmaf(xs[g], va[g], oa);
+              *qb = __builtin_fmaf(xs[g], vb[g], ob);
               for (uint32_t p = plo[g] + 64 + hl; p < phi[g]; p += 32) {
-                const uint32_t c = load_at(aat.idx, p * 4u) - c0;
-                float *q = acc_h + (c < cw ? c : W + hl);
+                float *q = acc_h + min(load_at(aat.idx, p * 4u) - c0, W + hl);
                 *q = __builtin_fmaf(xs[g], load_at(aat.val, p * 4u), *q);
               }
             }
@@ -430,18 +434,20 @@ __global__ void __launch_bounds__(kBThreads)
             if (gn[g] > 1) eb[g] = load_at(pa_ent + (size_t)(gq[g] + 1) * kWave, lane * 8u);
             if (gn[g] > 2) ec[g] = load_at(pa_ent + (size_t)(gq[g] + 2) * kWave, lane * 8u);
           }
+          // the three chunks of one run hold distinct columns (padding lanes
+          // point at their own dummy slot and add 0): their old values are
+          // read together, then written (one LDS round trip per run)
 #pragma unroll
           for (uint32_t g = 0; g < kGatherRows; ++g) {
             float *q = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + ea[g].x);
-            *q = __builtin_fmaf(xs[g], __uint_as_float(ea[g].y), *q);
-            if (gn[g] > 1) {
-              float *qb = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + eb[g].x);
-              *qb = __builtin_fmaf(xs[g], __uint_as_float(eb[g].y), *qb);
-            }
-            if (gn[g] > 2) {
-              float *qc = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + ec[g].x);
-              *qc = __builtin_fmaf(xs[g], __uint_as_float(ec[g].y), *qc);
-            }
+            float *qb = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + eb[g].x);
+            float *qc = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + ec[g].x);
+            const float oa = *q;
+            const float ob = gn[g] > 1 ? *qb : 0.0f;
+            const float oc = gn[g] > 2 ? *qc : 0.0f;
+            *q = __builtin_fmaf(xs[g], __uint_as_float(ea[g].y), oa);
+            if (gn[g] > 1) *qb = __builtin_fmaf(xs[g], __uint_as_float(eb[g].y), ob);
+            if (gn[g] > 2) *qc = __builtin_fmaf(xs[g], __uint_as_float(ec[g].y), oc);
             for (uint32_t j = 3; j < gn[g]; ++j) {
               const uint2 eg = load_at(pa_ent + (size_t)(gq[g] + j) * kWave, lane * 8u);
               float *qj = reinterpret_cast<float *>(reinterpret_cast<char *>(acc) + eg.x);
