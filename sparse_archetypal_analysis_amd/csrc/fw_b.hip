@@ -104,6 +104,19 @@ __global__ void __launch_bounds__(256)
   }
 }
 
+// AAt's columns within their slice as 16-bit words for the narrow-slice
+// gather (slices are at most 2048 columns wide): lcol[e] = column of entry e
+// mod slice_w, 2 bytes per entry instead of 4. A column >= k becomes 0xffff
+// (the gather sends it to the lane's dummy slot).
+__global__ void __launch_bounds__(256)
+    aat_local_cols_kernel(Csr aat, uint32_t k, uint32_t slice_w, uint16_t *__restrict__ lcol) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < aat.nnz; e += stride) {
+    const uint32_t c = aat.idx[e];
+    lcol[e] = (uint16_t)(c < k ? c % slice_w : 0xffffu);
+  }
+}
+
 // Row-slice table of an n x k operand whose rows are read slice by slice
 // (K2At): rs[i * (n_slices + 1) + s] = first position of row i with column
 // >= s * slice_w, rs[i * (n_slices + 1) + n_slices] = the row's end, so the
@@ -256,8 +269,8 @@ __global__ void __launch_bounds__(kBThreads)
     fw_b_partials_kernel(Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n, uint32_t k,
                          uint32_t slice_w, uint32_t n_slices, uint32_t n_row_blocks,
                          const uint32_t *__restrict__ seg, const uint32_t *__restrict__ pa_seg,
-                         const uint2 *__restrict__ pa_ent, const uint32_t *__restrict__ k2at_rs,
-                         uint64_t *__restrict__ part_key,
+                         const uint2 *__restrict__ pa_ent, const uint16_t *__restrict__ aat_lcol,
+                         const uint32_t *__restrict__ k2at_rs, uint64_t *__restrict__ part_key,
                          float *__restrict__ part_gap, uint32_t *__restrict__ stamps,
                          uint32_t *__restrict__ xcd_work, uint32_t epoch,
                          uint32_t *__restrict__ status) {
@@ -389,25 +402,25 @@ __global__ void __launch_bounds__(kBThreads)
               xs[g] = __uint_as_float(t.z);
               const uint32_t pa = plo[g] + hl, pb = pa + 32;
               ca[g] = kNoCol, va[g] = 0.0f, cb[g] = kNoCol, vb[g] = 0.0f;
-              if (pa < phi[g]) ca[g] = load_at(aat.idx, pa * 4u), va[g] = load_at(aat.val, pa * 4u);
-              if (pb < phi[g]) cb[g] = load_at(aat.idx, pb * 4u), vb[g] = load_at(aat.val, pb * 4u);
+              if (pa < phi[g]) ca[g] = load_at(aat_lcol, pa * 2u), va[g] = load_at(aat.val, pa * 4u);
+              if (pb < phi[g]) cb[g] = load_at(aat_lcol, pb * 2u), vb[g] = load_at(aat.val, pb * 4u);
             }
             // lanes without an entry go to this lane's dummy slot past the
-            // accumulator (their column is kNoCol; a column of a malformed
-            // row past the slice lands in the accumulator's padding or the
-            // dummy, both cleared or never read). The two entries of a lane
+            // accumulator (their column is kNoCol; columns are slice-local, so
+            // even a malformed row stays inside the accumulator, whose padding
+            // is cleared with it and never read). The two entries of a lane
             // belong to one run, so their columns differ: both old values are
             // read before either is written (one LDS round trip per run; the
             // dummy only ever takes + 0). Runs follow each other in K2B order.
 #pragma unroll
             for (uint32_t g = 0; g < kPairs; ++g) {
-              float *qa = acc_h + min(ca[g] - c0, W + hl);
-              float *qb = acc_h + min(cb[g] - c0, W + hl);
+              float *qa = acc_h + min(ca[g], W + hl);
+              float *qb = acc_h + min(cb[g], W + hl);
               const float oa = *qa, ob = *qb;
               *qa = __builtin_fmaf(xs[g], va[g], oa);
               *qb = __builtin_fmaf(xs[g], vb[g], ob);
               for (uint32_t p = plo[g] + 64 + hl; p < phi[g]; p += 32) {
-                float *q = acc_h + min(load_at(aat.idx, p * 4u) - c0, W + hl);
+                float *q = acc_h + min((uint32_t)load_at(aat_lcol, p * 2u), W + hl);
                 *q = __builtin_fmaf(xs[g], load_at(aat.val, p * 4u), *q);
               }
             }
@@ -681,7 +694,8 @@ __global__ void zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
 template <uint32_t S4, bool kDual>
 hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
                            uint32_t k, const uint32_t *seg, const uint32_t *pa_seg,
-                           const uint2 *pa_ent, const uint32_t *k2at_rs, uint64_t *keys,
+                           const uint2 *pa_ent, const uint16_t *aat_lcol, const uint32_t *k2at_rs,
+                           uint64_t *keys,
                            float *gap_part, uint32_t *stamps, uint32_t *xcd_work, uint32_t epoch,
                            uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
@@ -718,7 +732,8 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // the same number of blocks on every XCD
   hipLaunchKernelGGL(deep ? k_deep : k_std, dim3((uint32_t)blocks), dim3(kBThreads), lds,
                      stream, k2b, aat, k2at, b, n, k, p.slice_w, p.n_slices, p.n_row_blocks, seg,
-                     pa_seg, pa_ent, k2at_rs, keys, gap_part, stamps, xcd_work, epoch, status);
+                     pa_seg, pa_ent, aat_lcol, k2at_rs, keys, gap_part, stamps, xcd_work, epoch,
+                     status);
   return hipGetLastError();
 }
 
@@ -783,6 +798,8 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices, uint64_
   if (!p.dual) off = align_up(off + ((size_t)k * p.n_slices + 1) * sizeof(uint32_t), 256);
   p.off_pa_ent = off;
   off = align_up(off + (size_t)p.pa_chunks * p.pa_ch * sizeof(uint2), 256);
+  p.off_lcol = off;
+  if (p.dual) off = align_up(off + (size_t)aat_nnz * sizeof(uint16_t), 256);
   p.ws_bytes = off;
   return p;
 }
@@ -824,9 +841,16 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
                        dim3(256), 0, stream, aat, k, p.slice_w, p.n_slices, seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // the padded AAt copy (unless narrow slices gather two runs per wave
-  // instruction from AAt itself), then the partials
+  // the padded AAt copy (or, for narrow slices that gather two runs per wave
+  // instruction, AAt's slice-local columns as 16-bit words), then the partials
   const bool dual = p.dual;
+  uint16_t *aat_lcol = dual ? reinterpret_cast<uint16_t *>(base + p.off_lcol) : nullptr;
+  if (dual && aat.nnz > 0) {
+    const uint32_t blocks = (aat.nnz + 255) / 256;
+    hipLaunchKernelGGL(aat_local_cols_kernel, dim3(blocks < 65536u ? blocks : 65536u), dim3(256),
+                       0, stream, aat, k, p.slice_w, aat_lcol);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (!dual) {
     hipLaunchKernelGGL(pa_seg_kernel, dim3(1), dim3(1024), 0, stream, aat, seg, k, p.n_slices,
                        p.pa_ch, p.pa_chunks, pa_seg, status);
@@ -844,11 +868,11 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
 #define SEACELLS_B_CASE(S)                                                                      \
   case S:                                                                                       \
     e = dual ? launch_partials<S, true>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent,       \
-                                        k2at_rs, keys, gap_part, stamps, xcd_work, epoch,       \
-                                        status, stream)                                         \
+                                        aat_lcol, k2at_rs, keys, gap_part, stamps, xcd_work,   \
+                                        epoch, status, stream)                                  \
              : launch_partials<S, false>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent,      \
-                                         k2at_rs, keys, gap_part, stamps, xcd_work, epoch,      \
-                                         status, stream);                                       \
+                                         aat_lcol, k2at_rs, keys, gap_part, stamps, xcd_work,  \
+                                         epoch, status, stream);                                \
     break;
     SEACELLS_B_CASE(1)
     SEACELLS_B_CASE(2)
