@@ -174,7 +174,7 @@ struct BPlan {
   uint32_t pa_ch;         // entries per chunk (64), 0 without the copy
   uint64_t pa_chunks;     // bound on the chunks of all runs, chunk 0 included
   size_t off_keys, off_part2, off_gap, off_stamp, off_work, off_seg, off_rs, off_pa_seg,
-      off_pa_ent, off_lcol;
+      off_pa_ent, off_pc_col, off_pc_val;
   size_t ws_bytes;
 };
 BPlan plan_b(uint32_t n, uint32_t k, uint64_t aat_nnz);

@@ -104,19 +104,6 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// AAt's columns within their slice as 16-bit words for the narrow-slice
-// gather (slices are at most 2048 columns wide): lcol[e] = column of entry e
-// mod slice_w, 2 bytes per entry instead of 4. A column >= k becomes 0xffff
-// (the gather sends it to the lane's dummy slot).
-__global__ void __launch_bounds__(256)
-    aat_local_cols_kernel(Csr aat, uint32_t k, uint32_t slice_w, uint16_t *__restrict__ lcol) {
-  const uint32_t stride = gridDim.x * blockDim.x;
-  for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < aat.nnz; e += stride) {
-    const uint32_t c = aat.idx[e];
-    lcol[e] = (uint16_t)(c < k ? c % slice_w : 0xffffu);
-  }
-}
-
 // Row-slice table of an n x k operand whose rows are read slice by slice
 // (K2At): rs[i * (n_slices + 1) + s] = first position of row i with column
 // >= s * slice_w, rs[i * (n_slices + 1) + n_slices] = the row's end, so the
@@ -260,6 +247,55 @@ __global__ void __launch_bounds__(256)
   if (flags != 0) atomicOr(status, flags);
 }
 
+// Chunked copy of AAt for the narrow-slice gather (two half-waves, one run
+// each). The run of AAt row m inside slice s takes ceil(len / 32) chunks of
+// 32 entries starting at chunk pc_seg[s * k + m] (the chunk table is built by
+// pa_seg_kernel with chunks of 32): the entries' columns within the slice as
+// 16-bit words in pc_col and their values in pc_val, so one half-wave load
+// reads exactly one 64-byte run of columns and one 128-byte run of values.
+// Positions past the run hold column 0xffff (the gather sends it to the
+// lane's dummy slot) and value 0; chunk 0 is all padding (empty runs read
+// it). One wave per run.
+constexpr uint32_t kPcCh = 32;
+
+__global__ void __launch_bounds__(256)
+    pc_fill_kernel(Csr aat, const uint32_t *__restrict__ seg, uint32_t k, uint32_t n_slices,
+                   uint32_t slice_w, const uint32_t *__restrict__ pc_seg,
+                   uint16_t *__restrict__ pc_col, float *__restrict__ pc_val,
+                   uint32_t *__restrict__ status) {
+  const uint32_t lane = lane_id();
+  const uint64_t nw = (uint64_t)gridDim.x * (blockDim.x / kWave);
+  const uint64_t total_runs = (uint64_t)k * n_slices;
+  const uint64_t first = (uint64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (first == 0 && lane < kPcCh) pc_col[lane] = 0xffffu, pc_val[lane] = 0.0f;
+  uint32_t flags = 0;
+  for (uint64_t e = first; e < total_runs; e += nw) {
+    const uint32_t s = (uint32_t)(e / k), m = (uint32_t)(e - (uint64_t)s * k);
+    const uint32_t c0 = s * slice_w;
+    const uint32_t cw = (k - c0) < slice_w ? (k - c0) : slice_w;
+    const uint32_t q0 = pc_seg[e], q1 = pc_seg[e + 1];
+    uint32_t lo;
+    bool bad;
+    uint32_t len = run_of(aat, seg, k, s, m, lo, bad);
+    const uint64_t room = (uint64_t)(q1 - q0) * kPcCh;  // 0 when the runs were left empty
+    if (len > room) len = (uint32_t)room;
+    for (uint32_t i = lane; i < room; i += kWave) {
+      uint16_t c16 = 0xffffu;
+      float v = 0.0f;
+      if (i < len) {
+        const uint32_t c = aat.idx[lo + i] - c0;
+        if (c < cw)
+          c16 = (uint16_t)c, v = aat.val[lo + i];
+        else
+          flags |= kFlagBadIndex;
+      }
+      pc_col[(size_t)q0 * kPcCh + i] = c16;
+      pc_val[(size_t)q0 * kPcCh + i] = v;
+    }
+  }
+  if (flags != 0) atomicOr(status, flags);
+}
+
 // kDual: the two half-waves gather different K2B entries into two
 // accumulators (for the short AAt runs of narrow slices); each column then
 // sums the even-numbered entries of the row in one accumulator and the odd
@@ -269,7 +305,8 @@ __global__ void __launch_bounds__(kBThreads)
     fw_b_partials_kernel(Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n, uint32_t k,
                          uint32_t slice_w, uint32_t n_slices, uint32_t n_row_blocks,
                          const uint32_t *__restrict__ seg, const uint32_t *__restrict__ pa_seg,
-                         const uint2 *__restrict__ pa_ent, const uint16_t *__restrict__ aat_lcol,
+                         const uint2 *__restrict__ pa_ent, const uint16_t *__restrict__ pc_col,
+                         const float *__restrict__ pc_val,
                          const uint32_t *__restrict__ k2at_rs, uint64_t *__restrict__ part_key,
                          float *__restrict__ part_gap, uint32_t *__restrict__ stamps,
                          uint32_t *__restrict__ xcd_work, uint32_t epoch,
@@ -359,24 +396,19 @@ __global__ void __launch_bounds__(kBThreads)
       // -- acc[c] = sum_m K2B[i, m] AAt[m, c] over this slice
       uint32_t e0, e1;
       if (!row_ok(k2b, i, e0, e1)) flags |= kFlagBadIndex;
-      const uint32_t *pseg = kDual ? nullptr : pa_seg + (size_t)sl * k;
+      const uint32_t *pseg = pa_seg + (size_t)sl * k;  // the run table of this slice
       for (uint32_t eb = e0; eb < e1; eb += kWave) {
         const uint32_t e = eb + lane;
-        // this entry's run of AAt: [lo, hi) in AAt (two half-wave
-        // accumulators), or first chunk q0 and chunks nq of the padded copy
-        uint32_t lo = 0, hi = 0, q0 = 0, nq = 0;
+        // this entry's run of AAt: first chunk q0 and chunks nq of the
+        // slice's chunked copy
+        uint32_t q0 = 0, nq = 0;
         float x = 0.0f;
         if (e < e1) {
           const uint32_t m = k2b.idx[e];
           x = k2b.val[e];
           if (m < k) {
-            if constexpr (kDual) {
-              lo = seg[(size_t)sl * k + m];
-              hi = seg[(size_t)(sl + 1) * k + m];
-            } else {
-              q0 = pseg[m];
-              nq = pseg[m + 1] - q0;
-            }
+            q0 = pseg[m];
+            nq = pseg[m + 1] - q0;
           } else {
             flags |= kFlagBadIndex;
           }
@@ -385,33 +417,37 @@ __global__ void __launch_bounds__(kBThreads)
         const uint32_t cnt = (e1 - eb) < kWave ? (e1 - eb) : kWave;
         if constexpr (kDual) {
           // entries u + 2g (lanes 0-31) and u + 2g + 1 (lanes 32-63): runs of
-          // kPairs pairs in flight, 32 lanes per run. Each chunk's
-          // (run start, run end, K2B value) goes through LDS once, and a half
-          // reads its entry's triple with one broadcast load.
-          stage[lane] = make_uint4(lo, lane < cnt ? hi : lo, __float_as_uint(x), 0u);
+          // kPairs pairs in flight, 32 lanes per run, one chunk of 32 entries
+          // per half-wave load. Each chunk's (first chunk, chunks, K2B value)
+          // goes through LDS once, and a half reads its entry's triple with
+          // one broadcast load.
+          stage[lane] = make_uint4(q0, lane < cnt ? nq : 0u, __float_as_uint(x), 0u);
           wave_lds_sync();
           for (uint32_t u = 0; u < cnt; u += 2 * kPairs) {
-            uint32_t plo[kPairs], phi[kPairs];
+            uint32_t pq[kPairs], pn[kPairs];
             float xs[kPairs], va[kPairs], vb[kPairs];
             uint32_t ca[kPairs], cb[kPairs];
 #pragma unroll
             for (uint32_t g = 0; g < kPairs; ++g) {
               const uint4 t = stage[u + 2 * g + half];  // slots >= cnt hold empty runs
-              plo[g] = t.x;
-              phi[g] = t.y;
+              pq[g] = t.x;
+              pn[g] = t.y;
               xs[g] = __uint_as_float(t.z);
-              const uint32_t pa = plo[g] + hl, pb = pa + 32;
-              ca[g] = kNoCol, va[g] = 0.0f, cb[g] = kNoCol, vb[g] = 0.0f;
-              if (pa < phi[g]) ca[g] = load_at(aat_lcol, pa * 2u), va[g] = load_at(aat.val, pa * 4u);
-              if (pb < phi[g]) cb[g] = load_at(aat_lcol, pb * 2u), vb[g] = load_at(aat.val, pb * 4u);
+              const uint32_t pa = pq[g] * kPcCh + hl;  // chunk 0 (padding) for an empty run
+              ca[g] = load_at(pc_col, pa * 2u), va[g] = load_at(pc_val, pa * 4u);
+              cb[g] = kNoCol, vb[g] = 0.0f;
+              if (pn[g] > 1) {
+                const uint32_t pb = pa + kPcCh;
+                cb[g] = load_at(pc_col, pb * 2u), vb[g] = load_at(pc_val, pb * 4u);
+              }
             }
-            // lanes without an entry go to this lane's dummy slot past the
-            // accumulator (their column is kNoCol; columns are slice-local, so
-            // even a malformed row stays inside the accumulator, whose padding
-            // is cleared with it and never read). The two entries of a lane
-            // belong to one run, so their columns differ: both old values are
-            // read before either is written (one LDS round trip per run; the
-            // dummy only ever takes + 0). Runs follow each other in K2B order.
+            // padding and lanes without an entry go to this lane's dummy slot
+            // past the accumulator (column 0xffff or kNoCol; columns are
+            // slice-local, so nothing lands outside the accumulator). The two
+            // entries of a lane belong to one run, so their columns differ:
+            // both old values are read before either is written (one LDS
+            // round trip per run; the dummy only ever takes + 0). Runs follow
+            // each other in K2B order.
 #pragma unroll
             for (uint32_t g = 0; g < kPairs; ++g) {
               float *qa = acc_h + min(ca[g], W + hl);
@@ -419,9 +455,10 @@ __global__ void __launch_bounds__(kBThreads)
               const float oa = *qa, ob = *qb;
               *qa = __builtin_fmaf(xs[g], va[g], oa);
               *qb = __builtin_fmaf(xs[g], vb[g], ob);
-              for (uint32_t p = plo[g] + 64 + hl; p < phi[g]; p += 32) {
-                float *q = acc_h + min((uint32_t)load_at(aat_lcol, p * 2u), W + hl);
-                *q = __builtin_fmaf(xs[g], load_at(aat.val, p * 4u), *q);
+              for (uint32_t j = 2; j < pn[g]; ++j) {
+                const uint32_t p = (pq[g] + j) * kPcCh + hl;
+                float *q = acc_h + min((uint32_t)load_at(pc_col, p * 2u), W + hl);
+                *q = __builtin_fmaf(xs[g], load_at(pc_val, p * 4u), *q);
               }
             }
           }
@@ -694,7 +731,8 @@ __global__ void zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
 template <uint32_t S4, bool kDual>
 hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
                            uint32_t k, const uint32_t *seg, const uint32_t *pa_seg,
-                           const uint2 *pa_ent, const uint16_t *aat_lcol, const uint32_t *k2at_rs,
+                           const uint2 *pa_ent, const uint16_t *pc_col, const float *pc_val,
+                           const uint32_t *k2at_rs,
                            uint64_t *keys,
                            float *gap_part, uint32_t *stamps, uint32_t *xcd_work, uint32_t epoch,
                            uint32_t *status, hipStream_t stream) {
@@ -732,7 +770,7 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // the same number of blocks on every XCD
   hipLaunchKernelGGL(deep ? k_deep : k_std, dim3((uint32_t)blocks), dim3(kBThreads), lds,
                      stream, k2b, aat, k2at, b, n, k, p.slice_w, p.n_slices, p.n_row_blocks, seg,
-                     pa_seg, pa_ent, aat_lcol, k2at_rs, keys, gap_part, stamps, xcd_work, epoch,
+                     pa_seg, pa_ent, pc_col, pc_val, k2at_rs, keys, gap_part, stamps, xcd_work, epoch,
                      status);
   return hipGetLastError();
 }
@@ -787,19 +825,25 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices, uint64_
   if (p.n_slices > 1) off = align_up(off + (size_t)k * (p.n_slices + 1) * sizeof(uint32_t), 256);
   p.off_rs = off;
   if (p.n_slices > 1) off = align_up(off + (size_t)n * (p.n_slices + 1) * sizeof(uint32_t), 256);
-  // narrow slices gather two short AAt runs per wave instruction, reading
-  // AAt with 32-bit byte offsets; otherwise the padded AAt copy: a run of
-  // len entries takes ceil(len / 64) chunks, at most nnz / 64 + 1 per (row,
-  // slice) in all, plus chunk 0
-  p.dual = p.n_slices > 1 && aat_nnz < (1ull << 30);
-  p.pa_ch = p.dual ? 0u : kWave;
-  p.pa_chunks = p.dual ? 0u : (aat_nnz + kWave - 1) / kWave + (uint64_t)k * p.n_slices + 1;
+  // AAt copied per slice in chunks: narrow slices gather two short runs per
+  // wave instruction (one per half-wave) from chunks of 32 entries (16-bit
+  // columns and f32 values apart, addressed with 32-bit byte offsets);
+  // otherwise chunks of 64 (accumulator byte offset, value) pairs. A run of
+  // len entries takes ceil(len / ch) chunks, at most nnz / ch + 1 per (row,
+  // slice) in all, plus chunk 0 (padding)
+  const uint64_t runs = (uint64_t)k * p.n_slices;
+  const uint64_t pc_chunks = (aat_nnz + kPcCh - 1) / kPcCh + runs + 1;
+  p.dual = p.n_slices > 1 && pc_chunks < (1ull << 25);
+  p.pa_ch = p.dual ? kPcCh : kWave;
+  p.pa_chunks = p.dual ? pc_chunks : (aat_nnz + kWave - 1) / kWave + runs + 1;
   p.off_pa_seg = off;
-  if (!p.dual) off = align_up(off + ((size_t)k * p.n_slices + 1) * sizeof(uint32_t), 256);
+  off = align_up(off + (runs + 1) * sizeof(uint32_t), 256);
   p.off_pa_ent = off;
-  off = align_up(off + (size_t)p.pa_chunks * p.pa_ch * sizeof(uint2), 256);
-  p.off_lcol = off;
-  if (p.dual) off = align_up(off + (size_t)aat_nnz * sizeof(uint16_t), 256);
+  if (!p.dual) off = align_up(off + (size_t)p.pa_chunks * p.pa_ch * sizeof(uint2), 256);
+  p.off_pc_col = off;
+  if (p.dual) off = align_up(off + (size_t)p.pa_chunks * kPcCh * sizeof(uint16_t), 256);
+  p.off_pc_val = off;
+  if (p.dual) off = align_up(off + (size_t)p.pa_chunks * kPcCh * sizeof(float), 256);
   p.ws_bytes = off;
   return p;
 }
@@ -841,25 +885,23 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
                        dim3(256), 0, stream, aat, k, p.slice_w, p.n_slices, seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // the padded AAt copy (or, for narrow slices that gather two runs per wave
-  // instruction, AAt's slice-local columns as 16-bit words), then the partials
+  // the chunked copy of AAt per slice (run table, then the entries)
   const bool dual = p.dual;
-  uint16_t *aat_lcol = dual ? reinterpret_cast<uint16_t *>(base + p.off_lcol) : nullptr;
-  if (dual && aat.nnz > 0) {
-    const uint32_t blocks = (aat.nnz + 255) / 256;
-    hipLaunchKernelGGL(aat_local_cols_kernel, dim3(blocks < 65536u ? blocks : 65536u), dim3(256),
-                       0, stream, aat, k, p.slice_w, aat_lcol);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  if (!dual) {
-    hipLaunchKernelGGL(pa_seg_kernel, dim3(1), dim3(1024), 0, stream, aat, seg, k, p.n_slices,
-                       p.pa_ch, p.pa_chunks, pa_seg, status);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  uint16_t *pc_col = reinterpret_cast<uint16_t *>(base + p.off_pc_col);
+  float *pc_val = reinterpret_cast<float *>(base + p.off_pc_val);
+  hipLaunchKernelGGL(pa_seg_kernel, dim3(1), dim3(1024), 0, stream, aat, seg, k, p.n_slices,
+                     p.pa_ch, p.pa_chunks, pa_seg, status);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
     const uint64_t runs = (uint64_t)k * p.n_slices;
     const uint64_t blocks = (runs + 3) / 4;  // 4 waves per block, one run each
-    hipLaunchKernelGGL(pa_fill_kernel, dim3((uint32_t)(blocks < 65535u ? blocks : 65535u)),
-                       dim3(256), 0, stream, aat, seg, k, p.n_slices, p.slice_w, p.pa_ch,
-                       256u * p.s4, pa_seg, pa_ent, status);
+    const dim3 grid((uint32_t)(blocks < 65535u ? blocks : 65535u));
+    if (dual)
+      hipLaunchKernelGGL(pc_fill_kernel, grid, dim3(256), 0, stream, aat, seg, k, p.n_slices,
+                         p.slice_w, pa_seg, pc_col, pc_val, status);
+    else
+      hipLaunchKernelGGL(pa_fill_kernel, grid, dim3(256), 0, stream, aat, seg, k, p.n_slices,
+                         p.slice_w, p.pa_ch, 256u * p.s4, pa_seg, pa_ent, status);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, xcd_work, kXcds);
@@ -868,10 +910,10 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
 #define SEACELLS_B_CASE(S)                                                                      \
   case S:                                                                                       \
     e = dual ? launch_partials<S, true>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent,       \
-                                        aat_lcol, k2at_rs, keys, gap_part, stamps, xcd_work,   \
+                                        pc_col, pc_val, k2at_rs, keys, gap_part, stamps, xcd_work,   \
                                         epoch, status, stream)                                  \
              : launch_partials<S, false>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent,      \
-                                         aat_lcol, k2at_rs, keys, gap_part, stamps, xcd_work,  \
+                                         pc_col, pc_val, k2at_rs, keys, gap_part, stamps, xcd_work,  \
                                          epoch, status, stream);                                \
     break;
     SEACELLS_B_CASE(1)
