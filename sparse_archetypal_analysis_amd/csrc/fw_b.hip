@@ -46,7 +46,8 @@ constexpr size_t kSliceAatBytes = 5u << 19;  // AAt bytes per slice kept within 
 constexpr uint32_t kSlicedRowBlocks = 16384;  // row ranges per slice when k is sliced
 constexpr uint64_t kKeysBudget = 1ull << 31;  // bytes of partial keys beyond which row ranges shrink
 constexpr uint32_t kAccPad = 32;             // dummy slots after each dual accumulator
-constexpr uint32_t kStageSlots = kWave + 8;  // staged triples (a run of pairs reads past 64)
+constexpr uint32_t kStageSlots = kWave + 8;  // LDS staging per wave, in 16-byte slots
+constexpr uint32_t kChunkSlots = 2 * kStageSlots - 16;  // (chunk, value) pairs per window
 
 // base[byte_off / 4] with a 32-bit byte offset from a wave-uniform base (the
 // array must hold fewer than 2^30 entries)
@@ -312,9 +313,8 @@ __global__ void __launch_bounds__(kBThreads)
                          uint32_t *__restrict__ xcd_work, uint32_t epoch,
                          uint32_t *__restrict__ status) {
   constexpr uint32_t W = 256 * S4;  // accumulator columns (>= slice_w)
-  // the staged triples a group of kPairs pairs reads stay inside the stage
-  static_assert((kWave - 1) / (2 * kPairs) * (2 * kPairs) + 2 * kPairs <= kStageSlots,
-                "stage slots");
+  // a window's padding slots stay inside the stage
+  static_assert(kChunkSlots + 2 * kPairs <= 2 * kStageSlots, "stage slots");
   constexpr uint32_t NC = 4 * S4;   // columns per lane
   constexpr uint32_t NACC = kDual ? 2 : 1;
   extern __shared__ float lds_acc[];
@@ -358,7 +358,6 @@ __global__ void __launch_bounds__(kBThreads)
       *reinterpret_cast<float4 *>(acc + a * ACC2 + s4 * 256 + lane * 4) = zero4;
   if constexpr (kDual) {
     if (lane < kAccPad) acc[W + lane] = 0.0f, acc[ACC2 + W + lane] = 0.0f;
-    if (lane < kStageSlots - kWave) stage[kWave + lane] = make_uint4(0u, 0u, 0u, 0u);
   } else {
     acc[W + lane] = 0.0f;  // the dummy slots padding entries add 0 to
   }
@@ -416,51 +415,53 @@ __global__ void __launch_bounds__(kBThreads)
         if (nq == 0) q0 = 0;  // empty: the padding chunk (adds 0 to dummy slots)
         const uint32_t cnt = (e1 - eb) < kWave ? (e1 - eb) : kWave;
         if constexpr (kDual) {
-          // entries u + 2g (lanes 0-31) and u + 2g + 1 (lanes 32-63): runs of
-          // kPairs pairs in flight, 32 lanes per run, one chunk of 32 entries
-          // per half-wave load. Each chunk's (first chunk, chunks, K2B value)
-          // goes through LDS once, and a half reads its entry's triple with
-          // one broadcast load.
-          stage[lane] = make_uint4(q0, lane < cnt ? nq : 0u, __float_as_uint(x), 0u);
-          wave_lds_sync();
-          for (uint32_t u = 0; u < cnt; u += 2 * kPairs) {
-            uint32_t pq[kPairs], pn[kPairs];
-            float xs[kPairs], va[kPairs], vb[kPairs];
-            uint32_t ca[kPairs], cb[kPairs];
+          // The chunks of the 64 staged runs, flattened in K2B order, are
+          // dealt alternately to the two half-waves (chunk s to half s % 2),
+          // kPairs per half in flight: every half-wave load reads one whole
+          // chunk (32 entries, one 128-byte line of values) whatever the runs'
+          // lengths. Each half accumulates into its own array, so a column
+          // sums its terms of the even-numbered chunks in one and of the
+          // odd-numbered ones in the other, each in K2B order; the fold adds
+          // the two. Windows of kChunkSlots (chunk, K2B value) pairs go
+          // through LDS; slots past a window's end hold the padding chunk 0
+          // with coefficient 0.
+          const uint32_t my_nq = lane < cnt ? nq : 0u;
+          uint32_t incl = my_nq;
 #pragma unroll
-            for (uint32_t g = 0; g < kPairs; ++g) {
-              const uint4 t = stage[u + 2 * g + half];  // slots >= cnt hold empty runs
-              pq[g] = t.x;
-              pn[g] = t.y;
-              xs[g] = __uint_as_float(t.z);
-              const uint32_t pa = pq[g] * kPcCh + hl;  // chunk 0 (padding) for an empty run
-              ca[g] = load_at(pc_col, pa * 2u), va[g] = load_at(pc_val, pa * 4u);
-              cb[g] = kNoCol, vb[g] = 0.0f;
-              if (pn[g] > 1) {
-                const uint32_t pb = pa + kPcCh;
-                cb[g] = load_at(pc_col, pb * 2u), vb[g] = load_at(pc_val, pb * 4u);
+          for (uint32_t off = 1; off < kWave; off <<= 1) {
+            const uint32_t v = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += v;
+          }
+          const uint32_t pos = incl - my_nq;
+          const uint32_t total = readlane_u32(incl, kWave - 1);
+          uint2 *cst = reinterpret_cast<uint2 *>(stage);
+          for (uint32_t base = 0; base < total; base += kChunkSlots) {
+            const uint32_t win = (total - base) < kChunkSlots ? (total - base) : kChunkSlots;
+            for (uint32_t j = pos < base ? base - pos : 0u; j < my_nq && pos + j < base + win; ++j)
+              cst[pos + j - base] = make_uint2(q0 + j, __float_as_uint(x));
+            if (lane < 2 * kPairs) cst[win + lane] = make_uint2(0u, 0u);
+            wave_lds_sync();
+            for (uint32_t t = 0; t < win; t += 2 * kPairs) {
+              uint32_t ca[kPairs];
+              float xs[kPairs], va[kPairs];
+#pragma unroll
+              for (uint32_t g = 0; g < kPairs; ++g) {
+                const uint2 cx = cst[t + 2 * g + half];
+                xs[g] = __uint_as_float(cx.y);
+                const uint32_t p = cx.x * kPcCh + hl;
+                ca[g] = load_at(pc_col, p * 2u);
+                va[g] = load_at(pc_val, p * 4u);
+              }
+              // padding entries have column 0xffff and go to this lane's dummy
+              // slot past the accumulator (columns are slice-local, so nothing
+              // lands outside it; the dummy only ever takes + 0)
+#pragma unroll
+              for (uint32_t g = 0; g < kPairs; ++g) {
+                float *q = acc_h + min(ca[g], W + hl);
+                *q = __builtin_fmaf(xs[g], va[g], *q);
               }
             }
-            // padding and lanes without an entry go to this lane's dummy slot
-            // past the accumulator (column 0xffff or kNoCol; columns are
-            // slice-local, so nothing lands outside the accumulator). The two
-            // entries of a lane belong to one run, so their columns differ:
-            // both old values are read before either is written (one LDS
-            // round trip per run; the dummy only ever takes + 0). Runs follow
-            // each other in K2B order.
-#pragma unroll
-            for (uint32_t g = 0; g < kPairs; ++g) {
-              float *qa = acc_h + min(ca[g], W + hl);
-              float *qb = acc_h + min(cb[g], W + hl);
-              const float oa = *qa, ob = *qb;
-              *qa = __builtin_fmaf(xs[g], va[g], oa);
-              *qb = __builtin_fmaf(xs[g], vb[g], ob);
-              for (uint32_t j = 2; j < pn[g]; ++j) {
-                const uint32_t p = (pq[g] + j) * kPcCh + hl;
-                float *q = acc_h + min((uint32_t)load_at(pc_col, p * 2u), W + hl);
-                *q = __builtin_fmaf(xs[g], load_at(pc_val, p * 4u), *q);
-              }
-            }
+            wave_lds_sync();
           }
           wave_lds_sync();
           continue;
