@@ -40,6 +40,9 @@ typedef struct seacells_a_options {
     int32_t dense_argmin;   /* 1: a dense scan decides every step */
     uint32_t group;         /* 0: by k; 16, 32 or 64 lanes per cell in the
                                dense-state kernels */
+    int32_t support_wide;   /* -1: by K2B's mean row length (default); 0: the
+                               first support pass keeps 256 K2B entries per
+                               cell in registers; 1: 512 */
 } seacells_a_options;
 
 /* Set the overrides; NULL restores the defaults. SEACELLS_E_SHAPE on a value

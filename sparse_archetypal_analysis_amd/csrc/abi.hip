@@ -478,10 +478,12 @@ int seacells_debug_set_a_options(const seacells_a_options *opt) {
     if (opt->dense_argmin < 0 || opt->dense_argmin > 1) return SEACELLS_E_SHAPE;
     if (opt->group != 0 && opt->group != 16 && opt->group != 32 && opt->group != 64)
       return SEACELLS_E_SHAPE;
+    if (opt->support_wide < -1 || opt->support_wide > 1) return SEACELLS_E_SHAPE;
     o.support = opt->support;
     o.support_waves = opt->support_waves;
     o.dense_argmin = opt->dense_argmin == 1;
     o.group = opt->group;
+    o.support_wide = opt->support_wide;
   }
   a_options() = o;
   return SEACELLS_OK;

@@ -122,6 +122,7 @@ struct AOptions {
   uint32_t support_waves = 0;  // resident waves per CU the first support pass is sized for (0: default)
   bool dense_argmin = false;   // a dense scan decides every step
   uint32_t group = 0;          // lanes per cell of the dense kernels (0: by k; 16, 32, 64)
+  int support_wide = -1;       // first support pass: -1 by K2B row length, 0: 256, 1: 512 in registers
 };
 AOptions &a_options();
 

@@ -1727,6 +1727,14 @@ bool support_tier_size(const APlan &p, uint32_t waves, uint32_t &hc_out, uint32_
 
 // Resident waves per CU of the first support pass: the target, lowered
 // (in whole blocks) until its LDS fits.
+// The first support pass keeps 512 K2B entries per cell in registers (at
+// fewer resident waves) when K2B rows are long on average, else 256.
+bool first_pass_wide(const Csr &k2b, uint32_t n) {
+  const int o = a_options().support_wide;
+  if (o >= 0) return o == 1;
+  return k2b.nnz > (uint64_t)n * 192u;
+}
+
 uint32_t first_pass_waves(const APlan &p, bool wide) {
   uint32_t w = support_waves_per_cu();
   if (wide && w > kSupWideWaves) w = kSupWideWaves;  // register-limited
@@ -1804,7 +1812,7 @@ hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, uint32_t tie
                           float prune_thr, uint32_t *status, hipStream_t stream) {
   // t2 entries in registers: 256 for short K2B rows, 512 when rows are long
   // on average (the first pass) or by construction (the long-row pass)
-  const bool wide = tier > 0 || k2b.nnz > (uint64_t)n * 192u;
+  const bool wide = tier > 0 || first_pass_wide(k2b, n);
   const uint32_t waves = tier > 0 ? kSupLongWaves : first_pass_waves(plan, wide);
   uint32_t hc_cap = 0, lpw = 0;
   if (!support_tier_size(plan, waves, hc_cap, lpw)) return hipErrorInvalidValue;
@@ -1980,7 +1988,7 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
     hipLaunchKernelGGL(cell_scatter_kernel, dim3(nb), dim3(256), 0, stream, keys, n, hist, order);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // a second pass when it holds longer K2B rows than the first
-    const bool wide0 = k2b.nnz > (uint64_t)n * 192u;
+    const bool wide0 = first_pass_wide(k2b, n);
     uint32_t hc0 = 0, hc1 = 0, lpw_unused;
     support_tier_size(plan, first_pass_waves(plan, wide0), hc0, lpw_unused);
     const bool two = support_tier_size(plan, kSupLongWaves, hc1, lpw_unused) && hc1 > hc0;

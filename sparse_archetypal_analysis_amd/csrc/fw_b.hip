@@ -42,7 +42,8 @@ constexpr uint32_t kMaxChunks = 64;
 
 constexpr uint32_t kGatherRows = 4;  // AAt runs whose loads are in flight together
 constexpr uint32_t kXcds = 8;        // MI355X: 8 XCDs of 32 CUs, each with its own 4 MB L2
-constexpr size_t kSliceAatBytes = 5u << 19;  // AAt bytes per slice kept within one L2 (2.5 MB)
+constexpr size_t kSliceAatBytes = 15u << 18;  // AAt bytes (at 8 per entry) per slice: 3.75 MB
+constexpr uint32_t kSliceCols = 1024;          // columns per slice when k is sliced
 constexpr uint32_t kSlicedRowBlocks = 16384;  // row ranges per slice when k is sliced
 constexpr uint64_t kKeysBudget = 1ull << 31;  // bytes of partial keys beyond which row ranges shrink
 constexpr uint32_t kAccPad = 32;             // dummy slots after each dual accumulator
@@ -778,14 +779,16 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
 
 }  // namespace
 
-// Slices: one when k fits one accumulator; otherwise enough that each holds
-// at most ~2.5 MB of AAt (the L2 share of one XCD) and at most 2048
-// columns (so any k has a plan), as 2, 4 or a multiple of 8 slices so that
-// they spread evenly over the XCDs.
+// Slices: one when k fits one accumulator (k <= 2048); otherwise enough
+// that each holds at most kSliceCols columns (the running minima of wider
+// slices take registers that cost resident waves) and at most ~3.75 MB of
+// AAt at 8 bytes per entry (its chunked copy, ~6 bytes per entry plus
+// padding, stays within one XCD's 4 MB L2), as 2, 4 or a multiple of 8
+// slices so that they spread evenly over the XCDs.
 static uint32_t slices_for(uint32_t k, uint64_t aat_nnz) {
   const uint32_t wmax = 256u * kBMaxS4;
   if (k <= wmax) return 1;
-  uint64_t s = ((uint64_t)k + wmax - 1) / wmax;
+  uint64_t s = ((uint64_t)k + kSliceCols - 1) / kSliceCols;
   const uint64_t by_l2 = (aat_nnz * 8 + kSliceAatBytes - 1) / kSliceAatBytes;
   if (by_l2 > s) s = by_l2;
   if (s <= 2) return 2;

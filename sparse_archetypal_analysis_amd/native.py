@@ -47,7 +47,8 @@ class seacells_csr(ctypes.Structure):
 
 class seacells_a_options(ctypes.Structure):
     _fields_ = [("support", ctypes.c_int32), ("support_waves", ctypes.c_uint32),
-                ("dense_argmin", ctypes.c_int32), ("group", ctypes.c_uint32)]
+                ("dense_argmin", ctypes.c_int32), ("group", ctypes.c_uint32),
+                ("support_wide", ctypes.c_int32)]
 
 
 class seacells_b_layout(ctypes.Structure):
@@ -380,11 +381,12 @@ def seacells_fw_b_apply(bt_idx, bt_val, bt_cnt, n: int, arg_idx, gamma: float, s
 # test and experiment hooks (include/seacells_debug.h)
 # --------------------------------------------------------------------------
 
-def seacells_debug_set_a_options(support=-1, support_waves=0, dense_argmin=False, group=0):
+def seacells_debug_set_a_options(support=-1, support_waves=0, dense_argmin=False, group=0,
+                                 support_wide=-1):
     """Plan overrides of the A update (process-wide); no arguments restore
     the defaults."""
     opt = seacells_a_options(int(support), int(support_waves), 1 if dense_argmin else 0,
-                             int(group))
+                             int(group), int(support_wide))
     _check_rc(load().seacells_debug_set_a_options(ctypes.byref(opt)))
 
 

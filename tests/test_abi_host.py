@@ -279,11 +279,11 @@ def test_b_argmin_has_a_plan_for_every_k(k):
 
 def test_debug_hooks_reject_bad_options():
     lib = saa.load()
-    bad = native.seacells_a_options(2, 0, 0, 0)
+    bad = native.seacells_a_options(2, 0, 0, 0, -1)
     assert lib.seacells_debug_set_a_options(ctypes.byref(bad)) == -2
-    bad = native.seacells_a_options(-1, 3, 0, 0)
+    bad = native.seacells_a_options(-1, 3, 0, 0, -1)
     assert lib.seacells_debug_set_a_options(ctypes.byref(bad)) == -2
-    bad = native.seacells_a_options(-1, 0, 0, 48)
+    bad = native.seacells_a_options(-1, 0, 0, 48, -1)
     assert lib.seacells_debug_set_a_options(ctypes.byref(bad)) == -2
     assert lib.seacells_debug_set_a_options(None) == 0
     # the overrides reach the workspace query (the support state's queues)
