@@ -419,6 +419,48 @@ def _copy_scale(folder, counter, nbytes):
     return nbytes / (float(np.median(vals)) * 1024.0)
 
 
+def utilization(counters, by_k, calls):
+    """Busy fractions of the main kernel of each call (the one with the most
+    time), from the mean-per-dispatch counters, or {} without them."""
+    need = ("GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT",
+            "TD_TD_BUSY_sum", "TA_BUSY_avr", "TCC_HIT_sum", "TCC_MISS_sum")
+    if any(c not in counters for c in need):
+        return {}
+    out = {}
+    for c in ("fw_a_columns", "fw_b_argmin"):
+        ks = [k for k in by_k if _call_of(k) == c and all(k in counters[x] for x in need)]
+        if not ks:
+            continue
+        k = max(ks, key=lambda x: sum(by_k[x]))
+        m = {x: float(np.mean(counters[x][k])) for x in need}
+        cyc = m["GRBM_GUI_ACTIVE"] / 8.0
+        if cyc <= 0:
+            continue
+        out[c] = {"kernel": k, "valu": m["SQ_INSTS_VALU"] * 4.0 / (1024.0 * cyc),
+                  "lds": m["SQ_LDS_IDX_ACTIVE"] / (256.0 * cyc),
+                  "lds_conflict_share": m["SQ_LDS_BANK_CONFLICT"] / max(m["SQ_LDS_IDX_ACTIVE"], 1.0),
+                  "td": m["TD_TD_BUSY_sum"] / (256.0 * cyc), "ta": m["TA_BUSY_avr"] / cyc,
+                  "l2_hit": m["TCC_HIT_sum"] / max(m["TCC_HIT_sum"] + m["TCC_MISS_sum"], 1.0)}
+    return out
+
+
+def limiter_from_profile(call, workload, sha):
+    """The busiest unit of the call's main kernel in the committed counter
+    record (None when absent or the sources changed)."""
+    if not os.path.exists(TRAFFIC_JSON):
+        return None
+    with open(TRAFFIC_JSON) as f:
+        rec = json.load(f)
+    e = rec.get(call, {}).get(workload)
+    if not e or e.get("source_sha") != sha or "utilization" not in e:
+        return None
+    u = e["utilization"]
+    busy = {x: u[x] for x in ("valu", "lds", "td", "ta")}
+    top = max(busy, key=busy.get)
+    return {"unit": top, "busy": busy, "lds_conflict_share": u["lds_conflict_share"],
+            "l2_hit": u["l2_hit"], "kernel": u["kernel"]}
+
+
 def summarize_profile(args):
     """rocprofv3 folders -> markdown summary and the per-call traffic record."""
     name = args.config
@@ -499,6 +541,25 @@ def summarize_profile(args):
                           "us_per_call_trace": per_call_us.get(c),
                           "kernels": sorted(k for k in fetch if _call_of(k) == c),
                           "fetch_scale": fs, "write_scale": ws}
+    all_counters = {}
+    for folder in args.counters:
+        for c, ks in _counter_totals(folder).items():
+            all_counters[c] = ks
+    util = utilization(all_counters, by_k, calls)
+    if util:
+        lines += ["", "## Utilization of the main kernel of each call (from the counters below)", "",
+                  "Cycles = GRBM_GUI_ACTIVE / 8 (one per XCD). VALU: SQ_INSTS_VALU x 4 cycles per "
+                  "wave64 instruction over 1024 SIMDs; LDS: SQ_LDS_IDX_ACTIVE over 256 CUs (bank "
+                  "conflict cycles are part of it); TD: TD_TD_BUSY_sum over 256 CUs; TA: "
+                  "TA_BUSY_avr.", "",
+                  "| call | kernel | VALU | LDS | LDS conflicts | TD | TA | L2 hit |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for c, u in sorted(util.items()):
+            lines.append("| %s | %s | %.0f%% | %.0f%% | %.0f%% | %.0f%% | %.0f%% | %.0f%% |" % (
+                c, u["kernel"], 100 * u["valu"], 100 * u["lds"], 100 * u["lds_conflict_share"],
+                100 * u["td"], 100 * u["ta"], 100 * u["l2_hit"]))
+            if rec is not None and c in rec:
+                rec[c]["utilization"] = u
     for folder in args.counters:
         tots = _counter_totals(folder)
         names = sorted(tots)
@@ -802,10 +863,14 @@ def main():
                      "frac_beyond_l2": d["frac_beyond_l2"],
                      "compulsory_bytes": d["compulsory_bytes"],
                      "frac_compulsory": d["frac_compulsory"],
+                     "limiter": None if prune is not None else limiter_from_profile(
+                         dominant, args.config, source_sha(*CALL_SOURCES[dominant])),
                      "note": "achieved = algorithmic bytes (every sparse entry the method "
-                             "touches, re-reads counted) / mean call time; frac_beyond_l2 = "
-                             "rocprofv3 FETCH_SIZE + WRITE_SIZE per call (HBM and MALL) / time "
-                             "/ peak; frac_compulsory = every input read once / time / peak"},
+                             "touches, re-reads counted) / mean call time, so frac > 1 means "
+                             "re-reads served on chip; frac_beyond_l2 = rocprofv3 FETCH_SIZE + "
+                             "WRITE_SIZE per call (HBM and MALL) / time / peak; frac_compulsory "
+                             "= every input read once / time / peak; limiter = the busiest unit "
+                             "of the call's main kernel in the committed counters"},
         "calls": calls,
         "kernels_ms": {c: float(np.mean(v)) for c, v in per.items()},
         "kernels_ms_median": {c: _median(v) for c, v in per.items()},
