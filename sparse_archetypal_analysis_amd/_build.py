@@ -29,7 +29,7 @@ def stale() -> bool:
         return True
     t = os.path.getmtime(LIB)
     deps = sources() + [os.path.join(CSRC, h) for h in HEADERS] + \
-        [os.path.join(ROOT, "include", h) for h in ("seacells_fw.h", "seacells_sparse.h")]
+        [os.path.join(ROOT, "include", h) for h in ("seacells_fw.h", "seacells_sparse.h", "seacells_debug.h")]
     return any(os.path.getmtime(d) > t for d in deps)
 
 

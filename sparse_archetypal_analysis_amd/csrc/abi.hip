@@ -7,9 +7,9 @@
 #include <cstring>
 #include <mutex>
 
-#include "../../include/seacells_debug.h"
-#include "../../include/seacells_fw.h"
-#include "../../include/seacells_sparse.h"
+#include "seacells_debug.h"
+#include "seacells_fw.h"
+#include "seacells_sparse.h"
 #include "common.hpp"
 
 namespace seacells {

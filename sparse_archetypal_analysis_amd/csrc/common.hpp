@@ -174,8 +174,11 @@ struct BPlan {
   bool dual;
   uint32_t pa_ch;         // entries per chunk (64), 0 without the copy
   uint64_t pa_chunks;     // bound on the chunks of all runs, chunk 0 included
+  // narrow slices also place each slice's columns in the accumulator in an
+  // order of their own (two walk vectors of k floats, then the column ->
+  // position and position -> column tables, 16-bit, slice-local)
   size_t off_keys, off_part2, off_gap, off_stamp, off_work, off_seg, off_rs, off_pa_seg,
-      off_pa_ent, off_pc_col, off_pc_val;
+      off_pa_ent, off_pc_col, off_pc_val, off_walk, off_cpos, off_pcol;
   size_t ws_bytes;
 };
 BPlan plan_b(uint32_t n, uint32_t k, uint64_t aat_nnz);

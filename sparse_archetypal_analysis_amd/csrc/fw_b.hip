@@ -49,6 +49,8 @@ constexpr uint64_t kKeysBudget = 1ull << 31;  // bytes of partial keys beyond wh
 constexpr uint32_t kAccPad = 32;             // dummy slots after each dual accumulator
 constexpr uint32_t kStageSlots = kWave + 8;  // LDS staging per wave, in 16-byte slots
 constexpr uint32_t kChunkSlots = 2 * kStageSlots - 16;  // (chunk, value) pairs per window
+constexpr uint32_t kWalkSteps = 32;   // random-walk steps behind the in-slice column order
+constexpr uint32_t kOrderMax = 2048;  // widest slice the order kernel sorts
 
 // base[byte_off / 4] with a 32-bit byte offset from a wave-uniform base (the
 // array must hold fewer than 2^30 entries)
@@ -139,6 +141,99 @@ __global__ void __launch_bounds__(256)
     rs[e] = lo;
   }
   if (flags != 0) atomicOr(status, flags);
+}
+
+// ---------------------------------------------------------------------------
+// In-slice column order (narrow slices). Where a column sits in the slice
+// accumulator does not change any sum (the chunked copy keeps every run's
+// entries in the same chunks and order; only the LDS word each one is added
+// to moves), but it sets the LDS bank conflicts of the scatter: the runs of
+// AAt are neighbour sets of archetypes, so placing archetypes that share
+// neighbours next to each other turns a run's columns into few stretches of
+// consecutive words. The order comes from power iteration clustering (Lin
+// and Cohen, "Power Iteration Clustering", ICML 2010): a start vector of
+// hashed column numbers, kWalkSteps steps of the random walk over AAt,
+// x <- D^-1 AAt x, which averages x within groups of archetypes that share
+// much AAt mass long before it averages across groups; each slice then sorts
+// its columns by x (column number on ties). Every step is a fixed-order
+// computation, so the order is a function of AAt alone.
+
+// the start vector: a 32-bit integer mix of the column number (the
+// murmur3 finaliser), scaled to [0, 1)
+__device__ __forceinline__ float walk_start(uint32_t c) {
+  uint32_t x = c * 0x9E3779B1u + 1u;
+  x ^= x >> 16;
+  x *= 0x85ebca6bu;
+  x ^= x >> 13;
+  x *= 0xc2b2ae35u;
+  x ^= x >> 16;
+  return (float)x * 0x1p-32f;
+}
+
+// One step, one wave per row m: y[m] = sum_c AAt[m,c] x[c] / sum_c AAt[m,c]
+// (x = nullptr: the start vector). A row without mass, or malformed (the
+// chunked copy reports those), keeps its value.
+__global__ void __launch_bounds__(256)
+    col_walk_kernel(Csr aat, uint32_t k, const float *__restrict__ x, float *__restrict__ y) {
+  const uint32_t lane = lane_id();
+  const uint32_t nw = gridDim.x * (blockDim.x / kWave);
+  for (uint32_t m = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; m < k; m += nw) {
+    uint32_t lo, hi;
+    if (!row_ok(aat, m, lo, hi)) lo = hi = 0;
+    float sx = 0.0f, sv = 0.0f;
+    for (uint32_t q = lo + lane; q < hi; q += kWave) {
+      const uint32_t c = aat.idx[q];
+      if (c < k) {
+        const float v = aat.val[q];
+        sx = __builtin_fmaf(v, x != nullptr ? x[c] : walk_start(c), sx);
+        sv += v;
+      }
+    }
+    sx = wave_sum_f32(sx);
+    sv = wave_sum_f32(sv);
+    if (lane == 0) {
+      const float own = x != nullptr ? x[m] : walk_start(m);
+      const float r = sx / sv;
+      y[m] = (sv > 0.0f && r == r) ? r : own;
+    }
+  }
+}
+
+// One block per slice: sort the slice's columns by (order key of x, column)
+// in LDS (bitonic, a power of two >= the slice width, <= kOrderMax), then
+// cpos[c] = position of column c in its slice, pcol[s * slice_w + p] =
+// slice-local column at position p. Every column gets a position below the
+// slice's width (the padding keys sort last).
+__global__ void __launch_bounds__(1024)
+    slice_order_kernel(const float *__restrict__ x, uint32_t k, uint32_t slice_w,
+                       uint16_t *__restrict__ cpos, uint16_t *__restrict__ pcol) {
+  __shared__ uint64_t key[kOrderMax];
+  const uint32_t s = blockIdx.x;
+  const uint32_t c0 = s * slice_w;
+  const uint32_t cw = (k - c0) < slice_w ? (k - c0) : slice_w;
+  uint32_t len = 1;
+  while (len < cw) len <<= 1;
+  for (uint32_t j = threadIdx.x; j < len; j += blockDim.x)
+    key[j] = j < cw ? ((uint64_t)f32_order(x[c0 + j]) << 32) | j : ~0ull;
+  __syncthreads();
+  for (uint32_t size = 2; size <= len; size <<= 1) {
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      for (uint32_t j = threadIdx.x; j < len; j += blockDim.x) {
+        const uint32_t o = j ^ stride;
+        if (o > j) {
+          const bool up = (j & size) == 0;
+          const uint64_t a = key[j], b = key[o];
+          if ((a > b) == up) key[j] = b, key[o] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (uint32_t p = threadIdx.x; p < cw; p += blockDim.x) {
+    const uint32_t j = (uint32_t)key[p];
+    cpos[c0 + j] = (uint16_t)p;
+    pcol[(size_t)s * slice_w + p] = (uint16_t)j;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -252,23 +347,34 @@ __global__ void __launch_bounds__(256)
 // Chunked copy of AAt for the narrow-slice gather (two half-waves, one run
 // each). The run of AAt row m inside slice s takes ceil(len / 32) chunks of
 // 32 entries starting at chunk pc_seg[s * k + m] (the chunk table is built by
-// pa_seg_kernel with chunks of 32): the entries' columns within the slice as
-// 16-bit words in pc_col and their values in pc_val, so one half-wave load
-// reads exactly one 64-byte run of columns and one 128-byte run of values.
-// Positions past the run hold column 0xffff (the gather sends it to the
-// lane's dummy slot) and value 0; chunk 0 is all padding (empty runs read
-// it). One wave per run.
+// pa_seg_kernel with chunks of 32): the accumulator positions of the entries'
+// columns (cpos, the in-slice order) as 16-bit words in pc_col and their
+// values in pc_val, so one half-wave load reads exactly one 64-byte run of
+// positions and one 128-byte run of values. A run's entries are stored in
+// ascending position, so each chunk of a long run covers few stretches of
+// consecutive accumulator words. Positions past the run hold 0xffff (the
+// gather sends it to the lane's dummy slot) and value 0; chunk 0 is all
+// padding (empty runs read it). One wave per run: the run's positions go
+// into a bitmap of the slice (at most kOrderMax bits, two per lane), and an
+// entry's place is the number of set bits below its own. A column outside
+// the slice, or one that appears twice, raises BAD_INDEX.
 constexpr uint32_t kPcCh = 32;
+constexpr uint32_t kOrderWords = kOrderMax / 32;  // bitmap words per wave
+static_assert(kOrderWords == kWave, "one bitmap word per lane");
 
 __global__ void __launch_bounds__(256)
     pc_fill_kernel(Csr aat, const uint32_t *__restrict__ seg, uint32_t k, uint32_t n_slices,
                    uint32_t slice_w, const uint32_t *__restrict__ pc_seg,
-                   uint16_t *__restrict__ pc_col, float *__restrict__ pc_val,
-                   uint32_t *__restrict__ status) {
+                   const uint16_t *__restrict__ cpos, uint16_t *__restrict__ pc_col,
+                   float *__restrict__ pc_val, uint32_t *__restrict__ status) {
   const uint32_t lane = lane_id();
   const uint64_t nw = (uint64_t)gridDim.x * (blockDim.x / kWave);
   const uint64_t total_runs = (uint64_t)k * n_slices;
   const uint64_t first = (uint64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  __shared__ uint32_t bits_all[4][kOrderWords];
+  __shared__ uint32_t below_all[4][kOrderWords];
+  uint32_t *bits = bits_all[(threadIdx.x / kWave) & 3u];
+  uint32_t *below = below_all[(threadIdx.x / kWave) & 3u];
   if (first == 0 && lane < kPcCh) pc_col[lane] = 0xffffu, pc_val[lane] = 0.0f;
   uint32_t flags = 0;
   for (uint64_t e = first; e < total_runs; e += nw) {
@@ -281,19 +387,45 @@ __global__ void __launch_bounds__(256)
     uint32_t len = run_of(aat, seg, k, s, m, lo, bad);
     const uint64_t room = (uint64_t)(q1 - q0) * kPcCh;  // 0 when the runs were left empty
     if (len > room) len = (uint32_t)room;
-    for (uint32_t i = lane; i < room; i += kWave) {
-      uint16_t c16 = 0xffffu;
-      float v = 0.0f;
-      if (i < len) {
-        const uint32_t c = aat.idx[lo + i] - c0;
-        if (c < cw)
-          c16 = (uint16_t)c, v = aat.val[lo + i];
-        else
-          flags |= kFlagBadIndex;
+    float *vals = pc_val + (size_t)q0 * kPcCh;
+    uint16_t *cols = pc_col + (size_t)q0 * kPcCh;
+    // the run's positions as a bitmap of the slice
+    bits[lane] = 0u;
+    wave_lds_sync();
+    for (uint32_t i = lane; i < len; i += kWave) {
+      const uint32_t c = aat.idx[lo + i] - c0;
+      if (c < cw) {
+        const uint32_t pos = cpos[c0 + c];
+        const uint32_t bit = 1u << (pos & 31u);
+        if (atomicOr(bits + (pos >> 5), bit) & bit) flags |= kFlagBadIndex;
+      } else {
+        flags |= kFlagBadIndex;
       }
-      pc_col[(size_t)q0 * kPcCh + i] = c16;
-      pc_val[(size_t)q0 * kPcCh + i] = v;
     }
+    wave_lds_sync();
+    // set bits below each word, and in all
+    const uint32_t own = __builtin_popcount(bits[lane]);
+    uint32_t incl = own;
+#pragma unroll
+    for (uint32_t off = 1; off < kWave; off <<= 1) {
+      const uint32_t v = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += v;
+    }
+    below[lane] = incl - own;
+    const uint32_t placed = readlane_u32(incl, kWave - 1);
+    wave_lds_sync();
+    for (uint32_t i = lane; i < len; i += kWave) {
+      const uint32_t c = aat.idx[lo + i] - c0;
+      if (c < cw) {
+        const uint32_t pos = cpos[c0 + c];
+        const uint32_t r =
+            below[pos >> 5] + __builtin_popcount(bits[pos >> 5] & ((1u << (pos & 31u)) - 1u));
+        cols[r] = (uint16_t)pos;
+        vals[r] = aat.val[lo + i];
+      }
+    }
+    for (uint32_t i = placed + lane; i < room; i += kWave) cols[i] = 0xffffu, vals[i] = 0.0f;
+    wave_lds_sync();  // the bitmap is cleared for the next run only after every lane used it
   }
   if (flags != 0) atomicOr(status, flags);
 }
@@ -308,7 +440,8 @@ __global__ void __launch_bounds__(kBThreads)
                          uint32_t slice_w, uint32_t n_slices, uint32_t n_row_blocks,
                          const uint32_t *__restrict__ seg, const uint32_t *__restrict__ pa_seg,
                          const uint2 *__restrict__ pa_ent, const uint16_t *__restrict__ pc_col,
-                         const float *__restrict__ pc_val,
+                         const float *__restrict__ pc_val, const uint16_t *__restrict__ cpos,
+                         const uint16_t *__restrict__ pcol,
                          const uint32_t *__restrict__ k2at_rs, uint64_t *__restrict__ part_key,
                          float *__restrict__ part_gap, uint32_t *__restrict__ stamps,
                          uint32_t *__restrict__ xcd_work, uint32_t epoch,
@@ -521,7 +654,7 @@ __global__ void __launch_bounds__(kBThreads)
       }
       for (uint32_t q = q0 + lane; q < q1; q += kWave) {
         const uint32_t c = k2at.idx[q] - c0;
-        if (c < cw) lds_add(acc + c, -k2at.val[q]);
+        if (c < cw) lds_add(acc + (kDual ? (uint32_t)cpos[c0 + c] : c), -k2at.val[q]);
       }
       wave_lds_sync();
       // -- gap += sum_c B[i, c] G[i, c]
@@ -530,7 +663,10 @@ __global__ void __launch_bounds__(kBThreads)
         if (!row_ok(b, i, g0, g1)) flags |= kFlagBadIndex;
         for (uint32_t q = g0 + lane; q < g1; q += kWave) {
           const uint32_t c = b.idx[q] - c0;
-          if (c < cw) gsum += b.val[q] * (kDual ? acc[c] + acc[ACC2 + c] : acc[c]);
+          if (c < cw) {
+            const uint32_t pc = kDual ? (uint32_t)cpos[c0 + c] : c;
+            gsum += b.val[q] * (kDual ? acc[pc] + acc[ACC2 + pc] : acc[pc]);
+          }
         }
       }
       // -- running minimum per column (strict `<`: lowest row wins), clear
@@ -558,14 +694,17 @@ __global__ void __launch_bounds__(kBThreads)
       wave_lds_sync();
     }
 
-    // -- this unit's partials
+    // -- this unit's partials (the minima are held by accumulator position;
+    // narrow slices write each to its column)
     uint64_t *out = part_key + (size_t)rb * k + c0;
+    const uint16_t *pc = kDual ? pcol + (size_t)sl * slice_w : nullptr;
 #pragma unroll
     for (uint32_t s4 = 0; s4 < S4; ++s4) {
       const uint32_t cb = s4 * 256 + lane * 4;
 #pragma unroll
       for (uint32_t j = 0; j < 4; ++j)
-        if (cb + j < cw) out[cb + j] = pack_key(bv[4 * s4 + j], bi[4 * s4 + j]);
+        if (cb + j < cw)
+          out[kDual ? (uint32_t)pc[cb + j] : cb + j] = pack_key(bv[4 * s4 + j], bi[4 * s4 + j]);
     }
     const float g = wave_sum_f32(gsum);
     if (lane == 0) {
@@ -734,8 +873,8 @@ template <uint32_t S4, bool kDual>
 hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
                            uint32_t k, const uint32_t *seg, const uint32_t *pa_seg,
                            const uint2 *pa_ent, const uint16_t *pc_col, const float *pc_val,
-                           const uint32_t *k2at_rs,
-                           uint64_t *keys,
+                           const uint16_t *cpos, const uint16_t *pcol,
+                           const uint32_t *k2at_rs, uint64_t *keys,
                            float *gap_part, uint32_t *stamps, uint32_t *xcd_work, uint32_t epoch,
                            uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
@@ -772,8 +911,8 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
   blocks = (blocks + kXcds - 1) / kXcds * kXcds;  // the same number of blocks on every XCD
   hipLaunchKernelGGL(deep ? k_deep : k_std, dim3((uint32_t)blocks), dim3(kBThreads), lds,
                      stream, k2b, aat, k2at, b, n, k, p.slice_w, p.n_slices, p.n_row_blocks, seg,
-                     pa_seg, pa_ent, pc_col, pc_val, k2at_rs, keys, gap_part, stamps, xcd_work, epoch,
-                     status);
+                     pa_seg, pa_ent, pc_col, pc_val, cpos, pcol, k2at_rs, keys, gap_part, stamps,
+                     xcd_work, epoch, status);
   return hipGetLastError();
 }
 
@@ -837,7 +976,7 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices, uint64_
   // slice) in all, plus chunk 0 (padding)
   const uint64_t runs = (uint64_t)k * p.n_slices;
   const uint64_t pc_chunks = (aat_nnz + kPcCh - 1) / kPcCh + runs + 1;
-  p.dual = p.n_slices > 1 && pc_chunks < (1ull << 25);
+  p.dual = p.n_slices > 1 && pc_chunks < (1ull << 25) && p.slice_w <= kOrderMax;
   p.pa_ch = p.dual ? kPcCh : kWave;
   p.pa_chunks = p.dual ? pc_chunks : (aat_nnz + kWave - 1) / kWave + runs + 1;
   p.off_pa_seg = off;
@@ -848,6 +987,12 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices, uint64_
   if (p.dual) off = align_up(off + (size_t)p.pa_chunks * kPcCh * sizeof(uint16_t), 256);
   p.off_pc_val = off;
   if (p.dual) off = align_up(off + (size_t)p.pa_chunks * kPcCh * sizeof(float), 256);
+  p.off_walk = off;
+  if (p.dual) off = align_up(off + 2 * (size_t)k * sizeof(float), 256);
+  p.off_cpos = off;
+  if (p.dual) off = align_up(off + (size_t)k * sizeof(uint16_t), 256);
+  p.off_pcol = off;
+  if (p.dual) off = align_up(off + (size_t)p.n_slices * p.slice_w * sizeof(uint16_t), 256);
   p.ws_bytes = off;
   return p;
 }
@@ -893,6 +1038,23 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
   const bool dual = p.dual;
   uint16_t *pc_col = reinterpret_cast<uint16_t *>(base + p.off_pc_col);
   float *pc_val = reinterpret_cast<float *>(base + p.off_pc_val);
+  uint16_t *cpos = dual ? reinterpret_cast<uint16_t *>(base + p.off_cpos) : nullptr;
+  uint16_t *pcol = dual ? reinterpret_cast<uint16_t *>(base + p.off_pcol) : nullptr;
+  if (dual) {
+    // the in-slice column order: the walk, then one sort per slice
+    float *walk = reinterpret_cast<float *>(base + p.off_walk);
+    const uint32_t blocks = (k + 3) / 4;  // 4 waves per block, one row each
+    const dim3 grid(blocks < 65535u ? blocks : 65535u);
+    for (uint32_t t = 0; t < kWalkSteps; ++t) {
+      const float *x = t == 0 ? nullptr : walk + (size_t)((t + 1) & 1) * k;
+      hipLaunchKernelGGL(col_walk_kernel, grid, dim3(256), 0, stream, aat, k, x,
+                         walk + (size_t)(t & 1) * k);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(slice_order_kernel, dim3(p.n_slices), dim3(1024), 0, stream,
+                       walk + (size_t)((kWalkSteps - 1) & 1) * k, k, p.slice_w, cpos, pcol);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(pa_seg_kernel, dim3(1), dim3(1024), 0, stream, aat, seg, k, p.n_slices,
                      p.pa_ch, p.pa_chunks, pa_seg, status);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -902,7 +1064,7 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
     const dim3 grid((uint32_t)(blocks < 65535u ? blocks : 65535u));
     if (dual)
       hipLaunchKernelGGL(pc_fill_kernel, grid, dim3(256), 0, stream, aat, seg, k, p.n_slices,
-                         p.slice_w, pa_seg, pc_col, pc_val, status);
+                         p.slice_w, pa_seg, cpos, pc_col, pc_val, status);
     else
       hipLaunchKernelGGL(pa_fill_kernel, grid, dim3(256), 0, stream, aat, seg, k, p.n_slices,
                          p.slice_w, p.pa_ch, 256u * p.s4, pa_seg, pa_ent, status);
@@ -914,11 +1076,11 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
 #define SEACELLS_B_CASE(S)                                                                      \
   case S:                                                                                       \
     e = dual ? launch_partials<S, true>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent,       \
-                                        pc_col, pc_val, k2at_rs, keys, gap_part, stamps, xcd_work,   \
-                                        epoch, status, stream)                                  \
+                                        pc_col, pc_val, cpos, pcol, k2at_rs, keys, gap_part,    \
+                                        stamps, xcd_work, epoch, status, stream)                \
              : launch_partials<S, false>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent,      \
-                                         pc_col, pc_val, k2at_rs, keys, gap_part, stamps, xcd_work,  \
-                                         epoch, status, stream);                                \
+                                         pc_col, pc_val, cpos, pcol, k2at_rs, keys, gap_part,   \
+                                         stamps, xcd_work, epoch, status, stream);              \
     break;
     SEACELLS_B_CASE(1)
     SEACELLS_B_CASE(2)
