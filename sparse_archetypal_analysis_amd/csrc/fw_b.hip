@@ -465,6 +465,30 @@ __global__ void __launch_bounds__(kBThreads)
   const uint32_t half = kDual ? (lane >> 5) : 0u;
   const uint32_t hl = kDual ? (lane & 31u) : lane;  // lane within its half
   float *acc_h = acc + half * ACC2;                   // this half's accumulator
+  // narrow slices: gather the staged chunks [t0, t1) (a whole number of
+  // steps), chunk s to half s % 2, kPairs per half in flight
+  auto gather_steps = [&](const uint2 *cst, uint32_t t0, uint32_t t1) {
+    for (uint32_t t = t0; t < t1; t += 2 * kPairs) {
+      uint32_t ca[kPairs];
+      float xs[kPairs], va[kPairs];
+#pragma unroll
+      for (uint32_t g = 0; g < kPairs; ++g) {
+        const uint2 cx = cst[t + 2 * g + half];
+        xs[g] = __uint_as_float(cx.y);
+        const uint32_t p = cx.x * kPcCh + hl;
+        ca[g] = load_at(pc_col, p * 2u);
+        va[g] = load_at(pc_val, p * 4u);
+      }
+      // padding entries have position 0xffff and go to this lane's dummy
+      // slot past the accumulator (positions are slice-local, so nothing
+      // lands outside it; the dummy only ever takes + 0)
+#pragma unroll
+      for (uint32_t g = 0; g < kPairs; ++g) {
+        float *q = acc_h + min(ca[g], W + hl);
+        *q = __builtin_fmaf(xs[g], va[g], *q);
+      }
+    }
+  };
 
   // Blocks are dealt to the XCDs round-robin, so block b runs on XCD
   // b % kXcds. Each XCD takes its own slices (all row blocks of them), or,
@@ -527,6 +551,7 @@ __global__ void __launch_bounds__(kBThreads)
 
     for (uint32_t i = r0; i < r1; ++i) {
       // -- acc[c] = sum_m K2B[i, m] AAt[m, c] over this slice
+      uint32_t carry = 0;  // narrow slices: staged chunks left for the next batch
       uint32_t e0, e1;
       if (!row_ok(k2b, i, e0, e1)) flags |= kFlagBadIndex;
       const uint32_t *pseg = pa_seg + (size_t)sl * k;  // the run table of this slice
@@ -549,16 +574,16 @@ __global__ void __launch_bounds__(kBThreads)
         if (nq == 0) q0 = 0;  // empty: the padding chunk (adds 0 to dummy slots)
         const uint32_t cnt = (e1 - eb) < kWave ? (e1 - eb) : kWave;
         if constexpr (kDual) {
-          // The chunks of the 64 staged runs, flattened in K2B order, are
-          // dealt alternately to the two half-waves (chunk s to half s % 2),
+          // The chunks of the row's runs, flattened in K2B order, are dealt
+          // alternately to the two half-waves (chunk s to half s % 2),
           // kPairs per half in flight: every half-wave load reads one whole
           // chunk (32 entries, one 128-byte line of values) whatever the runs'
           // lengths. Each half accumulates into its own array, so a column
           // sums its terms of the even-numbered chunks in one and of the
           // odd-numbered ones in the other, each in K2B order; the fold adds
-          // the two. Windows of kChunkSlots (chunk, K2B value) pairs go
-          // through LDS; slots past a window's end hold the padding chunk 0
-          // with coefficient 0.
+          // the two. (chunk, K2B value) pairs go through LDS in windows of
+          // at most kChunkSlots; slots past the row's last chunk hold the
+          // padding chunk 0 with coefficient 0.
           const uint32_t my_nq = lane < cnt ? nq : 0u;
           uint32_t incl = my_nq;
 #pragma unroll
@@ -569,35 +594,28 @@ __global__ void __launch_bounds__(kBThreads)
           const uint32_t pos = incl - my_nq;
           const uint32_t total = readlane_u32(incl, kWave - 1);
           uint2 *cst = reinterpret_cast<uint2 *>(stage);
-          for (uint32_t base = 0; base < total; base += kChunkSlots) {
-            const uint32_t win = (total - base) < kChunkSlots ? (total - base) : kChunkSlots;
-            for (uint32_t j = pos < base ? base - pos : 0u; j < my_nq && pos + j < base + win; ++j)
-              cst[pos + j - base] = make_uint2(q0 + j, __float_as_uint(x));
-            if (lane < 2 * kPairs) cst[win + lane] = make_uint2(0u, 0u);
+          // the row's chunk sequence runs on across its batches: a window
+          // holds the chunks carried over from the last one, then new ones;
+          // whole steps of 2 kPairs chunks are gathered and the rest (fewer
+          // than a step) is carried again, so only the row's last step
+          // holds padding
+          for (uint32_t done = 0; done < total;) {
+            const uint32_t take =
+                (total - done) < (kChunkSlots - carry) ? (total - done) : (kChunkSlots - carry);
+            for (uint32_t j = pos < done ? done - pos : 0u; j < my_nq && pos + j < done + take; ++j)
+              cst[carry + pos + j - done] = make_uint2(q0 + j, __float_as_uint(x));
             wave_lds_sync();
-            for (uint32_t t = 0; t < win; t += 2 * kPairs) {
-              uint32_t ca[kPairs];
-              float xs[kPairs], va[kPairs];
-#pragma unroll
-              for (uint32_t g = 0; g < kPairs; ++g) {
-                const uint2 cx = cst[t + 2 * g + half];
-                xs[g] = __uint_as_float(cx.y);
-                const uint32_t p = cx.x * kPcCh + hl;
-                ca[g] = load_at(pc_col, p * 2u);
-                va[g] = load_at(pc_val, p * 4u);
-              }
-              // padding entries have column 0xffff and go to this lane's dummy
-              // slot past the accumulator (columns are slice-local, so nothing
-              // lands outside it; the dummy only ever takes + 0)
-#pragma unroll
-              for (uint32_t g = 0; g < kPairs; ++g) {
-                float *q = acc_h + min(ca[g], W + hl);
-                *q = __builtin_fmaf(xs[g], va[g], *q);
-              }
-            }
+            const uint32_t avail = carry + take;
+            const uint32_t full = avail / (2 * kPairs) * (2 * kPairs);
+            gather_steps(cst, 0, full);
+            carry = avail - full;
+            uint2 left = make_uint2(0u, 0u);
+            if (lane < carry) left = cst[full + lane];
             wave_lds_sync();
+            if (lane < carry) cst[lane] = left;
+            wave_lds_sync();
+            done += take;
           }
-          wave_lds_sync();
           continue;
         }
         // kGatherRows runs in flight at a time (their first three chunks); the
@@ -640,6 +658,16 @@ __global__ void __launch_bounds__(kBThreads)
             }
           }
         }
+      }
+      if constexpr (kDual) {
+        // the row's last chunks, with padding up to a whole step
+        if (carry != 0) {
+          uint2 *cst = reinterpret_cast<uint2 *>(stage);
+          if (lane >= carry && lane < 2 * kPairs) cst[lane] = make_uint2(0u, 0u);
+          wave_lds_sync();
+          gather_steps(cst, 0, 2 * kPairs);
+        }
+        wave_lds_sync();
       }
       // -- acc[c] -= K2At[i, c] (with several slices, only this slice's run
       // of the row, from the row-slice table)
