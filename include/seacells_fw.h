@@ -206,11 +206,16 @@ int seacells_fw_a_columns_noalloc(const seacells_csr *t1, const seacells_csr *k2
  * aat_nnz: the non-zeros of A A^T). It holds the per-row-range partials
  * (8 bytes per column each; 8192 row ranges for k <= 2048, else 16384, fewer
  * when that would pass 2 GiB, at least one), one stamp and one gap partial
- * per (row range, column slice), when k > 2048 the column-slice tables of
- * A A^T (4 (k + 1) bytes per slice) and of K2At's rows (4 (n + 1) bytes per
- * slice), and, when k fits one column slice (k <= 2048), a
- * copy of A A^T with every row padded to whole chunks of 64 entries (at
- * most 8 * (aat_nnz + 64 k) bytes). Depends only on its arguments.
+ * per (row range, column slice), and a copy of A A^T made per call. When k
+ * fits one column slice (k <= 2048) the copy pads every row to whole
+ * chunks of 64 entries (at most 8 (aat_nnz + 64 k) bytes). Otherwise the
+ * columns are cut into slices of at most 1024 columns (and about 3.75 MB of
+ * A A^T each) and the workspace also holds the column-slice tables of A A^T
+ * (4 (k + 1) bytes per slice) and of K2At's rows (4 (n + 1) bytes per
+ * slice), the run table and the chunked copy of A A^T per slice (chunks of
+ * 32 entries at 6 bytes each, at most aat_nnz / 32 + k slices + 1 chunks),
+ * and the in-slice column order (12 k bytes and 2 bytes per slice column).
+ * Depends only on its arguments.
  */
 size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k, uint32_t aat_nnz);
 

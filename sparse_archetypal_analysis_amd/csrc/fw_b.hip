@@ -6,29 +6,34 @@
 //
 // Work unit = (row range, column slice). A wave owns one unit at a time:
 // per row it scatters the AAt rows named by the row's K2B entries into a
-// dense slice accumulator in LDS (four runs in flight at a time; the
-// columns of one row are unique, so one scatter instruction never
-// collides). With one slice the runs come from a copy of AAt padded to
-// whole 64-entry chunks of (accumulator offset, value), so the gather does
-// no bounds or column arithmetic; narrow slices gather two short runs per
-// instruction (one per half-wave) straight from AAt. It then subtracts the K2At
-// row, adds the row's B . G term, then folds the slice into running
-// (min, row) pairs held in registers, 4 consecutive columns per float4
-// chunk, and clears the slice.
+// dense slice accumulator in LDS (the columns of one AAt row are unique, so
+// one scatter instruction never collides), subtracts the K2At row, adds the
+// row's B . G term, then folds the slice into running (min, row) pairs held
+// in registers, 4 accumulator words per float4 chunk, and clears the slice.
 // Rows run in ascending order under a strict `<`, so the lowest row wins a
 // tie inside a unit. The unit writes one (order-preserving f32 key << 32 |
 // row) per column, which makes "lower value, then lower row" a plain u64
 // minimum for the reduce stages, and a stamp with the call's epoch.
 //
-// Slices exist so k has no ceiling: a slice holds at most 2048 columns (8
-// KB of LDS and 64 registers per lane), and a segment table
-// seg[s, m] = first position of AAt row m with column >= s * slice_w
-// hands each slice its run of every AAt row without a search.
+// Each call first copies AAt into the layout its gather reads:
+// - one slice (k <= 2048): every row padded to whole 64-entry chunks of
+//   (accumulator byte offset, value); a whole wave gathers one chunk, four
+//   runs in flight;
+// - narrow slices (k > 2048, at most 1024 columns and ~3.75 MB of AAt
+//   each, so one XCD's slices stay in its L2): every (row, slice) run in
+//   chunks of 32 (16-bit accumulator position, f32 value); the row's chunks
+//   are dealt alternately to the two half-waves, each with its own
+//   accumulator. Each slice places its columns in the accumulator in an
+//   order of their own (power iteration clustering of AAt), which keeps
+//   the scatter's LDS bank conflicts down without changing any sum.
+// A segment table seg[s, m] = first position of AAt row m with column
+// >= s * slice_w hands each slice its run of every AAt row, and a row-slice
+// table does the same for K2At's rows.
 //
 // The reduce is two kernels: stage 1 takes u64 minima over groups of row
-// ranges (coalesced over columns) and checks every stamp it consumes;
-// stage 2 finishes each column, checks that the winning row is below n,
-// and sums the gap partials in a fixed order.
+// ranges (coalesced over columns) and checks every stamp and row it
+// consumes; stage 2 finishes each column, checks that the winning row is
+// below n, and sums the gap partials in a fixed order.
 #include "common.hpp"
 
 namespace seacells {
@@ -998,15 +1003,17 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices, uint64_
   if (p.n_slices > 1) off = align_up(off + (size_t)n * (p.n_slices + 1) * sizeof(uint32_t), 256);
   // AAt copied per slice in chunks: narrow slices gather two short runs per
   // wave instruction (one per half-wave) from chunks of 32 entries (16-bit
-  // columns and f32 values apart, addressed with 32-bit byte offsets);
-  // otherwise chunks of 64 (accumulator byte offset, value) pairs. A run of
-  // len entries takes ceil(len / ch) chunks, at most nnz / ch + 1 per (row,
-  // slice) in all, plus chunk 0 (padding)
+  // accumulator positions and f32 values apart, addressed with 32-bit byte
+  // offsets); otherwise chunks of 64 (accumulator byte offset, value) pairs.
+  // A run of len entries takes ceil(len / ch) <= len / ch + 1 chunks and an
+  // empty run none, so all runs take at most nnz / ch + min(runs, nnz)
+  // chunks, plus chunk 0 (padding)
   const uint64_t runs = (uint64_t)k * p.n_slices;
-  const uint64_t pc_chunks = (aat_nnz + kPcCh - 1) / kPcCh + runs + 1;
+  const uint64_t nonempty = runs < aat_nnz ? runs : aat_nnz;
+  const uint64_t pc_chunks = (aat_nnz + kPcCh - 1) / kPcCh + nonempty + 1;
   p.dual = p.n_slices > 1 && pc_chunks < (1ull << 25) && p.slice_w <= kOrderMax;
   p.pa_ch = p.dual ? kPcCh : kWave;
-  p.pa_chunks = p.dual ? pc_chunks : (aat_nnz + kWave - 1) / kWave + runs + 1;
+  p.pa_chunks = p.dual ? pc_chunks : (aat_nnz + kWave - 1) / kWave + nonempty + 1;
   p.off_pa_seg = off;
   off = align_up(off + (runs + 1) * sizeof(uint32_t), 256);
   p.off_pa_ent = off;

@@ -182,7 +182,7 @@ def test_nonfinite_minimum_raises_flag():
 
 
 def test_large_k_many_slices():
-    # k = 300,000 needs 152 column slices of 1976 columns (the plan has no
+    # k = 300,000 needs 296 column slices of 1016 columns (the plan has no
     # slice ceiling); a few hundred rows keep the oracle quick
     import scipy.sparse as sp
     rng = np.random.default_rng(79)
@@ -208,3 +208,20 @@ def test_large_k_many_slices():
     assert flags == []
     rep = parity.check_b(w, v, i, g)
     print("\nk=300000: %s" % (rep,))
+
+
+def test_sliced_copy_flags_a_repeated_aat_column():
+    # the narrow-slice copy ranks each run's entries by accumulator position;
+    # a column that appears twice in an AAt row (its indices must be
+    # strictly ascending) is reported instead of being dropped silently
+    w = W.random_workload(300, 5000, aat_per_row=30, k2b_per_row=12, k2at_per_row=10,
+                          b_per_col=3, seed=62)
+    assert saa.seacells_debug_b_layout(w.n, w.k, w.aat.nnz)["n_slices"] > 1
+    ops = (dev(w.k2b), dev(w.aat), dev(w.k2at), dev(w.b))
+    *_, flags = run_b(w, ops=ops)
+    assert flags == []
+    lo = int(w.aat.indptr[7])
+    assert int(w.aat.indptr[8]) - lo >= 2
+    ops[1].col_idx[lo + 1] = ops[1].col_idx[lo]
+    *_, flags = run_b(w, ops=ops)
+    assert flags == ["BAD_INDEX"]
