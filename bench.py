@@ -634,9 +634,9 @@ class HotPath:
 
     def b_apply(self, stream, t):
         # the B loop's step index continues after the workload's s_B prior steps
+        gamma, _ = self.saa.seacells_fw_step_size(self.w.cfg.s_b + 1 + t)
         self.saa.seacells_fw_b_apply(self.bt_idx, self.bt_val, self.bt_cnt, self.w.n,
-                                     self.out_idx, 2.0 / (self.w.cfg.s_b + 1 + t + 2),
-                                     status=self.st_p, stream=stream)
+                                     self.out_idx, gamma, status=self.st_p, stream=stream)
 
     def raise_on_status(self):
         for st in (self.st_a, self.st_b, self.st_p):

@@ -271,6 +271,16 @@ int seacells_fw_b_apply(uint32_t *bt_idx, float *bt_val, uint32_t *bt_cnt, uint3
                         uint32_t k, uint32_t cap_b, const uint32_t *arg_idx, float gamma,
                         uint32_t *status, seacells_stream_t stream);
 
+/*
+ * The default Frank-Wolfe step of step t (from 0), on the host: *gamma =
+ * 2 / (t + 2) and *keep = 1 - *gamma, both in f32 with IEEE division and
+ * subtraction, the values the A update computes on the device when it has no
+ * step-size table (the page's `fw_columns_a_gpu` loop; the B loop steps every
+ * column with the same schedule). Either pointer may be NULL. Returns
+ * SEACELLS_OK.
+ */
+int seacells_fw_step_size(uint32_t t, float *gamma, float *keep);
+
 /* Static text for a SEACELLS_E_* code. */
 const char *seacells_status_string(int code);
 

@@ -19,4 +19,5 @@ from .native import (DeviceCSR, SeacellsError, load, new_status, raise_on_status
                      seacells_fw_a_to_csr_workspace, seacells_fw_a_to_csr_rows,
                      seacells_fw_a_to_csr_fill, fw_a_to_csr, outer_iteration, csr_trim,
                      seacells_debug_set_a_options, seacells_debug_b_layout,
-                     seacells_debug_b_last_epoch, seacells_debug_b_reduce, status_flags)
+                     seacells_debug_b_last_epoch, seacells_debug_b_reduce, status_flags,
+                     seacells_fw_step_size)

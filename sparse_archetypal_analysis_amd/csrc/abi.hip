@@ -544,6 +544,13 @@ const char *seacells_status_string(int code) {
 
 const char *seacells_last_error(void) { return g_last_error; }
 
+int seacells_fw_step_size(uint32_t t, float *gamma, float *keep) {
+  const float g = 2.0f / (float)(t + 2u);
+  if (gamma != nullptr) *gamma = g;
+  if (keep != nullptr) *keep = 1.0f - g;
+  return SEACELLS_OK;
+}
+
 int seacells_version(void) { return (1 << 16) | 0; }
 
 }  // extern "C"

@@ -36,6 +36,7 @@ EXPORTS = ("seacells_fw_a_columns_workspace", "seacells_fw_a_columns",
            "seacells_fw_a_to_csr_fill",
            "seacells_debug_set_a_options", "seacells_debug_b_layout",
            "seacells_debug_b_last_epoch", "seacells_debug_b_reduce",
+           "seacells_fw_step_size",
            "seacells_status_string", "seacells_last_error", "seacells_version")
 
 
@@ -154,6 +155,9 @@ def load():
     lib.seacells_last_error.argtypes = []
     lib.seacells_version.restype = ctypes.c_int
     lib.seacells_version.argtypes = []
+    lib.seacells_fw_step_size.restype = ctypes.c_int
+    lib.seacells_fw_step_size.argtypes = [ctypes.c_uint32, ctypes.POINTER(ctypes.c_float),
+                                          ctypes.POINTER(ctypes.c_float)]
     _lib = lib
     return lib
 
@@ -720,6 +724,13 @@ def seacells_fw_b_vertex(arg_idx, n: int, value: float = 1.0, workspace=None, st
     return DeviceCSR(s_ptr, s_idx, s_val, (n, k))
 
 
+def seacells_fw_step_size(t: int):
+    """(gamma_t, 1 - gamma_t) of the default schedule, as f32 values."""
+    g, keep = ctypes.c_float(), ctypes.c_float()
+    _check_rc(load().seacells_fw_step_size(t, ctypes.byref(g), ctypes.byref(keep)))
+    return g.value, keep.value
+
+
 def fw_b_loop(K: DeviceCSR, k2b: DeviceCSR, aat: DeviceCSR, k2at: DeviceCSR, b: DeviceCSR,
               steps: int, gammas=None, status=None, stream=None):
     """``steps`` Frank-Wolfe steps of the B update on the device, A fixed.
@@ -749,13 +760,17 @@ def fw_b_loop(K: DeviceCSR, k2b: DeviceCSR, aat: DeviceCSR, k2at: DeviceCSR, b: 
     b_out, k_out = (OutBuffers(), OutBuffers()), (OutBuffers(), OutBuffers())
     kw = dict(status=status, stream=stream)
     for t in range(steps):
-        g = 2.0 / (t + 2.0) if gammas is None else float(gammas[t])
+        if gammas is None:
+            g, keep = seacells_fw_step_size(t)
+        else:  # a caller's table: its entries as given
+            g = float(gammas[t])
+            keep = 1.0 - g
         seacells_fw_b_argmin(k2b, aat, k2at, b, n, k, out_val=mins[t], out_idx=picks[t],
                              gap=gaps[t:t + 1], workspace=ws_b, **kw)
         S = seacells_fw_b_vertex(picks[t], n, 1.0, workspace=ws_v, **kw)
-        b = csr_add(1.0 - g, b, g, S, out=b_out[t % 2], **kw)
+        b = csr_add(keep, b, g, S, out=b_out[t % 2], **kw)
         k2s = csr_matmul(K, csr_matmul(K, S, **kw), **kw)
-        k2b = csr_add(1.0 - g, k2b, g, k2s, out=k_out[t % 2], **kw)
+        k2b = csr_add(keep, k2b, g, k2s, out=k_out[t % 2], **kw)
     raise_on_status(status)
     return b, k2b, picks, mins, gaps
 

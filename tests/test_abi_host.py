@@ -296,3 +296,14 @@ def test_debug_hooks_reject_bad_options():
     assert saa.seacells_fw_a_columns_workspace(1000, 6700, 50, 62, 10) == base
     assert lib.seacells_debug_b_layout(0, 5, 0, ctypes.byref(native.seacells_b_layout())) == -2
     assert lib.seacells_debug_b_reduce(10, 5, 0, 1, None, None, None, None, 0, None, None) == -1
+
+
+def test_default_step_size_in_f32():
+    import numpy as np
+    # gamma_t = 2 / (t + 2) and 1 - gamma_t, each rounded once to f32
+    for t in (0, 1, 2, 3, 7, 48, 49, 1000, 2**31):
+        g, keep = saa.seacells_fw_step_size(t)
+        want = np.float32(2.0) / np.float32(t + 2)
+        assert np.float32(g) == want
+        assert np.float32(keep) == np.float32(1.0) - want
+    assert saa.seacells_fw_step_size(0) == (1.0, 0.0)
