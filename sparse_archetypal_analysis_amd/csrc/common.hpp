@@ -179,6 +179,12 @@ struct BPlan {
   // position and position -> column tables, 16-bit, slice-local)
   size_t off_keys, off_part2, off_gap, off_stamp, off_work, off_seg, off_rs, off_pa_seg,
       off_pa_ent, off_pc_col, off_pc_val, off_walk, off_cpos, off_pcol;
+  // narrow slices, more than one per XCD: the slices each XCD owns, chosen
+  // per call to even out the XCDs' gather work (a K2B column histogram, the
+  // work of every slice, then the slices of XCD x at
+  // xcd_list[xcd_off[x] .. xcd_off[x + 1]))
+  bool balance;
+  size_t off_hist, off_swork, off_xcd_off, off_xcd_list;
   size_t ws_bytes;
 };
 BPlan plan_b(uint32_t n, uint32_t k, uint64_t aat_nnz);

@@ -56,6 +56,8 @@ constexpr uint32_t kStageSlots = kWave + 8;  // LDS staging per wave, in 16-byte
 constexpr uint32_t kChunkSlots = 2 * kStageSlots - 16;  // (chunk, value) pairs per window
 constexpr uint32_t kWalkSteps = 32;   // random-walk steps behind the in-slice column order
 constexpr uint32_t kOrderMax = 2048;  // widest slice the order kernel sorts
+constexpr uint32_t kBalanceMax = 4096;  // most slices the XCD assignment sorts
+constexpr uint32_t kHistRowStep = 16;   // K2B rows sampled for the column histogram
 
 // base[byte_off / 4] with a 32-bit byte offset from a wave-uniform base (the
 // array must hold fewer than 2^30 entries)
@@ -238,6 +240,110 @@ __global__ void __launch_bounds__(1024)
     const uint32_t j = (uint32_t)key[p];
     cpos[c0 + j] = (uint16_t)p;
     pcol[(size_t)s * slice_w + p] = (uint16_t)j;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Which XCD owns which slice (narrow slices, n_slices > kXcds). An XCD
+// gathers only its own slices (their AAt stays in its L2), so the kernel
+// ends when the XCD with the most work does. The work of slice s is close
+// to sum_m ref(m) nq(m, s): ref(m) = the K2B entries with column m (counted
+// on every kHistRowStep-th row), nq(m, s) = the chunks of AAt row m in slice
+// s (from the run table). The slices are dealt longest first, each to the
+// XCD with the least work so far (ties: the lower XCD). Only the speed
+// depends on the assignment: every unit writes its own partials.
+
+// hist[m] += 1 for every entry of column m in the sampled rows; one wave per
+// row, grid-stride
+__global__ void __launch_bounds__(256)
+    ref_hist_kernel(Csr k2b, uint32_t n, uint32_t k, uint32_t *__restrict__ hist) {
+  const uint32_t lane = lane_id();
+  const uint32_t nw = gridDim.x * (blockDim.x / kWave);
+  for (uint32_t j = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+       (uint64_t)j * kHistRowStep < n; j += nw) {
+    uint32_t lo, hi;
+    if (!row_ok(k2b, j * kHistRowStep, lo, hi)) continue;
+    for (uint32_t q = lo + lane; q < hi; q += kWave) {
+      const uint32_t m = k2b.idx[q];
+      if (m < k) atomicAdd(hist + m, 1u);
+    }
+  }
+}
+
+// One block per slice: swork[s] = sum_m hist[m] * nq(m, s)
+__global__ void __launch_bounds__(256)
+    slice_work_kernel(const uint32_t *__restrict__ hist, const uint32_t *__restrict__ pa_seg,
+                      uint32_t k, uint64_t *__restrict__ swork) {
+  __shared__ uint64_t part[256];
+  const uint32_t s = blockIdx.x;
+  const uint32_t *ps = pa_seg + (size_t)s * k;
+  uint64_t sum = 0;
+  for (uint32_t m = threadIdx.x; m < k; m += blockDim.x) {
+    const uint32_t q0 = ps[m], q1 = ps[m + 1];
+    sum += (uint64_t)hist[m] * (q1 > q0 ? q1 - q0 : 0u);
+  }
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  for (uint32_t off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) part[threadIdx.x] += part[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) swork[s] = part[0];
+}
+
+// One block: sort the slices by work (most first, lower slice on ties),
+// deal them longest first, then list each XCD's slices in that order.
+__global__ void __launch_bounds__(1024)
+    xcd_assign_kernel(const uint64_t *__restrict__ swork, uint32_t n_slices,
+                      uint32_t *__restrict__ xcd_off, uint32_t *__restrict__ xcd_list) {
+  __shared__ uint64_t key[kBalanceMax];
+  __shared__ uint8_t owner[kBalanceMax];
+  uint32_t len = 1;
+  while (len < n_slices) len <<= 1;
+  for (uint32_t j = threadIdx.x; j < len; j += blockDim.x) {
+    uint64_t kj = ~0ull;
+    if (j < n_slices) {
+      const uint64_t w = swork[j] >> 8;  // 24 bits of headroom; the order is what matters
+      const uint32_t w32 = w > 0xffffffffull ? 0xffffffffu : (uint32_t)w;
+      kj = ((uint64_t)(0xffffffffu - w32) << 32) | j;
+    }
+    key[j] = kj;
+  }
+  __syncthreads();
+  for (uint32_t size = 2; size <= len; size <<= 1) {
+    for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      for (uint32_t j = threadIdx.x; j < len; j += blockDim.x) {
+        const uint32_t o = j ^ stride;
+        if (o > j) {
+          const bool up = (j & size) == 0;
+          const uint64_t a = key[j], b = key[o];
+          if ((a > b) == up) key[j] = b, key[o] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  if (threadIdx.x == 0) {
+    uint64_t load[kXcds];
+    uint32_t count[kXcds];
+    for (uint32_t x = 0; x < kXcds; ++x) load[x] = 0, count[x] = 0;
+    for (uint32_t r = 0; r < n_slices; ++r) {
+      const uint32_t s = (uint32_t)key[r];
+      uint32_t best = 0;
+      for (uint32_t x = 1; x < kXcds; ++x)
+        if (load[x] < load[best]) best = x;
+      owner[r] = (uint8_t)best;
+      load[best] += swork[s] + 1;  // + 1: an empty slice still costs its units
+      ++count[best];
+    }
+    uint32_t at = 0;
+    for (uint32_t x = 0; x < kXcds; ++x) {
+      xcd_off[x] = at;
+      at += count[x];
+      count[x] = xcd_off[x];
+    }
+    xcd_off[kXcds] = at;
+    for (uint32_t r = 0; r < n_slices; ++r) xcd_list[count[owner[r]]++] = (uint32_t)key[r];
   }
 }
 
@@ -449,7 +555,8 @@ __global__ void __launch_bounds__(kBThreads)
                          const uint16_t *__restrict__ pcol,
                          const uint32_t *__restrict__ k2at_rs, uint64_t *__restrict__ part_key,
                          float *__restrict__ part_gap, uint32_t *__restrict__ stamps,
-                         uint32_t *__restrict__ xcd_work, uint32_t epoch,
+                         uint32_t *__restrict__ xcd_work, const uint32_t *__restrict__ xcd_off,
+                         const uint32_t *__restrict__ xcd_list, uint32_t epoch,
                          uint32_t *__restrict__ status) {
   constexpr uint32_t W = 256 * S4;  // accumulator columns (>= slice_w)
   // a window's padding slots stay inside the stage
@@ -496,18 +603,27 @@ __global__ void __launch_bounds__(kBThreads)
   };
 
   // Blocks are dealt to the XCDs round-robin, so block b runs on XCD
-  // b % kXcds. Each XCD takes its own slices (all row blocks of them), or,
-  // with fewer slices than XCDs, its share of the row blocks of one slice,
-  // and walks them slice after slice: the AAt columns an XCD gathers stay
-  // in its L2. (On another placement only the speed changes.)
+  // b % kXcds. Each XCD takes its own slices (all row blocks of them: the
+  // ones the assignment gave it, else every kXcds-th), or, with fewer slices
+  // than XCDs, its share of the row blocks of one slice, and walks them
+  // slice after slice: the AAt columns an XCD gathers stay in its L2. (On
+  // another placement only the speed changes.)
   const uint32_t xcd = blockIdx.x % kXcds;
-  uint32_t sl0, sl_step, rb0, rb_step;
-  if (n_slices >= kXcds) {
-    sl0 = xcd, sl_step = kXcds, rb0 = 0, rb_step = 1;
+  uint32_t sl0, sl_step, rb0, rb_step, my_sl;
+  const uint32_t *my_list = nullptr;
+  if (xcd_off != nullptr) {
+    const uint32_t o0 = xcd_off[xcd], o1 = xcd_off[xcd + 1];
+    my_list = xcd_list + o0;
+    my_sl = o1 > o0 ? o1 - o0 : 0u;
+    sl0 = 0, sl_step = 1, rb0 = 0, rb_step = 1;
   } else {
-    sl0 = xcd % n_slices, sl_step = kXcds, rb0 = xcd / n_slices, rb_step = kXcds / n_slices;
+    if (n_slices >= kXcds) {
+      sl0 = xcd, sl_step = kXcds, rb0 = 0, rb_step = 1;
+    } else {
+      sl0 = xcd % n_slices, sl_step = kXcds, rb0 = xcd / n_slices, rb_step = kXcds / n_slices;
+    }
+    my_sl = sl0 < n_slices ? (n_slices - sl0 + sl_step - 1) / sl_step : 0u;
   }
-  const uint32_t my_sl = sl0 < n_slices ? (n_slices - sl0 + sl_step - 1) / sl_step : 0u;
   const uint32_t my_rb = rb0 < n_row_blocks ? (n_row_blocks - rb0 + rb_step - 1) / rb_step : 0u;
   const uint32_t my_units = my_sl * my_rb;
   const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -541,7 +657,14 @@ __global__ void __launch_bounds__(kBThreads)
     if (u >= my_units) break;
     const uint32_t js = u / my_rb;
     const uint32_t rb = rb0 + (u - js * my_rb) * rb_step;
-    const uint32_t sl = sl0 + js * sl_step;
+    uint32_t sl = sl0 + js * sl_step;
+    if (my_list != nullptr) {
+      sl = my_list[js];
+      if (sl >= n_slices) {  // an assignment out of range: skip it (the reduce reports it)
+        flags |= kFlagBadIndex;
+        continue;
+      }
+    }
     const uint32_t unit = rb * n_slices + sl;
     const uint32_t c0 = sl * slice_w;
     const uint32_t cw = (k - c0) < slice_w ? (k - c0) : slice_w;
@@ -902,13 +1025,20 @@ __global__ void zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
   if (threadIdx.x < count) p[threadIdx.x] = 0u;
 }
 
+__global__ void __launch_bounds__(256)
+    fill_zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) p[i] = 0u;
+}
+
 template <uint32_t S4, bool kDual>
 hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32_t n,
                            uint32_t k, const uint32_t *seg, const uint32_t *pa_seg,
                            const uint2 *pa_ent, const uint16_t *pc_col, const float *pc_val,
                            const uint16_t *cpos, const uint16_t *pcol,
                            const uint32_t *k2at_rs, uint64_t *keys,
-                           float *gap_part, uint32_t *stamps, uint32_t *xcd_work, uint32_t epoch,
+                           float *gap_part, uint32_t *stamps, uint32_t *xcd_work,
+                           const uint32_t *xcd_off, const uint32_t *xcd_list, uint32_t epoch,
                            uint32_t *status, hipStream_t stream) {
   DeviceInfo dev;
   hipError_t e = device_info(&dev);
@@ -945,7 +1075,7 @@ hipError_t launch_partials(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, ui
   hipLaunchKernelGGL(deep ? k_deep : k_std, dim3((uint32_t)blocks), dim3(kBThreads), lds,
                      stream, k2b, aat, k2at, b, n, k, p.slice_w, p.n_slices, p.n_row_blocks, seg,
                      pa_seg, pa_ent, pc_col, pc_val, cpos, pcol, k2at_rs, keys, gap_part, stamps,
-                     xcd_work, epoch, status);
+                     xcd_work, xcd_off, xcd_list, epoch, status);
   return hipGetLastError();
 }
 
@@ -1028,6 +1158,17 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices, uint64_
   if (p.dual) off = align_up(off + (size_t)k * sizeof(uint16_t), 256);
   p.off_pcol = off;
   if (p.dual) off = align_up(off + (size_t)p.n_slices * p.slice_w * sizeof(uint16_t), 256);
+  // the XCDs' slices, when some XCD owns more than one (with one slice each
+  // there is nothing to even out)
+  p.balance = p.dual && p.n_slices > kXcds && p.n_slices <= kBalanceMax;
+  p.off_hist = off;
+  if (p.balance) off = align_up(off + (size_t)k * sizeof(uint32_t), 256);
+  p.off_swork = off;
+  if (p.balance) off = align_up(off + (size_t)p.n_slices * sizeof(uint64_t), 256);
+  p.off_xcd_off = off;
+  if (p.balance) off = align_up(off + (kXcds + 1) * sizeof(uint32_t), 256);
+  p.off_xcd_list = off;
+  if (p.balance) off = align_up(off + (size_t)p.n_slices * sizeof(uint32_t), 256);
   p.ws_bytes = off;
   return p;
 }
@@ -1105,6 +1246,31 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
                          p.slice_w, p.pa_ch, 256u * p.s4, pa_seg, pa_ent, status);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // which XCD owns which slice
+  const uint32_t *xcd_off = nullptr, *xcd_list = nullptr;
+  if (p.balance) {
+    uint32_t *hist = reinterpret_cast<uint32_t *>(base + p.off_hist);
+    uint64_t *swork = reinterpret_cast<uint64_t *>(base + p.off_swork);
+    uint32_t *off = reinterpret_cast<uint32_t *>(base + p.off_xcd_off);
+    uint32_t *list = reinterpret_cast<uint32_t *>(base + p.off_xcd_list);
+    const uint32_t zb = (k + 255) / 256;
+    hipLaunchKernelGGL(fill_zero_u32_kernel, dim3(zb < 4096u ? zb : 4096u), dim3(256), 0, stream,
+                       hist, k);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const uint64_t sampled = ((uint64_t)n + kHistRowStep - 1) / kHistRowStep;
+    const uint64_t hb = (sampled + 3) / 4;  // 4 waves per block, one row each
+    hipLaunchKernelGGL(ref_hist_kernel, dim3((uint32_t)(hb < 16384u ? (hb > 0 ? hb : 1) : 16384u)),
+                       dim3(256), 0, stream, k2b, n, k, hist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(slice_work_kernel, dim3(p.n_slices), dim3(256), 0, stream, hist, pa_seg,
+                       k, swork);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(xcd_assign_kernel, dim3(1), dim3(1024), 0, stream, swork, p.n_slices, off,
+                       list);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    xcd_off = off;
+    xcd_list = list;
+  }
   hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, xcd_work, kXcds);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   switch (p.s4) {
@@ -1112,10 +1278,12 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
   case S:                                                                                       \
     e = dual ? launch_partials<S, true>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent,       \
                                         pc_col, pc_val, cpos, pcol, k2at_rs, keys, gap_part,    \
-                                        stamps, xcd_work, epoch, status, stream)                \
+                                        stamps, xcd_work, xcd_off, xcd_list, epoch, status,     \
+                                        stream)                                                 \
              : launch_partials<S, false>(p, k2b, aat, k2at, b, n, k, seg, pa_seg, pa_ent,      \
                                          pc_col, pc_val, cpos, pcol, k2at_rs, keys, gap_part,   \
-                                         stamps, xcd_work, epoch, status, stream);              \
+                                         stamps, xcd_work, xcd_off, xcd_list, epoch, status,    \
+                                         stream);                                               \
     break;
     SEACELLS_B_CASE(1)
     SEACELLS_B_CASE(2)
