@@ -214,8 +214,9 @@ int seacells_fw_a_columns_noalloc(const seacells_csr *t1, const seacells_csr *k2
  * (4 (k + 1) bytes per slice) and of K2At's rows (4 (n + 1) bytes per
  * slice), the run table and the chunked copy of A A^T per slice (chunks of
  * 32 entries at 6 bytes each, at most aat_nnz / 32 + k slices + 1 chunks),
- * and the in-slice column order (12 k bytes and 2 bytes per slice column).
- * Depends only on its arguments.
+ * the in-slice column order (12 k bytes and 2 bytes per slice column) and,
+ * with more slices than the GPU's 8 XCDs, the slices each XCD owns (4 k +
+ * 12 bytes per slice + 36). Depends only on its arguments.
  */
 size_t seacells_fw_b_argmin_workspace(uint32_t n, uint32_t k, uint32_t aat_nnz);
 
