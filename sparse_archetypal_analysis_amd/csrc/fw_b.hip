@@ -65,7 +65,6 @@ template <typename T>
 __device__ __forceinline__ T load_at(const T *__restrict__ base, uint32_t byte_off) {
   return *reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
 }
-constexpr uint32_t kNoCol = 0xffffffffu;
 // the key a unit leaves in a column where no row gave a value below +inf
 constexpr uint64_t kNoValueKey = ((uint64_t)0xff800000u << 32) | 0xffffffffull;
 

@@ -677,7 +677,10 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
   uint32_t flags = 0;
   for (uint32_t r = blockIdx.x * kSpWaves + wib; r < m; r += gridDim.x * kSpWaves) {
     uint32_t x0, x1, y0, y1;
-    if (!sp_row(x, r, x0, x1) || !sp_row(y, r, y0, y1)) flags |= kFlagBadIndex;
+    // both ranges are always read: a malformed row of one operand leaves the
+    // other's range intact (and its own empty)
+    const bool x_ok = sp_row(x, r, x0, x1), y_ok = sp_row(y, r, y0, y1);
+    if (!x_ok || !y_ok) flags |= kFlagBadIndex;
     flags |= check_row(x, x0, x1, q, lane) | check_row(y, y0, y1, q, lane);
     // common columns: the shorter row's entries searched in the longer row
     const bool xs = x1 - x0 <= y1 - y0;
@@ -718,7 +721,10 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
       continue;
     }
     uint32_t x0, x1, y0, y1;
-    if (!sp_row(x, r, x0, x1) || !sp_row(y, r, y0, y1)) flags |= kFlagBadIndex;
+    // both ranges are always read: a malformed row of one operand leaves the
+    // other's range intact (and its own empty)
+    const bool x_ok = sp_row(x, r, x0, x1), y_ok = sp_row(y, r, y0, y1);
+    if (!x_ok || !y_ok) flags |= kFlagBadIndex;
     // place of an entry in the merged row: its rank in its own row, plus the
     // columns below it in the other row, less the common columns below it
     // (both rows ascending: the matched entries before it in its own row)
@@ -861,7 +867,10 @@ __global__ void __launch_bounds__(256)
   uint32_t flags = 0;
   for (uint32_t r = blockIdx.x * wpb + wib; r < m; r += gridDim.x * wpb) {
     uint32_t x0, x1, y0, y1;
-    if (!sp_row(x, r, x0, x1) || !sp_row(y, r, y0, y1)) flags |= kFlagBadIndex;
+    // both ranges are always read: a malformed row of one operand leaves the
+    // other's range intact (and its own empty)
+    const bool x_ok = sp_row(x, r, x0, x1), y_ok = sp_row(y, r, y0, y1);
+    if (!x_ok || !y_ok) flags |= kFlagBadIndex;
     for (uint32_t t = x0 + lane; t < x1; t += kWave) {
       const uint32_t c = x.idx[t];
       uint32_t lo = y0, hi = y1;

@@ -89,6 +89,26 @@ def test_sparse_add_keeps_cancelled_sums_and_flags_unsorted_rows():
     assert "BAD_INDEX" in saa.status_flags(st)
 
 
+def test_sparse_add_flags_a_row_pointer_past_the_entries():
+    # rows of one operand whose range runs past its entries or backwards:
+    # each operand's range is checked on its own, the bad ones count as
+    # empty, the other operand's rows stay in bounds, and the call reports it
+    x = sp.csr_matrix(np.array([[2.0, 0.0, 1.0], [0.0, 4.0, 0.0], [1.0, 1.0, 1.0]], np.float32))
+    y = sp.csr_matrix(np.array([[1.0, 1.0, 0.0], [0.0, 0.0, 5.0], [0.0, 2.0, 0.0]], np.float32))
+    for bad_first in (True, False):
+        xd, yd = dev(x), dev(y)
+        (xd if bad_first else yd).row_ptr[2] = 9  # row 1: (2, 9) past nnz; row 2: (9, 6)
+        st = saa.new_status()
+        ptr, _ = saa.seacells_csr_add_rows(xd, yd, status=st) if bad_first else \
+            saa.seacells_csr_add_rows(yd, xd, status=st)
+        torch.cuda.synchronize()
+        assert saa.status_flags(st) == ["BAD_INDEX"]
+        # row 0 is the plain sum; rows 1 and 2 keep the good operand's entries
+        counts = np.diff(ptr.cpu().numpy().astype(np.int64))
+        good = y if bad_first else x
+        assert counts[0] == 3 and list(counts[1:]) == list(np.diff(good.indptr)[1:])
+
+
 @pytest.mark.parametrize("n,k", [(1, 5), (7, 30), (100_000, 1300), (1_000_000, 10_000)])
 def test_vertex_matrix_bit_exact(n, k):
     rng = np.random.default_rng(n + k)
