@@ -225,3 +225,39 @@ def test_sliced_copy_flags_a_repeated_aat_column():
     ops[1].col_idx[lo + 1] = ops[1].col_idx[lo]
     *_, flags = run_b(w, ops=ops)
     assert flags == ["BAD_INDEX"]
+
+
+@pytest.mark.parametrize("k", [3000, 9000])
+def test_sliced_long_k2b_rows_empty_and_long_aat_rows(k):
+    # K2B rows of ~250 entries put several hundred chunks of every slice in a
+    # row (several staging windows, chunks carried from one batch to the
+    # next); every 11th AAt row and column is empty; three AAt rows of 1500
+    # entries give runs of many chunks; every 7th K2B row is empty. k = 3000
+    # takes 4 slices, k = 9000 16 (dealt to the XCDs by work).
+    import dataclasses
+    import scipy.sparse as sp
+    w = W.random_workload(300, k, k2b_per_row=250, aat_per_row=120, k2at_per_row=40,
+                          b_per_col=3, seed=83 + k, empty_k2b_every=7)
+    rng = np.random.default_rng(k)
+    coo = w.aat.tocoo()
+    keep = (coo.row % 11 != 0) & (coo.col % 11 != 0)
+    rows, cols = [coo.row[keep]], [coo.col[keep]]
+    vals = [coo.data[keep].astype(np.float64)]
+    for m in (5, 1234, k - 1):
+        c = rng.choice(k, size=1500, replace=False)
+        c = c[(c % 11 != 0) & (c != m)]
+        v = rng.uniform(0.05, 1.0, size=c.size)
+        rows += [np.full(c.size, m), c]
+        cols += [c, np.full(c.size, m)]
+        vals += [v, v]
+    a = sp.csr_matrix((np.concatenate(vals), (np.concatenate(rows), np.concatenate(cols))),
+                      shape=(k, k))
+    a.sum_duplicates()
+    w = dataclasses.replace(w, aat=W._f32(a, symmetric=True))
+    lay = saa.seacells_debug_b_layout(w.n, k, w.aat.nnz)
+    assert lay["n_slices"] == (4 if k == 3000 else 16)
+    assert np.diff(w.aat.indptr)[::11].max() == 0 and np.diff(w.aat.indptr).max() >= 1000
+    v, i, g, flags = run_b(w)
+    assert flags == []
+    rep = parity.check_b(w, v, i, g)
+    print("\nk=%d: %s" % (k, rep))
