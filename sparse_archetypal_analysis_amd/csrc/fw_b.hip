@@ -25,7 +25,7 @@
 //   are dealt alternately to the two half-waves, each with its own
 //   accumulator. Each slice places its columns in the accumulator in an
 //   order of their own (power iteration clustering of AAt), which keeps
-//   the scatter's LDS bank conflicts down without changing any sum.
+//   the scatter's LDS bank conflicts down.
 // A segment table seg[s, m] = first position of AAt row m with column
 // >= s * slice_w hands each slice its run of every AAt row, and a row-slice
 // table does the same for K2At's rows.
@@ -151,12 +151,13 @@ __global__ void __launch_bounds__(256)
 
 // ---------------------------------------------------------------------------
 // In-slice column order (narrow slices). Where a column sits in the slice
-// accumulator does not change any sum (the chunked copy keeps every run's
-// entries in the same chunks and order; only the LDS word each one is added
-// to moves), but it sets the LDS bank conflicts of the scatter: the runs of
-// AAt are neighbour sets of archetypes, so placing archetypes that share
+// accumulator sets the LDS bank conflicts of the scatter: the runs of AAt
+// are neighbour sets of archetypes, so placing archetypes that share
 // neighbours next to each other turns a run's columns into few stretches of
-// consecutive words. The order comes from power iteration clustering (Lin
+// consecutive words (the chunked copy stores each run in position order).
+// It also decides which chunk of its run, and so which of the two half-wave
+// accumulators, each term goes to; every sum stays a fixed function of the
+// operands. The order comes from power iteration clustering (Lin
 // and Cohen, "Power Iteration Clustering", ICML 2010): a start vector of
 // hashed column numbers, kWalkSteps steps of the random walk over AAt,
 // x <- D^-1 AAt x, which averages x within groups of archetypes that share
