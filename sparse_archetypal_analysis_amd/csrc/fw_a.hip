@@ -1185,8 +1185,7 @@ struct Count {
 // the dense kernel, the renormalisation is done here as the dense kernel does.
 template <uint32_t TR, bool kPrune>
 __global__ void __launch_bounds__(kABlockMaxThreads)
-    fw_a_support_kernel(const uint32_t *__restrict__ t1_ptr, const uint32_t *__restrict__ t1_idx,
-                        const float *__restrict__ t1_val, uint32_t t1_nnz,
+    fw_a_support_kernel(const uint32_t *__restrict__ pt_ptr, const uint2 *__restrict__ pt_ent,
                         const uint32_t *__restrict__ k2b_ptr, const uint32_t *__restrict__ k2b_idx,
                         const float *__restrict__ k2b_val, uint32_t k2b_nnz,
                         const uint32_t *__restrict__ ap_ptr, const uint32_t *__restrict__ ap_idx,
@@ -1222,17 +1221,16 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
   float *hdummy = hc + hc_cap + lane;
   const uint32_t cdummy = nwords * 32u;  // column of the all-zero word
 
-  // h += alpha * t1[p0:p1] (one row of t1) on supp(t2); marks the other
-  // columns that receive a non-zero product when `cover`. The row goes in
-  // batches of kRowBatch chunks, then one batch of the 1 to 3 chunks left:
-  // all loads of a batch are in flight together, then all bitmap lookups,
-  // then all state reads, then the writes (the positions of one row are
-  // distinct). Returns true when the row cannot be handled here (a bad
-  // index or a negative value).
-  auto scatter_row = [&](uint32_t p0, uint32_t p1, float alpha, bool cover,
-                         uint32_t nq) -> bool {
-    const uint32_t nit = (p1 - p0 + kWave - 1) / kWave;
-    bool lane_bad = false;
+  // h += alpha * t1[row] on supp(t2), the row being chunks [c0, c1) of the
+  // padded copy of t1 (64 entries each, every column checked by the copy;
+  // padding entries hold column k and value 0, whose bitmap bit is never
+  // set); marks the other columns that receive a non-zero product when
+  // `cover`. The row goes in batches of kRowBatch chunks, then one batch of
+  // the 1 to 3 chunks left: all loads of a batch are in flight together,
+  // then all bitmap lookups, then all state reads, then the writes (the
+  // positions of one row are distinct).
+  auto scatter_row = [&](uint32_t c0, uint32_t c1, float alpha, bool cover, uint32_t nq) {
+    const uint32_t nit = c1 - c0;
     // one batch of NB chunks from chunk i0 on (all of them within the row)
     auto batch = [&](auto nb, uint32_t i0) {
       constexpr uint32_t NB = decltype(nb)::value;
@@ -1240,20 +1238,13 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       float vv[NB];
 #pragma unroll
       for (uint32_t b = 0; b < NB; ++b) {
-        const uint32_t p = p0 + (i0 + b) * kWave + lane;
-        const uint32_t pc = p < p1 ? p : p0;  // in range; dropped below
-        cc[b] = load_at(t1_idx, pc * 4u);
-        vv[b] = load_at(t1_val, pc * 4u);
+        const uint2 e = load_at(pt_ent, ((c0 + i0 + b) * kWave + lane) * 8u);
+        cc[b] = e.x >> 2;
+        vv[b] = __uint_as_float(e.y);
       }
       uint2 rw[NB];
 #pragma unroll
-      for (uint32_t b = 0; b < NB; ++b) {
-        const uint32_t p = p0 + (i0 + b) * kWave + lane;
-        const bool valid = p < p1;
-        lane_bad |= valid && (cc[b] >= k || vv[b] < 0.0f);
-        if (!valid || cc[b] >= k) cc[b] = cdummy, vv[b] = 0.0f;
-        rw[b] = rec[cc[b] >> 5];
-      }
+      for (uint32_t b = 0; b < NB; ++b) rw[b] = rec[cc[b] >> 5];
       float *hp[NB];
       float hv[NB];
       bool in_t2[NB];
@@ -1285,7 +1276,6 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       batch(Count<2>{}, i0);
     else if (rest == 1)
       batch(Count<1>{}, i0);
-    return __ballot(lane_bad) != 0;
   };
 
   uint32_t ncells = n;
@@ -1403,9 +1393,11 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
         if (m >= k || aval[j] < 0.0f) {
           bad_seed = true;
         } else {
-          arow0[j] = t1_ptr[m];
-          arow1[j] = t1_ptr[m + 1];
-          if (arow1[j] > t1_nnz || arow0[j] > arow1[j]) bad_seed = true;
+          // the row's chunks in the padded copy (bit 0: it holds a value < 0)
+          const uint32_t w0 = pt_ptr[m];
+          arow0[j] = w0 >> 1;
+          arow1[j] = pt_ptr[m + 1] >> 1;
+          if ((w0 & 1u) != 0u) bad_seed = true;
         }
       }
     }
@@ -1423,7 +1415,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
           am = readlane_f32(aval[jj], l);
         }
       }
-      deferred = scatter_row(p0, p1, am, true, nq);
+      scatter_row(p0, p1, am, true, nq);
       wave_lds_sync();
     }
 
@@ -1564,9 +1556,10 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
         p1 = readlane_u32(hp1, hl);
       } else {
         cover = true;
-        p0 = t1_ptr[idx];
-        p1 = t1_ptr[idx + 1];
-        if (p1 > t1_nnz || p0 > p1) {
+        const uint32_t w0 = pt_ptr[idx];
+        p0 = w0 >> 1;
+        p1 = pt_ptr[idx + 1] >> 1;
+        if ((w0 & 1u) != 0u) {  // a row with a value < 0: the dense kernel takes the cell
           deferred = true;
           break;
         }
@@ -1591,10 +1584,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       }
       wave_lds_sync();
       // -- h += alpha * t1[idx, :]
-      if (scatter_row(p0, p1, alpha, cover, nq)) {
-        deferred = true;
-        break;
-      }
+      scatter_row(p0, p1, alpha, cover, nq);
       wave_lds_sync();
       float beta = alpha;
       if constexpr (kPrune) {
@@ -1808,7 +1798,7 @@ hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, uint32_t tie
                           Csr k2b, Csr ap, uint32_t n, uint32_t k, uint32_t T, uint32_t cap,
                           const float *gamma, uint32_t *atom_idx, float *atom_val,
                           uint32_t *atom_cnt, uint32_t *trace, float *fw_gap,
-                          const SupQueues &q,
+                          const SupQueues &q, const uint32_t *pt_ptr, const uint2 *pt_ent,
                           float prune_thr, uint32_t *status, hipStream_t stream) {
   // t2 entries in registers: 256 for short K2B rows, 512 when rows are long
   // on average (the first pass) or by construction (the long-row pass)
@@ -1838,8 +1828,8 @@ hipError_t launch_support(const APlan &plan, const DeviceInfo &dev, uint32_t tie
   const uint64_t want = ((uint64_t)n + wpb - 1) / wpb;
   const uint64_t cap_blocks = (uint64_t)dev.cus * (uint64_t)bpc;
   const uint32_t blocks = (uint32_t)(want < cap_blocks ? want : cap_blocks);
-  hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, t1.ptr,
-                     t1.idx, t1.val, t1.nnz, k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
+  hipLaunchKernelGGL(kern, dim3(blocks), dim3(threads), lds_bytes, stream, pt_ptr, pt_ent,
+                     k2b.ptr, k2b.idx, k2b.val, k2b.nnz, ap.ptr, ap.idx,
                      ap.val, ap.nnz, n, k, T, cap, gamma, atom_idx, atom_val, atom_cnt, trace,
                      fw_gap, plan.nwords, hc_cap, plan.sched_words, lpw / 4, q, prune_thr,
                      status);
@@ -1961,8 +1951,8 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
                        status);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // the support kernel addresses t1 with 32-bit byte offsets
-  if (plan.support && t1.nnz < (1u << 30)) {
+  // the support kernel reads t1 from the padded copy, with 32-bit byte offsets
+  if (plan.support && plan.padded && plan.pad_chunks < (1u << 23)) {
     char *w8 = static_cast<char *>(ws);
     uint32_t *ctr = reinterpret_cast<uint32_t *>(w8);  // work0, work1, long, dense
     uint32_t *long_list = reinterpret_cast<uint32_t *>(w8 + plan.ws_list_off);
@@ -1994,14 +1984,16 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
     const bool two = support_tier_size(plan, kSupLongWaves, hc1, lpw_unused) && hc1 > hc0;
     SupQueues q0{nullptr, nullptr, ctr + 0, order, ctr + 8, two ? long_list : nullptr, ctr + 2,
                  dense_list, ctr + 3};
+    const uint32_t *pt_ptr = reinterpret_cast<const uint32_t *>(w8 + plan.ws_pt_ptr_off);
+    const uint2 *pt_ent = reinterpret_cast<const uint2 *>(w8 + plan.ws_pt_ent_off);
     e = launch_support(plan, dev, 0, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
-                       atom_cnt, trace, fw_gap, q0, prune_thr, status, stream);
+                       atom_cnt, trace, fw_gap, q0, pt_ptr, pt_ent, prune_thr, status, stream);
     if (e != hipSuccess) return e;
     if (two) {
       SupQueues q1{long_list, ctr + 2, ctr + 1, nullptr, nullptr, nullptr, nullptr, dense_list,
                    ctr + 3};
       e = launch_support(plan, dev, 1, t1, k2b, ap, n, k, T, cap, gamma, atom_idx, atom_val,
-                         atom_cnt, trace, fw_gap, q1, prune_thr, status, stream);
+                         atom_cnt, trace, fw_gap, q1, pt_ptr, pt_ent, prune_thr, status, stream);
       if (e != hipSuccess) return e;
     }
     cell_list = dense_list;
