@@ -1215,11 +1215,12 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
   const uint32_t pad_bits = (k & 31u) != 0u ? ~((1u << (k & 31u)) - 1u) : 0u;
   const float inf = __builtin_inff();
 
-  // Each lane owns one dummy slot past the state (value 0, only ever given
-  // +0) and one all-zero bitmap word past the real ones, so lanes without an
-  // entry take the same path as the others and no branch splits a batch.
+  // Each lane owns one dummy slot past the state, which takes the products
+  // of entries outside supp(t2) and is never read as a value, and the bitmap
+  // ends in one all-zero word (the padding column k lands in it or in the
+  // last word's unused bits), so lanes without an entry take the same path
+  // as the others and no branch splits a batch.
   float *hdummy = hc + hc_cap + lane;
-  const uint32_t cdummy = nwords * 32u;  // column of the all-zero word
 
   // h += alpha * t1[row] on supp(t2), the row being chunks [c0, c1) of the
   // padded copy of t1 (64 entries each, every column checked by the copy;
@@ -1252,13 +1253,12 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
       for (uint32_t b = 0; b < NB; ++b) {
         const uint32_t bit = 1u << (cc[b] & 31u);
         const uint32_t pos = rw[b].y + __popc(rw[b].x & (bit - 1u));
-        in_t2[b] = (rw[b].x & bit) != 0u && pos < nq;
+        in_t2[b] = (rw[b].x & bit) != 0u;  // (then pos < nq: the bits are supp(t2)'s)
         hp[b] = in_t2[b] ? hc + pos : hdummy;
         hv[b] = *hp[b];
       }
 #pragma unroll
-      for (uint32_t b = 0; b < NB; ++b)
-        *hp[b] = __builtin_fmaf(alpha, in_t2[b] ? vv[b] : 0.0f, hv[b]);
+      for (uint32_t b = 0; b < NB; ++b) *hp[b] = __builtin_fmaf(alpha, vv[b], hv[b]);
       if (cover) {
 #pragma unroll
         for (uint32_t b = 0; b < NB; ++b)
