@@ -206,7 +206,8 @@ int seacells_fw_a_columns_noalloc(const seacells_csr *t1, const seacells_csr *k2
  * aat_nnz: the non-zeros of A A^T). It holds the per-row-range partials
  * (8 bytes per column each; 8192 row ranges for k <= 2048, else 16384, fewer
  * when that would pass 2 GiB, at least one), one stamp and one gap partial
- * per (row range, column slice), and a copy of A A^T made per call. When k
+ * per (row range, column slice), an f64 gap sum per reduce chunk (at most
+ * 64), and a copy of A A^T made per call. When k
  * fits one column slice (k <= 2048) the copy pads every row to whole
  * chunks of 64 entries (at most 8 (aat_nnz + 64 k) bytes). Otherwise the
  * columns are cut into slices of at most 1024 columns (and about 3.75 MB of

@@ -1685,7 +1685,7 @@ __global__ void __launch_bounds__(kABlockMaxThreads)
   if (flags != 0) atomicOr(status, flags);
 }
 
-__global__ void zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
+__global__ void fw_a_ctr_zero_kernel(uint32_t *__restrict__ p, uint32_t count) {
   if (threadIdx.x < count) p[threadIdx.x] = 0u;
 }
 
@@ -1957,7 +1957,7 @@ hipError_t launch_fw_a(const APlan &plan, Csr t1, Csr k2b, Csr ap, uint32_t n, u
     uint32_t *ctr = reinterpret_cast<uint32_t *>(w8);  // work0, work1, long, dense
     uint32_t *long_list = reinterpret_cast<uint32_t *>(w8 + plan.ws_list_off);
     uint32_t *dense_list = reinterpret_cast<uint32_t *>(w8 + plan.ws_list2_off);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, ctr, 16u);
+    hipLaunchKernelGGL(fw_a_ctr_zero_kernel, dim3(1), dim3(64), 0, stream, ctr, 16u);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // the locality order of the cells (counters 8 .. 15: one per XCD segment)
     uint32_t *keys = reinterpret_cast<uint32_t *>(w8 + plan.ws_keys_off);

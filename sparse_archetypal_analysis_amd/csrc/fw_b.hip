@@ -884,8 +884,10 @@ __global__ void __launch_bounds__(256)
     fw_b_reduce1_kernel(const uint64_t *__restrict__ part_key, const uint32_t *__restrict__ stamps,
                         uint32_t n, uint32_t n_row_blocks, uint32_t n_slices, uint32_t slice_w,
                         uint32_t n_chunks, uint32_t k, uint32_t epoch,
-                        uint64_t *__restrict__ part2, uint32_t *__restrict__ status) {
+                        const float *__restrict__ part_gap, uint64_t *__restrict__ part2,
+                        double *__restrict__ gap2, uint32_t *__restrict__ status) {
   __shared__ uint64_t red[4][kReduceCols];
+  __shared__ double gred[256];
   const uint32_t lane = lane_id();
   const uint32_t w = threadIdx.x / kWave;
   const uint32_t c = blockIdx.x * kReduceCols + lane;
@@ -916,14 +918,30 @@ __global__ void __launch_bounds__(256)
     part2[(size_t)ch * k + c] = m;
   }
   if (flags != 0) atomicOr(status, flags);
+  // the first column group also sums this chunk's share of the gap
+  // partials (f64, a fixed order: strided per thread, then a tree)
+  if (blockIdx.x == 0) {
+    const uint64_t units = (uint64_t)n_row_blocks * n_slices;
+    const uint32_t u0 = (uint32_t)(units * ch / n_chunks);
+    const uint32_t u1 = (uint32_t)(units * (ch + 1) / n_chunks);
+    double s = 0.0;
+    for (uint32_t u = u0 + threadIdx.x; u < u1; u += 256) s += (double)part_gap[u];
+    gred[threadIdx.x] = s;
+    __syncthreads();
+    for (uint32_t h = 128; h > 0; h >>= 1) {
+      if (threadIdx.x < h) gred[threadIdx.x] += gred[threadIdx.x + h];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) gap2[ch] = gred[0];
+  }
 }
 
-// Stage 2: one thread per column over the chunk minima; the last block
-// sums the gap partials (f64, fixed order).
+// Stage 2: one thread per column over the chunk minima; the last block's
+// first thread adds the chunks' gap sums in chunk order.
 __global__ void __launch_bounds__(256)
     fw_b_reduce2_kernel(const uint64_t *__restrict__ part2, uint32_t n_chunks,
-                        const float *__restrict__ part_gap, uint32_t n_units, uint32_t n,
-                        uint32_t k, float *__restrict__ out_val, uint32_t *__restrict__ out_idx,
+                        const double *__restrict__ gap2, uint32_t n, uint32_t k,
+                        float *__restrict__ out_val, uint32_t *__restrict__ out_idx,
                         float *__restrict__ gap, uint32_t *__restrict__ status) {
   const uint32_t col_blocks = (k + 255) / 256;
   if (blockIdx.x < col_blocks) {
@@ -943,42 +961,34 @@ __global__ void __launch_bounds__(256)
     out_val[c] = v;
     out_idx[c] = row;
     if (flags != 0) atomicOr(status, flags);
-  } else {
-    __shared__ double red[256];
+  } else if (threadIdx.x == 0 && gap != nullptr) {
     double s = 0.0;
-    for (uint32_t u = threadIdx.x; u < n_units; u += 256) s += (double)part_gap[u];
-    red[threadIdx.x] = s;
-    __syncthreads();
-    for (uint32_t w = 128; w > 0; w >>= 1) {
-      if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
-      __syncthreads();
-    }
-    if (threadIdx.x == 0 && gap != nullptr) *gap = (float)red[0];
+    for (uint32_t ch = 0; ch < n_chunks; ++ch) s += gap2[ch];
+    *gap = (float)s;
   }
 }
 
 // Full Frank-Wolfe duality gap of the B subproblem: sum(B * G) - sum_c
-// min_i G[i, c]. One block: the gap partials are summed exactly as the
-// final reduce sums them (same order, f64), the column minima likewise.
+// min_i G[i, c]. One block: the chunks' gap sums are added exactly as the
+// final reduce adds them (chunk order, f64), the column minima in f64.
 __global__ void __launch_bounds__(256)
-    fw_b_fw_gap_kernel(const float *__restrict__ part_gap, uint32_t n_units,
+    fw_b_fw_gap_kernel(const double *__restrict__ gap2, uint32_t n_chunks,
                        const float *__restrict__ out_val, uint32_t k,
                        float *__restrict__ fw_gap) {
-  __shared__ double red[2][256];
-  double s = 0.0, v = 0.0;
-  for (uint32_t u = threadIdx.x; u < n_units; u += 256) s += (double)part_gap[u];
+  __shared__ double red[256];
+  double v = 0.0;
   for (uint32_t c = threadIdx.x; c < k; c += 256) v += (double)out_val[c];
-  red[0][threadIdx.x] = s;
-  red[1][threadIdx.x] = v;
+  red[threadIdx.x] = v;
   __syncthreads();
   for (uint32_t w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) {
-      red[0][threadIdx.x] += red[0][threadIdx.x + w];
-      red[1][threadIdx.x] += red[1][threadIdx.x + w];
-    }
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) *fw_gap = (float)(red[0][0] - red[1][0]);
+  if (threadIdx.x == 0) {
+    double s = 0.0;
+    for (uint32_t ch = 0; ch < n_chunks; ++ch) s += gap2[ch];
+    *fw_gap = (float)(s - red[0]);
+  }
 }
 
 // B step on padded B^T rows, one thread per archetype.
@@ -1021,12 +1031,12 @@ __global__ void __launch_bounds__(256)
 
 __global__ void status_clear_kernel(uint32_t *__restrict__ status) { *status = 0u; }
 
-__global__ void zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
+__global__ void xcd_work_zero_kernel(uint32_t *__restrict__ p, uint32_t count) {
   if (threadIdx.x < count) p[threadIdx.x] = 0u;
 }
 
 __global__ void __launch_bounds__(256)
-    fill_zero_u32_kernel(uint32_t *__restrict__ p, uint32_t count) {
+    hist_zero_kernel(uint32_t *__restrict__ p, uint32_t count) {
   const uint32_t stride = gridDim.x * blockDim.x;
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) p[i] = 0u;
 }
@@ -1123,6 +1133,8 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices, uint64_
   off = align_up(off + (size_t)p.n_chunks * k * sizeof(uint64_t), 256);
   p.off_gap = off;
   off = align_up(off + units * sizeof(float), 256);
+  p.off_gap2 = off;
+  off = align_up(off + (size_t)p.n_chunks * sizeof(double), 256);
   p.off_stamp = off;
   off = align_up(off + units * sizeof(uint32_t), 256);
   p.off_work = off;
@@ -1254,7 +1266,7 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
     uint32_t *off = reinterpret_cast<uint32_t *>(base + p.off_xcd_off);
     uint32_t *list = reinterpret_cast<uint32_t *>(base + p.off_xcd_list);
     const uint32_t zb = (k + 255) / 256;
-    hipLaunchKernelGGL(fill_zero_u32_kernel, dim3(zb < 4096u ? zb : 4096u), dim3(256), 0, stream,
+    hipLaunchKernelGGL(hist_zero_kernel, dim3(zb < 4096u ? zb : 4096u), dim3(256), 0, stream,
                        hist, k);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const uint64_t sampled = ((uint64_t)n + kHistRowStep - 1) / kHistRowStep;
@@ -1271,7 +1283,7 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
     xcd_off = off;
     xcd_list = list;
   }
-  hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(64), 0, stream, xcd_work, kXcds);
+  hipLaunchKernelGGL(xcd_work_zero_kernel, dim3(1), dim3(64), 0, stream, xcd_work, kXcds);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   switch (p.s4) {
 #define SEACELLS_B_CASE(S)                                                                      \
@@ -1308,18 +1320,19 @@ hipError_t launch_fw_b_reduce(const BPlan &p, uint32_t n, uint32_t k, float *out
   const uint64_t *keys = reinterpret_cast<const uint64_t *>(base + p.off_keys);
   uint64_t *part2 = reinterpret_cast<uint64_t *>(base + p.off_part2);
   const float *gap_part = reinterpret_cast<const float *>(base + p.off_gap);
+  double *gap2 = reinterpret_cast<double *>(base + p.off_gap2);
   const uint32_t *stamps = reinterpret_cast<const uint32_t *>(base + p.off_stamp);
   hipError_t e;
   const dim3 g1((k + kReduceCols - 1) / kReduceCols, p.n_chunks);
   hipLaunchKernelGGL(fw_b_reduce1_kernel, g1, dim3(256), 0, stream, keys, stamps, n,
-                     p.n_row_blocks, p.n_slices, p.slice_w, p.n_chunks, k, epoch, part2, status);
+                     p.n_row_blocks, p.n_slices, p.slice_w, p.n_chunks, k, epoch, gap_part, part2,
+                     gap2, status);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const uint32_t units = p.n_row_blocks * p.n_slices;
   hipLaunchKernelGGL(fw_b_reduce2_kernel, dim3((k + 255) / 256 + 1), dim3(256), 0, stream, part2,
-                     p.n_chunks, gap_part, units, n, k, out_val, out_idx, gap, status);
+                     p.n_chunks, gap2, n, k, out_val, out_idx, gap, status);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (fw_gap != nullptr) {
-    hipLaunchKernelGGL(fw_b_fw_gap_kernel, dim3(1), dim3(256), 0, stream, gap_part, units,
+    hipLaunchKernelGGL(fw_b_fw_gap_kernel, dim3(1), dim3(256), 0, stream, gap2, p.n_chunks,
                        out_val, k, fw_gap);
     e = hipGetLastError();
   }
