@@ -322,7 +322,8 @@ def copy_calibration(mib):
 
 A_KERNELS = ("fw_a_", "pad_rows_kernel", "pad_fill_kernel", "cell_key_kernel", "key_scan_kernel",
              "cell_scatter_kernel", "fill_u32_kernel")
-B_KERNELS = ("seg_table_kernel", "row_slice_kernel", "pa_seg_kernel", "pa_fill_kernel",
+B_KERNELS = ("seg_table_kernel", "row_slice_kernel", "pa_count_kernel", "pa_bscan_kernel",
+             "pa_offs_kernel", "pa_fill_kernel",
              "pc_fill_kernel", "col_walk_kernel", "slice_order_kernel", "hist_zero_kernel",
              "ref_hist_kernel", "slice_work_kernel", "xcd_assign_kernel", "xcd_work_zero_kernel",
              "fw_b_partials_kernel", "fw_b_reduce1_kernel", "fw_b_reduce2_kernel",

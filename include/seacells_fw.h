@@ -213,7 +213,8 @@ int seacells_fw_a_columns_noalloc(const seacells_csr *t1, const seacells_csr *k2
  * columns are cut into slices of at most 1024 columns (and about 3.75 MB of
  * A A^T each) and the workspace also holds the column-slice tables of A A^T
  * (4 (k + 1) bytes per slice) and of K2At's rows (4 (n + 1) bytes per
- * slice), the run table and the chunked copy of A A^T per slice (chunks of
+ * slice), the run table (4 bytes per run and 8 per 1024 runs) and the
+ * chunked copy of A A^T per slice (chunks of
  * 32 entries at 6 bytes each, at most aat_nnz / 32 + k slices + 1 chunks),
  * the in-slice column order (12 k bytes and 2 bytes per slice column) and,
  * with more slices than the GPU's 8 XCDs, the slices each XCD owns (4 k +

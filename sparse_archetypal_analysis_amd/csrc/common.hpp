@@ -178,7 +178,7 @@ struct BPlan {
   // order of their own (two walk vectors of k floats, then the column ->
   // position and position -> column tables, 16-bit, slice-local)
   size_t off_keys, off_part2, off_gap, off_gap2, off_stamp, off_work, off_seg, off_rs, off_pa_seg,
-      off_pa_ent, off_pc_col, off_pc_val, off_walk, off_cpos, off_pcol;
+      off_pa_bsum, off_pa_ent, off_pc_col, off_pc_val, off_walk, off_cpos, off_pcol;
   // narrow slices, more than one per XCD: the slices each XCD owns, chosen
   // per call to even out the XCDs' gather work (a K2B column histogram, the
   // work of every slice, then the slices of XCD x at

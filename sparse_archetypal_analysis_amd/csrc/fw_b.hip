@@ -254,10 +254,20 @@ __global__ void __launch_bounds__(1024)
 // depends on the assignment: every unit writes its own partials.
 
 // hist[m] += 1 for every entry of column m in the sampled rows; one wave per
-// row, grid-stride
+// row, grid-stride. With k <= kHistLds each block counts into a histogram
+// of its own in LDS and adds its non-zero counts to hist once (few device
+// atomics); otherwise every entry is a device atomic.
+constexpr uint32_t kHistLds = 16384;    // columns an LDS histogram holds (64 KB)
+constexpr uint32_t kHistBlocks = 256;   // blocks of the LDS-histogram launch
 __global__ void __launch_bounds__(256)
     ref_hist_kernel(Csr k2b, uint32_t n, uint32_t k, uint32_t *__restrict__ hist) {
+  extern __shared__ uint32_t lh[];
   const uint32_t lane = lane_id();
+  const bool local = k <= kHistLds;
+  if (local) {
+    for (uint32_t m = threadIdx.x; m < k; m += blockDim.x) lh[m] = 0u;
+    __syncthreads();
+  }
   const uint32_t nw = gridDim.x * (blockDim.x / kWave);
   for (uint32_t j = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
        (uint64_t)j * kHistRowStep < n; j += nw) {
@@ -265,8 +275,13 @@ __global__ void __launch_bounds__(256)
     if (!row_ok(k2b, j * kHistRowStep, lo, hi)) continue;
     for (uint32_t q = lo + lane; q < hi; q += kWave) {
       const uint32_t m = k2b.idx[q];
-      if (m < k) atomicAdd(hist + m, 1u);
+      if (m < k) atomicAdd(local ? lh + m : hist + m, 1u);
     }
+  }
+  if (local) {
+    __syncthreads();
+    for (uint32_t m = threadIdx.x; m < k; m += blockDim.x)
+      if (lh[m] != 0u) atomicAdd(hist + m, lh[m]);
   }
 }
 
@@ -370,51 +385,107 @@ __device__ __forceinline__ uint32_t run_of(const Csr &aat, const uint32_t *seg, 
   return hi - lo;
 }
 
-// One block: chunk counts of every run and their exclusive prefix sum
+// The run table: chunk counts of every run and their exclusive prefix sum
 // (64-bit, checked against the bound the workspace was sized for; past it
-// every run is left empty and BAD_INDEX is raised).
-__global__ void __launch_bounds__(1024)
-    pa_seg_kernel(Csr aat, const uint32_t *__restrict__ seg, uint32_t k, uint32_t n_slices,
-                  uint32_t ch, uint64_t pa_chunks, uint32_t *__restrict__ pa_seg,
-                  uint32_t *__restrict__ status) {
-  __shared__ uint64_t part[1024];
-  const uint32_t tid = threadIdx.x;
+// every run is left empty and BAD_INDEX is raised). Three kernels over
+// blocks of kScanRuns runs (4 consecutive runs per thread): the blocks'
+// counts and sums, a scan of the sums (one block), then each block's
+// offsets. bsum holds one sum per block, then the total.
+constexpr uint32_t kScanRuns = 1024;
+
+// Exclusive prefix of v over a block of 256 threads; *total gets the sum.
+__device__ __forceinline__ uint64_t block_excl_scan_256(uint64_t v, uint64_t *red,
+                                                        uint64_t *total) {
+  const uint32_t lane = lane_id(), w = threadIdx.x / kWave;
+  uint64_t incl = v;
+#pragma unroll
+  for (uint32_t off = 1; off < kWave; off <<= 1) {
+    const uint64_t u = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += u;
+  }
+  if (lane == kWave - 1) red[w] = incl;
+  __syncthreads();
+  uint64_t before = 0, all = 0;
+  for (uint32_t x = 0; x < 4; ++x) {
+    if (x < w) before += red[x];
+    all += red[x];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
+
+__global__ void __launch_bounds__(256)
+    pa_count_kernel(Csr aat, const uint32_t *__restrict__ seg, uint32_t k, uint32_t n_slices,
+                    uint32_t ch, uint32_t *__restrict__ pa_seg, uint64_t *__restrict__ bsum,
+                    uint32_t *__restrict__ status) {
+  __shared__ uint64_t red[4];
   const uint64_t total_runs = (uint64_t)k * n_slices;
-  const uint64_t per = (total_runs + 1023) / 1024;
-  const uint64_t e0 = (uint64_t)tid * per < total_runs ? (uint64_t)tid * per : total_runs;
-  const uint64_t e1 = e0 + per < total_runs ? e0 + per : total_runs;
+  const uint64_t e0 = (uint64_t)blockIdx.x * kScanRuns + threadIdx.x * 4u;
   uint64_t sum = 0;
-  uint32_t bad_any = 0;
-  for (uint64_t e = e0; e < e1; ++e) {
+  bool bad_any = false;
+  for (uint32_t j = 0; j < 4; ++j) {
+    const uint64_t e = e0 + j;
+    if (e >= total_runs) break;
     const uint32_t s = (uint32_t)(e / k), m = (uint32_t)(e - (uint64_t)s * k);
     uint32_t lo;
     bool bad;
     const uint32_t len = run_of(aat, seg, k, s, m, lo, bad);
     bad_any |= bad;
-    sum += (len + ch - 1) / ch;
+    const uint32_t c = (len + ch - 1) / ch;
+    pa_seg[e] = c;
+    sum += c;
   }
-  part[tid] = sum;
-  __syncthreads();
-  for (uint32_t off = 1; off < 1024; off <<= 1) {
-    const uint64_t v = tid >= off ? part[tid - off] : 0u;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  const uint64_t total = part[1023] + 1;  // + the padding chunk 0
-  const bool overflow = total > pa_chunks;
-  uint64_t at = 1 + part[tid] - sum;
-  for (uint64_t e = e0; e < e1; ++e) {
-    const uint32_t s = (uint32_t)(e / k), m = (uint32_t)(e - (uint64_t)s * k);
-    uint32_t lo;
-    bool bad;
-    const uint32_t len = run_of(aat, seg, k, s, m, lo, bad);
-    pa_seg[e] = overflow ? 1u : (uint32_t)at;
-    at += (len + ch - 1) / ch;
-  }
-  if (tid == 1023) pa_seg[total_runs] = overflow ? 1u : (uint32_t)total;
+  uint64_t all;
+  block_excl_scan_256(sum, red, &all);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = all;
   if (bad_any) atomicOr(status, kFlagBadIndex);
-  if (tid == 0 && overflow) atomicOr(status, kFlagBadIndex);
+}
+
+// One block: exclusive scan of the nb block sums in place; bsum[nb] = the
+// total with the padding chunk 0, also written after the last run.
+__global__ void __launch_bounds__(256)
+    pa_bscan_kernel(uint64_t *__restrict__ bsum, uint32_t nb, uint64_t total_runs,
+                    uint64_t pa_chunks, uint32_t *__restrict__ pa_seg,
+                    uint32_t *__restrict__ status) {
+  __shared__ uint64_t red[4];
+  uint64_t carry = 0;
+  for (uint32_t b0 = 0; b0 < nb; b0 += 256) {
+    const uint32_t b = b0 + threadIdx.x;
+    const uint64_t v = b < nb ? bsum[b] : 0u;
+    uint64_t all;
+    const uint64_t ex = block_excl_scan_256(v, red, &all);
+    if (b < nb) bsum[b] = carry + ex;
+    carry += all;
+  }
+  if (threadIdx.x == 0) {
+    const uint64_t total = carry + 1;  // + the padding chunk 0
+    const bool overflow = total > pa_chunks;
+    bsum[nb] = total;
+    pa_seg[total_runs] = overflow ? 1u : (uint32_t)total;
+    if (overflow) atomicOr(status, kFlagBadIndex);
+  }
+}
+
+__global__ void __launch_bounds__(256)
+    pa_offs_kernel(uint32_t *__restrict__ pa_seg, const uint64_t *__restrict__ bsum,
+                   uint32_t nb, uint64_t total_runs, uint64_t pa_chunks) {
+  __shared__ uint64_t red[4];
+  const uint64_t e0 = (uint64_t)blockIdx.x * kScanRuns + threadIdx.x * 4u;
+  uint32_t c[4];
+  uint64_t sum = 0;
+  for (uint32_t j = 0; j < 4; ++j) {
+    c[j] = e0 + j < total_runs ? pa_seg[e0 + j] : 0u;
+    sum += c[j];
+  }
+  uint64_t all;
+  uint64_t at = 1 + bsum[blockIdx.x] + block_excl_scan_256(sum, red, &all);
+  const bool overflow = bsum[nb] > pa_chunks;
+  for (uint32_t j = 0; j < 4; ++j) {
+    if (e0 + j >= total_runs) break;
+    pa_seg[e0 + j] = overflow ? 1u : (uint32_t)at;
+    at += c[j];
+  }
 }
 
 // One wave per run: its entries, then padding; chunk 0 as padding.
@@ -458,7 +529,7 @@ __global__ void __launch_bounds__(256)
 // Chunked copy of AAt for the narrow-slice gather (two half-waves, one run
 // each). The run of AAt row m inside slice s takes ceil(len / 32) chunks of
 // 32 entries starting at chunk pc_seg[s * k + m] (the chunk table is built by
-// pa_seg_kernel with chunks of 32): the accumulator positions of the entries'
+// the run-table scan with chunks of 32): the accumulator positions of the entries'
 // columns (cpos, the in-slice order) as 16-bit words in pc_col and their
 // values in pc_val, so one half-wave load reads exactly one 64-byte run of
 // positions and one 128-byte run of values. A run's entries are stored in
@@ -1158,6 +1229,8 @@ static BPlan plan_with_slices(uint32_t n, uint32_t k, uint32_t n_slices, uint64_
   p.pa_chunks = p.dual ? pc_chunks : (aat_nnz + kWave - 1) / kWave + nonempty + 1;
   p.off_pa_seg = off;
   off = align_up(off + (runs + 1) * sizeof(uint32_t), 256);
+  p.off_pa_bsum = off;  // the run-table scan: one sum per kScanRuns runs, then the total
+  off = align_up(off + ((runs + kScanRuns - 1) / kScanRuns + 1) * sizeof(uint64_t), 256);
   p.off_pa_ent = off;
   if (!p.dual) off = align_up(off + (size_t)p.pa_chunks * p.pa_ch * sizeof(uint2), 256);
   p.off_pc_col = off;
@@ -1243,9 +1316,20 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
                        walk + (size_t)((kWalkSteps - 1) & 1) * k, k, p.slice_w, cpos, pcol);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(pa_seg_kernel, dim3(1), dim3(1024), 0, stream, aat, seg, k, p.n_slices,
-                     p.pa_ch, p.pa_chunks, pa_seg, status);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  {
+    const uint64_t runs = (uint64_t)k * p.n_slices;
+    const uint32_t nb = (uint32_t)((runs + kScanRuns - 1) / kScanRuns);
+    uint64_t *bsum = reinterpret_cast<uint64_t *>(base + p.off_pa_bsum);
+    hipLaunchKernelGGL(pa_count_kernel, dim3(nb), dim3(256), 0, stream, aat, seg, k, p.n_slices,
+                       p.pa_ch, pa_seg, bsum, status);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(pa_bscan_kernel, dim3(1), dim3(256), 0, stream, bsum, nb, runs,
+                       p.pa_chunks, pa_seg, status);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(pa_offs_kernel, dim3(nb), dim3(256), 0, stream, pa_seg, bsum, nb, runs,
+                       p.pa_chunks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   {
     const uint64_t runs = (uint64_t)k * p.n_slices;
     const uint64_t blocks = (runs + 3) / 4;  // 4 waves per block, one run each
@@ -1271,8 +1355,11 @@ hipError_t launch_fw_b(const BPlan &p, Csr k2b, Csr aat, Csr k2at, Csr b, uint32
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const uint64_t sampled = ((uint64_t)n + kHistRowStep - 1) / kHistRowStep;
     const uint64_t hb = (sampled + 3) / 4;  // 4 waves per block, one row each
-    hipLaunchKernelGGL(ref_hist_kernel, dim3((uint32_t)(hb < 16384u ? (hb > 0 ? hb : 1) : 16384u)),
-                       dim3(256), 0, stream, k2b, n, k, hist);
+    const bool local = k <= kHistLds;
+    const uint64_t cap = local ? kHistBlocks : 16384u;
+    hipLaunchKernelGGL(ref_hist_kernel, dim3((uint32_t)(hb < cap ? (hb > 0 ? hb : 1) : cap)),
+                       dim3(256), local ? (size_t)k * sizeof(uint32_t) : 0, stream, k2b, n, k,
+                       hist);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(slice_work_kernel, dim3(p.n_slices), dim3(256), 0, stream, hist, pa_seg,
                        k, swork);
