@@ -1115,10 +1115,18 @@ __global__ void __launch_bounds__(256)
     uint32_t key = k;  // empty or malformed rows go last
     if (lo < hi && hi <= k2b_nnz) {
       uint32_t bk = 0xffffffffu, bc = 0xffffffffu;  // ~order(value), column
-      for (uint32_t p = lo + lane; p < hi; p += kWave) {
-        const uint32_t kv = ~f32_order(k2b_val[p]);  // larger value, smaller key
-        const uint32_t col = k2b_idx[p];
-        if (kv < bk || (kv == bk && col < bc)) bk = kv, bc = col;
+      // four entries per lane in flight
+      for (uint32_t p0 = lo + lane; p0 < hi; p0 += 4 * kWave) {
+        uint32_t kv[4], col[4];
+#pragma unroll
+        for (uint32_t j = 0; j < 4; ++j) {
+          const uint32_t p = p0 + j * kWave;
+          kv[j] = p < hi ? ~f32_order(k2b_val[p]) : 0xffffffffu;  // larger value, smaller key
+          col[j] = p < hi ? k2b_idx[p] : 0xffffffffu;
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < 4; ++j)
+          if (kv[j] < bk || (kv[j] == bk && col[j] < bc)) bk = kv[j], bc = col[j];
       }
       const uint32_t best = wave_min_u32(bk);
       const uint32_t col = wave_min_u32(bk == best ? bc : 0xffffffffu);

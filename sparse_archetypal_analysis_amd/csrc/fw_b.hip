@@ -188,12 +188,25 @@ __global__ void __launch_bounds__(256)
     uint32_t lo, hi;
     if (!row_ok(aat, m, lo, hi)) lo = hi = 0;
     float sx = 0.0f, sv = 0.0f;
-    for (uint32_t q = lo + lane; q < hi; q += kWave) {
-      const uint32_t c = aat.idx[q];
-      if (c < k) {
-        const float v = aat.val[q];
-        sx = __builtin_fmaf(v, x != nullptr ? x[c] : walk_start(c), sx);
-        sv += v;
+    // four entries per lane in flight (their loads do not wait on each other)
+    for (uint32_t q0 = lo + lane; q0 < hi; q0 += 4 * kWave) {
+      uint32_t c[4];
+      float v[4], xc[4];
+#pragma unroll
+      for (uint32_t j = 0; j < 4; ++j) {
+        const uint32_t q = q0 + j * kWave;
+        c[j] = q < hi ? aat.idx[q] : k;
+        v[j] = q < hi ? aat.val[q] : 0.0f;
+      }
+#pragma unroll
+      for (uint32_t j = 0; j < 4; ++j)
+        xc[j] = c[j] < k ? (x != nullptr ? x[c[j]] : walk_start(c[j])) : 0.0f;
+#pragma unroll
+      for (uint32_t j = 0; j < 4; ++j) {
+        if (c[j] < k) {
+          sx = __builtin_fmaf(v[j], xc[j], sx);
+          sv += v[j];
+        }
       }
     }
     sx = wave_sum_f32(sx);
