@@ -84,7 +84,11 @@ int seacells_csr_matmul_rows(const seacells_csr *a, const seacells_csr *b, uint3
  * sizes the outputs by a bound, without reading c_row_ptr[m], stays safe).
  * c[i, c] = sum over the entries j of a's row i, in order, and then over
  * b's row j, of a[i, j] * b[j, c], accumulated in f32 with fused
- * multiply-adds in that order. c_col_idx / c_val may be NULL only when the
+ * multiply-adds in that order. A row of a with 2048 entries or more, when b
+ * has at most 16384 columns, is cut into 16 runs of consecutive entries
+ * (run w: entries len * w / 16 to len * (w + 1) / 16 of the row, rounded
+ * down), each run is summed that way from 0, and the 16 sums are added in
+ * run order (with or without the rows pass's bitmaps). c_col_idx / c_val may be NULL only when the
  * product is empty (a non-empty row with no output arrays is skipped and
  * flagged BAD_INDEX).
  */

@@ -23,7 +23,12 @@
 //   of one entry never collide), so every output sums its products in
 //   A-entry order, then B-entry order, in f32 with fma. The output keeps
 //   every column that some product reaches (a sum that cancels to 0 stays as
-//   an explicit 0).
+//   an explicit 0). A row of A with kHeavyEntries entries or more (when B has
+//   one column window) is taken by a block of kHvWaves waves instead, in both
+//   passes: wave w takes run w of the row's entries, marks its columns in the
+//   block's bitmap, and sums its products in slots of its own; the runs' sums
+//   are then added in run order. (An archetype that many cells keep as an
+//   atom makes such a row of A A^T, with ~10^5 to 10^6 products.)
 // Transpose: rows are cut into R blocks; one wave per block counts its
 //   entries per column, the counts become per-(block, column) write
 //   positions, and each wave writes its rows in order, so a transposed row
@@ -51,6 +56,15 @@ constexpr uint32_t kSpWaves = 4;        // waves per block
 constexpr uint32_t kSpWinWords = 512;   // bitmap words per column window (16384 columns)
 constexpr uint32_t kSpSlots = 1024;     // value slots per rank window
 constexpr uint32_t kSpGroup = 4;        // product windows loaded together
+// Rows of A with many entries (hub rows, e.g. an archetype many cells keep
+// as an atom in A A^T) go to a block of kHvWaves waves instead of one wave,
+// each wave taking one run of the row's entries, when b has at most one
+// column window of columns.
+constexpr uint32_t kHeavyEntries = 2048;
+constexpr uint32_t kHvWaves = 16;
+constexpr uint32_t kHvThreads = kHvWaves * kWave;
+constexpr uint32_t kHvSlots = 2048;     // value slots per wave and rank window (heavy rows)
+constexpr uint32_t kHvPartBytes = kHvWaves * kHvSlots * sizeof(float);  // 128 KB, dynamic LDS
 constexpr uint32_t kTrMaxBlocks = 1024;
 constexpr size_t kTrTableBytes = 64u << 20;  // per-(block, column) table of the transpose
 constexpr uint32_t kDotBlocks = 1024;
@@ -220,6 +234,37 @@ __device__ __forceinline__ uint32_t for_products(const Csr &a, const Csr &b, uin
   return flags;
 }
 
+__device__ __forceinline__ bool heavy_row(uint32_t a0, uint32_t a1, uint32_t q) {
+  return q <= kSpWinWords * 32u && a1 - a0 >= kHeavyEntries;
+}
+
+// Run w of kHvWaves consecutive runs of the entries [a0, a1).
+__device__ __forceinline__ void heavy_run(uint32_t a0, uint32_t a1, uint32_t w, uint32_t &s0,
+                                          uint32_t &s1) {
+  const uint64_t len = a1 - a0;
+  s0 = a0 + (uint32_t)(len * w / kHvWaves);
+  s1 = a0 + (uint32_t)(len * (w + 1u) / kHvWaves);
+}
+
+// The heavy rows among r = blockIdx.x + gridDim.x * j, kHvThreads values of
+// j at a time, into list[0 .. *nlist) (any order: each row is a unit of its
+// own). Returns false when the block has no rows left at j0.
+__device__ __forceinline__ bool heavy_batch(const Csr &a, uint32_t m, uint32_t q, uint64_t j0,
+                                            uint32_t *list, uint32_t *nlist) {
+  if ((uint64_t)blockIdx.x + (uint64_t)gridDim.x * j0 >= m) return false;
+  __syncthreads();  // every thread has read the last batch's count
+  if (threadIdx.x == 0) *nlist = 0u;
+  __syncthreads();
+  const uint64_t r = (uint64_t)blockIdx.x + (uint64_t)gridDim.x * (j0 + threadIdx.x);
+  if (r < m) {
+    uint32_t a0, a1;
+    if (sp_row(a, (uint32_t)r, a0, a1) && heavy_row(a0, a1, q))
+      list[atomicAdd(nlist, 1u)] = (uint32_t)r;
+  }
+  __syncthreads();
+  return true;
+}
+
 // Mark in bits[] (window starting at column w0, nw words) every column some
 // product of A's row [a0, a1) reaches. Returns the flags seen.
 __device__ __forceinline__ uint32_t mark_columns(const Csr &a, const Csr &b, uint32_t p,
@@ -253,6 +298,7 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
   for (uint32_t r = blockIdx.x * kSpWaves + wib; r < m; r += gridDim.x * kSpWaves) {
     uint32_t a0, a1;
     if (!sp_row(a, r, a0, a1)) flags |= kFlagBadIndex;
+    if (heavy_row(a0, a1, q)) continue;  // (spgemm_count_heavy_kernel)
     uint64_t total = 0;
     for (uint64_t w0 = 0; w0 < q; w0 += (uint64_t)kSpWinWords * 32u) {
       const uint32_t nw = (uint32_t)u64min(kSpWinWords, (q - w0 + 31u) / 32u);
@@ -273,6 +319,50 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
       cnt[r] = total > 0xffffffffull ? 0xffffffffu : (uint32_t)total;
       // rows of more than one value window: listed for the fill pass (any order)
       if (long_rows != nullptr && total > kSpSlots) long_rows[1u + atomicAdd(long_rows, 1u)] = r;
+    }
+  }
+  if (flags != 0) atomicOr(status, flags);
+}
+
+// Counts of the heavy rows: one block per row, wave w marks the columns of
+// run w of the row's entries in the block's bitmap (integer ORs: the result
+// does not depend on their order).
+__global__ void __launch_bounds__(kHvThreads)
+    spgemm_count_heavy_kernel(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
+                              uint32_t *__restrict__ cnt, uint32_t *__restrict__ pattern,
+                              uint32_t *__restrict__ status) {
+  __shared__ uint32_t bits[kSpWinWords];
+  __shared__ uint32_t list[kHvThreads];
+  __shared__ uint32_t nlist;
+  __shared__ uint32_t wsum[kHvWaves];
+  const uint32_t lane = lane_id(), w = threadIdx.x / kWave;
+  const uint32_t nw = (q + 31u) / 32u;  // <= kSpWinWords for heavy rows
+  uint32_t flags = 0;
+  for (uint64_t j0 = 0; heavy_batch(a, m, q, j0, list, &nlist); j0 += kHvThreads) {
+    const uint32_t nl = nlist;
+    for (uint32_t i = 0; i < nl; ++i) {
+      const uint32_t r = list[i];
+      uint32_t a0, a1, s0, s1;
+      sp_row(a, r, a0, a1);
+      heavy_run(a0, a1, w, s0, s1);
+      for (uint32_t x = threadIdx.x; x < nw; x += kHvThreads) bits[x] = 0u;
+      __syncthreads();
+      flags |= mark_columns(a, b, p, q, s0, s1, 0u, nw, bits, lane);
+      __syncthreads();
+      uint32_t part = 0;
+      for (uint32_t x = threadIdx.x; x < nw; x += kHvThreads) {
+        part += __popc(bits[x]);
+        if (pattern != nullptr) pattern[(size_t)r * nw + x] = bits[x];
+      }
+      part = wave_sum_u32(part);
+      if (lane == 0) wsum[w] = part;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint32_t total = 0;
+        for (uint32_t x = 0; x < kHvWaves; ++x) total += wsum[x];
+        cnt[r] = total;
+      }
+      __syncthreads();
     }
   }
   if (flags != 0) atomicOr(status, flags);
@@ -505,6 +595,9 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
           continue;
         }
       }
+      uint32_t a0, a1;
+      if (!sp_row(a, r, a0, a1)) flags |= kFlagBadIndex;
+      if (heavy_row(a0, a1, q)) continue;  // (spgemm_fill_heavy_kernel)
       const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
       const uint32_t cnt = end >= base ? end - base : 0u;
       const uint32_t s0 = vw * kSpSlots;
@@ -513,8 +606,6 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
         flags |= kFlagBadIndex;
         continue;
       }
-      uint32_t a0, a1;
-      if (!sp_row(a, r, a0, a1)) flags |= kFlagBadIndex;
       for (uint32_t w = lane; w < nw; w += kWave) bits[w] = pattern[(size_t)r * nw + w];
       wave_lds_sync();
       uint32_t v0w, v1w, first;
@@ -531,14 +622,15 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
     }
   } else {
     for (uint32_t r = gw; r < m; r += nwaves) {
+      uint32_t a0, a1;
+      if (!sp_row(a, r, a0, a1)) flags |= kFlagBadIndex;
+      if (heavy_row(a0, a1, q)) continue;  // (spgemm_fill_heavy_kernel)
       const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
       const uint32_t cnt = end >= base ? end - base : 0u;
       if (cnt > 0 && (c_idx == nullptr || c_val == nullptr)) {  // no output arrays given
         flags |= kFlagBadIndex;
         continue;
       }
-      uint32_t a0, a1;
-      if (!sp_row(a, r, a0, a1)) flags |= kFlagBadIndex;
       uint32_t done = 0;
       for (uint64_t w0l = 0; w0l < q; w0l += (uint64_t)kSpWinWords * 32u) {
         const uint32_t w0 = (uint32_t)w0l;
@@ -555,6 +647,117 @@ __global__ void __launch_bounds__(kSpWaves * kWave)
         done += nwin;
       }
       if (done != cnt) flags |= kFlagBadIndex;  // row pointers not those of the count pass
+    }
+  }
+  if (flags != 0) atomicOr(status, flags);
+}
+
+// Values of the heavy rows: one block per row. The row's columns come from
+// the rows pass's bitmap (kept) or are marked again (wave w: run w of the
+// entries); wave 0 ranks them. Per window of kHvSlots ranks, wave w sums
+// the products of run w in its own slots (entry by entry, in order, as a
+// light row's wave does), then slot s of the window gets the kHvWaves sums
+// added in run order.
+__global__ void __launch_bounds__(kHvThreads)
+    spgemm_fill_heavy_kernel(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
+                             const uint32_t *__restrict__ c_ptr, uint32_t *__restrict__ c_idx,
+                             float *__restrict__ c_val, uint64_t c_cap,
+                             const uint32_t *__restrict__ pattern,
+                             uint32_t *__restrict__ status) {
+  if (c_ptr[m] > c_cap) return;  // (spgemm_fill_kernel raises the flag)
+  __shared__ uint32_t bits[kSpWinWords];
+  __shared__ uint16_t rank[kSpWinWords];
+  __shared__ uint16_t colof[kHvSlots];
+  extern __shared__ float part[];  // kHvWaves x kHvSlots
+  __shared__ uint32_t list[kHvThreads];
+  __shared__ uint32_t nlist, nwin_s;
+  const uint32_t lane = lane_id(), w = threadIdx.x / kWave;
+  const uint32_t nw = (q + 31u) / 32u;  // <= kSpWinWords for heavy rows
+  float *acc = part + (size_t)w * kHvSlots;
+  uint32_t flags = 0;
+  for (uint64_t j0 = 0; heavy_batch(a, m, q, j0, list, &nlist); j0 += kHvThreads) {
+    const uint32_t nl = nlist;
+    for (uint32_t i = 0; i < nl; ++i) {
+      const uint32_t r = list[i];
+      uint32_t a0, a1, e0, e1;
+      sp_row(a, r, a0, a1);
+      heavy_run(a0, a1, w, e0, e1);
+      const uint32_t base = c_ptr[r], end = c_ptr[r + 1];
+      const uint32_t cnt = end >= base ? end - base : 0u;
+      if (cnt > 0 && (c_idx == nullptr || c_val == nullptr)) {  // (uniform over the block)
+        flags |= kFlagBadIndex;
+        continue;
+      }
+      if (pattern != nullptr) {
+        for (uint32_t x = threadIdx.x; x < nw; x += kHvThreads) bits[x] = pattern[(size_t)r * nw + x];
+      } else {
+        for (uint32_t x = threadIdx.x; x < nw; x += kHvThreads) bits[x] = 0u;
+        __syncthreads();
+        flags |= mark_columns(a, b, p, q, e0, e1, 0u, nw, bits, lane);
+      }
+      __syncthreads();
+      // wave 0: ranks of the words (each lane a contiguous run of words)
+      uint32_t v0w = 0, v1w = 0, first = 0;
+      if (w == 0) {
+        const uint32_t per = (nw + kWave - 1) / kWave;
+        v0w = min(lane * per, nw), v1w = min(v0w + per, nw);
+        uint32_t cnt_l = 0;
+        for (uint32_t x = v0w; x < v1w; ++x) cnt_l += __popc(bits[x]);
+        uint32_t run = wave_excl_scan_u32(cnt_l, lane);
+        first = run;
+        for (uint32_t x = v0w; x < v1w; ++x) {
+          rank[x] = (uint16_t)run;
+          run += __popc(bits[x]);
+        }
+        const uint32_t nwin = wave_sum_u32(cnt_l);
+        if (lane == 0) nwin_s = nwin;
+      }
+      __syncthreads();
+      const uint32_t nwin = nwin_s;
+      if (nwin != cnt) flags |= kFlagBadIndex;  // not the rows pass's pointers
+      for (uint32_t s0 = 0; s0 < nwin; s0 += kHvSlots) {
+        const uint32_t ns = min(kHvSlots, nwin - s0);
+        if (w == 0) {  // slot -> column
+          uint32_t pos = first;
+          for (uint32_t x = v0w; x < v1w && pos < s0 + ns; ++x) {
+            uint32_t bx = bits[x];
+            while (bx != 0u) {
+              const uint32_t bpos = (uint32_t)__builtin_ctz(bx);
+              bx &= bx - 1u;
+              if (pos >= s0 && pos < s0 + ns) colof[pos - s0] = (uint16_t)(x * 32u + bpos);
+              ++pos;
+            }
+          }
+        }
+        for (uint32_t x = lane; x < ns; x += kWave) acc[x] = 0.0f;
+        wave_lds_sync();
+        for_products<true>(a, b, p, e0, e1, lane,
+                           [&](bool valid, uint32_t c, float bv, float a_own, uint32_t own,
+                               uint64_t owners) {
+                             uint32_t pos = 0xffffffffu;
+                             if (valid && c < q) {
+                               const uint32_t x = c >> 5, bit = 1u << (c & 31u);
+                               pos = rank[x] + __popc(bits[x] & (bit - 1u)) - s0;
+                             }
+                             const bool mine = pos < ns;
+                             for (uint64_t mm = owners; mm != 0; mm &= mm - 1ull) {
+                               const uint32_t l = (uint32_t)__builtin_ctzll(mm);
+                               if (mine && own == l) acc[pos] = __builtin_fmaf(a_own, bv, acc[pos]);
+                               wave_lds_sync();
+                             }
+                           });
+        __syncthreads();
+        for (uint32_t x = threadIdx.x; x < ns; x += kHvThreads) {
+          float v = part[x];
+          for (uint32_t u = 1; u < kHvWaves; ++u) v += part[(size_t)u * kHvSlots + x];
+          const uint32_t o = s0 + x;
+          if (o < cnt) {
+            c_idx[(size_t)base + o] = colof[x];
+            c_val[(size_t)base + o] = v;
+          }
+        }
+        __syncthreads();
+      }
     }
   }
   if (flags != 0) atomicOr(status, flags);
@@ -936,6 +1139,13 @@ int resident_blocks(K kernel, int &cache) {
 
 int g_count_resident = 0, g_fill_resident = 0;
 
+// Blocks of the heavy-row kernels: two per CU (the fill kernel's LDS holds
+// one), never more than the rows.
+uint32_t heavy_blocks(uint32_t m, const DeviceInfo &dev) {
+  const uint64_t cap = 2ull * (uint64_t)(dev.cus > 0 ? dev.cus : 1);
+  return (uint32_t)(m < cap ? (m > 0 ? m : 1) : cap);
+}
+
 }  // namespace
 
 uint32_t tr_blocks(uint32_t m, uint32_t q) {
@@ -1002,6 +1212,11 @@ hipError_t launch_spgemm_count(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
     hipLaunchKernelGGL(spgemm_count_kernel, dim3(nb), dim3(kSpWaves * kWave), 0,
                        stream, a, b, m, p, q, c_ptr + 1, pattern, list, status);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (q <= kSpWinWords * 32u && a.nnz >= kHeavyEntries) {
+      hipLaunchKernelGGL(spgemm_count_heavy_kernel, dim3(heavy_blocks(m, dev)), dim3(kHvThreads), 0,
+                         stream, a, b, m, p, q, c_ptr + 1, pattern, status);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   return launch_scan(c_ptr, m, static_cast<uint64_t *>(ws), status, stream);
 }
@@ -1017,7 +1232,21 @@ hipError_t launch_spgemm_fill(Csr a, Csr b, uint32_t m, uint32_t p, uint32_t q,
   hipLaunchKernelGGL(spgemm_fill_kernel, dim3(nb), dim3(kSpWaves * kWave), 0,
                      stream, a, b, m, p, q, c_ptr, c_idx, c_val, c_cap, pattern,
                      long_row_list(const_cast<uint32_t *>(pattern), m, q), status);
-  return hipGetLastError();
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (q <= kSpWinWords * 32u && a.nnz >= kHeavyEntries) {
+    static bool configured = false;  // the kernel's dynamic LDS limit, raised once
+    if (!configured) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void *>(&spgemm_fill_heavy_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kHvPartBytes);
+      if (e != hipSuccess) return e;
+      configured = true;
+    }
+    hipLaunchKernelGGL(spgemm_fill_heavy_kernel, dim3(heavy_blocks(m, dev)), dim3(kHvThreads),
+                       kHvPartBytes, stream, a, b, m, p, q, c_ptr, c_idx, c_val, c_cap, pattern,
+                       status);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 hipError_t launch_transpose(Csr a, uint32_t m, uint32_t q, uint32_t *at_ptr, uint32_t *at_idx,

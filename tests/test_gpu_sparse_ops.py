@@ -10,7 +10,8 @@ of exact f64 products: within 1e-12 of the sum of |x y|. The RSS from device
 operands is within 1e-5 of the scale of its cancelling terms.
 
 Shapes cover several column windows (16384 columns each), rows with more
-than 2048 outputs (several value windows), empty rows on both sides,
+than 2048 outputs (several value windows), rows of a with 2048 entries or
+more (split over a block of waves), empty rows on both sides,
 explicit zeros and exact cancellation, a ragged last window, one-column and
 zero-row operands, and the kNN-kernel workloads (n = 2000, 20000, 100000).
 """
@@ -73,6 +74,11 @@ PRODUCT_CASES = {
     # one column window (rows pass keeps its bitmaps) and rows of up to 7
     # value windows: their further windows run as units of their own
     "long_rows_kept": (300, 64, 12000, 6, 110, {"dense_rows_a": (0, 7, 150, 299)}),
+    # rows of a with 2048 entries or more: a block per row (16 runs of the
+    # row's entries) while b has one column window, else one wave per row
+    "heavy_rows": (60, 5000, 3000, 20, 8, {"dense_rows_a": (0, 7, 59), "empty_every_b": 9}),
+    "heavy_rows_long_outputs": (20, 2500, 16384, 5, 12, {"dense_rows_a": (3, 19)}),
+    "heavy_rows_two_windows": (30, 3000, 20000, 10, 6, {"dense_rows_a": (1, 29)}),
 }
 
 
@@ -101,17 +107,21 @@ def test_product_matches_oracle(case):
     got = product_on_gpu(a, b)
     want = S.matmul(a, b)
     rel = check_product(got, want, what=case)
-    if case in ("wide_rows", "long_rows_kept"):
+    if case in ("wide_rows", "long_rows_kept", "heavy_rows_long_outputs"):
         assert np.diff(got.indptr).max() > 2048  # several value windows per row
+    if case.startswith("heavy_rows"):
+        assert np.diff(a.indptr).max() >= 2048
     print("\n%s: nnz %d, max error / sum|ab| = %.2e" % (case, got.nnz, rel))
 
 
-def test_product_with_kept_bitmaps_equals_recomputed_columns():
+@pytest.mark.parametrize("p", [400, 3000])
+def test_product_with_kept_bitmaps_equals_recomputed_columns(p):
     # the fill pass reading the rows pass's bitmaps, or marking the columns
-    # again, writes the same product bit for bit
+    # again, writes the same product bit for bit (p = 3000: the dense rows of
+    # a have 3000 entries and go to the heavy-row blocks in both)
     rng = np.random.default_rng(12)
-    a = rand_csr(rng, 3000, 400, 9, empty_every=7, dense_rows=(3, 1500, 2999))
-    b = rand_csr(rng, 400, 9000, 30, empty_every=5)
+    a = rand_csr(rng, 3000, p, 9, empty_every=7, dense_rows=(3, 1500, 2999))
+    b = rand_csr(rng, p, 9000, 30 if p == 400 else 4, empty_every=5)
     da, db = dev(a), dev(b)
     m, q = a.shape[0], b.shape[1]
     outs = []
