@@ -114,6 +114,35 @@ def test_product_matches_oracle(case):
     print("\n%s: nnz %d, max error / sum|ab| = %.2e" % (case, got.nnz, rel))
 
 
+def test_product_rows_at_the_heavy_threshold_and_empty_products():
+    # rows of a with 2047 and 2048 entries (one on each side of the
+    # block-per-row threshold), a heavy row that meets only empty rows of b,
+    # and a heavy row of explicit zeros: the same pattern rule and value bound
+    rng = np.random.default_rng(31)
+    p, q = 6000, 900
+    rows = [np.sort(rng.choice(p - 2100, size=2047, replace=False)),
+            np.sort(rng.choice(p - 2100, size=2048, replace=False)),
+            np.arange(p - 2100, p),
+            np.sort(rng.choice(p, size=3000, replace=False))]
+    r = np.concatenate([np.full(c.size, i) for i, c in enumerate(rows)])
+    c = np.concatenate(rows)
+    v = rng.uniform(0.1, 1.0, size=c.size).astype(np.float32)
+    v[r == 3] = 0.0  # products of value 0: their columns stay, as explicit zeros
+    a = sp.csr_matrix((v, (r, c)), shape=(4, p))
+    a.sort_indices()
+    b = rand_csr(rng, p, q, 6, zeros=0.0)
+    keep = b.indptr[p - 2100]  # b's last 2100 rows empty
+    b = sp.csr_matrix((b.data[:keep], b.indices[:keep],
+                       np.minimum(b.indptr, keep)), shape=(p, q))
+    assert list(np.diff(a.indptr)) == [2047, 2048, 2100, 3000]
+    assert b[p - 2100:].nnz == 0
+    got = product_on_gpu(a, b)
+    check_product(got, S.matmul(a, b), what="heavy threshold")
+    assert got.indptr[3] == got.indptr[2]  # no products: an empty row
+    assert got.indptr[4] > got.indptr[3]
+    assert np.all(got.data[got.indptr[3]:got.indptr[4]] == 0.0)
+
+
 @pytest.mark.parametrize("p", [400, 3000])
 def test_product_with_kept_bitmaps_equals_recomputed_columns(p):
     # the fill pass reading the rows pass's bitmaps, or marking the columns
